@@ -1,2 +1,196 @@
-"""additive_bias_gqa_amd: additive-bias GQA attention over an external static KV
-cache, for MI355X (gfx950)."""
+"""additive_bias_gqa_amd: additive-bias grouped-query attention over an external
+static KV cache, for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over libabgqa.so (include/abgqa.h). Each function checks
+device, dtype, shape and contiguity of its torch tensors, passes raw device
+pointers and the current HIP stream, and raises RuntimeError with the
+library's message on failure. Every step of the computation runs in the HIP
+kernels; there is no fallback: a missing library raises at the first call.
+
+    kv_tensor_scatter(cache, update, write_indices)            in place
+    build_static_cache_bias(nonpad, q_start, slot_kind, S_q, max_seq, window,
+                            dtype=torch.bfloat16, out=None)     -> bias
+    attn_bias_gqa_fwd(q, k_cache, v_cache, bias, nonpad, scale, q_start=None,
+                      slot_kind=None, window=0, out=None)       -> out
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = ["kv_tensor_scatter", "build_static_cache_bias", "attn_bias_gqa_fwd",
+           "attn_bias_gqa_workspace_bytes", "abgqa_last_error", "library_path", "load"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libabgqa.so")
+_lib = None
+_lock = threading.Lock()
+
+F32, BF16 = 0, 1
+_DTYPE = {torch.float32: F32, torch.bfloat16: BF16}
+_c_i64p = ctypes.c_void_p
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libabgqa.so (built by additive_bias_gqa_amd.build); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with `python -m additive_bias_gqa_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        lib.kv_tensor_scatter.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, vp]
+        lib.kv_tensor_scatter.restype = ctypes.c_int
+        lib.build_static_cache_bias.argtypes = [vp, ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, vp]
+        lib.build_static_cache_bias.restype = ctypes.c_int
+        lib.attn_bias_gqa_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
+                                          i64, i64, i64, i64, i64, i64, ctypes.c_float, i64,
+                                          ctypes.c_int, vp, sz, vp]
+        lib.attn_bias_gqa_fwd.restype = ctypes.c_int
+        lib.attn_bias_gqa_workspace_bytes.argtypes = [i64] * 6
+        lib.attn_bias_gqa_workspace_bytes.restype = sz
+        lib.abgqa_last_error.argtypes = []
+        lib.abgqa_last_error.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def abgqa_last_error() -> str:
+    return load().abgqa_last_error().decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise RuntimeError(f"{what} failed (status {status}): {abgqa_last_error()}")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _opt(t, name, dtype, shape=None) -> int | None:
+    return None if t is None else _dev(t, name, dtype, shape)
+
+
+def kv_tensor_scatter(cache: torch.Tensor, update: torch.Tensor,
+                      write_indices: torch.Tensor | None) -> torch.Tensor:
+    """cache[b, h, write_indices[b] + t, :] = update[b, h, t, :] (in place)."""
+    if cache.dim() != 4 or update.dim() != 4:
+        raise ValueError("cache and update must be 4-D [B, Hkv, slots, D]")
+    B, H, T, D = cache.shape
+    if update.shape[0] != B or update.shape[1] != H or update.shape[3] != D:
+        raise ValueError("update must be [B, Hkv, S_new, D] matching the cache")
+    if cache.dtype not in _DTYPE or update.dtype != cache.dtype:
+        raise ValueError("cache/update must both be float32 or bfloat16")
+    c = _dev(cache, "cache")
+    u = _dev(update, "update") if update.numel() else None
+    w = _opt(write_indices, "write_indices", torch.int64, (B,))
+    _check(load().kv_tensor_scatter(c, u, w, B, H, T, update.shape[2], D, _DTYPE[cache.dtype],
+                                    _stream(cache)), "kv_tensor_scatter")
+    return cache
+
+
+def build_static_cache_bias(nonpad: torch.Tensor, q_start: torch.Tensor | None,
+                            slot_kind: torch.Tensor | None, S_q: int, max_seq: int,
+                            window: int, dtype: torch.dtype = torch.bfloat16,
+                            out: torch.Tensor | None = None) -> torch.Tensor:
+    """(B, 1, S_q, max_seq) bias: +0.0 where allowed, -inf where masked."""
+    B = nonpad.shape[0]
+    if out is None:
+        out = torch.empty((B, 1, S_q, max_seq), dtype=dtype, device=nonpad.device)
+    if out.dtype not in _DTYPE:
+        raise ValueError("bias dtype must be float32 or bfloat16")
+    o = _dev(out, "bias", None, (B, 1, S_q, max_seq))
+    n = _dev(nonpad, "nonpad", torch.int64, (B,))
+    qs = _opt(q_start, "q_start", torch.int64, (B,))
+    sk = _opt(slot_kind, "slot_kind", torch.int32, (B, max_seq))
+    _check(load().build_static_cache_bias(o, _DTYPE[out.dtype], n, qs, sk, B, S_q, max_seq,
+                                          int(window), _stream(out)), "build_static_cache_bias")
+    return out
+
+
+def attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, max_seq, D) -> int:
+    return int(load().attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, max_seq, D))
+
+
+_workspaces: dict = {}
+
+
+def _workspace(device: torch.device, nbytes: int) -> torch.Tensor | None:
+    """A zero-initialised per-device workspace, grown on demand (the library
+    leaves its arrival counters at zero after every call)."""
+    if nbytes == 0:
+        return None
+    key = (device.type, device.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def attn_bias_gqa_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      bias: torch.Tensor | None, nonpad: torch.Tensor, scale: float,
+                      q_start: torch.Tensor | None = None,
+                      slot_kind: torch.Tensor | None = None, window: int = 0,
+                      out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """softmax(scale * Q K^T + bias) V over the static cache (GQA: head h reads
+    KV head h // (Hq // Hkv)). bias=None evaluates the static-cache rules
+    (nonpad, q_start, slot_kind, window) inside the kernel instead."""
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, S_q, D] and the caches [B, Hkv, max_seq, D]")
+    B, Hq, S_q, D = q.shape
+    Hkv, T = k_cache.shape[1], k_cache.shape[2]
+    if q.dtype not in _DTYPE:
+        raise ValueError("q must be float32 or bfloat16")
+    qp = _dev(q, "q")
+    kp = _dev(k_cache, "k_cache", q.dtype, (B, Hkv, T, D))
+    vp_ = _dev(v_cache, "v_cache", q.dtype, (B, Hkv, T, D))
+    bp, bdt = None, BF16
+    if bias is not None:
+        if bias.dtype not in _DTYPE:
+            raise ValueError("bias must be float32 or bfloat16")
+        bp, bdt = _dev(bias, "bias", None, (B, 1, S_q, T)), _DTYPE[bias.dtype]
+    npd = _dev(nonpad, "nonpad", torch.int64, (B,))
+    qs = _opt(q_start, "q_start", torch.int64, (B,))
+    sk = _opt(slot_kind, "slot_kind", torch.int32, (B, T))
+    if out is None:
+        out = torch.empty_like(q)
+    op = _dev(out, "out", q.dtype, q.shape)
+    lib = load()
+    need = int(lib.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, T, D))
+    if workspace is None:
+        workspace = _workspace(q.device, need)
+    wp = None if workspace is None else _dev(workspace, "workspace")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.attn_bias_gqa_fwd(op, qp, kp, vp_, bp, bdt, npd, qs, sk, B, Hq, Hkv, S_q, T, D,
+                                 float(scale), int(window), _DTYPE[q.dtype], wp, wbytes,
+                                 _stream(q)), "attn_bias_gqa_fwd")
+    return out

@@ -1,0 +1,172 @@
+// C ABI of libabgqa.so: host-side validation and dispatch. See include/abgqa.h
+// for the contract of each entry point and the passages it follows.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <string>
+
+#include "abgqa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+abgqa_status fail(abgqa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+abgqa_status hip_fail(const char* what, hipError_t e) {
+  return fail(ABGQA_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = getenv("ABGQA_LOG");
+    return v && v[0] && v[0] != '0';
+  }();
+  return on;
+}
+
+constexpr int64_t kMaxSeq = (int64_t)1 << 24;  // slot indices stay exact in int32
+
+bool head_dim_ok(int64_t D) { return D == 64 || D == 128 || D == 256 || D == 512; }
+
+}  // namespace
+
+extern "C" {
+
+abgqa_status kv_tensor_scatter(void* cache, const void* update, const int64_t* write_indices,
+                               int64_t B, int64_t Hkv, int64_t max_seq, int64_t S_new, int64_t D,
+                               abgqa_dtype dtype, void* stream) {
+  g_last_error.clear();
+  if (B <= 0 || Hkv <= 0 || max_seq <= 0 || D <= 0)
+    return fail(ABGQA_ERR_INVALID, "kv_tensor_scatter: B, Hkv, max_seq and D must be positive");
+  if (S_new < 0) return fail(ABGQA_ERR_INVALID, "kv_tensor_scatter: S_new must be >= 0");
+  if (max_seq > kMaxSeq) return fail(ABGQA_ERR_UNSUPPORTED, "kv_tensor_scatter: max_seq above 2^24");
+  if (dtype != ABGQA_F32 && dtype != ABGQA_BF16)
+    return fail(ABGQA_ERR_UNSUPPORTED, "kv_tensor_scatter: dtype must be ABGQA_F32 or ABGQA_BF16");
+  const int64_t row_bytes = D * (dtype == ABGQA_F32 ? 4 : 2);
+  if (row_bytes % 16 != 0 || row_bytes > 4096)
+    return fail(ABGQA_ERR_UNSUPPORTED,
+                "kv_tensor_scatter: D * element size must be a multiple of 16 bytes, at most 4096");
+  if (S_new == 0) return ABGQA_OK;  // nothing to append
+  if (!cache || !update) return fail(ABGQA_ERR_INVALID, "kv_tensor_scatter: null cache or update");
+  if (!aligned(cache, 16) || !aligned(update, 16) || (write_indices && !aligned(write_indices, 8)))
+    return fail(ABGQA_ERR_INVALID, "kv_tensor_scatter: misaligned pointer");
+  const hipError_t e = abgqa::launch_scatter(cache, update, write_indices, B, Hkv, max_seq, S_new,
+                                             row_bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("kv_tensor_scatter", e);
+  return ABGQA_OK;
+}
+
+abgqa_status build_static_cache_bias(void* bias, abgqa_dtype bias_dtype,
+                                     const int64_t* nonpad_kv_seqlen, const int64_t* q_start,
+                                     const int32_t* slot_kind, int64_t B, int64_t S_q,
+                                     int64_t max_seq, int64_t window, void* stream) {
+  g_last_error.clear();
+  if (B <= 0 || S_q <= 0 || max_seq <= 0)
+    return fail(ABGQA_ERR_INVALID, "build_static_cache_bias: B, S_q and max_seq must be positive");
+  if (max_seq > kMaxSeq) return fail(ABGQA_ERR_UNSUPPORTED, "build_static_cache_bias: max_seq above 2^24");
+  if (bias_dtype != ABGQA_F32 && bias_dtype != ABGQA_BF16)
+    return fail(ABGQA_ERR_UNSUPPORTED, "build_static_cache_bias: bias dtype must be ABGQA_F32 or ABGQA_BF16");
+  if (!bias || !nonpad_kv_seqlen)
+    return fail(ABGQA_ERR_INVALID, "build_static_cache_bias: null bias or nonpad_kv_seqlen");
+  if (!aligned(bias, 16) || !aligned(nonpad_kv_seqlen, 8) || (q_start && !aligned(q_start, 8)) ||
+      (slot_kind && !aligned(slot_kind, 16)))
+    return fail(ABGQA_ERR_INVALID, "build_static_cache_bias: misaligned pointer");
+  const hipError_t e = abgqa::launch_bias(bias, bias_dtype == ABGQA_BF16, nonpad_kv_seqlen, q_start,
+                                          slot_kind, B, S_q, max_seq, window, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("build_static_cache_bias", e);
+  return ABGQA_OK;
+}
+
+size_t attn_bias_gqa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q,
+                                     int64_t max_seq, int64_t D) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_q <= 0 || max_seq <= 0 || D <= 0 || Hq % Hkv) return 0;
+  const int64_t G = Hq / Hkv;
+  if (S_q * G > 16) return 0;  // prefill path: no workspace
+  return abgqa::decode_workspace_bytes(B, Hkv, S_q, G, D, max_seq);
+}
+
+abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const void* bias, abgqa_dtype bias_dtype,
+                               const int64_t* nonpad_kv_seqlen, const int64_t* q_start,
+                               const int32_t* slot_kind, int64_t B, int64_t Hq, int64_t Hkv,
+                               int64_t S_q, int64_t max_seq, int64_t D, float scale, int64_t window,
+                               abgqa_dtype dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  g_last_error.clear();
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_q <= 0 || max_seq <= 0 || D <= 0)
+    return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: B, Hq, Hkv, S_q, max_seq and D must be positive");
+  if (Hq % Hkv != 0) return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: Hq must be a multiple of Hkv");
+  if (S_q > max_seq) return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: S_q must not exceed max_seq");
+  if (!head_dim_ok(D)) return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: D must be 64, 128, 256 or 512");
+  if (max_seq > kMaxSeq) return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: max_seq above 2^24");
+  if (dtype != ABGQA_F32 && dtype != ABGQA_BF16)
+    return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: dtype must be ABGQA_F32 or ABGQA_BF16");
+  if (bias && bias_dtype != ABGQA_F32 && bias_dtype != ABGQA_BF16)
+    return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: bias dtype must be ABGQA_F32 or ABGQA_BF16");
+  if (!out || !q || !k_cache || !v_cache || !nonpad_kv_seqlen)
+    return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: null out, q, k_cache, v_cache or nonpad_kv_seqlen");
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      (bias && !aligned(bias, 16)) || !aligned(nonpad_kv_seqlen, 8) || (q_start && !aligned(q_start, 8)) ||
+      (slot_kind && !aligned(slot_kind, 16)))
+    return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: misaligned pointer");
+  if (out == q || out == k_cache || out == v_cache || out == bias)
+    return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: out must not alias an input");
+  const int64_t G = Hq / Hkv;
+  if (B * Hq * S_q > ((int64_t)1 << 31) || B * Hkv > ((int64_t)1 << 24))
+    return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: too many rows");
+
+  abgqa::AttnParams p{};
+  p.out = out; p.q = q; p.k = k_cache; p.v = v_cache; p.bias = bias;
+  p.nonpad = nonpad_kv_seqlen; p.q_start = q_start; p.slot_kind = slot_kind;
+  p.B = (int)B; p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.G = (int)G; p.S_q = (int)S_q;
+  p.T = (int)max_seq; p.D = (int)D; p.window = window; p.scale = scale;
+  p.bias_is_bf16 = (bias_dtype == ABGQA_BF16);
+  hipStream_t st = (hipStream_t)stream;
+
+  hipError_t e;
+  const char* path;
+  if (dtype == ABGQA_F32) {
+    path = "f32";
+    e = abgqa::launch_attn_f32(p, st);
+  } else if (S_q * G <= 16) {
+    path = "decode";
+    const size_t need = abgqa::decode_workspace_bytes(B, Hkv, S_q, G, D, max_seq);
+    if (!workspace || workspace_bytes < need)
+      return fail(ABGQA_ERR_WORKSPACE, "attn_bias_gqa_fwd: workspace of %zu bytes needed, %zu given",
+                  need, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: workspace not 256-byte aligned");
+    p.n_split = abgqa::decode_num_splits(B, Hkv, max_seq);
+    p.ws_ctr = (unsigned*)workspace;
+    p.ws_part = (float*)((char*)workspace + ((B * Hkv * 4 + 255) / 256) * 256);
+    e = abgqa::launch_attn_decode(p, st);
+  } else {
+    path = "prefill";
+    if (G > 64) return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: more than 64 query heads per KV head");
+    if (abgqa::prefill_lds_bytes((int)D, (int)max_seq) > 160 * 1024)
+      return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: max_seq too large for the prefill tile list");
+    e = abgqa::launch_attn_prefill(p, st);
+  }
+  if (log_enabled())
+    fprintf(stderr, "[abgqa] attn_bias_gqa_fwd path=%s B=%lld Hq=%lld Hkv=%lld S_q=%lld T=%lld D=%lld %s splits=%d\n",
+            path, (long long)B, (long long)Hq, (long long)Hkv, (long long)S_q, (long long)max_seq,
+            (long long)D, bias ? "bias" : "rules", p.n_split);
+  if (e != hipSuccess) return hip_fail("attn_bias_gqa_fwd", e);
+  return ABGQA_OK;
+}
+
+const char* abgqa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,473 @@
+// bf16 split-KV decode attention over the static cache (S_q * G <= 16 rows).
+//
+// What it computes: onnxruntime skill "cuda-attention-kernel-patterns",
+// section 4 (scale * QK^T, + bias, softmax, times V), section 6 (a row with no
+// allowed key, or nonpad = 0, writes zeros; masked keys removed by selection),
+// section 11 (external cache: keys are the slots < nonpad_kv_seqlen); mobius
+// issue #366 (the float bias carries causal/window/block/padding rules); query
+// head h reads KV head h / G (onnxruntime PR #28242, CPU GQA excerpt).
+//
+// Why split-KV: decode is bound by memory bandwidth whatever the kernel
+// (mobius skill "attention-optimization", "Flash Attention: when it actually
+// helps"), and the decode edge of the grouped-query op comes from a dedicated
+// single-token kernel (same skill, "In-place KV ... static cache"). So every
+// KV byte is read once, by one of n_split workgroups per (batch, KV head), and
+// every such read is shared by the G query heads of the group.
+//
+// Layout of the work
+//   grid      B * Hkv * n_split workgroups of 4 wavefronts; consecutive
+//             logical ids (the splits of one (b, kv head)) share an XCD.
+//   rows      r = s * G + g (query token s, head g of the group), R <= 16;
+//             the 16 rows of the matrix-core tile are padded with zeros.
+//   live      [lo, hi): the first and last key any row may attend, found from
+//             the bias (or from the rules); split i takes an even share of it.
+//   block     16 keys per wavefront step:
+//             S = Q K^T on the matrix cores (K read straight from HBM into the
+//             B-operand registers, 16 bytes per lane), online softmax on the
+//             S layout (lane = key, 4 rows per lane), then O += P V on the
+//             vector ALU with V rows read coalesced (lane = 8 values of d).
+//             The softmax weights cross layouts through a small LDS buffer.
+//   merge     the 4 wavefronts merge in LDS; each workgroup writes its
+//             (m, l, O) partial; the last workgroup of a (b, kv head) to arrive
+//             (device-scope counter) combines the partials:
+//             m = max m_i, y = sum 2^(m_i - m) O_i / sum 2^(m_i - m) l_i.
+//
+// Softmax runs in base 2 on x * log2(e). The running maximum is only raised
+// when a new score exceeds it by more than 8 (a factor 256), so rescaling the
+// accumulators is rare; weights stay <= 2^8 and the result is unchanged.
+#include "common.h"
+#include "kernels.h"
+#include "mask_rules.h"
+
+namespace abgqa {
+
+namespace {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecWaves = 4;
+constexpr float kRescaleThreshold = 8.f;
+
+template <typename BiasT>
+__device__ __forceinline__ bool bias_live_bits(BiasT v);
+template <>
+__device__ __forceinline__ bool bias_live_bits<uint16_t>(uint16_t v) { return v != 0xFF80; }
+template <>
+__device__ __forceinline__ bool bias_live_bits<uint32_t>(uint32_t v) { return v != 0xFF800000u; }
+
+template <typename BiasT>
+__device__ __forceinline__ float bias_value(BiasT v);
+template <>
+__device__ __forceinline__ float bias_value<uint16_t>(uint16_t v) { return bf16_bits_to_f32(v); }
+template <>
+__device__ __forceinline__ float bias_value<uint32_t>(uint32_t v) { return __uint_as_float(v); }
+
+}  // namespace
+
+int decode_num_splits(int64_t B, int64_t Hkv, int64_t max_seq) {
+  // about 1024 workgroups in flight over the 256 CUs, at least ~64 keys each
+  int64_t n = (1024 + B * Hkv - 1) / (B * Hkv);
+  const int64_t by_len = (max_seq + 63) / 64;
+  if (n > by_len) n = by_len;
+  if (n > 64) n = 64;
+  if (n < 1) n = 1;
+  return (int)n;
+}
+
+static inline int64_t round_up_rows(int64_t R) {
+  int64_t nr = 1;
+  while (nr < R) nr *= 2;
+  return nr;
+}
+
+// floats of one partial record: O[NR][D], then m[NR], l[NR], padded to 16 bytes
+__host__ __device__ constexpr int64_t part_floats(int64_t NR, int64_t D) {
+  return (NR * D + 2 * NR + 3) & ~(int64_t)3;
+}
+
+// workspace: counters [B*Hkv] u32 (region rounded up to 256 B), then one
+// partial record per (b, kv head, split)
+size_t decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_q, int64_t G, int64_t D,
+                              int64_t max_seq) {
+  const int64_t NR = round_up_rows(S_q * G);
+  const int64_t n_split = decode_num_splits(B, Hkv, max_seq);
+  const size_t ctr = (size_t)((B * Hkv * 4 + 255) / 256) * 256;
+  const size_t part = (size_t)B * Hkv * n_split * part_floats(NR, D) * sizeof(float);
+  return ctr + part;
+}
+
+template <int D, int NR, bool kRules, typename BiasT>
+__global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(AttnParams p) {
+  constexpr int KSTEPS = D / 32;    // matrix-core k-steps over the head dim
+  constexpr int LPR = D / 8;        // lanes per V row (8 bf16 per lane)
+  constexpr int KPI = 64 / LPR;     // V rows per wavefront load
+  constexpr int NV = 16 / KPI;      // V loads per 16-key block
+  constexpr int PART = (int)part_floats(NR, D);
+
+  __shared__ float s_p[kDecWaves][16][NR];  // softmax weights, key-major
+  __shared__ float s_alpha[kDecWaves][NR];
+  __shared__ float s_m[kDecWaves][NR];
+  __shared__ float s_l[kDecWaves][NR];
+  __shared__ float s_o[NR * D];             // merged O of the workgroup
+  __shared__ int s_range[2];
+  __shared__ int32_t s_kq[16];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int T = p.T, G = p.G, R = p.S_q * p.G;
+
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = wg % p.n_split;
+  const int bh = wg / p.n_split;
+  const int hk = bh % p.Hkv;
+  const int64_t b = bh / p.Hkv;
+  const int np = (int)clamp_nonpad(p.nonpad[b], T);
+
+  // ---- 1. live range [lo, hi) of keys, over all S_q rows -------------------
+  if (tid == 0) { s_range[0] = INT32_MAX; s_range[1] = -1; }
+  for (int i = tid; i < NR * D; i += kDecThreads) s_o[i] = 0.f;
+  __syncthreads();
+  {
+    int lo = INT32_MAX, hi = -1;
+    if constexpr (!kRules) {
+      const BiasT* bb = (const BiasT*)p.bias + b * p.S_q * (int64_t)T;
+      constexpr int EPV = 16 / sizeof(BiasT);  // elements per 16-byte load
+      const int nvec = (np + EPV - 1) / EPV;
+      const bool vec = (T % EPV) == 0;
+      for (int idx = tid; idx < p.S_q * nvec; idx += kDecThreads) {
+        const int s = idx / nvec;
+        const int j0 = (idx - s * nvec) * EPV;
+        const BiasT* row = bb + (int64_t)s * T;
+        BiasT vals[EPV];
+        if (vec) {
+          *reinterpret_cast<u32x4*>(vals) = ld_global<u32x4>(row + j0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) vals[e] = (j0 + e < T) ? row[j0 + e] : (BiasT)0;
+        }
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const int j = j0 + e;
+          if (j < np && bias_live_bits<BiasT>(vals[e])) {
+            lo = min(lo, j);
+            hi = max(hi, j);
+          }
+        }
+      }
+    } else {
+      // causal / window keys of every row, then the image block of any row
+      if (tid < p.S_q) {
+        const RowRule rr = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, tid, p.S_q, T, p.window);
+        s_kq[tid] = rr.kind_q;
+        int64_t a = (rr.window > 0) ? rr.q - rr.window + 1 : 0;
+        if (a < 0) a = 0;
+        const int64_t z = rr.q < (int64_t)np - 1 ? rr.q : (int64_t)np - 1;
+        if (a <= z) { lo = (int)a; hi = (int)z; }
+      }
+      __syncthreads();
+      bool any_block = false;
+      for (int s = 0; s < p.S_q; ++s) any_block |= s_kq[s] > 0;
+      if (any_block) {
+        const int32_t* kr = p.slot_kind + b * T;
+        for (int j = tid; j < np; j += kDecThreads) {
+          const int32_t kj = kr[j];
+          if (kj <= 0) continue;
+          for (int s = 0; s < p.S_q; ++s) {
+            if (s_kq[s] == kj) { lo = min(lo, j); hi = max(hi, j); break; }
+          }
+        }
+      }
+    }
+    if (hi >= 0) {
+      atomicMin(&s_range[0], lo);
+      atomicMax(&s_range[1], hi);
+    }
+  }
+  __syncthreads();
+  int live_lo = s_range[0], live_hi = s_range[1] + 1;
+  if (live_hi <= 0) { live_lo = 0; live_hi = 0; }
+  const int live = live_hi - live_lo;
+  const int per = ((live + p.n_split - 1) / p.n_split + 15) & ~15;
+  const int my_lo = live_lo + split * per;
+  const int my_hi = min(live_hi, my_lo + per);
+
+  // ---- 2. per-lane row data -------------------------------------------------
+  // Q as the A operand: lane holds row (lane % 16), d-slots 32*i + 8*(lane/16)
+  const int qrow = lane & 15;
+  const int kgrp = lane >> 4;
+  bf16x8 qa[KSTEPS];
+  {
+    const bool ok = qrow < R;
+    const int s = ok ? qrow / G : 0, g = ok ? qrow % G : 0;
+    const __bf16* qp = (const __bf16*)p.q +
+        (((b * p.Hq + hk * G + g) * p.S_q + s) * (int64_t)D) + 8 * kgrp;
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
+      if (ok) qa[i] = ld_global<bf16x8>(qp + 32 * i);
+      else qa[i] = bf16x8{};
+    }
+  }
+  // rows this lane holds in the S layout: r = 4 * kgrp + e
+  int row_s[4];
+  bool row_ok[4];
+  RowRule rules[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 4 * kgrp + e;
+    row_ok[e] = r < R;
+    row_s[e] = row_ok[e] ? r / G : 0;
+    if constexpr (kRules) rules[e] = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, row_s[e], p.S_q, T, p.window);
+  }
+  const float scale_log2 = p.scale * kLog2e;
+
+  const __bf16* kbase = (const __bf16*)p.k + (b * p.Hkv + hk) * (int64_t)T * D;
+  const __bf16* vbase = (const __bf16*)p.v + (b * p.Hkv + hk) * (int64_t)T * D;
+  const BiasT* biasb = kRules ? nullptr : (const BiasT*)p.bias + b * p.S_q * (int64_t)T;
+  const int32_t* kindb = p.slot_kind ? p.slot_kind + b * T : nullptr;
+
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { m_run[e] = -INFINITY; l_run[e] = 0.f; }
+  float o[NR][8];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[r][c] = 0.f;
+
+  const int vkey = lane / LPR;       // key offset within a V load
+  const int vd = 8 * (lane % LPR);   // first d of this lane in the PV layout
+
+  // ---- 3. stream 16-key blocks, wavefront w takes blocks w, w+4, ... --------
+  for (int j0 = my_lo + 16 * w; j0 < my_hi; j0 += 16 * kDecWaves) {
+    // K for the B operand: key j0 + (lane % 16), d-slots 32*i + 8*kgrp
+    const int jk = j0 + qrow;
+    const bool kin = jk < my_hi;
+    bf16x8 kb[KSTEPS];
+    const __bf16* kp = kbase + (int64_t)jk * D + 8 * kgrp;
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) kb[i] = kin ? ld_global<bf16x8>(kp + 32 * i) : bf16x8{};
+    // V rows for the PV step (zero beyond the range: never multiply garbage)
+    bf16x8 vv[NV];
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int jv = j0 + it * KPI + vkey;
+      vv[it] = (jv < my_hi) ? ld_global<bf16x8>(vbase + (int64_t)jv * D + vd) : bf16x8{};
+    }
+    // bias / rules for the 4 rows of this lane at key jk
+    float badd[4];
+    bool keep[4];
+    const int32_t kj = (kRules && kin && kindb) ? kindb[jk] : 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      badd[e] = 0.f;
+      if constexpr (kRules) {
+        keep[e] = row_ok[e] && kin && rules[e].allowed(jk, kj);
+      } else {
+        bool k_ = row_ok[e] && kin;
+        if (k_) {
+          const BiasT bv = biasb[(int64_t)row_s[e] * T + jk];
+          k_ = bias_live_bits<BiasT>(bv);
+          badd[e] = bias_value<BiasT>(bv) * kLog2e;
+        }
+        keep[e] = k_;
+      }
+    }
+    // S = Q K^T on the matrix cores
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) acc = mfma16x16x32(qa[i], kb[i], acc);
+
+    // online softmax on the S layout: lane = key (lane % 16), rows 4*kgrp + e
+    float x[4];
+    bool need_any = false;
+    float alpha[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = keep[e] ? fmaf(acc[e], scale_log2, badd[e]) : -INFINITY;
+      const float mt = row16_max(x[e]);
+      const float mn = fmaxf(m_run[e], mt);
+      const bool need = mn > m_run[e] + kRescaleThreshold;
+      alpha[e] = need ? fast_exp2(m_run[e] - mn) : 1.f;
+      if (need) m_run[e] = mn;
+      need_any |= need;
+    }
+    if (__any(need_any)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        l_run[e] *= alpha[e];
+        const int r = 4 * kgrp + e;
+        if (qrow == 0 && r < NR) s_alpha[w][r] = alpha[e];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const float a = s_alpha[w][r];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[r][c] *= a;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pe = (x[e] == -INFINITY) ? 0.f : fast_exp2(x[e] - m_run[e]);
+      l_run[e] += pe;
+      const int r = 4 * kgrp + e;
+      if (r < NR) s_p[w][qrow][r] = pe;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // O += P V on the vector ALU (fp32)
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int jj = it * KPI + vkey;
+      float pw[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) pw[r] = s_p[w][jj][r];
+      const u32x4 raw = __builtin_bit_cast(u32x4, vv[it]);
+      float vf[8];
+      vf[0] = bf16lo(raw.x); vf[1] = bf16hi(raw.x);
+      vf[2] = bf16lo(raw.y); vf[3] = bf16hi(raw.y);
+      vf[4] = bf16lo(raw.z); vf[5] = bf16hi(raw.z);
+      vf[6] = bf16lo(raw.w); vf[7] = bf16hi(raw.w);
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[r][c] = fmaf(pw[r], vf[c], o[r][c]);
+    }
+    __builtin_amdgcn_wave_barrier();  // s_p is rewritten by the next block
+  }
+
+  // ---- 4. merge the wavefronts of this workgroup ----------------------------
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float lt = row16_sum(l_run[e]);
+    const int r = 4 * kgrp + e;
+    if (qrow == 0 && r < NR) { s_m[w][r] = m_run[e]; s_l[w][r] = lt; }
+  }
+  // lanes sharing a d-chunk hold different keys: sum them
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float v = o[r][c];
+      if constexpr (KPI >= 2) v += lane_xor(v, 32);
+      if constexpr (KPI >= 4) v += lane_xor(v, 16);
+      if constexpr (KPI >= 8) v += lane_xor(v, 8);
+      o[r][c] = v;
+    }
+  __syncthreads();
+  float m_wg[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    float mm = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kDecWaves; ++ww) mm = fmaxf(mm, s_m[ww][r]);
+    m_wg[r] = mm;
+  }
+  if (lane < LPR) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const float f = (m_wg[r] == -INFINITY) ? 0.f : fast_exp2(s_m[w][r] - m_wg[r]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) atomicAdd(&s_o[r * D + vd + c], o[r][c] * f);
+    }
+  }
+  __syncthreads();
+
+  // ---- 5. write this workgroup's partial ------------------------------------
+  float* part = p.ws_part + ((int64_t)bh * p.n_split + split) * PART;
+  for (int i = tid; i < NR * D / 4; i += kDecThreads)
+    reinterpret_cast<f32x4*>(part)[i] = reinterpret_cast<const f32x4*>(s_o)[i];
+  if (tid < NR) {
+    const int r = tid;
+    float lsum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kDecWaves; ++ww) {
+      const float f = (m_wg[r] == -INFINITY) ? 0.f : fast_exp2(s_m[ww][r] - m_wg[r]);
+      lsum += s_l[ww][r] * f;
+    }
+    part[NR * D + r] = m_wg[r];
+    part[NR * D + NR + r] = lsum;
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = atomicAdd(&p.ws_ctr[bh], 1u);
+    s_last = (prev == (unsigned)(p.n_split - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- 6. last workgroup of (b, kv head): combine the splits ----------------
+  __threadfence();
+  const float* parts = p.ws_part + (int64_t)bh * p.n_split * PART;
+  for (int idx = tid; idx < R * (D / 8); idx += kDecThreads) {
+    const int r = idx / (D / 8);
+    const int d0 = (idx - r * (D / 8)) * 8;
+    float mm = -INFINITY;
+    for (int sp = 0; sp < p.n_split; ++sp) mm = fmaxf(mm, parts[sp * PART + NR * D + r]);
+    float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    if (mm != -INFINITY) {
+      for (int sp = 0; sp < p.n_split; ++sp) {
+        const float* ps = parts + sp * PART;
+        const float ms = ps[NR * D + r];
+        if (ms == -INFINITY) continue;  // an empty split
+        const float f = fast_exp2(ms - mm);
+        den = fmaf(ps[NR * D + NR + r], f, den);
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(ps + r * D + d0);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(ps + r * D + d0 + 4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) { num[c] = fmaf(a0[c], f, num[c]); num[4 + c] = fmaf(a1[c], f, num[4 + c]); }
+      }
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    const int s = r / G, g = r % G;
+    uint16_t* op = (uint16_t*)p.out + (((b * p.Hq + hk * G + g) * p.S_q + s) * (int64_t)D) + d0;
+    u32x4 pk;
+    pk.x = pack_bf16x2(num[0] * inv, num[1] * inv);
+    pk.y = pack_bf16x2(num[2] * inv, num[3] * inv);
+    pk.z = pack_bf16x2(num[4] * inv, num[5] * inv);
+    pk.w = pack_bf16x2(num[6] * inv, num[7] * inv);
+    *reinterpret_cast<u32x4*>(op) = pk;
+  }
+  if (tid == 0) atomicExch(&p.ws_ctr[bh], 0u);  // leave the counter at zero for the next call
+}
+
+template <int D, int NR>
+static hipError_t launch_decode_d(const AttnParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.n_split));
+  if (p.bias == nullptr)
+    hipLaunchKernelGGL((attn_decode_kernel<D, NR, true, uint16_t>), grid, dim3(kDecThreads), 0, stream, p);
+  else if (p.bias_is_bf16)
+    hipLaunchKernelGGL((attn_decode_kernel<D, NR, false, uint16_t>), grid, dim3(kDecThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_decode_kernel<D, NR, false, uint32_t>), grid, dim3(kDecThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_decode_nr(const AttnParams& p, hipStream_t stream) {
+  const int R = p.S_q * p.G;
+  if (R <= 1) return launch_decode_d<D, 1>(p, stream);
+  if (R <= 2) return launch_decode_d<D, 2>(p, stream);
+  if (R <= 4) return launch_decode_d<D, 4>(p, stream);
+  if (R <= 8) return launch_decode_d<D, 8>(p, stream);
+  return launch_decode_d<D, 16>(p, stream);
+}
+
+hipError_t launch_attn_decode(const AttnParams& p, hipStream_t stream) {
+  switch (p.D) {
+    case 64: return launch_decode_nr<64>(p, stream);
+    case 128: return launch_decode_nr<128>(p, stream);
+    case 256: return launch_decode_nr<256>(p, stream);
+    case 512: return launch_decode_nr<512>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace abgqa

@@ -1,0 +1,121 @@
+// Device helpers shared by the gfx950 kernels of libabgqa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace abgqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWave = 64;
+
+// ---- bf16 <-> fp32 ---------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+// low / high halves of a packed pair of bf16
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 with round-to-nearest-even (the language cast; gfx950 has a
+// native conversion for it).
+__device__ __forceinline__ __bf16 f32_to_bf16(float f) { return static_cast<__bf16>(f); }
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// ---- matrix cores ----------------------------------------------------------
+// D[16x16] += A[16x32] * B[32x16], bf16 in, fp32 accumulate.
+// Lane l holds A row (l % 16) and B column (l % 16), 8 consecutive k-slots each
+// (slots 8*(l/16) .. +7); the result lane l holds column (l % 16), rows
+// 4*(l/16) .. +3. Only the pairing of A and B slots matters for a contraction,
+// so callers may map the 32 k-slots to any 32 indices as long as A and B agree.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- cross-lane ------------------------------------------------------------
+// DPP row (16-lane) controls of the gfx9 family.
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// max / sum over the 16 lanes of a DPP row; every lane of the row gets the result
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppRowHalfMirror>(v);
+  v += dpp_f32<kDppRowMirror>(v);
+  return v;
+}
+
+// exchange with lane ^ mask through the LDS crossbar (no LDS memory used)
+__device__ __forceinline__ float lane_xor(float v, int mask) {
+  const int lane = __lane_id();
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(v)));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  v = fmaxf(v, lane_xor(v, 16));
+  v = fmaxf(v, lane_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += lane_xor(v, 16);
+  v += lane_xor(v, 32);
+  return v;
+}
+
+// exp2 that maps -inf to exactly 0 (v_exp_f32 does) without NaN for finite input
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- grid mapping ----------------------------------------------------------
+// MI355X dispatches consecutive workgroups round-robin over its 8 XCDs, each
+// with its own L2. Remap so that consecutive logical ids run on one XCD (and
+// share its L2): hardware id h -> logical (h % 8) * ceil(n/8) + h / 8, with the
+// ids past n (when n % 8 != 0) folded back in order.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ int xcd_remap(int hw, int n) {
+  const int per = (n + kNumXcd - 1) / kNumXcd;
+  const int full = n - (per - 1) * kNumXcd;  // XCDs that get `per` ids
+  const int xcd = hw % kNumXcd;
+  const int idx = hw / kNumXcd;
+  return (xcd < full) ? xcd * per + idx : full * per + (xcd - full) * (per - 1) + idx;
+}
+
+// ---- memory ----------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ T ld_global(const void* p) {
+  return *reinterpret_cast<const T*>(p);
+}
+
+__device__ __forceinline__ int64_t clamp_nonpad(int64_t np, int64_t max_seq) {
+  return np < 0 ? 0 : (np > max_seq ? max_seq : np);
+}
+
+}  // namespace abgqa

@@ -1,0 +1,53 @@
+// Internal launcher interface between the C ABI (abi.cpp) and the kernels.
+// Arguments arrive validated: sizes positive, pointers non-null and aligned.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace abgqa {
+
+hipError_t launch_scatter(void* cache, const void* update, const int64_t* write_indices,
+                          int64_t B, int64_t H, int64_t max_seq, int64_t S_new,
+                          int64_t row_bytes, hipStream_t stream);
+
+hipError_t launch_bias(void* bias, int bias_is_bf16, const int64_t* nonpad,
+                       const int64_t* q_start, const int32_t* slot_kind, int64_t B,
+                       int64_t S_q, int64_t max_seq, int64_t window, hipStream_t stream);
+
+// Everything an attention kernel reads, passed by value.
+struct AttnParams {
+  void* out;                 // [B, Hq, S_q, D]
+  const void* q;             // [B, Hq, S_q, D]
+  const void* k;             // [B, Hkv, T, D]
+  const void* v;             // [B, Hkv, T, D]
+  const void* bias;          // [B, 1, S_q, T] or null (in-kernel rules)
+  const int64_t* nonpad;     // [B]
+  const int64_t* q_start;    // [B] or null (rules variant only)
+  const int32_t* slot_kind;  // [B, T] or null (rules variant only)
+  int B, Hq, Hkv, G, S_q, T, D;
+  int64_t window;            // rules variant only; <= 0 none
+  float scale;               // multiplies q.k
+  int bias_is_bf16;          // bias dtype when bias != null
+  // split-KV decode
+  float* ws_part;            // partial results
+  unsigned* ws_ctr;          // [B * Hkv] arrival counters (zero between calls)
+  int n_split;
+};
+
+// fp32 path (any S_q): one wavefront per query row.
+hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
+
+// bf16 decode path (S_q * G <= 16): split-KV with an in-kernel combine.
+int decode_num_splits(int64_t B, int64_t Hkv, int64_t max_seq);
+size_t decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_q, int64_t G, int64_t D,
+                              int64_t max_seq);
+hipError_t launch_attn_decode(const AttnParams& p, hipStream_t stream);
+
+// bf16 prefill path: matrix-core tiles, K/V tiles in LDS shared by the G heads.
+// Returns hipErrorInvalidValue when the shape needs more LDS than a CU has.
+hipError_t launch_attn_prefill(const AttnParams& p, hipStream_t stream);
+size_t prefill_lds_bytes(int D, int max_seq);
+
+}  // namespace abgqa

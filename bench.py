@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Benchmark of the static-cache additive-bias GQA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--secondary | --no-secondary] [--eager] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch of seeded synthetic
+input: TensorScatter of K and V (skipped by the KV-shared variant), the bias
+build, and the attention. The default workload is the sliding-window decode
+layer (B8 Hq16 Hkv8 D256, max_seq 4096, window 1024, S_q 1).
+
+Timing. Inputs are resident in HBM before the timed region. R copies of every
+input rotate through the steps so that no step finds its KV cache in the 256 MB
+Infinity Cache left warm by the previous one. The steps of one rotation are
+captured once into a HIP graph (torch.cuda.CUDAGraph over the library's
+launches on the capture stream) and the graph is replayed; the replayed output
+is compared bit for bit with the eager result before anything is timed. A
+second graph holds only the attention launches of one rotation: its replay time
+per launch is the dominant kernel's average duration (HIP events on the stream
+the kernels run on). --eager times launch by launch instead (used under
+rocprofv3 counter runs).
+
+Output: one JSON line. value = algorithmic bytes of a step / step time (GB/s).
+roofline = the attention kernel's algorithmic bytes (decode) or flops
+(prefill) per launch / its average duration, against the MI355X peak (HBM 8 TB/s;
+bf16 dense matrix cores 2.5 PFLOP/s). cpu_baseline = the fp64 oracle timed on the
+host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+CACHE_BYTES = 256 << 20  # Infinity Cache
+
+WORKLOADS = ["decode_sliding", "decode_full", "decode_full_kvshared", "prefill_vision",
+             "prefill_long"]
+DECODE = {"decode_sliding", "decode_full", "decode_full_kvshared"}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def make_workload(name):
+    from additive_bias_gqa_amd import workloads as wl
+    return {
+        "decode_sliding": wl.decode_sliding,
+        "decode_full": wl.decode_full,
+        "decode_full_kvshared": lambda: wl.decode_full(kv_shared=True),
+        "prefill_vision": wl.prefill_vision,
+        "prefill_long": wl.prefill_long,
+    }[name]()
+
+
+class InputSet:
+    """One resident copy of every input and output of a step."""
+
+    def __init__(self, w, step, torch):
+        d = "cuda"
+        self.k = w.k_cache.to(d)
+        self.v = w.v_cache.to(d)
+        self.q = step.q.to(d)
+        self.k_new = None if step.k_new is None else step.k_new.to(d)
+        self.v_new = None if step.v_new is None else step.v_new.to(d)
+        self.wi = None if step.write_indices is None else step.write_indices.to(d)
+        self.nonpad = step.nonpad.to(d)
+        self.q_start = step.q_start.to(d)
+        self.kind = None if step.slot_kind is None else step.slot_kind.to(d)
+        self.bias = torch.empty((w.B, 1, step.S_q, w.max_seq), dtype=w.dtype, device=d)
+        self.out = torch.empty_like(self.q)
+
+
+def run_scatter_bias(ab, w, step, s):
+    if s.k_new is not None:
+        ab.kv_tensor_scatter(s.k, s.k_new, s.wi)
+        ab.kv_tensor_scatter(s.v, s.v_new, s.wi)
+    ab.build_static_cache_bias(s.nonpad, s.q_start, s.kind, step.S_q, w.max_seq, w.window,
+                               dtype=w.dtype, out=s.bias)
+
+
+def run_attention(ab, w, s, ws):
+    ab.attn_bias_gqa_fwd(s.q, s.k, s.v, s.bias, s.nonpad, w.scale, out=s.out, workspace=ws)
+
+
+def work_counts(w, step, s, torch):
+    """Algorithmic work of one step, counted from the bias the step builds:
+    live keys (allowed for some query row, below nonpad) and allowed pairs."""
+    T = w.max_seq
+    allowed = (s.bias[:, 0] == 0)                                  # [B, S_q, T]
+    valid = torch.arange(T, device="cuda")[None, None, :] < s.nonpad[:, None, None]
+    allowed &= valid
+    pairs = int(allowed.sum().item())
+    live_keys = int(allowed.any(dim=1).sum().item())              # sum over b of live slots
+    nonpad_sum = int(s.nonpad.clamp(0, T).sum().item())
+    e = 2 if w.dtype == torch.bfloat16 else 4
+    B, Hq, Hkv, D, S_q = w.B, w.Hq, w.Hkv, w.D, step.S_q
+    kv = live_keys * Hkv * D * 2 * e                               # K and V rows read once
+    bias_read = S_q * nonpad_sum * e                               # bias rows below nonpad
+    qo = 2 * B * Hq * S_q * D * e                                  # Q read + out written
+    attn_bytes = kv + bias_read + qo
+    attn_flops = 4.0 * D * Hq * pairs                              # QK^T and PV, 2 flop/MAC
+    S_new = 0 if step.k_new is None else step.k_new.shape[2]
+    scatter_bytes = 2 * 2 * B * Hkv * S_new * D * e                # K and V: read + write
+    kind_bytes = 0 if step.slot_kind is None else B * T * 4
+    bias_bytes = B * S_q * T * e + kind_bytes                      # written once, kinds read
+    return dict(pairs=pairs, live_keys=live_keys, attn_bytes=attn_bytes, attn_flops=attn_flops,
+                step_bytes=attn_bytes + scatter_bytes + bias_bytes,
+                scatter_bytes=scatter_bytes, bias_bytes=bias_bytes)
+
+
+def time_graph(torch, g, reps):
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(reps):
+        g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)  # ms
+
+
+def bench_workload(name, steps, warmup, eager, torch, ab):
+    w = make_workload(name)
+    step = w.steps[0]
+    log(f"{name}: {w.describe()}")
+    probe = InputSet(w, step, torch)
+    per_set = sum(t.numel() * t.element_size() for t in
+                  (probe.k, probe.v, probe.q, probe.bias, probe.out))
+    n_sets = max(2, min(8, math.ceil(3 * CACHE_BYTES / per_set)))
+    sets = [probe] + [InputSet(w, step, torch) for _ in range(n_sets - 1)]
+    need = ab.attn_bias_gqa_workspace_bytes(w.B, w.Hq, w.Hkv, step.S_q, w.max_seq, w.D)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda") if need else None
+    log(f"{name}: {n_sets} rotating input sets of {per_set / 2**20:.0f} MiB, workspace {need} B")
+
+    # eager warm-up and reference outputs
+    for i in range(max(warmup, n_sets)):
+        s = sets[i % n_sets]
+        run_scatter_bias(ab, w, step, s)
+        run_attention(ab, w, s, ws)
+    torch.cuda.synchronize()
+    ref_out = [s.out.clone() for s in sets]
+    counts = work_counts(w, step, sets[0], torch)
+    for s in sets:
+        assert torch.isfinite(s.out.float()).all(), "non-finite output"
+
+    K = max(steps, n_sets)
+    if eager:
+        st = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for i in range(K):
+            s = sets[i % n_sets]
+            run_scatter_bias(ab, w, step, s)
+            ev[i][0].record(st)
+            run_attention(ab, w, s, ws)
+            ev[i][1].record(st)
+        e1.record(st)
+        torch.cuda.synchronize()
+        step_ms = e0.elapsed_time(e1) / K
+        attn_ms = sum(a.elapsed_time(b) for a, b in ev) / K
+        mode = "eager"
+    else:
+        g_step, g_attn = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g_step):
+                for s in sets:
+                    run_scatter_bias(ab, w, step, s)
+                    run_attention(ab, w, s, ws)
+            with torch.cuda.graph(g_attn):
+                for s in sets:
+                    run_attention(ab, w, s, ws)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        # the graphs must reproduce the eager outputs bit for bit, replay after replay
+        for check in range(2):
+            for s in sets:
+                s.out.zero_()
+            torch.cuda.synchronize()
+            (g_step if check == 0 else g_attn).replay()
+            torch.cuda.synchronize()
+            for s, r in zip(sets, ref_out):
+                assert torch.equal(s.out.view(torch.int16 if w.dtype == torch.bfloat16
+                                              else torch.int32),
+                                   r.view(torch.int16 if w.dtype == torch.bfloat16
+                                          else torch.int32)), "graph replay differs from eager"
+        reps = max(1, K // n_sets)
+        time_graph(torch, g_step, 1)
+        step_ms = time_graph(torch, g_step, reps) / (reps * n_sets)
+        attn_ms = time_graph(torch, g_attn, reps) / (reps * n_sets)
+        K = reps * n_sets
+        mode = "graph"
+
+    res = dict(workload=name, mode=mode, steps=K, ms_per_step=step_ms, attn_ms=attn_ms,
+               counts=counts, desc=w.describe(), n_sets=n_sets)
+    if name in DECODE:
+        res["attn_rate"] = counts["attn_bytes"] / (attn_ms * 1e-3) / 1e9       # GB/s
+        res["roofline"] = dict(bound="hbm", achieved=round(res["attn_rate"], 1),
+                               peak=HBM_PEAK_GBS, unit="GB/s",
+                               frac=round(res["attn_rate"] / HBM_PEAK_GBS, 4))
+    else:
+        res["attn_rate"] = counts["attn_flops"] / (attn_ms * 1e-3) / 1e12      # TFLOP/s
+        res["roofline"] = dict(bound="mfma", achieved=round(res["attn_rate"], 1),
+                               peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                               frac=round(res["attn_rate"] / BF16_PEAK_TFLOPS, 4))
+    res["step_gbs"] = counts["step_bytes"] / (step_ms * 1e-3) / 1e9
+    log(f"{name}: {mode} step {step_ms * 1e3:.1f} us, attention {attn_ms * 1e3:.1f} us, "
+        f"{res['roofline']['achieved']} {res['roofline']['unit']} "
+        f"({100 * res['roofline']['frac']:.1f}% of peak)")
+    del sets, probe, ws
+    torch.cuda.empty_cache()
+    return res, w
+
+
+def traffic_for(name):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source; else None."""
+    path = os.path.join(HERE, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for rel in rec.get("sources", []):
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, counts, budget_s=20.0):
+    """The oracle (scatter + bias + attention, fp64, OpenMP) on whole batch
+    entries of the workload until ~budget_s of work; rate in the metric's unit."""
+    import numpy as np
+    import oracle
+    step = w.steps[0]
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    oracle.build(force=False)
+    t0 = time.perf_counter()
+    done = 0
+    for b in range(w.B):
+        sl = slice(b, b + 1)
+        k, v = w.k_cache[sl], w.v_cache[sl]
+        if step.k_new is not None:
+            k = oracle.scatter(k, step.k_new[sl], step.write_indices[sl])
+            v = oracle.scatter(v, step.v_new[sl], step.write_indices[sl])
+        kind = None if step.slot_kind is None else step.slot_kind[sl]
+        bias = oracle.bias(step.nonpad[sl], step.q_start[sl], kind, step.S_q, w.max_seq, w.window)
+        oracle.attention(step.q[sl], k, v, bias, step.nonpad[sl], w.scale)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    frac = done / w.B
+    rate = counts["step_bytes"] * frac / dt / 1e9
+    return dict(value=round(rate, 4), unit="GB/s", cores=cores, kind="oracle",
+                sample=f"{done} of {w.B} batch entries of one step (scatter + bias + attention), "
+                       f"{dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_sliding", choices=WORKLOADS)
+    ap.add_argument("--secondary", dest="secondary", action="store_true", default=True)
+    ap.add_argument("--no-secondary", dest="secondary", action="store_false")
+    ap.add_argument("--eager", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported: the "
+              f"hot path is measured on one GPU's share (see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import additive_bias_gqa_amd as ab
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ab.load()
+    log(f"device {torch.cuda.get_device_name(0)}, library {ab.library_path()}")
+
+    t_start = time.perf_counter()
+    main_res, w = bench_workload(args.workload, args.steps, args.warmup, args.eager, torch, ab)
+    secondary = {}
+    if args.secondary:
+        for name in WORKLOADS:
+            if name == args.workload:
+                continue
+            r, _ = bench_workload(name, max(8, args.steps // 10), 2, args.eager, torch, ab)
+            secondary[name] = dict(
+                attn_us=round(r["attn_ms"] * 1e3, 2), step_us=round(r["ms_per_step"] * 1e3, 2),
+                roofline=r["roofline"], step_gbs=round(r["step_gbs"], 1),
+                config=r["desc"])
+
+    rl = dict(main_res["roofline"])
+    rl["traffic"] = traffic_for(args.workload)
+    counts = main_res["counts"]
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(w, counts)
+    cfg = dict(main_res["desc"])
+    cfg.update({"kernel_timing": main_res["mode"], "rotating_input_sets": main_res["n_sets"],
+                "attn_us": round(main_res["attn_ms"] * 1e3, 2),
+                "attn_bytes": counts["attn_bytes"], "step_bytes": counts["step_bytes"],
+                "live_keys": counts["live_keys"]})
+    line = {
+        "metric": "decode KV GB/s (% of HBM peak) + prefill attention TFLOP/s (% of MFMA peak)",
+        "value": round(main_res["step_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": main_res["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded PCG64; N(0,1) bf16 values, random bits beyond nonpad)",
+        "config": cfg,
+        "roofline": rl,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+        "wall_s": round(time.perf_counter() - t_start, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

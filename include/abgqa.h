@@ -1,0 +1,175 @@
+/*
+ * abgqa.h - C ABI of libabgqa.so: additive-bias grouped-query attention over an
+ * external static KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The computation is the opset-24 ONNX Attention op used as an external static
+ * cache (onnxruntime skill "cuda-attention-kernel-patterns", section 11
+ * "TensorScatter decode"; mobius skill "attention-optimization", section
+ * "In-place KV for ONNX Attention via TensorScatter (static cache)"):
+ *
+ *   kv_tensor_scatter(K), kv_tensor_scatter(V)     write the new token(s)
+ *   build_static_cache_bias(...)                   (B,1,S_q,max_seq) float bias
+ *   attn_bias_gqa_fwd(Q, K, V, bias, nonpad, ...)  softmax(scale*QK^T + bias) V
+ *
+ * mobius issue #366, "Emit bias-aware external-KV (TensorScatter +
+ * nonpad_kv_seqlen) attention for float-bias decoders", states the problem
+ * these three calls solve.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major (last index fastest), in caller-owned device
+ *     memory, and 16-byte aligned. The library keeps no pointer after a call
+ *     returns and allocates no device memory.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and runs asynchronously to the host. Return codes report host-side
+ *     validation and launch errors only.
+ *   - On any status other than ABGQA_OK nothing was enqueued, and
+ *     abgqa_last_error() returns a stable one-line message (per thread).
+ *   - Device-side index values (write_indices, nonpad_kv_seqlen, q_start) cannot
+ *     be checked without a synchronisation; the kernels clamp nonpad into
+ *     [0, max_seq] and drop writes outside the cache.
+ *   - Layout names: B batch, Hq query heads, Hkv KV heads (G = Hq / Hkv query
+ *     heads share one KV head), S_q query tokens, max_seq cache slots, D head
+ *     size. D must be one of 64, 128, 256, 512.
+ */
+#ifndef ABGQA_H
+#define ABGQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ABGQA_F32 = 0,  /* IEEE binary32 */
+  ABGQA_BF16 = 1  /* bfloat16 (8-bit exponent, 7-bit mantissa) */
+} abgqa_dtype;
+
+typedef enum {
+  ABGQA_OK = 0,
+  ABGQA_ERR_INVALID = 1,     /* null pointer, bad size, misaligned pointer */
+  ABGQA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+  ABGQA_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+  ABGQA_ERR_HIP = 4          /* the HIP runtime reported an error */
+} abgqa_status;
+
+/*
+ * kv_tensor_scatter - in-place TensorScatter of new tokens into a static cache.
+ *
+ * Passage: mobius skill "attention-optimization", section "In-place KV for ONNX
+ * Attention via TensorScatter (static cache)": the new token(s) are written into
+ * the pre-allocated buffer at write_indices, with no growing concatenation.
+ * The scatter runs along the max_seq axis of this layout.
+ *
+ *   cache          [B, Hkv, max_seq, D] of `dtype`, updated in place
+ *   update         [B, Hkv, S_new, D]   of `dtype`
+ *   write_indices  [B] int64 on the device: update token t of batch row b goes
+ *                  to slot write_indices[b] + t. NULL means all zero. A slot
+ *                  outside [0, max_seq) is dropped (linear mode, no wrap).
+ *   S_new == 0     is a no-op (a KV-shared layer has nothing to append,
+ *                  onnxruntime PR #28242, kv_sequence_length = 0).
+ * Every other slot keeps its bits. The copy is bit-exact.
+ * Errors: ABGQA_ERR_INVALID for null cache/update (S_new > 0), non-positive
+ * B/Hkv/max_seq/D, negative S_new, misalignment; ABGQA_ERR_UNSUPPORTED for
+ * another dtype or a D that is not a multiple of 8.
+ */
+abgqa_status kv_tensor_scatter(void *cache, const void *update,
+                               const int64_t *write_indices, int64_t B,
+                               int64_t Hkv, int64_t max_seq, int64_t S_new,
+                               int64_t D, abgqa_dtype dtype, void *stream);
+
+/*
+ * build_static_cache_bias - the (B,1,S_q,max_seq) additive bias of a static
+ * cache, keyed on absolute query position.
+ *
+ * Passage: mobius issue #366, "Mobius-side deliverable" (second bullet): a bias
+ * keyed on absolute query positions with KV validity slot < nonpad_kv_seqlen,
+ * reusing the causal / sliding / block-overlay / padding logic. Window rule:
+ * mobius skill "attention-optimization", "GQA sliding window via
+ * local_window_size" (query q sees keys [q-W+1, q]). Default query offset:
+ * onnxruntime skill "cuda-attention-kernel-patterns", section 11 (bottom-right
+ * offset nonpad - S_q, clamped at 0).
+ *
+ *   bias             [B, 1, S_q, max_seq] of `bias_dtype`, fully written:
+ *                    +0.0 where allowed, -inf where masked
+ *   nonpad_kv_seqlen [B] int64 on the device (count of valid slots)
+ *   q_start          [B] int64 on the device: query row s sits at absolute slot
+ *                    q = q_start[b] + s. NULL means max(nonpad[b] - S_q, 0).
+ *   slot_kind        [B, max_seq] int32 on the device: < 0 padding token, 0 text,
+ *                    k > 0 a token of image block k. NULL means all text.
+ *   window           W > 0: sliding window of W keys; W <= 0: none
+ * allowed(b,s,j) = j < nonpad[b] && kind[j] >= 0
+ *                  && ((j <= q && q - j < W) || (kind[q] > 0 && kind[j] == kind[q]))
+ * (the window term is dropped when W <= 0; kind[q] is 0 when q is outside the
+ * cache). Positions are signed 64-bit throughout.
+ * Errors: ABGQA_ERR_INVALID for a null bias or nonpad, non-positive sizes,
+ * misalignment; ABGQA_ERR_UNSUPPORTED for a bias dtype other than f32/bf16.
+ */
+abgqa_status build_static_cache_bias(void *bias, abgqa_dtype bias_dtype,
+                                     const int64_t *nonpad_kv_seqlen,
+                                     const int64_t *q_start,
+                                     const int32_t *slot_kind, int64_t B,
+                                     int64_t S_q, int64_t max_seq,
+                                     int64_t window, void *stream);
+
+/*
+ * attn_bias_gqa_fwd - attention of S_q query tokens over the external cache.
+ *
+ * Passages: onnxruntime skill "cuda-attention-kernel-patterns", section 4
+ * (scale*QK^T, then + bias, then softmax, then times V; no softcap here),
+ * section 6 (a query row with no allowed key, or a batch row with nonpad = 0,
+ * outputs zeros, decided by selection so masked V never leaks), section 11
+ * (external cache: keys are the cache slots < nonpad_kv_seqlen); mobius issue
+ * #366 (bias present with is_causal = 0: the bias carries the causal rule);
+ * onnxruntime PR #28242, CPU GQA excerpt (query head h reads KV head h / G).
+ *
+ *   out              [B, Hq, S_q, D] of `dtype` (must not alias an input)
+ *   q                [B, Hq, S_q, D] of `dtype`
+ *   k_cache, v_cache [B, Hkv, max_seq, D] of `dtype`
+ *   bias             [B, 1, S_q, max_seq] of `bias_dtype`, broadcast over heads;
+ *                    -inf masks a key. NULL selects the in-kernel-rules variant:
+ *                    the mask of build_static_cache_bias is evaluated inside the
+ *                    attention kernel from nonpad, q_start, slot_kind and window,
+ *                    with the same result as passing that bias.
+ *   nonpad_kv_seqlen [B] int64 on the device
+ *   q_start, slot_kind, window: read only when bias == NULL (see above)
+ *   scale            multiplies q.k before the bias is added (1/sqrt(D) usually)
+ *   dtype            ABGQA_BF16 (fp32 accumulation, softmax weights rounded to
+ *                    bf16 for the matrix-core PV product in prefill) or
+ *                    ABGQA_F32 (fp32 throughout)
+ *   workspace        device scratch of at least attn_bias_gqa_workspace_bytes()
+ *                    bytes for the same shape, zero-filled by the caller once
+ *                    before its first use; every call leaves its first 4*B*Hkv
+ *                    bytes (arrival counters) at zero again. Calls that share a
+ *                    workspace must not overlap in time.
+ * Slots >= nonpad may hold any bits (NaN/Inf included); they never reach the
+ * arithmetic. K/V at slots < nonpad are expected to be finite: a key masked by
+ * the bias gets the exact weight 0, and 0 times a finite V is 0.
+ * Errors: ABGQA_ERR_INVALID (null pointers, sizes, Hq % Hkv != 0, S_q > max_seq,
+ * misalignment), ABGQA_ERR_UNSUPPORTED (D not in {64,128,256,512}, dtype pair
+ * not supported), ABGQA_ERR_WORKSPACE, ABGQA_ERR_HIP.
+ */
+abgqa_status attn_bias_gqa_fwd(void *out, const void *q, const void *k_cache,
+                               const void *v_cache, const void *bias,
+                               abgqa_dtype bias_dtype,
+                               const int64_t *nonpad_kv_seqlen,
+                               const int64_t *q_start, const int32_t *slot_kind,
+                               int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q,
+                               int64_t max_seq, int64_t D, float scale,
+                               int64_t window, abgqa_dtype dtype,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Bytes of workspace attn_bias_gqa_fwd needs for this shape (0 if none). */
+size_t attn_bias_gqa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv,
+                                     int64_t S_q, int64_t max_seq, int64_t D);
+
+/* Message of the last failed call on this thread ("" if none). The pointer stays
+ * valid until the next call into the library from the same thread. */
+const char *abgqa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ABGQA_H */

@@ -181,22 +181,24 @@ def attention(q, k_cache, v_cache, bias_, nonpad, scale: float, rows=None) -> np
     one batch entry at a time, so the repeated KV heads of one entry are the most
     that is materialised. Returns float64 [B,Hq,S_q,D] or [len(rows), D].
     """
-    qn, kn, vn, bn = _np(q), _np(k_cache), _np(v_cache), _np(bias_)
     npd = _i64(nonpad)
-    B, Hq, S_q, D = qn.shape
-    Hkv = kn.shape[1]
+    B, Hq, S_q, D = q.shape
+    Hkv = k_cache.shape[1]
     if Hq % Hkv != 0:
         raise ValueError("Hq must be a multiple of Hkv")
     G = Hq // Hkv
     if rows is None:
-        return attention_mha(qn, repeat_kv(kn, G), repeat_kv(vn, G), bn, npd, scale)
+        return attention_mha(_np(q), repeat_kv(_np(k_cache), G), repeat_kv(_np(v_cache), G),
+                             _np(bias_), npd, scale)
     rows = _i64(rows)
     out = np.empty((rows.shape[0], D), dtype=np.float64)
     per_batch = Hq * S_q
     for b in np.unique(rows // per_batch):
+        b = int(b)
         sel = np.nonzero(rows // per_batch == b)[0]
         local = rows[sel] - b * per_batch
-        out[sel] = attention_mha(qn[b:b + 1], repeat_kv(kn[b:b + 1], G),
-                                 repeat_kv(vn[b:b + 1], G), bn[b:b + 1],
+        # slice before widening: one batch entry in fp64 at a time
+        out[sel] = attention_mha(_np(q[b:b + 1]), repeat_kv(_np(k_cache[b:b + 1]), G),
+                                 repeat_kv(_np(v_cache[b:b + 1]), G), _np(bias_[b:b + 1]),
                                  npd[b:b + 1], scale, rows=local)
     return out

@@ -1,0 +1,100 @@
+"""One pass of the hot path on the GPU (through the C-ABI binding) and the same
+pass on the fp64 oracle, plus the parity comparison. The two sides share only
+the seeded host inputs."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import additive_bias_gqa_amd as ab
+import oracle
+from additive_bias_gqa_amd import workloads as wl
+
+NEG_INF = float("-inf")
+# tolerances of the method's statement: fp32 max-abs 1e-5; bf16 inputs with
+# fp32 accumulation max-abs 2e-2 and mean-rel 1e-2 (sum|d| / sum|ref|)
+TOL = {torch.float32: dict(max_abs=1e-5, mean_rel=None),
+       torch.bfloat16: dict(max_abs=2e-2, mean_rel=1e-2)}
+
+
+def announce(msg: str):
+    print(f"[case] {msg}", flush=True)
+
+
+def dev(t):
+    return None if t is None else t.to("cuda")
+
+
+def gpu_step(w: wl.Workload, step: wl.Step, k_dev, v_dev, rules: bool = False,
+             bias_dtype: torch.dtype | None = None, default_q_start: bool = False):
+    """Scatter K/V (unless KV-shared), build the bias (unless rules), attention.
+    Returns (bias or None, out) on the device."""
+    if step.k_new is not None:
+        wi = dev(step.write_indices)
+        ab.kv_tensor_scatter(k_dev, dev(step.k_new), wi)
+        ab.kv_tensor_scatter(v_dev, dev(step.v_new), wi)
+    nonpad = dev(step.nonpad)
+    q_start = None if default_q_start else dev(step.q_start)
+    kind = dev(step.slot_kind)
+    bias = None
+    if not rules:
+        bias = ab.build_static_cache_bias(nonpad, q_start, kind, step.S_q, w.max_seq, w.window,
+                                          dtype=bias_dtype or w.dtype)
+    out = ab.attn_bias_gqa_fwd(dev(step.q), k_dev, v_dev, bias, nonpad, w.scale,
+                               q_start=q_start, slot_kind=kind, window=w.window)
+    return bias, out
+
+
+def oracle_step(w: wl.Workload, step: wl.Step, k_host, v_host, rows=None,
+                default_q_start: bool = False):
+    """The same pass on the oracle. Returns (k_cache, v_cache, bias, out)."""
+    if step.k_new is not None:
+        k_host = oracle.scatter(k_host, step.k_new, step.write_indices)
+        v_host = oracle.scatter(v_host, step.v_new, step.write_indices)
+    qs = None if default_q_start else step.q_start
+    bias = oracle.bias(step.nonpad, qs, step.slot_kind, step.S_q, w.max_seq, w.window)
+    out = oracle.attention(step.q, k_host, v_host, bias, step.nonpad, w.scale, rows=rows)
+    return k_host, v_host, bias, out
+
+
+def dead_rows(bias: np.ndarray, nonpad, Hq: int) -> np.ndarray:
+    """[B, Hq, S_q] True where a query row has no allowed key below nonpad."""
+    B, _, S_q, T = bias.shape
+    npd = np.asarray(nonpad, dtype=np.int64).reshape(B, 1, 1)
+    live = ((bias[:, 0] == 0.0) & (np.arange(T)[None, None, :] < npd)).any(axis=-1)
+    return np.repeat(~live[:, None, :], Hq, axis=1)
+
+
+def check_parity(got: np.ndarray, ref: np.ndarray, dtype: torch.dtype, dead=None, what=""):
+    """Element-wise parity at the stated tolerance; dead rows must be exact zeros."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    tol = TOL[dtype]
+    max_abs = float(err.max()) if err.size else 0.0
+    mean_rel = float(err.sum() / max(np.abs(ref).sum(), 1e-300))
+    print(f"[parity] {what}: max_abs={max_abs:.3e} mean_rel={mean_rel:.3e} n={err.size}", flush=True)
+    assert max_abs <= tol["max_abs"], f"{what}: max_abs {max_abs:.3e} > {tol['max_abs']}"
+    if tol["mean_rel"] is not None:
+        assert mean_rel <= tol["mean_rel"], f"{what}: mean_rel {mean_rel:.3e} > {tol['mean_rel']}"
+    if dead is not None and dead.any():
+        assert np.all(got[dead] == 0.0), f"{what}: fully-masked rows are not exactly zero"
+    return max_abs, mean_rel
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def sample_rows(w: wl.Workload, step: wl.Step, n: int, seed: int) -> np.ndarray:
+    """Flat (b*Hq + h)*S_q + s row indices: the first and last rows of every
+    batch entry plus n random ones, sorted and unique."""
+    B, Hq, S_q = w.B, w.Hq, step.S_q
+    rng = np.random.Generator(np.random.PCG64(seed))
+    picks = set(rng.integers(0, B * Hq * S_q, size=n).tolist())
+    for b in range(B):
+        picks.add(b * Hq * S_q)
+        picks.add((b + 1) * Hq * S_q - 1)
+    return np.array(sorted(picks), dtype=np.int64)

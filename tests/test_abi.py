@@ -1,0 +1,88 @@
+"""The C-ABI library, host side only (no GPU): it loads, exports every entry
+point include/abgqa.h declares, and rejects bad arguments with a stable status
+and message before anything reaches the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import additive_bias_gqa_amd as ab
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "abgqa.h")
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "sizeof"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ab.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"kv_tensor_scatter", "build_static_cache_bias", "attn_bias_gqa_fwd",
+                          "attn_bias_gqa_workspace_bytes", "abgqa_last_error"}
+    out = subprocess.run(["nm", "-D", "--defined-only", ab.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def _fwd(lib, **kw):
+    a = dict(out=None, q=None, k=None, v=None, bias=None, bdt=1, nonpad=None, qs=None, kind=None,
+             B=1, Hq=4, Hkv=2, S_q=1, T=64, D=64, scale=0.125, window=0, dtype=1, ws=None,
+             wsb=0, stream=None)
+    a.update(kw)
+    return lib.attn_bias_gqa_fwd(a["out"], a["q"], a["k"], a["v"], a["bias"], a["bdt"],
+                                 a["nonpad"], a["qs"], a["kind"], a["B"], a["Hq"], a["Hkv"],
+                                 a["S_q"], a["T"], a["D"], a["scale"], a["window"], a["dtype"],
+                                 a["ws"], a["wsb"], a["stream"])
+
+
+FAKE = 1 << 20  # a 256-byte aligned address that is never dereferenced
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(B=0), INVALID, "must be positive"),
+    (dict(Hq=6, Hkv=4), INVALID, "multiple of Hkv"),
+    (dict(S_q=65), INVALID, "must not exceed max_seq"),
+    (dict(D=96), UNSUPPORTED, "D must be"),
+    (dict(dtype=7), UNSUPPORTED, "dtype"),
+    (dict(out=FAKE, q=FAKE + 4096, k=FAKE + 8192, v=FAKE + 12288), INVALID, "null"),
+    (dict(out=FAKE + 8, q=FAKE + 4096, k=FAKE + 8192, v=FAKE + 12288, nonpad=FAKE), INVALID,
+     "misaligned"),
+    (dict(out=FAKE, q=FAKE, k=FAKE + 8192, v=FAKE + 12288, nonpad=FAKE + 16384), INVALID, "alias"),
+    (dict(out=FAKE, q=FAKE + 4096, k=FAKE + 8192, v=FAKE + 12288, nonpad=FAKE + 16384), WORKSPACE,
+     "workspace"),
+])
+def test_attn_validation(lib, kw, status, msg):
+    assert _fwd(lib, **kw) == status
+    assert msg in ab.abgqa_last_error()
+
+
+def test_scatter_and_bias_validation(lib):
+    assert lib.kv_tensor_scatter(None, None, None, 1, 1, 8, 0, 64, 1, None) == OK  # S_new = 0
+    assert lib.kv_tensor_scatter(None, None, None, 1, 1, 8, 2, 64, 1, None) == INVALID
+    assert lib.kv_tensor_scatter(FAKE, FAKE, None, 1, 1, 8, 2, 12, 1, None) == UNSUPPORTED
+    assert "multiple of 16 bytes" in ab.abgqa_last_error()
+    assert lib.kv_tensor_scatter(FAKE, FAKE, None, 1, 1, 8, -1, 64, 1, None) == INVALID
+    assert lib.build_static_cache_bias(None, 1, FAKE, None, None, 1, 1, 8, 0, None) == INVALID
+    assert lib.build_static_cache_bias(FAKE, 5, FAKE, None, None, 1, 1, 8, 0, None) == UNSUPPORTED
+    assert lib.build_static_cache_bias(FAKE + 2, 1, FAKE, None, None, 1, 1, 8, 0, None) == INVALID
+    assert "misaligned" in ab.abgqa_last_error()
+
+
+def test_workspace_size(lib):
+    assert lib.attn_bias_gqa_workspace_bytes(8, 16, 8, 1, 4096, 256) > 0
+    assert lib.attn_bias_gqa_workspace_bytes(2, 16, 8, 512, 4096, 256) == 0   # prefill
+    assert lib.attn_bias_gqa_workspace_bytes(1, 6, 4, 1, 64, 64) == 0         # invalid heads

@@ -1,0 +1,320 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+TensorScatter and the bias are compared bit for bit; attention within fp32
+max-abs 1e-5, or bf16 max-abs 2e-2 and mean-rel 1e-2, with fully-masked rows
+required to be exact zeros. Small shapes compare every output element (several
+tiles, ragged tails); the five full-size workloads compare sampled rows.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import additive_bias_gqa_amd as ab
+import oracle
+from additive_bias_gqa_amd import workloads as wl
+from pipeline import (announce, check_parity, dead_rows, dev, gpu_step, oracle_step,
+                      sample_rows, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (run them with -m gpu on an MI355X)")
+    ab.load()
+    torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------- #
+# TensorScatter: bit-exact
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("D", [64, 256, 512])
+def test_scatter_bit_exact(dtype, D):
+    announce(f"scatter dtype={dtype} D={D}")
+    rng = wl.rng_for(200 + D)
+    B, H, T, S_new = 4, 3, 37, 9
+    cache = wl.garbage(rng, (B, H, T, D), dtype)
+    upd = wl.garbage(rng, (B, H, S_new, D), dtype)
+    w = torch.tensor([0, 5, T - S_new, T - 3], dtype=torch.int64)  # last runs off the end
+    ref = oracle.scatter(cache, upd, w)
+    c = dev(cache)
+    ab.kv_tensor_scatter(c, dev(upd), dev(w))
+    ibits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(c.cpu().view(ibits), ref.view(ibits))
+
+
+def test_scatter_null_indices_and_noop():
+    announce("scatter null indices / S_new=0")
+    rng = wl.rng_for(210)
+    cache = wl.garbage(rng, (2, 2, 16, 256), torch.bfloat16)
+    upd = wl.garbage(rng, (2, 2, 3, 256), torch.bfloat16)
+    c = dev(cache)
+    ab.kv_tensor_scatter(c, dev(upd), None)
+    ref = oracle.scatter(cache, upd, None)
+    assert torch.equal(c.cpu().view(torch.int16), ref.view(torch.int16))
+    empty = torch.empty((2, 2, 0, 256), dtype=torch.bfloat16)
+    ab.kv_tensor_scatter(c, dev(empty), None)
+    assert torch.equal(c.cpu().view(torch.int16), ref.view(torch.int16))
+
+
+# --------------------------------------------------------------------------- #
+# bias builder: bit-exact
+# --------------------------------------------------------------------------- #
+def _rand_kinds(rng, B, T):
+    kind = np.zeros((B, T), dtype=np.int32)
+    for b in range(B):
+        kind[b, rng.random(T) < 0.1] = wl.PAD
+        for blk in (1, 2):
+            lo = int(rng.integers(0, T))
+            kind[b, lo:lo + int(rng.integers(1, max(2, T // 4)))] = blk
+    return torch.from_numpy(kind)
+
+
+@pytest.mark.parametrize("bias_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("T,S_q,W", [(64, 16, 8), (1001, 33, 100), (4096, 1, 1024),
+                                     (777, 200, 0), (40, 40, 1000)])
+def test_bias_bit_exact(bias_dtype, T, S_q, W):
+    announce(f"bias dtype={bias_dtype} T={T} S_q={S_q} W={W}")
+    rng = wl.rng_for(300 + T + S_q)
+    B = 3
+    nonpad = torch.from_numpy(rng.integers(0, T, size=B, endpoint=True).astype(np.int64))
+    kind = _rand_kinds(rng, B, T)
+    q_start = torch.from_numpy(rng.integers(-5, T, size=B).astype(np.int64))
+    for qs in (q_start, None):
+        for kd in (kind, None):
+            ref = oracle.bias(nonpad, qs, kd, S_q, T, W)
+            got = ab.build_static_cache_bias(dev(nonpad), dev(qs), dev(kd), S_q, T, W,
+                                             dtype=bias_dtype)
+            g = got.cpu().to(torch.float32)
+            r = torch.from_numpy(ref).to(torch.float32)
+            assert torch.equal(g.view(torch.int32), r.view(torch.int32)), (qs is None, kd is None)
+
+
+# --------------------------------------------------------------------------- #
+# attention: small shapes, every element
+# --------------------------------------------------------------------------- #
+SMALL = {
+    "decode_sliding": lambda: wl.decode_sliding(B=3, Hq=4, Hkv=2, D=256, max_seq=1001,
+                                                window=100, nonpad_lo=50),
+    "decode_full": lambda: wl.decode_full(B=3, Hq=8, Hkv=2, D=512, max_seq=777, nonpad_lo=1),
+    "decode_full_kvshared": lambda: wl.decode_full(B=3, Hq=8, Hkv=2, D=512, max_seq=777,
+                                                   nonpad_lo=1, kv_shared=True),
+    "decode_d64_g8": lambda: wl.decode_sliding(B=2, Hq=16, Hkv=2, D=64, max_seq=300,
+                                               window=0, nonpad_lo=1),
+    "decode_d128_g1": lambda: wl.decode_full(B=2, Hq=4, Hkv=4, D=128, max_seq=512, nonpad_lo=1),
+    "decode_g3": lambda: wl.decode_full(B=2, Hq=6, Hkv=2, D=256, max_seq=200, nonpad_lo=1),
+    "prefill_vision": lambda: wl.prefill_vision(B=2, Hq=4, Hkv=2, D=256, S_q=100, max_seq=512,
+                                                window=64, start_hi=300, block=40),
+    "prefill_long": lambda: wl.prefill_long(B=2, Hq=8, Hkv=2, D=512, S_q=200, max_seq=300,
+                                            pad_hi=30, block=50),
+    "prefill_d64_g8": lambda: wl.prefill_vision(B=1, Hq=8, Hkv=1, D=64, S_q=70, max_seq=200,
+                                                window=30, start_hi=100, block=20),
+    "prefill_d128_g3": lambda: wl.prefill_long(B=2, Hq=6, Hkv=2, D=128, S_q=90, max_seq=130,
+                                               pad_hi=20, block=30),
+}
+
+
+@pytest.mark.parametrize("variant", ["bias", "rules"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_attention_small(name, variant):
+    w = SMALL[name]()
+    step = w.steps[0]
+    announce(f"attention small {name} variant={variant} {w.describe()}")
+    _, _, bias_ref, ref = oracle_step(w, step, w.k_cache, w.v_cache)
+    _, out = gpu_step(w, step, dev(w.k_cache), dev(w.v_cache), rules=(variant == "rules"))
+    check_parity(to_f64(out), ref, w.dtype, dead_rows(bias_ref, step.nonpad, w.Hq),
+                 f"{name}/{variant}")
+
+
+def test_attention_rules_equal_bias_bitwise():
+    for name in ("decode_sliding", "decode_full", "prefill_vision", "prefill_long"):
+        w = SMALL[name]()
+        step = w.steps[0]
+        announce(f"rules == bias {name}")
+        _, o_bias = gpu_step(w, step, dev(w.k_cache), dev(w.v_cache), rules=False)
+        _, o_rules = gpu_step(w, step, dev(w.k_cache), dev(w.v_cache), rules=True)
+        assert torch.equal(o_bias.view(torch.int16), o_rules.view(torch.int16)), name
+
+
+def test_attention_fp32_bias_dtype():
+    w = SMALL["prefill_vision"]()
+    step = w.steps[0]
+    announce("prefill with an fp32 bias tensor")
+    _, _, bias_ref, ref = oracle_step(w, step, w.k_cache, w.v_cache)
+    _, out = gpu_step(w, step, dev(w.k_cache), dev(w.v_cache), bias_dtype=torch.float32)
+    check_parity(to_f64(out), ref, w.dtype, dead_rows(bias_ref, step.nonpad, w.Hq), "fp32-bias")
+
+
+def test_tiny_fp32_prefill_then_decode():
+    """Prefill S_q=16 at slots 0..15, then decode at 16 (nonpad 17), fp32."""
+    w = wl.tiny_fp32()
+    k_d, v_d = dev(w.k_cache), dev(w.v_cache)
+    k_h, v_h = w.k_cache, w.v_cache
+    for i, step in enumerate(w.steps):
+        for variant in ("bias", "rules"):
+            announce(f"tiny fp32 step {i} {variant}")
+            k_run, v_run = k_d.clone(), v_d.clone()
+            _, out = gpu_step(w, step, k_run, v_run, rules=(variant == "rules"))
+            k_ref, v_ref, bias_ref, ref = oracle_step(w, step, k_h, v_h)
+            assert torch.equal(k_run.cpu(), k_ref) and torch.equal(v_run.cpu(), v_ref)
+            check_parity(to_f64(out), ref, torch.float32,
+                         dead_rows(bias_ref, step.nonpad, w.Hq), f"tiny/{i}/{variant}")
+        k_d, v_d, k_h, v_h = k_run, v_run, k_ref, v_ref
+
+
+# --------------------------------------------------------------------------- #
+# edge cases
+# --------------------------------------------------------------------------- #
+def test_empty_batch_and_negative_offset():
+    """nonpad = 0 for one batch row (zero output), nonpad < S_q for another."""
+    w = wl.prefill_vision(B=3, Hq=4, Hkv=2, D=256, S_q=64, max_seq=256, window=32,
+                          start_hi=100, block=16)
+    step = w.steps[0]
+    # slots below the new nonpad all hold finite data (earlier context or the chunk)
+    step.nonpad = torch.tensor([0, 20, int(step.nonpad[2])], dtype=torch.int64)
+    for dq in (True, False):
+        announce(f"empty batch / nonpad < S_q default_q_start={dq}")
+        _, _, bias_ref, ref = oracle_step(w, step, w.k_cache, w.v_cache, default_q_start=dq)
+        for rules in (False, True):
+            _, out = gpu_step(w, step, dev(w.k_cache), dev(w.v_cache), rules=rules,
+                              default_q_start=dq)
+            got = to_f64(out)
+            assert np.all(got[0] == 0.0)
+            check_parity(got, ref, w.dtype, dead_rows(bias_ref, step.nonpad, w.Hq),
+                         f"edge/dq={dq}/rules={rules}")
+
+
+def test_decode_empty_and_single_key():
+    # every slot valid (nonpad drawn = max_seq), then nonpad overridden
+    w = wl.decode_full(B=4, Hq=8, Hkv=2, D=512, max_seq=256, nonpad_lo=256, kv_shared=True)
+    step = w.steps[0]
+    step.nonpad = torch.tensor([0, 1, 2, 256], dtype=torch.int64)
+    step.q_start = (step.nonpad - 1).clamp(min=0)
+    announce("decode nonpad in {0,1,2,max}")
+    _, _, bias_ref, ref = oracle_step(w, step, w.k_cache, w.v_cache)
+    _, out = gpu_step(w, step, dev(w.k_cache), dev(w.v_cache))
+    got = to_f64(out)
+    assert np.all(got[0] == 0.0)
+    check_parity(got, ref, w.dtype, dead_rows(bias_ref, step.nonpad, w.Hq), "decode-edge")
+
+
+@pytest.mark.parametrize("S_q", [1, 3, 40])
+def test_random_finite_bias(S_q):
+    """A caller-supplied float bias with arbitrary finite values and -inf holes."""
+    rng = wl.rng_for(400 + S_q)
+    B, Hq, Hkv, T, D = 2, 8, 2, 333, 256
+    q = wl.normal(rng, (B, Hq, S_q, D), torch.bfloat16)
+    k = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    v = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    nonpad = torch.tensor([T, 200], dtype=torch.int64)
+    k[1, :, 200:] = wl.garbage(rng, (Hkv, T - 200, D), torch.bfloat16)
+    v[1, :, 200:] = wl.garbage(rng, (Hkv, T - 200, D), torch.bfloat16)
+    bias = (3.0 * wl.normal(rng, (B, 1, S_q, T), torch.float32)).to(torch.bfloat16)
+    bias[torch.from_numpy(rng.random((B, 1, S_q, T)) < 0.5)] = float("-inf")
+    bias[0, 0, 0, :] = float("-inf")          # one fully-masked row
+    announce(f"random finite bias S_q={S_q}")
+    ref = oracle.attention(q, k, v, bias, nonpad, 1 / math.sqrt(D))
+    out = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 1 / math.sqrt(D))
+    bias64 = bias.to(torch.float64).numpy()
+    check_parity(to_f64(out), ref, torch.bfloat16, dead_rows(bias64, nonpad, Hq), f"randbias/{S_q}")
+
+
+@pytest.mark.parametrize("name", ["decode_sliding", "prefill_long"])
+def test_poison_at_masked_slots(name):
+    """Huge finite K/V at slots below nonpad that the bias masks for every row
+    (pads, out-of-window) change nothing: their weight is exactly 0."""
+    w = SMALL[name]()
+    step = w.steps[0]
+    announce(f"poison masked slots {name}")
+    k_h, v_h, bias_ref, _ = oracle_step(w, step, w.k_cache, w.v_cache)
+    step2 = wl.Step(step.q, None, None, None, step.nonpad, step.q_start, step.slot_kind)
+    _, base = gpu_step(w, step2, dev(k_h), dev(v_h))
+    masked_all = (bias_ref[:, 0] == float("-inf")).all(axis=1)      # [B, T]
+    k2, v2 = k_h.clone(), v_h.clone()
+    for b in range(w.B):
+        idx = torch.from_numpy(np.nonzero(masked_all[b])[0])
+        idx = idx[idx < int(step.nonpad[b])]
+        k2[b][:, idx] = 1.0e30
+        v2[b][:, idx] = -1.0e30
+    _, out = gpu_step(w, step2, dev(k2), dev(v2))
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+
+
+def test_determinism():
+    for name in ("decode_full", "prefill_vision"):
+        w = SMALL[name]()
+        step = w.steps[0]
+        announce(f"determinism {name}")
+        _, a = gpu_step(w, step, dev(w.k_cache), dev(w.v_cache))
+        _, b = gpu_step(w, step, dev(w.k_cache), dev(w.v_cache))
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_invalid_arguments_raise():
+    q = torch.zeros((1, 3, 1, 256), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 2, 64, 256), dtype=torch.bfloat16, device="cuda")
+    n = torch.tensor([10], dtype=torch.int64, device="cuda")
+    with pytest.raises(RuntimeError, match="multiple of Hkv"):
+        ab.attn_bias_gqa_fwd(q, k, k, None, n, 0.1)
+    q = torch.zeros((1, 4, 1, 96), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 2, 64, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(RuntimeError, match="D must be"):
+        ab.attn_bias_gqa_fwd(q, k, k, None, n, 0.1)
+
+
+# --------------------------------------------------------------------------- #
+# the five full-size workloads, sampled rows
+# --------------------------------------------------------------------------- #
+FULL = {
+    "decode_sliding": (lambda: wl.decode_sliding(), None),
+    "decode_full": (lambda: wl.decode_full(), 48),
+    "decode_full_kvshared": (lambda: wl.decode_full(kv_shared=True), 48),
+    "prefill_vision": (lambda: wl.prefill_vision(), 160),
+    "prefill_long": (lambda: wl.prefill_long(), 96),
+}
+
+
+_full_cache = {}
+
+
+def _full_reference(name):
+    """Inputs, sampled rows and oracle results of one full-size workload (shared
+    by the bias and rules variants)."""
+    if name not in _full_cache:
+        _full_cache.clear()
+        make, n_rows = FULL[name]
+        w = make()
+        step = w.steps[0]
+        rows = None if n_rows is None else sample_rows(w, step, n_rows, seed=500)
+        announce(f"oracle for {name} rows={'all' if rows is None else len(rows)}")
+        k_h, v_h, bias_ref, ref = oracle_step(w, step, w.k_cache, w.v_cache, rows=rows)
+        _full_cache[name] = (w, rows, k_h, v_h, bias_ref, ref)
+    return _full_cache[name]
+
+
+@pytest.mark.parametrize("variant", ["bias", "rules"])
+@pytest.mark.parametrize("name", list(FULL))
+def test_attention_full_size(name, variant):
+    w, rows, k_h, v_h, bias_ref, ref = _full_reference(name)
+    step = w.steps[0]
+    announce(f"attention full {name} variant={variant} {w.describe()}")
+    k_d, v_d = dev(w.k_cache), dev(w.v_cache)
+    bias, out = gpu_step(w, step, k_d, v_d, rules=(variant == "rules"))
+    torch.cuda.synchronize()
+    if step.k_new is not None:   # the scatter landed bit-exactly
+        assert torch.equal(k_d.cpu().view(torch.int16), k_h.view(torch.int16))
+        assert torch.equal(v_d.cpu().view(torch.int16), v_h.view(torch.int16))
+    if bias is not None:         # and so did the bias
+        g = bias.cpu().to(torch.float32).view(torch.int32)
+        assert torch.equal(g, torch.from_numpy(bias_ref).to(torch.float32).view(torch.int32))
+    del k_d, v_d, bias
+    got = to_f64(out).reshape(-1, w.D)
+    dead = dead_rows(bias_ref, step.nonpad, w.Hq).reshape(-1)
+    exp = ref.reshape(-1, w.D)
+    if rows is not None:
+        got, dead = got[rows], dead[rows]
+    check_parity(got, exp, w.dtype, np.repeat(dead[:, None], w.D, axis=1), f"full/{name}/{variant}")
