@@ -12,6 +12,7 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local std::string g_launch_detail;
 
 abgqa_status fail(abgqa_status st, const char* fmt, ...) {
   char buf[512];
@@ -24,7 +25,10 @@ abgqa_status fail(abgqa_status st, const char* fmt, ...) {
 }
 
 abgqa_status hip_fail(const char* what, hipError_t e) {
-  return fail(ABGQA_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+  const std::string detail = g_launch_detail.empty() ? std::string() : " in " + g_launch_detail;
+  g_launch_detail.clear();
+  return fail(ABGQA_ERR_HIP, "%s: HIP error %d (%s)%s", what, (int)e, hipGetErrorString(e),
+              detail.c_str());
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -42,6 +46,8 @@ constexpr int64_t kMaxSeq = (int64_t)1 << 24;  // slot indices stay exact in int
 bool head_dim_ok(int64_t D) { return D == 64 || D == 128 || D == 256 || D == 512; }
 
 }  // namespace
+
+void abgqa::set_launch_detail(const char* what) { g_launch_detail = what; }
 
 extern "C" {
 

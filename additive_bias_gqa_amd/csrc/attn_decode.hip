@@ -27,7 +27,8 @@
 //             S layout (lane = key, 4 rows per lane), then O += P V on the
 //             vector ALU with V rows read coalesced (lane = 8 values of d).
 //             The softmax weights cross layouts through a small LDS buffer.
-//   merge     the 4 wavefronts merge in LDS; each workgroup writes its
+//   merge     the 4 wavefronts merge in LDS in a fixed order (bit-
+//             reproducible); each workgroup writes its
 //             (m, l, O) partial; the last workgroup of a (b, kv head) to arrive
 //             (device-scope counter) combines the partials:
 //             m = max m_i, y = sum 2^(m_i - m) O_i / sum 2^(m_i - m) l_i.
@@ -368,15 +369,20 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(AttnParams p) 
     for (int ww = 0; ww < kDecWaves; ++ww) mm = fmaxf(mm, s_m[ww][r]);
     m_wg[r] = mm;
   }
-  if (lane < LPR) {
+  // fixed order (wave 0, 1, 2, 3) so that the result is bit-reproducible
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const float f = (m_wg[r] == -INFINITY) ? 0.f : fast_exp2(s_m[w][r] - m_wg[r]);
+  for (int ww = 0; ww < kDecWaves; ++ww) {
+    if (w == ww && lane < LPR) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) atomicAdd(&s_o[r * D + vd + c], o[r][c] * f);
+      for (int r = 0; r < NR; ++r) {
+        const float f = (m_wg[r] == -INFINITY) ? 0.f : fast_exp2(s_m[w][r] - m_wg[r]);
+        float* dst = &s_o[r * D + vd];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) dst[c] = fmaf(o[r][c], f, dst[c]);
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- 5. write this workgroup's partial ------------------------------------
   float* part = p.ws_part + ((int64_t)bh * p.n_split + split) * PART;

@@ -431,16 +431,23 @@ static hipError_t launch_prefill_inst(const AttnParams& p, hipStream_t stream) {
   const int n_qt = (p.S_q + MQ - 1) / MQ;
   const size_t lds = prefill_lds_bytes(D, p.T);
   auto kern = attn_prefill_kernel<D, NW, kRules, BiasT>;
-  static bool attr_set = false;  // per instantiation
-  if (!attr_set) {
+  // Opt in to the dynamic LDS this launch needs (static LDS of the kernel comes
+  // on top, so the request is the exact size, not the CU's 160 KiB).
+  static size_t lds_set = 0;  // per instantiation
+  if (lds > lds_set) {
     const hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) {
+      set_launch_detail("hipFuncSetAttribute(MaxDynamicSharedMemorySize)");
+      return e;
+    }
+    lds_set = lds;
   }
   const dim3 grid((unsigned)((int64_t)n_qt * p.B * p.Hkv));
   hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, stream, p, n_qt);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) set_launch_detail("prefill kernel launch");
+  return e;
 }
 
 template <int D, int NW>

@@ -8,6 +8,10 @@
 
 namespace abgqa {
 
+// Names the HIP call that failed inside a launcher (per thread; read and
+// cleared by the C ABI when it reports ABGQA_ERR_HIP).
+void set_launch_detail(const char* what);
+
 hipError_t launch_scatter(void* cache, const void* update, const int64_t* write_indices,
                           int64_t B, int64_t H, int64_t max_seq, int64_t S_new,
                           int64_t row_bytes, hipStream_t stream);

@@ -61,7 +61,7 @@ def dead_rows(bias: np.ndarray, nonpad, Hq: int) -> np.ndarray:
     """[B, Hq, S_q] True where a query row has no allowed key below nonpad."""
     B, _, S_q, T = bias.shape
     npd = np.asarray(nonpad, dtype=np.int64).reshape(B, 1, 1)
-    live = ((bias[:, 0] == 0.0) & (np.arange(T)[None, None, :] < npd)).any(axis=-1)
+    live = ((bias[:, 0] != NEG_INF) & (np.arange(T)[None, None, :] < npd)).any(axis=-1)
     return np.repeat(~live[:, None, :], Hq, axis=1)
 
 
