@@ -143,14 +143,14 @@ _workspaces: dict = {}
 
 
 def _workspace(device: torch.device, nbytes: int) -> torch.Tensor | None:
-    """A zero-initialised per-device workspace, grown on demand (the library
-    leaves its arrival counters at zero after every call)."""
+    """A per-device workspace, grown on demand (calls on one device's current
+    stream are ordered, so they can share it)."""
     if nbytes == 0:
         return None
     key = (device.type, device.index)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 

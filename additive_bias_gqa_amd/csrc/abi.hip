@@ -153,10 +153,9 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
     if (!workspace || workspace_bytes < need)
       return fail(ABGQA_ERR_WORKSPACE, "attn_bias_gqa_fwd: workspace of %zu bytes needed, %zu given",
                   need, workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(workspace, 256)) return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: workspace not 256-byte aligned");
+    if (!aligned(workspace, 16)) return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: workspace not 16-byte aligned");
     p.n_split = abgqa::decode_num_splits(B, Hkv, max_seq);
-    p.ws_ctr = (unsigned*)workspace;
-    p.ws_part = (float*)((char*)workspace + ((B * Hkv * 4 + 255) / 256) * 256);
+    p.ws_part = (float*)workspace;
     e = abgqa::launch_attn_decode(p, st);
   } else {
     path = "prefill";

@@ -28,14 +28,19 @@
 //             vector ALU with V rows read coalesced (lane = 8 values of d).
 //             The softmax weights cross layouts through a small LDS buffer.
 //   merge     the 4 wavefronts merge in LDS in a fixed order (bit-
-//             reproducible); each workgroup writes its
-//             (m, l, O) partial; the last workgroup of a (b, kv head) to arrive
-//             (device-scope counter) combines the partials:
+//             reproducible); each workgroup writes its (m, l, O) partial to
+//             the workspace; a second small kernel combines the partials of
+//             each (b, kv head, row):
 //             m = max m_i, y = sum 2^(m_i - m) O_i / sum 2^(m_i - m) l_i.
+//             (A last-arriving-workgroup combine inside the split kernel
+//             would need device-scope fences, which on this multi-XCD part
+//             write back and invalidate the L2 once per workgroup.)
 //
 // Softmax runs in base 2 on x * log2(e). The running maximum is only raised
 // when a new score exceeds it by more than 8 (a factor 256), so rescaling the
 // accumulators is rare; weights stay <= 2^8 and the result is unchanged.
+#include <stdlib.h>
+
 #include "common.h"
 #include "kernels.h"
 #include "mask_rules.h"
@@ -44,8 +49,6 @@ namespace abgqa {
 
 namespace {
 
-constexpr int kDecThreads = 256;
-constexpr int kDecWaves = 4;
 constexpr float kRescaleThreshold = 8.f;
 
 template <typename BiasT>
@@ -65,6 +68,13 @@ __device__ __forceinline__ float bias_value<uint32_t>(uint32_t v) { return __uin
 }  // namespace
 
 int decode_num_splits(int64_t B, int64_t Hkv, int64_t max_seq) {
+  // ABGQA_DECODE_SPLITS overrides the heuristic (tuning); the workspace size
+  // query reads the same value, so both agree
+  static const int forced = [] {
+    const char* v = getenv("ABGQA_DECODE_SPLITS");
+    return v ? atoi(v) : 0;
+  }();
+  if (forced > 0) return forced > 256 ? 256 : forced;
   // about 1024 workgroups in flight over the 256 CUs, at least ~64 keys each
   int64_t n = (1024 + B * Hkv - 1) / (B * Hkv);
   const int64_t by_len = (max_seq + 63) / 64;
@@ -85,33 +95,34 @@ __host__ __device__ constexpr int64_t part_floats(int64_t NR, int64_t D) {
   return (NR * D + 2 * NR + 3) & ~(int64_t)3;
 }
 
-// workspace: counters [B*Hkv] u32 (region rounded up to 256 B), then one
-// partial record per (b, kv head, split)
+// workspace: one partial record per (b, kv head, split)
 size_t decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_q, int64_t G, int64_t D,
                               int64_t max_seq) {
   const int64_t NR = round_up_rows(S_q * G);
   const int64_t n_split = decode_num_splits(B, Hkv, max_seq);
-  const size_t ctr = (size_t)((B * Hkv * 4 + 255) / 256) * 256;
-  const size_t part = (size_t)B * Hkv * n_split * part_floats(NR, D) * sizeof(float);
-  return ctr + part;
+  return (size_t)B * Hkv * n_split * part_floats(NR, D) * sizeof(float);
 }
 
-template <int D, int NR, bool kRules, typename BiasT>
-__global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(AttnParams p) {
+template <int D, int NR, int NW, bool kRules, typename BiasT>
+__global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
+  constexpr int kDecThreads = NW * 64;
+  constexpr int kDecWaves = NW;
   constexpr int KSTEPS = D / 32;    // matrix-core k-steps over the head dim
   constexpr int LPR = D / 8;        // lanes per V row (8 bf16 per lane)
   constexpr int KPI = 64 / LPR;     // V rows per wavefront load
   constexpr int NV = 16 / KPI;      // V loads per 16-key block
   constexpr int PART = (int)part_floats(NR, D);
+  constexpr int E = NR < 4 ? NR : 4;      // real rows per lane group (r = 4*grp + e)
+  constexpr bool kQinLds = D >= 256;      // keep the A operand out of VGPRs
 
   __shared__ float s_p[kDecWaves][16][NR];  // softmax weights, key-major
   __shared__ float s_alpha[kDecWaves][NR];
   __shared__ float s_m[kDecWaves][NR];
   __shared__ float s_l[kDecWaves][NR];
   __shared__ float s_o[NR * D];             // merged O of the workgroup
+  __shared__ __align__(16) __bf16 s_q[kQinLds ? NR * D : 8];  // Q rows (A operand)
   __shared__ int s_range[2];
   __shared__ int32_t s_kq[16];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -197,8 +208,17 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(AttnParams p) 
   // Q as the A operand: lane holds row (lane % 16), d-slots 32*i + 8*(lane/16)
   const int qrow = lane & 15;
   const int kgrp = lane >> 4;
-  bf16x8 qa[KSTEPS];
-  {
+  bf16x8 qa[kQinLds ? 1 : KSTEPS];
+  if constexpr (kQinLds) {
+    // the R real rows of Q, row r = s * G + g, into LDS
+    for (int c = tid; c < R * (D / 8); c += kDecThreads) {
+      const int r = c / (D / 8), dc = c % (D / 8);
+      const __bf16* qp = (const __bf16*)p.q +
+          (((b * p.Hq + hk * G + r % G) * p.S_q + r / G) * (int64_t)D) + 8 * dc;
+      *reinterpret_cast<bf16x8*>(&s_q[r * D + 8 * dc]) = ld_global<bf16x8>(qp);
+    }
+    __syncthreads();
+  } else {
     const bool ok = qrow < R;
     const int s = ok ? qrow / G : 0, g = ok ? qrow % G : 0;
     const __bf16* qp = (const __bf16*)p.q +
@@ -210,11 +230,11 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(AttnParams p) 
     }
   }
   // rows this lane holds in the S layout: r = 4 * kgrp + e
-  int row_s[4];
-  bool row_ok[4];
-  RowRule rules[4];
+  int row_s[E];
+  bool row_ok[E];
+  RowRule rules[E];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
+  for (int e = 0; e < E; ++e) {
     const int r = 4 * kgrp + e;
     row_ok[e] = r < R;
     row_s[e] = row_ok[e] ? r / G : 0;
@@ -227,9 +247,9 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(AttnParams p) 
   const BiasT* biasb = kRules ? nullptr : (const BiasT*)p.bias + b * p.S_q * (int64_t)T;
   const int32_t* kindb = p.slot_kind ? p.slot_kind + b * T : nullptr;
 
-  float m_run[4], l_run[4];
+  float m_run[E], l_run[E];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) { m_run[e] = -INFINITY; l_run[e] = 0.f; }
+  for (int e = 0; e < E; ++e) { m_run[e] = -INFINITY; l_run[e] = 0.f; }
   float o[NR][8];
 #pragma unroll
   for (int r = 0; r < NR; ++r)
@@ -255,19 +275,23 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(AttnParams p) 
       const int jv = j0 + it * KPI + vkey;
       vv[it] = (jv < my_hi) ? ld_global<bf16x8>(vbase + (int64_t)jv * D + vd) : bf16x8{};
     }
-    // bias / rules for the 4 rows of this lane at key jk
-    float badd[4];
-    bool keep[4];
+    // bias / rules for the rows of this lane at key jk
+    float badd[E];
+    bool keep[E];
     const int32_t kj = (kRules && kin && kindb) ? kindb[jk] : 0;
+    BiasT bv0 = 0;
+    if constexpr (!kRules) {
+      if (kin && p.S_q == 1) bv0 = biasb[jk];   // one query token: one bias row
+    }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < E; ++e) {
       badd[e] = 0.f;
       if constexpr (kRules) {
         keep[e] = row_ok[e] && kin && rules[e].allowed(jk, kj);
       } else {
         bool k_ = row_ok[e] && kin;
         if (k_) {
-          const BiasT bv = biasb[(int64_t)row_s[e] * T + jk];
+          const BiasT bv = (p.S_q == 1) ? bv0 : biasb[(int64_t)row_s[e] * T + jk];
           k_ = bias_live_bits<BiasT>(bv);
           badd[e] = bias_value<BiasT>(bv) * kLog2e;
         }
@@ -277,14 +301,21 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(AttnParams p) 
     // S = Q K^T on the matrix cores
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < KSTEPS; ++i) acc = mfma16x16x32(qa[i], kb[i], acc);
+    for (int i = 0; i < KSTEPS; ++i) {
+      bf16x8 a;
+      if constexpr (kQinLds)
+        a = (qrow < R) ? *reinterpret_cast<const bf16x8*>(&s_q[qrow * D + 32 * i + 8 * kgrp]) : bf16x8{};
+      else
+        a = qa[i];
+      acc = mfma16x16x32(a, kb[i], acc);
+    }
 
     // online softmax on the S layout: lane = key (lane % 16), rows 4*kgrp + e
-    float x[4];
+    float x[E];
     bool need_any = false;
-    float alpha[4];
+    float alpha[E];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < E; ++e) {
       x[e] = keep[e] ? fmaf(acc[e], scale_log2, badd[e]) : -INFINITY;
       const float mt = row16_max(x[e]);
       const float mn = fmaxf(m_run[e], mt);
@@ -295,7 +326,7 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(AttnParams p) 
     }
     if (__any(need_any)) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < E; ++e) {
         l_run[e] *= alpha[e];
         const int r = 4 * kgrp + e;
         if (qrow == 0 && r < NR) s_alpha[w][r] = alpha[e];
@@ -311,7 +342,7 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(AttnParams p) 
       }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < E; ++e) {
       const float pe = (x[e] == -INFINITY) ? 0.f : fast_exp2(x[e] - m_run[e]);
       l_run[e] += pe;
       const int r = 4 * kgrp + e;
@@ -344,7 +375,7 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(AttnParams p) 
 
   // ---- 4. merge the wavefronts of this workgroup ----------------------------
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
+  for (int e = 0; e < E; ++e) {
     const float lt = row16_sum(l_run[e]);
     const int r = 4 * kgrp + e;
     if (qrow == 0 && r < NR) { s_m[w][r] = m_run[e]; s_l[w][r] = lt; }
@@ -399,61 +430,90 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(AttnParams p) 
     part[NR * D + r] = m_wg[r];
     part[NR * D + NR + r] = lsum;
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = atomicAdd(&p.ws_ctr[bh], 1u);
-    s_last = (prev == (unsigned)(p.n_split - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
+}
 
-  // ---- 6. last workgroup of (b, kv head): combine the splits ----------------
-  __threadfence();
+// Merge the n_split partials of one (b, kv head, row):
+//   m = max m_i,  y = sum 2^(m_i - m) O_i / sum 2^(m_i - m) l_i
+// (a split that saw no live key has m_i = -inf and drops out; no live key at
+// all gives y = 0). One workgroup of 64 threads per (b, kv head, row), each
+// thread 8 consecutive values of d.
+template <int D, int NR>
+__global__ __launch_bounds__(64) void attn_decode_combine_kernel(AttnParams p) {
+  constexpr int PART = (int)part_floats(NR, D);
+  const int R = p.S_q * p.G;
+  const int r = blockIdx.x % R;
+  const int bh = blockIdx.x / R;
+  const int hk = bh % p.Hkv;
+  const int64_t b = bh / p.Hkv;
+  const int d0 = threadIdx.x * 8;
+  if (d0 >= D) return;
   const float* parts = p.ws_part + (int64_t)bh * p.n_split * PART;
-  for (int idx = tid; idx < R * (D / 8); idx += kDecThreads) {
-    const int r = idx / (D / 8);
-    const int d0 = (idx - r * (D / 8)) * 8;
-    float mm = -INFINITY;
-    for (int sp = 0; sp < p.n_split; ++sp) mm = fmaxf(mm, parts[sp * PART + NR * D + r]);
-    float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    if (mm != -INFINITY) {
-      for (int sp = 0; sp < p.n_split; ++sp) {
-        const float* ps = parts + sp * PART;
-        const float ms = ps[NR * D + r];
-        if (ms == -INFINITY) continue;  // an empty split
-        const float f = fast_exp2(ms - mm);
-        den = fmaf(ps[NR * D + NR + r], f, den);
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(ps + r * D + d0);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(ps + r * D + d0 + 4);
+  float mm = -INFINITY;
+  for (int sp = 0; sp < p.n_split; ++sp) mm = fmaxf(mm, parts[sp * PART + NR * D + r]);
+  float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (mm != -INFINITY) {
+    for (int sp = 0; sp < p.n_split; ++sp) {
+      const float* ps = parts + sp * PART;
+      const float ms = ps[NR * D + r];
+      if (ms == -INFINITY) continue;  // an empty split
+      const float f = fast_exp2(ms - mm);
+      den = fmaf(ps[NR * D + NR + r], f, den);
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(ps + r * D + d0);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(ps + r * D + d0 + 4);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) { num[c] = fmaf(a0[c], f, num[c]); num[4 + c] = fmaf(a1[c], f, num[4 + c]); }
+      for (int c = 0; c < 4; ++c) {
+        num[c] = fmaf(a0[c], f, num[c]);
+        num[4 + c] = fmaf(a1[c], f, num[4 + c]);
       }
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    const int s = r / G, g = r % G;
-    uint16_t* op = (uint16_t*)p.out + (((b * p.Hq + hk * G + g) * p.S_q + s) * (int64_t)D) + d0;
-    u32x4 pk;
-    pk.x = pack_bf16x2(num[0] * inv, num[1] * inv);
-    pk.y = pack_bf16x2(num[2] * inv, num[3] * inv);
-    pk.z = pack_bf16x2(num[4] * inv, num[5] * inv);
-    pk.w = pack_bf16x2(num[6] * inv, num[7] * inv);
-    *reinterpret_cast<u32x4*>(op) = pk;
   }
-  if (tid == 0) atomicExch(&p.ws_ctr[bh], 0u);  // leave the counter at zero for the next call
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const int s = r / p.G, g = r % p.G;
+  uint16_t* op = (uint16_t*)p.out + (((b * p.Hq + hk * p.G + g) * p.S_q + s) * (int64_t)D) + d0;
+  u32x4 pk;
+  pk.x = pack_bf16x2(num[0] * inv, num[1] * inv);
+  pk.y = pack_bf16x2(num[2] * inv, num[3] * inv);
+  pk.z = pack_bf16x2(num[4] * inv, num[5] * inv);
+  pk.w = pack_bf16x2(num[6] * inv, num[7] * inv);
+  *reinterpret_cast<u32x4*>(op) = pk;
+}
+
+static int decode_waves() {
+  static const int forced = [] {
+    const char* v = getenv("ABGQA_DECODE_WAVES");
+    return v ? atoi(v) : 0;
+  }();
+  return forced == 8 ? 8 : 4;
+}
+
+template <int D, int NR, int NW>
+static void launch_decode_nw(const AttnParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.n_split));
+  if (p.bias == nullptr)
+    hipLaunchKernelGGL((attn_decode_kernel<D, NR, NW, true, uint16_t>), grid, dim3(NW * 64), 0, stream, p);
+  else if (p.bias_is_bf16)
+    hipLaunchKernelGGL((attn_decode_kernel<D, NR, NW, false, uint16_t>), grid, dim3(NW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_decode_kernel<D, NR, NW, false, uint32_t>), grid, dim3(NW * 64), 0, stream, p);
 }
 
 template <int D, int NR>
 static hipError_t launch_decode_d(const AttnParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.n_split));
-  if (p.bias == nullptr)
-    hipLaunchKernelGGL((attn_decode_kernel<D, NR, true, uint16_t>), grid, dim3(kDecThreads), 0, stream, p);
-  else if (p.bias_is_bf16)
-    hipLaunchKernelGGL((attn_decode_kernel<D, NR, false, uint16_t>), grid, dim3(kDecThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_decode_kernel<D, NR, false, uint32_t>), grid, dim3(kDecThreads), 0, stream, p);
-  return hipGetLastError();
+  if (decode_waves() == 8) launch_decode_nw<D, NR, 8>(p, stream);
+  else launch_decode_nw<D, NR, 4>(p, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_launch_detail("decode kernel launch");
+    return e;
+  }
+  // the combine reads the partials after the split kernel completes (stream
+  // order), so no device-scope fence is needed inside the split kernel
+  const dim3 cgrid((unsigned)((int64_t)p.B * p.Hkv * p.S_q * p.G));
+  hipLaunchKernelGGL((attn_decode_combine_kernel<D, NR>), cgrid, dim3(64), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) set_launch_detail("decode combine launch");
+  return e;
 }
 
 template <int D>

@@ -35,15 +35,14 @@ struct AttnParams {
   float scale;               // multiplies q.k
   int bias_is_bf16;          // bias dtype when bias != null
   // split-KV decode
-  float* ws_part;            // partial results
-  unsigned* ws_ctr;          // [B * Hkv] arrival counters (zero between calls)
+  float* ws_part;            // partial results, one record per (b, kv head, split)
   int n_split;
 };
 
 // fp32 path (any S_q): one wavefront per query row.
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
 
-// bf16 decode path (S_q * G <= 16): split-KV with an in-kernel combine.
+// bf16 decode path (S_q * G <= 16): split-KV kernel, then a combine kernel.
 int decode_num_splits(int64_t B, int64_t Hkv, int64_t max_seq);
 size_t decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_q, int64_t G, int64_t D,
                               int64_t max_seq);

@@ -139,9 +139,9 @@ abgqa_status build_static_cache_bias(void *bias, abgqa_dtype bias_dtype,
  *                    bf16 for the matrix-core PV product in prefill) or
  *                    ABGQA_F32 (fp32 throughout)
  *   workspace        device scratch of at least attn_bias_gqa_workspace_bytes()
- *                    bytes for the same shape, zero-filled by the caller once
- *                    before its first use; every call leaves its first 4*B*Hkv
- *                    bytes (arrival counters) at zero again. Calls that share a
+ *                    bytes for the same shape, 16-byte aligned, no initial
+ *                    contents needed (the decode path keeps one partial
+ *                    softmax result per split there). Calls that share a
  *                    workspace must not overlap in time.
  * Slots >= nonpad may hold any bits (NaN/Inf included); they never reach the
  * arithmetic. K/V at slots < nonpad are expected to be finite: a key masked by
