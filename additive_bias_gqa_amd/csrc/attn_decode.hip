@@ -27,7 +27,7 @@
 //             S layout (lane = key, 4 rows per lane), then O += P V on the
 //             vector ALU with V rows read coalesced (lane = 8 values of d).
 //             The softmax weights cross layouts through a small LDS buffer.
-//   merge     the 4 wavefronts merge in LDS in a fixed order (bit-
+//   merge     the wavefronts merge in LDS in a fixed order (bit-
 //             reproducible); each workgroup writes its (m, l, O) partial to
 //             the workspace; a second small kernel combines the partials of
 //             each (b, kv head, row):
@@ -75,8 +75,10 @@ int decode_num_splits(int64_t B, int64_t Hkv, int64_t max_seq) {
     return v ? atoi(v) : 0;
   }();
   if (forced > 0) return forced > 256 ? 256 : forced;
-  // about 1024 workgroups in flight over the 256 CUs, at least ~64 keys each
-  int64_t n = (1024 + B * Hkv - 1) / (B * Hkv);
+  // about one workgroup per CU (256 CUs): fewer, longer-lived workgroups keep
+  // their loads streaming; fixed per-workgroup costs (range scan, merge,
+  // partial write) dominate when each gets only a few blocks
+  int64_t n = (256 + B * Hkv - 1) / (B * Hkv);
   const int64_t by_len = (max_seq + 63) / 64;
   if (n > by_len) n = by_len;
   if (n > 64) n = 64;
@@ -119,7 +121,11 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   __shared__ float s_alpha[kDecWaves][NR];
   __shared__ float s_m[kDecWaves][NR];
   __shared__ float s_l[kDecWaves][NR];
-  __shared__ float s_o[NR * D];             // merged O of the workgroup
+  // wave merge: each wave's rescaled O in its own slot, summed in a fixed order
+  // (one barrier), unless that needs more than 32 KiB: then accumulate wave by
+  // wave into one buffer
+  constexpr bool kParMerge = NW * NR * D <= 8192;
+  __shared__ float s_o[kParMerge ? NW * NR * D : NR * D];
   __shared__ __align__(16) __bf16 s_q[kQinLds ? NR * D : 8];  // Q rows (A operand)
   __shared__ int s_range[2];
   __shared__ int32_t s_kq[16];
@@ -138,7 +144,8 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
 
   // ---- 1. live range [lo, hi) of keys, over all S_q rows -------------------
   if (tid == 0) { s_range[0] = INT32_MAX; s_range[1] = -1; }
-  for (int i = tid; i < NR * D; i += kDecThreads) s_o[i] = 0.f;
+  if constexpr (!kParMerge)
+    for (int i = tid; i < NR * D; i += kDecThreads) s_o[i] = 0.f;
   __syncthreads();
   {
     int lo = INT32_MAX, hi = -1;
@@ -147,6 +154,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
       constexpr int EPV = 16 / sizeof(BiasT);  // elements per 16-byte load
       const int nvec = (np + EPV - 1) / EPV;
       const bool vec = (T % EPV) == 0;
+#pragma unroll 4
       for (int idx = tid; idx < p.S_q * nvec; idx += kDecThreads) {
         const int s = idx / nvec;
         const int j0 = (idx - s * nvec) * EPV;
@@ -259,43 +267,61 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   const int vkey = lane / LPR;       // key offset within a V load
   const int vd = 8 * (lane % LPR);   // first d of this lane in the PV layout
 
-  // ---- 3. stream 16-key blocks, wavefront w takes blocks w, w+4, ... --------
-  for (int j0 = my_lo + 16 * w; j0 < my_hi; j0 += 16 * kDecWaves) {
-    // K for the B operand: key j0 + (lane % 16), d-slots 32*i + 8*kgrp
-    const int jk = j0 + qrow;
-    const bool kin = jk < my_hi;
-    bf16x8 kb[KSTEPS];
+  // ---- 3. stream 16-key blocks, wavefront w takes blocks w, w+NW, ... -------
+  // Loads are unconditional: a key index past the range is clamped to the last
+  // key of the range (a valid, finite row), and its score is masked by `keep`
+  // below, so its weight is exactly 0. No exec-masked branches means the
+  // compiler can keep every load of a block in flight at once.
+  // For D <= 256 the next block's K/V are loaded while this one is computed.
+  constexpr bool kPrefetch = D <= 256;
+  struct Blk {
+    BiasT bias[E];
+    int32_t kj;
+    bf16x8 k[KSTEPS];
+    bf16x8 v[NV];
+  };
+  // Issue order matters: loads retire in order, so the small bias / kind loads
+  // go first (waiting for them does not wait for K and V), then K (needed by
+  // the matrix cores first), then V.
+  auto load_blk = [&](int j0, Blk& bl) {
+    const int jk = min(j0 + qrow, my_hi - 1);
+    bl.kj = 0;
+    if constexpr (!kRules) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) bl.bias[e] = biasb[(int64_t)row_s[e] * T + jk];
+    } else {
+      if (kindb) bl.kj = kindb[jk];
+    }
     const __bf16* kp = kbase + (int64_t)jk * D + 8 * kgrp;
 #pragma unroll
-    for (int i = 0; i < KSTEPS; ++i) kb[i] = kin ? ld_global<bf16x8>(kp + 32 * i) : bf16x8{};
-    // V rows for the PV step (zero beyond the range: never multiply garbage)
-    bf16x8 vv[NV];
+    for (int i = 0; i < KSTEPS; ++i) bl.k[i] = ld_global<bf16x8>(kp + 32 * i);
 #pragma unroll
     for (int it = 0; it < NV; ++it) {
-      const int jv = j0 + it * KPI + vkey;
-      vv[it] = (jv < my_hi) ? ld_global<bf16x8>(vbase + (int64_t)jv * D + vd) : bf16x8{};
+      const int jv = min(j0 + it * KPI + vkey, my_hi - 1);
+      bl.v[it] = ld_global<bf16x8>(vbase + (int64_t)jv * D + vd);
     }
+  };
+  const int stride = 16 * kDecWaves;
+  // one 16-key block: S = Q K^T, online softmax, O += P V
+  auto compute_blk = [&](const int j0, const Blk& cur) {
+    const int jk = j0 + qrow;
+    const bool kin = jk < my_hi;
+    const bf16x8* kb = cur.k;
+    const bf16x8* vv = cur.v;
     // bias / rules for the rows of this lane at key jk
     float badd[E];
     bool keep[E];
-    const int32_t kj = (kRules && kin && kindb) ? kindb[jk] : 0;
-    BiasT bv0 = 0;
-    if constexpr (!kRules) {
-      if (kin && p.S_q == 1) bv0 = biasb[jk];   // one query token: one bias row
-    }
+    const int32_t kj = cur.kj;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       badd[e] = 0.f;
       if constexpr (kRules) {
         keep[e] = row_ok[e] && kin && rules[e].allowed(jk, kj);
       } else {
-        bool k_ = row_ok[e] && kin;
-        if (k_) {
-          const BiasT bv = (p.S_q == 1) ? bv0 : biasb[(int64_t)row_s[e] * T + jk];
-          k_ = bias_live_bits<BiasT>(bv);
-          badd[e] = bias_value<BiasT>(bv) * kLog2e;
-        }
-        keep[e] = k_;
+        // branch-free, so the bias loads stay at the head of the block's loads
+        const BiasT bv = cur.bias[e];
+        keep[e] = row_ok[e] & kin & bias_live_bits<BiasT>(bv);
+        badd[e] = bias_value<BiasT>(bv) * kLog2e;   // only read where keep[e]
       }
     }
     // S = Q K^T on the matrix cores
@@ -371,6 +397,34 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
         for (int c = 0; c < 8; ++c) o[r][c] = fmaf(pw[r], vf[c], o[r][c]);
     }
     __builtin_amdgcn_wave_barrier();  // s_p is rewritten by the next block
+  };
+
+  if constexpr (kPrefetch) {
+    // two named buffers, alternating: the next block's loads are in flight
+    // while this one is computed, with no register copies between them
+    // The prefetch is unconditional: past the end of the range every key
+    // clamps to the last row of the range (one cached row), and a
+    // conditional load would make the wait counts at the join cover both
+    // paths, i.e. wait for the prefetch too.
+    Blk A, B;
+    int j0 = my_lo + 16 * w;
+    if (j0 < my_hi) load_blk(j0, A);
+    while (j0 < my_hi) {
+      const int j1 = j0 + stride;
+      load_blk(j1, B);
+      compute_blk(j0, A);
+      if (j1 >= my_hi) break;
+      const int j2 = j1 + stride;
+      load_blk(j2, A);
+      compute_blk(j1, B);
+      j0 = j2;
+    }
+  } else {
+    for (int j0 = my_lo + 16 * w; j0 < my_hi; j0 += stride) {
+      Blk A;
+      load_blk(j0, A);
+      compute_blk(j0, A);
+    }
   }
 
   // ---- 4. merge the wavefronts of this workgroup ----------------------------
@@ -400,25 +454,43 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
     for (int ww = 0; ww < kDecWaves; ++ww) mm = fmaxf(mm, s_m[ww][r]);
     m_wg[r] = mm;
   }
-  // fixed order (wave 0, 1, 2, 3) so that the result is bit-reproducible
-#pragma unroll
-  for (int ww = 0; ww < kDecWaves; ++ww) {
-    if (w == ww && lane < LPR) {
+  // ---- 5. sum the waves in a fixed order (bit-reproducible), write the partial
+  float* part = p.ws_part + ((int64_t)bh * p.n_split + split) * PART;
+  if constexpr (kParMerge) {
+    if (lane < LPR) {
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         const float f = (m_wg[r] == -INFINITY) ? 0.f : fast_exp2(s_m[w][r] - m_wg[r]);
-        float* dst = &s_o[r * D + vd];
+        float* dst = &s_o[(w * NR + r) * D + vd];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) dst[c] = fmaf(o[r][c], f, dst[c]);
+        for (int c = 0; c < 8; ++c) dst[c] = o[r][c] * f;
       }
     }
     __syncthreads();
+    for (int i = tid; i < NR * D / 4; i += kDecThreads) {
+      f32x4 acc = reinterpret_cast<const f32x4*>(s_o)[i];
+#pragma unroll
+      for (int ww = 1; ww < kDecWaves; ++ww)
+        acc += reinterpret_cast<const f32x4*>(s_o + ww * NR * D)[i];
+      reinterpret_cast<f32x4*>(part)[i] = acc;
+    }
+  } else {
+#pragma unroll
+    for (int ww = 0; ww < kDecWaves; ++ww) {
+      if (w == ww && lane < LPR) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const float f = (m_wg[r] == -INFINITY) ? 0.f : fast_exp2(s_m[w][r] - m_wg[r]);
+          float* dst = &s_o[r * D + vd];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) dst[c] = fmaf(o[r][c], f, dst[c]);
+        }
+      }
+      __syncthreads();
+    }
+    for (int i = tid; i < NR * D / 4; i += kDecThreads)
+      reinterpret_cast<f32x4*>(part)[i] = reinterpret_cast<const f32x4*>(s_o)[i];
   }
-
-  // ---- 5. write this workgroup's partial ------------------------------------
-  float* part = p.ws_part + ((int64_t)bh * p.n_split + split) * PART;
-  for (int i = tid; i < NR * D / 4; i += kDecThreads)
-    reinterpret_cast<f32x4*>(part)[i] = reinterpret_cast<const f32x4*>(s_o)[i];
   if (tid < NR) {
     const int r = tid;
     float lsum = 0.f;
@@ -448,25 +520,29 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(AttnParams p) {
   const int d0 = threadIdx.x * 8;
   if (d0 >= D) return;
   const float* parts = p.ws_part + (int64_t)bh * p.n_split * PART;
-  float mm = -INFINITY;
-  for (int sp = 0; sp < p.n_split; ++sp) mm = fmaxf(mm, parts[sp * PART + NR * D + r]);
+  // one pass, rescaled on the fly (running max), so every split's m, l and O
+  // loads are independent of each other and can all be in flight at once
+  float mm = -INFINITY, den = 0.f;
   float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  if (mm != -INFINITY) {
-    for (int sp = 0; sp < p.n_split; ++sp) {
-      const float* ps = parts + sp * PART;
-      const float ms = ps[NR * D + r];
-      if (ms == -INFINITY) continue;  // an empty split
-      const float f = fast_exp2(ms - mm);
-      den = fmaf(ps[NR * D + NR + r], f, den);
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(ps + r * D + d0);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(ps + r * D + d0 + 4);
+#pragma unroll 4
+  for (int sp = 0; sp < p.n_split; ++sp) {
+    const float* ps = parts + sp * PART;
+    const float ms = ps[NR * D + r];
+    const float ls = ps[NR * D + NR + r];
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(ps + r * D + d0);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(ps + r * D + d0 + 4);
+    // branch-free: a split that saw no live key (m = -inf, l = 0, O = 0) gets
+    // weight 0, and nothing done so far is rescaled by its -inf
+    const float mn = fmaxf(mm, ms);
+    const float fo = (mm == -INFINITY) ? 0.f : fast_exp2(mm - mn);
+    const float fs = (ms == -INFINITY) ? 0.f : fast_exp2(ms - mn);
+    den = den * fo + ls * fs;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        num[c] = fmaf(a0[c], f, num[c]);
-        num[4 + c] = fmaf(a1[c], f, num[4 + c]);
-      }
+    for (int c = 0; c < 4; ++c) {
+      num[c] = num[c] * fo + a0[c] * fs;
+      num[4 + c] = num[4 + c] * fo + a1[c] * fs;
     }
+    mm = mn;
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const int s = r / p.G, g = r % p.G;

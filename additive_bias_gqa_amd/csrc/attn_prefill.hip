@@ -10,25 +10,30 @@
 // "attention-optimization", "Flash Attention: when it actually helps").
 //
 // Layout of the work
-//   workgroup  one (b, kv head, query tile): 16*NW rows r = s_local * G + g,
-//              i.e. MQ = 16*NW / G consecutive query tokens times the G heads
-//              of the group. NW wavefronts own 16 rows each.
+//   workgroup  one (b, kv head, query tile): NW wavefronts of 32 rows each,
+//              r = s_local * G + g, i.e. MQ = 32*NW / G consecutive query
+//              tokens times the G heads of the group. Every K/V tile staged
+//              in LDS is read by all G heads' rows.
 //   tiles      32 keys. The workgroup first lists its live tiles: tiles below
 //              nonpad that hold an allowed entry for one of its rows (scanned
-//              from the bias, or derived from the rules). Skipping a tile is
-//              exact: every masked key contributes exactly zero.
-//   LDS        per tile, K as [32][D+8] and V transposed as [D][32+4] (bf16),
-//              double-buffered; each tile is read by all G heads' rows.
-//   S^T = K Q^T    16x16x32 bf16 MFMA: A = K rows from LDS, B = Q^T held in
+//              from the bias, or derived from the rules). Skipping is exact:
+//              a masked key contributes exactly zero.
+//   LDS        per tile, K and V row-major [32][D] bf16, 16-byte chunks XOR-
+//              swizzled by (row & 7) against bank conflicts; double-buffered.
+//   S^T = K Q^T    32x32x16 bf16 MFMA: A = K rows from LDS, B = Q^T held in
 //                  registers for the whole loop. Result lane l: query row
-//                  (l % 16), keys 4*(l/16) + e (+16 for the second half).
-//   softmax        on that layout: a row's 32 scores sit in 4 lanes x 8 values;
+//                  (l % 32), keys 8*i + 4*(l/32) + j (i, j < 4).
+//   softmax        a row's 32 scores sit in lanes l and l^32 (16 each); base 2;
 //                  weights rounded to bf16 (RNE), the row sum adds the rounded
-//                  weights. The running max moves only when exceeded by > 8.
-//   O^T += V^T P^T 16x16x32 MFMA: A = V^T read from the transposed LDS tile,
-//                  B = P^T straight from the softmax registers (its 8 k-slots
-//                  are the 8 keys the lane holds). O^T lane l: query row l%16,
-//                  d = 16*blk + 4*(l/16) + e.
+//                  weights; the running max moves only when exceeded by > 8.
+//   O^T += V^T P^T 32x32x16 MFMA per (32-d block, 16-key step): B = P^T is 8
+//                  consecutive score registers, A = V^T comes from two
+//                  transposing LDS reads (ds_read_b64_tr_b16) of the row-major
+//                  V tile. O^T lane l: query row l % 32, d = 32*blk + 8*i +
+//                  4*(l/32) + j.
+// The next tile's bias values (registers) and K/V (registers, then LDS) are
+// fetched while the current tile is computed; the bias loads are issued first
+// so that waiting for them never waits for the K/V loads behind them.
 #include "common.h"
 #include "kernels.h"
 #include "mask_rules.h"
@@ -37,18 +42,30 @@ namespace abgqa {
 
 namespace {
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kTileKeys = 32;
 constexpr float kRescaleThreshold = 8.f;
 
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// gfx950 transposing LDS read: within each group of 16 lanes, lane i receives
+// element (i % 4) of the 4-element (8-byte) row addressed by lane 4*k + i/4 of
+// the same group, for k = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const __bf16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// element offset of 16-byte chunk c of row r in a swizzled [rows][D] tile
 template <int D>
-struct PrefillLds {
-  static constexpr int KST = D + 8;                 // K row stride (bf16)
-  static constexpr int VST = kTileKeys + 4;         // V^T row stride (bf16)
-  static constexpr int K_ELEMS = kTileKeys * KST;
-  static constexpr int V_ELEMS = D * VST;
-  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr size_t BUF_BYTES = (size_t)BUF_ELEMS * 2;
-};
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * D + 8 * (c ^ (r & 7));
+}
 
 __host__ __device__ inline int num_tiles(int n) { return (n + kTileKeys - 1) / kTileKeys; }
 
@@ -59,56 +76,78 @@ __device__ __forceinline__ bool live_bits<uint16_t>(uint16_t v) { return v != 0x
 template <>
 __device__ __forceinline__ bool live_bits<uint32_t>(uint32_t v) { return v != 0xFF800000u; }
 
+template <typename BiasT>
+__device__ __forceinline__ float bias_f32(BiasT v);
+template <>
+__device__ __forceinline__ float bias_f32<uint16_t>(uint16_t v) { return bf16_bits_to_f32(v); }
+template <>
+__device__ __forceinline__ float bias_f32<uint32_t>(uint32_t v) { return __uint_as_float(v); }
+
+// 4 consecutive bias values of one row, packed (bf16: 2 words, fp32: 4 words)
+template <typename BiasT> struct Bias4;
+template <> struct Bias4<uint16_t> {
+  u32x2 w;
+  __device__ __forceinline__ uint16_t get(int e) const {
+    const uint32_t x = (e < 2) ? w.x : w.y;
+    return (e & 1) ? (uint16_t)(x >> 16) : (uint16_t)(x & 0xffff);
+  }
+};
+template <> struct Bias4<uint32_t> {
+  u32x4 w;
+  __device__ __forceinline__ uint32_t get(int e) const { return w[e]; }
+};
+
+// keys j..j+3 of a bias row; `vec` (uniform): rows are 4-aligned, so one
+// aligned load at min(j, T-4); else element loads clamped into the row.
+// Values for keys past the row end are never used (those keys are masked).
+__device__ __forceinline__ Bias4<uint16_t> load_bias4(const uint16_t* row, int j, int T, bool vec) {
+  Bias4<uint16_t> b;
+  if (vec) {
+    b.w = ld_global<u32x2>(row + min(j, T - 4));
+  } else {
+    const uint32_t e0 = row[min(j, T - 1)], e1 = row[min(j + 1, T - 1)];
+    const uint32_t e2 = row[min(j + 2, T - 1)], e3 = row[min(j + 3, T - 1)];
+    b.w = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+  }
+  return b;
+}
+__device__ __forceinline__ Bias4<uint32_t> load_bias4(const uint32_t* row, int j, int T, bool vec) {
+  Bias4<uint32_t> b;
+  if (vec) {
+    b.w = ld_global<u32x4>(row + min(j, T - 4));
+  } else {
+    b.w = u32x4{row[min(j, T - 1)], row[min(j + 1, T - 1)], row[min(j + 2, T - 1)],
+                row[min(j + 3, T - 1)]};
+  }
+  return b;
+}
+
 }  // namespace
 
 size_t prefill_lds_bytes(int D, int max_seq) {
   const int nt = num_tiles(max_seq);
   const size_t words = (size_t)((nt + 31) / 32) * 4;  // live bitmap
   const size_t list = (size_t)nt * 2;                 // live tile list (u16)
-  const size_t buf = (size_t)(kTileKeys * (D + 8) + D * (kTileKeys + 4)) * 2;
-  return 2 * buf + ((words + list + 15) & ~(size_t)15) + 64;
+  const size_t stage = (size_t)2 * kTileKeys * D * 2;  // K and V
+  return 2 * stage + ((words + list + 15) & ~(size_t)15);
 }
 
-template <int D, int NW, bool kRules, typename BiasT>
-__global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnParams p, int n_qt) {
-  using L = PrefillLds<D>;
-  constexpr int NT = NW * 64;
-  constexpr int KSTEPS = D / 32;
-  constexpr int DBLK = D / 16;
-  constexpr int KCH = kTileKeys * (D / 8);   // 16-byte K chunks per tile
-  constexpr int VUN = 8 * (D / 8);           // V units: 4 keys x 8 d
-  constexpr int KPT = (KCH + NT - 1) / NT;   // K chunks per thread
-  constexpr int VPT = (VUN + NT - 1) / NT;   // V units per thread
-
-  extern __shared__ __align__(16) unsigned char smem[];
-  __bf16* bufs = reinterpret_cast<__bf16*>(smem);
-  const int T = p.T, G = p.G;
-  const int n_kt_max = num_tiles(T);
-  uint32_t* s_bits = reinterpret_cast<uint32_t*>(smem + 2 * L::BUF_BYTES);
-  const int n_words = (n_kt_max + 31) / 32;
-  uint16_t* s_list = reinterpret_cast<uint16_t*>(s_bits + n_words);
-  __shared__ int s_nlive;
-  __shared__ int32_t s_ids[4];
-  __shared__ int s_nids;
-
+// The live 32-key tiles of one workgroup's query rows [s0, s_end): tiles below
+// nonpad that hold an allowed entry for one of the rows. Bias variant: scanned
+// from the bias rows. Rules variant: the causal/window range of the rows plus
+// every tile holding a slot of an image block that one of the rows belongs to
+// (up to 4 distinct blocks; more makes every tile live). Skipping a dead tile
+// is exact: its keys contribute exactly zero. Returns the count; the tile
+// indices are in s_list[0 .. count).
+template <int NT, bool kRules, typename BiasT>
+__device__ int build_live_list(const AttnParams& p, int64_t b, int np, int s0, int s_end, int n_kt,
+                               uint32_t* s_bits, uint16_t* s_list, int n_words, int32_t* s_ids,
+                               int* s_nids_p, int* s_nlive_p) {
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int lane = tid & 63;
-  const int col = lane & 15;   // query row within the wavefront
-  const int grp = lane >> 4;   // k-slot group
-
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = n_qt - 1 - (wg % n_qt);   // later (heavier) query tiles first
-  const int bh = wg / n_qt;
-  const int hk = bh % p.Hkv;
-  const int64_t b = bh / p.Hkv;
-  const int np = (int)clamp_nonpad(p.nonpad[b], T);
-  const int MQ = (16 * NW) / G;
-  const int s0 = qt * MQ;
-  const int s_end = min(s0 + MQ, p.S_q);
-  const int n_kt = num_tiles(np);
-
-  // ---- 1. live tiles ---------------------------------------------------------
+  const int w = tid >> 6, lane = tid & 63;
+  const int T = p.T;
+  int& s_nids = *s_nids_p;
+  int& s_nlive = *s_nlive_p;
   for (int i = tid; i < n_words; i += NT) s_bits[i] = 0u;
   if (tid == 0) { s_nids = 0; s_nlive = 0; }
   if (tid < 4) s_ids[tid] = -1;  // never a block id: a racing reader cannot match it
@@ -119,6 +158,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnParams p, int
     const bool vec = (T % EPV) == 0;
     const BiasT* bb = (const BiasT*)p.bias + (b * p.S_q) * (int64_t)T;
     const int total = (s_end - s0) * nvec;
+#pragma unroll 4
     for (int idx = tid; idx < total; idx += NT) {
       const int s = s0 + idx / nvec;
       const int j0 = (idx % nvec) * EPV;
@@ -194,9 +234,329 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnParams p, int
     if (lane == 0) s_nlive = base;
   }
   __syncthreads();
-  const int n_live = s_nlive;
+  return s_nlive;
+}
+
+
+template <int D, int NW, bool kRules, typename BiasT>
+__global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnParams p, int n_qt) {
+  constexpr int NT = NW * 64;
+  constexpr int KSTEPS = D / 16;              // k-steps of S^T over the head dim
+  constexpr int DBLK = D / 32;                // 32-wide d blocks of O^T
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int CH = kTileKeys * CPR;         // chunks per K (or V) tile
+  constexpr int CPT = (CH + NT - 1) / NT;     // chunks per thread per tensor
+  constexpr int TILE_ELEMS = kTileKeys * D;
+  constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  __bf16* stages = reinterpret_cast<__bf16*>(smem);
+  const int T = p.T, G = p.G;
+  const int n_kt_max = num_tiles(T);
+  uint32_t* s_bits = reinterpret_cast<uint32_t*>(smem + (size_t)2 * STAGE_ELEMS * 2);
+  const int n_words = (n_kt_max + 31) / 32;
+  uint16_t* s_list = reinterpret_cast<uint16_t*>(s_bits + n_words);
+  __shared__ int s_nlive;
+  __shared__ int32_t s_ids[4];
+  __shared__ int s_nids;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 31;   // query row within the wavefront
+  const int hh = lane >> 5;    // half of the wavefront
+
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = n_qt - 1 - (wg % n_qt);   // later (heavier) query tiles first
+  const int bh = wg / n_qt;
+  const int hk = bh % p.Hkv;
+  const int64_t b = bh / p.Hkv;
+  const int np = (int)clamp_nonpad(p.nonpad[b], T);
+  const int MQ = (32 * NW) / G;
+  const int s0 = qt * MQ;
+  const int s_end = min(s0 + MQ, p.S_q);
+  const int n_kt = num_tiles(np);
+
+  // ---- 1. live tiles ---------------------------------------------------------
+  const int n_live = build_live_list<NT, kRules, BiasT>(p, b, np, s0, s_end, n_kt, s_bits, s_list,
+                                                       n_words, s_ids, &s_nids, &s_nlive);
 
   // ---- 2. this lane's query row and its Q^T fragments ------------------------
+  const int r = 32 * w + col;
+  const int sl = r / G, g = r % G;
+  const int s = s0 + sl;
+  const bool row_ok = (r < MQ * G) && (s < p.S_q);
+  const int h = hk * G + g;
+  bf16x8 qf[KSTEPS];
+  {
+    const __bf16* qp = (const __bf16*)p.q + ((b * p.Hq + h) * p.S_q + (row_ok ? s : 0)) * (int64_t)D + 8 * hh;
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) qf[i] = row_ok ? ld_global<bf16x8>(qp + 16 * i) : bf16x8{};
+  }
+  RowRule rule{};
+  if constexpr (kRules) {
+    if (row_ok) rule = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s, p.S_q, T, p.window);
+  }
+  const BiasT* brow = kRules ? nullptr : (const BiasT*)p.bias + (b * p.S_q + (row_ok ? s : 0)) * (int64_t)T;
+  const int32_t* kindb = p.slot_kind ? p.slot_kind + b * T : nullptr;
+  const bool vec4 = (T % 4) == 0;   // bias / kind rows 4-aligned (uniform)
+  const float scale_log2 = p.scale * kLog2e;
+
+  const __bf16* kg = (const __bf16*)p.k + (b * p.Hkv + hk) * (int64_t)T * D;
+  const __bf16* vg = (const __bf16*)p.v + (b * p.Hkv + hk) * (int64_t)T * D;
+
+  // ---- 3. staging: bias/kinds -> registers; K/V -> registers -> LDS ----------
+  struct TileMask {
+    Bias4<BiasT> bias[4];
+    int4 kind[4];
+  };
+  // this lane's 16 keys of tile t: j0 + 8*i + 4*hh + (0..3)
+  auto mask_load = [&](int t, TileMask& m) {
+    const int j0 = (int)s_list[t] * kTileKeys;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int jb = j0 + 8 * i + 4 * hh;
+      if constexpr (kRules) {
+        int4 k4 = {0, 0, 0, 0};
+        if (kindb) {
+          if (vec4) {
+            k4 = ld_global<int4>(kindb + min(jb, T - 4));
+          } else {
+            k4.x = kindb[min(jb, T - 1)]; k4.y = kindb[min(jb + 1, T - 1)];
+            k4.z = kindb[min(jb + 2, T - 1)]; k4.w = kindb[min(jb + 3, T - 1)];
+          }
+        }
+        m.kind[i] = k4;
+      } else {
+        m.bias[i] = load_bias4(brow, jb, T, vec4);
+      }
+    }
+  };
+  // K and V of a tile move global -> registers -> LDS. At D = 512 the two go
+  // through one register buffer in turn (K during S^T, V during PV): Q^T and
+  // the O^T accumulators leave no room for both.
+  constexpr bool kTwoPhase = D >= 512;
+  bf16x8 kreg[CPT];
+  bf16x8 vreg[kTwoPhase ? 1 : CPT];
+  auto load_rows = [&](int t, const __bf16* src, bf16x8* dst) {
+    const int j0 = (int)s_list[t] * kTileKeys;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = min(tid + i * NT, CH - 1);
+      const int kk = c / CPR, dc = c % CPR;
+      const int j = min(j0 + kk, np - 1);   // clamped: rows past nonpad are zeroed below
+      dst[i] = ld_global<bf16x8>(src + (int64_t)j * D + 8 * dc);
+    }
+  };
+  auto store_rows = [&](int t, __bf16* tile, const bf16x8* src) {
+    const int j0 = (int)s_list[t] * kTileKeys;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      if (CH % NT == 0 || c < CH) {
+        const int kk = c / CPR, dc = c % CPR;
+        // keys past nonpad hold arbitrary bits: select zeros (never multiply them)
+        *reinterpret_cast<bf16x8*>(tile + swz<D>(kk, dc)) = (j0 + kk < np) ? src[i] : bf16x8{};
+      }
+    }
+  };
+  auto stage_load = [&](int t) {
+    load_rows(t, kg, kreg);
+    if constexpr (!kTwoPhase) load_rows(t, vg, vreg);
+  };
+  auto stage_store = [&](int t, int buf) {
+    __bf16* ks = stages + buf * STAGE_ELEMS;
+    store_rows(t, ks, kreg);
+    if constexpr (!kTwoPhase) store_rows(t, ks + TILE_ELEMS, vreg);
+  };
+
+  // ---- 4. main loop ---------------------------------------------------------
+  f32x16 oacc[DBLK];
+#pragma unroll
+  for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // tr16 addressing of V^T: lane L = 16*gq + 4*kq + jq reads
+  // V[16*step + 8*half + 4*(gq/2) + kq][32*blk + 16*(gq%2) + 4*jq]
+  const int gq = lane >> 4, kq = (lane >> 2) & 3, jq = lane & 3;
+  const int vkey0 = 4 * (gq >> 1) + kq;
+  const int vdofs = 16 * (gq & 1) + 4 * jq;
+
+  TileMask mcur, mnxt;
+  if (n_live > 0) {
+    mask_load(0, mcur);
+    stage_load(0);
+    stage_store(0, 0);
+    if constexpr (kTwoPhase) {
+      load_rows(0, vg, kreg);
+      store_rows(0, stages + TILE_ELEMS, kreg);
+    }
+  }
+  __syncthreads();
+  for (int t = 0; t < n_live; ++t) {
+    const int buf = t & 1;
+    const int j0 = (int)s_list[t] * kTileKeys;
+    const bool more = t + 1 < n_live;
+    if (more) {
+      mask_load(t + 1, mnxt);   // small loads first (see the header)
+      stage_load(t + 1);
+    }
+
+    // S^T = K Q^T
+    const __bf16* ks = stages + buf * STAGE_ELEMS;
+    const __bf16* vs = ks + TILE_ELEMS;
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + swz<D>(col, 2 * i + hh));
+      sacc = mfma32x32x16(a, qf[i], sacc);
+    }
+
+    // keep = valid && allowed; x = keep ? (s*scale + bias)*log2e : -inf
+    float x[16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = j0 + 8 * i + 4 * hh + jj;
+        bool keep;
+        float badd = 0.f;
+        if constexpr (kRules) {
+          const int kj = jj == 0 ? mcur.kind[i].x : jj == 1 ? mcur.kind[i].y
+                       : jj == 2 ? mcur.kind[i].z : mcur.kind[i].w;
+          keep = row_ok & (j < np) & rule.allowed(j, kj);
+        } else {
+          const BiasT bv = mcur.bias[i].get(jj);
+          keep = row_ok & (j < np) & live_bits<BiasT>(bv);
+          badd = bias_f32<BiasT>(bv) * kLog2e;
+        }
+        const float v = fmaf(sacc[4 * i + jj], scale_log2, badd);
+        x[4 * i + jj] = keep ? v : -INFINITY;
+        mt = fmaxf(mt, x[4 * i + jj]);
+      }
+    mt = fmaxf(mt, lane_xor(mt, 32));
+    const float mn = fmaxf(m_run, mt);
+    const bool need = mn > m_run + kRescaleThreshold;
+    const bool rescale = __any(need);   // wave-uniform
+    float alpha = 1.f;
+    if (rescale) {
+      alpha = need ? fast_exp2(m_run - mn) : 1.f;
+      if (need) m_run = mn;
+      l_run *= alpha;
+    }
+    // weights, rounded to bf16; P^T for the two 16-key steps
+    uint32_t pw[8];
+    float lsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const float p0 = (x[e] == -INFINITY) ? 0.f : fast_exp2(x[e] - m_run);
+      const float p1 = (x[e + 1] == -INFINITY) ? 0.f : fast_exp2(x[e + 1] - m_run);
+      const uint32_t pk = pack_bf16x2(p0, p1);
+      lsum += bf16lo(pk) + bf16hi(pk);
+      pw[e >> 1] = pk;
+    }
+    l_run += lsum;
+    const bf16x8 pb0 = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+    const bf16x8 pb1 = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+    if constexpr (kTwoPhase) {
+      if (more) {   // K of the next tile to LDS, then its V into the same registers
+        store_rows(t + 1, stages + (buf ^ 1) * STAGE_ELEMS, kreg);
+        load_rows(t + 1, vg, kreg);
+      }
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int blk = 0; blk < DBLK; ++blk) {
+      // the O^T rescale, one 32-d block at a time right before its MFMAs, keeps
+      // only 16 accumulators in flight through the vector registers
+      if (rescale) oacc[blk] *= alpha;
+      const int d = 32 * blk + vdofs;
+      const int c = d >> 3, within = d & 7;
+#pragma unroll
+      for (int step = 0; step < 2; ++step) {
+        const int k0 = 16 * step + vkey0;
+        const u32x2 lo = lds_read_tr16(vs + swz<D>(k0, c) + within);
+        const u32x2 hi = lds_read_tr16(vs + swz<D>(k0 + 8, c) + within);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        oacc[blk] = mfma32x32x16(va, step == 0 ? pb0 : pb1, oacc[blk]);
+      }
+    }
+
+    if (more) {
+      if constexpr (kTwoPhase) store_rows(t + 1, stages + (buf ^ 1) * STAGE_ELEMS + TILE_ELEMS, kreg);
+      else stage_store(t + 1, buf ^ 1);
+      mcur = mnxt;
+    }
+    __syncthreads();
+  }
+
+  // ---- 5. normalise and store -----------------------------------------------
+  const float l_tot = l_run + lane_xor(l_run, 32);
+  if (row_ok) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* op = (uint16_t*)p.out + ((b * p.Hq + h) * p.S_q + s) * (int64_t)D + 4 * hh;
+#pragma unroll
+    for (int blk = 0; blk < DBLK; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 pk;
+        pk.x = pack_bf16x2(oacc[blk][4 * i + 0] * inv, oacc[blk][4 * i + 1] * inv);
+        pk.y = pack_bf16x2(oacc[blk][4 * i + 2] * inv, oacc[blk][4 * i + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + 32 * blk + 8 * i) = pk;
+      }
+  }
+}
+
+// The same computation with 16-row wavefronts (16x16x32 MFMAs), for D = 512:
+// a 32-row wavefront would need 256 accumulator registers for O^T at D = 512
+// plus 128 for Q^T, more than one lane has. Rows r = 16*w + (lane % 16);
+// S^T lane l: query row l % 16, keys 16*kb + 4*(l/16) + e; O^T lane l: query
+// row l % 16, d = 16*blk + 4*(l/16) + e. V^T comes from two transposing reads
+// per (16-d block): lane 16*g + 4*k + j addresses V[4*g + k (+16)][16*blk + 4*j].
+template <int D, int NW, bool kRules, typename BiasT>
+__global__ __launch_bounds__(NW * 64) void attn_prefill16_kernel(AttnParams p, int n_qt) {
+  constexpr int NT = NW * 64;
+  constexpr int KSTEPS = D / 32;
+  constexpr int DBLK = D / 16;
+  constexpr int CPR = D / 8;
+  constexpr int CH = kTileKeys * CPR;
+  constexpr int CPT = (CH + NT - 1) / NT;
+  constexpr int TILE_ELEMS = kTileKeys * D;
+  constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  __bf16* stages = reinterpret_cast<__bf16*>(smem);
+  const int T = p.T, G = p.G;
+  const int n_kt_max = num_tiles(T);
+  uint32_t* s_bits = reinterpret_cast<uint32_t*>(smem + (size_t)2 * STAGE_ELEMS * 2);
+  const int n_words = (n_kt_max + 31) / 32;
+  uint16_t* s_list = reinterpret_cast<uint16_t*>(s_bits + n_words);
+  __shared__ int s_nlive;
+  __shared__ int32_t s_ids[4];
+  __shared__ int s_nids;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;   // query row within the wavefront
+  const int grp = lane >> 4;   // k-slot group
+
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = n_qt - 1 - (wg % n_qt);
+  const int bh = wg / n_qt;
+  const int hk = bh % p.Hkv;
+  const int64_t b = bh / p.Hkv;
+  const int np = (int)clamp_nonpad(p.nonpad[b], T);
+  const int MQ = (16 * NW) / G;
+  const int s0 = qt * MQ;
+  const int s_end = min(s0 + MQ, p.S_q);
+  const int n_kt = num_tiles(np);
+
+  const int n_live = build_live_list<NT, kRules, BiasT>(p, b, np, s0, s_end, n_kt, s_bits, s_list,
+                                                       n_words, s_ids, &s_nids, &s_nlive);
+
   const int r = 16 * w + col;
   const int sl = r / G, g = r % G;
   const int s = s0 + sl;
@@ -214,223 +574,185 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnParams p, int
   }
   const BiasT* brow = kRules ? nullptr : (const BiasT*)p.bias + (b * p.S_q + (row_ok ? s : 0)) * (int64_t)T;
   const int32_t* kindb = p.slot_kind ? p.slot_kind + b * T : nullptr;
-  const bool bias_vec = (T % 4) == 0;
+  const bool vec4 = (T % 4) == 0;
   const float scale_log2 = p.scale * kLog2e;
-
   const __bf16* kg = (const __bf16*)p.k + (b * p.Hkv + hk) * (int64_t)T * D;
   const __bf16* vg = (const __bf16*)p.v + (b * p.Hkv + hk) * (int64_t)T * D;
 
-  // ---- 3. tile staging: global -> registers -> LDS ---------------------------
-  bf16x8 kreg[KPT];
-  bf16x8 vreg[VPT][4];
-  auto stage_load = [&](int t) {
+  struct TileMask {
+    Bias4<BiasT> bias[2];
+    int4 kind[2];
+  };
+  // this lane's 8 keys of tile t: j0 + 16*kb + 4*grp + (0..3)
+  auto mask_load = [&](int t, TileMask& m) {
     const int j0 = (int)s_list[t] * kTileKeys;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * NT;
-      const int kk = c / (D / 8), dc = c % (D / 8);
-      const int j = j0 + kk;
-      kreg[i] = (c < KCH && j < np) ? ld_global<bf16x8>(kg + (int64_t)j * D + 8 * dc) : bf16x8{};
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int u = tid + i * NT;
-      const int kgp = u % 8, dc = u / 8;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + 4 * kgp + e;
-        vreg[i][e] = (u < VUN && j < np) ? ld_global<bf16x8>(vg + (int64_t)j * D + 8 * dc) : bf16x8{};
+    for (int kb = 0; kb < 2; ++kb) {
+      const int jb = j0 + 16 * kb + 4 * grp;
+      if constexpr (kRules) {
+        int4 k4 = {0, 0, 0, 0};
+        if (kindb) {
+          if (vec4) {
+            k4 = ld_global<int4>(kindb + min(jb, T - 4));
+          } else {
+            k4.x = kindb[min(jb, T - 1)]; k4.y = kindb[min(jb + 1, T - 1)];
+            k4.z = kindb[min(jb + 2, T - 1)]; k4.w = kindb[min(jb + 3, T - 1)];
+          }
+        }
+        m.kind[kb] = k4;
+      } else {
+        m.bias[kb] = load_bias4(brow, jb, T, vec4);
       }
     }
   };
-  auto stage_store = [&](int buf) {
-    __bf16* ks = bufs + buf * L::BUF_ELEMS;
-    __bf16* vt = ks + L::K_ELEMS;
+  bf16x8 kreg[CPT], vreg[CPT];
+  auto stage_load = [&](int t) {
+    const int j0 = (int)s_list[t] * kTileKeys;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * NT;
-      if (c < KCH) {
-        const int kk = c / (D / 8), dc = c % (D / 8);
-        *reinterpret_cast<bf16x8*>(ks + kk * L::KST + 8 * dc) = kreg[i];
-      }
+    for (int i = 0; i < CPT; ++i) {
+      const int c = min(tid + i * NT, CH - 1);
+      const int kk = c / CPR, dc = c % CPR;
+      const int j = min(j0 + kk, np - 1);
+      kreg[i] = ld_global<bf16x8>(kg + (int64_t)j * D + 8 * dc);
+      vreg[i] = ld_global<bf16x8>(vg + (int64_t)j * D + 8 * dc);
     }
+  };
+  auto stage_store = [&](int t, int buf) {
+    const int j0 = (int)s_list[t] * kTileKeys;
+    __bf16* ks = stages + buf * STAGE_ELEMS;
+    __bf16* vs = ks + TILE_ELEMS;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int u = tid + i * NT;
-      if (u < VUN) {
-        const int kgp = u % 8, dc = u / 8;
-        const u32x4 a0 = __builtin_bit_cast(u32x4, vreg[i][0]);
-        const u32x4 a1 = __builtin_bit_cast(u32x4, vreg[i][1]);
-        const u32x4 a2 = __builtin_bit_cast(u32x4, vreg[i][2]);
-        const u32x4 a3 = __builtin_bit_cast(u32x4, vreg[i][3]);
-        // d = 8*dc + e: the 4 keys' values of that d, packed key-consecutive
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int wi = e >> 1;
-          const bool hi = e & 1;
-          const uint32_t x0 = hi ? (a0[wi] >> 16) : (a0[wi] & 0xffffu);
-          const uint32_t x1 = hi ? (a1[wi] >> 16) : (a1[wi] & 0xffffu);
-          const uint32_t x2 = hi ? (a2[wi] >> 16) : (a2[wi] & 0xffffu);
-          const uint32_t x3 = hi ? (a3[wi] >> 16) : (a3[wi] & 0xffffu);
-          u32x2 pk;
-          pk.x = x0 | (x1 << 16);
-          pk.y = x2 | (x3 << 16);
-          *reinterpret_cast<u32x2*>(vt + (8 * dc + e) * L::VST + 4 * kgp) = pk;
-        }
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      if (CH % NT == 0 || c < CH) {
+        const int kk = c / CPR, dc = c % CPR;
+        const bool ok = j0 + kk < np;   // keys past nonpad: zeros, never their bits
+        *reinterpret_cast<bf16x8*>(ks + swz<D>(kk, dc)) = ok ? kreg[i] : bf16x8{};
+        *reinterpret_cast<bf16x8*>(vs + swz<D>(kk, dc)) = ok ? vreg[i] : bf16x8{};
       }
     }
   };
 
-  // ---- 4. main loop ---------------------------------------------------------
   f32x4 oacc[DBLK];
 #pragma unroll
   for (int i = 0; i < DBLK; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  const int vkey0 = lane >> 2;          // 4*g + k for lane 16*g + 4*k + j
+  const int vdofs = 4 * (lane & 3);     // 4*j
 
+  TileMask mcur, mnxt;
   if (n_live > 0) {
+    mask_load(0, mcur);
     stage_load(0);
-    stage_store(0);
+    stage_store(0, 0);
   }
   __syncthreads();
   for (int t = 0; t < n_live; ++t) {
     const int buf = t & 1;
     const int j0 = (int)s_list[t] * kTileKeys;
-    if (t + 1 < n_live) stage_load(t + 1);
-
-    // bias / rules for this lane's 8 keys: j0 + 16*kb + 4*grp + e
-    float badd[2][4];
-    bool keep[2][4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int jb = j0 + 16 * kb + 4 * grp;
-      if constexpr (kRules) {
-        int32_t kv[4] = {0, 0, 0, 0};
-        if (kindb) {
-          if ((T % 4) == 0 && jb < T) {
-            const int4 k4 = ld_global<int4>(kindb + jb);
-            kv[0] = k4.x; kv[1] = k4.y; kv[2] = k4.z; kv[3] = k4.w;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) kv[e] = (jb + e < T) ? kindb[jb + e] : 0;
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = jb + e;
-          keep[kb][e] = row_ok && (j < np) && rule.allowed(j, kv[e]);
-          badd[kb][e] = 0.f;
-        }
-      } else {
-        BiasT bv[4];
-        if (row_ok && bias_vec && jb + 3 < T) {
-          if constexpr (sizeof(BiasT) == 2) {
-            const u32x2 raw = ld_global<u32x2>(brow + jb);
-            bv[0] = raw.x & 0xffff; bv[1] = raw.x >> 16; bv[2] = raw.y & 0xffff; bv[3] = raw.y >> 16;
-          } else {
-            const u32x4 raw = ld_global<u32x4>(brow + jb);
-            bv[0] = raw.x; bv[1] = raw.y; bv[2] = raw.z; bv[3] = raw.w;
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) bv[e] = (row_ok && jb + e < T) ? brow[jb + e] : (BiasT)0;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = jb + e;
-          keep[kb][e] = row_ok && (j < np) && live_bits<BiasT>(bv[e]);
-          float f;
-          if constexpr (sizeof(BiasT) == 2) f = bf16_bits_to_f32(bv[e]);
-          else f = __uint_as_float(bv[e]);
-          badd[kb][e] = keep[kb][e] ? f * kLog2e : 0.f;
-        }
-      }
+    const bool more = t + 1 < n_live;
+    if (more) {
+      mask_load(t + 1, mnxt);
+      stage_load(t + 1);
     }
-
-    // S^T = K Q^T
-    const __bf16* ks = bufs + buf * L::BUF_ELEMS;
-    const __bf16* vt = ks + L::K_ELEMS;
+    const __bf16* ks = stages + buf * STAGE_ELEMS;
+    const __bf16* vs = ks + TILE_ELEMS;
     f32x4 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const __bf16* kr = ks + (16 * kb + col) * L::KST + 8 * grp;
 #pragma unroll
-      for (int i = 0; i < KSTEPS; ++i)
-        sacc[kb] = mfma16x16x32(*reinterpret_cast<const bf16x8*>(kr + 32 * i), qf[i], sacc[kb]);
+      for (int i = 0; i < KSTEPS; ++i) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + swz<D>(16 * kb + col, 4 * i + grp));
+        sacc[kb] = mfma16x16x32(a, qf[i], sacc[kb]);
+      }
     }
-
-    // online softmax for query row `col` (values spread over the 4 groups)
-    float x[2][4];
+    float x[8];
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[kb][e] = keep[kb][e] ? fmaf(sacc[kb][e], scale_log2, badd[kb][e]) : -INFINITY;
-        mt = fmaxf(mt, x[kb][e]);
+        const int j = j0 + 16 * kb + 4 * grp + e;
+        bool keep;
+        float badd = 0.f;
+        if constexpr (kRules) {
+          const int kj = e == 0 ? mcur.kind[kb].x : e == 1 ? mcur.kind[kb].y
+                       : e == 2 ? mcur.kind[kb].z : mcur.kind[kb].w;
+          keep = row_ok & (j < np) & rule.allowed(j, kj);
+        } else {
+          const BiasT bv = mcur.bias[kb].get(e);
+          keep = row_ok & (j < np) & live_bits<BiasT>(bv);
+          badd = bias_f32<BiasT>(bv) * kLog2e;
+        }
+        const float v = fmaf(sacc[kb][e], scale_log2, badd);
+        x[4 * kb + e] = keep ? v : -INFINITY;
+        mt = fmaxf(mt, x[4 * kb + e]);
       }
     mt = fmaxf(mt, lane_xor(mt, 16));
     mt = fmaxf(mt, lane_xor(mt, 32));
     const float mn = fmaxf(m_run, mt);
     const bool need = mn > m_run + kRescaleThreshold;
-    if (__any(need)) {
-      const float alpha = need ? fast_exp2(m_run - mn) : 1.f;
+    const bool rescale = __any(need);
+    float alpha = 1.f;
+    if (rescale) {
+      alpha = need ? fast_exp2(m_run - mn) : 1.f;
       if (need) m_run = mn;
       l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < DBLK; ++i) oacc[i] *= alpha;
     }
     uint32_t pw[4];
     float lsum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 4; e += 2) {
-        const float p0 = (x[kb][e] == -INFINITY) ? 0.f : fast_exp2(x[kb][e] - m_run);
-        const float p1 = (x[kb][e + 1] == -INFINITY) ? 0.f : fast_exp2(x[kb][e + 1] - m_run);
-        const uint32_t pk = pack_bf16x2(p0, p1);
-        lsum += bf16lo(pk) + bf16hi(pk);
-        pw[2 * kb + (e >> 1)] = pk;
-      }
+    for (int e = 0; e < 8; e += 2) {
+      const float p0 = (x[e] == -INFINITY) ? 0.f : fast_exp2(x[e] - m_run);
+      const float p1 = (x[e + 1] == -INFINITY) ? 0.f : fast_exp2(x[e + 1] - m_run);
+      const uint32_t pk = pack_bf16x2(p0, p1);
+      lsum += bf16lo(pk) + bf16hi(pk);
+      pw[e >> 1] = pk;
+    }
     l_run += lsum;
     const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-
-    // O^T += V^T P^T
 #pragma unroll
-    for (int i = 0; i < DBLK; ++i) {
-      const __bf16* vr = vt + (16 * i + col) * L::VST + 4 * grp;
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 16);
+    for (int blk = 0; blk < DBLK; ++blk) {
+      if (rescale) oacc[blk] *= alpha;
+      const int d = 16 * blk + vdofs;
+      const int c = d >> 3, within = d & 7;
+      const u32x2 lo = lds_read_tr16(vs + swz<D>(vkey0, c) + within);
+      const u32x2 hi = lds_read_tr16(vs + swz<D>(16 + vkey0, c) + within);
       const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-      oacc[i] = mfma16x16x32(va, pb, oacc[i]);
+      oacc[blk] = mfma16x16x32(va, pb, oacc[blk]);
     }
-
-    if (t + 1 < n_live) stage_store(buf ^ 1);
+    if (more) {
+      stage_store(t + 1, buf ^ 1);
+      mcur = mnxt;
+    }
     __syncthreads();
   }
 
-  // ---- 5. normalise and store -----------------------------------------------
   float l_tot = l_run + lane_xor(l_run, 16);
   l_tot += lane_xor(l_tot, 32);
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* op = (uint16_t*)p.out + ((b * p.Hq + h) * p.S_q + s) * (int64_t)D + 4 * grp;
 #pragma unroll
-    for (int i = 0; i < DBLK; ++i) {
+    for (int blk = 0; blk < DBLK; ++blk) {
       u32x2 pk;
-      pk.x = pack_bf16x2(oacc[i][0] * inv, oacc[i][1] * inv);
-      pk.y = pack_bf16x2(oacc[i][2] * inv, oacc[i][3] * inv);
-      *reinterpret_cast<u32x2*>(op + 16 * i) = pk;
+      pk.x = pack_bf16x2(oacc[blk][0] * inv, oacc[blk][1] * inv);
+      pk.y = pack_bf16x2(oacc[blk][2] * inv, oacc[blk][3] * inv);
+      *reinterpret_cast<u32x2*>(op + 16 * blk) = pk;
     }
   }
 }
 
 template <int D, int NW, bool kRules, typename BiasT>
 static hipError_t launch_prefill_inst(const AttnParams& p, hipStream_t stream) {
-  const int MQ = (16 * NW) / p.G;
+  constexpr bool k16 = D >= 512;   // 16-row wavefronts (see attn_prefill16_kernel)
+  const int MQ = ((k16 ? 16 : 32) * NW) / p.G;
   const int n_qt = (p.S_q + MQ - 1) / MQ;
   const size_t lds = prefill_lds_bytes(D, p.T);
-  auto kern = attn_prefill_kernel<D, NW, kRules, BiasT>;
+  void (*kern)(AttnParams, int);
+  if constexpr (k16) kern = attn_prefill16_kernel<D, NW, kRules, BiasT>;
+  else kern = attn_prefill_kernel<D, NW, kRules, BiasT>;
   // Opt in to the dynamic LDS this launch needs (static LDS of the kernel comes
   // on top, so the request is the exact size, not the CU's 160 KiB).
   static size_t lds_set = 0;  // per instantiation
@@ -459,11 +781,15 @@ static hipError_t launch_prefill_v(const AttnParams& p, hipStream_t stream) {
 
 template <int D>
 static hipError_t launch_prefill_d(const AttnParams& p, hipStream_t stream) {
-  // 8 wavefronts (128 rows) when that still gives >= 2 workgroups per CU; at
-  // D = 512 the 8-wavefront variant would spill (its O^T alone is 128 VGPRs)
-  const int64_t wg8 = (int64_t)p.B * p.Hkv * ((p.S_q * (int64_t)p.G + 127) / 128);
-  if (D < 512 && wg8 >= 512) return launch_prefill_v<D, 8>(p, stream);
-  return launch_prefill_v<D, 4>(p, stream);
+  // 4 wavefronts (128 rows) when that still gives about one workgroup per CU,
+  // else 2 (64 rows): more, smaller workgroups
+  if constexpr (D >= 512) {
+    return launch_prefill_v<D, 4>(p, stream);
+  } else {
+    const int64_t wg4 = (int64_t)p.B * p.Hkv * ((p.S_q * (int64_t)p.G + 127) / 128);
+    if (wg4 >= 256) return launch_prefill_v<D, 4>(p, stream);
+    return launch_prefill_v<D, 2>(p, stream);
+  }
 }
 
 hipError_t launch_attn_prefill(const AttnParams& p, hipStream_t stream) {

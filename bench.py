@@ -81,16 +81,24 @@ class InputSet:
         self.out = torch.empty_like(self.q)
 
 
+VARIANT = "bias"   # "bias": materialised bias tensor; "rules": rules evaluated in-kernel
+
+
 def run_scatter_bias(ab, w, step, s):
     if s.k_new is not None:
         ab.kv_tensor_scatter(s.k, s.k_new, s.wi)
         ab.kv_tensor_scatter(s.v, s.v_new, s.wi)
-    ab.build_static_cache_bias(s.nonpad, s.q_start, s.kind, step.S_q, w.max_seq, w.window,
-                               dtype=w.dtype, out=s.bias)
+    if VARIANT == "bias":
+        ab.build_static_cache_bias(s.nonpad, s.q_start, s.kind, step.S_q, w.max_seq, w.window,
+                                   dtype=w.dtype, out=s.bias)
 
 
 def run_attention(ab, w, s, ws):
-    ab.attn_bias_gqa_fwd(s.q, s.k, s.v, s.bias, s.nonpad, w.scale, out=s.out, workspace=ws)
+    if VARIANT == "bias":
+        ab.attn_bias_gqa_fwd(s.q, s.k, s.v, s.bias, s.nonpad, w.scale, out=s.out, workspace=ws)
+    else:
+        ab.attn_bias_gqa_fwd(s.q, s.k, s.v, None, s.nonpad, w.scale, q_start=s.q_start,
+                             slot_kind=s.kind, window=w.window, out=s.out, workspace=ws)
 
 
 def work_counts(w, step, s, torch):
@@ -152,7 +160,14 @@ def bench_workload(name, steps, warmup, eager, torch, ab):
         run_attention(ab, w, s, ws)
     torch.cuda.synchronize()
     ref_out = [s.out.clone() for s in sets]
+    if VARIANT == "rules":   # the work is counted from the same rules, materialised once
+        ab.build_static_cache_bias(sets[0].nonpad, sets[0].q_start, sets[0].kind, step.S_q,
+                                   w.max_seq, w.window, dtype=w.dtype, out=sets[0].bias)
     counts = work_counts(w, step, sets[0], torch)
+    if VARIANT == "rules":   # no bias tensor is read or written in this variant
+        counts["attn_bytes"] -= step.S_q * int(sets[0].nonpad.clamp(0, w.max_seq).sum()) * (
+            2 if w.dtype == torch.bfloat16 else 4)
+        counts["step_bytes"] = counts["attn_bytes"] + counts["scatter_bytes"]
     for s in sets:
         assert torch.isfinite(s.out.float()).all(), "non-finite output"
 
@@ -229,6 +244,26 @@ def bench_workload(name, steps, warmup, eager, torch, ab):
     return res, w
 
 
+def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
+    """A plain device-to-device copy (torch copy_ kernel) of nbytes: the
+    practical HBM ceiling on this device, read + write bytes per second."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(st)
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def traffic_for(name):
     """HBM bytes per attention launch from committed rocprofv3 counter runs, if
     they were taken on the current kernel source; else None."""
@@ -286,7 +321,12 @@ def main():
     ap.add_argument("--no-secondary", dest="secondary", action="store_false")
     ap.add_argument("--eager", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant", default="bias", choices=["bias", "rules"],
+                    help="bias: build and read the bias tensor; rules: evaluate the mask "
+                         "rules inside the attention kernel (no bias tensor)")
     args = ap.parse_args()
+    global VARIANT
+    VARIANT = args.variant
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported: the "
@@ -303,6 +343,8 @@ def main():
     log(f"device {torch.cuda.get_device_name(0)}, library {ab.library_path()}")
 
     t_start = time.perf_counter()
+    copy_gbs = copy_bandwidth(torch)
+    log(f"device copy bandwidth {copy_gbs:.0f} GB/s (read + write)")
     main_res, w = bench_workload(args.workload, args.steps, args.warmup, args.eager, torch, ab)
     secondary = {}
     if args.secondary:
@@ -324,6 +366,7 @@ def main():
         cpu = cpu_baseline(w, counts)
     cfg = dict(main_res["desc"])
     cfg.update({"kernel_timing": main_res["mode"], "rotating_input_sets": main_res["n_sets"],
+                "device_copy_gbs": round(copy_gbs, 1), "variant": VARIANT,
                 "attn_us": round(main_res["attn_ms"] * 1e3, 2),
                 "attn_bytes": counts["attn_bytes"], "step_bytes": counts["step_bytes"],
                 "live_keys": counts["live_keys"]})
