@@ -264,34 +264,98 @@ def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
     return gbs
 
 
+KERNEL_SOURCES_DIR = os.path.join("additive_bias_gqa_amd", "csrc")
+
+
+def kernel_sources():
+    d = os.path.join(HERE, KERNEL_SOURCES_DIR)
+    return sorted(os.path.join(KERNEL_SOURCES_DIR, f) for f in os.listdir(d)
+                  if f.endswith((".hip", ".h")))
+
+
+def sources_sha256(rels):
+    h = hashlib.sha256()
+    for rel in rels:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
 def traffic_for(name):
-    """HBM bytes per attention launch from committed rocprofv3 counter runs, if
-    they were taken on the current kernel source; else None."""
+    """HBM bytes per attention call from committed rocprofv3 counter runs, if
+    they were taken on the current kernel sources; else None."""
     path = os.path.join(HERE, "profiles", f"traffic_{name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    h = hashlib.sha256()
-    for rel in rec.get("sources", []):
-        with open(os.path.join(HERE, rel), "rb") as f:
-            h.update(f.read())
-    if h.hexdigest() != rec.get("source_sha256"):
+    try:
+        if sources_sha256(rec.get("sources", [])) != rec.get("source_sha256") or \
+                rec.get("sources") != kernel_sources():
+            return None
+    except OSError:
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, counts, budget_s=20.0):
-    """The oracle (scatter + bias + attention, fp64, OpenMP) on whole batch
-    entries of the workload until ~budget_s of work; rate in the metric's unit."""
-    import numpy as np
+def write_traffic(name, fetch_csv, write_csv, copy_bytes=1 << 30):
+    """Turn two rocprofv3 --pmc runs of `bench.py --eager` (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch) into HBM bytes per attention call.
+
+    Each counter is scaled by what it reads for the plain 1 GiB device copy
+    that bench.py runs first (the largest __amd_rocclr_copyBuffer dispatch):
+    scale = copy bytes / (counter KiB * 1024). The attention call is every
+    abgqa::attn_* kernel it launches (split-KV decode: the split kernel and
+    the combine kernel), averaged per dispatch and summed."""
+    import csv
+    import collections
+
+    def read(path):
+        per = collections.defaultdict(list)
+        copy_max = 0.0
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k, v = r["Kernel_Name"], float(r["Counter_Value"])
+                if k == "__amd_rocclr_copyBuffer":
+                    copy_max = max(copy_max, v)
+                elif k.startswith("void abgqa::attn_"):
+                    per[k].append(v)
+        if not per or copy_max <= 0:
+            raise SystemExit(f"{path}: no attention or copy dispatches found")
+        return per, copy_bytes / (copy_max * 1024.0)
+
+    fetch, fs = read(fetch_csv)
+    write, ws = read(write_csv)
+    kernels = {}
+    total = 0.0
+    for k in sorted(fetch):
+        fk = sum(fetch[k]) / len(fetch[k]) * 1024.0 * fs
+        wk = sum(write[k]) / len(write[k]) * 1024.0 * ws if k in write else 0.0
+        kernels[k] = dict(dispatches=len(fetch[k]), fetch_bytes=round(fk), write_bytes=round(wk))
+        total += fk + wk
+    rels = kernel_sources()
+    rec = dict(workload=name, fetch_scale=round(fs, 5), write_scale=round(ws, 5),
+               copy_bytes=copy_bytes, kernels=kernels, hbm_bytes_per_launch=round(total),
+               sources=rels, source_sha256=sources_sha256(rels))
+    path = os.path.join(HERE, "profiles", f"traffic_{name}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
+def cpu_baseline(w, counts, budget_s=12.0):
+    """The oracle (scatter + bias + attention, fp64, OpenMP) on the workload's
+    batch entries, one after another and round again, until ~budget_s of host
+    work; rate in the metric's unit (algorithmic step bytes per second)."""
     import oracle
     step = w.steps[0]
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     oracle.build(force=False)
     t0 = time.perf_counter()
     done = 0
-    for b in range(w.B):
+    while True:
+        b = done % w.B
         sl = slice(b, b + 1)
         k, v = w.k_cache[sl], w.v_cache[sl]
         if step.k_new is not None:
@@ -304,11 +368,10 @@ def cpu_baseline(w, counts, budget_s=20.0):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    frac = done / w.B
-    rate = counts["step_bytes"] * frac / dt / 1e9
+    rate = counts["step_bytes"] * (done / w.B) / dt / 1e9
     return dict(value=round(rate, 4), unit="GB/s", cores=cores, kind="oracle",
-                sample=f"{done} of {w.B} batch entries of one step (scatter + bias + attention), "
-                       f"{dt:.1f} s")
+                sample=f"{done} batch-entry passes ({done / w.B:.2f} steps of B={w.B}; "
+                       f"scatter + bias + attention of one batch entry each) in {dt:.1f} s")
 
 
 def main():
@@ -324,7 +387,13 @@ def main():
     ap.add_argument("--variant", default="bias", choices=["bias", "rules"],
                     help="bias: build and read the bias tensor; rules: evaluate the mask "
                          "rules inside the attention kernel (no bias tensor)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
+                         "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(args.workload, *args.traffic_from)
+        return
     global VARIANT
     VARIANT = args.variant
 
