@@ -142,6 +142,22 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   const int64_t b = bh / p.Hkv;
   const int np = (int)clamp_nonpad(p.nonpad[b], T);
 
+  // ---- 0. Q rows (row r = s * G + g) into registers, to be parked in LDS ----
+  // Issued before the range scan so that both memory round trips overlap; the
+  // index is clamped (loads stay unconditional), the store is guarded.
+  constexpr int QCH = kQinLds ? (NR * (D / 8) + kDecThreads - 1) / kDecThreads : 1;
+  bf16x8 qtmp[QCH];
+  if constexpr (kQinLds) {
+    const int nq = R * (D / 8);
+#pragma unroll
+    for (int i = 0; i < QCH; ++i) {
+      const int c = min(tid + i * kDecThreads, nq - 1);
+      const int r = c / (D / 8), dc = c % (D / 8);
+      qtmp[i] = ld_global<bf16x8>((const __bf16*)p.q +
+          (((b * p.Hq + hk * G + r % G) * p.S_q + r / G) * (int64_t)D) + 8 * dc);
+    }
+  }
+
   // ---- 1. live range [lo, hi) of keys, over all S_q rows -------------------
   if (tid == 0) { s_range[0] = INT32_MAX; s_range[1] = -1; }
   if constexpr (!kParMerge)
@@ -150,28 +166,50 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   {
     int lo = INT32_MAX, hi = -1;
     if constexpr (!kRules) {
+      // NB 16-byte loads per thread in flight at once, unconditional (index
+      // clamped to the last vector; the extra copies are discarded below), so
+      // the scan costs one memory round trip per batch, not one per load
       const BiasT* bb = (const BiasT*)p.bias + b * p.S_q * (int64_t)T;
       constexpr int EPV = 16 / sizeof(BiasT);  // elements per 16-byte load
+      constexpr int NB = 4;
       const int nvec = (np + EPV - 1) / EPV;
-      const bool vec = (T % EPV) == 0;
-#pragma unroll 4
-      for (int idx = tid; idx < p.S_q * nvec; idx += kDecThreads) {
-        const int s = idx / nvec;
-        const int j0 = (idx - s * nvec) * EPV;
-        const BiasT* row = bb + (int64_t)s * T;
-        BiasT vals[EPV];
-        if (vec) {
-          *reinterpret_cast<u32x4*>(vals) = ld_global<u32x4>(row + j0);
-        } else {
+      const int total = p.S_q * nvec;
+      if ((T % EPV) == 0) {
+        for (int base = tid; base < total; base += NB * kDecThreads) {
+          u32x4 raw[NB];
 #pragma unroll
-          for (int e = 0; e < EPV; ++e) vals[e] = (j0 + e < T) ? row[j0 + e] : (BiasT)0;
+          for (int u = 0; u < NB; ++u) {
+            const int idx = min(base + u * kDecThreads, total - 1);
+            const int s = idx / nvec;
+            raw[u] = ld_global<u32x4>(bb + (int64_t)s * T + (idx - s * nvec) * EPV);
+          }
+#pragma unroll
+          for (int u = 0; u < NB; ++u) {
+            const int idx = base + u * kDecThreads;
+            const int j0 = (idx % nvec) * EPV;
+            BiasT vals[EPV];
+            *reinterpret_cast<u32x4*>(vals) = raw[u];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+              const int j = j0 + e;
+              if (idx < total && j < np && bias_live_bits<BiasT>(vals[e])) {
+                lo = min(lo, j);
+                hi = max(hi, j);
+              }
+            }
+          }
         }
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const int j = j0 + e;
-          if (j < np && bias_live_bits<BiasT>(vals[e])) {
-            lo = min(lo, j);
-            hi = max(hi, j);
+      } else {
+        for (int idx = tid; idx < total; idx += kDecThreads) {
+          const int s = idx / nvec;
+          const int j0 = (idx - s * nvec) * EPV;
+          const BiasT* row = bb + (int64_t)s * T;
+          for (int e = 0; e < EPV; ++e) {
+            const int j = j0 + e;
+            if (j < np && bias_live_bits<BiasT>(row[j])) {
+              lo = min(lo, j);
+              hi = max(hi, j);
+            }
           }
         }
       }
@@ -204,6 +242,14 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
       atomicMax(&s_range[1], hi);
     }
   }
+  if constexpr (kQinLds) {
+#pragma unroll
+    for (int i = 0; i < QCH; ++i) {
+      const int c = tid + i * kDecThreads;
+      if (c < R * (D / 8))
+        *reinterpret_cast<bf16x8*>(&s_q[(c / (D / 8)) * D + 8 * (c % (D / 8))]) = qtmp[i];
+    }
+  }
   __syncthreads();
   int live_lo = s_range[0], live_hi = s_range[1] + 1;
   if (live_hi <= 0) { live_lo = 0; live_hi = 0; }
@@ -217,16 +263,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   const int qrow = lane & 15;
   const int kgrp = lane >> 4;
   bf16x8 qa[kQinLds ? 1 : KSTEPS];
-  if constexpr (kQinLds) {
-    // the R real rows of Q, row r = s * G + g, into LDS
-    for (int c = tid; c < R * (D / 8); c += kDecThreads) {
-      const int r = c / (D / 8), dc = c % (D / 8);
-      const __bf16* qp = (const __bf16*)p.q +
-          (((b * p.Hq + hk * G + r % G) * p.S_q + r / G) * (int64_t)D) + 8 * dc;
-      *reinterpret_cast<bf16x8*>(&s_q[r * D + 8 * dc]) = ld_global<bf16x8>(qp);
-    }
-    __syncthreads();
-  } else {
+  if constexpr (!kQinLds) {
     const bool ok = qrow < R;
     const int s = ok ? qrow / G : 0, g = ok ? qrow % G : 0;
     const __bf16* qp = (const __bf16*)p.q +
@@ -272,8 +309,11 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   // key of the range (a valid, finite row), and its score is masked by `keep`
   // below, so its weight is exactly 0. No exec-masked branches means the
   // compiler can keep every load of a block in flight at once.
-  // For D <= 256 the next block's K/V are loaded while this one is computed.
-  constexpr bool kPrefetch = D <= 256;
+  // The next block's K/V are loaded while this one is computed, except for
+  // D = 512 with 8 wavefronts (two 32 KiB blocks per lane set do not fit the
+  // 256 registers a wavefront gets at two per SIMD; with one wavefront per
+  // SIMD the second buffer lives in the accumulation registers).
+  constexpr bool kPrefetch = D <= 256 || NW == 4;
   struct Blk {
     BiasT bias[E];
     int32_t kj;
@@ -555,12 +595,17 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(AttnParams p) {
   *reinterpret_cast<u32x4*>(op) = pk;
 }
 
-static int decode_waves() {
+// Wavefronts per split workgroup. D = 512 takes 8 (two per SIMD, one block
+// in flight each: more bytes in flight than 4 wavefronts with a prefetch
+// buffer); smaller heads take 4 with the prefetch buffer.
+// ABGQA_DECODE_WAVES (4 or 8) overrides the choice (tuning).
+static int decode_waves(int D) {
   static const int forced = [] {
     const char* v = getenv("ABGQA_DECODE_WAVES");
     return v ? atoi(v) : 0;
   }();
-  return forced == 8 ? 8 : 4;
+  if (forced == 4 || forced == 8) return forced;
+  return D >= 512 ? 8 : 4;
 }
 
 template <int D, int NR, int NW>
@@ -576,8 +621,14 @@ static void launch_decode_nw(const AttnParams& p, hipStream_t stream) {
 
 template <int D, int NR>
 static hipError_t launch_decode_d(const AttnParams& p, hipStream_t stream) {
-  if (decode_waves() == 8) launch_decode_nw<D, NR, 8>(p, stream);
-  else launch_decode_nw<D, NR, 4>(p, stream);
+  // 8 wavefronts (two per SIMD) only where their registers hold the work
+  // without spilling: up to 4 rows per lane group
+  if constexpr (NR <= 4) {
+    if (decode_waves(D) == 8) launch_decode_nw<D, NR, 8>(p, stream);
+    else launch_decode_nw<D, NR, 4>(p, stream);
+  } else {
+    launch_decode_nw<D, NR, 4>(p, stream);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_launch_detail("decode kernel launch");

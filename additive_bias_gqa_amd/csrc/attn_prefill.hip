@@ -34,54 +34,13 @@
 // The next tile's bias values (registers) and K/V (registers, then LDS) are
 // fetched while the current tile is computed; the bias loads are issued first
 // so that waiting for them never waits for the K/V loads behind them.
-#include "common.h"
-#include "kernels.h"
-#include "mask_rules.h"
+#include <stdlib.h>
+
+#include "prefill_common.h"
 
 namespace abgqa {
 
 namespace {
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kTileKeys = 32;
-constexpr float kRescaleThreshold = 8.f;
-
-__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// gfx950 transposing LDS read: within each group of 16 lanes, lane i receives
-// element (i % 4) of the 4-element (8-byte) row addressed by lane 4*k + i/4 of
-// the same group, for k = 0..3.
-__device__ __forceinline__ u32x2 lds_read_tr16(const __bf16* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p));
-  return __builtin_bit_cast(u32x2, v);
-}
-
-// element offset of 16-byte chunk c of row r in a swizzled [rows][D] tile
-template <int D>
-__device__ __forceinline__ int swz(int r, int c) {
-  return r * D + 8 * (c ^ (r & 7));
-}
-
-__host__ __device__ inline int num_tiles(int n) { return (n + kTileKeys - 1) / kTileKeys; }
-
-template <typename BiasT>
-__device__ __forceinline__ bool live_bits(BiasT v);
-template <>
-__device__ __forceinline__ bool live_bits<uint16_t>(uint16_t v) { return v != 0xFF80; }
-template <>
-__device__ __forceinline__ bool live_bits<uint32_t>(uint32_t v) { return v != 0xFF800000u; }
-
-template <typename BiasT>
-__device__ __forceinline__ float bias_f32(BiasT v);
-template <>
-__device__ __forceinline__ float bias_f32<uint16_t>(uint16_t v) { return bf16_bits_to_f32(v); }
-template <>
-__device__ __forceinline__ float bias_f32<uint32_t>(uint32_t v) { return __uint_as_float(v); }
 
 // 4 consecutive bias values of one row, packed (bf16: 2 words, fp32: 4 words)
 template <typename BiasT> struct Bias4;
@@ -132,110 +91,6 @@ size_t prefill_lds_bytes(int D, int max_seq) {
   return 2 * stage + ((words + list + 15) & ~(size_t)15);
 }
 
-// The live 32-key tiles of one workgroup's query rows [s0, s_end): tiles below
-// nonpad that hold an allowed entry for one of the rows. Bias variant: scanned
-// from the bias rows. Rules variant: the causal/window range of the rows plus
-// every tile holding a slot of an image block that one of the rows belongs to
-// (up to 4 distinct blocks; more makes every tile live). Skipping a dead tile
-// is exact: its keys contribute exactly zero. Returns the count; the tile
-// indices are in s_list[0 .. count).
-template <int NT, bool kRules, typename BiasT>
-__device__ int build_live_list(const AttnParams& p, int64_t b, int np, int s0, int s_end, int n_kt,
-                               uint32_t* s_bits, uint16_t* s_list, int n_words, int32_t* s_ids,
-                               int* s_nids_p, int* s_nlive_p) {
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
-  const int T = p.T;
-  int& s_nids = *s_nids_p;
-  int& s_nlive = *s_nlive_p;
-  for (int i = tid; i < n_words; i += NT) s_bits[i] = 0u;
-  if (tid == 0) { s_nids = 0; s_nlive = 0; }
-  if (tid < 4) s_ids[tid] = -1;  // never a block id: a racing reader cannot match it
-  __syncthreads();
-  if constexpr (!kRules) {
-    constexpr int EPV = 16 / sizeof(BiasT);
-    const int nvec = (np + EPV - 1) / EPV;
-    const bool vec = (T % EPV) == 0;
-    const BiasT* bb = (const BiasT*)p.bias + (b * p.S_q) * (int64_t)T;
-    const int total = (s_end - s0) * nvec;
-#pragma unroll 4
-    for (int idx = tid; idx < total; idx += NT) {
-      const int s = s0 + idx / nvec;
-      const int j0 = (idx % nvec) * EPV;
-      const BiasT* row = bb + (int64_t)s * T;
-      BiasT vals[EPV];
-      if (vec) {
-        *reinterpret_cast<u32x4*>(vals) = ld_global<u32x4>(row + j0);
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) vals[e] = (j0 + e < T) ? row[j0 + e] : (BiasT)0;
-      }
-      bool any = false;
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) any |= (j0 + e < np) && live_bits<BiasT>(vals[e]);
-      if (any) {
-        const int t = j0 / kTileKeys;   // EPV divides the tile size
-        atomicOr(&s_bits[t >> 5], 1u << (t & 31));
-      }
-    }
-  } else {
-    // causal + window: keys [q_first - W + 1, q_last] (q consecutive over rows)
-    if (tid == 0 && s_end > s0) {
-      const RowRule r0 = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s0, p.S_q, T, p.window);
-      const int64_t q_last = r0.q + (s_end - 1 - s0);
-      int64_t a = (p.window > 0) ? r0.q - p.window + 1 : 0;
-      if (a < 0) a = 0;
-      const int64_t z = q_last < (int64_t)np - 1 ? q_last : (int64_t)np - 1;
-      if (a <= z) {
-        for (int t = (int)(a / kTileKeys); t <= (int)(z / kTileKeys); ++t)
-          s_bits[t >> 5] |= 1u << (t & 31);
-      }
-    }
-    // image blocks of the rows (up to 4 distinct ids; more: every tile is live)
-    if (p.slot_kind) {
-      for (int s = s0 + tid; s < s_end; s += NT) {
-        const RowRule rr = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s, p.S_q, T, p.window);
-        if (rr.kind_q > 0) {
-          bool seen = false;
-          for (int i = 0; i < 4; ++i) seen |= (i < s_nids) && (s_ids[i] == rr.kind_q);
-          if (!seen) {
-            const int slot = atomicAdd(&s_nids, 1);
-            if (slot < 4) s_ids[slot] = rr.kind_q;
-          }
-        }
-      }
-    }
-    __syncthreads();
-    const int nids = s_nids;
-    if (nids > 4) {
-      for (int t = tid; t < n_kt; t += NT) atomicOr(&s_bits[t >> 5], 1u << (t & 31));
-    } else if (nids > 0) {
-      const int32_t* kr = p.slot_kind + b * T;
-      for (int j = tid; j < np; j += NT) {
-        const int32_t kj = kr[j];
-        bool hit = false;
-        for (int i = 0; i < nids; ++i) hit |= (kj == s_ids[i]);
-        if (hit) atomicOr(&s_bits[(j / kTileKeys) >> 5], 1u << ((j / kTileKeys) & 31));
-      }
-    }
-  }
-  __syncthreads();
-  // compact the bitmap into a list (wavefront 0, 64 tiles per step)
-  if (w == 0) {
-    int base = 0;
-    for (int t0 = 0; t0 < n_kt; t0 += 64) {
-      const int t = t0 + lane;
-      const bool live = (t < n_kt) && ((s_bits[t >> 5] >> (t & 31)) & 1u);
-      const uint64_t mask = __ballot(live);
-      const int pos = __popcll(mask & ((1ull << lane) - 1ull));
-      if (live) s_list[base + pos] = (uint16_t)t;
-      base += __popcll(mask);
-    }
-    if (lane == 0) s_nlive = base;
-  }
-  __syncthreads();
-  return s_nlive;
-}
 
 
 template <int D, int NW, bool kRules, typename BiasT>
@@ -792,7 +647,19 @@ static hipError_t launch_prefill_d(const AttnParams& p, hipStream_t stream) {
   }
 }
 
+// ABGQA_PREFILL_PATH=reg keeps every launch on the register-staged kernels of
+// this file (comparison and tuning); by default shapes whose rows allow 16-byte
+// direct-to-LDS fetches take attn_prefill_dma.hip.
+static bool force_register_path() {
+  static const bool v = [] {
+    const char* e = getenv("ABGQA_PREFILL_PATH");
+    return e != nullptr && e[0] == 'r';
+  }();
+  return v;
+}
+
 hipError_t launch_attn_prefill(const AttnParams& p, hipStream_t stream) {
+  if (!force_register_path() && prefill_dma_supported(p)) return launch_attn_prefill_dma(p, stream);
   if (prefill_lds_bytes(p.D, p.T) > 160 * 1024) return hipErrorInvalidValue;
   switch (p.D) {
     case 64: return launch_prefill_d<64>(p, stream);

@@ -51,6 +51,9 @@ hipError_t launch_attn_decode(const AttnParams& p, hipStream_t stream);
 // bf16 prefill path: matrix-core tiles, K/V tiles in LDS shared by the G heads.
 // Returns hipErrorInvalidValue when the shape needs more LDS than a CU has.
 hipError_t launch_attn_prefill(const AttnParams& p, hipStream_t stream);
+// direct-to-LDS prefill pipeline (attn_prefill_dma.hip) and when it applies
+bool prefill_dma_supported(const AttnParams& p);
+hipError_t launch_attn_prefill_dma(const AttnParams& p, hipStream_t stream);
 size_t prefill_lds_bytes(int D, int max_seq);
 
 }  // namespace abgqa
