@@ -32,9 +32,18 @@ FLAGS = [
 ]
 
 
+# Per-file additions. attn_prefill_dma.hip: matrix-core accumulators in the
+# ordinary vector registers (its O^T accumulators and every other value of the
+# loop fit in 256 of them), so the compiler does not copy the accumulators
+# between register files around the rare rescale branch on every tile.
+FILE_FLAGS = {
+    "attn_prefill_dma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -19,7 +19,7 @@
 //              from the bias, or derived from the rules). Skipping is exact:
 //              a masked key contributes exactly zero.
 //   LDS        per tile, K and V row-major [32][D] bf16, 16-byte chunks XOR-
-//              swizzled by (row & 7) against bank conflicts; double-buffered.
+//              swizzled by swz_bits<D>(row) against bank conflicts; double-buffered.
 //   S^T = K Q^T    32x32x16 bf16 MFMA: A = K rows from LDS, B = Q^T held in
 //                  registers for the whole loop. Result lane l: query row
 //                  (l % 32), keys 8*i + 4*(l/32) + j (i, j < 4).

@@ -31,12 +31,15 @@
 // the slots past nonpad are never read.
 //
 // The swizzle of the K/V tiles is the one attn_prefill.hip uses: LDS chunk
-// position c of row r holds global chunk c ^ (r & 7), so a wavefront fetching
-// one row's chunks in order writes them permuted, for free.
+// position c of row r holds global chunk c ^ swz_bits<D>(r), so a wavefront
+// fetching one row's chunks in order writes them permuted, for free.
 //
 // RW = 32: 32-row wavefronts on 32x32x16 MFMAs (D <= 256); RW = 16: 16-row
 // wavefronts on 16x16x32 MFMAs (D = 512, where Q^T and O^T of 32 rows would not
 // fit a lane's registers). The compute per tile is that of attn_prefill.hip.
+#include <stdlib.h>
+#include <string.h>
+
 #include <type_traits>
 
 #include "prefill_common.h"
@@ -53,8 +56,10 @@ namespace {
 // s_waitcnt below. M0 carries the LDS address (one wait state after writing
 // it) and is restored afterwards.
 __device__ __forceinline__ void dma16(const void* gsrc, const unsigned char* lds_wave_base) {
-  const unsigned lds =
-      (unsigned)(size_t)((__attribute__((address_space(3))) const unsigned char*)lds_wave_base);
+  // wave-uniform by construction; readfirstlane makes that visible to the
+  // compiler, which must place it in a scalar register
+  const unsigned lds = __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)((__attribute__((address_space(3))) const unsigned char*)lds_wave_base));
   unsigned saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -64,6 +69,23 @@ __device__ __forceinline__ void dma16(const void* gsrc, const unsigned char* lds
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(gsrc), "s"(lds));
+}
+
+// The same fetch from a wave-uniform base address plus a per-lane 32-bit byte
+// offset (the scalar-base form: no per-lane address arithmetic).
+__device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff,
+                                        const unsigned char* lds_wave_base) {
+  const unsigned lds = __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)((__attribute__((address_space(3))) const unsigned char*)lds_wave_base));
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds));
 }
 
 // s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
@@ -84,6 +106,26 @@ __device__ __forceinline__ void tile_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+
+// 32-bit LDS address of a generic pointer into shared memory
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)((__attribute__((address_space(3))) const void*)p);
+}
+
+// LDS reads at base + cofs. Bases are masked to 20 bits where they are formed
+// (LDS addresses are below 160 KiB), so the compiler knows base + cofs cannot
+// wrap and puts a constant cofs into the instruction's offset field instead of
+// adding it in a vector register for every read.
+template <typename T>
+__device__ __forceinline__ T lds_at(unsigned base, unsigned cofs) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T*>((size_t)(base + cofs));
+}
+__device__ __forceinline__ u32x2 lds_tr16_at(unsigned base, unsigned cofs) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s16x4*>((size_t)(base + cofs)));
+  return __builtin_bit_cast(u32x2, v);
+}
+constexpr unsigned kLdsMask = (1u << 20) - 1;
 
 constexpr int kLdsBudget = 160 * 1024 - 6 * 1024;   // stages; the rest: live list
 
@@ -172,8 +214,11 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   }
 
   // ---- 2. live tiles ---------------------------------------------------------
-  const int n_live = build_live_list<NT, kRules, BiasT>(p, b, np, s0, s_end, n_kt, s_bits, s_list,
-                                                       n_words, s_ids, &s_nids, &s_nlive);
+  // read from LDS, the count is the same in every lane: say so, so that the
+  // loop below (and every LDS address derived from its counter) is scalar
+  const int n_live = __builtin_amdgcn_readfirstlane(
+      build_live_list<NT, kRules, BiasT>(p, b, np, s0, s_end, n_kt, s_bits, s_list, n_words, s_ids,
+                                         &s_nids, &s_nlive));
   // nothing may be pending in registers once the pipeline starts: every wait
   // in the loop below is the explicit one
   wait_vmcnt<0>();
@@ -194,34 +239,80 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   constexpr int RPI = 64 / CPR;             // K/V rows per fetch
   static_assert(NKI % NW == 0 && 64 % CPR == 0 && PW == 2 * KPW + MPW, "fetch layout");
   const int lrow = lane / CPR, lcc = lane % CPR;
-  auto fetch_stage = [&](int t_idx, int stage) {
-    const int tt = min(t_idx, n_live - 1);
-    const int j0 = (int)s_list[tt] * kTileKeys;
-    unsigned char* sb = stages + stage * STAGE_BYTES;
+  // byte offsets of this lane's chunks within a tile fully below nonpad, from
+  // the tile's first row (K and V alike) / first bias row / first slot kind
+  unsigned kv_off[KPW];
 #pragma unroll
-    for (int k = 0; k < KPW; ++k) {
-      const int ii = w * KPW + k;
-      const int kr = ii * RPI + lrow;           // tile row of this lane's chunk
-      const int64_t off = (int64_t)min(j0 + kr, np - 1) * D + 8 * (lcc ^ (kr & 7));
-      dma16(kg + off, sb + ii * 1024);
-      dma16(vg + off, sb + TILE_BYTES + ii * 1024);
+  for (int k = 0; k < KPW; ++k) {
+    const int kr = (w * KPW + k) * RPI + lrow;
+    kv_off[k] = (unsigned)(kr * D + 8 * (lcc ^ swz_bits<D>(kr))) * 2u;
+  }
+  unsigned m_off[MPW];
+#pragma unroll
+  for (int m = 0; m < MPW; ++m) {
+    if constexpr (kRules) {
+      m_off[m] = 16u * (unsigned)(lane & 7);    // lanes 8.. repeat lanes 0..7
+    } else {
+      constexpr int EPV = 16 / (int)sizeof(BiasT);
+      constexpr int CB = Geo::BROW / 16;       // 16-byte chunks per bias row
+      const int c = min(w * MPW + m, NMI - 1) * 64 + lane;
+      const int row = min(s0 + c / CB, p.S_q - 1) - s0;
+      m_off[m] = (unsigned)(row * T + (c % CB) * EPV) * (unsigned)sizeof(BiasT);
     }
-#pragma unroll
-    for (int m = 0; m < MPW; ++m) {
-      const int ii = min(w * MPW + m, NMI - 1);   // surplus fetches repeat the last one
-      unsigned char* dst = sb + 2 * TILE_BYTES + ii * 1024;
-      if constexpr (kRules) {
-        // the tile's 32 slot kinds (128 bytes; lanes 8.. fetch clamped copies)
-        dma16(kindb ? (const void*)(kindb + min(j0 + 4 * lane, T - 4)) : (const void*)kg, dst);
+  }
+  // fetch f of this wavefront's PW for the tile starting at key j0 into the
+  // stage at sb: f < 2*KPW are K and V rows (K for even f), the rest bias rows
+  // or slot kinds. f is a compile-time constant at every call.
+  auto fetch_one = [&](const int f, const int j0, unsigned char* sb) {
+    if (j0 + kTileKeys <= np) {
+      // the usual case: every row of the tile is valid, uniform base + offsets
+      if (f < 2 * KPW) {
+        const int k = f >> 1;
+        const int ii = w * KPW + k;
+        if ((f & 1) == 0) dma16_s(kg + (int64_t)j0 * D, kv_off[k], sb + ii * 1024);
+        else dma16_s(vg + (int64_t)j0 * D, kv_off[k], sb + TILE_BYTES + ii * 1024);
       } else {
-        constexpr int EPV = 16 / (int)sizeof(BiasT);
-        constexpr int CB = Geo::BROW / 16;     // 16-byte chunks per bias row
-        const int c = ii * 64 + lane;
-        const int row = c / CB, cc = c % CB;
-        const int srow = min(s0 + row, p.S_q - 1);
-        dma16(biasb + (int64_t)srow * T + min(j0 + cc * EPV, T - EPV), dst);
+        const int m = f - 2 * KPW;
+        const int ii = min(w * MPW + m, NMI - 1);   // surplus fetches repeat the last one
+        const void* mb;
+        if constexpr (kRules) mb = kindb ? (const void*)(kindb + j0) : (const void*)kg;
+        else mb = biasb + (int64_t)s0 * T + j0;
+        dma16_s(mb, m_off[m], sb + 2 * TILE_BYTES + ii * 1024);
+      }
+    } else {
+      // the tile crossing nonpad: rows at or past it are fetched from row
+      // nonpad - 1; bias / kind chunks past the cache end from its last chunk
+      if (f < 2 * KPW) {
+        const int k = f >> 1;
+        const int ii = w * KPW + k;
+        const int kr = ii * RPI + lrow;
+        const int64_t off = (int64_t)min(j0 + kr, np - 1) * D + 8 * (lcc ^ swz_bits<D>(kr));
+        if ((f & 1) == 0) dma16(kg + off, sb + ii * 1024);
+        else dma16(vg + off, sb + TILE_BYTES + ii * 1024);
+      } else {
+        const int m = f - 2 * KPW;
+        const int ii = min(w * MPW + m, NMI - 1);
+        unsigned char* dst = sb + 2 * TILE_BYTES + ii * 1024;
+        if constexpr (kRules) {
+          dma16(kindb ? (const void*)(kindb + min(j0 + 4 * (lane & 7), T - 4)) : (const void*)kg, dst);
+        } else {
+          constexpr int EPV = 16 / (int)sizeof(BiasT);
+          constexpr int CB = Geo::BROW / 16;
+          const int c = ii * 64 + lane;
+          const int srow = min(s0 + c / CB, p.S_q - 1);
+          dma16(biasb + (int64_t)srow * T + min(j0 + (c % CB) * EPV, T - EPV), dst);
+        }
       }
     }
+  };
+  auto tile_key0 = [&](int t_idx) {
+    return __builtin_amdgcn_readfirstlane((int)s_list[min(t_idx, n_live - 1)] * kTileKeys);
+  };
+  auto fetch_stage = [&](int t_idx, int stage) {
+    const int j0 = tile_key0(t_idx);
+    unsigned char* sb = stages + stage * STAGE_BYTES;
+#pragma unroll
+    for (int f = 0; f < PW; ++f) fetch_one(f, j0, sb);
   };
 
   // ---- 4. main loop ---------------------------------------------------------
@@ -244,66 +335,170 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
         const int qr = c / CPR, cc = c % CPR;
         const int qs = min(s0 + qr / G, p.S_q - 1);
         const int qh = hk * G + qr % G;
-        dma16((const __bf16*)p.q + ((b * p.Hq + qh) * p.S_q + qs) * (int64_t)D + 8 * (cc ^ (qr & 7)),
+        dma16((const __bf16*)p.q + ((b * p.Hq + qh) * p.S_q + qs) * (int64_t)D + 8 * (cc ^ swz_bits<D>(qr)),
               smem + ii * 1024);
       }
     }
 #pragma unroll
     for (int st = 0; st < NSTAGE - 1; ++st) fetch_stage(st, st);
   }
-  const __bf16* qs_lds = reinterpret_cast<const __bf16*>(smem);
+  // Per-lane byte offsets into the swizzled tiles. Chunk c of row r sits at
+  // 16 * (c ^ swz_bits<D>(r)); the XOR touches only the low SWB bits of c, so the
+  // reads of one lane need a few base offsets (by those low bits of c) plus
+  // compile-time multiples of SPAN = 16 << SWB bytes.
+  constexpr int SWB = swz_width<D>();
+  constexpr int SPAN = 16 << SWB;
+  // RW = 32: K/Q chunk 2*i + grp -> groups i % NKG; V chunk 4*blk + vdofs/8 ->
+  // groups blk % NVG, times the two 8-row halves (the swizzle sees row bit 3).
+  // RW = 16: K chunk 4*i + grp -> groups i % NKG; V chunk 2*blk + vdofs/8 ->
+  // groups blk % NVG.
+  constexpr int NKG = RW == 32 ? (1 << SWB) / 2 : (1 << SWB) / 4;
+  constexpr int NVG = RW == 32 ? (1 << SWB) / 4 : (1 << SWB) / 2;
+  unsigned k_lane[NKG];                  // K (and, RW = 32, Q) rows
+  unsigned v_lane[RW == 32 ? 2 : 1][NVG];  // V^T transposing reads
+  if constexpr (RW == 32) {
+    // S^T: lane reads row col, chunk 2*i + grp
+#pragma unroll
+    for (int m = 0; m < NKG; ++m)
+      k_lane[m] = (unsigned)(col * D * 2 + 16 * ((2 * m + grp) ^ swz_bits<D>(col)));
+    // PV: lane 16*gq + 4*kq + jq reads row 16*step + 8*half + vkey0, d = 32*blk +
+    // vdofs: chunk 4*blk + vdofs/8
+    const int gq = lane >> 4, kq = (lane >> 2) & 3, jq = lane & 3;
+    const int vkey0 = 4 * (gq >> 1) + kq;
+    const int vdofs = 16 * (gq & 1) + 4 * jq;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int m = 0; m < NVG; ++m) {
+        const int row = 8 * hf + vkey0;
+        v_lane[hf][m] = (unsigned)(row * D * 2 + 16 * ((4 * m + (vdofs >> 3)) ^ swz_bits<D>(row)) +
+                                   2 * (vdofs & 7));
+      }
+  } else {
+    // S^T: row 16*kb + col, chunk 4*i + grp
+#pragma unroll
+    for (int m = 0; m < NKG; ++m)
+      k_lane[m] = (unsigned)(col * D * 2 + 16 * ((4 * m + grp) ^ swz_bits<D>(col)));
+    // PV: lane 16*g + 4*k + j reads row vkey0 (+16), d = 16*blk + vdofs:
+    // chunk 2*blk + vdofs/8
+    const int vkey0 = lane >> 2;
+    const int vdofs = 4 * (lane & 3);
+#pragma unroll
+    for (int m = 0; m < NVG; ++m)
+      v_lane[0][m] = (unsigned)(vkey0 * D * 2 + 16 * ((2 * m + (vdofs >> 3)) ^ swz_bits<D>(vkey0)) +
+                                2 * (vdofs & 7));
+  }
+  // this wavefront's Q rows (RW = 32), one base per k-chunk group
+  unsigned q_base[RW == 32 ? NKG : 1];
+  if constexpr (RW == 32) {
+    const unsigned qa0 = lds_addr(smem) + (unsigned)(RW * w * D * 2);
+#pragma unroll
+    for (int m = 0; m < NKG; ++m) q_base[m] = (qa0 + k_lane[m]) & kLdsMask;
+  }
   for (int t = 0; t < n_live; ++t) {
     wait_vmcnt<PW * (NSTAGE - 2)>();
     tile_barrier();
     fetch_stage(t + NSTAGE - 1, (t + NSTAGE - 1) % NSTAGE);
 
-    const int j0 = (int)s_list[t] * kTileKeys;
+    const int j0 = __builtin_amdgcn_readfirstlane((int)s_list[t] * kTileKeys);
     const unsigned char* sb = stages + (t % NSTAGE) * STAGE_BYTES;
     const bool full = j0 + kTileKeys <= np;   // no key of the tile at or past nonpad
-    const __bf16* ks = reinterpret_cast<const __bf16*>(sb);
-    const __bf16* vs = reinterpret_cast<const __bf16*>(sb + TILE_BYTES);
     const unsigned char* ms = sb + 2 * TILE_BYTES;
+    const unsigned sb_a = lds_addr(sb);
+    unsigned k_base[NKG], v_base[RW == 32 ? 2 : 1][NVG];
+#pragma unroll
+    for (int m = 0; m < NKG; ++m) k_base[m] = (sb_a + k_lane[m]) & kLdsMask;
+#pragma unroll
+    for (int hf = 0; hf < (RW == 32 ? 2 : 1); ++hf)
+#pragma unroll
+      for (int m = 0; m < NVG; ++m) v_base[hf][m] = (sb_a + TILE_BYTES + v_lane[hf][m]) & kLdsMask;
 
     if constexpr (RW == 32) {
+      // this lane's bias values (or slot kinds) for keys 8*i + 4*(l/32) + jj,
+      // read first so their latency hides under the S^T MFMAs
+      BiasT bvs[4][4];
+      int32_t kvs[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kb = 8 * i + 4 * grp;
+        if constexpr (kRules) {
+          if (kindb) *reinterpret_cast<int4*>(kvs[i]) = *reinterpret_cast<const int4*>(ms + 4 * kb);
+          else *reinterpret_cast<int4*>(kvs[i]) = int4{0, 0, 0, 0};
+        } else {
+          const BiasT* br = reinterpret_cast<const BiasT*>(ms) + sl * kTileKeys + kb;
+          if constexpr (sizeof(BiasT) == 2) *reinterpret_cast<u32x2*>(bvs[i]) = *reinterpret_cast<const u32x2*>(br);
+          else *reinterpret_cast<u32x4*>(bvs[i]) = *reinterpret_cast<const u32x4*>(br);
+        }
+      }
       // S^T = K Q^T; lane l: query row l % 32, keys 8*i + 4*(l/32) + jj
+      // fragments of k-step i + PD are read while the MFMA of step i runs
+      constexpr int PD = KSTEPS < 4 ? KSTEPS : 4;
       f32x16 sacc = f32x16{};
+      bf16x8 ka[PD], qa[PD];
+#pragma unroll
+      for (int i = 0; i < PD; ++i) {
+        ka[i] = lds_at<bf16x8>(k_base[i % NKG], SPAN * (i / NKG));
+        qa[i] = lds_at<bf16x8>(q_base[i % NKG], SPAN * (i / NKG));
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD, 0);
 #pragma unroll
       for (int i = 0; i < KSTEPS; ++i) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + swz<D>(col, 2 * i + grp));
-        const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qs_lds + swz<D>(r, 2 * i + grp));
+        const bf16x8 a = ka[i % PD], qb = qa[i % PD];
+        if (i + PD < KSTEPS) {
+          ka[i % PD] = lds_at<bf16x8>(k_base[(i + PD) % NKG], SPAN * ((i + PD) / NKG));
+          qa[i % PD] = lds_at<bf16x8>(q_base[(i + PD) % NKG], SPAN * ((i + PD) / NKG));
+        }
         sacc = mfma32x32x16(a, qb, sacc);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + PD < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+      // V^T fragments of the first PV MFMAs, read while the softmax runs.
+      // MFMA u = 2*blk + step; lane 16*gq + 4*kq + jq reads
+      // V[16*step + 8*half + 4*(gq/2) + kq][32*blk + 16*(gq%2) + 4*jq]
+      constexpr int NU = 2 * DBLK;
+      constexpr int PVD = NU < 4 ? NU : 4;
+      auto vread = [&](int u) {
+        const int blk = u >> 1;
+        const unsigned so = SPAN * (blk / NVG) + 16 * (u & 1) * D * 2;
+        const u32x2 lo = lds_tr16_at(v_base[0][blk % NVG], so);
+        const u32x2 hi = lds_tr16_at(v_base[1][blk % NVG], so);
+        return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+      };
+      bf16x8 vf[PVD];
+#pragma unroll
+      for (int u = 0; u < PVD; ++u) vf[u] = vread(u);
       float x[16];
       float mt = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int kb = 8 * i + 4 * grp;          // first of this lane's 4 keys
-        BiasT bv[4];
-        int32_t kv[4] = {0, 0, 0, 0};
-        if constexpr (kRules) {
-          if (kindb) *reinterpret_cast<int4*>(kv) = *reinterpret_cast<const int4*>(ms + 4 * kb);
-        } else {
-          const BiasT* br = reinterpret_cast<const BiasT*>(ms) + sl * kTileKeys + kb;
-          if constexpr (sizeof(BiasT) == 2) *reinterpret_cast<u32x2*>(bv) = *reinterpret_cast<const u32x2*>(br);
-          else *reinterpret_cast<u32x4*>(bv) = *reinterpret_cast<const u32x4*>(br);
-        }
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int j = j0 + kb + jj;
           float v;
           if constexpr (kRules) {
             // allowed() includes j < nonpad; a row past the chunk has no rule
-            v = rule.allowed(j, kv[jj]) ? sacc[4 * i + jj] * scale_log2 : -INFINITY;
+            v = rule.allowed(j, kvs[i][jj]) ? sacc[4 * i + jj] * scale_log2 : -INFINITY;
           } else {
             // a -inf bias gives -inf (the score is finite: every fetched key row
             // is a valid row); keys at or past nonpad only in a partial tile
-            v = fmaf(sacc[4 * i + jj], scale_log2, bias_f32<BiasT>(bv[jj]) * kLog2e);
-            if (!full && j >= np) v = -INFINITY;
+            v = fmaf(sacc[4 * i + jj], scale_log2, bias_f32<BiasT>(bvs[i][jj]) * kLog2e);
           }
           x[4 * i + jj] = v;
-          mt = fmaxf(mt, v);
         }
       }
+      if constexpr (!kRules) {
+        if (!full) {
+          // the tile crossing nonpad: keys at or past it are not keys (a real
+          // branch, taken at most once per workgroup)
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (j0 + 8 * (e >> 2) + 4 * grp + (e & 3) >= np) x[e] = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, x[e]);
       mt = fmaxf(mt, lane_xor(mt, 32));
       const float mn = fmaxf(m_run, mt);
       const bool need = mn > m_run + kRescaleThreshold;
@@ -337,65 +532,93 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
 #pragma unroll
         for (int blk = 0; blk < DBLK; ++blk) oacc[blk] *= alpha;
       }
-      // O^T += V^T P^T; V^T from transposing reads: lane 16*gq + 4*kq + jq
-      // reads V[16*step + 8*half + 4*(gq/2) + kq][32*blk + 16*(gq%2) + 4*jq]
-      const int gq = lane >> 4, kq = (lane >> 2) & 3, jq = lane & 3;
-      const int vkey0 = 4 * (gq >> 1) + kq;
-      const int vdofs = 16 * (gq & 1) + 4 * jq;
+      // O^T += V^T P^T, fragments read PVD MFMAs ahead
 #pragma unroll
-      for (int blk = 0; blk < DBLK; ++blk) {
-        const int d = 32 * blk + vdofs;
-        const int c = d >> 3, within = d & 7;
-#pragma unroll
-        for (int step = 0; step < 2; ++step) {
-          const int k0 = 16 * step + vkey0;
-          const u32x2 lo = lds_read_tr16(vs + swz<D>(k0, c) + within);
-          const u32x2 hi = lds_read_tr16(vs + swz<D>(k0 + 8, c) + within);
-          const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-          oacc[blk] = mfma32x32x16(va, step == 0 ? pb0 : pb1, oacc[blk]);
-        }
+      for (int u = 0; u < NU; ++u) {
+        const bf16x8 va = vf[u % PVD];
+        if (u + PVD < NU) vf[u % PVD] = vread(u + PVD);
+        oacc[u >> 1] = mfma32x32x16(va, (u & 1) ? pb1 : pb0, oacc[u >> 1]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (u + PVD < NU) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     } else {
+      // this lane's bias values (or slot kinds) for keys 16*kb + 4*(l/16) + e,
+      // read first so their latency hides under the S^T MFMAs
+      BiasT bvs[2][4];
+      int32_t kvs[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kf = 16 * kb + 4 * grp;
+        if constexpr (kRules) {
+          if (kindb) *reinterpret_cast<int4*>(kvs[kb]) = *reinterpret_cast<const int4*>(ms + 4 * kf);
+          else *reinterpret_cast<int4*>(kvs[kb]) = int4{0, 0, 0, 0};
+        } else {
+          const BiasT* br = reinterpret_cast<const BiasT*>(ms) + sl * kTileKeys + kf;
+          if constexpr (sizeof(BiasT) == 2) *reinterpret_cast<u32x2*>(bvs[kb]) = *reinterpret_cast<const u32x2*>(br);
+          else *reinterpret_cast<u32x4*>(bvs[kb]) = *reinterpret_cast<const u32x4*>(br);
+        }
+      }
       // S^T = K Q^T in two 16-key halves; lane l: query row l % 16, keys
       // 16*kb + 4*(l/16) + e
       f32x4 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        constexpr int PD = 8;   // K fragments read PD steps ahead of their MFMA
+        bf16x8 ka[PD];
+#pragma unroll
+        for (int i = 0; i < PD; ++i)
+          ka[i] = lds_at<bf16x8>(k_base[i % NKG], SPAN * (i / NKG) + kb * 16 * D * 2);
+        __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
 #pragma unroll
         for (int i = 0; i < KSTEPS; ++i) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + swz<D>(16 * kb + col, 4 * i + grp));
+          const bf16x8 a = ka[i % PD];
+          if (i + PD < KSTEPS)
+            ka[i % PD] = lds_at<bf16x8>(k_base[(i + PD) % NKG], SPAN * ((i + PD) / NKG) + kb * 16 * D * 2);
           sacc[kb] = mfma16x16x32(a, qf[i], sacc[kb]);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i + PD < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       }
+      // V^T fragments of the first PV MFMAs, read while the softmax runs;
+      // lane 16*gq + 4*kq + jq reads V[4*gq + kq (+16)][16*blk + 4*jq]
+      constexpr int PVD = 4;
+      auto vread = [&](int blk) {
+        const unsigned so = SPAN * (blk / NVG);
+        const u32x2 lo = lds_tr16_at(v_base[0][blk % NVG], so);
+        const u32x2 hi = lds_tr16_at(v_base[0][blk % NVG], so + 16 * D * 2);
+        return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+      };
+      bf16x8 vf[PVD];
+#pragma unroll
+      for (int u = 0; u < PVD; ++u) vf[u] = vread(u);
       float x[8];
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int kf = 16 * kb + 4 * grp;
-        BiasT bv[4];
-        int32_t kv[4] = {0, 0, 0, 0};
-        if constexpr (kRules) {
-          if (kindb) *reinterpret_cast<int4*>(kv) = *reinterpret_cast<const int4*>(ms + 4 * kf);
-        } else {
-          const BiasT* br = reinterpret_cast<const BiasT*>(ms) + sl * kTileKeys + kf;
-          if constexpr (sizeof(BiasT) == 2) *reinterpret_cast<u32x2*>(bv) = *reinterpret_cast<const u32x2*>(br);
-          else *reinterpret_cast<u32x4*>(bv) = *reinterpret_cast<const u32x4*>(br);
-        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = j0 + kf + e;
           float v;
           if constexpr (kRules) {
-            v = rule.allowed(j, kv[e]) ? sacc[kb][e] * scale_log2 : -INFINITY;
+            v = rule.allowed(j, kvs[kb][e]) ? sacc[kb][e] * scale_log2 : -INFINITY;
           } else {
-            v = fmaf(sacc[kb][e], scale_log2, bias_f32<BiasT>(bv[e]) * kLog2e);
-            if (!full && j >= np) v = -INFINITY;
+            v = fmaf(sacc[kb][e], scale_log2, bias_f32<BiasT>(bvs[kb][e]) * kLog2e);
           }
           x[4 * kb + e] = v;
-          mt = fmaxf(mt, v);
         }
       }
+      if constexpr (!kRules) {
+        if (!full) {
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (j0 + 16 * (e >> 2) + 4 * grp + (e & 3) >= np) x[e] = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mt = fmaxf(mt, x[e]);
       mt = fmaxf(mt, lane_xor(mt, 16));
       mt = fmaxf(mt, lane_xor(mt, 32));
       const float mn = fmaxf(m_run, mt);
@@ -428,17 +651,14 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
 #pragma unroll
         for (int blk = 0; blk < DBLK; ++blk) oacc[blk] *= alpha;
       }
-      // O^T += V^T P^T; lane 16*gq + 4*kq + jq reads V[4*gq + kq (+16)][16*blk + 4*jq]
-      const int vkey0 = lane >> 2;
-      const int vdofs = 4 * (lane & 3);
+      // O^T += V^T P^T, fragments read PVD MFMAs ahead
 #pragma unroll
       for (int blk = 0; blk < DBLK; ++blk) {
-        const int d = 16 * blk + vdofs;
-        const int c = d >> 3, within = d & 7;
-        const u32x2 lo = lds_read_tr16(vs + swz<D>(vkey0, c) + within);
-        const u32x2 hi = lds_read_tr16(vs + swz<D>(16 + vkey0, c) + within);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        const bf16x8 va = vf[blk % PVD];
+        if (blk + PVD < DBLK) vf[blk % PVD] = vread(blk + PVD);
         oacc[blk] = mfma16x16x32(va, pb, oacc[blk]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (blk + PVD < DBLK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     }
   }
@@ -515,13 +735,38 @@ hipError_t launch_dma_v(const AttnParams& p, hipStream_t stream) {
   return launch_dma_inst<D, RW, NW, false, uint32_t>(p, stream);
 }
 
+// ABGQA_PREFILL_CFG (tuning): "32x2", "32x4", "16x4", "16x8" picks rows per
+// wavefront x wavefronts per workgroup; otherwise the default below.
+static int prefill_cfg() {
+  static const int v = [] {
+    const char* e = getenv("ABGQA_PREFILL_CFG");
+    if (!e) return 0;
+    if (!strcmp(e, "32x2")) return 1;
+    if (!strcmp(e, "32x4")) return 2;
+    if (!strcmp(e, "16x4")) return 3;
+    if (!strcmp(e, "16x8")) return 4;
+    return 0;
+  }();
+  return v;
+}
+
 template <int D>
 hipError_t launch_dma_d(const AttnParams& p, hipStream_t stream) {
+  const int cfg = prefill_cfg();
   if constexpr (D >= 512) {
+    if (cfg == 4) return launch_dma_v<D, 16, 8>(p, stream);
     return launch_dma_v<D, 16, 4>(p, stream);
   } else {
-    // 4 wavefronts (128 rows) when that still gives about one workgroup per
-    // CU, else 2 (64 rows)
+    if (cfg == 1) return launch_dma_v<D, 32, 2>(p, stream);
+    if (cfg == 2) return launch_dma_v<D, 32, 4>(p, stream);
+    if constexpr (D >= 128) {   // a tile must split evenly over the wavefronts
+      if (cfg == 3) return launch_dma_v<D, 16, 4>(p, stream);
+      if (cfg == 4) return launch_dma_v<D, 16, 8>(p, stream);
+    }
+    // D >= 128: 4 wavefronts of 16 rows keep all four SIMDs of a CU busy with
+    // one workgroup per CU (64 rows; the LDS holds one workgroup's stages).
+    // D = 64 (a tile too small to split four ways): 32-row wavefronts.
+    if constexpr (D >= 128) return launch_dma_v<D, 16, 4>(p, stream);
     const int64_t wg4 = (int64_t)p.B * p.Hkv * ((p.S_q * (int64_t)p.G + 127) / 128);
     if (wg4 >= 256) return launch_dma_v<D, 32, 4>(p, stream);
     return launch_dma_v<D, 32, 2>(p, stream);

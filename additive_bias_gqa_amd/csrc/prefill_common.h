@@ -30,10 +30,30 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const __bf16* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// XOR pattern applied to the 16-byte chunk index of tile row r (the LDS has
+// 64 banks of 4 bytes: a 16-byte read serves 16 lanes per cycle, a transposing
+// 8-byte read 32 lanes). For rows of at least 16 chunks (D >= 128) it is
+// 4 bits wide and
+//   - over any 16 consecutive rows a permutation of 0..15: 16 lanes reading
+//     one chunk of 16 rows hit 16 distinct 16-byte bank groups;
+//   - over rows 8a..8a+7 it maps the chunk pair {2m, 2m+1} of each row to 16
+//     distinct chunks (16-row transposing reads: 8 rows x 32 bytes);
+//   - over rows 4a..4a+3 it maps the chunk quad {4m..4m+3} of each row to 16
+//     distinct chunks (32-row transposing reads: 4 rows x 64 bytes).
+// Rows of 8 chunks (D = 64) take the 3-bit analogue. A plain r & 7 leaves
+// two- to four-way conflicts on the transposing reads.
+template <int D>
+__device__ __forceinline__ int swz_bits(int r) {
+  if constexpr (D >= 128) return ((r & 3) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+  else return ((r & 3) << 1) | ((r >> 2) & 1);
+}
+template <int D>
+constexpr int swz_width() { return D >= 128 ? 4 : 3; }
+
 // element offset of 16-byte chunk c of row r in a swizzled [rows][D] tile
 template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
-  return r * D + 8 * (c ^ (r & 7));
+  return r * D + 8 * (c ^ swz_bits<D>(r));
 }
 
 __host__ __device__ inline int num_tiles(int n) { return (n + kTileKeys - 1) / kTileKeys; }
