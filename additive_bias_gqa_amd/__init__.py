@@ -8,6 +8,9 @@ library's message on failure. Every step of the computation runs in the HIP
 kernels; there is no fallback: a missing library raises at the first call.
 
     kv_tensor_scatter(cache, update, write_indices)            in place
+    kv_scatter_and_bias(k_cache, v_cache, k_update, v_update, write_indices,
+                        nonpad, q_start, slot_kind, S_q, window, bias=None)
+                                  both scatters + the bias, one launch
     build_static_cache_bias(nonpad, q_start, slot_kind, S_q, max_seq, window,
                             dtype=torch.bfloat16, out=None)     -> bias
     attn_bias_gqa_fwd(q, k_cache, v_cache, bias, nonpad, scale, q_start=None,
@@ -21,7 +24,7 @@ import threading
 
 import torch
 
-__all__ = ["kv_tensor_scatter", "build_static_cache_bias", "attn_bias_gqa_fwd",
+__all__ = ["kv_tensor_scatter", "kv_scatter_and_bias", "build_static_cache_bias", "attn_bias_gqa_fwd",
            "attn_bias_gqa_workspace_bytes", "abgqa_last_error", "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +56,9 @@ def load():
         vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
         lib.kv_tensor_scatter.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, vp]
         lib.kv_tensor_scatter.restype = ctypes.c_int
+        lib.kv_scatter_and_bias.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
+                                            vp, ctypes.c_int, vp, vp, vp, i64, i64, vp]
+        lib.kv_scatter_and_bias.restype = ctypes.c_int
         lib.build_static_cache_bias.argtypes = [vp, ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, vp]
         lib.build_static_cache_bias.restype = ctypes.c_int
         lib.attn_bias_gqa_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
@@ -114,6 +120,44 @@ def kv_tensor_scatter(cache: torch.Tensor, update: torch.Tensor,
     _check(load().kv_tensor_scatter(c, u, w, B, H, T, update.shape[2], D, _DTYPE[cache.dtype],
                                     _stream(cache)), "kv_tensor_scatter")
     return cache
+
+
+def kv_scatter_and_bias(k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        k_update: torch.Tensor, v_update: torch.Tensor,
+                        write_indices: torch.Tensor | None, nonpad: torch.Tensor | None,
+                        q_start: torch.Tensor | None, slot_kind: torch.Tensor | None,
+                        S_q: int, window: int, bias: torch.Tensor | None = None):
+    """kv_tensor_scatter(k_cache, k_update, write_indices),
+    kv_tensor_scatter(v_cache, v_update, write_indices) and, when `bias` is
+    given, build_static_cache_bias(..., out=bias), in one launch."""
+    if k_cache.dim() != 4 or k_update.dim() != 4:
+        raise ValueError("caches and updates must be 4-D [B, Hkv, slots, D]")
+    B, H, T, D = k_cache.shape
+    S_new = k_update.shape[2]
+    for name, t in (("v_cache", v_cache),):
+        if tuple(t.shape) != (B, H, T, D) or t.dtype != k_cache.dtype:
+            raise ValueError(f"{name} must match k_cache")
+    for name, t in (("k_update", k_update), ("v_update", v_update)):
+        if tuple(t.shape) != (B, H, S_new, D) or t.dtype != k_cache.dtype:
+            raise ValueError(f"{name} must be [B, Hkv, S_new, D] of the cache dtype")
+    if k_cache.dtype not in _DTYPE:
+        raise ValueError("caches must be float32 or bfloat16")
+    kc, vc = _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache")
+    ku = _dev(k_update, "k_update") if S_new else None
+    vu = _dev(v_update, "v_update") if S_new else None
+    w = _opt(write_indices, "write_indices", torch.int64, (B,))
+    bp, bdt, npd, qs, sk = None, BF16, None, None, None
+    if bias is not None:
+        if bias.dtype not in _DTYPE:
+            raise ValueError("bias dtype must be float32 or bfloat16")
+        bp, bdt = _dev(bias, "bias", None, (B, 1, S_q, T)), _DTYPE[bias.dtype]
+        npd = _dev(nonpad, "nonpad", torch.int64, (B,))
+        qs = _opt(q_start, "q_start", torch.int64, (B,))
+        sk = _opt(slot_kind, "slot_kind", torch.int32, (B, T))
+    _check(load().kv_scatter_and_bias(kc, vc, ku, vu, w, B, H, T, S_new, D, _DTYPE[k_cache.dtype],
+                                      bp, bdt, npd, qs, sk, int(S_q), int(window),
+                                      _stream(k_cache)), "kv_scatter_and_bias")
+    return bias
 
 
 def build_static_cache_bias(nonpad: torch.Tensor, q_start: torch.Tensor | None,

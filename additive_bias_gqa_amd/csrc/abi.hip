@@ -96,6 +96,49 @@ abgqa_status build_static_cache_bias(void* bias, abgqa_dtype bias_dtype,
   return ABGQA_OK;
 }
 
+abgqa_status kv_scatter_and_bias(void* k_cache, void* v_cache, const void* k_update,
+                                 const void* v_update, const int64_t* write_indices, int64_t B,
+                                 int64_t Hkv, int64_t max_seq, int64_t S_new, int64_t D,
+                                 abgqa_dtype dtype, void* bias, abgqa_dtype bias_dtype,
+                                 const int64_t* nonpad_kv_seqlen, const int64_t* q_start,
+                                 const int32_t* slot_kind, int64_t S_q, int64_t window,
+                                 void* stream) {
+  g_last_error.clear();
+  const char* me = "kv_scatter_and_bias";
+  if (B <= 0 || Hkv <= 0 || max_seq <= 0 || D <= 0)
+    return fail(ABGQA_ERR_INVALID, "%s: B, Hkv, max_seq and D must be positive", me);
+  if (S_new < 0) return fail(ABGQA_ERR_INVALID, "%s: S_new must be >= 0", me);
+  if (max_seq > kMaxSeq) return fail(ABGQA_ERR_UNSUPPORTED, "%s: max_seq above 2^24", me);
+  if (dtype != ABGQA_F32 && dtype != ABGQA_BF16)
+    return fail(ABGQA_ERR_UNSUPPORTED, "%s: dtype must be ABGQA_F32 or ABGQA_BF16", me);
+  const int64_t row_bytes = D * (dtype == ABGQA_F32 ? 4 : 2);
+  if (row_bytes % 16 != 0 || row_bytes > 4096)
+    return fail(ABGQA_ERR_UNSUPPORTED, "%s: D * element size must be a multiple of 16 bytes, at most 4096", me);
+  if (S_new > 0) {
+    if (!k_cache || !v_cache || !k_update || !v_update)
+      return fail(ABGQA_ERR_INVALID, "%s: null cache or update", me);
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_update, 16) ||
+        !aligned(v_update, 16) || (write_indices && !aligned(write_indices, 8)))
+      return fail(ABGQA_ERR_INVALID, "%s: misaligned cache, update or write_indices", me);
+  }
+  if (bias) {
+    if (S_q <= 0) return fail(ABGQA_ERR_INVALID, "%s: S_q must be positive", me);
+    if (bias_dtype != ABGQA_F32 && bias_dtype != ABGQA_BF16)
+      return fail(ABGQA_ERR_UNSUPPORTED, "%s: bias dtype must be ABGQA_F32 or ABGQA_BF16", me);
+    if (!nonpad_kv_seqlen) return fail(ABGQA_ERR_INVALID, "%s: null nonpad_kv_seqlen", me);
+    if (!aligned(bias, 16) || !aligned(nonpad_kv_seqlen, 8) || (q_start && !aligned(q_start, 8)) ||
+        (slot_kind && !aligned(slot_kind, 16)))
+      return fail(ABGQA_ERR_INVALID, "%s: misaligned bias, nonpad, q_start or slot_kind", me);
+  }
+  if (S_new == 0 && !bias) return ABGQA_OK;  // nothing to do
+  const hipError_t e = abgqa::launch_prepare(k_cache, v_cache, k_update, v_update, write_indices, B,
+                                             Hkv, max_seq, S_new, row_bytes, bias,
+                                             bias_dtype == ABGQA_BF16, nonpad_kv_seqlen, q_start,
+                                             slot_kind, S_q, window, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(me, e);
+  return ABGQA_OK;
+}
+
 size_t attn_bias_gqa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q,
                                      int64_t max_seq, int64_t D) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_q <= 0 || max_seq <= 0 || D <= 0 || Hq % Hkv) return 0;

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   constexpr bool kParMerge = NW * NR * D <= 8192;
   __shared__ float s_o[kParMerge ? NW * NR * D : NR * D];
   __shared__ __align__(16) __bf16 s_q[kQinLds ? NR * D : 8];  // Q rows (A operand)
-  __shared__ int s_range[2];
+  __shared__ int s_rlo[kDecWaves], s_rhi[kDecWaves];
   __shared__ int32_t s_kq[16];
 
   const int tid = threadIdx.x;
@@ -159,22 +159,25 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   }
 
   // ---- 1. live range [lo, hi) of keys, over all S_q rows -------------------
-  if (tid == 0) { s_range[0] = INT32_MAX; s_range[1] = -1; }
+  // (no barrier before the scan: a workgroup barrier here would first wait for
+  // the Q loads above, putting two memory round trips ahead of the K/V loads)
   if constexpr (!kParMerge)
     for (int i = tid; i < NR * D; i += kDecThreads) s_o[i] = 0.f;
-  __syncthreads();
   {
     int lo = INT32_MAX, hi = -1;
     if constexpr (!kRules) {
       // NB 16-byte loads per thread in flight at once, unconditional (index
       // clamped to the last vector; the extra copies are discarded below), so
-      // the scan costs one memory round trip per batch, not one per load
+      // the scan costs one memory round trip per batch, not one per load. The
+      // vector path reads whole rows (max_seq keys) and applies j < nonpad
+      // afterwards, so its loads do not wait for nonpad to arrive first.
       const BiasT* bb = (const BiasT*)p.bias + b * p.S_q * (int64_t)T;
       constexpr int EPV = 16 / sizeof(BiasT);  // elements per 16-byte load
       constexpr int NB = 4;
-      const int nvec = (np + EPV - 1) / EPV;
+      const bool vec_rows = (T % EPV) == 0;
+      const int nvec = vec_rows ? T / EPV : (np + EPV - 1) / EPV;
       const int total = p.S_q * nvec;
-      if ((T % EPV) == 0) {
+      if (vec_rows) {
         for (int base = tid; base < total; base += NB * kDecThreads) {
           u32x4 raw[NB];
 #pragma unroll
@@ -237,10 +240,9 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
         }
       }
     }
-    if (hi >= 0) {
-      atomicMin(&s_range[0], lo);
-      atomicMax(&s_range[1], hi);
-    }
+    lo = wave_min_i32(lo);
+    hi = wave_max_i32(hi);
+    if (lane == 0) { s_rlo[w] = lo; s_rhi[w] = hi; }
   }
   if constexpr (kQinLds) {
 #pragma unroll
@@ -251,7 +253,12 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
     }
   }
   __syncthreads();
-  int live_lo = s_range[0], live_hi = s_range[1] + 1;
+  int live_lo = INT32_MAX, live_hi = 0;
+#pragma unroll
+  for (int ww = 0; ww < kDecWaves; ++ww) {
+    live_lo = min(live_lo, s_rlo[ww]);
+    live_hi = max(live_hi, s_rhi[ww] + 1);
+  }
   if (live_hi <= 0) { live_lo = 0; live_hi = 0; }
   const int live = live_hi - live_lo;
   const int per = ((live + p.n_split - 1) / p.n_split + 15) & ~15;

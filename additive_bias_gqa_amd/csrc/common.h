@@ -92,6 +92,18 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // exp2 that maps -inf to exactly 0 (v_exp_f32 does) without NaN for finite input
+// minimum / maximum of an int over the 64 lanes of a wavefront
+__device__ __forceinline__ int wave_min_i32(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ int wave_max_i32(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m));
+  return v;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---- grid mapping ----------------------------------------------------------

@@ -20,6 +20,18 @@ hipError_t launch_bias(void* bias, int bias_is_bf16, const int64_t* nonpad,
                        const int64_t* q_start, const int32_t* slot_kind, int64_t B,
                        int64_t S_q, int64_t max_seq, int64_t window, hipStream_t stream);
 
+// grid sizes of the two (capped, grid-stride)
+int64_t scatter_blocks(int64_t n_rows, int vec_per_row);
+int64_t bias_blocks(int64_t B, int64_t S_q, int64_t max_seq);
+
+// K scatter + V scatter + bias build in one launch (prepare.hip); S_new == 0
+// skips the scatters, bias == null skips the bias.
+hipError_t launch_prepare(void* k_cache, void* v_cache, const void* k_update, const void* v_update,
+                          const int64_t* write_indices, int64_t B, int64_t H, int64_t max_seq,
+                          int64_t S_new, int64_t row_bytes, void* bias, int bias_is_bf16,
+                          const int64_t* nonpad, const int64_t* q_start, const int32_t* slot_kind,
+                          int64_t S_q, int64_t window, hipStream_t stream);
+
 // Everything an attention kernel reads, passed by value.
 struct AttnParams {
   void* out;                 // [B, Hq, S_q, D]

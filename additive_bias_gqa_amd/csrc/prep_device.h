@@ -1,0 +1,97 @@
+// Device bodies of the per-step preparation work, shared by the separate
+// entry points (scatter.hip: TensorScatter; bias.hip: bias build) and by the
+// fused one (prepare.hip: both K and V scatters and the bias in one launch).
+// Each body is a grid-stride loop over its own work items, run by `nblk`
+// workgroups of 256 threads numbered `blk`.
+#pragma once
+
+#include "common.h"
+#include "mask_rules.h"
+
+namespace abgqa {
+
+// TensorScatter (mobius skill "attention-optimization", "In-place KV for ONNX
+// Attention via TensorScatter (static cache)"): update row (b, h, t) lands in
+// cache slot write_indices[b] + t; slots outside [0, max_seq) are dropped. One
+// thread moves 16 bytes; a workgroup covers 256 / vec_per_row rows per step.
+__device__ __forceinline__ void scatter_rows(u32x4* __restrict__ cache,
+                                             const u32x4* __restrict__ update,
+                                             const int64_t* __restrict__ write_indices, int H,
+                                             int max_seq, int S_new, int vec_per_row,
+                                             int64_t n_rows, int64_t blk, int64_t nblk) {
+  const int rows_per_iter = 256 / vec_per_row;
+  const int sub = threadIdx.x / vec_per_row;
+  const int c = threadIdx.x % vec_per_row;
+  if (sub >= rows_per_iter) return;
+  for (int64_t row = blk * rows_per_iter + sub; row < n_rows; row += nblk * rows_per_iter) {
+    const int64_t bh = row / S_new;
+    const int t = (int)(row - bh * S_new);
+    const int64_t b = bh / H;
+    const int64_t slot = (write_indices ? write_indices[b] : 0) + t;
+    if (slot < 0 || slot >= max_seq) continue;  // dropped (no wrap-around)
+    cache[(bh * max_seq + slot) * vec_per_row + c] = update[row * vec_per_row + c];
+  }
+}
+
+// bits of +0.0 / -inf in the bias element type
+template <typename T> struct MaskBits;
+template <> struct MaskBits<uint16_t> {
+  static constexpr uint16_t kZero = 0x0000, kNegInf = 0xFF80;
+};
+template <> struct MaskBits<uint32_t> {
+  static constexpr uint32_t kZero = 0x00000000u, kNegInf = 0xFF800000u;
+};
+
+// Static-cache bias (mobius issue #366, "Mobius-side deliverable"; rule in
+// mask_rules.h). One thread writes 8 consecutive keys of one (b, s) row; `vec`
+// (max_seq % 8 == 0) selects 16-byte kind loads and bias stores.
+template <typename T>
+__device__ __forceinline__ void bias_chunks(T* __restrict__ bias, const int64_t* __restrict__ nonpad,
+                                            const int64_t* __restrict__ q_start,
+                                            const int32_t* __restrict__ slot_kind, int S_q,
+                                            int max_seq, int64_t window, int chunks_per_row,
+                                            int64_t n_chunks, bool vec, int64_t blk, int64_t nblk) {
+  for (int64_t idx = blk * 256 + threadIdx.x; idx < n_chunks; idx += nblk * 256) {
+    const int64_t row = idx / chunks_per_row;
+    const int j0 = (int)(idx - row * chunks_per_row) * 8;
+    const int64_t b = row / S_q;
+    const int s = (int)(row - b * S_q);
+    const RowRule rule = make_row_rule(nonpad, q_start, slot_kind, b, s, S_q, max_seq, window);
+    const int32_t* kind_row = slot_kind ? slot_kind + b * max_seq : nullptr;
+    T* out = bias + row * max_seq + j0;
+    if (vec) {
+      int32_t kinds[8];
+      if (kind_row) {
+        const int4 k0 = ld_global<int4>(kind_row + j0);
+        const int4 k1 = ld_global<int4>(kind_row + j0 + 4);
+        kinds[0] = k0.x; kinds[1] = k0.y; kinds[2] = k0.z; kinds[3] = k0.w;
+        kinds[4] = k1.x; kinds[5] = k1.y; kinds[6] = k1.z; kinds[7] = k1.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kinds[e] = 0;
+      }
+      T v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[e] = rule.allowed(j0 + e, kinds[e]) ? MaskBits<T>::kZero : MaskBits<T>::kNegInf;
+      if constexpr (sizeof(T) == 2) {
+        u32x4 w;
+        w.x = v[0] | ((uint32_t)v[1] << 16);
+        w.y = v[2] | ((uint32_t)v[3] << 16);
+        w.z = v[4] | ((uint32_t)v[5] << 16);
+        w.w = v[6] | ((uint32_t)v[7] << 16);
+        *reinterpret_cast<u32x4*>(out) = w;
+      } else {
+        *reinterpret_cast<u32x4*>(out) = u32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<u32x4*>(out + 4) = u32x4{v[4], v[5], v[6], v[7]};
+      }
+    } else {
+      for (int e = 0; e < 8 && j0 + e < max_seq; ++e) {
+        const int32_t kj = kind_row ? kind_row[j0 + e] : 0;
+        out[e] = rule.allowed(j0 + e, kj) ? MaskBits<T>::kZero : MaskBits<T>::kNegInf;
+      }
+    }
+  }
+}
+
+}  // namespace abgqa

@@ -114,6 +114,41 @@ abgqa_status build_static_cache_bias(void *bias, abgqa_dtype bias_dtype,
                                      int64_t window, void *stream);
 
 /*
+ * kv_scatter_and_bias - the whole per-step preparation in one launch:
+ *   kv_tensor_scatter(k_cache, k_update, write_indices, ...),
+ *   kv_tensor_scatter(v_cache, v_update, write_indices, ...),
+ *   build_static_cache_bias(bias, bias_dtype, nonpad_kv_seqlen, q_start,
+ *                           slot_kind, B, S_q, max_seq, window, ...).
+ *
+ * Passages: those of the three calls it stands for (mobius skill
+ * "attention-optimization", "In-place KV for ONNX Attention via TensorScatter
+ * (static cache)"; mobius issue #366, "Mobius-side deliverable"). The results
+ * are bit-identical to the three separate calls; the bias reads no cache, so
+ * the three pieces of work run side by side in one grid.
+ *
+ *   k_cache, v_cache    [B, Hkv, max_seq, D] of `dtype`, updated in place
+ *   k_update, v_update  [B, Hkv, S_new, D] of `dtype`
+ *   write_indices       [B] int64 on the device, or NULL (all zero)
+ *   bias                [B, 1, S_q, max_seq] of `bias_dtype`, fully written; NULL
+ *                       skips the bias (the in-kernel-rules variant needs none)
+ *   nonpad_kv_seqlen, q_start, slot_kind, S_q, window: as build_static_cache_bias
+ *                       (read only when bias != NULL)
+ *   S_new == 0 skips both scatters (KV-shared layer).
+ * Layout, alignment, ownership and device-side index handling are those of the
+ * separate calls.
+ * Errors: the union of the errors of the separate calls (ABGQA_ERR_INVALID for
+ * null or misaligned pointers or bad sizes, ABGQA_ERR_UNSUPPORTED for dtypes or
+ * row sizes they reject); nothing is enqueued on any error.
+ */
+abgqa_status kv_scatter_and_bias(void *k_cache, void *v_cache, const void *k_update,
+                                 const void *v_update, const int64_t *write_indices,
+                                 int64_t B, int64_t Hkv, int64_t max_seq, int64_t S_new,
+                                 int64_t D, abgqa_dtype dtype, void *bias,
+                                 abgqa_dtype bias_dtype, const int64_t *nonpad_kv_seqlen,
+                                 const int64_t *q_start, const int32_t *slot_kind,
+                                 int64_t S_q, int64_t window, void *stream);
+
+/*
  * attn_bias_gqa_fwd - attention of S_q query tokens over the external cache.
  *
  * Passages: onnxruntime skill "cuda-attention-kernel-patterns", section 4

@@ -86,3 +86,24 @@ def test_workspace_size(lib):
     assert lib.attn_bias_gqa_workspace_bytes(8, 16, 8, 1, 4096, 256) > 0
     assert lib.attn_bias_gqa_workspace_bytes(2, 16, 8, 512, 4096, 256) == 0   # prefill
     assert lib.attn_bias_gqa_workspace_bytes(1, 6, 4, 1, 64, 64) == 0         # invalid heads
+
+
+def test_fused_prepare_validation(lib):
+    f = lib.kv_scatter_and_bias
+    # nothing to do: no new tokens, no bias
+    assert f(None, None, None, None, None, 1, 1, 8, 0, 64, 1, None, 1, None, None, None, 1, 0, None) == OK
+    # new tokens but null caches / updates
+    assert f(None, None, None, None, None, 1, 1, 8, 2, 64, 1, None, 1, None, None, None, 1, 0, None) == INVALID
+    assert "null cache or update" in ab.abgqa_last_error()
+    # rows that are not a multiple of 16 bytes
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 8, 2, 12, 1, None, 1, None, None, None, 1, 0, None) == UNSUPPORTED
+    # misaligned V update
+    assert f(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 8200, None, 1, 1, 8, 2, 64, 1, None, 1, None, None,
+             None, 1, 0, None) == INVALID
+    assert "misaligned" in ab.abgqa_last_error()
+    # a bias without nonpad, with a bad dtype, with S_q = 0
+    assert f(None, None, None, None, None, 1, 1, 8, 0, 64, 1, FAKE, 1, None, None, None, 1, 0, None) == INVALID
+    assert "nonpad" in ab.abgqa_last_error()
+    assert f(None, None, None, None, None, 1, 1, 8, 0, 64, 1, FAKE, 4, FAKE, None, None, 1, 0, None) == UNSUPPORTED
+    assert f(None, None, None, None, None, 1, 1, 8, 0, 64, 1, FAKE, 1, FAKE, None, None, 0, 0, None) == INVALID
+    assert f(None, None, None, None, None, 0, 1, 8, 0, 64, 1, None, 1, None, None, None, 1, 0, None) == INVALID

@@ -95,6 +95,39 @@ def test_bias_bit_exact(bias_dtype, T, S_q, W):
 
 
 # --------------------------------------------------------------------------- #
+# the fused preparation (K scatter + V scatter + bias, one launch): bit-exact
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("dtype,bias_dtype", [(torch.bfloat16, torch.bfloat16),
+                                              (torch.float32, torch.float32),
+                                              (torch.bfloat16, torch.float32)])
+@pytest.mark.parametrize("B,H,T,D,S_new,S_q,W", [(4, 3, 37, 64, 9, 9, 8),      # ragged, off the end
+                                                (8, 8, 4096, 256, 1, 1, 1024), # decode_sliding-like
+                                                (2, 4, 300, 512, 0, 1, 0),     # KV-shared: bias only
+                                                (2, 2, 520, 128, 130, 130, 64)])
+def test_fused_prepare_bit_exact(dtype, bias_dtype, B, H, T, D, S_new, S_q, W):
+    announce(f"fused prepare dtype={dtype} bias={bias_dtype} B={B} H={H} T={T} D={D} "
+             f"S_new={S_new} S_q={S_q} W={W}")
+    rng = wl.rng_for(400 + T + D + S_new)
+    kc, vc = wl.garbage(rng, (B, H, T, D), dtype), wl.garbage(rng, (B, H, T, D), dtype)
+    ku, vu = wl.garbage(rng, (B, H, S_new, D), dtype), wl.garbage(rng, (B, H, S_new, D), dtype)
+    w = torch.from_numpy(rng.integers(-2, T, size=B).astype(np.int64))   # some off either end
+    nonpad = torch.from_numpy(rng.integers(0, T, size=B, endpoint=True).astype(np.int64))
+    kind = _rand_kinds(rng, B, T)
+    ibits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    for with_bias in (True, False):
+        k_d, v_d = dev(kc), dev(vc)
+        bias = torch.empty((B, 1, S_q, T), dtype=bias_dtype, device="cuda") if with_bias else None
+        ab.kv_scatter_and_bias(k_d, v_d, dev(ku), dev(vu), dev(w), dev(nonpad), None, dev(kind),
+                               S_q, W, bias=bias)
+        torch.cuda.synchronize()
+        assert torch.equal(k_d.cpu().view(ibits), oracle.scatter(kc, ku, w).view(ibits))
+        assert torch.equal(v_d.cpu().view(ibits), oracle.scatter(vc, vu, w).view(ibits))
+        if with_bias:
+            ref = torch.from_numpy(oracle.bias(nonpad, None, kind, S_q, T, W)).to(torch.float32)
+            assert torch.equal(bias.cpu().to(torch.float32).view(torch.int32), ref.view(torch.int32))
+
+
+# --------------------------------------------------------------------------- #
 # attention: small shapes, every element
 # --------------------------------------------------------------------------- #
 SMALL = {
