@@ -60,7 +60,7 @@ def _load():
         lib.oracle_repeat_kv.restype = None
         lib.oracle_attention_mha.argtypes = (
             [_f64p, _f64p, _f64p, _f64p, _f64p, _i64p] + [ctypes.c_int64] * 5
-            + [ctypes.c_double, _i64p, ctypes.c_int64, _f64p])
+            + [ctypes.c_double, ctypes.c_double, _i64p, ctypes.c_int64, _f64p])
         lib.oracle_attention_mha.restype = None
         _lib = lib
     return _lib
@@ -151,9 +151,11 @@ def repeat_kv(x, G: int) -> np.ndarray:
     return dst
 
 
-def attention_mha(q, k, v, bias_, nonpad, scale: float, rows=None) -> np.ndarray:
+def attention_mha(q, k, v, bias_, nonpad, scale: float, rows=None, softcap: float = 0.0) -> np.ndarray:
     """Dense attention with K/V already at Hq heads. Returns [B,H,S_q,D] float64,
-    or [len(rows), D] for the flat rows (b*H + h)*S_q + s when ``rows`` is given."""
+    or [len(rows), D] for the flat rows (b*H + h)*S_q + s when ``rows`` is given.
+    softcap > 0 applies softcap * tanh(score / softcap) to scale * q.k before the
+    bias is added (0 = none)."""
     qd, kd, vd, bd = _f64(q), _f64(k), _f64(v), _f64(bias_)
     npd = _i64(nonpad)
     B, H, S_q, D = qd.shape
@@ -168,12 +170,13 @@ def attention_mha(q, k, v, bias_, nonpad, scale: float, rows=None) -> np.ndarray
     scratch = np.empty((n, T), dtype=np.float64)
     _load().oracle_attention_mha(
         _ptr(out, _f64p), _ptr(qd, _f64p), _ptr(kd, _f64p), _ptr(vd, _f64p),
-        _ptr(bd, _f64p), _ptr(npd, _i64p), B, H, S_q, T, D, float(scale),
+        _ptr(bd, _f64p), _ptr(npd, _i64p), B, H, S_q, T, D, float(scale), float(softcap),
         _ptr(r, _i64p), 0 if r is None else n, _ptr(scratch, _f64p))
     return out.reshape(B, H, S_q, D) if r is None else out
 
 
-def attention(q, k_cache, v_cache, bias_, nonpad, scale: float, rows=None) -> np.ndarray:
+def attention(q, k_cache, v_cache, bias_, nonpad, scale: float, rows=None,
+              softcap: float = 0.0) -> np.ndarray:
     """GQA attention: repeat the KV heads (h // G), then dense attention.
 
     q [B,Hq,S_q,D], k_cache/v_cache [B,Hkv,T,D], bias [B,1,S_q,T], nonpad [B].
@@ -189,7 +192,7 @@ def attention(q, k_cache, v_cache, bias_, nonpad, scale: float, rows=None) -> np
     G = Hq // Hkv
     if rows is None:
         return attention_mha(_np(q), repeat_kv(_np(k_cache), G), repeat_kv(_np(v_cache), G),
-                             _np(bias_), npd, scale)
+                             _np(bias_), npd, scale, softcap=softcap)
     rows = _i64(rows)
     out = np.empty((rows.shape[0], D), dtype=np.float64)
     per_batch = Hq * S_q
@@ -200,5 +203,5 @@ def attention(q, k_cache, v_cache, bias_, nonpad, scale: float, rows=None) -> np
         # slice before widening: one batch entry in fp64 at a time
         out[sel] = attention_mha(_np(q[b:b + 1]), repeat_kv(_np(k_cache[b:b + 1]), G),
                                  repeat_kv(_np(v_cache[b:b + 1]), G), _np(bias_[b:b + 1]),
-                                 npd[b:b + 1], scale, rows=local)
+                                 npd[b:b + 1], scale, rows=local, softcap=softcap)
     return out

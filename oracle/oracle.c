@@ -145,7 +145,7 @@ void oracle_attention_mha(double *out, const double *q, const double *k,
                           const double *v, const double *bias,
                           const int64_t *nonpad, int64_t B, int64_t H,
                           int64_t S_q, int64_t T, int64_t D, double scale,
-                          const int64_t *rows, int64_t n_rows,
+                          double softcap, const int64_t *rows, int64_t n_rows,
                           double *scratch /* [n_rows or B*H*S_q, T] */) {
   const int64_t total = rows ? n_rows : B * H * S_q;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -174,7 +174,11 @@ void oracle_attention_mha(double *out, const double *q, const double *k,
       const double *kr = k + ((b * H + h) * T + j) * D;
       double dot = 0.0;
       for (int64_t d = 0; d < D; ++d) dot += qr[d] * kr[d];
-      x[j] = scale * dot + br[j];
+      /* the skill page, section 4 "Softcap Ordering": stage 0 scale * QK^T,
+         stage 1 softcap * tanh(. / softcap) when softcap > 0, stage 2 + bias */
+      double sc = scale * dot;
+      if (softcap > 0.0) sc = softcap * tanh(sc / softcap);
+      x[j] = sc + br[j];
       if (x[j] > m) m = x[j];
       ++kept;
     }

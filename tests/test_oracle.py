@@ -119,6 +119,20 @@ def test_bias_window_is_band(W):
     np.testing.assert_array_equal(out[0, 0], ref)
 
 
+@pytest.mark.parametrize("S_q,nonpad,T", [(1, 17, 32), (5, 17, 32), (17, 17, 17), (40, 30, 64), (8, 0, 16)])
+def test_bias_maskless_causal_is_bottom_right(S_q, nonpad, T):
+    # Maskless is_causal=1 over an external cache (onnx#8068, as the skill page's
+    # section 11 states it): query i sees key j iff j <= i + max(nonpad - S_q, 0)
+    # and j < nonpad. With no window and no slot kinds the default query offset
+    # gives exactly that: a lower triangle shifted by the offset (torch.tril with
+    # a diagonal), cut at nonpad.
+    out = oracle.bias([nonpad], None, None, S_q=S_q, max_seq=T, window=0)
+    off = max(nonpad - S_q, 0)
+    tri = torch.tril(torch.ones(S_q, T, dtype=torch.bool), diagonal=off)
+    tri[:, nonpad:] = False
+    np.testing.assert_array_equal(out[0, 0], _torch_mask_to_bias(tri))
+
+
 def test_bias_decode_row():
     # decode (S_q = 1) with the default q_start: the query sits at slot nonpad-1
     # and, without a window, sees exactly the nonpad valid slots.
@@ -462,3 +476,91 @@ def test_workload_generator_is_seeded():
     assert torch.equal(a.k_cache.view(torch.int16), b.k_cache.view(torch.int16))
     s = a.steps[0]
     assert torch.equal(s.write_indices, s.nonpad - 1) and torch.equal(s.q_start, s.nonpad - 1)
+
+
+# --------------------------------------------------------------------------- #
+# softcap (the skill page, section 4 "Softcap Ordering"): stage 1 between the
+# scaled scores and the bias
+# --------------------------------------------------------------------------- #
+def test_softcap_mpmath_bruteforce():
+    # 50-digit brute force with the stage order of the page: scale*QK^T, then
+    # c * tanh(. / c), then + bias (a -inf bias stays -inf), softmax, times V
+    import mpmath as mp
+    mp.mp.dps = 50
+    rng = wl.rng_for(120)
+    B, Hq, Hkv, S_q, T, D = 1, 4, 2, 3, 7, 4
+    q, k, v = _rand(rng, (B, Hq, S_q, D)), 3.0 * _rand(rng, (B, Hkv, T, D)), _rand(rng, (B, Hkv, T, D))
+    bias = 2.0 * _rand(rng, (B, 1, S_q, T))
+    bias[rng.random(bias.shape) < 0.3] = NEG_INF
+    nonpad, scale, cap = [6], 0.9, 1.7
+    y = oracle.attention(q, k, v, bias, nonpad, scale, softcap=cap)
+    G = Hq // Hkv
+    for h in range(Hq):
+        for s in range(S_q):
+            keys = [j for j in range(T) if j < nonpad[0] and bias[0, 0, s, j] != NEG_INF]
+            if not keys:
+                assert np.all(y[0, h, s] == 0.0)
+                continue
+            xs = {}
+            for j in keys:
+                raw = mp.mpf(scale) * mp.fsum(mp.mpf(q[0, h, s, d]) * mp.mpf(k[0, h // G, j, d])
+                                              for d in range(D))
+                xs[j] = mp.mpf(cap) * mp.tanh(raw / mp.mpf(cap)) + mp.mpf(bias[0, 0, s, j])
+            ws = {j: mp.exp(xs[j]) for j in keys}
+            tot = mp.fsum(ws.values())
+            for d in range(D):
+                ref = mp.fsum(ws[j] * mp.mpf(v[0, h // G, j, d]) for j in keys) / tot
+                assert abs(float(ref) - y[0, h, s, d]) <= 1e-13
+
+
+def test_softcap_limits():
+    rng = wl.rng_for(121)
+    B, Hq, Hkv, S_q, T, D = 2, 4, 2, 5, 20, 8
+    q, k, v = _rand(rng, (B, Hq, S_q, D)), _rand(rng, (B, Hkv, T, D)), _rand(rng, (B, Hkv, T, D))
+    nonpad = np.array([17, 20])
+    bias = oracle.bias(nonpad, None, None, S_q, T, 0)
+    plain = oracle.attention(q, k, v, bias, nonpad, 0.5)
+    # a cap far above every score: tanh(y) = y + O(y^3), the cap changes nothing
+    big = oracle.attention(q, k, v, bias, nonpad, 0.5, softcap=1e7)
+    np.testing.assert_allclose(big, plain, rtol=0, atol=1e-12)
+    # a vanishing cap flattens every score to ~0: the weights become uniform and
+    # each row is the plain mean of its live V rows
+    flat = oracle.attention(q, k, v, bias, nonpad, 0.5, softcap=1e-12)
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            for s in range(S_q):
+                live = [j for j in range(T) if j < nonpad[b] and bias[b, 0, s, j] != NEG_INF]
+                np.testing.assert_allclose(flat[b, h, s], v[b, h // G, live].mean(axis=0),
+                                           rtol=0, atol=1e-10)
+
+
+def test_softcap_keeps_masks_and_bounds_weights():
+    # the ordering property the page motivates: with a small cap, a -inf bias
+    # entry still removes its key (poison V there changes nothing), because the
+    # cap acts before the bias; and two live keys with equal bias have weights
+    # within a factor e^(2c) of each other
+    rng = wl.rng_for(122)
+    B, Hq, Hkv, S_q, T, D = 1, 2, 1, 4, 12, 12
+    q, k, v = 4.0 * _rand(rng, (B, Hq, S_q, D)), 4.0 * _rand(rng, (B, Hkv, T, D)), _rand(rng, (B, Hkv, T, D))
+    nonpad = np.array([T])
+    bias = np.zeros((B, 1, S_q, T))
+    bias[0, 0, :, 3] = NEG_INF
+    cap = 0.5
+    y = oracle.attention(q, k, v, bias, nonpad, 1.0, softcap=cap)
+    for poison in (np.nan, np.inf, 1e30):
+        v2 = v.copy()
+        v2[0, :, 3] = poison
+        np.testing.assert_array_equal(oracle.attention(q, k, v2, bias, nonpad, 1.0, softcap=cap), y)
+    # the weights themselves, from one-hot V rows (V = identity over the keys)
+    eye = np.zeros((B, Hkv, T, D))
+    eye[0, 0] = np.eye(T)
+    w = oracle.attention(q, k, eye, bias, nonpad, 1.0, softcap=cap)   # [B,Hq,S_q,T] = weights
+    live = w[0][..., [j for j in range(T) if j != 3]]
+    assert np.all(w[0][..., 3] == 0.0)
+    np.testing.assert_allclose(w.sum(axis=-1), 1.0, rtol=0, atol=1e-12)
+    assert np.all(live.max(axis=-1) / live.min(axis=-1) <= math.exp(2 * cap) * (1 + 1e-12))
+    # without the cap the same scores spread far wider (the bound above is not vacuous)
+    w0 = oracle.attention(q, k, eye, bias, nonpad, 1.0)
+    live0 = w0[0][..., [j for j in range(T) if j != 3]]
+    assert np.any(live0.max(axis=-1) / live0.min(axis=-1) > math.exp(2 * cap))

@@ -235,6 +235,37 @@ def test_decode_empty_and_single_key():
     check_parity(got, ref, w.dtype, dead_rows(bias_ref, step.nonpad, w.Hq), "decode-edge")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,D,T,S_q,causal", [
+    (3, 8, 2, 256, 300, 1, True),      # decode: bottom-right = every valid key
+    (2, 8, 2, 128, 200, 40, True),     # prefill chunk, some rows with nonpad < S_q
+    (2, 4, 2, 256, 512, 100, True),
+    (2, 8, 2, 512, 256, 33, True),
+    (3, 8, 2, 256, 300, 1, False),     # is_causal=0: every valid key
+    (2, 4, 2, 128, 200, 40, False)])
+def test_maskless_static_cache(B, Hq, Hkv, D, T, S_q, causal):
+    """Maskless Attention over the external cache (no bias tensor): is_causal=1
+    is the in-kernel-rules call with no window, no slot kinds and the default
+    query offset (bottom-right from nonpad); is_causal=0 passes q_start =
+    max_seq so that every valid slot precedes every query."""
+    announce(f"maskless causal={causal} B={B} Hq={Hq} Hkv={Hkv} D={D} T={T} S_q={S_q}")
+    rng = wl.rng_for(500 + T + S_q + D)
+    dt = torch.bfloat16
+    q = wl.normal(rng, (B, Hq, S_q, D), dt)
+    k = wl.normal(rng, (B, Hkv, T, D), dt)
+    v = wl.normal(rng, (B, Hkv, T, D), dt)
+    nonpad = torch.from_numpy(rng.integers(max(1, S_q // 2), T, size=B, endpoint=True).astype(np.int64))
+    nonpad[0] = min(int(nonpad[0]), S_q - 1) if S_q > 1 else nonpad[0]   # an offset clamped at 0
+    qs = None if causal else torch.full((B,), T, dtype=torch.int64)
+    scale = 1.0 / math.sqrt(D)
+    ws_bytes = ab.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, T, D)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
+    out = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale, q_start=dev(qs),
+                               slot_kind=None, window=0, workspace=ws)
+    bias = oracle.bias(nonpad, qs, None, S_q, T, 0)
+    ref = oracle.attention(q, k, v, bias, nonpad, scale)
+    check_parity(to_f64(out.cpu()), ref, dt, dead_rows(bias, nonpad, Hq), what="maskless")
+
+
 @pytest.mark.parametrize("S_q", [1, 3, 40])
 def test_random_finite_bias(S_q):
     """A caller-supplied float bias with arbitrary finite values and -inf holes."""
