@@ -62,8 +62,8 @@ def load():
         lib.build_static_cache_bias.argtypes = [vp, ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, vp]
         lib.build_static_cache_bias.restype = ctypes.c_int
         lib.attn_bias_gqa_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
-                                          i64, i64, i64, i64, i64, i64, ctypes.c_float, i64,
-                                          ctypes.c_int, vp, sz, vp]
+                                          i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                                          ctypes.c_float, i64, ctypes.c_int, vp, sz, vp]
         lib.attn_bias_gqa_fwd.restype = ctypes.c_int
         lib.attn_bias_gqa_workspace_bytes.argtypes = [i64] * 6
         lib.attn_bias_gqa_workspace_bytes.restype = sz
@@ -204,10 +204,12 @@ def attn_bias_gqa_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       q_start: torch.Tensor | None = None,
                       slot_kind: torch.Tensor | None = None, window: int = 0,
                       out: torch.Tensor | None = None,
-                      workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """softmax(scale * Q K^T + bias) V over the static cache (GQA: head h reads
-    KV head h // (Hq // Hkv)). bias=None evaluates the static-cache rules
-    (nonpad, q_start, slot_kind, window) inside the kernel instead."""
+                      workspace: torch.Tensor | None = None,
+                      softcap: float = 0.0) -> torch.Tensor:
+    """softmax(cap(scale * Q K^T) + bias) V over the static cache (GQA: head h
+    reads KV head h // (Hq // Hkv)); cap(x) = softcap * tanh(x / softcap) when
+    softcap > 0, else x. bias=None evaluates the static-cache rules (nonpad,
+    q_start, slot_kind, window) inside the kernel instead."""
     if q.dim() != 4 or k_cache.dim() != 4:
         raise ValueError("q must be [B, Hq, S_q, D] and the caches [B, Hkv, max_seq, D]")
     B, Hq, S_q, D = q.shape
@@ -235,6 +237,6 @@ def attn_bias_gqa_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     wp = None if workspace is None else _dev(workspace, "workspace")
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.attn_bias_gqa_fwd(op, qp, kp, vp_, bp, bdt, npd, qs, sk, B, Hq, Hkv, S_q, T, D,
-                                 float(scale), int(window), _DTYPE[q.dtype], wp, wbytes,
+                                 float(scale), float(softcap), int(window), _DTYPE[q.dtype], wp, wbytes,
                                  _stream(q)), "attn_bias_gqa_fwd")
     return out

@@ -151,13 +151,15 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
                                const void* bias, abgqa_dtype bias_dtype,
                                const int64_t* nonpad_kv_seqlen, const int64_t* q_start,
                                const int32_t* slot_kind, int64_t B, int64_t Hq, int64_t Hkv,
-                               int64_t S_q, int64_t max_seq, int64_t D, float scale, int64_t window,
-                               abgqa_dtype dtype, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+                               int64_t S_q, int64_t max_seq, int64_t D, float scale, float softcap,
+                               int64_t window, abgqa_dtype dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_q <= 0 || max_seq <= 0 || D <= 0)
     return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: B, Hq, Hkv, S_q, max_seq and D must be positive");
   if (Hq % Hkv != 0) return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: Hq must be a multiple of Hkv");
+  if (!(softcap >= 0.f) || softcap == INFINITY)
+    return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: softcap must be finite and >= 0 (0 = none)");
   if (S_q > max_seq) return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: S_q must not exceed max_seq");
   if (!head_dim_ok(D)) return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: D must be 64, 128, 256 or 512");
   if (max_seq > kMaxSeq) return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: max_seq above 2^24");
@@ -181,7 +183,7 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
   p.out = out; p.q = q; p.k = k_cache; p.v = v_cache; p.bias = bias;
   p.nonpad = nonpad_kv_seqlen; p.q_start = q_start; p.slot_kind = slot_kind;
   p.B = (int)B; p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.G = (int)G; p.S_q = (int)S_q;
-  p.T = (int)max_seq; p.D = (int)D; p.window = window; p.scale = scale;
+  p.T = (int)max_seq; p.D = (int)D; p.window = window; p.scale = scale; p.softcap = softcap;
   p.bias_is_bf16 = (bias_dtype == ABGQA_BF16);
   hipStream_t st = (hipStream_t)stream;
 

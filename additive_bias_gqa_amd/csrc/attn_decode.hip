@@ -293,6 +293,8 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
     if constexpr (kRules) rules[e] = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, row_s[e], p.S_q, T, p.window);
   }
   const float scale_log2 = p.scale * kLog2e;
+  const bool cap_on = p.softcap > 0.f;
+  const float cap2 = p.softcap * kLog2e, scale_over_cap = cap_on ? p.scale / p.softcap : 0.f;
 
   const __bf16* kbase = (const __bf16*)p.k + (b * p.Hkv + hk) * (int64_t)T * D;
   const __bf16* vbase = (const __bf16*)p.v + (b * p.Hkv + hk) * (int64_t)T * D;
@@ -383,13 +385,22 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
       acc = mfma16x16x32(a, kb[i], acc);
     }
 
+    // softcap (0 = none) acts on scale * q.k before the bias is added: the raw
+    // scores become the capped base-2 scores and the multiplier below 1
+    float sl = scale_log2;
+    if (cap_on) {
+      asm volatile("" ::: "memory");   // a real branch, not selects on every block
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = softcap_base2(acc[e], cap2, scale_over_cap);
+      sl = 1.f;
+    }
     // online softmax on the S layout: lane = key (lane % 16), rows 4*kgrp + e
     float x[E];
     bool need_any = false;
     float alpha[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      x[e] = keep[e] ? fmaf(acc[e], scale_log2, badd[e]) : -INFINITY;
+      x[e] = keep[e] ? fmaf(acc[e], sl, badd[e]) : -INFINITY;
       const float mt = row16_max(x[e]);
       const float mn = fmaxf(m_run[e], mt);
       const bool need = mn > m_run[e] + kRescaleThreshold;

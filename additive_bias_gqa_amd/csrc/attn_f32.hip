@@ -67,7 +67,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p, int64_t n_ro
           const float* kr = kbase + j * D;
           float dot = 0.f;
           for (int d = 0; d < D; ++d) dot = fmaf(q_s[d], kr[d], dot);
-          x = (dot * p.scale + bv) * kLog2e;
+          float sc = dot * p.scale;
+          // softcap (skill page, section 4): before the bias; 0 = none
+          if (p.softcap > 0.f) sc = p.softcap * tanhf(sc / p.softcap);
+          x = (sc + bv) * kLog2e;
         }
       }
       const float m_new = fmaxf(m, wave_max(x));

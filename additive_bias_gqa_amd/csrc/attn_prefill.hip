@@ -156,6 +156,8 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnParams p, int
   const int32_t* kindb = p.slot_kind ? p.slot_kind + b * T : nullptr;
   const bool vec4 = (T % 4) == 0;   // bias / kind rows 4-aligned (uniform)
   const float scale_log2 = p.scale * kLog2e;
+  const bool cap_on = p.softcap > 0.f;
+  const float cap2 = p.softcap * kLog2e, scale_over_cap = cap_on ? p.scale / p.softcap : 0.f;
 
   const __bf16* kg = (const __bf16*)p.k + (b * p.Hkv + hk) * (int64_t)T * D;
   const __bf16* vg = (const __bf16*)p.v + (b * p.Hkv + hk) * (int64_t)T * D;
@@ -267,6 +269,14 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnParams p, int
       sacc = mfma32x32x16(a, qf[i], sacc);
     }
 
+    // softcap (0 = none) on scale * q.k, before the bias
+    float sl = scale_log2;
+    if (cap_on) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[e] = softcap_base2(sacc[e], cap2, scale_over_cap);
+      sl = 1.f;
+    }
     // keep = valid && allowed; x = keep ? (s*scale + bias)*log2e : -inf
     float x[16];
     float mt = -INFINITY;
@@ -286,7 +296,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnParams p, int
           keep = row_ok & (j < np) & live_bits<BiasT>(bv);
           badd = bias_f32<BiasT>(bv) * kLog2e;
         }
-        const float v = fmaf(sacc[4 * i + jj], scale_log2, badd);
+        const float v = fmaf(sacc[4 * i + jj], sl, badd);
         x[4 * i + jj] = keep ? v : -INFINITY;
         mt = fmaxf(mt, x[4 * i + jj]);
       }
@@ -431,6 +441,8 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill16_kernel(AttnParams p, i
   const int32_t* kindb = p.slot_kind ? p.slot_kind + b * T : nullptr;
   const bool vec4 = (T % 4) == 0;
   const float scale_log2 = p.scale * kLog2e;
+  const bool cap_on = p.softcap > 0.f;
+  const float cap2 = p.softcap * kLog2e, scale_over_cap = cap_on ? p.scale / p.softcap : 0.f;
   const __bf16* kg = (const __bf16*)p.k + (b * p.Hkv + hk) * (int64_t)T * D;
   const __bf16* vg = (const __bf16*)p.v + (b * p.Hkv + hk) * (int64_t)T * D;
 
@@ -522,6 +534,15 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill16_kernel(AttnParams p, i
         sacc[kb] = mfma16x16x32(a, qf[i], sacc[kb]);
       }
     }
+    float sl = scale_log2;
+    if (cap_on) {   // softcap (0 = none) on scale * q.k, before the bias
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sacc[kb][e] = softcap_base2(sacc[kb][e], cap2, scale_over_cap);
+      sl = 1.f;
+    }
     float x[8];
     float mt = -INFINITY;
 #pragma unroll
@@ -540,7 +561,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill16_kernel(AttnParams p, i
           keep = row_ok & (j < np) & live_bits<BiasT>(bv);
           badd = bias_f32<BiasT>(bv) * kLog2e;
         }
-        const float v = fmaf(sacc[kb][e], scale_log2, badd);
+        const float v = fmaf(sacc[kb][e], sl, badd);
         x[4 * kb + e] = keep ? v : -INFINITY;
         mt = fmaxf(mt, x[4 * kb + e]);
       }

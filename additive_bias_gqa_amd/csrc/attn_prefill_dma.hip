@@ -224,6 +224,8 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   wait_vmcnt<0>();
 
   const float scale_log2 = p.scale * kLog2e;
+  const bool cap_on = p.softcap > 0.f;
+  const float cap2 = p.softcap * kLog2e, scale_over_cap = cap_on ? p.scale / p.softcap : 0.f;
   const __bf16* kg = (const __bf16*)p.k + (b * p.Hkv + hk) * (int64_t)T * D;
   const __bf16* vg = (const __bf16*)p.v + (b * p.Hkv + hk) * (int64_t)T * D;
   const int32_t* kindb = p.slot_kind ? p.slot_kind + b * T : nullptr;
@@ -467,6 +469,15 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
       bf16x8 vf[PVD];
 #pragma unroll
       for (int u = 0; u < PVD; ++u) vf[u] = vread(u);
+      // softcap (0 = none) on scale * q.k, before the bias: capped base-2 scores,
+      // multiplier 1 (a real branch, not selects on every tile)
+      float sl = scale_log2;
+      if (cap_on) {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[e] = softcap_base2(sacc[e], cap2, scale_over_cap);
+        sl = 1.f;
+      }
       float x[16];
       float mt = -INFINITY;
 #pragma unroll
@@ -478,11 +489,11 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
           float v;
           if constexpr (kRules) {
             // allowed() includes j < nonpad; a row past the chunk has no rule
-            v = rule.allowed(j, kvs[i][jj]) ? sacc[4 * i + jj] * scale_log2 : -INFINITY;
+            v = rule.allowed(j, kvs[i][jj]) ? sacc[4 * i + jj] * sl : -INFINITY;
           } else {
             // a -inf bias gives -inf (the score is finite: every fetched key row
             // is a valid row); keys at or past nonpad only in a partial tile
-            v = fmaf(sacc[4 * i + jj], scale_log2, bias_f32<BiasT>(bvs[i][jj]) * kLog2e);
+            v = fmaf(sacc[4 * i + jj], sl, bias_f32<BiasT>(bvs[i][jj]) * kLog2e);
           }
           x[4 * i + jj] = v;
         }
@@ -592,6 +603,15 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
       bf16x8 vf[PVD];
 #pragma unroll
       for (int u = 0; u < PVD; ++u) vf[u] = vread(u);
+      float sl = scale_log2;
+      if (cap_on) {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sacc[kb][e] = softcap_base2(sacc[kb][e], cap2, scale_over_cap);
+        sl = 1.f;
+      }
       float x[8];
       float mt = -INFINITY;
 #pragma unroll
@@ -602,9 +622,9 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
           const int j = j0 + kf + e;
           float v;
           if constexpr (kRules) {
-            v = rule.allowed(j, kvs[kb][e]) ? sacc[kb][e] * scale_log2 : -INFINITY;
+            v = rule.allowed(j, kvs[kb][e]) ? sacc[kb][e] * sl : -INFINITY;
           } else {
-            v = fmaf(sacc[kb][e], scale_log2, bias_f32<BiasT>(bvs[kb][e]) * kLog2e);
+            v = fmaf(sacc[kb][e], sl, bias_f32<BiasT>(bvs[kb][e]) * kLog2e);
           }
           x[4 * kb + e] = v;
         }

@@ -106,6 +106,21 @@ __device__ __forceinline__ int wave_max_i32(int v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// tanh(y) = 1 - 2 / (e^(2y) + 1), from the definition: e^(2y) = 2^(2y log2 e)
+// on the exponential unit and one hardware reciprocal. The limits are exact
+// (2^(2y log2 e) overflows to inf, or underflows to 0, giving +1 or -1); near 0
+// the error is a few units in the last place of 1.
+__device__ __forceinline__ float fast_tanh(float y) {
+  return 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + fast_exp2(y * (2.f * kLog2e)));
+}
+
+// The softcap stage on base-2 scores t = scale * q.k * log2(e): c * tanh(v / c)
+// in natural units is (c log2 e) * tanh(t / (c log2 e)) in base 2, i.e.
+// cap2 * tanh(raw * (scale / c)) for the raw dot product `raw`.
+__device__ __forceinline__ float softcap_base2(float raw, float cap2, float scale_over_cap) {
+  return cap2 * fast_tanh(raw * scale_over_cap);
+}
+
 // ---- grid mapping ----------------------------------------------------------
 // MI355X dispatches consecutive workgroups round-robin over its 8 XCDs, each
 // with its own L2. Remap so that consecutive logical ids run on one XCD (and

@@ -45,6 +45,7 @@ struct AttnParams {
   int B, Hq, Hkv, G, S_q, T, D;
   int64_t window;            // rules variant only; <= 0 none
   float scale;               // multiplies q.k
+  float softcap;             // > 0: softcap * tanh(scale * q.k / softcap) before the bias
   int bias_is_bf16;          // bias dtype when bias != null
   // split-KV decode
   float* ws_part;            // partial results, one record per (b, kv head, split)

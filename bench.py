@@ -82,6 +82,7 @@ class InputSet:
 
 
 VARIANT = "bias"   # "bias": materialised bias tensor; "rules": rules evaluated in-kernel
+SOFTCAP = 0.0      # > 0: softcap * tanh(score / softcap) before the bias
 
 
 def run_scatter_bias(ab, w, step, s):
@@ -98,10 +99,12 @@ def run_scatter_bias(ab, w, step, s):
 
 def run_attention(ab, w, s, ws):
     if VARIANT == "bias":
-        ab.attn_bias_gqa_fwd(s.q, s.k, s.v, s.bias, s.nonpad, w.scale, out=s.out, workspace=ws)
+        ab.attn_bias_gqa_fwd(s.q, s.k, s.v, s.bias, s.nonpad, w.scale, out=s.out, workspace=ws,
+                             softcap=SOFTCAP)
     else:
         ab.attn_bias_gqa_fwd(s.q, s.k, s.v, None, s.nonpad, w.scale, q_start=s.q_start,
-                             slot_kind=s.kind, window=w.window, out=s.out, workspace=ws)
+                             slot_kind=s.kind, window=w.window, out=s.out, workspace=ws,
+                             softcap=SOFTCAP)
 
 
 def work_counts(w, step, s, torch):
@@ -393,12 +396,15 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
                          "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--softcap", type=float, default=0.0,
+                    help="softcap of the attention scores (0 = none, the workloads' setting)")
     args = ap.parse_args()
     if args.traffic_from:
         write_traffic(args.workload, *args.traffic_from)
         return
-    global VARIANT
+    global VARIANT, SOFTCAP
     VARIANT = args.variant
+    SOFTCAP = args.softcap
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported: the "
@@ -438,7 +444,7 @@ def main():
         cpu = cpu_baseline(w, counts)
     cfg = dict(main_res["desc"])
     cfg.update({"kernel_timing": main_res["mode"], "rotating_input_sets": main_res["n_sets"],
-                "device_copy_gbs": round(copy_gbs, 1), "variant": VARIANT,
+                "device_copy_gbs": round(copy_gbs, 1), "variant": VARIANT, "softcap": SOFTCAP,
                 "attn_us": round(main_res["attn_ms"] * 1e3, 2),
                 "attn_bytes": counts["attn_bytes"], "step_bytes": counts["step_bytes"],
                 "live_keys": counts["live_keys"]})

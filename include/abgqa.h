@@ -152,7 +152,7 @@ abgqa_status kv_scatter_and_bias(void *k_cache, void *v_cache, const void *k_upd
  * attn_bias_gqa_fwd - attention of S_q query tokens over the external cache.
  *
  * Passages: onnxruntime skill "cuda-attention-kernel-patterns", section 4
- * (scale*QK^T, then + bias, then softmax, then times V; no softcap here),
+ * (scale*QK^T, then the optional softcap, then + bias, then softmax, then times V),
  * section 6 (a query row with no allowed key, or a batch row with nonpad = 0,
  * outputs zeros, decided by selection so masked V never leaks), section 11
  * (external cache: keys are the cache slots < nonpad_kv_seqlen); mobius issue
@@ -170,6 +170,9 @@ abgqa_status kv_scatter_and_bias(void *k_cache, void *v_cache, const void *k_upd
  *   nonpad_kv_seqlen [B] int64 on the device
  *   q_start, slot_kind, window: read only when bias == NULL (see above)
  *   scale            multiplies q.k before the bias is added (1/sqrt(D) usually)
+ *   softcap          > 0: the score becomes softcap * tanh(scale * q.k / softcap)
+ *                    before the bias is added (skill page, section 4 "Softcap
+ *                    Ordering": a -inf bias still removes its key); 0 = none
  *   dtype            ABGQA_BF16 (fp32 accumulation, softmax weights rounded to
  *                    bf16 for the matrix-core PV product in prefill) or
  *                    ABGQA_F32 (fp32 throughout)
@@ -181,8 +184,13 @@ abgqa_status kv_scatter_and_bias(void *k_cache, void *v_cache, const void *k_upd
  * Slots >= nonpad may hold any bits (NaN/Inf included); they never reach the
  * arithmetic. K/V at slots < nonpad are expected to be finite: a key masked by
  * the bias gets the exact weight 0, and 0 times a finite V is 0.
+ * Maskless static-cache Attention (no bias tensor; skill page section 11, the
+ * onnx#8068 alignment; mobius issue #366, sibling #345): is_causal = 1 is
+ * bias = NULL, q_start = NULL, slot_kind = NULL, window = 0 - query i sees key
+ * j iff j <= i + max(nonpad - S_q, 0) and j < nonpad; is_causal = 0 passes in
+ * addition q_start[b] = max_seq (every valid key precedes every query).
  * Errors: ABGQA_ERR_INVALID (null pointers, sizes, Hq % Hkv != 0, S_q > max_seq,
- * misalignment), ABGQA_ERR_UNSUPPORTED (D not in {64,128,256,512}, dtype pair
+ * softcap negative or not finite, misalignment), ABGQA_ERR_UNSUPPORTED (D not in {64,128,256,512}, dtype pair
  * not supported), ABGQA_ERR_WORKSPACE, ABGQA_ERR_HIP.
  */
 abgqa_status attn_bias_gqa_fwd(void *out, const void *q, const void *k_cache,
@@ -192,7 +200,7 @@ abgqa_status attn_bias_gqa_fwd(void *out, const void *q, const void *k_cache,
                                const int64_t *q_start, const int32_t *slot_kind,
                                int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q,
                                int64_t max_seq, int64_t D, float scale,
-                               int64_t window, abgqa_dtype dtype,
+                               float softcap, int64_t window, abgqa_dtype dtype,
                                void *workspace, size_t workspace_bytes,
                                void *stream);
 

@@ -26,7 +26,8 @@ def dev(t):
 
 
 def gpu_step(w: wl.Workload, step: wl.Step, k_dev, v_dev, rules: bool = False,
-             bias_dtype: torch.dtype | None = None, default_q_start: bool = False):
+             bias_dtype: torch.dtype | None = None, default_q_start: bool = False,
+             softcap: float = 0.0):
     """Scatter K/V (unless KV-shared), build the bias (unless rules), attention.
     Returns (bias or None, out) on the device."""
     if step.k_new is not None:
@@ -41,19 +42,20 @@ def gpu_step(w: wl.Workload, step: wl.Step, k_dev, v_dev, rules: bool = False,
         bias = ab.build_static_cache_bias(nonpad, q_start, kind, step.S_q, w.max_seq, w.window,
                                           dtype=bias_dtype or w.dtype)
     out = ab.attn_bias_gqa_fwd(dev(step.q), k_dev, v_dev, bias, nonpad, w.scale,
-                               q_start=q_start, slot_kind=kind, window=w.window)
+                               q_start=q_start, slot_kind=kind, window=w.window, softcap=softcap)
     return bias, out
 
 
 def oracle_step(w: wl.Workload, step: wl.Step, k_host, v_host, rows=None,
-                default_q_start: bool = False):
+                default_q_start: bool = False, softcap: float = 0.0):
     """The same pass on the oracle. Returns (k_cache, v_cache, bias, out)."""
     if step.k_new is not None:
         k_host = oracle.scatter(k_host, step.k_new, step.write_indices)
         v_host = oracle.scatter(v_host, step.v_new, step.write_indices)
     qs = None if default_q_start else step.q_start
     bias = oracle.bias(step.nonpad, qs, step.slot_kind, step.S_q, w.max_seq, w.window)
-    out = oracle.attention(step.q, k_host, v_host, bias, step.nonpad, w.scale, rows=rows)
+    out = oracle.attention(step.q, k_host, v_host, bias, step.nonpad, w.scale, rows=rows,
+                           softcap=softcap)
     return k_host, v_host, bias, out
 
 

@@ -40,12 +40,12 @@ def test_exports_every_declared_symbol(lib):
 
 def _fwd(lib, **kw):
     a = dict(out=None, q=None, k=None, v=None, bias=None, bdt=1, nonpad=None, qs=None, kind=None,
-             B=1, Hq=4, Hkv=2, S_q=1, T=64, D=64, scale=0.125, window=0, dtype=1, ws=None,
-             wsb=0, stream=None)
+             B=1, Hq=4, Hkv=2, S_q=1, T=64, D=64, scale=0.125, softcap=0.0, window=0, dtype=1,
+             ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib.attn_bias_gqa_fwd(a["out"], a["q"], a["k"], a["v"], a["bias"], a["bdt"],
                                  a["nonpad"], a["qs"], a["kind"], a["B"], a["Hq"], a["Hkv"],
-                                 a["S_q"], a["T"], a["D"], a["scale"], a["window"], a["dtype"],
+                                 a["S_q"], a["T"], a["D"], a["scale"], a["softcap"], a["window"], a["dtype"],
                                  a["ws"], a["wsb"], a["stream"])
 
 
@@ -57,6 +57,9 @@ FAKE = 1 << 20  # a 256-byte aligned address that is never dereferenced
     (dict(Hq=6, Hkv=4), INVALID, "multiple of Hkv"),
     (dict(S_q=65), INVALID, "must not exceed max_seq"),
     (dict(D=96), UNSUPPORTED, "D must be"),
+    (dict(softcap=-1.0), INVALID, "softcap"),
+    (dict(softcap=float("inf")), INVALID, "softcap"),
+    (dict(softcap=float("nan")), INVALID, "softcap"),
     (dict(dtype=7), UNSUPPORTED, "dtype"),
     (dict(out=FAKE, q=FAKE + 4096, k=FAKE + 8192, v=FAKE + 12288), INVALID, "null"),
     (dict(out=FAKE + 8, q=FAKE + 4096, k=FAKE + 8192, v=FAKE + 12288, nonpad=FAKE), INVALID,

@@ -163,6 +163,50 @@ def test_attention_small(name, variant):
                  f"{name}/{variant}")
 
 
+@pytest.mark.parametrize("variant", ["bias", "rules"])
+@pytest.mark.parametrize("name", ["decode_sliding", "decode_full", "decode_d64_g8", "prefill_vision",
+                                  "prefill_long", "prefill_d64_g8", "prefill_d128_g3"])
+@pytest.mark.parametrize("cap", [0.5, 20.0])
+def test_attention_softcap(name, variant, cap):
+    """softcap * tanh(scale * q.k / softcap) before the bias (skill page,
+    section 4), every kernel path: decode, direct-to-LDS prefill (D 64/256/512),
+    register-staged prefill (unaligned max_seq)."""
+    w = SMALL[name]()
+    step = w.steps[0]
+    announce(f"softcap={cap} {name} variant={variant} {w.describe()}")
+    _, _, bias_ref, ref = oracle_step(w, step, w.k_cache, w.v_cache, softcap=cap)
+    _, out = gpu_step(w, step, dev(w.k_cache), dev(w.v_cache), rules=(variant == "rules"), softcap=cap)
+    check_parity(to_f64(out), ref, w.dtype, dead_rows(bias_ref, step.nonpad, w.Hq),
+                 f"softcap{cap}/{name}/{variant}")
+
+
+def test_softcap_fp32_and_masked_poison():
+    """fp32 path with softcap, and the ordering property: a small cap with a -inf
+    bias entry and huge V at that key leaves the output as without the key."""
+    w = wl.tiny_fp32()
+    step = w.steps[0]
+    cap = 0.3
+    announce("softcap fp32 tiny")
+    _, _, bias_ref, ref = oracle_step(w, step, w.k_cache, w.v_cache, softcap=cap)
+    k_d, v_d = dev(w.k_cache), dev(w.v_cache)
+    _, out = gpu_step(w, step, k_d, v_d, softcap=cap)
+    check_parity(to_f64(out), ref, w.dtype, dead_rows(bias_ref, step.nonpad, w.Hq), "softcap/fp32")
+    # bf16 decode: mask one valid key of every row with -inf, poison its V
+    rng = wl.rng_for(610)
+    B, Hq, Hkv, T, D = 2, 8, 2, 96, 256
+    q = wl.normal(rng, (B, Hq, 1, D), torch.bfloat16)
+    k = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    v = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    nonpad = torch.tensor([T, 70], dtype=torch.int64)
+    bias = torch.zeros((B, 1, 1, T), dtype=torch.bfloat16)
+    bias[:, 0, 0, 10] = float("-inf")
+    v_poison = v.clone()
+    v_poison[:, :, 10] = 1e30
+    got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v_poison), dev(bias), dev(nonpad), 0.0625, softcap=cap)
+    ref2 = oracle.attention(q, k, v, bias, nonpad, 0.0625, softcap=cap)
+    check_parity(to_f64(got), ref2, torch.bfloat16, what="softcap/poison")
+
+
 def test_attention_rules_equal_bias_bitwise():
     for name in ("decode_sliding", "decode_full", "prefill_vision", "prefill_long"):
         w = SMALL[name]()
