@@ -32,12 +32,14 @@ FLAGS = [
 ]
 
 
-# Per-file additions. attn_prefill_dma.hip: matrix-core accumulators in the
-# ordinary vector registers (its O^T accumulators and every other value of the
-# loop fit in 256 of them), so the compiler does not copy the accumulators
-# between register files around the rare rescale branch on every tile.
+# Per-file additions. The direct-to-LDS prefill files: matrix-core
+# accumulators in the ordinary vector registers, so the compiler does not copy
+# them between register files around the rare rescale branch on every tile
+# (attn_prefill_dma_wide.hip places its D = 512 O^T accumulators in the
+# accumulation registers itself, through inline-asm operands).
 FILE_FLAGS = {
     "attn_prefill_dma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "attn_prefill_dma_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

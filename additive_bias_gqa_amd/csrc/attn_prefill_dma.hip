@@ -1,762 +1,17 @@
-// bf16 prefill attention with a direct-to-LDS tile pipeline (gfx950).
-//
-// Same computation as attn_prefill.hip: onnxruntime skill
-// "cuda-attention-kernel-patterns", section 4 (scale * QK^T, + bias, softmax,
-// times V), section 6 (rows with no allowed key write zeros; masked keys are
-// removed by selection), section 11 (external cache: keys are the slots below
-// nonpad_kv_seqlen); mobius issue #366 (the float bias carries the causal,
-// window, block-overlay and padding rules); query head h reads KV head h / G
-// (onnxruntime PR #28242, CPU GQA excerpt).
-//
-// What differs is how tiles reach LDS. Here every byte a tile needs - K and V
-// rows, and the tile's bias rows (or slot kinds) - is fetched with
-// global_load_lds_dwordx4 (RW = 32: the workgroup's Q rows too): each lane names a 16-byte global chunk and the
-// hardware writes the wavefront's 64 chunks to 1 KiB of consecutive LDS bytes
-// (lane i at base + 16*i). No vector registers hold tile data, so nothing in
-// the loop makes the compiler wait on a load, and NSTAGE tiles are in flight:
-//
-//   prologue   fetch tiles 0 .. NSTAGE-2
-//   tile t     wait until this wavefront's fetches of tile t have landed
-//              (s_waitcnt vmcnt: the fetches of the NSTAGE-2 younger tiles may
-//              still be in flight), barrier (every wavefront's part of tile t
-//              is in LDS, and every wavefront is done with tile t-1), fetch
-//              tile t+NSTAGE-1 into the stage tile t-1 used, compute tile t.
-//
-// Every wavefront issues the same number of fetches per stage (surplus bias or
-// kind fetches repeat one of identical bytes to the same place), so the wait
-// count is a compile-time constant.
-// Fetch indices past the end of the live list re-fetch the last live tile into
-// a stage nobody reads. Keys at or beyond nonpad are fetched from row
-// nonpad - 1 (a valid, finite row) and masked by selection, so the bits of
-// the slots past nonpad are never read.
-//
-// The swizzle of the K/V tiles is the one attn_prefill.hip uses: LDS chunk
-// position c of row r holds global chunk c ^ swz_bits<D>(r), so a wavefront
-// fetching one row's chunks in order writes them permuted, for free.
-//
-// RW = 32: 32-row wavefronts on 32x32x16 MFMAs (D <= 256); RW = 16: 16-row
-// wavefronts on 16x16x32 MFMAs (D = 512, where Q^T and O^T of 32 rows would not
-// fit a lane's registers). The compute per tile is that of attn_prefill.hip.
-#include <stdlib.h>
-#include <string.h>
-
-#include <type_traits>
-
-#include "prefill_common.h"
+// Dispatch of the direct-to-LDS prefill kernel (prefill_dma.h): which rows per
+// wavefront and wavefronts per workgroup serve a head size, and when the path
+// applies. Instantiations whose accumulators live in the ordinary vector
+// registers are compiled here; the D = 512 kernel with 32-row wavefronts
+// (accumulators in the accumulation registers) in attn_prefill_dma_wide.hip.
+#include "prefill_dma.h"
 
 namespace abgqa {
 
 namespace {
 
-// One wavefront-wide 16-byte-per-lane fetch into LDS at lds_wave_base (wave-
-// uniform) + 16 * lane. Issued as inline asm on purpose: the compiler tracks
-// its own direct-to-LDS loads and, unable to tell which LDS bytes they write,
-// waits for all of them before any later LDS read - which would drain the
-// whole pipeline every tile. Every wait for these fetches is the explicit
-// s_waitcnt below. M0 carries the LDS address (one wait state after writing
-// it) and is restored afterwards.
-__device__ __forceinline__ void dma16(const void* gsrc, const unsigned char* lds_wave_base) {
-  // wave-uniform by construction; readfirstlane makes that visible to the
-  // compiler, which must place it in a scalar register
-  const unsigned lds = __builtin_amdgcn_readfirstlane(
-      (unsigned)(size_t)((__attribute__((address_space(3))) const unsigned char*)lds_wave_base));
-  unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(gsrc), "s"(lds));
-}
-
-// The same fetch from a wave-uniform base address plus a per-lane 32-bit byte
-// offset (the scalar-base form: no per-lane address arithmetic).
-__device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff,
-                                        const unsigned char* lds_wave_base) {
-  const unsigned lds = __builtin_amdgcn_readfirstlane(
-      (unsigned)(size_t)((__attribute__((address_space(3))) const unsigned char*)lds_wave_base));
-  unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(sbase), "s"(lds));
-}
-
-// s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N <= 63, "vmcnt range");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-  asm volatile("" ::: "memory");
-}
-
-// Workgroup barrier without the memory fences of __syncthreads (which would
-// wait for every outstanding fetch); the asm statements keep the compiler from
-// moving LDS accesses across it.
-__device__ __forceinline__ void tile_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// 32-bit LDS address of a generic pointer into shared memory
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return (unsigned)(size_t)((__attribute__((address_space(3))) const void*)p);
-}
-
-// LDS reads at base + cofs. Bases are masked to 20 bits where they are formed
-// (LDS addresses are below 160 KiB), so the compiler knows base + cofs cannot
-// wrap and puts a constant cofs into the instruction's offset field instead of
-// adding it in a vector register for every read.
-template <typename T>
-__device__ __forceinline__ T lds_at(unsigned base, unsigned cofs) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) T*>((size_t)(base + cofs));
-}
-__device__ __forceinline__ u32x2 lds_tr16_at(unsigned base, unsigned cofs) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      reinterpret_cast<__attribute__((address_space(3))) s16x4*>((size_t)(base + cofs)));
-  return __builtin_bit_cast(u32x2, v);
-}
-constexpr unsigned kLdsMask = (1u << 20) - 1;
-
-constexpr int kLdsBudget = 160 * 1024 - 6 * 1024;   // stages; the rest: live list
-
-template <int D, int RW, int NW, bool kRules, typename BiasT>
-struct DmaGeom {
-  static constexpr int TILE_BYTES = kTileKeys * D * 2;         // one K (or V) tile
-  static constexpr int NKI = TILE_BYTES / 1024;                // fetches per K (or V) tile
-  static constexpr int MQ_MAX = RW * NW / 2;                   // query tokens, G >= 2
-  static constexpr int BROW = kTileKeys * (int)sizeof(BiasT);  // bias bytes per row per tile
-  static constexpr int MASK_BYTES = kRules ? 1024 : ((MQ_MAX * BROW + 1023) / 1024) * 1024;
-  static constexpr int NMI = MASK_BYTES / 1024;                // fetches for bias / kinds
-  static constexpr int PW = 2 * (NKI / NW) + (NMI + NW - 1) / NW;  // fetches per wavefront per stage
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + MASK_BYTES;
-  // RW = 32: the workgroup's Q rows live in LDS (the B operand of S^T is read
-  // from there), which keeps a lane's registers for the O^T accumulators
-  static constexpr bool kQLds = RW == 32;
-  static constexpr int Q_BYTES = kQLds ? RW * NW * D * 2 : 0;
-  static constexpr int NSTAGE0 = (kLdsBudget - Q_BYTES) / STAGE_BYTES;
-  static constexpr int NSTAGE = NSTAGE0 > 4 ? 4 : NSTAGE0;
-  static_assert(NSTAGE >= 2, "two stages must fit");
-  static_assert(PW * (NSTAGE - 2) <= 63, "wait count");
-};
-
-}  // namespace
-
-template <int D, int RW, int NW, bool kRules, typename BiasT>
-__global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p, int n_qt) {
-  using Geo = DmaGeom<D, RW, NW, kRules, BiasT>;
-  constexpr int NT = NW * 64;
-  constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
-  constexpr int NSTAGE = Geo::NSTAGE;
-  constexpr int TILE_BYTES = Geo::TILE_BYTES;
-  constexpr int STAGE_BYTES = Geo::STAGE_BYTES;
-  constexpr int NKI = Geo::NKI;
-  constexpr int PW = Geo::PW;
-  constexpr int KSTEPS = RW == 32 ? D / 16 : D / 32;   // k-steps of S^T over the head dim
-  constexpr int DBLK = D / RW;                         // d blocks of O^T
-  constexpr bool kQLds = Geo::kQLds;
-  constexpr int Q_BYTES = Geo::Q_BYTES;
-
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int T = p.T, G = p.G;
-  const int n_kt_max = num_tiles(T);
-  unsigned char* const stages = smem + Q_BYTES;   // [Q tile][stage 0][stage 1]...
-  uint32_t* s_bits = reinterpret_cast<uint32_t*>(stages + (size_t)NSTAGE * STAGE_BYTES);
-  const int n_words = (n_kt_max + 31) / 32;
-  uint16_t* s_list = reinterpret_cast<uint16_t*>(s_bits + n_words);
-  __shared__ int s_nlive;
-  __shared__ int32_t s_ids[4];
-  __shared__ int s_nids;
-
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = n_qt - 1 - (wg % n_qt);   // later (heavier) query tiles first
-  const int bh = wg / n_qt;
-  const int hk = bh % p.Hkv;
-  const int64_t b = bh / p.Hkv;
-  const int np = (int)clamp_nonpad(p.nonpad[b], T);
-  const int MQ = (RW * NW) / G;
-  const int s0 = qt * MQ;
-  const int s_end = min(s0 + MQ, p.S_q);
-  const int n_kt = num_tiles(np);
-
-  // ---- 1. this lane's query row (RW = 32: row 32*w + (l % 32); RW = 16: row
-  // 16*w + (l % 16)). RW = 16 keeps its Q^T fragments (k-chunk 4*i + l/16) in
-  // registers, loaded first so that the live-list scan's waits cover them. ----
-  const int col = lane & (RW - 1);
-  const int grp = lane / RW;
-  const int r = RW * w + col;
-  const int sl = r / G, g = r % G;
-  const int s = s0 + sl;
-  const bool row_ok = (r < MQ * G) && (s < p.S_q);
-  const int h = hk * G + g;
-  bf16x8 qf[kQLds ? 1 : KSTEPS];
-  if constexpr (!kQLds) {
-    const __bf16* qp = (const __bf16*)p.q + ((b * p.Hq + h) * p.S_q + (row_ok ? s : 0)) * (int64_t)D;
-#pragma unroll
-    for (int i = 0; i < KSTEPS; ++i) qf[i] = row_ok ? ld_global<bf16x8>(qp + 8 * (4 * i + grp)) : bf16x8{};
-  }
-  RowRule rule{};
-  if constexpr (kRules) {
-    if (row_ok) rule = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s, p.S_q, T, p.window);
-  }
-
-  // ---- 2. live tiles ---------------------------------------------------------
-  // read from LDS, the count is the same in every lane: say so, so that the
-  // loop below (and every LDS address derived from its counter) is scalar
-  const int n_live = __builtin_amdgcn_readfirstlane(
-      build_live_list<NT, kRules, BiasT>(p, b, np, s0, s_end, n_kt, s_bits, s_list, n_words, s_ids,
-                                         &s_nids, &s_nlive));
-  // nothing may be pending in registers once the pipeline starts: every wait
-  // in the loop below is the explicit one
-  wait_vmcnt<0>();
-
-  const float scale_log2 = p.scale * kLog2e;
-  const bool cap_on = p.softcap > 0.f;
-  const float cap2 = p.softcap * kLog2e, scale_over_cap = cap_on ? p.scale / p.softcap : 0.f;
-  const __bf16* kg = (const __bf16*)p.k + (b * p.Hkv + hk) * (int64_t)T * D;
-  const __bf16* vg = (const __bf16*)p.v + (b * p.Hkv + hk) * (int64_t)T * D;
-  const int32_t* kindb = p.slot_kind ? p.slot_kind + b * T : nullptr;
-  const BiasT* biasb = kRules ? nullptr : (const BiasT*)p.bias + b * p.S_q * (int64_t)T;
-
-  // ---- 3. one stage's fetches ----------------------------------------------
-  // Wavefront w fetches K rows [w*KPW*RPI, (w+1)*KPW*RPI) of the tile, the
-  // same V rows, and its share of the bias rows (or the slot kinds), so the
-  // kind of every fetch is known at compile time and the issue is branch-free.
-  constexpr int KPW = NKI / NW;            // K (and V) fetches per wavefront
-  constexpr int NMI = Geo::NMI;
-  constexpr int MPW = (NMI + NW - 1) / NW;  // bias / kind fetches per wavefront
-  constexpr int RPI = 64 / CPR;             // K/V rows per fetch
-  static_assert(NKI % NW == 0 && 64 % CPR == 0 && PW == 2 * KPW + MPW, "fetch layout");
-  const int lrow = lane / CPR, lcc = lane % CPR;
-  // byte offsets of this lane's chunks within a tile fully below nonpad, from
-  // the tile's first row (K and V alike) / first bias row / first slot kind
-  unsigned kv_off[KPW];
-#pragma unroll
-  for (int k = 0; k < KPW; ++k) {
-    const int kr = (w * KPW + k) * RPI + lrow;
-    kv_off[k] = (unsigned)(kr * D + 8 * (lcc ^ swz_bits<D>(kr))) * 2u;
-  }
-  unsigned m_off[MPW];
-#pragma unroll
-  for (int m = 0; m < MPW; ++m) {
-    if constexpr (kRules) {
-      m_off[m] = 16u * (unsigned)(lane & 7);    // lanes 8.. repeat lanes 0..7
-    } else {
-      constexpr int EPV = 16 / (int)sizeof(BiasT);
-      constexpr int CB = Geo::BROW / 16;       // 16-byte chunks per bias row
-      const int c = min(w * MPW + m, NMI - 1) * 64 + lane;
-      const int row = min(s0 + c / CB, p.S_q - 1) - s0;
-      m_off[m] = (unsigned)(row * T + (c % CB) * EPV) * (unsigned)sizeof(BiasT);
-    }
-  }
-  // fetch f of this wavefront's PW for the tile starting at key j0 into the
-  // stage at sb: f < 2*KPW are K and V rows (K for even f), the rest bias rows
-  // or slot kinds. f is a compile-time constant at every call.
-  auto fetch_one = [&](const int f, const int j0, unsigned char* sb) {
-    if (j0 + kTileKeys <= np) {
-      // the usual case: every row of the tile is valid, uniform base + offsets
-      if (f < 2 * KPW) {
-        const int k = f >> 1;
-        const int ii = w * KPW + k;
-        if ((f & 1) == 0) dma16_s(kg + (int64_t)j0 * D, kv_off[k], sb + ii * 1024);
-        else dma16_s(vg + (int64_t)j0 * D, kv_off[k], sb + TILE_BYTES + ii * 1024);
-      } else {
-        const int m = f - 2 * KPW;
-        const int ii = min(w * MPW + m, NMI - 1);   // surplus fetches repeat the last one
-        const void* mb;
-        if constexpr (kRules) mb = kindb ? (const void*)(kindb + j0) : (const void*)kg;
-        else mb = biasb + (int64_t)s0 * T + j0;
-        dma16_s(mb, m_off[m], sb + 2 * TILE_BYTES + ii * 1024);
-      }
-    } else {
-      // the tile crossing nonpad: rows at or past it are fetched from row
-      // nonpad - 1; bias / kind chunks past the cache end from its last chunk
-      if (f < 2 * KPW) {
-        const int k = f >> 1;
-        const int ii = w * KPW + k;
-        const int kr = ii * RPI + lrow;
-        const int64_t off = (int64_t)min(j0 + kr, np - 1) * D + 8 * (lcc ^ swz_bits<D>(kr));
-        if ((f & 1) == 0) dma16(kg + off, sb + ii * 1024);
-        else dma16(vg + off, sb + TILE_BYTES + ii * 1024);
-      } else {
-        const int m = f - 2 * KPW;
-        const int ii = min(w * MPW + m, NMI - 1);
-        unsigned char* dst = sb + 2 * TILE_BYTES + ii * 1024;
-        if constexpr (kRules) {
-          dma16(kindb ? (const void*)(kindb + min(j0 + 4 * (lane & 7), T - 4)) : (const void*)kg, dst);
-        } else {
-          constexpr int EPV = 16 / (int)sizeof(BiasT);
-          constexpr int CB = Geo::BROW / 16;
-          const int c = ii * 64 + lane;
-          const int srow = min(s0 + c / CB, p.S_q - 1);
-          dma16(biasb + (int64_t)srow * T + min(j0 + (c % CB) * EPV, T - EPV), dst);
-        }
-      }
-    }
-  };
-  auto tile_key0 = [&](int t_idx) {
-    return __builtin_amdgcn_readfirstlane((int)s_list[min(t_idx, n_live - 1)] * kTileKeys);
-  };
-  auto fetch_stage = [&](int t_idx, int stage) {
-    const int j0 = tile_key0(t_idx);
-    unsigned char* sb = stages + stage * STAGE_BYTES;
-#pragma unroll
-    for (int f = 0; f < PW; ++f) fetch_one(f, j0, sb);
-  };
-
-  // ---- 4. main loop ---------------------------------------------------------
-  using Acc = typename std::conditional<RW == 32, f32x16, f32x4>::type;
-  Acc oacc[DBLK];
-#pragma unroll
-  for (int i = 0; i < DBLK; ++i) oacc[i] = Acc{};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  if (n_live > 0) {
-    if constexpr (kQLds) {
-      // the workgroup's Q rows into the swizzled Q tile (row r = s_local*G + g,
-      // clamped to a valid row past the chunk); older than every stage fetch,
-      // so the first tile's wait covers them too
-      constexpr int QPW = Q_BYTES / 1024 / NW;
-#pragma unroll
-      for (int k = 0; k < QPW; ++k) {
-        const int ii = w * QPW + k;
-        const int c = ii * 64 + lane;
-        const int qr = c / CPR, cc = c % CPR;
-        const int qs = min(s0 + qr / G, p.S_q - 1);
-        const int qh = hk * G + qr % G;
-        dma16((const __bf16*)p.q + ((b * p.Hq + qh) * p.S_q + qs) * (int64_t)D + 8 * (cc ^ swz_bits<D>(qr)),
-              smem + ii * 1024);
-      }
-    }
-#pragma unroll
-    for (int st = 0; st < NSTAGE - 1; ++st) fetch_stage(st, st);
-  }
-  // Per-lane byte offsets into the swizzled tiles. Chunk c of row r sits at
-  // 16 * (c ^ swz_bits<D>(r)); the XOR touches only the low SWB bits of c, so the
-  // reads of one lane need a few base offsets (by those low bits of c) plus
-  // compile-time multiples of SPAN = 16 << SWB bytes.
-  constexpr int SWB = swz_width<D>();
-  constexpr int SPAN = 16 << SWB;
-  // RW = 32: K/Q chunk 2*i + grp -> groups i % NKG; V chunk 4*blk + vdofs/8 ->
-  // groups blk % NVG, times the two 8-row halves (the swizzle sees row bit 3).
-  // RW = 16: K chunk 4*i + grp -> groups i % NKG; V chunk 2*blk + vdofs/8 ->
-  // groups blk % NVG.
-  constexpr int NKG = RW == 32 ? (1 << SWB) / 2 : (1 << SWB) / 4;
-  constexpr int NVG = RW == 32 ? (1 << SWB) / 4 : (1 << SWB) / 2;
-  unsigned k_lane[NKG];                  // K (and, RW = 32, Q) rows
-  unsigned v_lane[RW == 32 ? 2 : 1][NVG];  // V^T transposing reads
-  if constexpr (RW == 32) {
-    // S^T: lane reads row col, chunk 2*i + grp
-#pragma unroll
-    for (int m = 0; m < NKG; ++m)
-      k_lane[m] = (unsigned)(col * D * 2 + 16 * ((2 * m + grp) ^ swz_bits<D>(col)));
-    // PV: lane 16*gq + 4*kq + jq reads row 16*step + 8*half + vkey0, d = 32*blk +
-    // vdofs: chunk 4*blk + vdofs/8
-    const int gq = lane >> 4, kq = (lane >> 2) & 3, jq = lane & 3;
-    const int vkey0 = 4 * (gq >> 1) + kq;
-    const int vdofs = 16 * (gq & 1) + 4 * jq;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int m = 0; m < NVG; ++m) {
-        const int row = 8 * hf + vkey0;
-        v_lane[hf][m] = (unsigned)(row * D * 2 + 16 * ((4 * m + (vdofs >> 3)) ^ swz_bits<D>(row)) +
-                                   2 * (vdofs & 7));
-      }
-  } else {
-    // S^T: row 16*kb + col, chunk 4*i + grp
-#pragma unroll
-    for (int m = 0; m < NKG; ++m)
-      k_lane[m] = (unsigned)(col * D * 2 + 16 * ((4 * m + grp) ^ swz_bits<D>(col)));
-    // PV: lane 16*g + 4*k + j reads row vkey0 (+16), d = 16*blk + vdofs:
-    // chunk 2*blk + vdofs/8
-    const int vkey0 = lane >> 2;
-    const int vdofs = 4 * (lane & 3);
-#pragma unroll
-    for (int m = 0; m < NVG; ++m)
-      v_lane[0][m] = (unsigned)(vkey0 * D * 2 + 16 * ((2 * m + (vdofs >> 3)) ^ swz_bits<D>(vkey0)) +
-                                2 * (vdofs & 7));
-  }
-  // this wavefront's Q rows (RW = 32), one base per k-chunk group
-  unsigned q_base[RW == 32 ? NKG : 1];
-  if constexpr (RW == 32) {
-    const unsigned qa0 = lds_addr(smem) + (unsigned)(RW * w * D * 2);
-#pragma unroll
-    for (int m = 0; m < NKG; ++m) q_base[m] = (qa0 + k_lane[m]) & kLdsMask;
-  }
-  for (int t = 0; t < n_live; ++t) {
-    wait_vmcnt<PW * (NSTAGE - 2)>();
-    tile_barrier();
-    fetch_stage(t + NSTAGE - 1, (t + NSTAGE - 1) % NSTAGE);
-
-    const int j0 = __builtin_amdgcn_readfirstlane((int)s_list[t] * kTileKeys);
-    const unsigned char* sb = stages + (t % NSTAGE) * STAGE_BYTES;
-    const bool full = j0 + kTileKeys <= np;   // no key of the tile at or past nonpad
-    const unsigned char* ms = sb + 2 * TILE_BYTES;
-    const unsigned sb_a = lds_addr(sb);
-    unsigned k_base[NKG], v_base[RW == 32 ? 2 : 1][NVG];
-#pragma unroll
-    for (int m = 0; m < NKG; ++m) k_base[m] = (sb_a + k_lane[m]) & kLdsMask;
-#pragma unroll
-    for (int hf = 0; hf < (RW == 32 ? 2 : 1); ++hf)
-#pragma unroll
-      for (int m = 0; m < NVG; ++m) v_base[hf][m] = (sb_a + TILE_BYTES + v_lane[hf][m]) & kLdsMask;
-
-    if constexpr (RW == 32) {
-      // this lane's bias values (or slot kinds) for keys 8*i + 4*(l/32) + jj,
-      // read first so their latency hides under the S^T MFMAs
-      BiasT bvs[4][4];
-      int32_t kvs[4][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kb = 8 * i + 4 * grp;
-        if constexpr (kRules) {
-          if (kindb) *reinterpret_cast<int4*>(kvs[i]) = *reinterpret_cast<const int4*>(ms + 4 * kb);
-          else *reinterpret_cast<int4*>(kvs[i]) = int4{0, 0, 0, 0};
-        } else {
-          const BiasT* br = reinterpret_cast<const BiasT*>(ms) + sl * kTileKeys + kb;
-          if constexpr (sizeof(BiasT) == 2) *reinterpret_cast<u32x2*>(bvs[i]) = *reinterpret_cast<const u32x2*>(br);
-          else *reinterpret_cast<u32x4*>(bvs[i]) = *reinterpret_cast<const u32x4*>(br);
-        }
-      }
-      // S^T = K Q^T; lane l: query row l % 32, keys 8*i + 4*(l/32) + jj
-      // fragments of k-step i + PD are read while the MFMA of step i runs
-      constexpr int PD = KSTEPS < 4 ? KSTEPS : 4;
-      f32x16 sacc = f32x16{};
-      bf16x8 ka[PD], qa[PD];
-#pragma unroll
-      for (int i = 0; i < PD; ++i) {
-        ka[i] = lds_at<bf16x8>(k_base[i % NKG], SPAN * (i / NKG));
-        qa[i] = lds_at<bf16x8>(q_base[i % NKG], SPAN * (i / NKG));
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD, 0);
-#pragma unroll
-      for (int i = 0; i < KSTEPS; ++i) {
-        const bf16x8 a = ka[i % PD], qb = qa[i % PD];
-        if (i + PD < KSTEPS) {
-          ka[i % PD] = lds_at<bf16x8>(k_base[(i + PD) % NKG], SPAN * ((i + PD) / NKG));
-          qa[i % PD] = lds_at<bf16x8>(q_base[(i + PD) % NKG], SPAN * ((i + PD) / NKG));
-        }
-        sacc = mfma32x32x16(a, qb, sacc);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i + PD < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      // V^T fragments of the first PV MFMAs, read while the softmax runs.
-      // MFMA u = 2*blk + step; lane 16*gq + 4*kq + jq reads
-      // V[16*step + 8*half + 4*(gq/2) + kq][32*blk + 16*(gq%2) + 4*jq]
-      constexpr int NU = 2 * DBLK;
-      constexpr int PVD = NU < 4 ? NU : 4;
-      auto vread = [&](int u) {
-        const int blk = u >> 1;
-        const unsigned so = SPAN * (blk / NVG) + 16 * (u & 1) * D * 2;
-        const u32x2 lo = lds_tr16_at(v_base[0][blk % NVG], so);
-        const u32x2 hi = lds_tr16_at(v_base[1][blk % NVG], so);
-        return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-      };
-      bf16x8 vf[PVD];
-#pragma unroll
-      for (int u = 0; u < PVD; ++u) vf[u] = vread(u);
-      // softcap (0 = none) on scale * q.k, before the bias: capped base-2 scores,
-      // multiplier 1 (a real branch, not selects on every tile)
-      float sl = scale_log2;
-      if (cap_on) {
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[e] = softcap_base2(sacc[e], cap2, scale_over_cap);
-        sl = 1.f;
-      }
-      float x[16];
-      float mt = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kb = 8 * i + 4 * grp;          // first of this lane's 4 keys
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int j = j0 + kb + jj;
-          float v;
-          if constexpr (kRules) {
-            // allowed() includes j < nonpad; a row past the chunk has no rule
-            v = rule.allowed(j, kvs[i][jj]) ? sacc[4 * i + jj] * sl : -INFINITY;
-          } else {
-            // a -inf bias gives -inf (the score is finite: every fetched key row
-            // is a valid row); keys at or past nonpad only in a partial tile
-            v = fmaf(sacc[4 * i + jj], sl, bias_f32<BiasT>(bvs[i][jj]) * kLog2e);
-          }
-          x[4 * i + jj] = v;
-        }
-      }
-      if constexpr (!kRules) {
-        if (!full) {
-          // the tile crossing nonpad: keys at or past it are not keys (a real
-          // branch, taken at most once per workgroup)
-          asm volatile("" ::: "memory");
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (j0 + 8 * (e >> 2) + 4 * grp + (e & 3) >= np) x[e] = -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, x[e]);
-      mt = fmaxf(mt, lane_xor(mt, 32));
-      const float mn = fmaxf(m_run, mt);
-      const bool need = mn > m_run + kRescaleThreshold;
-      const bool rescale = __any(need);
-      float alpha = 1.f;
-      if (rescale) {
-        alpha = need ? fast_exp2(m_run - mn) : 1.f;
-        if (need) m_run = mn;
-        l_run *= alpha;
-      }
-      // 2^(-inf) = 0 for masked keys; a row with no live key yet subtracts 0
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      uint32_t pw[8];
-      float lsum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        const float p0 = fast_exp2(x[e] - m_use);
-        const float p1 = fast_exp2(x[e + 1] - m_use);
-        const uint32_t pk = pack_bf16x2(p0, p1);
-        lsum += bf16lo(pk) + bf16hi(pk);
-        pw[e >> 1] = pk;
-      }
-      l_run += lsum;
-      const bf16x8 pb0 = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-      const bf16x8 pb1 = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
-      if (rescale) {
-        // rare (the running maximum rose by more than 8): a real branch - the
-        // asm keeps the compiler from turning it into selects executed on every
-        // tile, which would also pull the accumulators out of their registers
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int blk = 0; blk < DBLK; ++blk) oacc[blk] *= alpha;
-      }
-      // O^T += V^T P^T, fragments read PVD MFMAs ahead
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const bf16x8 va = vf[u % PVD];
-        if (u + PVD < NU) vf[u % PVD] = vread(u + PVD);
-        oacc[u >> 1] = mfma32x32x16(va, (u & 1) ? pb1 : pb0, oacc[u >> 1]);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (u + PVD < NU) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-    } else {
-      // this lane's bias values (or slot kinds) for keys 16*kb + 4*(l/16) + e,
-      // read first so their latency hides under the S^T MFMAs
-      BiasT bvs[2][4];
-      int32_t kvs[2][4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int kf = 16 * kb + 4 * grp;
-        if constexpr (kRules) {
-          if (kindb) *reinterpret_cast<int4*>(kvs[kb]) = *reinterpret_cast<const int4*>(ms + 4 * kf);
-          else *reinterpret_cast<int4*>(kvs[kb]) = int4{0, 0, 0, 0};
-        } else {
-          const BiasT* br = reinterpret_cast<const BiasT*>(ms) + sl * kTileKeys + kf;
-          if constexpr (sizeof(BiasT) == 2) *reinterpret_cast<u32x2*>(bvs[kb]) = *reinterpret_cast<const u32x2*>(br);
-          else *reinterpret_cast<u32x4*>(bvs[kb]) = *reinterpret_cast<const u32x4*>(br);
-        }
-      }
-      // S^T = K Q^T in two 16-key halves; lane l: query row l % 16, keys
-      // 16*kb + 4*(l/16) + e
-      f32x4 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        constexpr int PD = 8;   // K fragments read PD steps ahead of their MFMA
-        bf16x8 ka[PD];
-#pragma unroll
-        for (int i = 0; i < PD; ++i)
-          ka[i] = lds_at<bf16x8>(k_base[i % NKG], SPAN * (i / NKG) + kb * 16 * D * 2);
-        __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
-#pragma unroll
-        for (int i = 0; i < KSTEPS; ++i) {
-          const bf16x8 a = ka[i % PD];
-          if (i + PD < KSTEPS)
-            ka[i % PD] = lds_at<bf16x8>(k_base[(i + PD) % NKG], SPAN * ((i + PD) / NKG) + kb * 16 * D * 2);
-          sacc[kb] = mfma16x16x32(a, qf[i], sacc[kb]);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i + PD < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-      }
-      // V^T fragments of the first PV MFMAs, read while the softmax runs;
-      // lane 16*gq + 4*kq + jq reads V[4*gq + kq (+16)][16*blk + 4*jq]
-      constexpr int PVD = 4;
-      auto vread = [&](int blk) {
-        const unsigned so = SPAN * (blk / NVG);
-        const u32x2 lo = lds_tr16_at(v_base[0][blk % NVG], so);
-        const u32x2 hi = lds_tr16_at(v_base[0][blk % NVG], so + 16 * D * 2);
-        return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-      };
-      bf16x8 vf[PVD];
-#pragma unroll
-      for (int u = 0; u < PVD; ++u) vf[u] = vread(u);
-      float sl = scale_log2;
-      if (cap_on) {
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sacc[kb][e] = softcap_base2(sacc[kb][e], cap2, scale_over_cap);
-        sl = 1.f;
-      }
-      float x[8];
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int kf = 16 * kb + 4 * grp;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = j0 + kf + e;
-          float v;
-          if constexpr (kRules) {
-            v = rule.allowed(j, kvs[kb][e]) ? sacc[kb][e] * sl : -INFINITY;
-          } else {
-            v = fmaf(sacc[kb][e], sl, bias_f32<BiasT>(bvs[kb][e]) * kLog2e);
-          }
-          x[4 * kb + e] = v;
-        }
-      }
-      if constexpr (!kRules) {
-        if (!full) {
-          asm volatile("" ::: "memory");
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (j0 + 16 * (e >> 2) + 4 * grp + (e & 3) >= np) x[e] = -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mt = fmaxf(mt, x[e]);
-      mt = fmaxf(mt, lane_xor(mt, 16));
-      mt = fmaxf(mt, lane_xor(mt, 32));
-      const float mn = fmaxf(m_run, mt);
-      const bool need = mn > m_run + kRescaleThreshold;
-      const bool rescale = __any(need);
-      float alpha = 1.f;
-      if (rescale) {
-        alpha = need ? fast_exp2(m_run - mn) : 1.f;
-        if (need) m_run = mn;
-        l_run *= alpha;
-      }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      uint32_t pw[4];
-      float lsum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float p0 = fast_exp2(x[e] - m_use);
-        const float p1 = fast_exp2(x[e + 1] - m_use);
-        const uint32_t pk = pack_bf16x2(p0, p1);
-        lsum += bf16lo(pk) + bf16hi(pk);
-        pw[e >> 1] = pk;
-      }
-      l_run += lsum;
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-      if (rescale) {
-        // rare (the running maximum rose by more than 8): a real branch - the
-        // asm keeps the compiler from turning it into selects executed on every
-        // tile, which would also pull the accumulators out of their registers
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int blk = 0; blk < DBLK; ++blk) oacc[blk] *= alpha;
-      }
-      // O^T += V^T P^T, fragments read PVD MFMAs ahead
-#pragma unroll
-      for (int blk = 0; blk < DBLK; ++blk) {
-        const bf16x8 va = vf[blk % PVD];
-        if (blk + PVD < DBLK) vf[blk % PVD] = vread(blk + PVD);
-        oacc[blk] = mfma16x16x32(va, pb, oacc[blk]);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (blk + PVD < DBLK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-    }
-  }
-  // the fetches of the re-fetched tail stages must land before the workgroup
-  // (and its LDS) ends
-  wait_vmcnt<0>();
-
-  // ---- 5. normalise and store -----------------------------------------------
-  float l_tot = l_run;
-  if constexpr (RW == 16) l_tot += lane_xor(l_tot, 16);
-  l_tot += lane_xor(l_tot, 32);
-  if (row_ok) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* op = (uint16_t*)p.out + ((b * p.Hq + h) * p.S_q + s) * (int64_t)D;
-    if constexpr (RW == 32) {
-      // O^T lane l: row l % 32, d = 32*blk + 8*i + 4*(l/32) + jj
-#pragma unroll
-      for (int blk = 0; blk < DBLK; ++blk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          u32x2 pk;
-          pk.x = pack_bf16x2(oacc[blk][4 * i + 0] * inv, oacc[blk][4 * i + 1] * inv);
-          pk.y = pack_bf16x2(oacc[blk][4 * i + 2] * inv, oacc[blk][4 * i + 3] * inv);
-          *reinterpret_cast<u32x2*>(op + 32 * blk + 8 * i + 4 * grp) = pk;
-        }
-    } else {
-      // O^T lane l: row l % 16, d = 16*blk + 4*(l/16) + e
-#pragma unroll
-      for (int blk = 0; blk < DBLK; ++blk) {
-        u32x2 pk;
-        pk.x = pack_bf16x2(oacc[blk][0] * inv, oacc[blk][1] * inv);
-        pk.y = pack_bf16x2(oacc[blk][2] * inv, oacc[blk][3] * inv);
-        *reinterpret_cast<u32x2*>(op + 16 * blk + 4 * grp) = pk;
-      }
-    }
-  }
-}
-
-namespace {
-
-template <int D, int RW, int NW, bool kRules, typename BiasT>
-hipError_t launch_dma_inst(const AttnParams& p, hipStream_t stream) {
-  using Geo = DmaGeom<D, RW, NW, kRules, BiasT>;
-  const int MQ = (RW * NW) / p.G;
-  const int n_qt = (p.S_q + MQ - 1) / MQ;
-  const int n_kt = num_tiles(p.T);
-  const size_t list = (size_t)((n_kt + 31) / 32) * 4 + (size_t)n_kt * 2;
-  const size_t lds = (size_t)Geo::Q_BYTES + (size_t)Geo::NSTAGE * Geo::STAGE_BYTES +
-                     ((list + 15) & ~(size_t)15);
-  auto kern = attn_prefill_dma_kernel<D, RW, NW, kRules, BiasT>;
-  // opt in to exactly the dynamic LDS of this launch (the kernel's static LDS
-  // comes on top)
-  static size_t lds_set = 0;   // per instantiation
-  if (lds > lds_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) {
-      set_launch_detail("hipFuncSetAttribute(MaxDynamicSharedMemorySize), direct-to-LDS prefill");
-      return e;
-    }
-    lds_set = lds;
-  }
-  const dim3 grid((unsigned)((int64_t)n_qt * p.B * p.Hkv));
-  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, stream, p, n_qt);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) set_launch_detail("direct-to-LDS prefill kernel launch");
-  return e;
-}
-
-template <int D, int RW, int NW>
-hipError_t launch_dma_v(const AttnParams& p, hipStream_t stream) {
-  if (p.bias == nullptr) return launch_dma_inst<D, RW, NW, true, uint16_t>(p, stream);
-  if (p.bias_is_bf16) return launch_dma_inst<D, RW, NW, false, uint16_t>(p, stream);
-  return launch_dma_inst<D, RW, NW, false, uint32_t>(p, stream);
-}
-
 // ABGQA_PREFILL_CFG (tuning): "32x2", "32x4", "16x4", "16x8" picks rows per
-// wavefront x wavefronts per workgroup; otherwise the default below.
+// wavefront x wavefronts per workgroup ("32x2r", "32x4r": Q^T in registers);
+// otherwise the default below.
 static int prefill_cfg() {
   static const int v = [] {
     const char* e = getenv("ABGQA_PREFILL_CFG");
@@ -765,6 +20,8 @@ static int prefill_cfg() {
     if (!strcmp(e, "32x4")) return 2;
     if (!strcmp(e, "16x4")) return 3;
     if (!strcmp(e, "16x8")) return 4;
+    if (!strcmp(e, "32x2r")) return 5;
+    if (!strcmp(e, "32x4r")) return 6;
     return 0;
   }();
   return v;
@@ -775,8 +32,16 @@ hipError_t launch_dma_d(const AttnParams& p, hipStream_t stream) {
   const int cfg = prefill_cfg();
   if constexpr (D >= 512) {
     if (cfg == 4) return launch_dma_v<D, 16, 8>(p, stream);
-    return launch_dma_v<D, 16, 4>(p, stream);
+    if (cfg == 3) return launch_dma_v<D, 16, 4>(p, stream);
+    // 4 wavefronts of 32 rows (Q^T in registers, O^T in the accumulation
+    // registers): each K/V tile fetched once for 128 rows, each LDS read
+    // feeding a 32-row MFMA
+    return launch_attn_prefill_dma_qreg(p, 4, stream);
   } else {
+    if constexpr (D == 256) {
+      if (cfg == 5) return launch_attn_prefill_dma_qreg(p, 2, stream);
+      if (cfg == 6) return launch_attn_prefill_dma_qreg(p, 4, stream);
+    }
     if (cfg == 1) return launch_dma_v<D, 32, 2>(p, stream);
     if (cfg == 2) return launch_dma_v<D, 32, 4>(p, stream);
     if constexpr (D >= 128) {   // a tile must split evenly over the wavefronts

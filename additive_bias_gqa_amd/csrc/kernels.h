@@ -67,6 +67,9 @@ hipError_t launch_attn_prefill(const AttnParams& p, hipStream_t stream);
 // direct-to-LDS prefill pipeline (attn_prefill_dma.hip) and when it applies
 bool prefill_dma_supported(const AttnParams& p);
 hipError_t launch_attn_prefill_dma(const AttnParams& p, hipStream_t stream);
+// the same kernel with 32-row wavefronts and Q^T in registers
+// (attn_prefill_dma_wide.hip): D = 512 with nw = 4, D = 256 with nw = 2 or 4
+hipError_t launch_attn_prefill_dma_qreg(const AttnParams& p, int nw, hipStream_t stream);
 size_t prefill_lds_bytes(int D, int max_seq);
 
 }  // namespace abgqa
