@@ -143,7 +143,7 @@ size_t attn_bias_gqa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t
                                      int64_t max_seq, int64_t D) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_q <= 0 || max_seq <= 0 || D <= 0 || Hq % Hkv) return 0;
   const int64_t G = Hq / Hkv;
-  if (S_q * G > 16) return 0;  // prefill path: no workspace
+  if (S_q * G > 16) return abgqa::prefill_workspace_bytes(B, Hq, Hkv, S_q, max_seq, D);
   return abgqa::decode_workspace_bytes(B, Hkv, S_q, G, D, max_seq);
 }
 
@@ -207,6 +207,12 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
     if (G > 64) return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: more than 64 query heads per KV head");
     if (abgqa::prefill_lds_bytes((int)D, (int)max_seq) > 160 * 1024)
       return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: max_seq too large for the prefill tile list");
+    if (workspace && !aligned(workspace, 16))
+      return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: workspace not 16-byte aligned");
+    // optional here: with less than attn_bias_gqa_workspace_bytes() the
+    // kernel finds its live tiles from the bias itself
+    p.ws = workspace;
+    p.ws_bytes = workspace ? workspace_bytes : 0;
     e = abgqa::launch_attn_prefill(p, st);
   }
   if (log_enabled())

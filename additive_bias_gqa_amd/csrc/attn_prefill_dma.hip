@@ -27,33 +27,53 @@ static int prefill_cfg() {
   return v;
 }
 
+// Rows per wavefront x wavefronts per workgroup for a shape. D = 512: 4
+// wavefronts of 32 rows (Q^T in registers, O^T in the accumulation registers):
+// each K/V tile fetched once for 128 rows, each LDS read feeding a 32-row MFMA.
+// D = 128, 256: 4 wavefronts of 16 rows keep all four SIMDs of a CU busy with
+// one workgroup per CU (64 rows; the LDS holds one workgroup's stages). D = 64
+// (a tile too small to split four ways): 32-row wavefronts, 4 of them when
+// that still gives a workgroup per CU.
+enum class DmaCfg { k16x4, k16x8, k32x2, k32x4, k32x2r, k32x4r };
+
+DmaCfg dma_cfg(int D, int64_t B, int64_t Hkv, int64_t S_q, int64_t G) {
+  const int cfg = prefill_cfg();
+  if (D >= 512) {
+    if (cfg == 4) return DmaCfg::k16x8;
+    if (cfg == 3) return DmaCfg::k16x4;
+    return DmaCfg::k32x4r;
+  }
+  if (D == 256 && cfg == 5) return DmaCfg::k32x2r;
+  if (D == 256 && cfg == 6) return DmaCfg::k32x4r;
+  if (cfg == 1) return DmaCfg::k32x2;
+  if (cfg == 2) return DmaCfg::k32x4;
+  if (D >= 128) return cfg == 4 ? DmaCfg::k16x8 : DmaCfg::k16x4;
+  const int64_t wg4 = B * Hkv * ((S_q * G + 127) / 128);
+  return wg4 >= 256 ? DmaCfg::k32x4 : DmaCfg::k32x2;
+}
+
+int dma_rows(DmaCfg c) {
+  return (c == DmaCfg::k16x4 || c == DmaCfg::k32x2 || c == DmaCfg::k32x2r) ? 64 : 128;
+}
+
 template <int D>
 hipError_t launch_dma_d(const AttnParams& p, hipStream_t stream) {
-  const int cfg = prefill_cfg();
+  const DmaCfg c = dma_cfg(D, p.B, p.Hkv, p.S_q, p.G);
   if constexpr (D >= 512) {
-    if (cfg == 4) return launch_dma_v<D, 16, 8>(p, stream);
-    if (cfg == 3) return launch_dma_v<D, 16, 4>(p, stream);
-    // 4 wavefronts of 32 rows (Q^T in registers, O^T in the accumulation
-    // registers): each K/V tile fetched once for 128 rows, each LDS read
-    // feeding a 32-row MFMA
+    if (c == DmaCfg::k16x8) return launch_dma_v<D, 16, 8>(p, stream);
+    if (c == DmaCfg::k16x4) return launch_dma_v<D, 16, 4>(p, stream);
     return launch_attn_prefill_dma_qreg(p, 4, stream);
   } else {
     if constexpr (D == 256) {
-      if (cfg == 5) return launch_attn_prefill_dma_qreg(p, 2, stream);
-      if (cfg == 6) return launch_attn_prefill_dma_qreg(p, 4, stream);
+      if (c == DmaCfg::k32x2r) return launch_attn_prefill_dma_qreg(p, 2, stream);
+      if (c == DmaCfg::k32x4r) return launch_attn_prefill_dma_qreg(p, 4, stream);
     }
-    if (cfg == 1) return launch_dma_v<D, 32, 2>(p, stream);
-    if (cfg == 2) return launch_dma_v<D, 32, 4>(p, stream);
+    if (c == DmaCfg::k32x2) return launch_dma_v<D, 32, 2>(p, stream);
+    if (c == DmaCfg::k32x4) return launch_dma_v<D, 32, 4>(p, stream);
     if constexpr (D >= 128) {   // a tile must split evenly over the wavefronts
-      if (cfg == 3) return launch_dma_v<D, 16, 4>(p, stream);
-      if (cfg == 4) return launch_dma_v<D, 16, 8>(p, stream);
+      if (c == DmaCfg::k16x8) return launch_dma_v<D, 16, 8>(p, stream);
+      return launch_dma_v<D, 16, 4>(p, stream);
     }
-    // D >= 128: 4 wavefronts of 16 rows keep all four SIMDs of a CU busy with
-    // one workgroup per CU (64 rows; the LDS holds one workgroup's stages).
-    // D = 64 (a tile too small to split four ways): 32-row wavefronts.
-    if constexpr (D >= 128) return launch_dma_v<D, 16, 4>(p, stream);
-    const int64_t wg4 = (int64_t)p.B * p.Hkv * ((p.S_q * (int64_t)p.G + 127) / 128);
-    if (wg4 >= 256) return launch_dma_v<D, 32, 4>(p, stream);
     return launch_dma_v<D, 32, 2>(p, stream);
   }
 }
@@ -75,6 +95,20 @@ bool prefill_dma_supported(const AttnParams& p) {
     if ((p.T % 4) != 0) return false;
   }
   return p.T >= 8;
+}
+
+// The live-tile map of the shape's configuration: one bit per (batch row,
+// query tile, key tile). Shapes that take another path simply leave the
+// scratch unused.
+size_t prefill_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q, int64_t max_seq,
+                               int64_t D) {
+  if (D != 64 && D != 128 && D != 256 && D != 512) return 0;
+  const int64_t G = Hq / Hkv;
+  if (G < 2 || G > 64 || max_seq > 32768) return 0;
+  const int64_t mq = dma_rows(dma_cfg((int)D, B, Hkv, S_q, G)) / G;
+  const int64_t n_qt = (S_q + mq - 1) / mq;
+  const int64_t n_words = (num_tiles((int)max_seq) + 31) / 32;
+  return (size_t)(B * n_qt * n_words) * sizeof(uint32_t);
 }
 
 hipError_t launch_attn_prefill_dma(const AttnParams& p, hipStream_t stream) {

@@ -50,6 +50,14 @@ struct AttnParams {
   // split-KV decode
   float* ws_part;            // partial results, one record per (b, kv head, split)
   int n_split;
+  // prefill: caller scratch (may be null); the direct-to-LDS path keeps its
+  // live-tile map there when it is large enough
+  void* ws;
+  size_t ws_bytes;
+  // prefill, bias variant: live-tile map [B][query tiles][words] built by a
+  // pass over the bias before the attention kernel, or null (each workgroup
+  // then scans its bias rows itself)
+  const uint32_t* tilemap;
 };
 
 // fp32 path (any S_q): one wavefront per query row.
@@ -67,6 +75,9 @@ hipError_t launch_attn_prefill(const AttnParams& p, hipStream_t stream);
 // direct-to-LDS prefill pipeline (attn_prefill_dma.hip) and when it applies
 bool prefill_dma_supported(const AttnParams& p);
 hipError_t launch_attn_prefill_dma(const AttnParams& p, hipStream_t stream);
+// scratch bytes the prefill path can use for this shape (its live-tile map)
+size_t prefill_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q, int64_t max_seq,
+                               int64_t D);
 // the same kernel with 32-row wavefronts and Q^T in registers
 // (attn_prefill_dma_wide.hip): D = 512 with nw = 4, D = 256 with nw = 2 or 4
 hipError_t launch_attn_prefill_dma_qreg(const AttnParams& p, int nw, hipStream_t stream);

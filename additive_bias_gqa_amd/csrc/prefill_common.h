@@ -81,10 +81,13 @@ __device__ __forceinline__ float bias_f32<uint32_t>(uint32_t v) { return __uint_
 // (up to 4 distinct blocks; more makes every tile live). Skipping a dead tile
 // is exact: its keys contribute exactly zero. Returns the count; the tile
 // indices are in s_list[0 .. count).
+// map_row (bias variant): this workgroup's words of a live-tile map built by
+// tilemap_kernel for the same rows - copied instead of scanning the bias.
 template <int NT, bool kRules, typename BiasT>
 __device__ __forceinline__ int build_live_list(const AttnParams& p, int64_t b, int np, int s0, int s_end, int n_kt,
                                uint32_t* s_bits, uint16_t* s_list, int n_words, int32_t* s_ids,
-                               int* s_nids_p, int* s_nlive_p) {
+                               int* s_nids_p, int* s_nlive_p,
+                               const uint32_t* map_row = nullptr) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int T = p.T;
@@ -94,7 +97,9 @@ __device__ __forceinline__ int build_live_list(const AttnParams& p, int64_t b, i
   if (tid == 0) { s_nids = 0; s_nlive = 0; }
   if (tid < 4) s_ids[tid] = -1;  // never a block id: a racing reader cannot match it
   __syncthreads();
-  if constexpr (!kRules) {
+  if (!kRules && map_row) {
+    for (int i = tid; i < n_words; i += NT) s_bits[i] = map_row[i];
+  } else if constexpr (!kRules) {
     // NB 16-byte loads per thread in flight at once, unconditional (index
     // clamped to the last vector, the copies discarded), so the scan costs one
     // memory round trip per batch rather than one per load

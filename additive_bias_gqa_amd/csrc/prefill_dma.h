@@ -277,9 +277,11 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   // ---- 2. live tiles ---------------------------------------------------------
   // read from LDS, the count is the same in every lane: say so, so that the
   // loop below (and every LDS address derived from its counter) is scalar
+  const uint32_t* map_row =
+      (!kRules && p.tilemap) ? p.tilemap + ((size_t)(b * n_qt + qt)) * n_words : nullptr;
   const int n_live = __builtin_amdgcn_readfirstlane(
       build_live_list<NT, kRules, BiasT>(p, b, np, s0, s_end, n_kt, s_bits, s_list, n_words, s_ids,
-                                         &s_nids, &s_nlive));
+                                         &s_nids, &s_nlive, map_row));
   // nothing may be pending in registers once the pipeline starts: every wait
   // in the loop below is the explicit one
   wait_vmcnt<0>();
@@ -503,7 +505,16 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
 #define ABGQA_PD32 4
 #endif
       constexpr int PD = KSTEPS < ABGQA_PD32 ? KSTEPS : ABGQA_PD32;
-      f32x16 sacc = f32x16{};
+      // NCH independent accumulation chains (k-step i into chain i % NCH),
+      // summed at the end: an MFMA that accumulates onto the result of the one
+      // just issued waits for it to finish (half the matrix-core rate)
+#ifndef ABGQA_SCH32
+#define ABGQA_SCH32 2
+#endif
+      constexpr int NCH = KSTEPS < ABGQA_SCH32 ? KSTEPS : ABGQA_SCH32;
+      f32x16 schain[NCH];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) schain[c] = f32x16{};
       constexpr int NQR = kQLds ? 2 : 1;   // LDS reads per k-step
       bf16x8 ka[PD], qa[kQLds ? PD : 1];
 #pragma unroll
@@ -522,12 +533,15 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
           ka[i % PD] = lds_at<bf16x8>(k_base[(i + PD) % NKG], KO + SPAN * ((i + PD) / NKG));
           if constexpr (kQLds) qa[i % PD] = lds_at<bf16x8>(q_base[(i + PD) % NKG], SPAN * ((i + PD) / NKG));
         }
-        sacc = mfma32x32x16(a, qb, sacc);
+        schain[i % NCH] = mfma32x32x16(a, qb, schain[i % NCH]);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (i + PD < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, NQR, 0);
         constexpr int GS = KSTEPS / kFG;   // k-steps per fetch group
         if (kFG > 1 && i % GS == GS - 1 && i / GS + 1 < kFG) fetch_group(i / GS + 1, jn, stn);
       }
+      f32x16 sacc = schain[0];
+#pragma unroll
+      for (int c = 1; c < NCH; ++c) sacc += schain[c];
       // V^T fragments of the first PV MFMAs, read while the softmax runs.
       // MFMA u = 2*blk + step; lane 16*gq + 4*kq + jq reads
       // V[16*step + 8*half + 4*(gq/2) + kq][32*blk + 16*(gq%2) + 4*jq]
@@ -673,25 +687,28 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
         }
       }
       // S^T = K Q^T in two 16-key halves; lane l: query row l % 16, keys
-      // 16*kb + 4*(l/16) + e
-      f32x4 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        constexpr int PD = 8;   // K fragments read PD steps ahead of their MFMA
+      // 16*kb + 4*(l/16) + e. The halves' MFMAs alternate: an MFMA that
+      // accumulates onto the result of the one just issued waits for it to
+      // finish, which halves the matrix-core rate of a single chain.
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      {
+        constexpr int NS = 2 * KSTEPS;   // step n: k-step n / 2 of key half n % 2
+        constexpr int PD = 8;            // K fragments read PD steps ahead of their MFMA
+        auto kread = [&](int n) {
+          const int i = n >> 1;
+          return lds_at<bf16x8>(k_base[i % NKG], KO + SPAN * (i / NKG) + (n & 1) * 16 * D * 2);
+        };
         bf16x8 ka[PD];
 #pragma unroll
-        for (int i = 0; i < PD; ++i)
-          ka[i] = lds_at<bf16x8>(k_base[i % NKG], KO + SPAN * (i / NKG) + kb * 16 * D * 2);
+        for (int n = 0; n < PD; ++n) ka[n] = kread(n);
         __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
 #pragma unroll
-        for (int i = 0; i < KSTEPS; ++i) {
-          const bf16x8 a = ka[i % PD];
-          if (i + PD < KSTEPS)
-            ka[i % PD] = lds_at<bf16x8>(k_base[(i + PD) % NKG], KO + SPAN * ((i + PD) / NKG) + kb * 16 * D * 2);
-          sacc[kb] = mfma16x16x32(a, qf[i], sacc[kb]);
+        for (int n = 0; n < NS; ++n) {
+          const bf16x8 a = ka[n % PD];
+          if (n + PD < NS) ka[n % PD] = kread(n + PD);
+          sacc[n & 1] = mfma16x16x32(a, qf[n >> 1], sacc[n & 1]);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i + PD < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (n + PD < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       }
       // V^T fragments of the first PV MFMAs, read while the softmax runs;
@@ -832,6 +849,54 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
 
 namespace {
 
+// Live-tile map of the bias variant: bit kt % 32 of word (b, qt, kt / 32) is
+// set iff some row of query tile qt (MQ tokens from qt * MQ) allows some key
+// of key tile kt below nonpad (a bias entry other than -inf) - the set a
+// workgroup's own bias scan finds (build_live_list), computed once per batch
+// row instead of once per KV head, by a grid that keeps the memory busy.
+// One workgroup per (b, query tile, word = 32 key tiles = 1024 keys).
+template <typename BiasT>
+__global__ __launch_bounds__(256) void tilemap_kernel(const BiasT* __restrict__ bias,
+                                                      const int64_t* __restrict__ nonpad,
+                                                      uint32_t* __restrict__ map, int S_q, int T,
+                                                      int MQ, int n_qt, int n_words) {
+  __shared__ uint32_t s_word;
+  const int wid = blockIdx.x;
+  const int word = wid % n_words;
+  const int qt = (wid / n_words) % n_qt;
+  const int64_t b = wid / (n_words * n_qt);
+  const int np = (int)clamp_nonpad(nonpad[b], T);
+  const int s0 = qt * MQ, nrows = min(MQ, S_q - s0);
+  const int j_lo = word * 32 * kTileKeys, j_hi = min(j_lo + 32 * kTileKeys, np);
+  if (threadIdx.x == 0) s_word = 0u;
+  __syncthreads();
+  constexpr int EPV = 16 / (int)sizeof(BiasT);
+  constexpr int CPW = 32 * kTileKeys / EPV;   // 16-byte chunks of a row's 1024 keys
+  constexpr int RPP = 256 / CPW;              // rows per pass
+  const int c = threadIdx.x % CPW, rr = threadIdx.x / CPW;
+  const int j = j_lo + c * EPV;               // rows are multiples of 16 bytes
+  bool any = false;
+  if (j < j_hi && nrows > 0) {
+    const BiasT* col = bias + ((int64_t)b * S_q + s0) * T + j;
+    constexpr int U = 8;   // loads in flight per thread (rows past the tile repeat its last)
+    for (int r0 = rr; r0 < nrows; r0 += U * RPP) {
+      u32x4 raw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) raw[u] = ld_global<u32x4>(col + (int64_t)min(r0 + u * RPP, nrows - 1) * T);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        BiasT vals[EPV];
+        *reinterpret_cast<u32x4*>(vals) = raw[u];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) any |= (j + e < np) && live_bits<BiasT>(vals[e]);
+      }
+    }
+  }
+  if (any) atomicOr(&s_word, 1u << ((c * EPV) / kTileKeys));
+  __syncthreads();
+  if (threadIdx.x == 0) map[wid] = s_word;
+}
+
 template <int D, int RW, int NW, bool kRules, typename BiasT, bool kQReg>
 hipError_t launch_dma_inst(const AttnParams& p, hipStream_t stream) {
   using Geo = DmaGeom<D, RW, NW, kRules, BiasT, kQReg>;
@@ -854,8 +919,26 @@ hipError_t launch_dma_inst(const AttnParams& p, hipStream_t stream) {
     }
     lds_set = lds;
   }
+  AttnParams pp = p;
+  pp.tilemap = nullptr;
+  if constexpr (!kRules) {
+    // the live-tile map, when the caller's scratch holds it
+    const int n_words = (n_kt + 31) / 32;
+    const size_t need = (size_t)p.B * n_qt * n_words * sizeof(uint32_t);
+    if (p.ws != nullptr && p.ws_bytes >= need) {
+      hipLaunchKernelGGL(tilemap_kernel<BiasT>, dim3((unsigned)((int64_t)p.B * n_qt * n_words)), dim3(256),
+                         0, stream, (const BiasT*)p.bias, p.nonpad, (uint32_t*)p.ws, p.S_q, p.T, MQ, n_qt,
+                         n_words);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) {
+        set_launch_detail("live-tile map kernel launch");
+        return e;
+      }
+      pp.tilemap = (const uint32_t*)p.ws;
+    }
+  }
   const dim3 grid((unsigned)((int64_t)n_qt * p.B * p.Hkv));
-  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, stream, p, n_qt);
+  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, stream, pp, n_qt);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) set_launch_detail("direct-to-LDS prefill kernel launch");
   return e;

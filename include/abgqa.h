@@ -178,9 +178,15 @@ abgqa_status kv_scatter_and_bias(void *k_cache, void *v_cache, const void *k_upd
  *                    ABGQA_F32 (fp32 throughout)
  *   workspace        device scratch of at least attn_bias_gqa_workspace_bytes()
  *                    bytes for the same shape, 16-byte aligned, no initial
- *                    contents needed (the decode path keeps one partial
- *                    softmax result per split there). Calls that share a
- *                    workspace must not overlap in time.
+ *                    contents needed. Decode (S_q * Hq / Hkv <= 16) keeps one
+ *                    partial softmax result per split there and requires it.
+ *                    Prefill with a bias tensor keeps a live-tile map there
+ *                    (one bit per batch row, query tile and 32-key tile,
+ *                    built by a pass over the bias before the attention
+ *                    kernel); for prefill it is optional: with a smaller or
+ *                    NULL workspace every workgroup scans its bias rows
+ *                    itself (same result). Calls that share a workspace must
+ *                    not overlap in time.
  * Slots >= nonpad may hold any bits (NaN/Inf included); they never reach the
  * arithmetic. K/V at slots < nonpad are expected to be finite: a key masked by
  * the bias gets the exact weight 0, and 0 times a finite V is 0.

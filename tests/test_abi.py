@@ -87,7 +87,10 @@ def test_scatter_and_bias_validation(lib):
 
 def test_workspace_size(lib):
     assert lib.attn_bias_gqa_workspace_bytes(8, 16, 8, 1, 4096, 256) > 0
-    assert lib.attn_bias_gqa_workspace_bytes(2, 16, 8, 512, 4096, 256) == 0   # prefill
+    # prefill (D 256, G 2: 64-row workgroups of 32 tokens): one bit per batch
+    # row x 16 query tiles x 128 key tiles
+    assert lib.attn_bias_gqa_workspace_bytes(2, 16, 8, 512, 4096, 256) == 2 * 16 * 4 * 4
+    assert lib.attn_bias_gqa_workspace_bytes(2, 8, 8, 512, 4096, 256) == 0    # G = 1: no map
     assert lib.attn_bias_gqa_workspace_bytes(1, 6, 4, 1, 64, 64) == 0         # invalid heads
 
 

@@ -142,8 +142,12 @@ SMALL = {
     "decode_g3": lambda: wl.decode_full(B=2, Hq=6, Hkv=2, D=256, max_seq=200, nonpad_lo=1),
     "prefill_vision": lambda: wl.prefill_vision(B=2, Hq=4, Hkv=2, D=256, S_q=100, max_seq=512,
                                                 window=64, start_hi=300, block=40),
+    # max_seq 300: bf16 bias rows not 16-byte multiples (register-staged kernel
+    # for the bias, direct-to-LDS for the rules); 320: direct-to-LDS for both
     "prefill_long": lambda: wl.prefill_long(B=2, Hq=8, Hkv=2, D=512, S_q=200, max_seq=300,
                                             pad_hi=30, block=50),
+    "prefill_long_a": lambda: wl.prefill_long(B=2, Hq=8, Hkv=2, D=512, S_q=200, max_seq=320,
+                                              pad_hi=30, block=50),
     "prefill_d64_g8": lambda: wl.prefill_vision(B=1, Hq=8, Hkv=1, D=64, S_q=70, max_seq=200,
                                                 window=30, start_hi=100, block=20),
     "prefill_d128_g3": lambda: wl.prefill_long(B=2, Hq=6, Hkv=2, D=128, S_q=90, max_seq=130,
@@ -208,13 +212,45 @@ def test_softcap_fp32_and_masked_poison():
 
 
 def test_attention_rules_equal_bias_bitwise():
-    for name in ("decode_sliding", "decode_full", "prefill_vision", "prefill_long"):
+    # shapes where both variants take the same kernel (prefill_long at
+    # max_seq 300 does not: see SMALL)
+    for name in ("decode_sliding", "decode_full", "prefill_vision", "prefill_long_a"):
         w = SMALL[name]()
         step = w.steps[0]
         announce(f"rules == bias {name}")
         _, o_bias = gpu_step(w, step, dev(w.k_cache), dev(w.v_cache), rules=False)
         _, o_rules = gpu_step(w, step, dev(w.k_cache), dev(w.v_cache), rules=True)
         assert torch.equal(o_bias.view(torch.int16), o_rules.view(torch.int16)), name
+
+
+@pytest.mark.parametrize("D", [64, 256, 512])
+@pytest.mark.parametrize("bias_dtype", [torch.bfloat16, torch.float32])
+def test_prefill_live_tile_map(D, bias_dtype):
+    """The live-tile map built by a pass over the bias (used when the caller's
+    workspace holds it) and each workgroup's own bias scan (no workspace) give
+    bit-identical outputs, on a bias whose -inf blocks leave dead 32-key tiles
+    at arbitrary places; both match the oracle."""
+    rng = wl.rng_for(620 + D)
+    B, Hq, Hkv, S_q, T = 2, 8, 2, 100, 512
+    q = wl.normal(rng, (B, Hq, S_q, D), torch.bfloat16)
+    k = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    v = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    nonpad = torch.tensor([T, 300], dtype=torch.int64)
+    # -inf over random (8-row, 32-key) blocks, plus scattered single entries
+    dead_blk = torch.from_numpy(rng.random((B, (S_q + 7) // 8, T // 32)) < 0.45)
+    mask = dead_blk.repeat_interleave(8, dim=1)[:, :S_q].repeat_interleave(32, dim=2)
+    mask |= torch.from_numpy(rng.random((B, S_q, T)) < 0.05)
+    bias = torch.where(mask, float("-inf"), 0.25 * torch.from_numpy(rng.standard_normal((B, S_q, T))))
+    bias = bias.to(bias_dtype).reshape(B, 1, S_q, T)
+    announce(f"live-tile map D={D} bias={bias_dtype}")
+    ref = oracle.attention(q, k, v, bias, nonpad, 1.0 / math.sqrt(D))
+    args = (dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 1.0 / math.sqrt(D))
+    assert ab.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, T, D) > 0
+    o_map = ab.attn_bias_gqa_fwd(*args)
+    o_scan = ab.attn_bias_gqa_fwd(*args, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    assert torch.equal(o_map.view(torch.int16), o_scan.view(torch.int16))
+    check_parity(to_f64(o_map), ref, torch.bfloat16,
+                 dead_rows(bias.float().numpy(), nonpad, Hq), f"tilemap/D{D}")
 
 
 def test_attention_fp32_bias_dtype():
