@@ -97,12 +97,20 @@ __host__ __device__ constexpr int64_t part_floats(int64_t NR, int64_t D) {
   return (NR * D + 2 * NR + 3) & ~(int64_t)3;
 }
 
-// workspace: one partial record per (b, kv head, split)
+// Rows whose live ranges every split workgroup learns (several splits per row:
+// then B * Hkv < 256 with the default split count)
+constexpr int kMaxBalanceRows = 256;
+// keys between the samples that estimate a row's live length
+constexpr int kSampleStride = 256;
+
+// workspace: one partial record per (kv head, rank), rank < B * n_split, then
+// per (kv head, b) the first rank and the number of splits of that row
 size_t decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_q, int64_t G, int64_t D,
                               int64_t max_seq) {
   const int64_t NR = round_up_rows(S_q * G);
   const int64_t n_split = decode_num_splits(B, Hkv, max_seq);
-  return (size_t)B * Hkv * n_split * part_floats(NR, D) * sizeof(float);
+  return (size_t)B * Hkv * n_split * part_floats(NR, D) * sizeof(float) +
+         (size_t)B * Hkv * 2 * sizeof(int);
 }
 
 template <int D, int NR, int NW, bool kRules, typename BiasT>
@@ -129,53 +137,70 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   __shared__ __align__(16) __bf16 s_q[kQinLds ? NR * D : 8];  // Q rows (A operand)
   __shared__ int s_rlo[kDecWaves], s_rhi[kDecWaves];
   __shared__ int32_t s_kq[16];
+  // several splits per row: live samples of every batch row
+  __shared__ int s_cnt[kMaxBalanceRows];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
   const int T = p.T, G = p.G, R = p.S_q * p.G;
 
+  // ---- 0. which (kv head, batch row, split) ----------------------------------
+  // Workgroups are numbered (kv head, rank), rank < B * n_split. With one split
+  // per row the rank is the batch row. With several, rows of very different
+  // live length would leave the workgroups of short rows idle while those of
+  // the longest row run on, so every workgroup of a kv head first learns the
+  // live key count of every batch row from samples (the same data
+  // everywhere, hence the same answer) and the rows get splits in proportion
+  // to it (section 1b). Until then b is the equal-split guess, which starts the Q
+  // loads; a workgroup whose row changes loads Q again.
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int split = wg % p.n_split;
-  const int bh = wg / p.n_split;
-  const int hk = bh % p.Hkv;
-  const int64_t b = bh / p.Hkv;
-  const int np = (int)clamp_nonpad(p.nonpad[b], T);
+  const int S = p.B * p.n_split;   // workgroups per kv head
+  const int hk = wg / S;
+  const int rank = wg % S;
+  const bool multi = p.n_split > 1 && p.B <= kMaxBalanceRows;
+  const int64_t b_guess = rank / p.n_split;
+  int64_t b = b_guess;
 
-  // ---- 0. Q rows (row r = s * G + g) into registers, to be parked in LDS ----
+  // ---- 0b. Q rows (row r = s * G + g) into registers, to be parked in LDS ----
   // Issued before the range scan so that both memory round trips overlap; the
   // index is clamped (loads stay unconditional), the store is guarded.
   constexpr int QCH = kQinLds ? (NR * (D / 8) + kDecThreads - 1) / kDecThreads : 1;
   bf16x8 qtmp[QCH];
-  if constexpr (kQinLds) {
-    const int nq = R * (D / 8);
+  auto load_q = [&](int64_t bq) {
+    if constexpr (kQinLds) {
+      const int nq = R * (D / 8);
 #pragma unroll
-    for (int i = 0; i < QCH; ++i) {
-      const int c = min(tid + i * kDecThreads, nq - 1);
-      const int r = c / (D / 8), dc = c % (D / 8);
-      qtmp[i] = ld_global<bf16x8>((const __bf16*)p.q +
-          (((b * p.Hq + hk * G + r % G) * p.S_q + r / G) * (int64_t)D) + 8 * dc);
+      for (int i = 0; i < QCH; ++i) {
+        const int c = min(tid + i * kDecThreads, nq - 1);
+        const int r = c / (D / 8), dc = c % (D / 8);
+        qtmp[i] = ld_global<bf16x8>((const __bf16*)p.q +
+            (((bq * p.Hq + hk * G + r % G) * p.S_q + r / G) * (int64_t)D) + 8 * dc);
+      }
     }
-  }
+  };
+  load_q(b);
 
-  // ---- 1. live range [lo, hi) of keys, over all S_q rows -------------------
-  // (no barrier before the scan: a workgroup barrier here would first wait for
-  // the Q loads above, putting two memory round trips ahead of the K/V loads)
+  // ---- 1. live key ranges ----------------------------------------------------
+  // (no memory fence before the scan: waiting here for the Q loads above would
+  // put two memory round trips ahead of the K/V loads)
   if constexpr (!kParMerge)
     for (int i = tid; i < NR * D; i += kDecThreads) s_o[i] = 0.f;
-  {
+  // this row's exact range (bias variant): every key below nonpad whose bias
+  // is not -inf, over the S_q rows, reduced into s_rlo / s_rhi per wavefront.
+  // NB loads per thread in flight at once, unconditional (index clamped to the
+  // last vector; the extra copies are discarded), so the scan costs one memory
+  // round trip; the vector path reads whole rows (max_seq keys) and applies
+  // j < nonpad afterwards, so its loads do not wait for nonpad first.
+  auto scan_own = [&](int64_t bq) {
     int lo = INT32_MAX, hi = -1;
     if constexpr (!kRules) {
-      // NB 16-byte loads per thread in flight at once, unconditional (index
-      // clamped to the last vector; the extra copies are discarded below), so
-      // the scan costs one memory round trip per batch, not one per load. The
-      // vector path reads whole rows (max_seq keys) and applies j < nonpad
-      // afterwards, so its loads do not wait for nonpad to arrive first.
-      const BiasT* bb = (const BiasT*)p.bias + b * p.S_q * (int64_t)T;
+      const int npq = (int)clamp_nonpad(p.nonpad[bq], T);
       constexpr int EPV = 16 / sizeof(BiasT);  // elements per 16-byte load
       constexpr int NB = 4;
+      const BiasT* bb = (const BiasT*)p.bias + bq * p.S_q * (int64_t)T;
       const bool vec_rows = (T % EPV) == 0;
-      const int nvec = vec_rows ? T / EPV : (np + EPV - 1) / EPV;
+      const int nvec = vec_rows ? T / EPV : (npq + EPV - 1) / EPV;
       const int total = p.S_q * nvec;
       if (vec_rows) {
         for (int base = tid; base < total; base += NB * kDecThreads) {
@@ -195,7 +220,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
 #pragma unroll
             for (int e = 0; e < EPV; ++e) {
               const int j = j0 + e;
-              if (idx < total && j < np && bias_live_bits<BiasT>(vals[e])) {
+              if (idx < total && j < npq && bias_live_bits<BiasT>(vals[e])) {
                 lo = min(lo, j);
                 hi = max(hi, j);
               }
@@ -209,42 +234,155 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
           const BiasT* row = bb + (int64_t)s * T;
           for (int e = 0; e < EPV; ++e) {
             const int j = j0 + e;
-            if (j < np && bias_live_bits<BiasT>(row[j])) {
+            if (j < npq && bias_live_bits<BiasT>(row[j])) {
               lo = min(lo, j);
               hi = max(hi, j);
             }
           }
         }
       }
-    } else {
-      // causal / window keys of every row, then the image block of any row
-      if (tid < p.S_q) {
-        const RowRule rr = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, tid, p.S_q, T, p.window);
-        s_kq[tid] = rr.kind_q;
-        int64_t a = (rr.window > 0) ? rr.q - rr.window + 1 : 0;
-        if (a < 0) a = 0;
-        const int64_t z = rr.q < (int64_t)np - 1 ? rr.q : (int64_t)np - 1;
-        if (a <= z) { lo = (int)a; hi = (int)z; }
-      }
-      __syncthreads();
-      bool any_block = false;
-      for (int s = 0; s < p.S_q; ++s) any_block |= s_kq[s] > 0;
-      if (any_block) {
-        const int32_t* kr = p.slot_kind + b * T;
-        for (int j = tid; j < np; j += kDecThreads) {
-          const int32_t kj = kr[j];
-          if (kj <= 0) continue;
+      lo = wave_min_i32(lo);
+      hi = wave_max_i32(hi);
+      if (lane == 0) { s_rlo[w] = lo; s_rhi[w] = hi; }
+    }
+  };
+  // Live estimate of every batch row (several splits per row): the number of
+  // sampled keys j = 256 i + 128 below nonpad that some query row of the batch
+  // row allows - the bias entry not -inf, or the in-kernel rule, which gives
+  // the same mask, so both variants balance alike. One load (or rule) per
+  // sample: 32 per row of 8192 keys.
+  if (multi) {
+    for (int i = tid; i < p.B; i += kDecThreads) s_cnt[i] = 0;
+    lds_barrier();
+  }
+  scan_own(b);
+  if (multi) {
+    const int ns = (T + kSampleStride - 1) / kSampleStride;
+    for (int i = tid; i < p.B * ns; i += kDecThreads) {
+      const int bb = i / ns;
+      const int j = (i - bb * ns) * kSampleStride + kSampleStride / 2;
+      const int npb = (int)clamp_nonpad(p.nonpad[bb], T);
+      bool live = false;
+      if (j < npb) {
+        if constexpr (kRules) {
+          const int32_t kj = p.slot_kind ? p.slot_kind[bb * (int64_t)T + j] : 0;
           for (int s = 0; s < p.S_q; ++s) {
-            if (s_kq[s] == kj) { lo = min(lo, j); hi = max(hi, j); break; }
+            const RowRule rr = make_row_rule(p.nonpad, p.q_start, p.slot_kind, bb, s, p.S_q, T, p.window);
+            live |= rr.allowed(j, kj);
           }
+        } else {
+          const BiasT* col = (const BiasT*)p.bias + (int64_t)bb * p.S_q * T + j;
+          for (int s = 0; s < p.S_q; ++s) live |= bias_live_bits<BiasT>(col[(int64_t)s * T]);
+        }
+      }
+      if (live) atomicAdd(&s_cnt[bb], 1);
+    }
+  }
+  __syncthreads();
+
+  // ---- 1b. splits per batch row ----------------------------------------------
+  // Each wavefront computes the same assignment from the same LDS data. Rows
+  // get nsp_b = max(1, ceil(c_b / X)) splits, c_b the live samples of row b,
+  // X the smallest cap for which sum_b nsp_b <= B * n_split (a binary search),
+  // when the busiest row has more than 1.25 times the mean; otherwise n_split
+  // splits each. Ranks past sum_b nsp_b have no work.
+  int split = rank % p.n_split, nsp = p.n_split, first = (int)b * p.n_split;
+  if (multi) {
+    int cnt4[4];
+    int tot = 0, mx = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bb = lane + 64 * i;
+      cnt4[i] = bb < p.B ? s_cnt[bb] : 0;
+      tot += cnt4[i];
+      mx = max(mx, cnt4[i]);
+    }
+    tot = wave_sum_i32(tot);
+    mx = wave_max_i32(mx);
+    if ((int64_t)mx * p.B * 4 > (int64_t)tot * 5) {
+      int xl = 1, xh = mx;
+      while (xl < xh) {
+        const int xm = (xl + xh) >> 1;
+        int need = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (lane + 64 * i < p.B) need += max(1, (cnt4[i] + xm - 1) / xm);
+        need = wave_sum_i32(need);
+        if (need <= S) xh = xm;
+        else xl = xm + 1;
+      }
+      // batch row bb = lane + 64 i: prefix sums in row order, find this rank
+      int carry = 0;
+      int found = -1, f_first = 0, f_n = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int bb = lane + 64 * i;
+        const int n = bb < p.B ? max(1, (cnt4[i] + xl - 1) / xl) : 0;
+        const int incl = wave_incl_sum_i32(n) + carry;
+        const int fst = incl - n;
+        if (n > 0 && rank >= fst && rank < fst + n) { found = bb; f_first = fst; f_n = n; }
+        carry = __shfl(incl, 63);
+      }
+      const uint64_t hit = __ballot(found >= 0);
+      if (hit == 0) return;   // a rank past every row's splits: no work
+      const int src = __builtin_ctzll(hit);
+      b = __shfl(found, src);
+      first = __shfl(f_first, src);
+      nsp = __shfl(f_n, src);
+      split = rank - first;
+    }
+  }
+  const int np = (int)clamp_nonpad(p.nonpad[b], T);
+  // where the combine finds this row's partial records
+  if (split == 0 && tid == 0) {
+    int* tab = reinterpret_cast<int*>(p.ws_part + (int64_t)p.Hkv * S * PART);
+    tab[2 * (hk * p.B + b)] = first;
+    tab[2 * (hk * p.B + b) + 1] = nsp;
+  }
+
+  // ---- 1c. this row's live range [live_lo, live_hi) ---------------------------
+  if constexpr (kRules) {
+    // causal / window keys of every query row, then the image block of any row
+    int lo = INT32_MAX, hi = -1;
+    if (tid < p.S_q) {
+      const RowRule rr = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, tid, p.S_q, T, p.window);
+      s_kq[tid] = rr.kind_q;
+      int64_t a = (rr.window > 0) ? rr.q - rr.window + 1 : 0;
+      if (a < 0) a = 0;
+      const int64_t z = rr.q < (int64_t)np - 1 ? rr.q : (int64_t)np - 1;
+      if (a <= z) { lo = (int)a; hi = (int)z; }
+    }
+    __syncthreads();
+    bool any_block = false;
+    for (int s = 0; s < p.S_q; ++s) any_block |= s_kq[s] > 0;
+    if (any_block) {
+      const int32_t* kr = p.slot_kind + b * T;
+      for (int j = tid; j < np; j += kDecThreads) {
+        const int32_t kj = kr[j];
+        if (kj <= 0) continue;
+        for (int s = 0; s < p.S_q; ++s) {
+          if (s_kq[s] == kj) { lo = min(lo, j); hi = max(hi, j); break; }
         }
       }
     }
     lo = wave_min_i32(lo);
     hi = wave_max_i32(hi);
     if (lane == 0) { s_rlo[w] = lo; s_rhi[w] = hi; }
+    __syncthreads();
+  } else if (b != b_guess) {
+    // the row changed with the assignment: scan the new one
+    scan_own(b);
+    __syncthreads();
   }
+  int live_lo = INT32_MAX, live_hi = 0;
+#pragma unroll
+  for (int ww = 0; ww < kDecWaves; ++ww) {
+    live_lo = min(live_lo, s_rlo[ww]);
+    live_hi = max(live_hi, s_rhi[ww] + 1);
+  }
+  if (live_hi <= live_lo) { live_lo = 0; live_hi = 0; }
   if constexpr (kQinLds) {
+    if (b != b_guess) load_q(b);
 #pragma unroll
     for (int i = 0; i < QCH; ++i) {
       const int c = tid + i * kDecThreads;
@@ -253,15 +391,8 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
     }
   }
   __syncthreads();
-  int live_lo = INT32_MAX, live_hi = 0;
-#pragma unroll
-  for (int ww = 0; ww < kDecWaves; ++ww) {
-    live_lo = min(live_lo, s_rlo[ww]);
-    live_hi = max(live_hi, s_rhi[ww] + 1);
-  }
-  if (live_hi <= 0) { live_lo = 0; live_hi = 0; }
   const int live = live_hi - live_lo;
-  const int per = ((live + p.n_split - 1) / p.n_split + 15) & ~15;
+  const int per = ((live + nsp - 1) / nsp + 15) & ~15;
   const int my_lo = live_lo + split * per;
   const int my_hi = min(live_hi, my_lo + per);
 
@@ -513,7 +644,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
     m_wg[r] = mm;
   }
   // ---- 5. sum the waves in a fixed order (bit-reproducible), write the partial
-  float* part = p.ws_part + ((int64_t)bh * p.n_split + split) * PART;
+  float* part = p.ws_part + ((int64_t)hk * S + rank) * PART;
   if constexpr (kParMerge) {
     if (lane < LPR) {
 #pragma unroll
@@ -562,7 +693,8 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   }
 }
 
-// Merge the n_split partials of one (b, kv head, row):
+// Merge the partials of one (b, kv head, row) - the row's splits, found
+// through the table the split kernel writes:
 //   m = max m_i,  y = sum 2^(m_i - m) O_i / sum 2^(m_i - m) l_i
 // (a split that saw no live key has m_i = -inf and drops out; no live key at
 // all gives y = 0). One workgroup of 64 threads per (b, kv head, row), each
@@ -577,20 +709,14 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(AttnParams p) {
   const int64_t b = bh / p.Hkv;
   const int d0 = threadIdx.x * 8;
   if (d0 >= D) return;
-  const float* parts = p.ws_part + (int64_t)bh * p.n_split * PART;
-  // one pass, rescaled on the fly (running max), so every split's m, l and O
-  // loads are independent of each other and can all be in flight at once
+  const int S = p.B * p.n_split;
+  const int* tab = reinterpret_cast<const int*>(p.ws_part + (int64_t)p.Hkv * S * PART);
+  // one pass, rescaled on the fly (running max): a split that saw no live key
+  // (m = -inf, l = 0, O = 0) gets weight 0, and nothing done so far is
+  // rescaled by its -inf
   float mm = -INFINITY, den = 0.f;
   float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int sp = 0; sp < p.n_split; ++sp) {
-    const float* ps = parts + sp * PART;
-    const float ms = ps[NR * D + r];
-    const float ls = ps[NR * D + NR + r];
-    const f32x4 a0 = *reinterpret_cast<const f32x4*>(ps + r * D + d0);
-    const f32x4 a1 = *reinterpret_cast<const f32x4*>(ps + r * D + d0 + 4);
-    // branch-free: a split that saw no live key (m = -inf, l = 0, O = 0) gets
-    // weight 0, and nothing done so far is rescaled by its -inf
+  auto merge = [&](float ms, float ls, const f32x4& a0, const f32x4& a1) {
     const float mn = fmaxf(mm, ms);
     const float fo = (mm == -INFINITY) ? 0.f : fast_exp2(mm - mn);
     const float fs = (ms == -INFINITY) ? 0.f : fast_exp2(ms - mn);
@@ -601,6 +727,35 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(AttnParams p) {
       num[4 + c] = num[4 + c] * fo + a1[c] * fs;
     }
     mm = mn;
+  };
+  // The records of the equal split (rank b * n_split + i) are loaded together
+  // with the row's table entry, so the common case costs one memory round
+  // trip; rows the split kernel balanced otherwise load theirs afterwards.
+  constexpr int PRE = 4;
+  const int first_eq = (int)b * p.n_split;
+  float pm[PRE], pl[PRE];
+  f32x4 pa0[PRE], pa1[PRE];
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) {
+    const float* ps = p.ws_part + ((int64_t)hk * S + first_eq + min(i, p.n_split - 1)) * PART;
+    pm[i] = ps[NR * D + r];
+    pl[i] = ps[NR * D + NR + r];
+    pa0[i] = *reinterpret_cast<const f32x4*>(ps + r * D + d0);
+    pa1[i] = *reinterpret_cast<const f32x4*>(ps + r * D + d0 + 4);
+  }
+  const int first = tab[2 * (hk * p.B + b)], n_parts = tab[2 * (hk * p.B + b) + 1];
+  if (first == first_eq && n_parts == p.n_split && n_parts <= PRE) {
+#pragma unroll
+    for (int i = 0; i < PRE; ++i)
+      if (i < n_parts) merge(pm[i], pl[i], pa0[i], pa1[i]);
+  } else {
+    const float* parts = p.ws_part + ((int64_t)hk * S + first) * PART;
+#pragma unroll 4
+    for (int sp = 0; sp < n_parts; ++sp) {
+      const float* ps = parts + sp * PART;
+      merge(ps[NR * D + r], ps[NR * D + NR + r], *reinterpret_cast<const f32x4*>(ps + r * D + d0),
+            *reinterpret_cast<const f32x4*>(ps + r * D + d0 + 4));
+    }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const int s = r / p.G, g = r % p.G;

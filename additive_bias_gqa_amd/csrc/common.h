@@ -103,6 +103,26 @@ __device__ __forceinline__ int wave_max_i32(int v) {
   for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m));
   return v;
 }
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+// inclusive prefix sum over the lanes of a wavefront (lane order)
+__device__ __forceinline__ int wave_incl_sum_i32(int v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+// workgroup barrier for LDS data only: waits for this wavefront's LDS
+// accesses, not for its outstanding global loads (__syncthreads waits for both)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

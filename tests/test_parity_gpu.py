@@ -253,6 +253,31 @@ def test_prefill_live_tile_map(D, bias_dtype):
                  dead_rows(bias.float().numpy(), nonpad, Hq), f"tilemap/D{D}")
 
 
+@pytest.mark.parametrize("variant", ["bias", "rules"])
+@pytest.mark.parametrize("D,Hq,Hkv", [(512, 4, 1), (256, 8, 2)])
+def test_decode_uneven_rows(D, Hq, Hkv, variant):
+    """Decode with batch rows of very different live length (an empty row, a
+    one-key row, full rows): the split workgroups share the rows' work in
+    proportion to their live keys, and ranks past the last split do nothing."""
+    rng = wl.rng_for(640 + D)
+    B, T = 6, 1024
+    q = wl.normal(rng, (B, Hq, 1, D), torch.bfloat16)
+    k = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    v = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    nonpad = torch.tensor([0, 1, T, 37, T - 5, 300], dtype=torch.int64)
+    q_start = (nonpad - 1).clamp(min=0)
+    bias = torch.from_numpy(oracle.bias(nonpad, q_start, None, 1, T, 0)).to(torch.bfloat16)
+    announce(f"decode uneven rows D={D} Hq={Hq} Hkv={Hkv} {variant}")
+    ref = oracle.attention(q, k, v, bias, nonpad, 1.0 / math.sqrt(D))
+    if variant == "bias":
+        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 1.0 / math.sqrt(D))
+    else:
+        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), None, dev(nonpad), 1.0 / math.sqrt(D),
+                                   q_start=dev(q_start), window=0)
+    check_parity(to_f64(got), ref, torch.bfloat16,
+                 dead_rows(bias.float().numpy(), nonpad, Hq), f"uneven/{variant}")
+
+
 def test_attention_fp32_bias_dtype():
     w = SMALL["prefill_vision"]()
     step = w.steps[0]
