@@ -179,7 +179,9 @@ abgqa_status kv_scatter_and_bias(void *k_cache, void *v_cache, const void *k_upd
  *   workspace        device scratch of at least attn_bias_gqa_workspace_bytes()
  *                    bytes for the same shape, 16-byte aligned, no initial
  *                    contents needed. Decode (S_q * Hq / Hkv <= 16) keeps one
- *                    partial softmax result per split there and requires it.
+ *                    partial softmax result per split workgroup there, and
+ *                    per (batch row, kv head) where its splits' results are,
+ *                    and requires it.
  *                    Prefill with a bias tensor keeps a live-tile map there
  *                    (one bit per batch row, query tile and 32-key tile,
  *                    built by a pass over the bias before the attention
