@@ -10,7 +10,8 @@ namespace abgqa {
 namespace {
 
 // ABGQA_PREFILL_CFG (tuning): "32x2", "32x4", "16x4", "16x8" picks rows per
-// wavefront x wavefronts per workgroup ("32x2r", "32x4r": Q^T in registers);
+// wavefront x wavefronts per workgroup ("32x2r", "32x4r": Q^T in registers;
+// "16x8k": 8 wavefronts of 16 rows as 4 row groups x 2 key halves);
 // otherwise the default below.
 static int prefill_cfg() {
   static const int v = [] {
@@ -22,6 +23,7 @@ static int prefill_cfg() {
     if (!strcmp(e, "16x8")) return 4;
     if (!strcmp(e, "32x2r")) return 5;
     if (!strcmp(e, "32x4r")) return 6;
+    if (!strcmp(e, "16x8k")) return 7;
     return 0;
   }();
   return v;
@@ -30,11 +32,15 @@ static int prefill_cfg() {
 // Rows per wavefront x wavefronts per workgroup for a shape. D = 512: 4
 // wavefronts of 32 rows (Q^T in registers, O^T in the accumulation registers):
 // each K/V tile fetched once for 128 rows, each LDS read feeding a 32-row MFMA.
-// D = 128, 256: 4 wavefronts of 16 rows keep all four SIMDs of a CU busy with
-// one workgroup per CU (64 rows; the LDS holds one workgroup's stages). D = 64
+// D = 256: 8 wavefronts of 16 rows, as 4 row groups x 2 key halves that take
+// alternate tiles and merge at the end: 64 rows per workgroup like 4
+// wavefronts, but two wavefronts per SIMD, each hiding the other's LDS and
+// softmax latency (a prefill chunk rarely has the rows for two 16-row
+// wavefronts per SIMD otherwise). D = 128: 4 wavefronts of 16 rows keep all
+// four SIMDs of a CU busy with one workgroup per CU. D = 64
 // (a tile too small to split four ways): 32-row wavefronts, 4 of them when
 // that still gives a workgroup per CU.
-enum class DmaCfg { k16x4, k16x8, k32x2, k32x4, k32x2r, k32x4r };
+enum class DmaCfg { k16x4, k16x8, k32x2, k32x4, k32x2r, k32x4r, k16x8k };
 
 DmaCfg dma_cfg(int D, int64_t B, int64_t Hkv, int64_t S_q, int64_t G) {
   const int cfg = prefill_cfg();
@@ -47,13 +53,18 @@ DmaCfg dma_cfg(int D, int64_t B, int64_t Hkv, int64_t S_q, int64_t G) {
   if (D == 256 && cfg == 6) return DmaCfg::k32x4r;
   if (cfg == 1) return DmaCfg::k32x2;
   if (cfg == 2) return DmaCfg::k32x4;
-  if (D >= 128) return cfg == 4 ? DmaCfg::k16x8 : DmaCfg::k16x4;
+  if (D >= 128 && cfg == 7) return DmaCfg::k16x8k;
+  if (D >= 128 && cfg == 4) return DmaCfg::k16x8;
+  if (D >= 128 && cfg == 3) return DmaCfg::k16x4;
+  if (D == 256) return DmaCfg::k16x8k;
+  if (D >= 128) return DmaCfg::k16x4;
   const int64_t wg4 = B * Hkv * ((S_q * G + 127) / 128);
   return wg4 >= 256 ? DmaCfg::k32x4 : DmaCfg::k32x2;
 }
 
 int dma_rows(DmaCfg c) {
-  return (c == DmaCfg::k16x4 || c == DmaCfg::k32x2 || c == DmaCfg::k32x2r) ? 64 : 128;
+  return (c == DmaCfg::k16x4 || c == DmaCfg::k32x2 || c == DmaCfg::k32x2r || c == DmaCfg::k16x8k) ? 64
+                                                                                                 : 128;
 }
 
 template <int D>
@@ -72,6 +83,7 @@ hipError_t launch_dma_d(const AttnParams& p, hipStream_t stream) {
     if (c == DmaCfg::k32x4) return launch_dma_v<D, 32, 4>(p, stream);
     if constexpr (D >= 128) {   // a tile must split evenly over the wavefronts
       if (c == DmaCfg::k16x8) return launch_dma_v<D, 16, 8>(p, stream);
+      if (c == DmaCfg::k16x8k) return launch_dma_v<D, 16, 8, true, 2>(p, stream);
       return launch_dma_v<D, 16, 4>(p, stream);
     }
     return launch_dma_v<D, 32, 2>(p, stream);

@@ -170,12 +170,13 @@ __device__ __forceinline__ void acc_settle(f32x16 (&o)[16]) {
                  "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15]));
 }
 
-template <int D, int RW, int NW, bool kRules, typename BiasT, bool kQReg>
+template <int D, int RW, int NW, bool kRules, typename BiasT, bool kQReg, int KS>
 struct DmaGeom {
   static_assert(kQReg || RW == 32, "an LDS Q tile needs 32-row wavefronts");
+  static_assert(KS == 1 || (KS == 2 && kQReg && NW % 2 == 0), "key halves: Q^T in registers");
   static constexpr int TILE_BYTES = kTileKeys * D * 2;         // one K (or V) tile
   static constexpr int NKI = TILE_BYTES / 1024;                // fetches per K (or V) tile
-  static constexpr int MQ_MAX = RW * NW / 2;                   // query tokens, G >= 2
+  static constexpr int MQ_MAX = RW * NW / KS / 2;              // query tokens, G >= 2
   static constexpr int BROW = kTileKeys * (int)sizeof(BiasT);  // bias bytes per row per tile
   static constexpr int MASK_BYTES = kRules ? 1024 : ((MQ_MAX * BROW + 1023) / 1024) * 1024;
   static constexpr int NMI = MASK_BYTES / 1024;                // fetches for bias / kinds
@@ -186,16 +187,17 @@ struct DmaGeom {
   static constexpr bool kQLds = !kQReg;
   static constexpr int Q_BYTES = kQLds ? RW * NW * D * 2 : 0;
   static constexpr int NSTAGE0 = (kLdsBudget - Q_BYTES) / STAGE_BYTES;
-  static constexpr int NSTAGE = NSTAGE0 > 4 ? 4 : NSTAGE0;
-  static_assert(NSTAGE >= 2, "two stages must fit");
-  static_assert(PW * (NSTAGE - 2) <= 63, "wait count");
+  static constexpr int NSTAGE1 = NSTAGE0 > 4 ? 4 : NSTAGE0;
+  static constexpr int NSTAGE = NSTAGE1 - NSTAGE1 % KS;   // whole super-stages of KS tiles
+  static_assert(NSTAGE / KS >= 2, "two super-stages must fit");
+  static_assert(KS * PW * (NSTAGE / KS - 2) <= 63, "wait count");
 };
 
 }  // namespace
 
-template <int D, int RW, int NW, bool kRules, typename BiasT, bool kQReg>
+template <int D, int RW, int NW, bool kRules, typename BiasT, bool kQReg, int KS>
 __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p, int n_qt) {
-  using Geo = DmaGeom<D, RW, NW, kRules, BiasT, kQReg>;
+  using Geo = DmaGeom<D, RW, NW, kRules, BiasT, kQReg, KS>;
   constexpr int NT = NW * 64;
   constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
   constexpr int NSTAGE = Geo::NSTAGE;
@@ -209,14 +211,16 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   constexpr bool kQLds = Geo::kQLds;
   constexpr int Q_BYTES = Geo::Q_BYTES;
   constexpr bool kAsmAcc = kQReg && RW == 32 && D >= 512;   // O^T via mfma32x32x16_acc
-  // 32-row wavefronts issue the next stage's fetches in kFG groups spread over
-  // the S^T MFMAs of the tile instead of all at its start: a wavefront that
-  // issues a whole stage at once stalls until the memory pipeline has taken
-  // most of it, with the matrix cores idle.
+  static_assert(!(kAsmAcc && KS > 1), "key halves with accumulation-register O^T");
+  constexpr int NSUP = NSTAGE / KS;   // super-stages: KS tiles each
+  // The next stage's fetches go out in kFG groups spread over the S^T MFMAs of
+  // the tile instead of all at its start: a wavefront that issues a whole
+  // stage at once stalls until the memory pipeline has taken most of it, with
+  // the matrix cores idle.
 #ifndef ABGQA_FETCH_GROUPS
 #define ABGQA_FETCH_GROUPS 4
 #endif
-  constexpr int kFG = RW != 32 ? 1 : (ABGQA_FETCH_GROUPS < KSTEPS ? ABGQA_FETCH_GROUPS : KSTEPS);
+  constexpr int kFG = ABGQA_FETCH_GROUPS < KSTEPS ? ABGQA_FETCH_GROUPS : KSTEPS;
 
   extern __shared__ __align__(16) unsigned char smem[];
   if constexpr (kQReg && RW == 32) {
@@ -233,12 +237,17 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   const int n_words = (n_kt_max + 31) / 32;
   uint16_t* s_list = reinterpret_cast<uint16_t*>(s_bits + n_words);
   __shared__ int s_nlive;
+  __shared__ int s_nhalf[2];
   __shared__ int32_t s_ids[4];
   __shared__ int s_nids;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
+  // KS = 2: wavefronts w and w + NW/2 hold the same rows (row group w % (NW/2))
+  // and take alternate live tiles (key half kh), merged at the end
+  constexpr int NWR = NW / KS;   // row groups
+  const int rg = w % NWR, kh = w / NWR;
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = n_qt - 1 - (wg % n_qt);   // later (heavier) query tiles first
@@ -246,7 +255,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   const int hk = bh % p.Hkv;
   const int64_t b = bh / p.Hkv;
   const int np = (int)clamp_nonpad(p.nonpad[b], T);
-  const int MQ = (RW * NW) / G;
+  const int MQ = (RW * NWR) / G;
   const int s0 = qt * MQ;
   const int s_end = min(s0 + MQ, p.S_q);
   const int n_kt = num_tiles(np);
@@ -257,7 +266,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   // cover them. ----
   const int col = lane & (RW - 1);
   const int grp = lane / RW;
-  const int r = RW * w + col;
+  const int r = RW * rg + col;
   const int sl = r / G, g = r % G;
   const int s = s0 + sl;
   const bool row_ok = (r < MQ * G) && (s < p.S_q);
@@ -282,6 +291,33 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   const int n_live = __builtin_amdgcn_readfirstlane(
       build_live_list<NT, kRules, BiasT>(p, b, np, s0, s_end, n_kt, s_bits, s_list, n_words, s_ids,
                                          &s_nids, &s_nlive, map_row));
+  // KS = 2: the live tiles split by parity of their key tile, even tiles for
+  // key half 0 (s_list[0, ...)), odd ones for half 1 (s_list[khalf, ...)), so
+  // a fully masked tile that one variant lists and another skips changes no
+  // other tile's half (it only adds exact zeros to its own)
+  const int khalf = (n_kt_max + 1) / 2;
+  int n_h0 = n_live, n_h1 = 0;
+  if constexpr (KS == 2) {
+    if (w == 0) {
+      int be = 0, bo = 0;
+      for (int t0 = 0; t0 < n_kt; t0 += 64) {
+        const int t = t0 + lane;
+        const bool live = (t < n_kt) && ((s_bits[t >> 5] >> (t & 31)) & 1u);
+        const uint64_t me = __ballot(live && !(t & 1)), mo = __ballot(live && (t & 1));
+        const uint64_t below = (1ull << lane) - 1ull;
+        if (live) {
+          if (t & 1) s_list[khalf + bo + __popcll(mo & below)] = (uint16_t)t;
+          else s_list[be + __popcll(me & below)] = (uint16_t)t;
+        }
+        be += __popcll(me);
+        bo += __popcll(mo);
+      }
+      if (lane == 0) { s_nhalf[0] = be; s_nhalf[1] = bo; }
+    }
+    __syncthreads();
+    n_h0 = __builtin_amdgcn_readfirstlane(s_nhalf[0]);
+    n_h1 = __builtin_amdgcn_readfirstlane(s_nhalf[1]);
+  }
   // nothing may be pending in registers once the pipeline starts: every wait
   // in the loop below is the explicit one
   wait_vmcnt<0>();
@@ -363,18 +399,29 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
       }
     }
   };
-  auto tile_key0 = [&](int t_idx) {
-    return __builtin_amdgcn_readfirstlane((int)s_list[min(t_idx, n_live - 1)] * kTileKeys);
+  // first key of tile u of key half k (KS = 1: of the live list). Past the end
+  // of a list: its last tile again; an empty half takes the other half's
+  // tiles (fetched, never computed).
+  auto key_of = [&](int k, int u) {
+    int idx;
+    if constexpr (KS == 1) {
+      idx = min(u, n_live - 1);
+    } else {
+      const int kk = (k == 0 ? n_h0 : n_h1) > 0 ? k : 1 - k;
+      idx = kk * khalf + min(u, (kk == 0 ? n_h0 : n_h1) - 1);
+    }
+    return __builtin_amdgcn_readfirstlane((int)s_list[idx] * kTileKeys);
   };
-  auto fetch_stage = [&](int t_idx, int st) {
-    const int j0 = tile_key0(t_idx);
+  auto fetch_stage = [&](int j0, int st) {
 #pragma unroll
     for (int f = 0; f < PW; ++f) fetch_one(f, j0, st);
   };
-  // the fetches of one stage in kFG groups: group g is [PW*g/kFG, PW*(g+1)/kFG)
-  auto fetch_group = [&](const int g, const int j0, const int st) {
+  // the fetches of one super-stage (KS tiles: tile k from key jn[k] into stage
+  // KS*ssn + k) in kFG groups: group g is [KS*PW*g/kFG, KS*PW*(g+1)/kFG)
+  auto fetch_group = [&](const int g, const int* jn, const int ssn) {
 #pragma unroll
-    for (int f = PW * g / kFG; f < PW * (g + 1) / kFG; ++f) fetch_one(f, j0, st);
+    for (int f = KS * PW * g / kFG; f < KS * PW * (g + 1) / kFG; ++f)
+      fetch_one(f % PW, jn[f / PW], KS * ssn + f / PW);
   };
 
   // ---- 4. main loop ---------------------------------------------------------
@@ -405,7 +452,9 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
       }
     }
 #pragma unroll
-    for (int st = 0; st < NSTAGE - 1; ++st) fetch_stage(st, st);
+    for (int u = 0; u < NSUP - 1; ++u)
+#pragma unroll
+      for (int k = 0; k < KS; ++k) fetch_stage(key_of(k, u), KS * u + k);
   }
   // Per-lane byte offsets into the swizzled tiles. Chunk c of row r sits at
   // 16 * (c ^ swz_bits<D>(r)); the XOR touches only the low SWB bits of c, so the
@@ -456,31 +505,28 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   // this wavefront's Q rows in the LDS Q tile, one base per k-chunk group
   unsigned q_base[kQLds ? NKG : 1];
   if constexpr (kQLds) {
-    const unsigned qa0 = lds_addr(smem) + (unsigned)(RW * w * D * 2);
+    const unsigned qa0 = lds_addr(smem) + (unsigned)(RW * rg * D * 2);
 #pragma unroll
     for (int m = 0; m < NKG; ++m) q_base[m] = (qa0 + k_lane[m]) & kLdsMask;
   }
   // loop-invariant read bases of stage 0 (stage st adds st * TILE_BYTES)
   unsigned k_base[NKG], v_base[RW == 32 ? 2 : 1][NVG];
 #pragma unroll
-  for (int m = 0; m < NKG; ++m) k_base[m] = (lds0 + k_lane[m]) & kLdsMask;
+  for (int m = 0; m < NKG; ++m) k_base[m] = (lds0 + kh * TILE_BYTES + k_lane[m]) & kLdsMask;
 #pragma unroll
   for (int hf = 0; hf < (RW == 32 ? 2 : 1); ++hf)
 #pragma unroll
-    for (int m = 0; m < NVG; ++m) v_base[hf][m] = (lds0 + NSTAGE * TILE_BYTES + v_lane[hf][m]) & kLdsMask;
+    for (int m = 0; m < NVG; ++m)
+      v_base[hf][m] = (lds0 + (NSTAGE + kh) * TILE_BYTES + v_lane[hf][m]) & kLdsMask;
 
-  // one tile: t in the live list, held by stage st
-  auto tile_step = [&](const int t, const int st) __attribute__((always_inline)) {
-    wait_vmcnt<PW * (NSTAGE - 2)>();
-    tile_barrier();
-    const int jn = tile_key0(t + NSTAGE - 1);
-    const int stn = (st + NSTAGE - 1) % NSTAGE;   // the stage tile t - 1 used
-    fetch_group(0, jn, stn);
-
-    const int j0 = __builtin_amdgcn_readfirstlane((int)s_list[t] * kTileKeys);
+  // one tile from key j0, held by stage KS*ss + kh (super-stage ss); jn / ssn
+  // name the super-stage whose fetches go out during its S^T MFMAs
+  auto tile_step = [&](const int j0, const int ss, const int* jn, const int ssn)
+                       __attribute__((always_inline)) {
     const bool full = j0 + kTileKeys <= np;   // no key of the tile at or past nonpad
-    const unsigned char* ms = stages + 2 * NSTAGE * TILE_BYTES + st * MASK_BYTES;
-    const unsigned KO = (unsigned)(st * TILE_BYTES);   // stage offset of K and V reads
+    const unsigned char* ms = stages + 2 * NSTAGE * TILE_BYTES + (KS * ss + kh) * MASK_BYTES;
+    // stage offset of K and V reads (the key half's kh * TILE_BYTES is in the bases)
+    const unsigned KO = (unsigned)(KS * ss * TILE_BYTES);
 
     if constexpr (RW == 32) {
       // this lane's bias values (or slot kinds) for keys 8*i + 4*(l/32) + jj,
@@ -537,7 +583,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (i + PD < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, NQR, 0);
         constexpr int GS = KSTEPS / kFG;   // k-steps per fetch group
-        if (kFG > 1 && i % GS == GS - 1 && i / GS + 1 < kFG) fetch_group(i / GS + 1, jn, stn);
+        if (kFG > 1 && i % GS == GS - 1 && i / GS + 1 < kFG) fetch_group(i / GS + 1, jn, ssn);
       }
       f32x16 sacc = schain[0];
 #pragma unroll
@@ -709,6 +755,8 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
           sacc[n & 1] = mfma16x16x32(a, qf[n >> 1], sacc[n & 1]);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           if (n + PD < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          constexpr int GS = NS / kFG;   // steps per fetch group
+          if (kFG > 1 && n % GS == GS - 1 && n / GS + 1 < kFG) fetch_group(n / GS + 1, jn, ssn);
         }
       }
       // V^T fragments of the first PV MFMAs, read while the softmax runs;
@@ -802,19 +850,68 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
       }
     }
   };
-  if constexpr (NSTAGE == 2) {
-    // two tiles per iteration: each with its stage known at compile time
-    for (int t = 0; t < n_live; t += 2) {
-      tile_step(t, 0);
-      if (t + 1 < n_live) tile_step(t + 1, 1);
+  // super-iteration u: wait for this wavefront's fetches of super-stage ss,
+  // barrier, start the fetches of super-iteration u + NSUP - 1 (into the
+  // super-stage u - 1 used), compute tile u of this key half
+  const int n_sup = KS == 1 ? n_live : max(n_h0, n_h1);
+  const int n_mine = kh == 0 ? n_h0 : n_h1;
+  auto step = [&](const int u, const int ss) __attribute__((always_inline)) {
+    wait_vmcnt<KS * PW * (NSUP - 2)>();
+    tile_barrier();
+    int jn[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) jn[k] = key_of(k, u + NSUP - 1);
+    const int ssn = (ss + NSUP - 1) % NSUP;
+    fetch_group(0, jn, ssn);
+    if (KS == 1 || u < n_mine) {
+      tile_step(key_of(kh, u), ss, jn, ssn);
+    } else {
+      // no tile for this key half: the fetches still go out
+#pragma unroll
+      for (int g = 1; g < kFG; ++g) fetch_group(g, jn, ssn);
+    }
+  };
+  if constexpr (NSUP == 2) {
+    // two super-stages per iteration: each known at compile time
+    for (int u = 0; u < n_sup; u += 2) {
+      step(u, 0);
+      if (u + 1 < n_sup) step(u + 1, 1);
     }
   } else {
-    for (int t = 0; t < n_live; ++t) tile_step(t, t % NSTAGE);
+    for (int u = 0; u < n_sup; ++u) step(u, u % NSUP);
   }
   // the fetches of the re-fetched tail stages must land before the workgroup
   // (and its LDS) ends
   wait_vmcnt<0>();
   if constexpr (kAsmAcc) acc_settle(oacc);
+  if constexpr (KS == 2) {
+    // merge the key halves: half 1 leaves (m, l, O^T) in LDS (the stages are
+    // free now), half 0 rescales both to the larger maximum and adds
+    constexpr int NACC = DBLK * (RW == 32 ? 16 : 4);
+    constexpr int NF = NACC + 2;
+    float* xo = reinterpret_cast<float*>(stages) + (size_t)rg * NF * 64 + lane;
+    __syncthreads();
+    if (kh == 1) {
+      xo[0] = m_run;
+      xo[64] = l_run;
+#pragma unroll
+      for (int blk = 0; blk < DBLK; ++blk)
+#pragma unroll
+        for (int e = 0; e < NACC / DBLK; ++e) xo[(2 + blk * (NACC / DBLK) + e) * 64] = oacc[blk][e];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = xo[0], l1 = xo[64];
+    const float mm = fmaxf(m_run, m1);
+    const float f0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mm);
+    const float f1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
+    l_run = l_run * f0 + l1 * f1;
+#pragma unroll
+    for (int blk = 0; blk < DBLK; ++blk)
+#pragma unroll
+      for (int e = 0; e < NACC / DBLK; ++e)
+        oacc[blk][e] = oacc[blk][e] * f0 + xo[(2 + blk * (NACC / DBLK) + e) * 64] * f1;
+  }
 
   // ---- 5. normalise and store -----------------------------------------------
   float l_tot = l_run;
@@ -897,16 +994,16 @@ __global__ __launch_bounds__(256) void tilemap_kernel(const BiasT* __restrict__ 
   if (threadIdx.x == 0) map[wid] = s_word;
 }
 
-template <int D, int RW, int NW, bool kRules, typename BiasT, bool kQReg>
+template <int D, int RW, int NW, bool kRules, typename BiasT, bool kQReg, int KS>
 hipError_t launch_dma_inst(const AttnParams& p, hipStream_t stream) {
-  using Geo = DmaGeom<D, RW, NW, kRules, BiasT, kQReg>;
-  const int MQ = (RW * NW) / p.G;
+  using Geo = DmaGeom<D, RW, NW, kRules, BiasT, kQReg, KS>;
+  const int MQ = (RW * NW / KS) / p.G;
   const int n_qt = (p.S_q + MQ - 1) / MQ;
   const int n_kt = num_tiles(p.T);
   const size_t list = (size_t)((n_kt + 31) / 32) * 4 + (size_t)n_kt * 2;
   const size_t lds = (size_t)Geo::Q_BYTES + (size_t)Geo::NSTAGE * Geo::STAGE_BYTES +
                      ((list + 15) & ~(size_t)15);
-  auto kern = attn_prefill_dma_kernel<D, RW, NW, kRules, BiasT, kQReg>;
+  auto kern = attn_prefill_dma_kernel<D, RW, NW, kRules, BiasT, kQReg, KS>;
   // opt in to exactly the dynamic LDS of this launch (the kernel's static LDS
   // comes on top)
   static size_t lds_set = 0;   // per instantiation
@@ -946,11 +1043,12 @@ hipError_t launch_dma_inst(const AttnParams& p, hipStream_t stream) {
 
 // kQReg: Q^T fragments in registers (RW = 16 always; RW = 32 where the
 // accumulators live in the accumulation registers)
-template <int D, int RW, int NW, bool kQReg = (RW == 16)>
+// KS = 2: two wavefronts per row group, on alternate tiles
+template <int D, int RW, int NW, bool kQReg = (RW == 16), int KS = 1>
 hipError_t launch_dma_v(const AttnParams& p, hipStream_t stream) {
-  if (p.bias == nullptr) return launch_dma_inst<D, RW, NW, true, uint16_t, kQReg>(p, stream);
-  if (p.bias_is_bf16) return launch_dma_inst<D, RW, NW, false, uint16_t, kQReg>(p, stream);
-  return launch_dma_inst<D, RW, NW, false, uint32_t, kQReg>(p, stream);
+  if (p.bias == nullptr) return launch_dma_inst<D, RW, NW, true, uint16_t, kQReg, KS>(p, stream);
+  if (p.bias_is_bf16) return launch_dma_inst<D, RW, NW, false, uint16_t, kQReg, KS>(p, stream);
+  return launch_dma_inst<D, RW, NW, false, uint32_t, kQReg, KS>(p, stream);
 }
 
 }  // namespace
