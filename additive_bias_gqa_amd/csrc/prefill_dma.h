@@ -975,7 +975,7 @@ __global__ __launch_bounds__(256) void tilemap_kernel(const BiasT* __restrict__ 
   bool any = false;
   if (j < j_hi && nrows > 0) {
     const BiasT* col = bias + ((int64_t)b * S_q + s0) * T + j;
-    constexpr int U = 8;   // loads in flight per thread (rows past the tile repeat its last)
+    constexpr int U = 16;  // loads in flight per thread (rows past the tile repeat its last)
     for (int r0 = rr; r0 < nrows; r0 += U * RPP) {
       u32x4 raw[U];
 #pragma unroll

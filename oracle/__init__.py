@@ -49,7 +49,7 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
             build(force=True)
         lib = ctypes.CDLL(_LIB_PATH)
         lib.oracle_scatter.argtypes = [_u8p, _u8p, _i64p] + [ctypes.c_int64] * 6
@@ -59,7 +59,7 @@ def _load():
         lib.oracle_repeat_kv.argtypes = [_f64p, _f64p] + [ctypes.c_int64] * 5
         lib.oracle_repeat_kv.restype = None
         lib.oracle_attention_mha.argtypes = (
-            [_f64p, _f64p, _f64p, _f64p, _f64p, _i64p] + [ctypes.c_int64] * 5
+            [_f64p, _f64p, _f64p, _f64p, _f64p, _i64p] + [ctypes.c_int64] * 6
             + [ctypes.c_double, ctypes.c_double, _i64p, ctypes.c_int64, _f64p])
         lib.oracle_attention_mha.restype = None
         _lib = lib
@@ -152,37 +152,40 @@ def repeat_kv(x, G: int) -> np.ndarray:
 
 
 def attention_mha(q, k, v, bias_, nonpad, scale: float, rows=None, softcap: float = 0.0) -> np.ndarray:
-    """Dense attention with K/V already at Hq heads. Returns [B,H,S_q,D] float64,
-    or [len(rows), D] for the flat rows (b*H + h)*S_q + s when ``rows`` is given.
+    """Dense attention with K/V already at Hq heads: q, k [.., D], v [.., Dv]
+    (the value head size may differ). Returns [B,H,S_q,Dv] float64, or
+    [len(rows), Dv] for the flat rows (b*H + h)*S_q + s when ``rows`` is given.
     softcap > 0 applies softcap * tanh(score / softcap) to scale * q.k before the
     bias is added (0 = none)."""
     qd, kd, vd, bd = _f64(q), _f64(k), _f64(v), _f64(bias_)
     npd = _i64(nonpad)
     B, H, S_q, D = qd.shape
     T = kd.shape[2]
-    if kd.shape != (B, H, T, D) or vd.shape != (B, H, T, D):
-        raise ValueError("k/v must be [B,H,T,D] with the query's heads")
+    Dv = vd.shape[3]
+    if kd.shape != (B, H, T, D) or vd.shape != (B, H, T, Dv):
+        raise ValueError("k must be [B,H,T,D] and v [B,H,T,Dv] with the query's heads")
     if bd.shape != (B, 1, S_q, T):
         raise ValueError("bias must be [B,1,S_q,T]")
     r = _i64(rows)
     n = B * H * S_q if r is None else r.shape[0]
-    out = np.empty((n, D), dtype=np.float64)
+    out = np.empty((n, Dv), dtype=np.float64)
     scratch = np.empty((n, T), dtype=np.float64)
     _load().oracle_attention_mha(
         _ptr(out, _f64p), _ptr(qd, _f64p), _ptr(kd, _f64p), _ptr(vd, _f64p),
-        _ptr(bd, _f64p), _ptr(npd, _i64p), B, H, S_q, T, D, float(scale), float(softcap),
+        _ptr(bd, _f64p), _ptr(npd, _i64p), B, H, S_q, T, D, Dv, float(scale), float(softcap),
         _ptr(r, _i64p), 0 if r is None else n, _ptr(scratch, _f64p))
-    return out.reshape(B, H, S_q, D) if r is None else out
+    return out.reshape(B, H, S_q, Dv) if r is None else out
 
 
 def attention(q, k_cache, v_cache, bias_, nonpad, scale: float, rows=None,
               softcap: float = 0.0) -> np.ndarray:
     """GQA attention: repeat the KV heads (h // G), then dense attention.
 
-    q [B,Hq,S_q,D], k_cache/v_cache [B,Hkv,T,D], bias [B,1,S_q,T], nonpad [B].
-    With ``rows`` (flat (b*Hq + h)*S_q + s indices) only those rows are computed,
-    one batch entry at a time, so the repeated KV heads of one entry are the most
-    that is materialised. Returns float64 [B,Hq,S_q,D] or [len(rows), D].
+    q [B,Hq,S_q,D], k_cache [B,Hkv,T,D], v_cache [B,Hkv,T,Dv], bias [B,1,S_q,T],
+    nonpad [B]. With ``rows`` (flat (b*Hq + h)*S_q + s indices) only those rows
+    are computed, one batch entry at a time, so the repeated KV heads of one
+    entry are the most that is materialised. Returns float64 [B,Hq,S_q,Dv] or
+    [len(rows), Dv].
     """
     npd = _i64(nonpad)
     B, Hq, S_q, D = q.shape
@@ -194,7 +197,7 @@ def attention(q, k_cache, v_cache, bias_, nonpad, scale: float, rows=None,
         return attention_mha(_np(q), repeat_kv(_np(k_cache), G), repeat_kv(_np(v_cache), G),
                              _np(bias_), npd, scale, softcap=softcap)
     rows = _i64(rows)
-    out = np.empty((rows.shape[0], D), dtype=np.float64)
+    out = np.empty((rows.shape[0], v_cache.shape[3]), dtype=np.float64)
     per_batch = Hq * S_q
     for b in np.unique(rows // per_batch):
         b = int(b)

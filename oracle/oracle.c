@@ -130,11 +130,12 @@ void oracle_repeat_kv(double *dst, const double *src, int64_t B, int64_t Hkv,
 
 /* ------------------------------------------------------------------------- */
 /* Dense multi-head attention with an additive bias broadcast over heads.     */
-/* Q [B,H,S_q,D], K/V [B,H,T,D] (KV heads already repeated), bias [B,1,S_q,T], */
-/* out [n_rows, D] for the listed rows (row = (b*H + h)*S_q + s), or          */
-/* [B,H,S_q,D] when rows == NULL.                                             */
-/* [SKL] section 4: x_j = scale * (q . k_j), then + bias, then softmax, then  */
-/* times V (no softcap on this path).                                         */
+/* Q [B,H,S_q,D], K [B,H,T,D], V [B,H,T,Dv] (KV heads already repeated; the    */
+/* value head size Dv may differ from D), bias [B,1,S_q,T], out [n_rows, Dv]  */
+/* for the listed rows (row = (b*H + h)*S_q + s), or [B,H,S_q,Dv] when rows   */
+/* == NULL.                                                                    */
+/* [SKL] section 4: x_j = scale * (q . k_j), softcap when asked, then + bias, */
+/* then softmax, then times V.                                                */
 /* A key j is kept iff j < nonpad[b] and bias != -inf. Excluded keys are left  */
 /* out by selection, so whatever K/V hold there never enters the arithmetic   */
 /* ([SKL] section 6: select, not multiply).                                   */
@@ -144,7 +145,7 @@ void oracle_repeat_kv(double *dst, const double *src, int64_t B, int64_t Hkv,
 void oracle_attention_mha(double *out, const double *q, const double *k,
                           const double *v, const double *bias,
                           const int64_t *nonpad, int64_t B, int64_t H,
-                          int64_t S_q, int64_t T, int64_t D, double scale,
+                          int64_t S_q, int64_t T, int64_t D, int64_t Dv, double scale,
                           double softcap, const int64_t *rows, int64_t n_rows,
                           double *scratch /* [n_rows or B*H*S_q, T] */) {
   const int64_t total = rows ? n_rows : B * H * S_q;
@@ -160,7 +161,7 @@ void oracle_attention_mha(double *out, const double *q, const double *k,
     const double *qr = q + ((b * H + h) * S_q + s) * D;
     const double *br = bias + (b * S_q + s) * T;
     double *x = scratch + r * T;
-    double *o = out + r * D;
+    double *o = out + r * Dv;
 
     /* scores of the kept keys; -inf marks an excluded key */
     double m = -INFINITY;
@@ -183,7 +184,7 @@ void oracle_attention_mha(double *out, const double *q, const double *k,
       ++kept;
     }
 
-    for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+    for (int64_t d = 0; d < Dv; ++d) o[d] = 0.0;
     if (kept == 0) continue; /* fully masked row: Y = 0 */
 
     double denom = 0.0;
@@ -192,9 +193,9 @@ void oracle_attention_mha(double *out, const double *q, const double *k,
       if (!keep) continue;
       const double w = exp(x[j] - m);
       denom += w;
-      const double *vr = v + ((b * H + h) * T + j) * D;
-      for (int64_t d = 0; d < D; ++d) o[d] += w * vr[d];
+      const double *vr = v + ((b * H + h) * T + j) * Dv;
+      for (int64_t d = 0; d < Dv; ++d) o[d] += w * vr[d];
     }
-    for (int64_t d = 0; d < D; ++d) o[d] /= denom;
+    for (int64_t d = 0; d < Dv; ++d) o[d] /= denom;
   }
 }

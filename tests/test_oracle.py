@@ -323,6 +323,49 @@ def test_attention_masks_and_nonpad_are_sdpa():
                 assert np.all(y[b, :, s] == 0.0)
 
 
+@pytest.mark.parametrize("D,Dv", [(4, 12), (12, 4)])
+def test_value_head_size_is_sdpa(D, Dv):
+    # head_size != v_head_size (K and V of different head sizes, as KV-shared
+    # layers borrowing another layer's V produce): the scores use D, the
+    # output takes V's Dv columns; SDPA defines the same product
+    rng = wl.rng_for(104 + D)
+    B, Hq, Hkv, S_q, T = 2, 6, 3, 5, 13
+    q, k = _rand(rng, (B, Hq, S_q, D)), _rand(rng, (B, Hkv, T, D))
+    v = _rand(rng, (B, Hkv, T, Dv))
+    bias = _rand(rng, (B, 1, S_q, T))
+    bias[rng.random(bias.shape) < 0.3] = NEG_INF
+    nonpad = np.array([T, 8])
+    y = oracle.attention(q, k, v, bias, nonpad, 0.6)
+    assert y.shape == (B, Hq, S_q, Dv)
+    full = bias.copy()
+    for b in range(B):
+        full[b, :, :, nonpad[b]:] = NEG_INF
+    live = np.isfinite(full).any(axis=-1)
+    ref = _sdpa(q, k, v, full, 0.6)
+    for b in range(B):
+        for s in range(S_q):
+            if live[b, 0, s]:
+                np.testing.assert_allclose(y[b, :, s], ref[b, :, s], rtol=0, atol=1e-12)
+            else:
+                assert np.all(y[b, :, s] == 0.0)
+
+
+def test_value_head_size_columns_are_independent():
+    # each output column is the same weighted mean of one V column: a V of
+    # Dv columns gives what Dv single-column V's give, and the weights do not
+    # depend on V at all (a closed form of softmax(.) V)
+    rng = wl.rng_for(106)
+    B, Hq, Hkv, S_q, T, D, Dv = 1, 2, 1, 3, 9, 5, 7
+    q, k, v = _rand(rng, (B, Hq, S_q, D)), _rand(rng, (B, Hkv, T, D)), _rand(rng, (B, Hkv, T, Dv))
+    bias = oracle.bias(np.array([T]), None, None, S_q, T, 0)
+    y = oracle.attention(q, k, v, bias, [T], 0.4)
+    for c in range(Dv):
+        yc = oracle.attention(q, k, v[..., c:c + 1], bias, [T], 0.4)
+        np.testing.assert_allclose(y[..., c:c + 1], yc, rtol=0, atol=0)
+    ones = oracle.attention(q, k, np.ones((B, Hkv, T, 3)), bias, [T], 0.4)
+    np.testing.assert_allclose(ones, 1.0, rtol=0, atol=1e-14)
+
+
 def test_attention_mpmath_bruteforce():
     import mpmath as mp
     mp.mp.dps = 50
