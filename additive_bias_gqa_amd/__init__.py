@@ -62,10 +62,10 @@ def load():
         lib.build_static_cache_bias.argtypes = [vp, ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, vp]
         lib.build_static_cache_bias.restype = ctypes.c_int
         lib.attn_bias_gqa_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
-                                          i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                                          i64, i64, i64, i64, i64, i64, i64, ctypes.c_float,
                                           ctypes.c_float, i64, ctypes.c_int, vp, sz, vp]
         lib.attn_bias_gqa_fwd.restype = ctypes.c_int
-        lib.attn_bias_gqa_workspace_bytes.argtypes = [i64] * 6
+        lib.attn_bias_gqa_workspace_bytes.argtypes = [i64] * 7
         lib.attn_bias_gqa_workspace_bytes.restype = sz
         lib.abgqa_last_error.argtypes = []
         lib.abgqa_last_error.restype = ctypes.c_char_p
@@ -179,8 +179,9 @@ def build_static_cache_bias(nonpad: torch.Tensor, q_start: torch.Tensor | None,
     return out
 
 
-def attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, max_seq, D) -> int:
-    return int(load().attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, max_seq, D))
+def attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, max_seq, D, D_v=None) -> int:
+    return int(load().attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, max_seq, D,
+                                                    D if D_v is None else D_v))
 
 
 _workspaces: dict = {}
@@ -209,16 +210,19 @@ def attn_bias_gqa_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     """softmax(cap(scale * Q K^T) + bias) V over the static cache (GQA: head h
     reads KV head h // (Hq // Hkv)); cap(x) = softcap * tanh(x / softcap) when
     softcap > 0, else x. bias=None evaluates the static-cache rules (nonpad,
-    q_start, slot_kind, window) inside the kernel instead."""
-    if q.dim() != 4 or k_cache.dim() != 4:
-        raise ValueError("q must be [B, Hq, S_q, D] and the caches [B, Hkv, max_seq, D]")
+    q_start, slot_kind, window) inside the kernel instead. V may have another
+    head size than Q and K (the output takes V's)."""
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, S_q, D], k_cache [B, Hkv, max_seq, D], "
+                         "v_cache [B, Hkv, max_seq, D_v]")
     B, Hq, S_q, D = q.shape
     Hkv, T = k_cache.shape[1], k_cache.shape[2]
+    Dv = v_cache.shape[3]
     if q.dtype not in _DTYPE:
         raise ValueError("q must be float32 or bfloat16")
     qp = _dev(q, "q")
     kp = _dev(k_cache, "k_cache", q.dtype, (B, Hkv, T, D))
-    vp_ = _dev(v_cache, "v_cache", q.dtype, (B, Hkv, T, D))
+    vp_ = _dev(v_cache, "v_cache", q.dtype, (B, Hkv, T, Dv))
     bp, bdt = None, BF16
     if bias is not None:
         if bias.dtype not in _DTYPE:
@@ -228,15 +232,15 @@ def attn_bias_gqa_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     qs = _opt(q_start, "q_start", torch.int64, (B,))
     sk = _opt(slot_kind, "slot_kind", torch.int32, (B, T))
     if out is None:
-        out = torch.empty_like(q)
-    op = _dev(out, "out", q.dtype, q.shape)
+        out = q.new_empty((B, Hq, S_q, Dv))
+    op = _dev(out, "out", q.dtype, (B, Hq, S_q, Dv))
     lib = load()
-    need = int(lib.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, T, D))
+    need = int(lib.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, T, D, Dv))
     if workspace is None:
         workspace = _workspace(q.device, need)
     wp = None if workspace is None else _dev(workspace, "workspace")
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.attn_bias_gqa_fwd(op, qp, kp, vp_, bp, bdt, npd, qs, sk, B, Hq, Hkv, S_q, T, D,
+    _check(lib.attn_bias_gqa_fwd(op, qp, kp, vp_, bp, bdt, npd, qs, sk, B, Hq, Hkv, S_q, T, D, Dv,
                                  float(scale), float(softcap), int(window), _DTYPE[q.dtype], wp, wbytes,
                                  _stream(q)), "attn_bias_gqa_fwd")
     return out

@@ -140,28 +140,33 @@ abgqa_status kv_scatter_and_bias(void* k_cache, void* v_cache, const void* k_upd
 }
 
 size_t attn_bias_gqa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q,
-                                     int64_t max_seq, int64_t D) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_q <= 0 || max_seq <= 0 || D <= 0 || Hq % Hkv) return 0;
+                                     int64_t max_seq, int64_t D, int64_t D_v) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_q <= 0 || max_seq <= 0 || D <= 0 || D_v <= 0 || Hq % Hkv)
+    return 0;
   const int64_t G = Hq / Hkv;
-  if (S_q * G > 16) return abgqa::prefill_workspace_bytes(B, Hq, Hkv, S_q, max_seq, D);
-  return abgqa::decode_workspace_bytes(B, Hkv, S_q, G, D, max_seq);
+  if (S_q * G > 16)
+    return D == D_v ? abgqa::prefill_workspace_bytes(B, Hq, Hkv, S_q, max_seq, D) : 0;
+  if (!abgqa::decode_supports((int)D, (int)D_v)) return 0;
+  return abgqa::decode_workspace_bytes(B, Hkv, S_q, G, D_v, max_seq);
 }
 
 abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, const void* v_cache,
                                const void* bias, abgqa_dtype bias_dtype,
                                const int64_t* nonpad_kv_seqlen, const int64_t* q_start,
                                const int32_t* slot_kind, int64_t B, int64_t Hq, int64_t Hkv,
-                               int64_t S_q, int64_t max_seq, int64_t D, float scale, float softcap,
+                               int64_t S_q, int64_t max_seq, int64_t D, int64_t D_v, float scale,
+                               float softcap,
                                int64_t window, abgqa_dtype dtype, void* workspace,
                                size_t workspace_bytes, void* stream) {
   g_last_error.clear();
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_q <= 0 || max_seq <= 0 || D <= 0)
-    return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: B, Hq, Hkv, S_q, max_seq and D must be positive");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_q <= 0 || max_seq <= 0 || D <= 0 || D_v <= 0)
+    return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: B, Hq, Hkv, S_q, max_seq, D and D_v must be positive");
   if (Hq % Hkv != 0) return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: Hq must be a multiple of Hkv");
   if (!(softcap >= 0.f) || softcap == INFINITY)
     return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: softcap must be finite and >= 0 (0 = none)");
   if (S_q > max_seq) return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: S_q must not exceed max_seq");
-  if (!head_dim_ok(D)) return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: D must be 64, 128, 256 or 512");
+  if (!head_dim_ok(D) || !head_dim_ok(D_v))
+    return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: D and D_v must be 64, 128, 256 or 512");
   if (max_seq > kMaxSeq) return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: max_seq above 2^24");
   if (dtype != ABGQA_F32 && dtype != ABGQA_BF16)
     return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: dtype must be ABGQA_F32 or ABGQA_BF16");
@@ -183,7 +188,7 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
   p.out = out; p.q = q; p.k = k_cache; p.v = v_cache; p.bias = bias;
   p.nonpad = nonpad_kv_seqlen; p.q_start = q_start; p.slot_kind = slot_kind;
   p.B = (int)B; p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.G = (int)G; p.S_q = (int)S_q;
-  p.T = (int)max_seq; p.D = (int)D; p.window = window; p.scale = scale; p.softcap = softcap;
+  p.T = (int)max_seq; p.D = (int)D; p.Dv = (int)D_v; p.window = window; p.scale = scale; p.softcap = softcap;
   p.bias_is_bf16 = (bias_dtype == ABGQA_BF16);
   hipStream_t st = (hipStream_t)stream;
 
@@ -192,9 +197,13 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
   if (dtype == ABGQA_F32) {
     path = "f32";
     e = abgqa::launch_attn_f32(p, st);
+  } else if ((S_q * G <= 16 && !abgqa::decode_supports((int)D, (int)D_v)) || (S_q * G > 16 && D != D_v)) {
+    // head sizes the matrix-core kernels are not built for: the vector path
+    path = "vector";
+    e = abgqa::launch_attn_vec_bf16(p, st);
   } else if (S_q * G <= 16) {
     path = "decode";
-    const size_t need = abgqa::decode_workspace_bytes(B, Hkv, S_q, G, D, max_seq);
+    const size_t need = abgqa::decode_workspace_bytes(B, Hkv, S_q, G, D_v, max_seq);
     if (!workspace || workspace_bytes < need)
       return fail(ABGQA_ERR_WORKSPACE, "attn_bias_gqa_fwd: workspace of %zu bytes needed, %zu given",
                   need, workspace ? workspace_bytes : (size_t)0);
@@ -216,9 +225,9 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
     e = abgqa::launch_attn_prefill(p, st);
   }
   if (log_enabled())
-    fprintf(stderr, "[abgqa] attn_bias_gqa_fwd path=%s B=%lld Hq=%lld Hkv=%lld S_q=%lld T=%lld D=%lld %s splits=%d\n",
+    fprintf(stderr, "[abgqa] attn_bias_gqa_fwd path=%s B=%lld Hq=%lld Hkv=%lld S_q=%lld T=%lld D=%lld D_v=%lld %s splits=%d\n",
             path, (long long)B, (long long)Hq, (long long)Hkv, (long long)S_q, (long long)max_seq,
-            (long long)D, bias ? "bias" : "rules", p.n_split);
+            (long long)D, (long long)D_v, bias ? "bias" : "rules", p.n_split);
   if (e != hipSuccess) return hip_fail("attn_bias_gqa_fwd", e);
   return ABGQA_OK;
 }

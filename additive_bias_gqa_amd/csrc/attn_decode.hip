@@ -105,23 +105,24 @@ constexpr int kSampleStride = 256;
 
 // workspace: one partial record per (kv head, rank), rank < B * n_split, then
 // per (kv head, b) the first rank and the number of splits of that row
-size_t decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_q, int64_t G, int64_t D,
+size_t decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_q, int64_t G, int64_t Dv,
                               int64_t max_seq) {
   const int64_t NR = round_up_rows(S_q * G);
   const int64_t n_split = decode_num_splits(B, Hkv, max_seq);
-  return (size_t)B * Hkv * n_split * part_floats(NR, D) * sizeof(float) +
+  return (size_t)B * Hkv * n_split * part_floats(NR, Dv) * sizeof(float) +
          (size_t)B * Hkv * 2 * sizeof(int);
 }
 
-template <int D, int NR, int NW, bool kRules, typename BiasT>
+// D: head size of Q and K; DV: of V and the output (they may differ)
+template <int D, int DV, int NR, int NW, bool kRules, typename BiasT>
 __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   constexpr int kDecThreads = NW * 64;
   constexpr int kDecWaves = NW;
   constexpr int KSTEPS = D / 32;    // matrix-core k-steps over the head dim
-  constexpr int LPR = D / 8;        // lanes per V row (8 bf16 per lane)
+  constexpr int LPR = DV / 8;       // lanes per V row (8 bf16 per lane)
   constexpr int KPI = 64 / LPR;     // V rows per wavefront load
   constexpr int NV = 16 / KPI;      // V loads per 16-key block
-  constexpr int PART = (int)part_floats(NR, D);
+  constexpr int PART = (int)part_floats(NR, DV);
   constexpr int E = NR < 4 ? NR : 4;      // real rows per lane group (r = 4*grp + e)
   constexpr bool kQinLds = D >= 256;      // keep the A operand out of VGPRs
 
@@ -132,8 +133,8 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   // wave merge: each wave's rescaled O in its own slot, summed in a fixed order
   // (one barrier), unless that needs more than 32 KiB: then accumulate wave by
   // wave into one buffer
-  constexpr bool kParMerge = NW * NR * D <= 8192;
-  __shared__ float s_o[kParMerge ? NW * NR * D : NR * D];
+  constexpr bool kParMerge = NW * NR * DV <= 8192;
+  __shared__ float s_o[kParMerge ? NW * NR * DV : NR * DV];
   __shared__ __align__(16) __bf16 s_q[kQinLds ? NR * D : 8];  // Q rows (A operand)
   __shared__ int s_rlo[kDecWaves], s_rhi[kDecWaves];
   __shared__ int32_t s_kq[16];
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   // (no memory fence before the scan: waiting here for the Q loads above would
   // put two memory round trips ahead of the K/V loads)
   if constexpr (!kParMerge)
-    for (int i = tid; i < NR * D; i += kDecThreads) s_o[i] = 0.f;
+    for (int i = tid; i < NR * DV; i += kDecThreads) s_o[i] = 0.f;
   // this row's exact range (bias variant): every key below nonpad whose bias
   // is not -inf, over the S_q rows, reduced into s_rlo / s_rhi per wavefront.
   // NB loads per thread in flight at once, unconditional (index clamped to the
@@ -428,7 +429,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   const float cap2 = p.softcap * kLog2e, scale_over_cap = cap_on ? p.scale / p.softcap : 0.f;
 
   const __bf16* kbase = (const __bf16*)p.k + (b * p.Hkv + hk) * (int64_t)T * D;
-  const __bf16* vbase = (const __bf16*)p.v + (b * p.Hkv + hk) * (int64_t)T * D;
+  const __bf16* vbase = (const __bf16*)p.v + (b * p.Hkv + hk) * (int64_t)T * DV;
   const BiasT* biasb = kRules ? nullptr : (const BiasT*)p.bias + b * p.S_q * (int64_t)T;
   const int32_t* kindb = p.slot_kind ? p.slot_kind + b * T : nullptr;
 
@@ -453,7 +454,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   // D = 512 with 8 wavefronts (two 32 KiB blocks per lane set do not fit the
   // 256 registers a wavefront gets at two per SIMD; with one wavefront per
   // SIMD the second buffer lives in the accumulation registers).
-  constexpr bool kPrefetch = D <= 256 || NW == 4;
+  constexpr bool kPrefetch = (D <= 256 && DV <= 256) || NW == 4;
   struct Blk {
     BiasT bias[E];
     int32_t kj;
@@ -478,7 +479,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
 #pragma unroll
     for (int it = 0; it < NV; ++it) {
       const int jv = min(j0 + it * KPI + vkey, my_hi - 1);
-      bl.v[it] = ld_global<bf16x8>(vbase + (int64_t)jv * D + vd);
+      bl.v[it] = ld_global<bf16x8>(vbase + (int64_t)jv * DV + vd);
     }
   };
   const int stride = 16 * kDecWaves;
@@ -650,17 +651,17 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         const float f = (m_wg[r] == -INFINITY) ? 0.f : fast_exp2(s_m[w][r] - m_wg[r]);
-        float* dst = &s_o[(w * NR + r) * D + vd];
+        float* dst = &s_o[(w * NR + r) * DV + vd];
 #pragma unroll
         for (int c = 0; c < 8; ++c) dst[c] = o[r][c] * f;
       }
     }
     __syncthreads();
-    for (int i = tid; i < NR * D / 4; i += kDecThreads) {
+    for (int i = tid; i < NR * DV / 4; i += kDecThreads) {
       f32x4 acc = reinterpret_cast<const f32x4*>(s_o)[i];
 #pragma unroll
       for (int ww = 1; ww < kDecWaves; ++ww)
-        acc += reinterpret_cast<const f32x4*>(s_o + ww * NR * D)[i];
+        acc += reinterpret_cast<const f32x4*>(s_o + ww * NR * DV)[i];
       reinterpret_cast<f32x4*>(part)[i] = acc;
     }
   } else {
@@ -670,14 +671,14 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
           const float f = (m_wg[r] == -INFINITY) ? 0.f : fast_exp2(s_m[w][r] - m_wg[r]);
-          float* dst = &s_o[r * D + vd];
+          float* dst = &s_o[r * DV + vd];
 #pragma unroll
           for (int c = 0; c < 8; ++c) dst[c] = fmaf(o[r][c], f, dst[c]);
         }
       }
       __syncthreads();
     }
-    for (int i = tid; i < NR * D / 4; i += kDecThreads)
+    for (int i = tid; i < NR * DV / 4; i += kDecThreads)
       reinterpret_cast<f32x4*>(part)[i] = reinterpret_cast<const f32x4*>(s_o)[i];
   }
   if (tid < NR) {
@@ -688,8 +689,8 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
       const float f = (m_wg[r] == -INFINITY) ? 0.f : fast_exp2(s_m[ww][r] - m_wg[r]);
       lsum += s_l[ww][r] * f;
     }
-    part[NR * D + r] = m_wg[r];
-    part[NR * D + NR + r] = lsum;
+    part[NR * DV + r] = m_wg[r];
+    part[NR * DV + NR + r] = lsum;
   }
 }
 
@@ -699,6 +700,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
 // (a split that saw no live key has m_i = -inf and drops out; no live key at
 // all gives y = 0). One workgroup of 64 threads per (b, kv head, row), each
 // thread 8 consecutive values of d.
+// D here: the head size of V and the output
 template <int D, int NR>
 __global__ __launch_bounds__(64) void attn_decode_combine_kernel(AttnParams p) {
   constexpr int PART = (int)part_floats(NR, D);
@@ -781,26 +783,26 @@ static int decode_waves(int D) {
   return D >= 512 ? 8 : 4;
 }
 
-template <int D, int NR, int NW>
+template <int D, int DV, int NR, int NW>
 static void launch_decode_nw(const AttnParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.n_split));
   if (p.bias == nullptr)
-    hipLaunchKernelGGL((attn_decode_kernel<D, NR, NW, true, uint16_t>), grid, dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_decode_kernel<D, DV, NR, NW, true, uint16_t>), grid, dim3(NW * 64), 0, stream, p);
   else if (p.bias_is_bf16)
-    hipLaunchKernelGGL((attn_decode_kernel<D, NR, NW, false, uint16_t>), grid, dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_decode_kernel<D, DV, NR, NW, false, uint16_t>), grid, dim3(NW * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_decode_kernel<D, NR, NW, false, uint32_t>), grid, dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_decode_kernel<D, DV, NR, NW, false, uint32_t>), grid, dim3(NW * 64), 0, stream, p);
 }
 
-template <int D, int NR>
+template <int D, int DV, int NR>
 static hipError_t launch_decode_d(const AttnParams& p, hipStream_t stream) {
   // 8 wavefronts (two per SIMD) only where their registers hold the work
   // without spilling: up to 4 rows per lane group
   if constexpr (NR <= 4) {
-    if (decode_waves(D) == 8) launch_decode_nw<D, NR, 8>(p, stream);
-    else launch_decode_nw<D, NR, 4>(p, stream);
+    if (decode_waves(D > DV ? D : DV) == 8) launch_decode_nw<D, DV, NR, 8>(p, stream);
+    else launch_decode_nw<D, DV, NR, 4>(p, stream);
   } else {
-    launch_decode_nw<D, NR, 4>(p, stream);
+    launch_decode_nw<D, DV, NR, 4>(p, stream);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -810,30 +812,43 @@ static hipError_t launch_decode_d(const AttnParams& p, hipStream_t stream) {
   // the combine reads the partials after the split kernel completes (stream
   // order), so no device-scope fence is needed inside the split kernel
   const dim3 cgrid((unsigned)((int64_t)p.B * p.Hkv * p.S_q * p.G));
-  hipLaunchKernelGGL((attn_decode_combine_kernel<D, NR>), cgrid, dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((attn_decode_combine_kernel<DV, NR>), cgrid, dim3(64), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) set_launch_detail("decode combine launch");
   return e;
 }
 
-template <int D>
+template <int D, int DV>
 static hipError_t launch_decode_nr(const AttnParams& p, hipStream_t stream) {
   const int R = p.S_q * p.G;
-  if (R <= 1) return launch_decode_d<D, 1>(p, stream);
-  if (R <= 2) return launch_decode_d<D, 2>(p, stream);
-  if (R <= 4) return launch_decode_d<D, 4>(p, stream);
-  if (R <= 8) return launch_decode_d<D, 8>(p, stream);
-  return launch_decode_d<D, 16>(p, stream);
+  if (R <= 1) return launch_decode_d<D, DV, 1>(p, stream);
+  if (R <= 2) return launch_decode_d<D, DV, 2>(p, stream);
+  if (R <= 4) return launch_decode_d<D, DV, 4>(p, stream);
+  if (R <= 8) return launch_decode_d<D, DV, 8>(p, stream);
+  return launch_decode_d<D, DV, 16>(p, stream);
+}
+
+// Head sizes the split-KV kernel is built for: every D with DV = D, and the
+// pairs of the 256 / 512 heads of sliding and full-attention layers (a
+// KV-shared layer reading the V of a layer with the other head size).
+bool decode_supports(int D, int Dv) {
+  if (D == Dv) return D == 64 || D == 128 || D == 256 || D == 512;
+  return (D == 256 && Dv == 512) || (D == 512 && Dv == 256);
 }
 
 hipError_t launch_attn_decode(const AttnParams& p, hipStream_t stream) {
-  switch (p.D) {
-    case 64: return launch_decode_nr<64>(p, stream);
-    case 128: return launch_decode_nr<128>(p, stream);
-    case 256: return launch_decode_nr<256>(p, stream);
-    case 512: return launch_decode_nr<512>(p, stream);
-    default: return hipErrorInvalidValue;
+  if (p.D == p.Dv) {
+    switch (p.D) {
+      case 64: return launch_decode_nr<64, 64>(p, stream);
+      case 128: return launch_decode_nr<128, 128>(p, stream);
+      case 256: return launch_decode_nr<256, 256>(p, stream);
+      case 512: return launch_decode_nr<512, 512>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
   }
+  if (p.D == 256 && p.Dv == 512) return launch_decode_nr<256, 512>(p, stream);
+  if (p.D == 512 && p.Dv == 256) return launch_decode_nr<512, 256>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace abgqa

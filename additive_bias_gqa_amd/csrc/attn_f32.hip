@@ -7,27 +7,37 @@
 // key writes zeros (section 6). Query head h reads KV head h / G (onnxruntime
 // PR #28242, CPU GQA excerpt). Softmax is online, in base 2.
 //
-// This path serves fp32 inputs (small shapes, exactness at 1e-5); bf16 inputs
-// use the matrix-core kernels.
+// This path serves fp32 inputs (small shapes, exactness at 1e-5). Built for
+// bf16 inputs as well (fp32 arithmetic, the output rounded to bf16 once), it
+// is the path for head-size pairs the matrix-core kernels are not built for;
+// Q and K have head size D, V and the output Dv (which may differ: onnxruntime
+// skill "cuda-attention-kernel-patterns", the head_size != v_head_size rows of
+// its dispatch table).
 #include "common.h"
 #include "kernels.h"
 #include "mask_rules.h"
 
 namespace abgqa {
 
-template <bool kRules, typename BiasT>
+// element loads and stores: fp32, or bf16 held as its 16 bits
+__device__ __forceinline__ float ld_elem(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld_elem(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+__device__ __forceinline__ void st_elem(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void st_elem(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+
+template <typename Elem, bool kRules, typename BiasT>
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p, int64_t n_rows) {
   extern __shared__ float smem[];
   float* q_s = smem;            // [D]
   float* p_s = smem + p.D;      // [64]
   const int lane = threadIdx.x;
-  const int D = p.D, T = p.T;
-  const float* qg = (const float*)p.q;
-  const float* kg = (const float*)p.k;
-  const float* vg = (const float*)p.v;
-  float* og = (float*)p.out;
-  constexpr int kMaxDPerLane = 8;  // D <= 512
-  const int d_per_lane = (D + 63) / 64;
+  const int D = p.D, Dv = p.Dv, T = p.T;
+  const Elem* qg = (const Elem*)p.q;
+  const Elem* kg = (const Elem*)p.k;
+  const Elem* vg = (const Elem*)p.v;
+  Elem* og = (Elem*)p.out;
+  constexpr int kMaxDPerLane = 8;  // Dv <= 512
+  const int d_per_lane = (Dv + 63) / 64;
 
   for (int64_t row = blockIdx.x; row < n_rows; row += gridDim.x) {
     const int s = (int)(row % p.S_q);
@@ -39,10 +49,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p, int64_t n_ro
     if constexpr (kRules) rule = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s, p.S_q, T, p.window);
     const BiasT* brow = kRules ? nullptr : (const BiasT*)p.bias + (b * p.S_q + s) * T;
     const int32_t* krow = p.slot_kind ? p.slot_kind + b * T : nullptr;
-    const float* kbase = kg + (b * p.Hkv + hk) * (int64_t)T * D;
-    const float* vbase = vg + (b * p.Hkv + hk) * (int64_t)T * D;
+    const Elem* kbase = kg + (b * p.Hkv + hk) * (int64_t)T * D;
+    const Elem* vbase = vg + (b * p.Hkv + hk) * (int64_t)T * Dv;
 
-    for (int d = lane; d < D; d += 64) q_s[d] = qg[row * D + d];
+    for (int d = lane; d < D; d += 64) q_s[d] = ld_elem(qg, row * D + d);
     __syncthreads();
 
     float o[kMaxDPerLane];
@@ -64,9 +74,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p, int64_t n_ro
           keep = bv != -INFINITY;
         }
         if (keep) {
-          const float* kr = kbase + j * D;
+          const Elem* kr = kbase + j * D;
           float dot = 0.f;
-          for (int d = 0; d < D; ++d) dot = fmaf(q_s[d], kr[d], dot);
+          for (int d = 0; d < D; ++d) dot = fmaf(q_s[d], ld_elem(kr, d), dot);
           float sc = dot * p.scale;
           // softcap (skill page, section 4): before the bias; 0 = none
           if (p.softcap > 0.f) sc = p.softcap * tanhf(sc / p.softcap);
@@ -86,10 +96,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p, int64_t n_ro
         if (i < d_per_lane) {
           const int d = lane + 64 * i;
           float acc = o[i] * alpha;
-          if (d < D) {
+          if (d < Dv) {
             for (int jj = 0; jj < nj; ++jj) {
               const float w = p_s[jj];
-              if (w != 0.f) acc = fmaf(w, vbase[(j0 + jj) * D + d], acc);  // select, not multiply
+              if (w != 0.f) acc = fmaf(w, ld_elem(vbase, (j0 + jj) * Dv + d), acc);  // select, not multiply
             }
           }
           o[i] = acc;
@@ -100,24 +110,33 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p, int64_t n_ro
 #pragma unroll
     for (int i = 0; i < kMaxDPerLane; ++i) {
       const int d = lane + 64 * i;
-      if (i < d_per_lane && d < D) og[row * D + d] = (l > 0.f) ? o[i] / l : 0.f;
+      if (i < d_per_lane && d < Dv) st_elem(og, row * Dv + d, (l > 0.f) ? o[i] / l : 0.f);
     }
     __syncthreads();
   }
 }
 
-hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream) {
+template <typename Elem>
+static hipError_t launch_vec(const AttnParams& p, hipStream_t stream) {
   const int64_t n_rows = (int64_t)p.B * p.Hq * p.S_q;
   int64_t blocks = n_rows < 65535 ? n_rows : 65535;
   const size_t lds = (size_t)(p.D + 64) * sizeof(float);
   if (p.bias == nullptr) {
-    hipLaunchKernelGGL((attn_f32_kernel<true, float>), dim3((unsigned)blocks), dim3(64), lds, stream, p, n_rows);
+    hipLaunchKernelGGL((attn_f32_kernel<Elem, true, float>), dim3((unsigned)blocks), dim3(64), lds, stream, p,
+                       n_rows);
   } else if (p.bias_is_bf16) {
-    hipLaunchKernelGGL((attn_f32_kernel<false, uint16_t>), dim3((unsigned)blocks), dim3(64), lds, stream, p, n_rows);
+    hipLaunchKernelGGL((attn_f32_kernel<Elem, false, uint16_t>), dim3((unsigned)blocks), dim3(64), lds, stream,
+                       p, n_rows);
   } else {
-    hipLaunchKernelGGL((attn_f32_kernel<false, float>), dim3((unsigned)blocks), dim3(64), lds, stream, p, n_rows);
+    hipLaunchKernelGGL((attn_f32_kernel<Elem, false, float>), dim3((unsigned)blocks), dim3(64), lds, stream, p,
+                       n_rows);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream) { return launch_vec<float>(p, stream); }
+hipError_t launch_attn_vec_bf16(const AttnParams& p, hipStream_t stream) {
+  return launch_vec<uint16_t>(p, stream);
 }
 
 }  // namespace abgqa

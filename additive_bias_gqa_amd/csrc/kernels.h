@@ -34,15 +34,16 @@ hipError_t launch_prepare(void* k_cache, void* v_cache, const void* k_update, co
 
 // Everything an attention kernel reads, passed by value.
 struct AttnParams {
-  void* out;                 // [B, Hq, S_q, D]
+  void* out;                 // [B, Hq, S_q, Dv]
   const void* q;             // [B, Hq, S_q, D]
   const void* k;             // [B, Hkv, T, D]
-  const void* v;             // [B, Hkv, T, D]
+  const void* v;             // [B, Hkv, T, Dv]
   const void* bias;          // [B, 1, S_q, T] or null (in-kernel rules)
   const int64_t* nonpad;     // [B]
   const int64_t* q_start;    // [B] or null (rules variant only)
   const int32_t* slot_kind;  // [B, T] or null (rules variant only)
   int B, Hq, Hkv, G, S_q, T, D;
+  int Dv;                    // head size of V and the output
   int64_t window;            // rules variant only; <= 0 none
   float scale;               // multiplies q.k
   float softcap;             // > 0: softcap * tanh(scale * q.k / softcap) before the bias
@@ -62,11 +63,15 @@ struct AttnParams {
 
 // fp32 path (any S_q): one wavefront per query row.
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
+// the same computation for bf16 inputs (fp32 arithmetic, bf16 output): the
+// path for head sizes the matrix-core kernels are not built for
+hipError_t launch_attn_vec_bf16(const AttnParams& p, hipStream_t stream);
 
 // bf16 decode path (S_q * G <= 16): split-KV kernel, then a combine kernel.
 int decode_num_splits(int64_t B, int64_t Hkv, int64_t max_seq);
-size_t decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_q, int64_t G, int64_t D,
+size_t decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_q, int64_t G, int64_t Dv,
                               int64_t max_seq);
+bool decode_supports(int D, int Dv);
 hipError_t launch_attn_decode(const AttnParams& p, hipStream_t stream);
 
 // bf16 prefill path: matrix-core tiles, K/V tiles in LDS shared by the G heads.

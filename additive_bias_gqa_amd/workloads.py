@@ -84,13 +84,20 @@ class Workload:
     window: int            # <= 0: no sliding window
     scale: float
     k_cache: torch.Tensor  # [B, Hkv, max_seq, D], contents before the first step
-    v_cache: torch.Tensor
+    v_cache: torch.Tensor  # [B, Hkv, max_seq, Dv]
     steps: List[Step]
 
+    @property
+    def Dv(self) -> int:
+        return int(self.v_cache.shape[3])
+
     def describe(self) -> dict:
-        return {"workload": self.name, "B": self.B, "Hq": self.Hq, "Hkv": self.Hkv,
-                "D": self.D, "S_q": self.steps[-1].S_q, "max_seq": self.max_seq,
-                "window": self.window, "dtype": str(self.dtype).replace("torch.", "")}
+        d = {"workload": self.name, "B": self.B, "Hq": self.Hq, "Hkv": self.Hkv,
+             "D": self.D, "S_q": self.steps[-1].S_q, "max_seq": self.max_seq,
+             "window": self.window, "dtype": str(self.dtype).replace("torch.", "")}
+        if self.Dv != self.D:
+            d["Dv"] = self.Dv
+        return d
 
 
 def _fill_cache(rng, B, H, max_seq, D, n_valid, dtype) -> torch.Tensor:
@@ -129,24 +136,27 @@ def tiny_fp32(index: int = 0) -> Workload:
                     1.0 / math.sqrt(D), z, z.clone(), steps)
 
 
-def _decode(name, index, B, Hq, Hkv, D, max_seq, window, nonpad_lo, kv_shared, dtype):
+def _decode(name, index, B, Hq, Hkv, D, max_seq, window, nonpad_lo, kv_shared, dtype, Dv=None):
     """Decode step (S_q = 1) at slot nonpad-1 with nonpad ~ U{nonpad_lo..max_seq}.
     Scatter variant: slots < nonpad-1 valid, the new token is scattered at
     nonpad-1, slots >= nonpad-1 start as garbage. KV-shared variant: slots
     < nonpad already valid (written by the layer that owns the cache), no scatter.
-    Draw order: nonpad, q, K cache, V cache, k_new, v_new (scatter variant only)."""
+    Draw order: nonpad, q, K cache, V cache, k_new, v_new (scatter variant only).
+    Dv: head size of V (default D; KV-shared layers may read a V of another
+    head size)."""
+    Dv = D if Dv is None else Dv
     rng = rng_for(index)
     nonpad = rng.integers(nonpad_lo, max_seq, size=B, endpoint=True).astype(np.int64)
     q = normal(rng, (B, Hq, 1, D), dtype)
     n_valid = nonpad if kv_shared else nonpad - 1
     kc = _fill_cache(rng, B, Hkv, max_seq, D, n_valid, dtype)
-    vc = _fill_cache(rng, B, Hkv, max_seq, D, n_valid, dtype)
+    vc = _fill_cache(rng, B, Hkv, max_seq, Dv, n_valid, dtype)
     npt = torch.from_numpy(nonpad)
     if kv_shared:
         kn = vn = wi = None
     else:
         kn = normal(rng, (B, Hkv, 1, D), dtype)
-        vn = normal(rng, (B, Hkv, 1, D), dtype)
+        vn = normal(rng, (B, Hkv, 1, Dv), dtype)
         wi = npt - 1
     kind = torch.zeros((B, max_seq), dtype=torch.int32)  # causal + padding, no pads
     step = Step(q, kn, vn, wi, npt, npt - 1, kind)
@@ -162,12 +172,14 @@ def decode_sliding(index: int = 1, B=8, Hq=16, Hkv=8, D=256, max_seq=4096, windo
 
 
 def decode_full(index: int = 2, B=16, Hq=16, Hkv=4, D=512, max_seq=8192, nonpad_lo=1024,
-                kv_shared: bool = False, dtype=torch.bfloat16) -> Workload:
+                kv_shared: bool = False, dtype=torch.bfloat16, Dv=None) -> Workload:
     """Full-attention decode layer (head_dim 512, no window); ``kv_shared`` reads a
-    borrowed cache with nothing to scatter (kv_sequence_length = 0)."""
+    borrowed cache with nothing to scatter (kv_sequence_length = 0), whose V may
+    have another head size (Dv)."""
     tag = "_kvshared" if kv_shared else ""
-    return _decode(f"decode_full_B{B}_Hq{Hq}_Hkv{Hkv}_D{D}_T{max_seq}{tag}",
-                   index, B, Hq, Hkv, D, max_seq, 0, nonpad_lo, kv_shared, dtype)
+    vtag = "" if Dv is None or Dv == D else f"_Dv{Dv}"
+    return _decode(f"decode_full_B{B}_Hq{Hq}_Hkv{Hkv}_D{D}{vtag}_T{max_seq}{tag}",
+                   index, B, Hq, Hkv, D, max_seq, 0, nonpad_lo, kv_shared, dtype, Dv)
 
 
 def prefill_vision(index: int = 3, B=2, Hq=16, Hkv=8, D=256, S_q=512, max_seq=4096,

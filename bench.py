@@ -52,12 +52,15 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+V_HEAD = None      # --v-head-size: V head size of the KV-shared decode workload
+
+
 def make_workload(name):
     from additive_bias_gqa_amd import workloads as wl
     return {
         "decode_sliding": wl.decode_sliding,
         "decode_full": wl.decode_full,
-        "decode_full_kvshared": lambda: wl.decode_full(kv_shared=True),
+        "decode_full_kvshared": lambda: wl.decode_full(kv_shared=True, Dv=V_HEAD),
         "prefill_vision": wl.prefill_vision,
         "prefill_long": wl.prefill_long,
     }[name]()
@@ -78,7 +81,7 @@ class InputSet:
         self.q_start = step.q_start.to(d)
         self.kind = None if step.slot_kind is None else step.slot_kind.to(d)
         self.bias = torch.empty((w.B, 1, step.S_q, w.max_seq), dtype=w.dtype, device=d)
-        self.out = torch.empty_like(self.q)
+        self.out = torch.empty((w.B, w.Hq, step.S_q, w.Dv), dtype=w.dtype, device=d)
 
 
 VARIANT = "bias"   # "bias": materialised bias tensor; "rules": rules evaluated in-kernel
@@ -89,11 +92,13 @@ def run_scatter_bias(ab, w, step, s):
     """TensorScatter of K and V and the bias build, as one fused launch
     (kv_scatter_and_bias; bit-identical to the three separate calls). The
     KV-shared workload has nothing to scatter; the rules variant builds no bias."""
-    if s.k_new is None and VARIANT != "bias":
+    if s.k_new is None:
+        # KV-shared: nothing to scatter (and V may have another head size)
+        if VARIANT == "bias":
+            ab.build_static_cache_bias(s.nonpad, s.q_start, s.kind, step.S_q, w.max_seq, w.window,
+                                       out=s.bias)
         return
-    k_new = s.k_new if s.k_new is not None else s.k[:, :, :0]
-    v_new = s.v_new if s.v_new is not None else s.v[:, :, :0]
-    ab.kv_scatter_and_bias(s.k, s.v, k_new, v_new, s.wi, s.nonpad, s.q_start, s.kind, step.S_q,
+    ab.kv_scatter_and_bias(s.k, s.v, s.k_new, s.v_new, s.wi, s.nonpad, s.q_start, s.kind, step.S_q,
                            w.window, bias=s.bias if VARIANT == "bias" else None)
 
 
@@ -118,14 +123,14 @@ def work_counts(w, step, s, torch):
     live_keys = int(allowed.any(dim=1).sum().item())              # sum over b of live slots
     nonpad_sum = int(s.nonpad.clamp(0, T).sum().item())
     e = 2 if w.dtype == torch.bfloat16 else 4
-    B, Hq, Hkv, D, S_q = w.B, w.Hq, w.Hkv, w.D, step.S_q
-    kv = live_keys * Hkv * D * 2 * e                               # K and V rows read once
+    B, Hq, Hkv, D, Dv, S_q = w.B, w.Hq, w.Hkv, w.D, w.Dv, step.S_q
+    kv = live_keys * Hkv * (D + Dv) * e                            # K and V rows read once
     bias_read = S_q * nonpad_sum * e                               # bias rows below nonpad
-    qo = 2 * B * Hq * S_q * D * e                                  # Q read + out written
+    qo = B * Hq * S_q * (D + Dv) * e                               # Q read + out written
     attn_bytes = kv + bias_read + qo
-    attn_flops = 4.0 * D * Hq * pairs                              # QK^T and PV, 2 flop/MAC
+    attn_flops = 2.0 * (D + Dv) * Hq * pairs                       # QK^T and PV, 2 flop/MAC
     S_new = 0 if step.k_new is None else step.k_new.shape[2]
-    scatter_bytes = 2 * 2 * B * Hkv * S_new * D * e                # K and V: read + write
+    scatter_bytes = 2 * B * Hkv * S_new * (D + Dv) * e             # K and V: read + write
     kind_bytes = 0 if step.slot_kind is None else B * T * 4
     bias_bytes = B * S_q * T * e + kind_bytes                      # written once, kinds read
     return dict(pairs=pairs, live_keys=live_keys, attn_bytes=attn_bytes, attn_flops=attn_flops,
@@ -155,7 +160,7 @@ def bench_workload(name, steps, warmup, eager, torch, ab):
                   (probe.k, probe.v, probe.q, probe.bias, probe.out))
     n_sets = max(2, min(8, math.ceil(3 * CACHE_BYTES / per_set)))
     sets = [probe] + [InputSet(w, step, torch) for _ in range(n_sets - 1)]
-    need = ab.attn_bias_gqa_workspace_bytes(w.B, w.Hq, w.Hkv, step.S_q, w.max_seq, w.D)
+    need = ab.attn_bias_gqa_workspace_bytes(w.B, w.Hq, w.Hkv, step.S_q, w.max_seq, w.D, w.Dv)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda") if need else None
     log(f"{name}: {n_sets} rotating input sets of {per_set / 2**20:.0f} MiB, workspace {need} B")
 
@@ -398,13 +403,19 @@ def main():
                          "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) and exit")
     ap.add_argument("--softcap", type=float, default=0.0,
                     help="softcap of the attention scores (0 = none, the workloads' setting)")
+    ap.add_argument("--v-head-size", type=int, default=None,
+                    help="head size of V for decode_full_kvshared (KV-shared layers may read "
+                         "a V of another head size; default: the query's)")
     args = ap.parse_args()
+    if args.v_head_size is not None and args.workload != "decode_full_kvshared":
+        ap.error("--v-head-size applies to --workload decode_full_kvshared")
     if args.traffic_from:
         write_traffic(args.workload, *args.traffic_from)
         return
-    global VARIANT, SOFTCAP
+    global VARIANT, SOFTCAP, V_HEAD
     VARIANT = args.variant
     SOFTCAP = args.softcap
+    V_HEAD = args.v_head_size
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported: the "

@@ -159,9 +159,17 @@ abgqa_status kv_scatter_and_bias(void *k_cache, void *v_cache, const void *k_upd
  * #366 (bias present with is_causal = 0: the bias carries the causal rule);
  * onnxruntime PR #28242, CPU GQA excerpt (query head h reads KV head h / G).
  *
- *   out              [B, Hq, S_q, D] of `dtype` (must not alias an input)
+ *   out              [B, Hq, S_q, D_v] of `dtype` (must not alias an input)
  *   q                [B, Hq, S_q, D] of `dtype`
- *   k_cache, v_cache [B, Hkv, max_seq, D] of `dtype`
+ *   k_cache          [B, Hkv, max_seq, D] of `dtype`
+ *   v_cache          [B, Hkv, max_seq, D_v] of `dtype`
+ *   D, D_v           head sizes of Q/K and of V/out, each 64, 128, 256 or 512;
+ *                    they may differ (head_size != v_head_size, the skill
+ *                    page's dispatch table: KV-shared layers reading the V of a
+ *                    layer with another head size). bf16 decode runs on the
+ *                    matrix cores for D_v == D and for (D, D_v) = (256, 512) or
+ *                    (512, 256), bf16 prefill for D_v == D; other pairs take a
+ *                    vector-ALU path (fp32 arithmetic) with the same results.
  *   bias             [B, 1, S_q, max_seq] of `bias_dtype`, broadcast over heads;
  *                    -inf masks a key. NULL selects the in-kernel-rules variant:
  *                    the mask of build_static_cache_bias is evaluated inside the
@@ -207,14 +215,16 @@ abgqa_status attn_bias_gqa_fwd(void *out, const void *q, const void *k_cache,
                                const int64_t *nonpad_kv_seqlen,
                                const int64_t *q_start, const int32_t *slot_kind,
                                int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q,
-                               int64_t max_seq, int64_t D, float scale,
-                               float softcap, int64_t window, abgqa_dtype dtype,
+                               int64_t max_seq, int64_t D, int64_t D_v,
+                               float scale, float softcap, int64_t window,
+                               abgqa_dtype dtype,
                                void *workspace, size_t workspace_bytes,
                                void *stream);
 
 /* Bytes of workspace attn_bias_gqa_fwd needs for this shape (0 if none). */
 size_t attn_bias_gqa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv,
-                                     int64_t S_q, int64_t max_seq, int64_t D);
+                                     int64_t S_q, int64_t max_seq, int64_t D,
+                                     int64_t D_v);
 
 /* Message of the last failed call on this thread ("" if none). The pointer stays
  * valid until the next call into the library from the same thread. */

@@ -40,12 +40,13 @@ def test_exports_every_declared_symbol(lib):
 
 def _fwd(lib, **kw):
     a = dict(out=None, q=None, k=None, v=None, bias=None, bdt=1, nonpad=None, qs=None, kind=None,
-             B=1, Hq=4, Hkv=2, S_q=1, T=64, D=64, scale=0.125, softcap=0.0, window=0, dtype=1,
+             B=1, Hq=4, Hkv=2, S_q=1, T=64, D=64, Dv=64, scale=0.125, softcap=0.0, window=0, dtype=1,
              ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib.attn_bias_gqa_fwd(a["out"], a["q"], a["k"], a["v"], a["bias"], a["bdt"],
                                  a["nonpad"], a["qs"], a["kind"], a["B"], a["Hq"], a["Hkv"],
-                                 a["S_q"], a["T"], a["D"], a["scale"], a["softcap"], a["window"], a["dtype"],
+                                 a["S_q"], a["T"], a["D"], a["Dv"], a["scale"], a["softcap"], a["window"],
+                                 a["dtype"],
                                  a["ws"], a["wsb"], a["stream"])
 
 
@@ -56,7 +57,9 @@ FAKE = 1 << 20  # a 256-byte aligned address that is never dereferenced
     (dict(B=0), INVALID, "must be positive"),
     (dict(Hq=6, Hkv=4), INVALID, "multiple of Hkv"),
     (dict(S_q=65), INVALID, "must not exceed max_seq"),
-    (dict(D=96), UNSUPPORTED, "D must be"),
+    (dict(D=96), UNSUPPORTED, "D and D_v must be"),
+    (dict(Dv=80), UNSUPPORTED, "D and D_v must be"),
+    (dict(Dv=0), INVALID, "must be positive"),
     (dict(softcap=-1.0), INVALID, "softcap"),
     (dict(softcap=float("inf")), INVALID, "softcap"),
     (dict(softcap=float("nan")), INVALID, "softcap"),
@@ -86,12 +89,17 @@ def test_scatter_and_bias_validation(lib):
 
 
 def test_workspace_size(lib):
-    assert lib.attn_bias_gqa_workspace_bytes(8, 16, 8, 1, 4096, 256) > 0
+    r256 = lib.attn_bias_gqa_workspace_bytes(8, 16, 8, 1, 4096, 256, 256)
+    assert r256 > 0
+    # decode partial records hold the V head size
+    assert lib.attn_bias_gqa_workspace_bytes(8, 16, 8, 1, 4096, 256, 512) > r256
+    assert lib.attn_bias_gqa_workspace_bytes(8, 16, 8, 1, 4096, 64, 512) == 0   # vector path
     # prefill (D 256, G 2: 64-row workgroups of 32 tokens): one bit per batch
     # row x 16 query tiles x 128 key tiles
-    assert lib.attn_bias_gqa_workspace_bytes(2, 16, 8, 512, 4096, 256) == 2 * 16 * 4 * 4
-    assert lib.attn_bias_gqa_workspace_bytes(2, 8, 8, 512, 4096, 256) == 0    # G = 1: no map
-    assert lib.attn_bias_gqa_workspace_bytes(1, 6, 4, 1, 64, 64) == 0         # invalid heads
+    assert lib.attn_bias_gqa_workspace_bytes(2, 16, 8, 512, 4096, 256, 256) == 2 * 16 * 4 * 4
+    assert lib.attn_bias_gqa_workspace_bytes(2, 16, 8, 512, 4096, 256, 512) == 0   # vector path
+    assert lib.attn_bias_gqa_workspace_bytes(2, 8, 8, 512, 4096, 256, 256) == 0    # G = 1: no map
+    assert lib.attn_bias_gqa_workspace_bytes(1, 6, 4, 1, 64, 64, 64) == 0         # invalid heads
 
 
 def test_fused_prepare_validation(lib):

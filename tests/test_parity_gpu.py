@@ -278,6 +278,43 @@ def test_decode_uneven_rows(D, Hq, Hkv, variant):
                  dead_rows(bias.float().numpy(), nonpad, Hq), f"uneven/{variant}")
 
 
+@pytest.mark.parametrize("variant", ["bias", "rules"])
+@pytest.mark.parametrize("D,Dv,S_q,dtype", [
+    (256, 512, 1, torch.bfloat16),    # decode on the matrix cores
+    (512, 256, 1, torch.bfloat16),
+    (512, 256, 2, torch.bfloat16),    # two query tokens per step
+    (64, 512, 1, torch.bfloat16),     # decode, a pair without matrix-core kernels
+    (256, 512, 40, torch.bfloat16),   # prefill chunk: vector path
+    (64, 128, 9, torch.float32),      # fp32 path
+])
+def test_value_head_size(D, Dv, S_q, dtype, variant):
+    """V with another head size than Q and K (head_size != v_head_size): the
+    scores use D, the output has V's Dv columns."""
+    rng = wl.rng_for(660 + D + Dv + S_q)
+    B, Hq, Hkv, T = 3, 8, 2, 300
+    q = wl.normal(rng, (B, Hq, S_q, D), dtype)
+    k = wl.normal(rng, (B, Hkv, T, D), dtype)
+    v = wl.normal(rng, (B, Hkv, T, Dv), dtype)
+    nonpad = torch.tensor([T, 77, 150], dtype=torch.int64)
+    q_start = (nonpad - S_q).clamp(min=0)
+    kind = torch.zeros((B, T), dtype=torch.int32)
+    kind[1, :5] = -1                                   # pads
+    kind[2, 100:130] = 1                               # an image block
+    window = 64
+    bias = torch.from_numpy(oracle.bias(nonpad, q_start, kind, S_q, T, window)).to(
+        torch.float32 if dtype == torch.float32 else torch.bfloat16)
+    announce(f"value head size D={D} Dv={Dv} S_q={S_q} {dtype} {variant}")
+    scale = 1.0 / math.sqrt(D)
+    ref = oracle.attention(q, k, v, bias, nonpad, scale)
+    if variant == "bias":
+        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), scale)
+    else:
+        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale,
+                                   q_start=dev(q_start), slot_kind=dev(kind), window=window)
+    assert got.shape == (B, Hq, S_q, Dv)
+    check_parity(to_f64(got), ref, dtype, dead_rows(bias.float().numpy(), nonpad, Hq), f"Dv/{variant}")
+
+
 def test_attention_fp32_bias_dtype():
     w = SMALL["prefill_vision"]()
     step = w.steps[0]
@@ -431,7 +468,7 @@ def test_invalid_arguments_raise():
         ab.attn_bias_gqa_fwd(q, k, k, None, n, 0.1)
     q = torch.zeros((1, 4, 1, 96), dtype=torch.bfloat16, device="cuda")
     k = torch.zeros((1, 2, 64, 96), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(RuntimeError, match="D must be"):
+    with pytest.raises(RuntimeError, match="D and D_v must be"):
         ab.attn_bias_gqa_fwd(q, k, k, None, n, 0.1)
 
 
