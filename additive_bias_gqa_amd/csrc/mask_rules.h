@@ -20,17 +20,18 @@
 namespace abgqa {
 
 struct RowRule {
-  int64_t np;      // valid slots, clamped to [0, max_seq]
-  int64_t q;       // absolute query position
-  int64_t window;  // <= 0: none
-  int32_t kind_q;  // kind of the query slot (0 outside the cache)
+  int64_t np = 0;      // valid slots, clamped to [0, max_seq]
+  int64_t q = 0;       // absolute query position
+  int64_t window = 0;  // <= 0: none
+  int32_t kind_q = 0;  // kind of the query slot (0 outside the cache)
+  // The same predicate in 32-bit form (max_seq < 2^30): causal-and-window is
+  // the key interval [lo, hi], found once per row in 64-bit arithmetic (empty
+  // when hi < lo), and a block key matches blk (-1, which no valid key has,
+  // when the query slot starts no block). A default rule allows nothing.
+  int32_t np32 = 0, lo = 0, hi = -1, blk = -1;
 
-  __device__ __forceinline__ bool allowed(int64_t j, int32_t kind_j) const {
-    const bool valid = (j < np) && (kind_j >= 0);
-    const bool causal = j <= q;
-    const bool in_window = (window <= 0) || (q - j < window);
-    const bool block = (kind_q > 0) && (kind_j == kind_q);
-    return valid && ((causal && in_window) || block);
+  __device__ __forceinline__ bool allowed(int j, int32_t kind_j) const {
+    return (j < np32) & (kind_j >= 0) & (((j >= lo) & (j <= hi)) | (kind_j == blk));
   }
 };
 
@@ -48,6 +49,13 @@ __device__ __forceinline__ RowRule make_row_rule(const int64_t* nonpad, const in
   r.q = qs + s;
   r.window = window;
   r.kind_q = (slot_kind && r.q >= 0 && r.q < max_seq) ? slot_kind[b * max_seq + r.q] : 0;
+  // keys j in [0, np) with j <= q and (no window or j >= q - W + 1)
+  const int64_t lo = window > 0 ? r.q - window + 1 : 0;
+  const int64_t hi = r.q < r.np - 1 ? r.q : r.np - 1;
+  r.np32 = (int32_t)r.np;
+  r.lo = (int32_t)(lo < 0 ? 0 : (lo > max_seq ? max_seq : lo));
+  r.hi = (int32_t)(hi < -1 ? -1 : hi);
+  r.blk = r.kind_q > 0 ? r.kind_q : -1;
   return r;
 }
 

@@ -146,20 +146,24 @@ __device__ __forceinline__ int build_live_list(const AttnParams& p, int64_t b, i
       }
     }
   } else {
-    // causal + window: keys [q_first - W + 1, q_last] (q consecutive over rows)
-    if (tid == 0 && s_end > s0) {
+    // causal + window: the rows' key intervals lie in [a, z] (q is consecutive
+    // over the rows)
+    int a = 0, z = -1;
+    if (s_end > s0) {
       const RowRule r0 = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s0, p.S_q, T, p.window);
       const int64_t q_last = r0.q + (s_end - 1 - s0);
-      int64_t a = (p.window > 0) ? r0.q - p.window + 1 : 0;
-      if (a < 0) a = 0;
-      const int64_t z = q_last < (int64_t)np - 1 ? q_last : (int64_t)np - 1;
-      if (a <= z) {
-        for (int t = (int)(a / kTileKeys); t <= (int)(z / kTileKeys); ++t)
-          s_bits[t >> 5] |= 1u << (t & 31);
-      }
+      int64_t a64 = (p.window > 0) ? r0.q - p.window + 1 : 0;
+      if (a64 < 0) a64 = 0;
+      const int64_t z64 = q_last < (int64_t)np - 1 ? q_last : (int64_t)np - 1;
+      a = (int)(a64 < T ? a64 : T);
+      z = (int)(z64 < -1 ? -1 : z64);
     }
-    // image blocks of the rows (up to 4 distinct ids; more: every tile is live)
-    if (p.slot_kind) {
+    if (!p.slot_kind) {
+      // every slot is text: the interval alone
+      if (a <= z)
+        for (int t = a / kTileKeys + tid; t <= z / kTileKeys; t += NT) atomicOr(&s_bits[t >> 5], 1u << (t & 31));
+    } else {
+      // the rows' image-block kinds (up to 4 distinct; more: any block key counts)
       for (int s = s0 + tid; s < s_end; s += NT) {
         const RowRule rr = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s, p.S_q, T, p.window);
         if (rr.kind_q > 0) {
@@ -171,18 +175,36 @@ __device__ __forceinline__ int build_live_list(const AttnParams& p, int64_t b, i
           }
         }
       }
-    }
-    __syncthreads();
-    const int nids = s_nids;
-    if (nids > 4) {
-      for (int t = tid; t < n_kt; t += NT) atomicOr(&s_bits[t >> 5], 1u << (t & 31));
-    } else if (nids > 0) {
+      __syncthreads();
+      const int nids = s_nids;
+      // a tile is live if it holds a key that is no pad inside [a, z], or a
+      // key of one of the rows' blocks (a superset of the tiles some row
+      // allows a key of; pad-only tiles drop out). Lanes 0-31 and 32-63 of a
+      // wavefront read one tile each (NT is a multiple of 64), NB kinds per
+      // thread in flight.
       const int32_t* kr = p.slot_kind + b * T;
-      for (int j = tid; j < np; j += NT) {
-        const int32_t kj = kr[j];
-        bool hit = false;
-        for (int i = 0; i < nids; ++i) hit |= (kj == s_ids[i]);
-        if (hit) atomicOr(&s_bits[(j / kTileKeys) >> 5], 1u << ((j / kTileKeys) & 31));
+      constexpr int NB = 8;
+      for (int base0 = w * 64; base0 < np; base0 += NB * NT) {   // uniform over the wavefront
+        const int base = base0 + lane;
+        int32_t kv[NB];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) kv[u] = kr[min(base + u * NT, np - 1)];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const int j = base + u * NT;
+          bool hit = (kv[u] >= 0) && (j >= a) && (j <= z);
+          if (nids > 4) {
+            hit |= kv[u] > 0;
+          } else {
+            for (int i = 0; i < nids; ++i) hit |= (kv[u] == s_ids[i]);
+          }
+          const uint64_t m = __ballot(hit && j < np);
+          if (lane == 0 && m != 0) {
+            const int t0 = (j - lane) / kTileKeys;   // the tile of lane 0
+            if (m & 0xffffffffull) atomicOr(&s_bits[t0 >> 5], 1u << (t0 & 31));
+            if (m >> 32) atomicOr(&s_bits[(t0 + 1) >> 5], 1u << ((t0 + 1) & 31));
+          }
+        }
       }
     }
   }

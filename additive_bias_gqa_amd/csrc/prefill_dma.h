@@ -282,6 +282,9 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   if constexpr (kRules) {
     if (row_ok) rule = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s, p.S_q, T, p.window);
   }
+  // the row's causal/window key interval for the whole-tile test of the rules
+  // variant; a row past the chunk passes it (its output is never stored)
+  const int rule_lo = row_ok ? rule.lo : INT_MIN, rule_hi = row_ok ? rule.hi : INT_MAX;
 
   // ---- 2. live tiles ---------------------------------------------------------
   // read from LDS, the count is the same in every lane: say so, so that the
@@ -328,6 +331,10 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   const __bf16* kg = (const __bf16*)p.k + (b * p.Hkv + hk) * (int64_t)T * D;
   const __bf16* vg = (const __bf16*)p.v + (b * p.Hkv + hk) * (int64_t)T * D;
   const int32_t* kindb = p.slot_kind ? p.slot_kind + b * T : nullptr;
+  // rules variant: the kind stage is read unconditionally (it holds K bytes
+  // when there are no slot kinds) and masked to kind 0 then, so no branch
+  // separates these reads from the K reads they are scheduled with
+  const int32_t kind_mask = kindb ? -1 : 0;
   const BiasT* biasb = kRules ? nullptr : (const BiasT*)p.bias + b * p.S_q * (int64_t)T;
 
   // ---- 3. one stage's fetches ----------------------------------------------
@@ -529,22 +536,8 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
     const unsigned KO = (unsigned)(KS * ss * TILE_BYTES);
 
     if constexpr (RW == 32) {
-      // this lane's bias values (or slot kinds) for keys 8*i + 4*(l/32) + jj,
-      // read first so their latency hides under the S^T MFMAs
       BiasT bvs[4][4];
       int32_t kvs[4][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kb = 8 * i + 4 * grp;
-        if constexpr (kRules) {
-          if (kindb) *reinterpret_cast<int4*>(kvs[i]) = *reinterpret_cast<const int4*>(ms + 4 * kb);
-          else *reinterpret_cast<int4*>(kvs[i]) = int4{0, 0, 0, 0};
-        } else {
-          const BiasT* br = reinterpret_cast<const BiasT*>(ms) + sl * kTileKeys + kb;
-          if constexpr (sizeof(BiasT) == 2) *reinterpret_cast<u32x2*>(bvs[i]) = *reinterpret_cast<const u32x2*>(br);
-          else *reinterpret_cast<u32x4*>(bvs[i]) = *reinterpret_cast<const u32x4*>(br);
-        }
-      }
       // S^T = K Q^T; lane l: query row l % 32, keys 8*i + 4*(l/32) + jj
       // fragments of k-step i + PD are read while the MFMA of step i runs. With
       // one wavefront per SIMD the LDS round trip, not the matrix core, sets the
@@ -572,6 +565,21 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
         if constexpr (kQLds) qa[i] = lds_at<bf16x8>(q_base[i % NKG], SPAN * (i / NKG));
       }
       __builtin_amdgcn_sched_group_barrier(0x100, NQR * PD, 0);
+      // this lane's bias values (or slot kinds) for keys 8*i + 4*(l/32) + jj,
+      // read behind the first K fragments (ahead of them they would take
+      // places of the read-ahead) so their latency hides under the MFMAs
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kb = 8 * i + 4 * grp;
+        if constexpr (kRules) {
+          const int4 kk = *reinterpret_cast<const int4*>(ms + 4 * kb);
+          *reinterpret_cast<int4*>(kvs[i]) = int4{kk.x & kind_mask, kk.y & kind_mask, kk.z & kind_mask, kk.w & kind_mask};
+        } else {
+          const BiasT* br = reinterpret_cast<const BiasT*>(ms) + sl * kTileKeys + kb;
+          if constexpr (sizeof(BiasT) == 2) *reinterpret_cast<u32x2*>(bvs[i]) = *reinterpret_cast<const u32x2*>(br);
+          else *reinterpret_cast<u32x4*>(bvs[i]) = *reinterpret_cast<const u32x4*>(br);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < KSTEPS; ++i) {
         const bf16x8 a = ka[i % PD];
@@ -622,23 +630,42 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
       }
       float x[16];
       float mt = -INFINITY;
+      if constexpr (kRules) {
+        // the common case: the tile lies inside every row's causal/window
+        // interval (so below nonpad) and holds no pad slot (the OR of the kinds
+        // is not negative), so every key is allowed, block or not, and no score
+        // needs the per-element rule (a real branch; both sides give an
+        // allowed score the same bits)
+        int kor = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kb = 8 * i + 4 * grp;          // first of this lane's 4 keys
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int j = j0 + kb + jj;
-          float v;
-          if constexpr (kRules) {
-            // allowed() includes j < nonpad; a row past the chunk has no rule
-            v = rule.allowed(j, kvs[i][jj]) ? sacc[4 * i + jj] * sl : -INFINITY;
-          } else {
+          for (int jj = 0; jj < 4; ++jj) kor |= kvs[i][jj];
+        const bool inside = j0 >= rule_lo && j0 + kTileKeys - 1 <= rule_hi;
+        if (!__any(kor < 0 || !inside)) {
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int e = 0; e < 16; ++e) x[e] = sacc[e] * sl;
+        } else {
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              // allowed() includes j < nonpad; a row past the chunk has no rule
+              const int j = j0 + 8 * i + 4 * grp + jj;
+              x[4 * i + jj] = rule.allowed(j, kvs[i][jj]) ? sacc[4 * i + jj] * sl : -INFINITY;
+            }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
             // a -inf bias gives -inf (the score is finite: every fetched key row
             // is a valid row); keys at or past nonpad only in a partial tile
-            v = fmaf(sacc[4 * i + jj], sl, bias_f32<BiasT>(bvs[i][jj]) * kLog2e);
+            x[4 * i + jj] = fmaf(sacc[4 * i + jj], sl, bias_f32<BiasT>(bvs[i][jj]) * kLog2e);
           }
-          x[4 * i + jj] = v;
-        }
       }
       if constexpr (!kRules) {
         if (!full) {
@@ -727,8 +754,8 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
       for (int kb = 0; kb < 2; ++kb) {
         const int kf = 16 * kb + 4 * grp;
         if constexpr (kRules) {
-          if (kindb) *reinterpret_cast<int4*>(kvs[kb]) = *reinterpret_cast<const int4*>(ms + 4 * kf);
-          else *reinterpret_cast<int4*>(kvs[kb]) = int4{0, 0, 0, 0};
+          const int4 kk = *reinterpret_cast<const int4*>(ms + 4 * kf);
+          *reinterpret_cast<int4*>(kvs[kb]) = int4{kk.x & kind_mask, kk.y & kind_mask, kk.z & kind_mask, kk.w & kind_mask};
         } else {
           const BiasT* br = reinterpret_cast<const BiasT*>(ms) + sl * kTileKeys + kf;
           if constexpr (sizeof(BiasT) == 2) *reinterpret_cast<u32x2*>(bvs[kb]) = *reinterpret_cast<const u32x2*>(br);
@@ -785,20 +812,33 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
       }
       float x[8];
       float mt = -INFINITY;
+      if constexpr (kRules) {
+        // the whole-tile test of the 32-row branch
+        int kor = 0;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int kf = 16 * kb + 4 * grp;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = j0 + kf + e;
-          float v;
-          if constexpr (kRules) {
-            v = rule.allowed(j, kvs[kb][e]) ? sacc[kb][e] * sl : -INFINITY;
-          } else {
-            v = fmaf(sacc[kb][e], sl, bias_f32<BiasT>(bvs[kb][e]) * kLog2e);
-          }
-          x[4 * kb + e] = v;
+          for (int e = 0; e < 4; ++e) kor |= kvs[kb][e];
+        const bool inside = j0 >= rule_lo && j0 + kTileKeys - 1 <= rule_hi;
+        if (!__any(kor < 0 || !inside)) {
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[4 * kb + e] = sacc[kb][e] * sl;
+        } else {
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              x[4 * kb + e] = rule.allowed(j0 + 16 * kb + 4 * grp + e, kvs[kb][e]) ? sacc[kb][e] * sl : -INFINITY;
         }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * kb + e] = fmaf(sacc[kb][e], sl, bias_f32<BiasT>(bvs[kb][e]) * kLog2e);
       }
       if constexpr (!kRules) {
         if (!full) {
