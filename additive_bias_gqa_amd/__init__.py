@@ -189,13 +189,15 @@ _workspaces: dict = {}
 
 def _workspace(device: torch.device, nbytes: int) -> torch.Tensor | None:
     """A per-device workspace, grown on demand (calls on one device's current
-    stream are ordered, so they can share it)."""
+    stream are ordered, so they can share it). Zero-filled when allocated: its
+    first bytes are the decode kernel's arrival counts, which every call
+    leaves at zero."""
     if nbytes == 0:
         return None
     key = (device.type, device.index)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 

@@ -144,9 +144,11 @@ size_t attn_bias_gqa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_q <= 0 || max_seq <= 0 || D <= 0 || D_v <= 0 || Hq % Hkv)
     return 0;
   const int64_t G = Hq / Hkv;
-  if (S_q * G > 16)
-    return D == D_v ? abgqa::prefill_workspace_bytes(B, Hq, Hkv, S_q, max_seq, D) : 0;
-  if (!abgqa::decode_supports((int)D, (int)D_v)) return 0;
+  if (S_q * G > 16) {
+    const size_t map = D == D_v ? abgqa::prefill_workspace_bytes(B, Hq, Hkv, S_q, max_seq, D) : 0;
+    return map ? abgqa::kWsCounterBytes + map : 0;
+  }
+  if (!abgqa::decode_supports((int)D, (int)D_v) || B * Hkv > abgqa::kMaxDecodeRows) return 0;
   return abgqa::decode_workspace_bytes(B, Hkv, S_q, G, D_v, max_seq);
 }
 
@@ -197,8 +199,10 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
   if (dtype == ABGQA_F32) {
     path = "f32";
     e = abgqa::launch_attn_f32(p, st);
-  } else if ((S_q * G <= 16 && !abgqa::decode_supports((int)D, (int)D_v)) || (S_q * G > 16 && D != D_v)) {
-    // head sizes the matrix-core kernels are not built for: the vector path
+  } else if ((S_q * G <= 16 && (!abgqa::decode_supports((int)D, (int)D_v) || B * Hkv > abgqa::kMaxDecodeRows)) ||
+             (S_q * G > 16 && D != D_v)) {
+    // head sizes the matrix-core kernels are not built for, or more (b, kv
+    // head) pairs than the decode arrival counts cover: the vector path
     path = "vector";
     e = abgqa::launch_attn_vec_bf16(p, st);
   } else if (S_q * G <= 16) {
@@ -209,7 +213,8 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
                   need, workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 16)) return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: workspace not 16-byte aligned");
     p.n_split = abgqa::decode_num_splits(B, Hkv, max_seq);
-    p.ws_part = (float*)workspace;
+    p.arrive = (int*)workspace;
+    p.ws_part = (float*)((char*)workspace + abgqa::kWsCounterBytes);
     e = abgqa::launch_attn_decode(p, st);
   } else {
     path = "prefill";
@@ -219,9 +224,11 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
     if (workspace && !aligned(workspace, 16))
       return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: workspace not 16-byte aligned");
     // optional here: with less than attn_bias_gqa_workspace_bytes() the
-    // kernel finds its live tiles from the bias itself
-    p.ws = workspace;
-    p.ws_bytes = workspace ? workspace_bytes : 0;
+    // kernel finds its live tiles from the bias itself. The decode arrival
+    // counts at the start of the workspace are left alone.
+    const bool have = workspace && workspace_bytes > abgqa::kWsCounterBytes;
+    p.ws = have ? (void*)((char*)workspace + abgqa::kWsCounterBytes) : nullptr;
+    p.ws_bytes = have ? workspace_bytes - abgqa::kWsCounterBytes : 0;
     e = abgqa::launch_attn_prefill(p, st);
   }
   if (log_enabled())

@@ -29,12 +29,14 @@
 //             The softmax weights cross layouts through a small LDS buffer.
 //   merge     the wavefronts merge in LDS in a fixed order (bit-
 //             reproducible); each workgroup writes its (m, l, O) partial to
-//             the workspace; a second small kernel combines the partials of
-//             each (b, kv head, row):
+//             the workspace and counts its arrival; the last of a row's
+//             splits to arrive merges the row's partials:
 //             m = max m_i, y = sum 2^(m_i - m) O_i / sum 2^(m_i - m) l_i.
-//             (A last-arriving-workgroup combine inside the split kernel
-//             would need device-scope fences, which on this multi-XCD part
-//             write back and invalidate the L2 once per workgroup.)
+//             The partials travel through agent-scope stores and loads,
+//             which are coherent across the XCDs by themselves: no fence that
+//             writes back or invalidates an L2 cache is needed (such fences,
+//             once per workgroup, made an earlier form of this merge five
+//             times slower than a separate combine kernel).
 //
 // Softmax runs in base 2 on x * log2(e). The running maximum is only raised
 // when a new score exceeds it by more than 8 (a factor 256), so rescaling the
@@ -103,14 +105,38 @@ constexpr int kMaxBalanceRows = 256;
 // keys between the samples that estimate a row's live length
 constexpr int kSampleStride = 256;
 
-// workspace: one partial record per (kv head, rank), rank < B * n_split, then
-// per (kv head, b) the first rank and the number of splits of that row
+// workspace: the arrival counts, then one partial record per (kv head, rank),
+// rank < B * n_split
 size_t decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_q, int64_t G, int64_t Dv,
                               int64_t max_seq) {
   const int64_t NR = round_up_rows(S_q * G);
   const int64_t n_split = decode_num_splits(B, Hkv, max_seq);
-  return (size_t)B * Hkv * n_split * part_floats(NR, Dv) * sizeof(float) +
-         (size_t)B * Hkv * 2 * sizeof(int);
+  return kWsCounterBytes + (size_t)B * Hkv * n_split * part_floats(NR, Dv) * sizeof(float);
+}
+
+// Agent-scope (whole-GPU) stores and loads: they complete at, and read from,
+// the level every XCD shares, so a record written by a workgroup on one XCD is
+// read back exactly by a workgroup on another, without writing back or
+// invalidating any L2 cache.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes at once (sc1: agent scope). There is no 16-byte scoped-store
+// builtin, so this is asm, which the compiler does not count among the
+// outstanding stores: the explicit s_waitcnt vmcnt(0) that follows the record
+// stores waits for them.
+__device__ __forceinline__ void st_agent4(float* p, f32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" :: "v"(p), "v"(v) : "memory");
+}
+// two floats in one agent-scope 8-byte load
+__device__ __forceinline__ void ld_agent2(const float* p, float& x, float& y) {
+  const uint64_t u = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  x = __uint_as_float((uint32_t)u);
+  y = __uint_as_float((uint32_t)(u >> 32));
 }
 
 // D: head size of Q and K; DV: of V and the output (they may differ)
@@ -334,12 +360,6 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
     }
   }
   const int np = (int)clamp_nonpad(p.nonpad[b], T);
-  // where the combine finds this row's partial records
-  if (split == 0 && tid == 0) {
-    int* tab = reinterpret_cast<int*>(p.ws_part + (int64_t)p.Hkv * S * PART);
-    tab[2 * (hk * p.B + b)] = first;
-    tab[2 * (hk * p.B + b) + 1] = nsp;
-  }
 
   // ---- 1c. this row's live range [live_lo, live_hi) ---------------------------
   if constexpr (kRules) {
@@ -662,7 +682,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
 #pragma unroll
       for (int ww = 1; ww < kDecWaves; ++ww)
         acc += reinterpret_cast<const f32x4*>(s_o + ww * NR * DV)[i];
-      reinterpret_cast<f32x4*>(part)[i] = acc;
+      st_agent4(part + 4 * i, acc);
     }
   } else {
 #pragma unroll
@@ -679,7 +699,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
       __syncthreads();
     }
     for (int i = tid; i < NR * DV / 4; i += kDecThreads)
-      reinterpret_cast<f32x4*>(part)[i] = reinterpret_cast<const f32x4*>(s_o)[i];
+      st_agent4(part + 4 * i, reinterpret_cast<const f32x4*>(s_o)[i]);
   }
   if (tid < NR) {
     const int r = tid;
@@ -689,85 +709,66 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
       const float f = (m_wg[r] == -INFINITY) ? 0.f : fast_exp2(s_m[ww][r] - m_wg[r]);
       lsum += s_l[ww][r] * f;
     }
-    part[NR * DV + r] = m_wg[r];
-    part[NR * DV + NR + r] = lsum;
+    st_agent(part + NR * DV + r, m_wg[r]);
+    st_agent(part + NR * DV + NR + r, lsum);
   }
-}
 
-// Merge the partials of one (b, kv head, row) - the row's splits, found
-// through the table the split kernel writes:
-//   m = max m_i,  y = sum 2^(m_i - m) O_i / sum 2^(m_i - m) l_i
-// (a split that saw no live key has m_i = -inf and drops out; no live key at
-// all gives y = 0). One workgroup of 64 threads per (b, kv head, row), each
-// thread 8 consecutive values of d.
-// D here: the head size of V and the output
-template <int D, int NR>
-__global__ __launch_bounds__(64) void attn_decode_combine_kernel(AttnParams p) {
-  constexpr int PART = (int)part_floats(NR, D);
-  const int R = p.S_q * p.G;
-  const int r = blockIdx.x % R;
-  const int bh = blockIdx.x / R;
-  const int hk = bh % p.Hkv;
-  const int64_t b = bh / p.Hkv;
-  const int d0 = threadIdx.x * 8;
-  if (d0 >= D) return;
-  const int S = p.B * p.n_split;
-  const int* tab = reinterpret_cast<const int*>(p.ws_part + (int64_t)p.Hkv * S * PART);
-  // one pass, rescaled on the fly (running max): a split that saw no live key
-  // (m = -inf, l = 0, O = 0) gets weight 0, and nothing done so far is
-  // rescaled by its -inf
-  float mm = -INFINITY, den = 0.f;
-  float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  auto merge = [&](float ms, float ls, const f32x4& a0, const f32x4& a1) {
-    const float mn = fmaxf(mm, ms);
-    const float fo = (mm == -INFINITY) ? 0.f : fast_exp2(mm - mn);
-    const float fs = (ms == -INFINITY) ? 0.f : fast_exp2(ms - mn);
-    den = den * fo + ls * fs;
+  // ---- 6. the row's last split merges the row's records ---------------------
+  // Each wavefront waits until its record stores are complete, then the
+  // workgroup counts one arrival for its (kv head, b). The workgroup that finds
+  // nsp - 1 arrivals before its own merges the nsp records in split order (the
+  // same arithmetic, hence the same bits, whichever workgroup it is) and sets
+  // the count back to zero for the next call:
+  //   m = max m_i,  y = sum 2^(m_i - m) O_i / sum 2^(m_i - m) l_i
+  // (a split that saw no live key has m_i = -inf and drops out; no live key at
+  // all gives y = 0).
+  __shared__ int s_arrived;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int* const cnt = p.arrive + hk * p.B + b;
+  if (tid == 0) s_arrived = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_arrived != nsp - 1) return;
+  if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float* parts = p.ws_part + ((int64_t)hk * S + first) * PART;
+  constexpr int NQ = DV / 4;   // 4-float chunks of a row
+  for (int it = tid; it < R * NQ; it += kDecThreads) {
+    const int r = it / NQ, d0 = (it - r * NQ) * 4;
+    // one pass, rescaled on the fly (running max); the records of 4 splits
+    // are loaded together
+    float mm = -INFINITY, den = 0.f;
+    float num[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = 0; sp0 < nsp; sp0 += 4) {
+      float pm[4], pl[4], pa[4][4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      num[c] = num[c] * fo + a0[c] * fs;
-      num[4 + c] = num[4 + c] * fo + a1[c] * fs;
+      for (int u = 0; u < 4; ++u) {
+        const float* ps = parts + (int64_t)min(sp0 + u, nsp - 1) * PART;
+        pm[u] = ld_agent(ps + NR * DV + r);
+        pl[u] = ld_agent(ps + NR * DV + NR + r);
+        ld_agent2(ps + r * DV + d0, pa[u][0], pa[u][1]);
+        ld_agent2(ps + r * DV + d0 + 2, pa[u][2], pa[u][3]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (sp0 + u < nsp) {
+          const float mn = fmaxf(mm, pm[u]);
+          const float fo = (mm == -INFINITY) ? 0.f : fast_exp2(mm - mn);
+          const float fs = (pm[u] == -INFINITY) ? 0.f : fast_exp2(pm[u] - mn);
+          den = den * fo + pl[u] * fs;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) num[c] = num[c] * fo + pa[u][c] * fs;
+          mm = mn;
+        }
+      }
     }
-    mm = mn;
-  };
-  // The records of the equal split (rank b * n_split + i) are loaded together
-  // with the row's table entry, so the common case costs one memory round
-  // trip; rows the split kernel balanced otherwise load theirs afterwards.
-  constexpr int PRE = 4;
-  const int first_eq = (int)b * p.n_split;
-  float pm[PRE], pl[PRE];
-  f32x4 pa0[PRE], pa1[PRE];
-#pragma unroll
-  for (int i = 0; i < PRE; ++i) {
-    const float* ps = p.ws_part + ((int64_t)hk * S + first_eq + min(i, p.n_split - 1)) * PART;
-    pm[i] = ps[NR * D + r];
-    pl[i] = ps[NR * D + NR + r];
-    pa0[i] = *reinterpret_cast<const f32x4*>(ps + r * D + d0);
-    pa1[i] = *reinterpret_cast<const f32x4*>(ps + r * D + d0 + 4);
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    const int s = r / G, g = r % G;
+    uint16_t* op = (uint16_t*)p.out + (((b * p.Hq + hk * G + g) * p.S_q + s) * (int64_t)DV) + d0;
+    u32x2 pk;
+    pk.x = pack_bf16x2(num[0] * inv, num[1] * inv);
+    pk.y = pack_bf16x2(num[2] * inv, num[3] * inv);
+    *reinterpret_cast<u32x2*>(op) = pk;
   }
-  const int first = tab[2 * (hk * p.B + b)], n_parts = tab[2 * (hk * p.B + b) + 1];
-  if (first == first_eq && n_parts == p.n_split && n_parts <= PRE) {
-#pragma unroll
-    for (int i = 0; i < PRE; ++i)
-      if (i < n_parts) merge(pm[i], pl[i], pa0[i], pa1[i]);
-  } else {
-    const float* parts = p.ws_part + ((int64_t)hk * S + first) * PART;
-#pragma unroll 4
-    for (int sp = 0; sp < n_parts; ++sp) {
-      const float* ps = parts + sp * PART;
-      merge(ps[NR * D + r], ps[NR * D + NR + r], *reinterpret_cast<const f32x4*>(ps + r * D + d0),
-            *reinterpret_cast<const f32x4*>(ps + r * D + d0 + 4));
-    }
-  }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  const int s = r / p.G, g = r % p.G;
-  uint16_t* op = (uint16_t*)p.out + (((b * p.Hq + hk * p.G + g) * p.S_q + s) * (int64_t)D) + d0;
-  u32x4 pk;
-  pk.x = pack_bf16x2(num[0] * inv, num[1] * inv);
-  pk.y = pack_bf16x2(num[2] * inv, num[3] * inv);
-  pk.z = pack_bf16x2(num[4] * inv, num[5] * inv);
-  pk.w = pack_bf16x2(num[6] * inv, num[7] * inv);
-  *reinterpret_cast<u32x4*>(op) = pk;
 }
 
 // Wavefronts per split workgroup. D = 512 takes 8 (two per SIMD, one block
@@ -804,17 +805,8 @@ static hipError_t launch_decode_d(const AttnParams& p, hipStream_t stream) {
   } else {
     launch_decode_nw<D, DV, NR, 4>(p, stream);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    set_launch_detail("decode kernel launch");
-    return e;
-  }
-  // the combine reads the partials after the split kernel completes (stream
-  // order), so no device-scope fence is needed inside the split kernel
-  const dim3 cgrid((unsigned)((int64_t)p.B * p.Hkv * p.S_q * p.G));
-  hipLaunchKernelGGL((attn_decode_combine_kernel<DV, NR>), cgrid, dim3(64), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) set_launch_detail("decode combine launch");
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) set_launch_detail("decode kernel launch");
   return e;
 }
 

@@ -33,6 +33,13 @@ hipError_t launch_prepare(void* k_cache, void* v_cache, const void* k_update, co
                           int64_t S_q, int64_t window, hipStream_t stream);
 
 // Everything an attention kernel reads, passed by value.
+// The first bytes of every attention workspace: the decode kernel's arrival
+// counts, one int per (kv head, batch row). They must be zero before the first
+// call that uses the workspace; every call leaves them zero. The rest of the
+// workspace (decode partial records, prefill live-tile map) follows.
+constexpr size_t kWsCounterBytes = 64 * 1024;
+constexpr int64_t kMaxDecodeRows = (int64_t)(kWsCounterBytes / sizeof(int));
+
 struct AttnParams {
   void* out;                 // [B, Hq, S_q, Dv]
   const void* q;             // [B, Hq, S_q, D]
@@ -50,6 +57,7 @@ struct AttnParams {
   int bias_is_bf16;          // bias dtype when bias != null
   // split-KV decode
   float* ws_part;            // partial results, one record per (b, kv head, split)
+  int* arrive;               // split arrivals per (kv head, b): zero between calls
   int n_split;
   // prefill: caller scratch (may be null); the direct-to-LDS path keeps its
   // live-tile map there when it is large enough

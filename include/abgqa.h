@@ -185,12 +185,19 @@ abgqa_status kv_scatter_and_bias(void *k_cache, void *v_cache, const void *k_upd
  *                    bf16 for the matrix-core PV product in prefill) or
  *                    ABGQA_F32 (fp32 throughout)
  *   workspace        device scratch of at least attn_bias_gqa_workspace_bytes()
- *                    bytes for the same shape, 16-byte aligned, no initial
- *                    contents needed. Decode (S_q * Hq / Hkv <= 16) keeps one
- *                    partial softmax result per split workgroup there, and
- *                    per (batch row, kv head) where its splits' results are,
- *                    and requires it.
- *                    Prefill with a bias tensor keeps a live-tile map there
+ *                    bytes for the same shape, 16-byte aligned. Its first
+ *                    64 KiB are the decode kernel's arrival counts (one int32
+ *                    per kv head and batch row): ZERO-FILL THEM ONCE when the
+ *                    workspace is allocated; every call leaves them zero (a
+ *                    prefill call never touches them, so one workspace can
+ *                    serve both). Decode (S_q * Hq / Hkv <= 16) keeps one
+ *                    partial softmax result per split workgroup after them,
+ *                    and requires the workspace; the last of a row's splits
+ *                    to finish merges that row's results (decode with more
+ *                    than 16384 kv-head-and-batch-row pairs takes the vector
+ *                    kernel instead and needs none).
+ *                    Prefill with a bias tensor keeps a live-tile map after
+ *                    the counts
  *                    (one bit per batch row, query tile and 32-key tile,
  *                    built by a pass over the bias before the attention
  *                    kernel); for prefill it is optional: with a smaller or

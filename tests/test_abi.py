@@ -89,17 +89,22 @@ def test_scatter_and_bias_validation(lib):
 
 
 def test_workspace_size(lib):
+    CNT = 64 * 1024   # decode arrival counts at the start of every workspace
     r256 = lib.attn_bias_gqa_workspace_bytes(8, 16, 8, 1, 4096, 256, 256)
-    assert r256 > 0
+    # 64 (b, kv head) pairs x 4 splits, records of 2 rows x 256 + m, l (16-byte padded)
+    assert r256 == CNT + 8 * 8 * 4 * ((2 * 256 + 4 + 3) // 4 * 4) * 4
     # decode partial records hold the V head size
     assert lib.attn_bias_gqa_workspace_bytes(8, 16, 8, 1, 4096, 256, 512) > r256
     assert lib.attn_bias_gqa_workspace_bytes(8, 16, 8, 1, 4096, 64, 512) == 0   # vector path
     # prefill (D 256, G 2: 64-row workgroups of 32 tokens): one bit per batch
     # row x 16 query tiles x 128 key tiles
-    assert lib.attn_bias_gqa_workspace_bytes(2, 16, 8, 512, 4096, 256, 256) == 2 * 16 * 4 * 4
+    assert lib.attn_bias_gqa_workspace_bytes(2, 16, 8, 512, 4096, 256, 256) == CNT + 2 * 16 * 4 * 4
     assert lib.attn_bias_gqa_workspace_bytes(2, 16, 8, 512, 4096, 256, 512) == 0   # vector path
     assert lib.attn_bias_gqa_workspace_bytes(2, 8, 8, 512, 4096, 256, 256) == 0    # G = 1: no map
     assert lib.attn_bias_gqa_workspace_bytes(1, 6, 4, 1, 64, 64, 64) == 0         # invalid heads
+    # more (b, kv head) pairs than the counts cover: the vector path, no workspace
+    assert lib.attn_bias_gqa_workspace_bytes(2049, 16, 8, 1, 64, 64, 64) == 0
+    assert lib.attn_bias_gqa_workspace_bytes(2048, 16, 8, 1, 64, 64, 64) > CNT
 
 
 def test_fused_prepare_validation(lib):

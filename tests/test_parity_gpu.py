@@ -278,6 +278,55 @@ def test_decode_uneven_rows(D, Hq, Hkv, variant):
                  dead_rows(bias.float().numpy(), nonpad, Hq), f"uneven/{variant}")
 
 
+def test_shared_workspace_counts():
+    """One zero-filled workspace serves decode calls of two shapes and a
+    prefill call with a live-tile map in between: every decode result matches
+    the oracle, and the decode arrival counts (the first 64 KiB) are zero
+    again after every call, ready for the next."""
+    rng = wl.rng_for(700)
+    ws = torch.zeros(4 << 20, dtype=torch.uint8, device="cuda")
+
+    def decode(B, Hq, Hkv, T, D, seed):
+        r = wl.rng_for(seed)
+        q = wl.normal(r, (B, Hq, 1, D), torch.bfloat16)
+        k = wl.normal(r, (B, Hkv, T, D), torch.bfloat16)
+        v = wl.normal(r, (B, Hkv, T, D), torch.bfloat16)
+        nonpad = torch.from_numpy(r.integers(1, T, size=B, endpoint=True).astype(np.int64))
+        q_start = nonpad - 1
+        bias = torch.from_numpy(oracle.bias(nonpad, q_start, None, 1, T, 128)).to(torch.bfloat16)
+        assert ab.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, 1, T, D) <= ws.numel()
+        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 1.0 / math.sqrt(D),
+                                   workspace=ws)
+        ref = oracle.attention(q, k, v, bias, nonpad, 1.0 / math.sqrt(D))
+        check_parity(to_f64(got), ref, torch.bfloat16, dead_rows(bias.float().numpy(), nonpad, Hq),
+                     f"shared ws decode B={B} Hkv={Hkv} D={D}")
+
+    def counts_zero():
+        torch.cuda.synchronize()
+        assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
+
+    announce("shared workspace: decode, prefill with map, decode")
+    for rep in range(3):
+        decode(8, 16, 8, 700, 256, 701 + rep)
+        counts_zero()
+    # prefill with a live-tile map in the same workspace
+    B, Hq, Hkv, S_q, T, D = 2, 8, 2, 96, 320, 128
+    q = wl.normal(rng, (B, Hq, S_q, D), torch.bfloat16)
+    k = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    v = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    nonpad = torch.tensor([T, 200], dtype=torch.int64)
+    q_start = (nonpad - S_q).clamp(min=0)
+    bias = torch.from_numpy(oracle.bias(nonpad, q_start, None, S_q, T, 64)).to(torch.bfloat16)
+    assert ab.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, T, D) > 65536
+    got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 1.0 / math.sqrt(D), workspace=ws)
+    ref = oracle.attention(q, k, v, bias, nonpad, 1.0 / math.sqrt(D))
+    check_parity(to_f64(got), ref, torch.bfloat16, dead_rows(bias.float().numpy(), nonpad, Hq), "shared ws prefill")
+    counts_zero()
+    for rep in range(2):
+        decode(5, 8, 2, 1000, 512, 711 + rep)
+        counts_zero()
+
+
 @pytest.mark.parametrize("variant", ["bias", "rules"])
 @pytest.mark.parametrize("D,Dv,S_q,dtype", [
     (256, 512, 1, torch.bfloat16),    # decode on the matrix cores
@@ -400,7 +449,7 @@ def test_maskless_static_cache(B, Hq, Hkv, D, T, S_q, causal):
     qs = None if causal else torch.full((B,), T, dtype=torch.int64)
     scale = 1.0 / math.sqrt(D)
     ws_bytes = ab.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, T, D)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
     out = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale, q_start=dev(qs),
                                slot_kind=None, window=0, workspace=ws)
     bias = oracle.bias(nonpad, qs, None, S_q, T, 0)
