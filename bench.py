@@ -278,10 +278,16 @@ def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
 KERNEL_SOURCES_DIR = os.path.join("additive_bias_gqa_amd", "csrc")
 
 
-def kernel_sources():
-    d = os.path.join(HERE, KERNEL_SOURCES_DIR)
-    return sorted(os.path.join(KERNEL_SOURCES_DIR, f) for f in os.listdir(d)
-                  if f.endswith((".hip", ".h")))
+def kernel_sources(name):
+    """The sources that build the attention call of a workload: the ABI
+    dispatch, the phase's kernel files and the headers they include."""
+    common = ["abi.hip", "common.h", "kernels.h", "mask_rules.h"]
+    if name.startswith("decode"):
+        files = common + ["attn_decode.hip"]
+    else:
+        files = common + ["attn_prefill_dma.hip", "attn_prefill_dma_wide.hip", "prefill_dma.h",
+                          "prefill_common.h"]
+    return sorted(os.path.join(KERNEL_SOURCES_DIR, f) for f in files)
 
 
 def sources_sha256(rels):
@@ -302,7 +308,7 @@ def traffic_for(name):
         rec = json.load(f)
     try:
         if sources_sha256(rec.get("sources", [])) != rec.get("source_sha256") or \
-                rec.get("sources") != kernel_sources():
+                rec.get("sources") != kernel_sources(name):
             return None
     except OSError:
         return None
@@ -316,8 +322,7 @@ def write_traffic(name, fetch_csv, write_csv, copy_bytes=1 << 30):
     Each counter is scaled by what it reads for the plain 1 GiB device copy
     that bench.py runs first (the largest __amd_rocclr_copyBuffer dispatch):
     scale = copy bytes / (counter KiB * 1024). The attention call is every
-    abgqa::attn_* kernel it launches (split-KV decode: the split kernel and
-    the combine kernel), averaged per dispatch and summed."""
+    abgqa::attn_* kernel it launches, averaged per dispatch and summed."""
     import csv
     import collections
 
@@ -344,7 +349,7 @@ def write_traffic(name, fetch_csv, write_csv, copy_bytes=1 << 30):
         wk = sum(write[k]) / len(write[k]) * 1024.0 * ws if k in write else 0.0
         kernels[k] = dict(dispatches=len(fetch[k]), fetch_bytes=round(fk), write_bytes=round(wk))
         total += fk + wk
-    rels = kernel_sources()
+    rels = kernel_sources(name)
     rec = dict(workload=name, fetch_scale=round(fs, 5), write_scale=round(ws, 5),
                copy_bytes=copy_bytes, kernels=kernels, hbm_bytes_per_launch=round(total),
                sources=rels, source_sha256=sources_sha256(rels))

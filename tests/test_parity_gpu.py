@@ -426,6 +426,31 @@ def test_decode_empty_and_single_key():
     check_parity(got, ref, w.dtype, dead_rows(bias_ref, step.nonpad, w.Hq), "decode-edge")
 
 
+@pytest.mark.parametrize("variant", ["bias", "rules"])
+def test_decode_many_rows_vector_path(variant):
+    """Decode with more (batch row, kv head) pairs than the split kernel's
+    arrival counts cover (B * Hkv > 16384): the vector kernel serves it, with
+    no workspace."""
+    rng = wl.rng_for(720)
+    B, Hq, Hkv, T, D = 1100, 32, 16, 40, 64
+    assert ab.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, 1, T, D) == 0
+    q = wl.normal(rng, (B, Hq, 1, D), torch.bfloat16)
+    k = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    v = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    nonpad = torch.from_numpy(rng.integers(0, T, size=B, endpoint=True).astype(np.int64))
+    q_start = (nonpad - 1).clamp(min=0)
+    bias = torch.from_numpy(oracle.bias(nonpad, q_start, None, 1, T, 16)).to(torch.bfloat16)
+    announce(f"decode B*Hkv={B * Hkv} {variant}")
+    if variant == "bias":
+        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 0.125)
+    else:
+        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), None, dev(nonpad), 0.125, q_start=dev(q_start),
+                                   window=16)
+    ref = oracle.attention(q, k, v, bias, nonpad, 0.125)
+    check_parity(to_f64(got), ref, torch.bfloat16, dead_rows(bias.float().numpy(), nonpad, Hq),
+                 f"many rows/{variant}")
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,D,T,S_q,causal", [
     (3, 8, 2, 256, 300, 1, True),      # decode: bottom-right = every valid key
     (2, 8, 2, 128, 200, 40, True),     # prefill chunk, some rows with nonpad < S_q
