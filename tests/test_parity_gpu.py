@@ -534,6 +534,61 @@ def test_determinism():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("variant", ["bias", "rules"])
+def test_graph_replay_decode_and_prefill(variant):
+    """Calls captured in a HIP graph (a decode step with its in-kernel merge of
+    the splits and a prefill with its live-tile map, sharing one workspace)
+    replay bit-identically to the eager calls, several times, with eager work
+    and synchronisations between the replays; the decode arrival counts are
+    zero after every replay."""
+    dec = wl.decode_sliding(B=4, Hq=16, Hkv=8, D=256, max_seq=1024, window=256)
+    pre = SMALL["prefill_vision"]()
+    ws = torch.zeros(8 << 20, dtype=torch.uint8, device="cuda")
+    jobs = []
+    for w in (dec, pre):
+        st = w.steps[0]
+        k, v = dev(w.k_cache), dev(w.v_cache)
+        if st.k_new is not None:
+            ab.kv_tensor_scatter(k, dev(st.k_new), dev(st.write_indices))
+            ab.kv_tensor_scatter(v, dev(st.v_new), dev(st.write_indices))
+        q, npd, qs = dev(st.q), dev(st.nonpad), dev(st.q_start)
+        kind = None if st.slot_kind is None else dev(st.slot_kind)
+        bias = ab.build_static_cache_bias(npd, qs, kind, st.S_q, w.max_seq, w.window, dtype=w.dtype)
+        out = torch.empty((w.B, w.Hq, st.S_q, w.Dv), dtype=w.dtype, device="cuda")
+        jobs.append((w, q, k, v, bias, npd, qs, kind, out))
+
+    def run_all():
+        for w, q, k, v, bias, npd, qs, kind, out in jobs:
+            if variant == "bias":
+                ab.attn_bias_gqa_fwd(q, k, v, bias, npd, w.scale, out=out, workspace=ws)
+            else:
+                ab.attn_bias_gqa_fwd(q, k, v, None, npd, w.scale, q_start=qs, slot_kind=kind,
+                                     window=w.window, out=out, workspace=ws)
+
+    announce(f"graph replay decode + prefill {variant}")
+    run_all()
+    torch.cuda.synchronize()
+    eager = [j[-1].clone() for j in jobs]
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        run_all()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            run_all()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for j in jobs:
+            j[-1].fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        for j, ref in zip(jobs, eager):
+            assert torch.equal(j[-1].view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+        assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
+        run_all()   # eager work between the replays
+        torch.cuda.synchronize()
+
+
 def test_invalid_arguments_raise():
     q = torch.zeros((1, 3, 1, 256), dtype=torch.bfloat16, device="cuda")
     k = torch.zeros((1, 2, 64, 256), dtype=torch.bfloat16, device="cuda")
