@@ -994,7 +994,8 @@ namespace {
 // of key tile kt below nonpad (a bias entry other than -inf) - the set a
 // workgroup's own bias scan finds (build_live_list), computed once per batch
 // row instead of once per KV head, by a grid that keeps the memory busy.
-// One workgroup per (b, query tile, word = 32 key tiles = 1024 keys).
+// One workgroup per (b, query tile, word = 32 key tiles = 1024 keys); a word
+// wholly at or past nonpad is written 0 without loads.
 template <typename BiasT>
 __global__ __launch_bounds__(256) void tilemap_kernel(const BiasT* __restrict__ bias,
                                                       const int64_t* __restrict__ nonpad,
@@ -1008,6 +1009,10 @@ __global__ __launch_bounds__(256) void tilemap_kernel(const BiasT* __restrict__ 
   const int np = (int)clamp_nonpad(nonpad[b], T);
   const int s0 = qt * MQ, nrows = min(MQ, S_q - s0);
   const int j_lo = word * 32 * kTileKeys, j_hi = min(j_lo + 32 * kTileKeys, np);
+  if (j_lo >= np || nrows <= 0) {
+    if (threadIdx.x == 0) map[wid] = 0u;
+    return;
+  }
   if (threadIdx.x == 0) s_word = 0u;
   __syncthreads();
   constexpr int EPV = 16 / (int)sizeof(BiasT);
@@ -1016,7 +1021,7 @@ __global__ __launch_bounds__(256) void tilemap_kernel(const BiasT* __restrict__ 
   const int c = threadIdx.x % CPW, rr = threadIdx.x / CPW;
   const int j = j_lo + c * EPV;               // rows are multiples of 16 bytes
   bool any = false;
-  if (j < j_hi && nrows > 0) {
+  if (j < j_hi) {
     const BiasT* col = bias + ((int64_t)b * S_q + s0) * T + j;
     constexpr int U = 16;  // loads in flight per thread (rows past the tile repeat its last)
     for (int r0 = rr; r0 < nrows; r0 += U * RPP) {
@@ -1032,7 +1037,12 @@ __global__ __launch_bounds__(256) void tilemap_kernel(const BiasT* __restrict__ 
       }
     }
   }
-  if (any) atomicOr(&s_word, 1u << ((c * EPV) / kTileKeys));
+  // OR the lanes' tile bits over the wavefront: one LDS atomic per wavefront
+  // instead of one per lane on the same word
+  unsigned bits = any ? 1u << ((c * EPV) / kTileKeys) : 0u;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) bits |= (unsigned)__shfl_xor((int)bits, m);
+  if ((threadIdx.x & 63) == 0 && bits) atomicOr(&s_word, bits);
   __syncthreads();
   if (threadIdx.x == 0) map[wid] = s_word;
 }
