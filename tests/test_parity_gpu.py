@@ -140,6 +140,9 @@ SMALL = {
                                                window=0, nonpad_lo=1),
     "decode_d128_g1": lambda: wl.decode_full(B=2, Hq=4, Hkv=4, D=128, max_seq=512, nonpad_lo=1),
     "decode_g3": lambda: wl.decode_full(B=2, Hq=6, Hkv=2, D=256, max_seq=200, nonpad_lo=1),
+    # 16 rows per KV head: the largest row block of the decode kernel
+    "decode_g16": lambda: wl.decode_sliding(B=2, Hq=32, Hkv=2, D=128, max_seq=400, window=0,
+                                            nonpad_lo=1),
     "prefill_vision": lambda: wl.prefill_vision(B=2, Hq=4, Hkv=2, D=256, S_q=100, max_seq=512,
                                                 window=64, start_hi=300, block=40),
     # max_seq 300: bf16 bias rows not 16-byte multiples (register-staged kernel
