@@ -424,7 +424,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported: the "
-              f"hot path is measured on one GPU's share (see DESIGN.md for how it would shard)",
+              f"hot path is measured on one GPU's share of the work (the kernels need no exchange "
+              f"when batch rows or KV heads are split across GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
