@@ -49,7 +49,7 @@ typedef enum {
 typedef enum {
   ABGQA_OK = 0,
   ABGQA_ERR_INVALID = 1,     /* null pointer, bad size, misaligned pointer */
-  ABGQA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+  ABGQA_ERR_UNSUPPORTED = 2, /* valid request the library does not implement */
   ABGQA_ERR_WORKSPACE = 3,   /* workspace missing or too small */
   ABGQA_ERR_HIP = 4          /* the HIP runtime reported an error */
 } abgqa_status;
