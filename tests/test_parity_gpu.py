@@ -592,6 +592,43 @@ def test_graph_replay_decode_and_prefill(variant):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("S_q,T,D", [
+    (1, 40000, 64),      # decode over a cache longer than the prefill fast path's limit
+    (24, 32768, 128),    # prefill at the direct-to-LDS path's longest cache
+    (24, 40000, 128),    # prefill past it: the register-staged kernel
+])
+def test_long_cache(S_q, T, D):
+    """The longest caches each path takes, every slot valid, a window and a bias."""
+    rng = wl.rng_for(730 + S_q + T)
+    B, Hq, Hkv = 1, 4, 2
+    q = wl.normal(rng, (B, Hq, S_q, D), torch.bfloat16)
+    k = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    v = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    nonpad = torch.tensor([T], dtype=torch.int64)
+    q_start = nonpad - S_q
+    bias = torch.from_numpy(oracle.bias(nonpad, q_start, None, S_q, T, 3000)).to(torch.bfloat16)
+    announce(f"long cache S_q={S_q} T={T} D={D}")
+    scale = 1.0 / math.sqrt(D)
+    got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), scale)
+    ref = oracle.attention(q, k, v, bias, nonpad, scale)
+    check_parity(to_f64(got), ref, torch.bfloat16, dead_rows(bias.float().numpy(), nonpad, Hq), f"long/{T}")
+    got_r = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale, q_start=dev(q_start),
+                                 window=3000)
+    check_parity(to_f64(got_r), ref, torch.bfloat16, dead_rows(bias.float().numpy(), nonpad, Hq), f"long/{T}/rules")
+
+
+def test_prefill_cache_too_long_raises():
+    """A prefill whose live-tile list does not fit beside two K/V stages in LDS
+    is refused with a clear error, before any kernel runs."""
+    B, Hq, Hkv, S_q, T, D = 1, 4, 2, 32, 600000, 512
+    q = torch.empty((B, Hq, S_q, D), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((B, Hkv, T, D), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((B, Hkv, T, D), dtype=torch.bfloat16, device="cuda")
+    nonpad = torch.tensor([T], dtype=torch.int64, device="cuda")
+    with pytest.raises(RuntimeError, match="max_seq too large"):
+        ab.attn_bias_gqa_fwd(q, k, v, None, nonpad, 0.05)
+
+
 def test_invalid_arguments_raise():
     q = torch.zeros((1, 3, 1, 256), dtype=torch.bfloat16, device="cuda")
     k = torch.zeros((1, 2, 64, 256), dtype=torch.bfloat16, device="cuda")
