@@ -87,7 +87,7 @@ template <int NT, bool kRules, typename BiasT>
 __device__ __forceinline__ int build_live_list(const AttnParams& p, int64_t b, int np, int s0, int s_end, int n_kt,
                                uint32_t* s_bits, uint16_t* s_list, int n_words, int32_t* s_ids,
                                int* s_nids_p, int* s_nlive_p,
-                               const uint32_t* map_row = nullptr) {
+                               const uint32_t* map_row = nullptr, uint32_t map_pre = 0u) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int T = p.T;
@@ -98,7 +98,8 @@ __device__ __forceinline__ int build_live_list(const AttnParams& p, int64_t b, i
   if (tid < 4) s_ids[tid] = -1;  // never a block id: a racing reader cannot match it
   __syncthreads();
   if (!kRules && map_row) {
-    for (int i = tid; i < n_words; i += NT) s_bits[i] = map_row[i];
+    // map_pre: word tid of map_row, already loaded by the caller (n_words <= NT)
+    if (tid < n_words) s_bits[tid] = map_pre;
   } else if constexpr (!kRules) {
     // NB 16-byte loads per thread in flight at once, unconditional (index
     // clamped to the last vector, the copies discarded), so the scan costs one

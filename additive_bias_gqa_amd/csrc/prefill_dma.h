@@ -271,8 +271,42 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   const int s = s0 + sl;
   const bool row_ok = (r < MQ * G) && (s < p.S_q);
   const int h = hk * G + g;
+  // this workgroup's words of the live-tile map (bias variant with a
+  // workspace), loaded before anything waits so that they share the first
+  // memory round trip with Q (n_words <= 32 <= NT: at most 32768 slots)
+  const uint32_t* map_row =
+      (!kRules && p.tilemap) ? p.tilemap + ((size_t)(b * n_qt + qt)) * n_words : nullptr;
+  const uint32_t map_pre = (map_row && tid < n_words) ? map_row[tid] : 0u;
   bf16x8 qf[kQLds ? 1 : KSTEPS];
-  if constexpr (!kQLds) {
+#ifndef ABGQA_QSTAGE
+#define ABGQA_QSTAGE 1
+#endif
+  if constexpr (!kQLds && RW == 32 && ABGQA_QSTAGE) {
+    // 32-row wavefronts: each wavefront copies its 32 Q rows whole into its
+    // own part of the (still unused) stage area with direct-to-LDS fetches (a
+    // row's chunks contiguous, swizzled like the K tiles) and reads its Q^T
+    // fragments from there: the global reads are whole rows instead of 32-byte
+    // pieces of 32 rows per instruction. Rows past the chunk copy a valid row
+    // (finite; their outputs are never stored).
+    static_assert(NW * RW * D * 2 <= NSTAGE * STAGE_BYTES, "Q rows fit in the stage area");
+    constexpr int RPF = 64 / CPR;   // Q rows per fetch
+    unsigned char* const qw = stages + (size_t)w * RW * D * 2;
+#pragma unroll
+    for (int k = 0; k < RW / RPF; ++k) {
+      const int rl = k * RPF + lane / CPR, cc = lane % CPR;
+      const int rq = RW * rg + rl;
+      const int sq = min(s0 + rq / G, p.S_q - 1);
+      const __bf16* src = (const __bf16*)p.q + ((b * p.Hq + hk * G + rq % G) * p.S_q + sq) * (int64_t)D;
+      dma16(src + 8 * (cc ^ swz_bits<D>(rl)), qw + k * 1024);
+    }
+    wait_vmcnt<0>();
+    const unsigned qb = lds_addr(qw) & kLdsMask;
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
+      const int c = 2 * i + grp;
+      qf[i] = lds_at<bf16x8>(qb, (unsigned)(col * D * 2 + 16 * ((c & ~15) | ((c & 15) ^ swz_bits<D>(col)))));
+    }
+  } else if constexpr (!kQLds) {
     const __bf16* qp = (const __bf16*)p.q + ((b * p.Hq + h) * p.S_q + (row_ok ? s : 0)) * (int64_t)D;
 #pragma unroll
     for (int i = 0; i < KSTEPS; ++i)
@@ -289,11 +323,9 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   // ---- 2. live tiles ---------------------------------------------------------
   // read from LDS, the count is the same in every lane: say so, so that the
   // loop below (and every LDS address derived from its counter) is scalar
-  const uint32_t* map_row =
-      (!kRules && p.tilemap) ? p.tilemap + ((size_t)(b * n_qt + qt)) * n_words : nullptr;
   const int n_live = __builtin_amdgcn_readfirstlane(
       build_live_list<NT, kRules, BiasT>(p, b, np, s0, s_end, n_kt, s_bits, s_list, n_words, s_ids,
-                                         &s_nids, &s_nlive, map_row));
+                                         &s_nids, &s_nlive, map_row, map_pre));
   // KS = 2: the live tiles split by parity of their key tile, even tiles for
   // key half 0 (s_list[0, ...)), odd ones for half 1 (s_list[khalf, ...)), so
   // a fully masked tile that one variant lists and another skips changes no
