@@ -75,7 +75,8 @@ hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
 // path for head sizes the matrix-core kernels are not built for
 hipError_t launch_attn_vec_bf16(const AttnParams& p, hipStream_t stream);
 
-// bf16 decode path (S_q * G <= 16): split-KV kernel, then a combine kernel.
+// bf16 decode path (S_q * G <= 16): one split-KV kernel; the last split of each
+// row merges the row's partial results.
 int decode_num_splits(int64_t B, int64_t Hkv, int64_t max_seq);
 size_t decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_q, int64_t G, int64_t Dv,
                               int64_t max_seq);
