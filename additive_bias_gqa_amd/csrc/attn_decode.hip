@@ -666,6 +666,17 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   }
   // ---- 5. sum the waves in a fixed order (bit-reproducible), write the partial
   float* part = p.ws_part + ((int64_t)hk * S + rank) * PART;
+  __shared__ float s_lrow[NR];
+  if (tid < NR) {
+    const int r = tid;
+    float lsum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kDecWaves; ++ww) {
+      const float f = (m_wg[r] == -INFINITY) ? 0.f : fast_exp2(s_m[ww][r] - m_wg[r]);
+      lsum += s_l[ww][r] * f;
+    }
+    s_lrow[r] = lsum;
+  }
   if constexpr (kParMerge) {
     if (lane < LPR) {
 #pragma unroll
@@ -677,13 +688,6 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
       }
     }
     __syncthreads();
-    for (int i = tid; i < NR * DV / 4; i += kDecThreads) {
-      f32x4 acc = reinterpret_cast<const f32x4*>(s_o)[i];
-#pragma unroll
-      for (int ww = 1; ww < kDecWaves; ++ww)
-        acc += reinterpret_cast<const f32x4*>(s_o + ww * NR * DV)[i];
-      st_agent4(part + 4 * i, acc);
-    }
   } else {
 #pragma unroll
     for (int ww = 0; ww < kDecWaves; ++ww) {
@@ -698,19 +702,43 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
       }
       __syncthreads();
     }
-    for (int i = tid; i < NR * DV / 4; i += kDecThreads)
-      st_agent4(part + 4 * i, reinterpret_cast<const f32x4*>(s_o)[i]);
   }
-  if (tid < NR) {
-    const int r = tid;
-    float lsum = 0.f;
+  // this workgroup's (m, l, O) of 4 values of d
+  auto part_o = [&](int i) {
+    f32x4 acc = reinterpret_cast<const f32x4*>(s_o)[i];
+    if constexpr (kParMerge) {
 #pragma unroll
-    for (int ww = 0; ww < kDecWaves; ++ww) {
-      const float f = (m_wg[r] == -INFINITY) ? 0.f : fast_exp2(s_m[ww][r] - m_wg[r]);
-      lsum += s_l[ww][r] * f;
+      for (int ww = 1; ww < kDecWaves; ++ww) acc += reinterpret_cast<const f32x4*>(s_o + ww * NR * DV)[i];
     }
-    st_agent(part + NR * DV + r, m_wg[r]);
-    st_agent(part + NR * DV + NR + r, lsum);
+    return acc;
+  };
+  // a row with a single split: its partial is the result, written directly
+  // with the arithmetic the merge below applies to one record (bit-identical)
+  if (nsp == 1) {
+    for (int i = tid; i < NR * DV / 4; i += kDecThreads) {
+      const int r = (4 * i) / DV, d0 = (4 * i) % DV;
+      if (r >= R) continue;
+      const f32x4 a = part_o(i);
+      const float mm = m_wg[r];
+      const float fs = (mm == -INFINITY) ? 0.f : fast_exp2(mm - mm);
+      const float den = 0.f * 0.f + s_lrow[r] * fs;
+      float num[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) num[c] = 0.f * 0.f + a[c] * fs;
+      const float inv = den > 0.f ? 1.f / den : 0.f;
+      const int s = r / G, g = r % G;
+      uint16_t* op = (uint16_t*)p.out + (((b * p.Hq + hk * G + g) * p.S_q + s) * (int64_t)DV) + d0;
+      u32x2 pk;
+      pk.x = pack_bf16x2(num[0] * inv, num[1] * inv);
+      pk.y = pack_bf16x2(num[2] * inv, num[3] * inv);
+      *reinterpret_cast<u32x2*>(op) = pk;
+    }
+    return;
+  }
+  for (int i = tid; i < NR * DV / 4; i += kDecThreads) st_agent4(part + 4 * i, part_o(i));
+  if (tid < NR) {
+    st_agent(part + NR * DV + tid, m_wg[tid]);
+    st_agent(part + NR * DV + NR + tid, s_lrow[tid]);
   }
 
   // ---- 6. the row's last split merges the row's records ---------------------

@@ -140,6 +140,8 @@ SMALL = {
                                                window=0, nonpad_lo=1),
     "decode_d128_g1": lambda: wl.decode_full(B=2, Hq=4, Hkv=4, D=128, max_seq=512, nonpad_lo=1),
     "decode_g3": lambda: wl.decode_full(B=2, Hq=6, Hkv=2, D=256, max_seq=200, nonpad_lo=1),
+    # 256 (b, kv head) pairs: one split per row, written without the merge
+    "decode_b64": lambda: wl.decode_full(B=64, Hq=8, Hkv=4, D=128, max_seq=300, nonpad_lo=1),
     # 16 rows per KV head: the largest row block of the decode kernel
     "decode_g16": lambda: wl.decode_sliding(B=2, Hq=32, Hkv=2, D=128, max_seq=400, window=0,
                                             nonpad_lo=1),
