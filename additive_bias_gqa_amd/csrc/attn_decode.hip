@@ -703,7 +703,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
       __syncthreads();
     }
   }
-  // this workgroup's (m, l, O) of 4 values of d
+  // this workgroup's O at item i (row 4i / DV, 4 values of d from 4i % DV)
   auto part_o = [&](int i) {
     f32x4 acc = reinterpret_cast<const f32x4*>(s_o)[i];
     if constexpr (kParMerge) {
