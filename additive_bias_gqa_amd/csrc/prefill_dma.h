@@ -170,6 +170,20 @@ __device__ __forceinline__ void acc_settle(f32x16 (&o)[16]) {
                  "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15]));
 }
 
+// Chunk permutation of a bias row in the LDS bias stage: rows 256 bytes apart
+// (4 bf16 rows or 2 fp32 rows of a 32-key tile) get different chunk orders.
+template <typename BiasT>
+__device__ __forceinline__ int bias_swz(int r) {
+  constexpr int BROW = kTileKeys * (int)sizeof(BiasT);   // bytes per row
+  return (r / (256 / BROW)) & (BROW / 16 - 1);
+}
+// element offset, within its row, of key k of the tile in that layout
+template <typename BiasT>
+__device__ __forceinline__ int bias_pos(int r, int k) {
+  constexpr int EPV = 16 / (int)sizeof(BiasT);
+  return ((k / EPV) ^ bias_swz<BiasT>(r)) * EPV + k % EPV;
+}
+
 template <int D, int RW, int NW, bool kRules, typename BiasT, bool kQReg, int KS>
 struct DmaGeom {
   static_assert(kQReg || RW == 32, "an LDS Q tile needs 32-row wavefronts");
@@ -387,17 +401,25 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
     const int kr = (w * KPW + k) * RPI + lrow;
     kv_off[k] = (unsigned)(kr * D + 8 * (lcc ^ swz_bits<D>(kr))) * 2u;
   }
+  // Bias rows sit in LDS with their 16-byte chunks permuted by bias_swz (row
+  // r's chunk c at position c ^ bias_swz(r)): rows 256 bytes apart would
+  // otherwise hit the same banks when the lanes of a wavefront read the rows
+  // of their query tokens.
   unsigned m_off[MPW];
+  int m_col[MPW];   // first key of the lane's chunk in its row
 #pragma unroll
   for (int m = 0; m < MPW; ++m) {
     if constexpr (kRules) {
       m_off[m] = 16u * (unsigned)(lane & 7);    // lanes 8.. repeat lanes 0..7
+      m_col[m] = 0;
     } else {
       constexpr int EPV = 16 / (int)sizeof(BiasT);
       constexpr int CB = Geo::BROW / 16;       // 16-byte chunks per bias row
       const int c = min(w * MPW + m, NMI - 1) * 64 + lane;
-      const int row = min(s0 + c / CB, p.S_q - 1) - s0;
-      m_off[m] = (unsigned)(row * T + (c % CB) * EPV) * (unsigned)sizeof(BiasT);
+      const int lrow = c / CB;                 // the row in LDS
+      const int row = min(s0 + lrow, p.S_q - 1) - s0;
+      m_col[m] = ((c % CB) ^ bias_swz<BiasT>(lrow)) * EPV;
+      m_off[m] = (unsigned)(row * T + m_col[m]) * (unsigned)sizeof(BiasT);
     }
   }
   // LDS layout of the stages: the K tiles of every stage, then the V tiles,
@@ -432,7 +454,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
       } else {
         constexpr int EPV = 16 / (int)sizeof(BiasT);
         constexpr int CB = Geo::BROW / 16;
-        const int col = (lane % CB) * EPV;   // this lane's first key in the row
+        const int col = m_col[m];   // this lane's first key in the row
         const unsigned off = m_off[m] + (unsigned)(min(T - EPV - j0 - col, 0) * (int)sizeof(BiasT));
         dma16_sl(biasb + (int64_t)s0 * T + j0, off, dst);
       }
@@ -607,7 +629,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
           const int4 kk = *reinterpret_cast<const int4*>(ms + 4 * kb);
           *reinterpret_cast<int4*>(kvs[i]) = int4{kk.x & kind_mask, kk.y & kind_mask, kk.z & kind_mask, kk.w & kind_mask};
         } else {
-          const BiasT* br = reinterpret_cast<const BiasT*>(ms) + sl * kTileKeys + kb;
+          const BiasT* br = reinterpret_cast<const BiasT*>(ms) + sl * kTileKeys + bias_pos<BiasT>(sl, kb);
           if constexpr (sizeof(BiasT) == 2) *reinterpret_cast<u32x2*>(bvs[i]) = *reinterpret_cast<const u32x2*>(br);
           else *reinterpret_cast<u32x4*>(bvs[i]) = *reinterpret_cast<const u32x4*>(br);
         }
@@ -789,7 +811,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
           const int4 kk = *reinterpret_cast<const int4*>(ms + 4 * kf);
           *reinterpret_cast<int4*>(kvs[kb]) = int4{kk.x & kind_mask, kk.y & kind_mask, kk.z & kind_mask, kk.w & kind_mask};
         } else {
-          const BiasT* br = reinterpret_cast<const BiasT*>(ms) + sl * kTileKeys + kf;
+          const BiasT* br = reinterpret_cast<const BiasT*>(ms) + sl * kTileKeys + bias_pos<BiasT>(sl, kf);
           if constexpr (sizeof(BiasT) == 2) *reinterpret_cast<u32x2*>(bvs[kb]) = *reinterpret_cast<const u32x2*>(br);
           else *reinterpret_cast<u32x4*>(bvs[kb]) = *reinterpret_cast<const u32x4*>(br);
         }
