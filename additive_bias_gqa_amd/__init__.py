@@ -213,7 +213,10 @@ def attn_bias_gqa_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     reads KV head h // (Hq // Hkv)); cap(x) = softcap * tanh(x / softcap) when
     softcap > 0, else x. bias=None evaluates the static-cache rules (nonpad,
     q_start, slot_kind, window) inside the kernel instead. V may have another
-    head size than Q and K (the output takes V's)."""
+    head size than Q and K (the output takes V's). Without `workspace`, a
+    per-device workspace is allocated (zero-filled) on the first call that
+    needs it: make that call outside HIP graph capture, or pass a zero-filled
+    `workspace` of attn_bias_gqa_workspace_bytes() bytes."""
     if q.dim() != 4 or k_cache.dim() != 4 or v_cache.dim() != 4:
         raise ValueError("q must be [B, Hq, S_q, D], k_cache [B, Hkv, max_seq, D], "
                          "v_cache [B, Hkv, max_seq, D_v]")
