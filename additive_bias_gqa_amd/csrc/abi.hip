@@ -145,7 +145,7 @@ size_t attn_bias_gqa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t
     return 0;
   const int64_t G = Hq / Hkv;
   if (S_q * G > 16) {
-    const size_t map = D == D_v ? abgqa::prefill_workspace_bytes(B, Hq, Hkv, S_q, max_seq, D) : 0;
+    const size_t map = abgqa::prefill_workspace_bytes(B, Hq, Hkv, S_q, max_seq, D, D_v);
     return map ? abgqa::kWsCounterBytes + map : 0;
   }
   if (!abgqa::decode_supports((int)D, (int)D_v) || B * Hkv > abgqa::kMaxDecodeRows) return 0;
@@ -200,7 +200,7 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
     path = "f32";
     e = abgqa::launch_attn_f32(p, st);
   } else if ((S_q * G <= 16 && (!abgqa::decode_supports((int)D, (int)D_v) || B * Hkv > abgqa::kMaxDecodeRows)) ||
-             (S_q * G > 16 && D != D_v)) {
+             (S_q * G > 16 && D != D_v && !abgqa::prefill_dma_supported(p))) {
     // head sizes the matrix-core kernels are not built for, or more (b, kv
     // head) pairs than the decode arrival counts cover: the vector path
     path = "vector";
@@ -219,7 +219,7 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
   } else {
     path = "prefill";
     if (G > 64) return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: more than 64 query heads per KV head");
-    if (abgqa::prefill_lds_bytes((int)D, (int)max_seq) > 160 * 1024)
+    if (abgqa::prefill_lds_bytes((int)(D > D_v ? D : D_v), (int)max_seq) > 160 * 1024)
       return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: max_seq too large for the prefill tile list");
     if (workspace && !aligned(workspace, 16))
       return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: workspace not 16-byte aligned");

@@ -680,6 +680,8 @@ static bool force_register_path() {
 }
 
 hipError_t launch_attn_prefill(const AttnParams& p, hipStream_t stream) {
+  if (p.Dv != p.D)   // only the direct-to-LDS kernel has a V head size of its own
+    return prefill_dma_supported(p) ? launch_attn_prefill_dma(p, stream) : hipErrorInvalidValue;
   if (!force_register_path() && prefill_dma_supported(p)) return launch_attn_prefill_dma(p, stream);
   if (prefill_lds_bytes(p.D, p.T) > 160 * 1024) return hipErrorInvalidValue;
   switch (p.D) {

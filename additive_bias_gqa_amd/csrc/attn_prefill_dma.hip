@@ -40,6 +40,10 @@ static int prefill_cfg() {
 // four SIMDs of a CU busy with one workgroup per CU. D = 64
 // (a tile too small to split four ways): 32-row wavefronts, 4 of them when
 // that still gives a workgroup per CU.
+// the (D, DV) pairs with a V head size of their own that the kernel is built
+// for (D = 256 beside DV = 512, and the reverse)
+bool dma_dv_pair(int D, int Dv) { return (D == 256 && Dv == 512) || (D == 512 && Dv == 256); }
+
 enum class DmaCfg { k16x4, k16x8, k32x2, k32x4, k32x2r, k32x4r, k16x8k };
 
 DmaCfg dma_cfg(int D, int64_t B, int64_t Hkv, int64_t S_q, int64_t G) {
@@ -99,6 +103,7 @@ hipError_t launch_dma_d(const AttnParams& p, hipStream_t stream) {
 // workgroup); one head per KV head takes the register-staged kernels.
 bool prefill_dma_supported(const AttnParams& p) {
   if (p.D != 64 && p.D != 128 && p.D != 256 && p.D != 512) return false;
+  if (p.Dv != p.D && !dma_dv_pair(p.D, p.Dv)) return false;
   if (p.G < 2) return false;   // the bias stage holds the rows of G >= 2 heads per token
   if (p.T > 32768) return false;
   if (p.bias != nullptr) {
@@ -113,17 +118,21 @@ bool prefill_dma_supported(const AttnParams& p) {
 // query tile, key tile). Shapes that take another path simply leave the
 // scratch unused.
 size_t prefill_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q, int64_t max_seq,
-                               int64_t D) {
+                               int64_t D, int64_t D_v) {
   if (D != 64 && D != 128 && D != 256 && D != 512) return 0;
+  if (D_v != D && !dma_dv_pair((int)D, (int)D_v)) return 0;
   const int64_t G = Hq / Hkv;
   if (G < 2 || G > 64 || max_seq > 32768) return 0;
-  const int64_t mq = dma_rows(dma_cfg((int)D, B, Hkv, S_q, G)) / G;
+  const int64_t rows = D_v != D ? 128 : dma_rows(dma_cfg((int)D, B, Hkv, S_q, G));
+  const int64_t mq = rows / G;
   const int64_t n_qt = (S_q + mq - 1) / mq;
   const int64_t n_words = (num_tiles((int)max_seq) + 31) / 32;
   return (size_t)(B * n_qt * n_words) * sizeof(uint32_t);
 }
 
 hipError_t launch_attn_prefill_dma(const AttnParams& p, hipStream_t stream) {
+  // a V head size of its own: 4 wavefronts of 32 rows, Q^T in registers
+  if (p.Dv != p.D) return launch_attn_prefill_dma_qreg(p, 4, stream);
   switch (p.D) {
     case 64: return launch_dma_d<64>(p, stream);
     case 128: return launch_dma_d<128>(p, stream);

@@ -87,13 +87,15 @@ hipError_t launch_attn_decode(const AttnParams& p, hipStream_t stream);
 // Returns hipErrorInvalidValue when the shape needs more LDS than a CU has.
 hipError_t launch_attn_prefill(const AttnParams& p, hipStream_t stream);
 // direct-to-LDS prefill pipeline (attn_prefill_dma.hip) and when it applies
+// (the only prefill path for D != Dv: D = 256 with Dv = 512, or the reverse)
 bool prefill_dma_supported(const AttnParams& p);
 hipError_t launch_attn_prefill_dma(const AttnParams& p, hipStream_t stream);
 // scratch bytes the prefill path can use for this shape (its live-tile map)
 size_t prefill_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q, int64_t max_seq,
-                               int64_t D);
+                               int64_t D, int64_t D_v);
 // the same kernel with 32-row wavefronts and Q^T in registers
-// (attn_prefill_dma_wide.hip): D = 512 with nw = 4, D = 256 with nw = 2 or 4
+// (attn_prefill_dma_wide.hip): D = 512 with nw = 4, D = 256 with nw = 2 or 4,
+// and the (D, Dv) pairs (256, 512) and (512, 256) with nw = 4
 hipError_t launch_attn_prefill_dma_qreg(const AttnParams& p, int nw, hipStream_t stream);
 size_t prefill_lds_bytes(int D, int max_seq);
 

@@ -44,6 +44,9 @@
 // once for twice the rows; for D = 512 that needs Q^T in registers (128) and
 // O^T in the accumulation registers (256). The compute per tile is that of
 // attn_prefill.hip.
+//
+// V may have its own head size DV (the output rows are DV wide): a V tile
+// holds DV-wide rows, swizzled by swz_bits<DV>, and O^T has DV / RW blocks.
 #include <stdlib.h>
 #include <string.h>
 
@@ -169,6 +172,11 @@ __device__ __forceinline__ void acc_settle(f32x16 (&o)[16]) {
                  "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]),
                  "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15]));
 }
+__device__ __forceinline__ void acc_settle(f32x16 (&o)[8]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
+                 "+a"(o[6]), "+a"(o[7]));
+}
 
 // Chunk permutation of a bias row in the LDS bias stage: rows 256 bytes apart
 // (4 bf16 rows or 2 fp32 rows of a 32-key tile) get different chunk orders.
@@ -184,18 +192,20 @@ __device__ __forceinline__ int bias_pos(int r, int k) {
   return ((k / EPV) ^ bias_swz<BiasT>(r)) * EPV + k % EPV;
 }
 
-template <int D, int RW, int NW, bool kRules, typename BiasT, bool kQReg, int KS>
+template <int D, int RW, int NW, bool kRules, typename BiasT, bool kQReg, int KS, int DV = D>
 struct DmaGeom {
   static_assert(kQReg || RW == 32, "an LDS Q tile needs 32-row wavefronts");
   static_assert(KS == 1 || (KS == 2 && kQReg && NW % 2 == 0), "key halves: Q^T in registers");
-  static constexpr int TILE_BYTES = kTileKeys * D * 2;         // one K (or V) tile
-  static constexpr int NKI = TILE_BYTES / 1024;                // fetches per K (or V) tile
+  static constexpr int TILE_K = kTileKeys * D * 2;             // one K tile
+  static constexpr int TILE_V = kTileKeys * DV * 2;            // one V tile
+  static constexpr int NKI = TILE_K / 1024;                    // fetches per K tile
+  static constexpr int NVI = TILE_V / 1024;                    // fetches per V tile
   static constexpr int MQ_MAX = RW * NW / KS / 2;              // query tokens, G >= 2
   static constexpr int BROW = kTileKeys * (int)sizeof(BiasT);  // bias bytes per row per tile
   static constexpr int MASK_BYTES = kRules ? 1024 : ((MQ_MAX * BROW + 1023) / 1024) * 1024;
   static constexpr int NMI = MASK_BYTES / 1024;                // fetches for bias / kinds
-  static constexpr int PW = 2 * (NKI / NW) + (NMI + NW - 1) / NW;  // fetches per wavefront per stage
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + MASK_BYTES;
+  static constexpr int PW = (NKI + NVI) / NW + (NMI + NW - 1) / NW;  // fetches per wavefront per stage
+  static constexpr int STAGE_BYTES = TILE_K + TILE_V + MASK_BYTES;
   // !kQReg: the workgroup's Q rows live in LDS (the B operand of S^T is read
   // from there)
   static constexpr bool kQLds = !kQReg;
@@ -205,26 +215,34 @@ struct DmaGeom {
   static constexpr int NSTAGE = NSTAGE1 - NSTAGE1 % KS;   // whole super-stages of KS tiles
   static_assert(NSTAGE / KS >= 2, "two super-stages must fit");
   static_assert(KS * PW * (NSTAGE / KS - 2) <= 63, "wait count");
+  // KS = 2: the key halves merge through the stage area
+  static_assert(KS == 1 || (NW / KS) * (DV / RW * (RW == 32 ? 16 : 4) + 2) * 64 * 4 <= NSTAGE * STAGE_BYTES,
+                "merge area");
 };
 
 }  // namespace
 
-template <int D, int RW, int NW, bool kRules, typename BiasT, bool kQReg, int KS>
+template <int D, int RW, int NW, bool kRules, typename BiasT, bool kQReg, int KS, int DV = D>
 __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p, int n_qt) {
-  using Geo = DmaGeom<D, RW, NW, kRules, BiasT, kQReg, KS>;
+  using Geo = DmaGeom<D, RW, NW, kRules, BiasT, kQReg, KS, DV>;
   constexpr int NT = NW * 64;
-  constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
+  constexpr int CPR = D / 8;                 // 16-byte chunks per Q/K row
+  constexpr int CPRV = DV / 8;               // 16-byte chunks per V row
   constexpr int NSTAGE = Geo::NSTAGE;
-  constexpr int TILE_BYTES = Geo::TILE_BYTES;
+  constexpr int TILE_K = Geo::TILE_K;
+  constexpr int TILE_V = Geo::TILE_V;
   constexpr int STAGE_BYTES = Geo::STAGE_BYTES;
   constexpr int MASK_BYTES = Geo::MASK_BYTES;
   constexpr int NKI = Geo::NKI;
+  constexpr int NVI = Geo::NVI;
   constexpr int PW = Geo::PW;
   constexpr int KSTEPS = RW == 32 ? D / 16 : D / 32;   // k-steps of S^T over the head dim
-  constexpr int DBLK = D / RW;                         // d blocks of O^T
+  constexpr int DBLK = DV / RW;                        // d blocks of O^T
   constexpr bool kQLds = Geo::kQLds;
   constexpr int Q_BYTES = Geo::Q_BYTES;
-  constexpr bool kAsmAcc = kQReg && RW == 32 && D >= 512;   // O^T via mfma32x32x16_acc
+  // O^T via mfma32x32x16_acc where O^T and Q^T of 32 rows do not fit the
+  // ordinary registers together
+  constexpr bool kAsmAcc = kQReg && RW == 32 && (D >= 512 || DV >= 512);
   static_assert(!(kAsmAcc && KS > 1), "key halves with accumulation-register O^T");
   constexpr int NSUP = NSTAGE / KS;   // super-stages: KS tiles each
   // The next stage's fetches go out in kFG groups spread over the S^T MFMAs of
@@ -295,14 +313,15 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
 #ifndef ABGQA_QSTAGE
 #define ABGQA_QSTAGE 1
 #endif
-  if constexpr (!kQLds && RW == 32 && ABGQA_QSTAGE) {
+  constexpr bool kQStage = !kQLds && RW == 32 && ABGQA_QSTAGE && NW * RW * D * 2 <= NSTAGE * STAGE_BYTES;
+  if constexpr (kQStage) {
     // 32-row wavefronts: each wavefront copies its 32 Q rows whole into its
     // own part of the (still unused) stage area with direct-to-LDS fetches (a
     // row's chunks contiguous, swizzled like the K tiles) and reads its Q^T
     // fragments from there: the global reads are whole rows instead of 32-byte
     // pieces of 32 rows per instruction. Rows past the chunk copy a valid row
-    // (finite; their outputs are never stored).
-    static_assert(NW * RW * D * 2 <= NSTAGE * STAGE_BYTES, "Q rows fit in the stage area");
+    // (finite; their outputs are never stored). Only where the workgroup's Q
+    // rows fit in the stage area (not with D = 512 beside DV = 256).
     constexpr int RPF = 64 / CPR;   // Q rows per fetch
     unsigned char* const qw = stages + (size_t)w * RW * D * 2;
 #pragma unroll
@@ -375,7 +394,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   const bool cap_on = p.softcap > 0.f;
   const float cap2 = p.softcap * kLog2e, scale_over_cap = cap_on ? p.scale / p.softcap : 0.f;
   const __bf16* kg = (const __bf16*)p.k + (b * p.Hkv + hk) * (int64_t)T * D;
-  const __bf16* vg = (const __bf16*)p.v + (b * p.Hkv + hk) * (int64_t)T * D;
+  const __bf16* vg = (const __bf16*)p.v + (b * p.Hkv + hk) * (int64_t)T * DV;
   const int32_t* kindb = p.slot_kind ? p.slot_kind + b * T : nullptr;
   // rules variant: the kind stage is read unconditionally (it holds K bytes
   // when there are no slot kinds) and masked to kind 0 then, so no branch
@@ -384,22 +403,36 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   const BiasT* biasb = kRules ? nullptr : (const BiasT*)p.bias + b * p.S_q * (int64_t)T;
 
   // ---- 3. one stage's fetches ----------------------------------------------
-  // Wavefront w fetches K rows [w*KPW*RPI, (w+1)*KPW*RPI) of the tile, the
-  // same V rows, and its share of the bias rows (or the slot kinds), so the
-  // kind of every fetch is known at compile time and the issue is branch-free.
-  constexpr int KPW = NKI / NW;            // K (and V) fetches per wavefront
+  // Wavefront w fetches K rows [w*KPW*RPI, (w+1)*KPW*RPI) of the tile, V rows
+  // [w*VPW*RPIV, (w+1)*VPW*RPIV), and its share of the bias rows (or the slot
+  // kinds), so the kind of every fetch is known at compile time and the issue
+  // is branch-free.
+  constexpr int KPW = NKI / NW;            // K fetches per wavefront
+  constexpr int VPW = NVI / NW;            // V fetches per wavefront
   constexpr int NMI = Geo::NMI;
   constexpr int MPW = (NMI + NW - 1) / NW;  // bias / kind fetches per wavefront
-  constexpr int RPI = 64 / CPR;             // K/V rows per fetch
-  static_assert(NKI % NW == 0 && 64 % CPR == 0 && PW == 2 * KPW + MPW, "fetch layout");
+  constexpr int RPI = 64 / CPR;             // K rows per fetch
+  constexpr int RPIV = 64 / CPRV;           // V rows per fetch
+  static_assert(NKI % NW == 0 && NVI % NW == 0 && 64 % CPR == 0 && 64 % CPRV == 0 &&
+                    PW == KPW + VPW + MPW,
+                "fetch layout");
+  // fetch order: K and V alternate while both have fetches left, then the
+  // rest of the larger, then bias / kinds
+  constexpr int NIL = KPW < VPW ? KPW : VPW;
   const int lrow = lane / CPR, lcc = lane % CPR;
-  // byte offsets of this lane's chunks from the tile's first row (K and V
-  // alike) / first bias row / first slot kind
-  unsigned kv_off[KPW];
+  const int lrowv = lane / CPRV, lccv = lane % CPRV;
+  // byte offsets of this lane's chunks from the tile's first K row / first V
+  // row / first bias row / first slot kind
+  unsigned kv_off[KPW], v_off[VPW];
 #pragma unroll
   for (int k = 0; k < KPW; ++k) {
     const int kr = (w * KPW + k) * RPI + lrow;
     kv_off[k] = (unsigned)(kr * D + 8 * (lcc ^ swz_bits<D>(kr))) * 2u;
+  }
+#pragma unroll
+  for (int k = 0; k < VPW; ++k) {
+    const int vr = (w * VPW + k) * RPIV + lrowv;
+    v_off[k] = (unsigned)(vr * DV + 8 * (lccv ^ swz_bits<DV>(vr))) * 2u;
   }
   // Bias rows sit in LDS with their 16-byte chunks permuted by bias_swz (row
   // r's chunk c at position c ^ bias_swz(r)): rows 256 bytes apart would
@@ -423,30 +456,37 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
     }
   }
   // LDS layout of the stages: the K tiles of every stage, then the V tiles,
-  // then the bias / kind blocks. A stage's tile lies a multiple of TILE_BYTES
-  // from stage 0's, so with the stage known at compile time (the loop below
+  // then the bias / kind blocks. A stage's tile lies a multiple of TILE_K (or
+  // TILE_V) from stage 0's, so with the stage known at compile time (the loop below
   // runs NSTAGE tiles per iteration when NSTAGE == 2) a read of stage st
   // differs from one of stage 0 only in the instruction's offset field.
   const unsigned lds0 = lds_addr(stages);
   // fetch f of this wavefront's PW for the tile starting at key j0 into stage
-  // st: f < 2*KPW are K and V rows (K for even f), the rest bias rows or slot
-  // kinds. Rows at or past nonpad are fetched from row nonpad - 1, and bias /
+  // st: f < KPW + VPW are K and V rows (f < 2*NIL: K for even f), the rest
+  // bias rows or slot kinds. Rows at or past nonpad are fetched from row nonpad - 1, and bias /
   // kind chunks past the end of the cache from its last chunk; both clamps are
   // folded into the lane's offset, so the issue has no branch. f is a
   // compile-time constant at every call.
   auto fetch_one = [&](const int f, const int j0, const int st) {
     const int lim = np - 1 - j0;   // the tile's last valid row (j0 < nonpad)
-    if (f < 2 * KPW) {
-      const int k = f >> 1;
-      const int ii = w * KPW + k;
-      const int kr = ii * RPI + lrow;
-      const unsigned off = kv_off[k] + (unsigned)(min(lim - kr, 0) * (2 * D));
-      if ((f & 1) == 0) dma16_sl(kg + (int64_t)j0 * D, off, lds0 + st * TILE_BYTES + ii * 1024);
-      else dma16_sl(vg + (int64_t)j0 * D, off, lds0 + (NSTAGE + st) * TILE_BYTES + ii * 1024);
+    if (f < KPW + VPW) {
+      const bool is_k = f < 2 * NIL ? (f & 1) == 0 : KPW > VPW;
+      const int k = f < 2 * NIL ? f >> 1 : f - NIL;
+      if (is_k) {
+        const int ii = w * KPW + k;
+        const int kr = ii * RPI + lrow;
+        const unsigned off = kv_off[k] + (unsigned)(min(lim - kr, 0) * (2 * D));
+        dma16_sl(kg + (int64_t)j0 * D, off, lds0 + st * TILE_K + ii * 1024);
+      } else {
+        const int ii = w * VPW + k;
+        const int vr = ii * RPIV + lrowv;
+        const unsigned off = v_off[k] + (unsigned)(min(lim - vr, 0) * (2 * DV));
+        dma16_sl(vg + (int64_t)j0 * DV, off, lds0 + NSTAGE * TILE_K + st * TILE_V + ii * 1024);
+      }
     } else {
-      const int m = f - 2 * KPW;
+      const int m = f - KPW - VPW;
       const int ii = min(w * MPW + m, NMI - 1);   // surplus fetches repeat the last one
-      const unsigned dst = lds0 + 2 * NSTAGE * TILE_BYTES + st * MASK_BYTES + ii * 1024;
+      const unsigned dst = lds0 + NSTAGE * (TILE_K + TILE_V) + st * MASK_BYTES + ii * 1024;
       if constexpr (kRules) {
         const int c = 4 * (lane & 7);   // this lane's first slot kind
         const unsigned off = m_off[m] + (unsigned)(min(T - 4 - j0 - c, 0) * 4);
@@ -518,17 +558,19 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
       for (int k = 0; k < KS; ++k) fetch_stage(key_of(k, u), KS * u + k);
   }
   // Per-lane byte offsets into the swizzled tiles. Chunk c of row r sits at
-  // 16 * (c ^ swz_bits<D>(r)); the XOR touches only the low SWB bits of c, so the
-  // reads of one lane need a few base offsets (by those low bits of c) plus
-  // compile-time multiples of SPAN = 16 << SWB bytes.
+  // 16 * (c ^ swz_bits<D>(r)) (V: swz_bits<DV>); the XOR touches only the low
+  // SWB bits of c, so the reads of one lane need a few base offsets (by those
+  // low bits of c) plus compile-time multiples of SPAN = 16 << SWB bytes.
   constexpr int SWB = swz_width<D>();
   constexpr int SPAN = 16 << SWB;
+  constexpr int SWBV = swz_width<DV>();
+  constexpr int SPANV = 16 << SWBV;
   // RW = 32: K/Q chunk 2*i + grp -> groups i % NKG; V chunk 4*blk + vdofs/8 ->
   // groups blk % NVG, times the two 8-row halves (the swizzle sees row bit 3).
   // RW = 16: K chunk 4*i + grp -> groups i % NKG; V chunk 2*blk + vdofs/8 ->
   // groups blk % NVG.
   constexpr int NKG = RW == 32 ? (1 << SWB) / 2 : (1 << SWB) / 4;
-  constexpr int NVG = RW == 32 ? (1 << SWB) / 4 : (1 << SWB) / 2;
+  constexpr int NVG = RW == 32 ? (1 << SWBV) / 4 : (1 << SWBV) / 2;
   unsigned k_lane[NKG];                  // K (and, RW = 32, Q) rows
   unsigned v_lane[RW == 32 ? 2 : 1][NVG];  // V^T transposing reads
   if constexpr (RW == 32) {
@@ -546,7 +588,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
 #pragma unroll
       for (int m = 0; m < NVG; ++m) {
         const int row = 8 * hf + vkey0;
-        v_lane[hf][m] = (unsigned)(row * D * 2 + 16 * ((4 * m + (vdofs >> 3)) ^ swz_bits<D>(row)) +
+        v_lane[hf][m] = (unsigned)(row * DV * 2 + 16 * ((4 * m + (vdofs >> 3)) ^ swz_bits<DV>(row)) +
                                    2 * (vdofs & 7));
       }
   } else {
@@ -560,7 +602,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
     const int vdofs = 4 * (lane & 3);
 #pragma unroll
     for (int m = 0; m < NVG; ++m)
-      v_lane[0][m] = (unsigned)(vkey0 * D * 2 + 16 * ((2 * m + (vdofs >> 3)) ^ swz_bits<D>(vkey0)) +
+      v_lane[0][m] = (unsigned)(vkey0 * DV * 2 + 16 * ((2 * m + (vdofs >> 3)) ^ swz_bits<DV>(vkey0)) +
                                 2 * (vdofs & 7));
   }
   // this wavefront's Q rows in the LDS Q tile, one base per k-chunk group
@@ -570,24 +612,27 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
 #pragma unroll
     for (int m = 0; m < NKG; ++m) q_base[m] = (qa0 + k_lane[m]) & kLdsMask;
   }
-  // loop-invariant read bases of stage 0 (stage st adds st * TILE_BYTES)
+  // loop-invariant read bases of stage 0 (stage st adds st * TILE_K, or
+  // st * TILE_V)
   unsigned k_base[NKG], v_base[RW == 32 ? 2 : 1][NVG];
 #pragma unroll
-  for (int m = 0; m < NKG; ++m) k_base[m] = (lds0 + kh * TILE_BYTES + k_lane[m]) & kLdsMask;
+  for (int m = 0; m < NKG; ++m) k_base[m] = (lds0 + kh * TILE_K + k_lane[m]) & kLdsMask;
 #pragma unroll
   for (int hf = 0; hf < (RW == 32 ? 2 : 1); ++hf)
 #pragma unroll
     for (int m = 0; m < NVG; ++m)
-      v_base[hf][m] = (lds0 + (NSTAGE + kh) * TILE_BYTES + v_lane[hf][m]) & kLdsMask;
+      v_base[hf][m] = (lds0 + NSTAGE * TILE_K + kh * TILE_V + v_lane[hf][m]) & kLdsMask;
 
   // one tile from key j0, held by stage KS*ss + kh (super-stage ss); jn / ssn
   // name the super-stage whose fetches go out during its S^T MFMAs
   auto tile_step = [&](const int j0, const int ss, const int* jn, const int ssn)
                        __attribute__((always_inline)) {
     const bool full = j0 + kTileKeys <= np;   // no key of the tile at or past nonpad
-    const unsigned char* ms = stages + 2 * NSTAGE * TILE_BYTES + (KS * ss + kh) * MASK_BYTES;
-    // stage offset of K and V reads (the key half's kh * TILE_BYTES is in the bases)
-    const unsigned KO = (unsigned)(KS * ss * TILE_BYTES);
+    const unsigned char* ms = stages + NSTAGE * (TILE_K + TILE_V) + (KS * ss + kh) * MASK_BYTES;
+    // stage offsets of K and V reads (the key half's kh * TILE_K or kh * TILE_V
+    // is in the bases)
+    const unsigned KO = (unsigned)(KS * ss * TILE_K);
+    const unsigned VO = (unsigned)(KS * ss * TILE_V);
 
     if constexpr (RW == 32) {
       BiasT bvs[4][4];
@@ -663,9 +708,9 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
       constexpr int PVD = NU < ABGQA_PVD32 ? NU : ABGQA_PVD32;
       auto vread = [&](int u) {
         const int blk = u >> 1;
-        const unsigned so = SPAN * (blk / NVG) + 16 * (u & 1) * D * 2;
-        const u32x2 lo = lds_tr16_at(v_base[0][blk % NVG], KO + so);
-        const u32x2 hi = lds_tr16_at(v_base[1][blk % NVG], KO + so);
+        const unsigned so = SPANV * (blk / NVG) + 16 * (u & 1) * DV * 2;
+        const u32x2 lo = lds_tr16_at(v_base[0][blk % NVG], VO + so);
+        const u32x2 hi = lds_tr16_at(v_base[1][blk % NVG], VO + so);
         return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
       };
       bf16x8 vf[PVD];
@@ -847,9 +892,9 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
       // lane 16*gq + 4*kq + jq reads V[4*gq + kq (+16)][16*blk + 4*jq]
       constexpr int PVD = 4;
       auto vread = [&](int blk) {
-        const unsigned so = SPAN * (blk / NVG);
-        const u32x2 lo = lds_tr16_at(v_base[0][blk % NVG], KO + so);
-        const u32x2 hi = lds_tr16_at(v_base[0][blk % NVG], KO + so + 16 * D * 2);
+        const unsigned so = SPANV * (blk / NVG);
+        const u32x2 lo = lds_tr16_at(v_base[0][blk % NVG], VO + so);
+        const u32x2 hi = lds_tr16_at(v_base[0][blk % NVG], VO + so + 16 * DV * 2);
         return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
       };
       bf16x8 vf[PVD];
@@ -1016,7 +1061,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   l_tot += lane_xor(l_tot, 32);
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* op = (uint16_t*)p.out + ((b * p.Hq + h) * p.S_q + s) * (int64_t)D;
+    uint16_t* op = (uint16_t*)p.out + ((b * p.Hq + h) * p.S_q + s) * (int64_t)DV;
     if constexpr (RW == 32) {
       // O^T lane l: row l % 32, d = 32*blk + 8*i + 4*(l/32) + jj
 #pragma unroll
@@ -1101,16 +1146,16 @@ __global__ __launch_bounds__(256) void tilemap_kernel(const BiasT* __restrict__ 
   if (threadIdx.x == 0) map[wid] = s_word;
 }
 
-template <int D, int RW, int NW, bool kRules, typename BiasT, bool kQReg, int KS>
+template <int D, int RW, int NW, bool kRules, typename BiasT, bool kQReg, int KS, int DV>
 hipError_t launch_dma_inst(const AttnParams& p, hipStream_t stream) {
-  using Geo = DmaGeom<D, RW, NW, kRules, BiasT, kQReg, KS>;
+  using Geo = DmaGeom<D, RW, NW, kRules, BiasT, kQReg, KS, DV>;
   const int MQ = (RW * NW / KS) / p.G;
   const int n_qt = (p.S_q + MQ - 1) / MQ;
   const int n_kt = num_tiles(p.T);
   const size_t list = (size_t)((n_kt + 31) / 32) * 4 + (size_t)n_kt * 2;
   const size_t lds = (size_t)Geo::Q_BYTES + (size_t)Geo::NSTAGE * Geo::STAGE_BYTES +
                      ((list + 15) & ~(size_t)15);
-  auto kern = attn_prefill_dma_kernel<D, RW, NW, kRules, BiasT, kQReg, KS>;
+  auto kern = attn_prefill_dma_kernel<D, RW, NW, kRules, BiasT, kQReg, KS, DV>;
   // opt in to exactly the dynamic LDS of this launch (the kernel's static LDS
   // comes on top)
   static size_t lds_set = 0;   // per instantiation
@@ -1151,11 +1196,12 @@ hipError_t launch_dma_inst(const AttnParams& p, hipStream_t stream) {
 // kQReg: Q^T fragments in registers (RW = 16 always; RW = 32 where the
 // accumulators live in the accumulation registers)
 // KS = 2: two wavefronts per row group, on alternate tiles
-template <int D, int RW, int NW, bool kQReg = (RW == 16), int KS = 1>
+// DV: the V head size (that of the output rows)
+template <int D, int RW, int NW, bool kQReg = (RW == 16), int KS = 1, int DV = D>
 hipError_t launch_dma_v(const AttnParams& p, hipStream_t stream) {
-  if (p.bias == nullptr) return launch_dma_inst<D, RW, NW, true, uint16_t, kQReg, KS>(p, stream);
-  if (p.bias_is_bf16) return launch_dma_inst<D, RW, NW, false, uint16_t, kQReg, KS>(p, stream);
-  return launch_dma_inst<D, RW, NW, false, uint32_t, kQReg, KS>(p, stream);
+  if (p.bias == nullptr) return launch_dma_inst<D, RW, NW, true, uint16_t, kQReg, KS, DV>(p, stream);
+  if (p.bias_is_bf16) return launch_dma_inst<D, RW, NW, false, uint16_t, kQReg, KS, DV>(p, stream);
+  return launch_dma_inst<D, RW, NW, false, uint32_t, kQReg, KS, DV>(p, stream);
 }
 
 }  // namespace

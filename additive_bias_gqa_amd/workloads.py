@@ -212,12 +212,13 @@ def prefill_vision(index: int = 3, B=2, Hq=16, Hkv=8, D=256, S_q=512, max_seq=40
 
 
 def prefill_long(index: int = 4, B=4, Hq=16, Hkv=4, D=512, S_q=2048, max_seq=8192,
-                 pad_hi=256, block=256, dtype=torch.bfloat16) -> Workload:
+                 pad_hi=256, block=256, dtype=torch.bfloat16, Dv=None) -> Workload:
     """Prefill of S_q tokens from slot 0 with left padding pad_b ~ U{0..pad_hi}
     (slot kind PAD, expressed through the bias) and one image block of ``block``
     tokens at an offset ~ U{pad_b..S_q-block}. nonpad = S_q, q_start = 0; the
-    cache is garbage before the scatter. Draw order: pads, block offsets, q,
-    K cache, V cache, k_new, v_new."""
+    cache is garbage before the scatter. Dv: head size of V (default D).
+    Draw order: pads, block offsets, q, K cache, V cache, k_new, v_new."""
+    Dv = D if Dv is None else Dv
     assert S_q <= max_seq and pad_hi + block <= S_q
     rng = rng_for(index)
     pads = rng.integers(0, pad_hi, size=B, endpoint=True).astype(np.int64)
@@ -226,14 +227,15 @@ def prefill_long(index: int = 4, B=4, Hq=16, Hkv=4, D=512, S_q=2048, max_seq=819
     q = normal(rng, (B, Hq, S_q, D), dtype)
     zero = np.zeros(B, dtype=np.int64)
     kc = _fill_cache(rng, B, Hkv, max_seq, D, zero, dtype)
-    vc = _fill_cache(rng, B, Hkv, max_seq, D, zero, dtype)
+    vc = _fill_cache(rng, B, Hkv, max_seq, Dv, zero, dtype)
     kn = normal(rng, (B, Hkv, S_q, D), dtype)
-    vn = normal(rng, (B, Hkv, S_q, D), dtype)
+    vn = normal(rng, (B, Hkv, S_q, Dv), dtype)
     kind = torch.zeros((B, max_seq), dtype=torch.int32)
     for b in range(B):
         kind[b, :int(pads[b])] = PAD
         kind[b, int(offs[b]):int(offs[b]) + block] = 1
     z = torch.zeros(B, dtype=torch.int64)
     step = Step(q, kn, vn, z.clone(), torch.full((B,), S_q, dtype=torch.int64), z.clone(), kind)
-    return Workload(f"prefill_long_B{B}_Hq{Hq}_Hkv{Hkv}_D{D}_Sq{S_q}_T{max_seq}",
+    vtag = "" if Dv == D else f"_Dv{Dv}"
+    return Workload(f"prefill_long_B{B}_Hq{Hq}_Hkv{Hkv}_D{D}{vtag}_Sq{S_q}_T{max_seq}",
                     dtype, B, Hq, Hkv, D, max_seq, 0, 1.0 / math.sqrt(D), kc, vc, [step])

@@ -52,7 +52,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-V_HEAD = None      # --v-head-size: V head size of the KV-shared decode workload
+V_HEAD = None      # --v-head-size: V head size of the KV-shared decode or the long prefill
 
 
 def make_workload(name):
@@ -62,7 +62,7 @@ def make_workload(name):
         "decode_full": wl.decode_full,
         "decode_full_kvshared": lambda: wl.decode_full(kv_shared=True, Dv=V_HEAD),
         "prefill_vision": wl.prefill_vision,
-        "prefill_long": wl.prefill_long,
+        "prefill_long": lambda: wl.prefill_long(Dv=V_HEAD),
     }[name]()
 
 
@@ -92,8 +92,12 @@ def run_scatter_bias(ab, w, step, s):
     """TensorScatter of K and V and the bias build, as one fused launch
     (kv_scatter_and_bias; bit-identical to the three separate calls). The
     KV-shared workload has nothing to scatter; the rules variant builds no bias."""
-    if s.k_new is None:
-        # KV-shared: nothing to scatter (and V may have another head size)
+    if s.k_new is None or s.v.shape[-1] != s.k.shape[-1]:
+        # KV-shared: nothing to scatter; V of another head size: the two
+        # scatters apart (the fused launch takes one row size)
+        if s.k_new is not None:
+            ab.kv_tensor_scatter(s.k, s.k_new, s.wi)
+            ab.kv_tensor_scatter(s.v, s.v_new, s.wi)
         if VARIANT == "bias":
             ab.build_static_cache_bias(s.nonpad, s.q_start, s.kind, step.S_q, w.max_seq, w.window,
                                        out=s.bias)
@@ -409,11 +413,11 @@ def main():
     ap.add_argument("--softcap", type=float, default=0.0,
                     help="softcap of the attention scores (0 = none, the workloads' setting)")
     ap.add_argument("--v-head-size", type=int, default=None,
-                    help="head size of V for decode_full_kvshared (KV-shared layers may read "
-                         "a V of another head size; default: the query's)")
+                    help="head size of V for decode_full_kvshared or prefill_long (V may have "
+                         "another head size than Q and K; default: the query's)")
     args = ap.parse_args()
-    if args.v_head_size is not None and args.workload != "decode_full_kvshared":
-        ap.error("--v-head-size applies to --workload decode_full_kvshared")
+    if args.v_head_size is not None and args.workload not in ("decode_full_kvshared", "prefill_long"):
+        ap.error("--v-head-size applies to --workload decode_full_kvshared or prefill_long")
     if args.traffic_from:
         write_traffic(args.workload, *args.traffic_from)
         return

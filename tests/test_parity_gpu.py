@@ -338,7 +338,7 @@ def test_shared_workspace_counts():
     (512, 256, 1, torch.bfloat16),
     (512, 256, 2, torch.bfloat16),    # two query tokens per step
     (64, 512, 1, torch.bfloat16),     # decode, a pair without matrix-core kernels
-    (256, 512, 40, torch.bfloat16),   # prefill chunk: vector path
+    (256, 512, 40, torch.bfloat16),   # prefill chunk (bias rows of 600 bytes: bias on the vector path)
     (64, 128, 9, torch.float32),      # fp32 path
 ])
 def test_value_head_size(D, Dv, S_q, dtype, variant):
@@ -367,6 +367,41 @@ def test_value_head_size(D, Dv, S_q, dtype, variant):
                                    q_start=dev(q_start), slot_kind=dev(kind), window=window)
     assert got.shape == (B, Hq, S_q, Dv)
     check_parity(to_f64(got), ref, dtype, dead_rows(bias.float().numpy(), nonpad, Hq), f"Dv/{variant}")
+
+
+@pytest.mark.parametrize("variant,cap", [("bf16", 0.0), ("f32", 0.0), ("rules", 0.0), ("rules", 20.0),
+                                         ("bf16", 20.0)])
+@pytest.mark.parametrize("D,Dv", [(256, 512), (512, 256)])
+def test_value_head_size_prefill_mfma(D, Dv, variant, cap):
+    """Prefill with V's own head size on the direct-to-LDS matrix-core kernel:
+    five query tiles (the last ragged), eleven key tiles (the last partial),
+    a batch row whose nonpad ends inside a tile, pads, an image block, and the
+    live-tile map of the bias variant (the binding's workspace holds it)."""
+    rng = wl.rng_for(680 + D + Dv + int(cap))
+    B, Hq, Hkv, T, S_q = 3, 8, 2, 344, 150
+    q = wl.normal(rng, (B, Hq, S_q, D), torch.bfloat16)
+    k = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    v = wl.normal(rng, (B, Hkv, T, Dv), torch.bfloat16)
+    nonpad = torch.tensor([T, 201, 150], dtype=torch.int64)
+    q_start = (nonpad - S_q).clamp(min=0)
+    kind = torch.zeros((B, T), dtype=torch.int32)
+    kind[1, :7] = -1
+    kind[2, 40:90] = 1
+    window = 96
+    bias = torch.from_numpy(oracle.bias(nonpad, q_start, kind, S_q, T, window)).to(
+        torch.float32 if variant == "f32" else torch.bfloat16)
+    assert ab.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, T, D, Dv) > 65536   # the map fits
+    announce(f"value head size prefill D={D} Dv={Dv} {variant} cap={cap}")
+    scale = 1.0 / math.sqrt(D)
+    ref = oracle.attention(q, k, v, bias, nonpad, scale, softcap=cap)
+    if variant == "rules":
+        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale, q_start=dev(q_start),
+                                   slot_kind=dev(kind), window=window, softcap=cap)
+    else:
+        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), scale, softcap=cap)
+    assert got.shape == (B, Hq, S_q, Dv)
+    check_parity(to_f64(got), ref, torch.bfloat16, dead_rows(bias.float().numpy(), nonpad, Hq),
+                 f"Dv prefill/{variant}/cap{cap}")
 
 
 def test_attention_fp32_bias_dtype():
