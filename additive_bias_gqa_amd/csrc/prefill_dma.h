@@ -159,9 +159,10 @@ constexpr int kLdsBudget = 160 * 1024 - 6 * 1024;   // stages; the rest: live li
 // are issued as inline asm on "a" operands, so each accumulator lives in the
 // accumulation registers from its zeroing to its final read. The compiler sees
 // no matrix-core op in that asm and so inserts no wait states for it; the
-// ordering below provides them: two MFMAs into one accumulator are 16 MFMAs
-// apart, and every VALU access to the accumulators (the rare rescale, the
-// final read) first passes acc_settle, 32 wait states after the last MFMA.
+// ordering below provides them: two MFMAs into one accumulator are DV / 32
+// MFMAs apart (16, or 8 at DV = 256, each of 8 passes), and every VALU access
+// to the accumulators (the rare rescale, the final read) first passes
+// acc_settle, 32 wait states after the last MFMA.
 __device__ __forceinline__ void mfma32x32x16_acc(f32x16& c, bf16x8 a, bf16x8 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
