@@ -404,6 +404,37 @@ def test_value_head_size_prefill_mfma(D, Dv, variant, cap):
                  f"Dv prefill/{variant}/cap{cap}")
 
 
+@pytest.mark.parametrize("D,Dv", [(256, 512), (512, 256)])
+def test_value_head_size_prefill_shapes(D, Dv):
+    """The same kernel over group sizes and tile counts: G = 2 with a chunk just
+    above the decode limit (one query tile, two key tiles), G = 16 (8 tokens
+    per query tile, nine tiles), G = 2 with 64-token tiles over 32 key tiles;
+    bias and rules variants each."""
+    for idx, (Hq, Hkv, S_q, T, npv) in enumerate([(16, 8, 9, 64, [64, 41]),
+                                                   (32, 2, 70, 520, [520, 333]),
+                                                   (4, 2, 300, 1024, [1000, 300])]):
+        rng = wl.rng_for(700 + idx + D // 64)
+        B = len(npv)
+        q = wl.normal(rng, (B, Hq, S_q, D), torch.bfloat16)
+        k = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+        v = wl.normal(rng, (B, Hkv, T, Dv), torch.bfloat16)
+        nonpad = torch.tensor(npv, dtype=torch.int64)
+        q_start = (nonpad - S_q).clamp(min=0)
+        kind = torch.zeros((B, T), dtype=torch.int32)
+        kind[1, :3] = -1
+        window = 0 if idx == 1 else 48
+        bias = torch.from_numpy(oracle.bias(nonpad, q_start, kind, S_q, T, window)).to(torch.bfloat16)
+        scale = 1.0 / math.sqrt(D)
+        ref = oracle.attention(q, k, v, bias, nonpad, scale)
+        dead = dead_rows(bias.float().numpy(), nonpad, Hq)
+        announce(f"value head size prefill shapes D={D} Dv={Dv} Hq={Hq} Hkv={Hkv} S_q={S_q} T={T}")
+        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), scale)
+        check_parity(to_f64(got), ref, torch.bfloat16, dead, f"Dv shapes/bias/{idx}")
+        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale, q_start=dev(q_start),
+                                   slot_kind=dev(kind), window=window)
+        check_parity(to_f64(got), ref, torch.bfloat16, dead, f"Dv shapes/rules/{idx}")
+
+
 def test_attention_fp32_bias_dtype():
     w = SMALL["prefill_vision"]()
     step = w.steps[0]
