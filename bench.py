@@ -250,10 +250,16 @@ def bench_workload(name, steps, warmup, eager, torch, ab):
         res["roofline"] = dict(bound="mfma", achieved=round(res["attn_rate"], 1),
                                peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                                frac=round(res["attn_rate"] / BF16_PEAK_TFLOPS, 4))
+        # the same call against HBM (a prefill chunk of few rows per key sits
+        # near the ridge point): its algorithmic bytes over the same time
+        hbm = counts["attn_bytes"] / (attn_ms * 1e-3) / 1e9
+        res["hbm_side"] = dict(achieved=round(hbm, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                               frac=round(hbm / HBM_PEAK_GBS, 4))
     res["step_gbs"] = counts["step_bytes"] / (step_ms * 1e-3) / 1e9
+    side = f", HBM side {100 * res['hbm_side']['frac']:.1f}%" if "hbm_side" in res else ""
     log(f"{name}: {mode} step {step_ms * 1e3:.1f} us, attention {attn_ms * 1e3:.1f} us, "
         f"{res['roofline']['achieved']} {res['roofline']['unit']} "
-        f"({100 * res['roofline']['frac']:.1f}% of peak)")
+        f"({100 * res['roofline']['frac']:.1f}% of peak{side})")
     del sets, probe, ws
     torch.cuda.empty_cache()
     return res, w
@@ -455,6 +461,8 @@ def main():
                 attn_us=round(r["attn_ms"] * 1e3, 2), step_us=round(r["ms_per_step"] * 1e3, 2),
                 roofline=r["roofline"], step_gbs=round(r["step_gbs"], 1),
                 config=r["desc"])
+            if "hbm_side" in r:
+                secondary[name]["hbm_side"] = r["hbm_side"]
 
     rl = dict(main_res["roofline"])
     rl["traffic"] = traffic_for(args.workload)
@@ -468,6 +476,7 @@ def main():
                 "device_copy_gbs": round(copy_gbs, 1), "variant": VARIANT, "softcap": SOFTCAP,
                 "attn_us": round(main_res["attn_ms"] * 1e3, 2),
                 "attn_bytes": counts["attn_bytes"], "step_bytes": counts["step_bytes"],
+                **({"hbm_side": main_res["hbm_side"]} if "hbm_side" in main_res else {}),
                 "live_keys": counts["live_keys"]})
     line = {
         "metric": "decode KV GB/s (% of HBM peak) + prefill attention TFLOP/s (% of MFMA peak)",
