@@ -160,9 +160,10 @@ constexpr int kLdsBudget = 160 * 1024 - 6 * 1024;   // stages; the rest: live li
 // accumulation registers from its zeroing to its final read. The compiler sees
 // no matrix-core op in that asm and so inserts no wait states for it; the
 // ordering below provides them: two MFMAs into one accumulator are DV / 32
-// MFMAs apart (16, or 8 at DV = 256, each of 8 passes), and every VALU access
+// MFMAs apart (16, or 8 at DV = 256, each of 8 passes), every VALU access
 // to the accumulators (the rare rescale, the final read) first passes
-// acc_settle, 32 wait states after the last MFMA.
+// acc_settle, 32 wait states after the last MFMA, and the VALU-built P^T
+// operands pass an s_nop that takes them as operands before the first PV MFMA.
 __device__ __forceinline__ void mfma32x32x16_acc(f32x16& c, bf16x8 a, bf16x8 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
@@ -802,8 +803,8 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
         pw[e >> 1] = pk;
       }
       l_run += lsum;
-      const bf16x8 pb0 = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-      const bf16x8 pb1 = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+      bf16x8 pb0 = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+      bf16x8 pb1 = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
       if (rescale) {
         // rare (the running maximum rose by more than 8): a real branch - the
         // asm keeps the compiler from turning it into selects executed on every
@@ -824,6 +825,11 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
       }
       // O^T += V^T P^T, fragments read PVD MFMAs ahead
       if constexpr (kAsmAcc) {
+        // P^T comes from VALU instructions, and an MFMA reading a register that
+        // a VALU instruction wrote needs two wait states in between, which the
+        // compiler does not insert before an asm MFMA: this asm sits after the
+        // last write of pb0 / pb1 (it takes them as operands) and provides them
+        asm volatile("s_nop 1" : "+v"(pb0), "+v"(pb1));
         // the first key half of every d block, then the second half
         auto useq = [](int q) { return q < DBLK ? 2 * q : 2 * (q - DBLK) + 1; };
 #pragma unroll
