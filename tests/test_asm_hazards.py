@@ -1,0 +1,98 @@
+"""Wait states before the inline-asm MFMAs of the direct-to-LDS prefill kernel.
+
+The PV products of the 32-row kernels with O^T in the accumulation registers
+are inline asm, so the compiler inserts no hazard wait states for them. An
+MFMA that reads a register a VALU instruction wrote (the softmax weights P^T,
+or an accumulator rewritten by the rescale) needs two wait states in between
+(CDNA3/CDNA4 ISA, MFMA dependency rules: VALU write of a VGPR followed by an
+MFMA read of it is not interlocked). This test disassembles the gfx950 code of
+the built library and checks every such MFMA: scanning back from it to the
+previous MFMA, the last VALU write of one of its source registers must be at
+least two wait states earlier (s_nop N counts N + 1, any other instruction 1).
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import additive_bias_gqa_amd as ab
+
+OBJDUMP = "/opt/rocm/llvm/bin/llvm-objdump"
+MFMA = re.compile(r"v_mfma_f32_32x32x16_bf16 a\[(\d+):(\d+)\], v\[(\d+):(\d+)\], v\[(\d+):(\d+)\], a\[(\d+):(\d+)\]")
+DEST = re.compile(r"^(v_\S+)\s+([va])(?:\[(\d+):(\d+)\]|(\d+))\b")
+NEED = 2
+
+
+def _regs(lo, hi):
+    return set(range(int(lo), int(hi) + 1))
+
+
+def _kernel_bodies(text):
+    """{symbol: [instruction text]} for the prefill kernels of one disassembly."""
+    bodies, cur = {}, None
+    for line in text.splitlines():
+        head = re.match(r"^[0-9a-f]+ <(\S+)>:$", line)
+        if head:
+            cur = head.group(1) if "attn_prefill_dma_kernel" in head.group(1) else None
+            if cur:
+                bodies[cur] = []
+            continue
+        if cur and line.startswith("\t"):
+            ins = line.strip().split("//")[0].strip()
+            if ins:
+                bodies[cur].append(ins)
+    return bodies
+
+
+def _min_wait_states(ins):
+    """(number of asm-form MFMAs, smallest wait-state distance found)."""
+    worst, n = 99, 0
+    for i, line in enumerate(ins):
+        m = MFMA.match(line)
+        if not m:
+            continue
+        n += 1
+        vsrc = _regs(m.group(3), m.group(4)) | _regs(m.group(5), m.group(6))
+        asrc = _regs(m.group(7), m.group(8))
+        ws = 0
+        for k in range(1, 64):
+            if i - k < 0:
+                break
+            prev = ins[i - k]
+            if prev.startswith("v_mfma"):
+                break
+            d = DEST.match(prev)
+            if d:
+                lo = d.group(3) if d.group(3) is not None else d.group(5)
+                hi = d.group(4) if d.group(4) is not None else d.group(5)
+                written = _regs(lo, hi)
+                if written & (vsrc if d.group(2) == "v" else asrc):
+                    worst = min(worst, ws)
+                    break
+            nop = re.match(r"s_nop (\d+)", prev)
+            ws += int(nop.group(1)) + 1 if nop else 1
+    return n, worst
+
+
+@pytest.mark.skipif(not os.path.exists(OBJDUMP), reason="ROCm llvm-objdump not installed")
+def test_asm_mfma_operands_have_wait_states(tmp_path):
+    lib = ab.library_path()
+    if not os.path.exists(lib):
+        pytest.skip("library not built")
+    shutil.copy(lib, tmp_path / "lib.so")
+    subprocess.run([OBJDUMP, "--offloading", "lib.so"], cwd=tmp_path, check=True, capture_output=True)
+    checked = 0
+    for f in sorted(os.listdir(tmp_path)):
+        if not f.endswith("gfx950"):
+            continue
+        text = subprocess.run([OBJDUMP, "-d", "--mcpu=gfx950", f], cwd=tmp_path, check=True,
+                              capture_output=True, text=True).stdout
+        for sym, ins in _kernel_bodies(text).items():
+            n, worst = _min_wait_states(ins)
+            if n:
+                checked += n
+                assert worst >= NEED, f"{sym}: an asm MFMA reads a register {worst} wait states after a VALU write"
+    # the 32-row kernels with accumulation-register O^T are built and checked
+    assert checked > 0
