@@ -9,6 +9,9 @@ MFMA read of it is not interlocked). This test disassembles the gfx950 code of
 the built library and checks every such MFMA: scanning back from it to the
 previous MFMA, the last VALU write of one of its source registers must be at
 least two wait states earlier (s_nop N counts N + 1, any other instruction 1).
+The other direction too: a VALU read of an accumulator (v_accvgpr_read) must
+come at least passes + 2 wait states after the MFMA that wrote it; 18 is
+taken (16 passes + 2, more than a 32x32x16 MFMA takes).
 """
 import os
 import re
@@ -23,6 +26,7 @@ OBJDUMP = "/opt/rocm/llvm/bin/llvm-objdump"
 MFMA = re.compile(r"v_mfma_f32_32x32x16_bf16 a\[(\d+):(\d+)\], v\[(\d+):(\d+)\], v\[(\d+):(\d+)\], a\[(\d+):(\d+)\]")
 DEST = re.compile(r"^(v_\S+)\s+([va])(?:\[(\d+):(\d+)\]|(\d+))\b")
 NEED = 2
+NEED_READ = 18
 
 
 def _regs(lo, hi):
@@ -76,6 +80,28 @@ def _min_wait_states(ins):
     return n, worst
 
 
+def _min_read_wait_states(ins):
+    """(VALU reads of an asm MFMA's accumulator found, smallest distance)."""
+    worst, n = 999, 0
+    for i, line in enumerate(ins):
+        m = re.match(r"v_accvgpr_read_b32 v\d+, a(\d+)", line)
+        if not m:
+            continue
+        a, ws = int(m.group(1)), 0
+        for k in range(1, 128):
+            if i - k < 0:
+                break
+            prev = ins[i - k]
+            mm = MFMA.match(prev)
+            if mm and a in _regs(mm.group(1), mm.group(2)):
+                n += 1
+                worst = min(worst, ws)
+                break
+            nop = re.match(r"s_nop (\d+)", prev)
+            ws += int(nop.group(1)) + 1 if nop else 1
+    return n, worst
+
+
 @pytest.mark.skipif(not os.path.exists(OBJDUMP), reason="ROCm llvm-objdump not installed")
 def test_asm_mfma_operands_have_wait_states(tmp_path):
     lib = ab.library_path()
@@ -94,5 +120,8 @@ def test_asm_mfma_operands_have_wait_states(tmp_path):
             if n:
                 checked += n
                 assert worst >= NEED, f"{sym}: an asm MFMA reads a register {worst} wait states after a VALU write"
+            n, worst = _min_read_wait_states(ins)
+            if n:
+                assert worst >= NEED_READ, f"{sym}: an accumulator is read {worst} wait states after its MFMA"
     # the 32-row kernels with accumulation-register O^T are built and checked
     assert checked > 0
