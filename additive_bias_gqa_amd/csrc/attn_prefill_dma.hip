@@ -44,6 +44,20 @@ static int prefill_cfg() {
 // for (D = 256 beside DV = 512, and the reverse)
 bool dma_dv_pair(int D, int Dv) { return (D == 256 && Dv == 512) || (D == 512 && Dv == 256); }
 
+// Rows per workgroup of those pairs: 4 wavefronts of 32 rows (O^T in the
+// accumulation registers) when that grid has a workgroup for every CU, else 4
+// wavefronts of 16 rows (O^T in the ordinary registers, twice the
+// workgroups). Vision-chunk shape (B 2, 8 KV heads, 512 tokens, G 2) with
+// DV = 512: 63 us against 78; long-prefill shape with DV = 256 (1024
+// workgroups of 32-row wavefronts): 298 us against 403.
+int dv_rows(int64_t B, int64_t Hkv, int64_t S_q, int64_t G) {
+  const int cfg = prefill_cfg();
+  if (cfg == 3) return 64;    // "16x4"
+  if (cfg == 6) return 128;   // "32x4r"
+  const int64_t wg32 = B * Hkv * ((S_q * G + 127) / 128);
+  return wg32 >= 256 ? 128 : 64;
+}
+
 enum class DmaCfg { k16x4, k16x8, k32x2, k32x4, k32x2r, k32x4r, k16x8k };
 
 DmaCfg dma_cfg(int D, int64_t B, int64_t Hkv, int64_t S_q, int64_t G) {
@@ -123,7 +137,7 @@ size_t prefill_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q, 
   if (D_v != D && !dma_dv_pair((int)D, (int)D_v)) return 0;
   const int64_t G = Hq / Hkv;
   if (G < 2 || G > 64 || max_seq > 32768) return 0;
-  const int64_t rows = D_v != D ? 128 : dma_rows(dma_cfg((int)D, B, Hkv, S_q, G));
+  const int64_t rows = D_v != D ? dv_rows(B, Hkv, S_q, G) : dma_rows(dma_cfg((int)D, B, Hkv, S_q, G));
   const int64_t mq = rows / G;
   const int64_t n_qt = (S_q + mq - 1) / mq;
   const int64_t n_words = (num_tiles((int)max_seq) + 31) / 32;
@@ -131,8 +145,14 @@ size_t prefill_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q, 
 }
 
 hipError_t launch_attn_prefill_dma(const AttnParams& p, hipStream_t stream) {
-  // a V head size of its own: 4 wavefronts of 32 rows, Q^T in registers
-  if (p.Dv != p.D) return launch_attn_prefill_dma_qreg(p, 4, stream);
+  // a V head size of its own
+  if (p.Dv != p.D) {
+    if (dv_rows(p.B, p.Hkv, p.S_q, p.G) == 64) {
+      if (p.D == 256) return launch_dma_v<256, 16, 4, true, 1, 512>(p, stream);
+      return launch_dma_v<512, 16, 4, true, 1, 256>(p, stream);
+    }
+    return launch_attn_prefill_dma_qreg(p, 4, stream);
+  }
   switch (p.D) {
     case 64: return launch_dma_d<64>(p, stream);
     case 128: return launch_dma_d<128>(p, stream);

@@ -95,7 +95,8 @@ size_t prefill_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q, 
                                int64_t D, int64_t D_v);
 // the same kernel with 32-row wavefronts and Q^T in registers
 // (attn_prefill_dma_wide.hip): D = 512 with nw = 4, D = 256 with nw = 2 or 4,
-// and the (D, Dv) pairs (256, 512) and (512, 256) with nw = 4
+// and the (D, Dv) pairs (256, 512) and (512, 256) with nw = 4 (their 16-row
+// form is in attn_prefill_dma.hip)
 hipError_t launch_attn_prefill_dma_qreg(const AttnParams& p, int nw, hipStream_t stream);
 size_t prefill_lds_bytes(int D, int max_seq);
 

@@ -184,22 +184,24 @@ def decode_full(index: int = 2, B=16, Hq=16, Hkv=4, D=512, max_seq=8192, nonpad_
 
 def prefill_vision(index: int = 3, B=2, Hq=16, Hkv=8, D=256, S_q=512, max_seq=4096,
                    window=1024, start_hi=2048, block=256, n_blocks=2,
-                   dtype=torch.bfloat16) -> Workload:
+                   dtype=torch.bfloat16, Dv=None) -> Workload:
     """Prefill chunk of S_q tokens at absolute start ~ U{0..start_hi}, with
     ``n_blocks`` image blocks of ``block`` tokens at offsets ~ U{0..S_q-block}
     inside the chunk (ids 1, 2, ...; a later block overwrites an overlap).
     Slots [0, start) hold earlier context ~ N(0,1); slots >= start are garbage
-    until the chunk is scattered at start; nonpad = start + S_q.
-    Draw order: start, block offsets, q, K cache, V cache, k_new, v_new."""
+    until the chunk is scattered at start; nonpad = start + S_q. Dv: head size
+    of V (default D). Draw order: start, block offsets, q, K cache, V cache,
+    k_new, v_new."""
     assert start_hi + S_q <= max_seq and block <= S_q
+    Dv = D if Dv is None else Dv
     rng = rng_for(index)
     start = rng.integers(0, start_hi, size=B, endpoint=True).astype(np.int64)
     offs = rng.integers(0, S_q - block, size=(B, n_blocks), endpoint=True)
     q = normal(rng, (B, Hq, S_q, D), dtype)
     kc = _fill_cache(rng, B, Hkv, max_seq, D, start, dtype)
-    vc = _fill_cache(rng, B, Hkv, max_seq, D, start, dtype)
+    vc = _fill_cache(rng, B, Hkv, max_seq, Dv, start, dtype)
     kn = normal(rng, (B, Hkv, S_q, D), dtype)
-    vn = normal(rng, (B, Hkv, S_q, D), dtype)
+    vn = normal(rng, (B, Hkv, S_q, Dv), dtype)
     kind = torch.zeros((B, max_seq), dtype=torch.int32)
     for b in range(B):
         for i in range(n_blocks):
@@ -207,7 +209,8 @@ def prefill_vision(index: int = 3, B=2, Hq=16, Hkv=8, D=256, S_q=512, max_seq=40
             kind[b, lo:lo + block] = i + 1
     st = torch.from_numpy(start)
     step = Step(q, kn, vn, st.clone(), st + S_q, st.clone(), kind)
-    return Workload(f"prefill_vision_B{B}_Hq{Hq}_Hkv{Hkv}_D{D}_Sq{S_q}_T{max_seq}_W{window}",
+    vtag = "" if Dv == D else f"_Dv{Dv}"
+    return Workload(f"prefill_vision_B{B}_Hq{Hq}_Hkv{Hkv}_D{D}{vtag}_Sq{S_q}_T{max_seq}_W{window}",
                     dtype, B, Hq, Hkv, D, max_seq, window, 1.0 / math.sqrt(D), kc, vc, [step])
 
 

@@ -52,7 +52,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-V_HEAD = None      # --v-head-size: V head size of the KV-shared decode or the long prefill
+V_HEAD = None      # --v-head-size: V head size of the KV-shared decode or of a prefill
 
 
 def make_workload(name):
@@ -61,7 +61,7 @@ def make_workload(name):
         "decode_sliding": wl.decode_sliding,
         "decode_full": wl.decode_full,
         "decode_full_kvshared": lambda: wl.decode_full(kv_shared=True, Dv=V_HEAD),
-        "prefill_vision": wl.prefill_vision,
+        "prefill_vision": lambda: wl.prefill_vision(Dv=V_HEAD),
         "prefill_long": lambda: wl.prefill_long(Dv=V_HEAD),
     }[name]()
 
@@ -419,11 +419,12 @@ def main():
     ap.add_argument("--softcap", type=float, default=0.0,
                     help="softcap of the attention scores (0 = none, the workloads' setting)")
     ap.add_argument("--v-head-size", type=int, default=None,
-                    help="head size of V for decode_full_kvshared or prefill_long (V may have "
-                         "another head size than Q and K; default: the query's)")
+                    help="head size of V for decode_full_kvshared, prefill_vision or prefill_long (V "
+                         "may have another head size than Q and K; default: the query's)")
     args = ap.parse_args()
-    if args.v_head_size is not None and args.workload not in ("decode_full_kvshared", "prefill_long"):
-        ap.error("--v-head-size applies to --workload decode_full_kvshared or prefill_long")
+    if args.v_head_size is not None and args.workload not in ("decode_full_kvshared", "prefill_vision",
+                                                               "prefill_long"):
+        ap.error("--v-head-size applies to --workload decode_full_kvshared, prefill_vision or prefill_long")
     if args.traffic_from:
         write_traffic(args.workload, *args.traffic_from)
         return

@@ -99,9 +99,12 @@ def test_workspace_size(lib):
     # prefill (D 256, G 2: 64-row workgroups of 32 tokens): one bit per batch
     # row x 16 query tiles x 128 key tiles
     assert lib.attn_bias_gqa_workspace_bytes(2, 16, 8, 512, 4096, 256, 256) == CNT + 2 * 16 * 4 * 4
-    # a V head size of its own (256 beside 512): 128-row workgroups of 64 tokens
-    assert lib.attn_bias_gqa_workspace_bytes(2, 16, 8, 512, 4096, 256, 512) == CNT + 2 * 8 * 4 * 4
-    assert lib.attn_bias_gqa_workspace_bytes(2, 16, 8, 512, 4096, 512, 256) == CNT + 2 * 8 * 4 * 4
+    # a V head size of its own (256 beside 512): 64-row workgroups of 32 tokens
+    # while 128-row ones would number fewer than 256 (here 2 x 8 x 8)...
+    assert lib.attn_bias_gqa_workspace_bytes(2, 16, 8, 512, 4096, 256, 512) == CNT + 2 * 16 * 4 * 4
+    assert lib.attn_bias_gqa_workspace_bytes(2, 16, 8, 512, 4096, 512, 256) == CNT + 2 * 16 * 4 * 4
+    # ... and 128-row workgroups (G 4: 32 tokens) beyond: 4 x 4 x 64 of them
+    assert lib.attn_bias_gqa_workspace_bytes(4, 16, 4, 2048, 8192, 512, 256) == CNT + 4 * 64 * 8 * 4
     assert lib.attn_bias_gqa_workspace_bytes(2, 16, 8, 512, 4096, 128, 512) == 0   # vector path
     assert lib.attn_bias_gqa_workspace_bytes(2, 8, 8, 512, 4096, 256, 256) == 0    # G = 1: no map
     assert lib.attn_bias_gqa_workspace_bytes(1, 6, 4, 1, 64, 64, 64) == 0         # invalid heads

@@ -718,6 +718,10 @@ FULL = {
     "decode_full_kvshared": (lambda: wl.decode_full(kv_shared=True), 48),
     "prefill_vision": (lambda: wl.prefill_vision(), 160),
     "prefill_long": (lambda: wl.prefill_long(), 96),
+    # V of another head size: the 16-row kernel at the vision chunk's grid, the
+    # 32-row one at the long prefill's
+    "prefill_vision_dv512": (lambda: wl.prefill_vision(Dv=512), 160),
+    "prefill_long_dv256": (lambda: wl.prefill_long(Dv=256), 96),
 }
 
 
@@ -755,9 +759,9 @@ def test_attention_full_size(name, variant):
         g = bias.cpu().to(torch.float32).view(torch.int32)
         assert torch.equal(g, torch.from_numpy(bias_ref).to(torch.float32).view(torch.int32))
     del k_d, v_d, bias
-    got = to_f64(out).reshape(-1, w.D)
+    got = to_f64(out).reshape(-1, w.Dv)
     dead = dead_rows(bias_ref, step.nonpad, w.Hq).reshape(-1)
-    exp = ref.reshape(-1, w.D)
+    exp = ref.reshape(-1, w.Dv)
     if rows is not None:
         got, dead = got[rows], dead[rows]
-    check_parity(got, exp, w.dtype, np.repeat(dead[:, None], w.D, axis=1), f"full/{name}/{variant}")
+    check_parity(got, exp, w.dtype, np.repeat(dead[:, None], w.Dv, axis=1), f"full/{name}/{variant}")
