@@ -4,7 +4,11 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "abgqa.h"
 #include "kernels.h"
@@ -43,11 +47,120 @@ bool log_enabled() {
 
 constexpr int64_t kMaxSeq = (int64_t)1 << 24;  // slot indices stay exact in int32
 
+// ABGQA_CHECK=1: before enqueuing, synchronise the stream, copy the device-side
+// index arrays to the host and validate them; after enqueuing, synchronise
+// again and report any asynchronous HIP error. Read at every call. Skipped while
+// the stream is being captured into a graph (no synchronisation is allowed then).
+bool check_requested() {
+  const char* v = getenv("ABGQA_CHECK");
+  return v && v[0] && v[0] != '0';
+}
+
+bool check_enabled(hipStream_t st) {
+  if (!check_requested()) return false;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return cs == hipStreamCaptureStatusNone;
+}
+
+// The n values of a device array, after the work already on `st` has finished.
+// Fails (returns a status) if the pointer is not device-accessible memory or a
+// HIP call fails.
+abgqa_status fetch_device(const void* dptr, size_t bytes, void* host, hipStream_t st, const char* me,
+                          const char* what) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, dptr) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(ABGQA_ERR_INVALID, "%s: ABGQA_CHECK: %s is not device-accessible memory", me, what);
+  }
+  hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(me, e);
+  e = hipMemcpy(host, dptr, bytes, hipMemcpyDefault);
+  if (e != hipSuccess) return hip_fail(me, e);
+  return ABGQA_OK;
+}
+
+abgqa_status fetch_i64(const int64_t* dptr, int64_t n, std::vector<int64_t>& out, hipStream_t st,
+                       const char* me, const char* what) {
+  out.assign((size_t)n, 0);
+  return fetch_device(dptr, (size_t)n * sizeof(int64_t), out.data(), st, me, what);
+}
+
+// nonpad_kv_seqlen[b] in [0, max_seq] for every batch row
+abgqa_status check_nonpad(const int64_t* nonpad, int64_t B, int64_t max_seq, hipStream_t st,
+                          const char* me) {
+  std::vector<int64_t> v;
+  abgqa_status r = fetch_i64(nonpad, B, v, st, me, "nonpad_kv_seqlen");
+  if (r != ABGQA_OK) return r;
+  for (int64_t b = 0; b < B; ++b)
+    if (v[b] < 0 || v[b] > max_seq)
+      return fail(ABGQA_ERR_INVALID,
+                  "%s: ABGQA_CHECK: nonpad_kv_seqlen[%lld] = %lld is outside [0, max_seq = %lld]", me,
+                  (long long)b, (long long)v[b], (long long)max_seq);
+  return ABGQA_OK;
+}
+
+// q_start[b] >= 0: a query sits at a cache position
+abgqa_status check_q_start(const int64_t* q_start, int64_t B, hipStream_t st, const char* me) {
+  if (!q_start) return ABGQA_OK;
+  std::vector<int64_t> v;
+  abgqa_status r = fetch_i64(q_start, B, v, st, me, "q_start");
+  if (r != ABGQA_OK) return r;
+  for (int64_t b = 0; b < B; ++b)
+    if (v[b] < 0)
+      return fail(ABGQA_ERR_INVALID, "%s: ABGQA_CHECK: q_start[%lld] = %lld is negative", me,
+                  (long long)b, (long long)v[b]);
+  return ABGQA_OK;
+}
+
+// every written slot write_indices[b] + t, t < S_new, inside [0, max_seq)
+abgqa_status check_write_indices(const int64_t* wi, int64_t B, int64_t max_seq, int64_t S_new,
+                                 hipStream_t st, const char* me) {
+  if (!wi || S_new == 0) return S_new <= max_seq ? ABGQA_OK
+                                                 : fail(ABGQA_ERR_INVALID,
+                                                        "%s: ABGQA_CHECK: S_new = %lld slots past max_seq = %lld",
+                                                        me, (long long)S_new, (long long)max_seq);
+  std::vector<int64_t> v;
+  abgqa_status r = fetch_i64(wi, B, v, st, me, "write_indices");
+  if (r != ABGQA_OK) return r;
+  for (int64_t b = 0; b < B; ++b)
+    if (v[b] < 0 || v[b] > max_seq - S_new)
+      return fail(ABGQA_ERR_INVALID,
+                  "%s: ABGQA_CHECK: write_indices[%lld] = %lld puts slots of the %lld new tokens "
+                  "outside [0, max_seq = %lld)",
+                  me, (long long)b, (long long)v[b], (long long)S_new, (long long)max_seq);
+  return ABGQA_OK;
+}
+
+// after the launch: wait for it and report what went wrong asynchronously
+abgqa_status check_after(hipStream_t st, const char* me) {
+  const hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(me, e);
+  return ABGQA_OK;
+}
+
 bool head_dim_ok(int64_t D) { return D == 64 || D == 128 || D == 256 || D == 512; }
 
 }  // namespace
 
 void abgqa::set_launch_detail(const char* what) { g_launch_detail = what; }
+
+hipError_t abgqa::opt_in_dynamic_lds(const void* kern, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, size_t> done;   // (kernel, device) -> bytes
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  size_t& have = done[{kern, dev}];
+  if (lds <= have) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) have = lds;
+  return e;
+}
 
 extern "C" {
 
@@ -69,10 +182,16 @@ abgqa_status kv_tensor_scatter(void* cache, const void* update, const int64_t* w
   if (!cache || !update) return fail(ABGQA_ERR_INVALID, "kv_tensor_scatter: null cache or update");
   if (!aligned(cache, 16) || !aligned(update, 16) || (write_indices && !aligned(write_indices, 8)))
     return fail(ABGQA_ERR_INVALID, "kv_tensor_scatter: misaligned pointer");
+  const hipStream_t st = (hipStream_t)stream;
+  const bool chk = check_enabled(st);
+  if (chk) {
+    const abgqa_status r = check_write_indices(write_indices, B, max_seq, S_new, st, "kv_tensor_scatter");
+    if (r != ABGQA_OK) return r;
+  }
   const hipError_t e = abgqa::launch_scatter(cache, update, write_indices, B, Hkv, max_seq, S_new,
-                                             row_bytes, (hipStream_t)stream);
+                                             row_bytes, st);
   if (e != hipSuccess) return hip_fail("kv_tensor_scatter", e);
-  return ABGQA_OK;
+  return chk ? check_after(st, "kv_tensor_scatter") : ABGQA_OK;
 }
 
 abgqa_status build_static_cache_bias(void* bias, abgqa_dtype bias_dtype,
@@ -90,10 +209,18 @@ abgqa_status build_static_cache_bias(void* bias, abgqa_dtype bias_dtype,
   if (!aligned(bias, 16) || !aligned(nonpad_kv_seqlen, 8) || (q_start && !aligned(q_start, 8)) ||
       (slot_kind && !aligned(slot_kind, 16)))
     return fail(ABGQA_ERR_INVALID, "build_static_cache_bias: misaligned pointer");
+  const char* me = "build_static_cache_bias";
+  const hipStream_t st = (hipStream_t)stream;
+  const bool chk = check_enabled(st);
+  if (chk) {
+    abgqa_status r = check_nonpad(nonpad_kv_seqlen, B, max_seq, st, me);
+    if (r == ABGQA_OK) r = check_q_start(q_start, B, st, me);
+    if (r != ABGQA_OK) return r;
+  }
   const hipError_t e = abgqa::launch_bias(bias, bias_dtype == ABGQA_BF16, nonpad_kv_seqlen, q_start,
-                                          slot_kind, B, S_q, max_seq, window, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail("build_static_cache_bias", e);
-  return ABGQA_OK;
+                                          slot_kind, B, S_q, max_seq, window, st);
+  if (e != hipSuccess) return hip_fail(me, e);
+  return chk ? check_after(st, me) : ABGQA_OK;
 }
 
 abgqa_status kv_scatter_and_bias(void* k_cache, void* v_cache, const void* k_update,
@@ -131,12 +258,20 @@ abgqa_status kv_scatter_and_bias(void* k_cache, void* v_cache, const void* k_upd
       return fail(ABGQA_ERR_INVALID, "%s: misaligned bias, nonpad, q_start or slot_kind", me);
   }
   if (S_new == 0 && !bias) return ABGQA_OK;  // nothing to do
+  const hipStream_t st = (hipStream_t)stream;
+  const bool chk = check_enabled(st);
+  if (chk) {
+    abgqa_status r = S_new > 0 ? check_write_indices(write_indices, B, max_seq, S_new, st, me) : ABGQA_OK;
+    if (r == ABGQA_OK && bias) r = check_nonpad(nonpad_kv_seqlen, B, max_seq, st, me);
+    if (r == ABGQA_OK && bias) r = check_q_start(q_start, B, st, me);
+    if (r != ABGQA_OK) return r;
+  }
   const hipError_t e = abgqa::launch_prepare(k_cache, v_cache, k_update, v_update, write_indices, B,
                                              Hkv, max_seq, S_new, row_bytes, bias,
                                              bias_dtype == ABGQA_BF16, nonpad_kv_seqlen, q_start,
-                                             slot_kind, S_q, window, (hipStream_t)stream);
+                                             slot_kind, S_q, window, st);
   if (e != hipSuccess) return hip_fail(me, e);
-  return ABGQA_OK;
+  return chk ? check_after(st, me) : ABGQA_OK;
 }
 
 size_t attn_bias_gqa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q,
@@ -193,6 +328,13 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
   p.T = (int)max_seq; p.D = (int)D; p.Dv = (int)D_v; p.window = window; p.scale = scale; p.softcap = softcap;
   p.bias_is_bf16 = (bias_dtype == ABGQA_BF16);
   hipStream_t st = (hipStream_t)stream;
+  const char* me = "attn_bias_gqa_fwd";
+  const bool chk = check_enabled(st);
+  if (chk) {
+    abgqa_status r = check_nonpad(nonpad_kv_seqlen, B, max_seq, st, me);
+    if (r == ABGQA_OK && !bias) r = check_q_start(q_start, B, st, me);
+    if (r != ABGQA_OK) return r;
+  }
 
   hipError_t e;
   const char* path;
@@ -212,6 +354,19 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
       return fail(ABGQA_ERR_WORKSPACE, "attn_bias_gqa_fwd: workspace of %zu bytes needed, %zu given",
                   need, workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 16)) return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: workspace not 16-byte aligned");
+    if (chk) {
+      // the arrival counts this call uses must be zero
+      std::vector<int32_t> cnt((size_t)(B * Hkv));
+      const abgqa_status r = fetch_device(workspace, cnt.size() * sizeof(int32_t), cnt.data(), st, me,
+                                          "workspace");
+      if (r != ABGQA_OK) return r;
+      for (size_t i = 0; i < cnt.size(); ++i)
+        if (cnt[i] != 0)
+          return fail(ABGQA_ERR_WORKSPACE,
+                      "attn_bias_gqa_fwd: ABGQA_CHECK: decode arrival count %zu of the workspace is %d, "
+                      "not 0 (workspace not zero-filled, or a call on it did not complete)",
+                      i, (int)cnt[i]);
+    }
     p.n_split = abgqa::decode_num_splits(B, Hkv, max_seq);
     p.arrive = (int*)workspace;
     p.ws_part = (float*)((char*)workspace + abgqa::kWsCounterBytes);
@@ -219,7 +374,9 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
   } else {
     path = "prefill";
     if (G > 64) return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: more than 64 query heads per KV head");
-    if (abgqa::prefill_lds_bytes((int)(D > D_v ? D : D_v), (int)max_seq) > 160 * 1024)
+    // live key tiles are numbered in 16 bits and listed in LDS beside the K/V stages
+    if ((max_seq + 31) / 32 > 65535 ||
+        abgqa::prefill_lds_bytes((int)(D > D_v ? D : D_v), (int)max_seq) > 160 * 1024)
       return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: max_seq too large for the prefill tile list");
     if (workspace && !aligned(workspace, 16))
       return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: workspace not 16-byte aligned");
@@ -235,8 +392,8 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
     fprintf(stderr, "[abgqa] attn_bias_gqa_fwd path=%s B=%lld Hq=%lld Hkv=%lld S_q=%lld T=%lld D=%lld D_v=%lld %s splits=%d\n",
             path, (long long)B, (long long)Hq, (long long)Hkv, (long long)S_q, (long long)max_seq,
             (long long)D, (long long)D_v, bias ? "bias" : "rules", p.n_split);
-  if (e != hipSuccess) return hip_fail("attn_bias_gqa_fwd", e);
-  return ABGQA_OK;
+  if (e != hipSuccess) return hip_fail(me, e);
+  return chk ? check_after(st, me) : ABGQA_OK;
 }
 
 const char* abgqa_last_error(void) { return g_last_error.c_str(); }

@@ -70,12 +70,13 @@ __device__ __forceinline__ float bias_value<uint32_t>(uint32_t v) { return __uin
 }  // namespace
 
 int decode_num_splits(int64_t B, int64_t Hkv, int64_t max_seq) {
-  // ABGQA_DECODE_SPLITS overrides the heuristic (tuning); the workspace size
-  // query reads the same value, so both agree
-  static const int forced = [] {
-    const char* v = getenv("ABGQA_DECODE_SPLITS");
-    return v ? atoi(v) : 0;
-  }();
+  // ABGQA_DECODE_SPLITS (1..256) overrides the heuristic: rows of very uneven
+  // live length over a long cache can gain from more splits than one per CU.
+  // Read at every call, so the workspace size query and the call agree as long
+  // as the variable does not change between them (a call whose workspace is too
+  // small for its split count is refused).
+  const char* v = getenv("ABGQA_DECODE_SPLITS");
+  const int forced = v ? atoi(v) : 0;
   if (forced > 0) return forced > 256 ? 256 : forced;
   // about one workgroup per CU (256 CUs): fewer, longer-lived workgroups keep
   // their loads streaming; fixed per-workgroup costs (range scan, merge,
@@ -799,19 +800,6 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   }
 }
 
-// Wavefronts per split workgroup. D = 512 takes 8 (two per SIMD, one block
-// in flight each: more bytes in flight than 4 wavefronts with a prefetch
-// buffer); smaller heads take 4 with the prefetch buffer.
-// ABGQA_DECODE_WAVES (4 or 8) overrides the choice (tuning).
-static int decode_waves(int D) {
-  static const int forced = [] {
-    const char* v = getenv("ABGQA_DECODE_WAVES");
-    return v ? atoi(v) : 0;
-  }();
-  if (forced == 4 || forced == 8) return forced;
-  return D >= 512 ? 8 : 4;
-}
-
 template <int D, int DV, int NR, int NW>
 static void launch_decode_nw(const AttnParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.n_split));
@@ -823,16 +811,14 @@ static void launch_decode_nw(const AttnParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((attn_decode_kernel<D, DV, NR, NW, false, uint32_t>), grid, dim3(NW * 64), 0, stream, p);
 }
 
+// Wavefronts per split workgroup: heads of 512 with up to 4 rows per lane
+// group take 8 (two per SIMD, one block in flight each: more bytes in flight
+// than 4 wavefronts with a prefetch buffer, and their registers hold the work
+// without spilling); the rest take 4 with the prefetch buffer.
 template <int D, int DV, int NR>
 static hipError_t launch_decode_d(const AttnParams& p, hipStream_t stream) {
-  // 8 wavefronts (two per SIMD) only where their registers hold the work
-  // without spilling: up to 4 rows per lane group
-  if constexpr (NR <= 4) {
-    if (decode_waves(D > DV ? D : DV) == 8) launch_decode_nw<D, DV, NR, 8>(p, stream);
-    else launch_decode_nw<D, DV, NR, 4>(p, stream);
-  } else {
-    launch_decode_nw<D, DV, NR, 4>(p, stream);
-  }
+  constexpr int NW = (NR <= 4 && (D > DV ? D : DV) >= 512) ? 8 : 4;
+  launch_decode_nw<D, DV, NR, NW>(p, stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) set_launch_detail("decode kernel launch");
   return e;

@@ -631,15 +631,12 @@ static hipError_t launch_prefill_inst(const AttnParams& p, hipStream_t stream) {
   else kern = attn_prefill_kernel<D, NW, kRules, BiasT>;
   // Opt in to the dynamic LDS this launch needs (static LDS of the kernel comes
   // on top, so the request is the exact size, not the CU's 160 KiB).
-  static size_t lds_set = 0;  // per instantiation
-  if (lds > lds_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    const hipError_t e = opt_in_dynamic_lds((const void*)kern, lds);
     if (e != hipSuccess) {
       set_launch_detail("hipFuncSetAttribute(MaxDynamicSharedMemorySize)");
       return e;
     }
-    lds_set = lds;
   }
   const dim3 grid((unsigned)((int64_t)n_qt * p.B * p.Hkv));
   hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, stream, p, n_qt);
@@ -668,21 +665,11 @@ static hipError_t launch_prefill_d(const AttnParams& p, hipStream_t stream) {
   }
 }
 
-// ABGQA_PREFILL_PATH=reg keeps every launch on the register-staged kernels of
-// this file (comparison and tuning); by default shapes whose rows allow 16-byte
-// direct-to-LDS fetches take attn_prefill_dma.hip.
-static bool force_register_path() {
-  static const bool v = [] {
-    const char* e = getenv("ABGQA_PREFILL_PATH");
-    return e != nullptr && e[0] == 'r';
-  }();
-  return v;
-}
-
 hipError_t launch_attn_prefill(const AttnParams& p, hipStream_t stream) {
   if (p.Dv != p.D)   // only the direct-to-LDS kernel has a V head size of its own
     return prefill_dma_supported(p) ? launch_attn_prefill_dma(p, stream) : hipErrorInvalidValue;
-  if (!force_register_path() && prefill_dma_supported(p)) return launch_attn_prefill_dma(p, stream);
+  // rows that allow 16-byte direct-to-LDS fetches take attn_prefill_dma.hip
+  if (prefill_dma_supported(p)) return launch_attn_prefill_dma(p, stream);
   if (prefill_lds_bytes(p.D, p.T) > 160 * 1024) return hipErrorInvalidValue;
   switch (p.D) {
     case 64: return launch_prefill_d<64>(p, stream);

@@ -9,26 +9,6 @@ namespace abgqa {
 
 namespace {
 
-// ABGQA_PREFILL_CFG (tuning): "32x2", "32x4", "16x4", "16x8" picks rows per
-// wavefront x wavefronts per workgroup ("32x2r", "32x4r": Q^T in registers;
-// "16x8k": 8 wavefronts of 16 rows as 4 row groups x 2 key halves);
-// otherwise the default below.
-static int prefill_cfg() {
-  static const int v = [] {
-    const char* e = getenv("ABGQA_PREFILL_CFG");
-    if (!e) return 0;
-    if (!strcmp(e, "32x2")) return 1;
-    if (!strcmp(e, "32x4")) return 2;
-    if (!strcmp(e, "16x4")) return 3;
-    if (!strcmp(e, "16x8")) return 4;
-    if (!strcmp(e, "32x2r")) return 5;
-    if (!strcmp(e, "32x4r")) return 6;
-    if (!strcmp(e, "16x8k")) return 7;
-    return 0;
-  }();
-  return v;
-}
-
 // Rows per wavefront x wavefronts per workgroup for a shape. D = 512: 4
 // wavefronts of 32 rows (Q^T in registers, O^T in the accumulation registers):
 // each K/V tile fetched once for 128 rows, each LDS read feeding a 32-row MFMA.
@@ -37,9 +17,9 @@ static int prefill_cfg() {
 // wavefronts, but two wavefronts per SIMD, each hiding the other's LDS and
 // softmax latency (a prefill chunk rarely has the rows for two 16-row
 // wavefronts per SIMD otherwise). D = 128: 4 wavefronts of 16 rows keep all
-// four SIMDs of a CU busy with one workgroup per CU. D = 64
-// (a tile too small to split four ways): 32-row wavefronts, 4 of them when
-// that still gives a workgroup per CU.
+// four SIMDs of a CU busy with one workgroup per CU. D = 64 (a tile too small
+// to split four ways): 32-row wavefronts, 4 of them when that still gives a
+// workgroup per CU.
 // the (D, DV) pairs with a V head size of their own that the kernel is built
 // for (D = 256 beside DV = 512, and the reverse)
 bool dma_dv_pair(int D, int Dv) { return (D == 256 && Dv == 512) || (D == 512 && Dv == 256); }
@@ -51,59 +31,28 @@ bool dma_dv_pair(int D, int Dv) { return (D == 256 && Dv == 512) || (D == 512 &&
 // DV = 512: 63 us against 78; long-prefill shape with DV = 256 (1024
 // workgroups of 32-row wavefronts): 298 us against 403.
 int dv_rows(int64_t B, int64_t Hkv, int64_t S_q, int64_t G) {
-  const int cfg = prefill_cfg();
-  if (cfg == 3) return 64;    // "16x4"
-  if (cfg == 6) return 128;   // "32x4r"
   const int64_t wg32 = B * Hkv * ((S_q * G + 127) / 128);
   return wg32 >= 256 ? 128 : 64;
 }
 
-enum class DmaCfg { k16x4, k16x8, k32x2, k32x4, k32x2r, k32x4r, k16x8k };
-
-DmaCfg dma_cfg(int D, int64_t B, int64_t Hkv, int64_t S_q, int64_t G) {
-  const int cfg = prefill_cfg();
-  if (D >= 512) {
-    if (cfg == 4) return DmaCfg::k16x8;
-    if (cfg == 3) return DmaCfg::k16x4;
-    return DmaCfg::k32x4r;
-  }
-  if (D == 256 && cfg == 5) return DmaCfg::k32x2r;
-  if (D == 256 && cfg == 6) return DmaCfg::k32x4r;
-  if (cfg == 1) return DmaCfg::k32x2;
-  if (cfg == 2) return DmaCfg::k32x4;
-  if (D >= 128 && cfg == 7) return DmaCfg::k16x8k;
-  if (D >= 128 && cfg == 4) return DmaCfg::k16x8;
-  if (D >= 128 && cfg == 3) return DmaCfg::k16x4;
-  if (D == 256) return DmaCfg::k16x8k;
-  if (D >= 128) return DmaCfg::k16x4;
+// query rows per workgroup of the D = DV kernels (see launch_dma_d)
+int dma_rows(int D, int64_t B, int64_t Hkv, int64_t S_q, int64_t G) {
+  if (D >= 512) return 128;
+  if (D >= 128) return 64;
   const int64_t wg4 = B * Hkv * ((S_q * G + 127) / 128);
-  return wg4 >= 256 ? DmaCfg::k32x4 : DmaCfg::k32x2;
-}
-
-int dma_rows(DmaCfg c) {
-  return (c == DmaCfg::k16x4 || c == DmaCfg::k32x2 || c == DmaCfg::k32x2r || c == DmaCfg::k16x8k) ? 64
-                                                                                                 : 128;
+  return wg4 >= 256 ? 128 : 64;
 }
 
 template <int D>
 hipError_t launch_dma_d(const AttnParams& p, hipStream_t stream) {
-  const DmaCfg c = dma_cfg(D, p.B, p.Hkv, p.S_q, p.G);
   if constexpr (D >= 512) {
-    if (c == DmaCfg::k16x8) return launch_dma_v<D, 16, 8>(p, stream);
-    if (c == DmaCfg::k16x4) return launch_dma_v<D, 16, 4>(p, stream);
     return launch_attn_prefill_dma_qreg(p, 4, stream);
+  } else if constexpr (D == 256) {
+    return launch_dma_v<D, 16, 8, true, 2>(p, stream);
+  } else if constexpr (D == 128) {
+    return launch_dma_v<D, 16, 4>(p, stream);
   } else {
-    if constexpr (D == 256) {
-      if (c == DmaCfg::k32x2r) return launch_attn_prefill_dma_qreg(p, 2, stream);
-      if (c == DmaCfg::k32x4r) return launch_attn_prefill_dma_qreg(p, 4, stream);
-    }
-    if (c == DmaCfg::k32x2) return launch_dma_v<D, 32, 2>(p, stream);
-    if (c == DmaCfg::k32x4) return launch_dma_v<D, 32, 4>(p, stream);
-    if constexpr (D >= 128) {   // a tile must split evenly over the wavefronts
-      if (c == DmaCfg::k16x8) return launch_dma_v<D, 16, 8>(p, stream);
-      if (c == DmaCfg::k16x8k) return launch_dma_v<D, 16, 8, true, 2>(p, stream);
-      return launch_dma_v<D, 16, 4>(p, stream);
-    }
+    if (dma_rows(D, p.B, p.Hkv, p.S_q, p.G) == 128) return launch_dma_v<D, 32, 4>(p, stream);
     return launch_dma_v<D, 32, 2>(p, stream);
   }
 }
@@ -137,7 +86,7 @@ size_t prefill_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q, 
   if (D_v != D && !dma_dv_pair((int)D, (int)D_v)) return 0;
   const int64_t G = Hq / Hkv;
   if (G < 2 || G > 64 || max_seq > 32768) return 0;
-  const int64_t rows = D_v != D ? dv_rows(B, Hkv, S_q, G) : dma_rows(dma_cfg((int)D, B, Hkv, S_q, G));
+  const int64_t rows = D_v != D ? dv_rows(B, Hkv, S_q, G) : dma_rows((int)D, B, Hkv, S_q, G);
   const int64_t mq = rows / G;
   const int64_t n_qt = (S_q + mq - 1) / mq;
   const int64_t n_words = (num_tiles((int)max_seq) + 31) / 32;

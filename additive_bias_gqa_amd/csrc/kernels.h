@@ -12,6 +12,11 @@ namespace abgqa {
 // cleared by the C ABI when it reports ABGQA_ERR_HIP).
 void set_launch_detail(const char* what);
 
+// Opts kernel `kern` in to `lds` bytes of dynamic LDS on the current device
+// (hipFuncSetAttribute, MaxDynamicSharedMemorySize), once per kernel, device
+// and larger size; safe to call from several threads.
+hipError_t opt_in_dynamic_lds(const void* kern, size_t lds);
+
 hipError_t launch_scatter(void* cache, const void* update, const int64_t* write_indices,
                           int64_t B, int64_t H, int64_t max_seq, int64_t S_new,
                           int64_t row_bytes, hipStream_t stream);

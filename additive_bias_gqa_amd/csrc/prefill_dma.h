@@ -1165,15 +1165,12 @@ hipError_t launch_dma_inst(const AttnParams& p, hipStream_t stream) {
   auto kern = attn_prefill_dma_kernel<D, RW, NW, kRules, BiasT, kQReg, KS, DV>;
   // opt in to exactly the dynamic LDS of this launch (the kernel's static LDS
   // comes on top)
-  static size_t lds_set = 0;   // per instantiation
-  if (lds > lds_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    const hipError_t e = opt_in_dynamic_lds((const void*)kern, lds);
     if (e != hipSuccess) {
       set_launch_detail("hipFuncSetAttribute(MaxDynamicSharedMemorySize), direct-to-LDS prefill");
       return e;
     }
-    lds_set = lds;
   }
   AttnParams pp = p;
   pp.tilemap = nullptr;

@@ -132,3 +132,38 @@ def test_fused_prepare_validation(lib):
     assert f(None, None, None, None, None, 1, 1, 8, 0, 64, 1, FAKE, 4, FAKE, None, None, 1, 0, None) == UNSUPPORTED
     assert f(None, None, None, None, None, 1, 1, 8, 0, 64, 1, FAKE, 1, FAKE, None, None, 0, 0, None) == INVALID
     assert f(None, None, None, None, None, 0, 1, 8, 0, 64, 1, None, 1, None, None, None, 1, 0, None) == INVALID
+
+
+def test_prefill_tile_index_limit(lib):
+    """Live key tiles of a prefill are numbered in 16 bits: a cache of more than
+    65535 tiles of 32 keys is refused before any launch (D = 64 leaves room in
+    LDS for such a tile list, so the size of the list alone would not refuse it)."""
+    T = 32 * 65537
+    args = dict(out=FAKE, q=FAKE + 4096, k=FAKE + 8192, v=FAKE + 12288, nonpad=FAKE + 16384,
+                B=1, Hq=4, Hkv=2, S_q=32, T=T, D=64, Dv=64)
+    assert _fwd(lib, **args) == UNSUPPORTED
+    assert "max_seq too large for the prefill tile list" in ab.abgqa_last_error()
+    args.update(T=32 * 65536)
+    assert _fwd(lib, **args) == UNSUPPORTED
+
+
+def test_workspace_per_stream():
+    """The binding's default workspace is one per (device, stream): two streams
+    never share one, a stream reuses its own, a buffer that grows leaves the
+    old one alive (a captured graph may still hold its address), and growth
+    during graph capture is refused."""
+    import torch
+    ab._workspaces.clear()
+    alloc = lambda n: torch.zeros(n, dtype=torch.uint8)
+    a = ab._workspace_for((0, 111), 1000, False, alloc)
+    b = ab._workspace_for((0, 222), 1000, False, alloc)
+    assert a.data_ptr() != b.data_ptr()
+    assert ab._workspace_for((0, 111), 800, False, alloc) is a
+    assert ab._workspace_for((0, 111), 1000, True, alloc) is a      # no growth: fine under capture
+    big = ab._workspace_for((0, 111), 5000, False, alloc)
+    assert big.numel() >= 5000 and big is not a
+    assert any(t is a for t in ab._workspaces[(0, 111)])           # the old buffer is kept
+    assert ab._workspace_for((1, 111), 100, False, alloc) is not a  # another device
+    with pytest.raises(RuntimeError, match="during graph capture"):
+        ab._workspace_for((0, 222), 4000, True, alloc)
+    ab._workspaces.clear()
