@@ -188,17 +188,30 @@ _workspaces: dict = {}
 
 
 def _workspace(device: torch.device, nbytes: int) -> torch.Tensor | None:
-    """A per-device workspace, grown on demand (calls on one device's current
-    stream are ordered, so they can share it). Zero-filled when allocated: its
-    first bytes are the decode kernel's arrival counts, which every call
-    leaves at zero."""
+    """The workspace of the current stream on `device`, grown on demand. One per
+    (device, stream): calls on one stream are ordered and can share it, calls on
+    two streams may overlap and must not. Zero-filled when allocated: its first
+    bytes are the decode kernel's arrival counts, which every call leaves at
+    zero. A buffer that has been replaced stays alive (a captured graph may
+    still use it), and none is allocated while the stream is being captured."""
     if nbytes == 0:
         return None
-    key = (device.type, device.index)
-    ws = _workspaces.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    return _workspace_for(key, nbytes, torch.cuda.is_current_stream_capturing(),
+                          lambda n: torch.zeros(n, dtype=torch.uint8, device=device))
+
+
+def _workspace_for(key, nbytes: int, capturing: bool, alloc):
+    held = _workspaces.setdefault(key, [])
+    if held and held[-1].numel() >= nbytes:
+        return held[-1]
+    if capturing:
+        raise RuntimeError(
+            f"attn_bias_gqa_fwd: the stream's workspace must grow to {nbytes} bytes during graph "
+            f"capture; make one call of this shape before capturing, or pass a zero-filled "
+            f"workspace of attn_bias_gqa_workspace_bytes() bytes")
+    ws = alloc(nbytes)
+    held.append(ws)
     return ws
 
 
@@ -213,10 +226,10 @@ def attn_bias_gqa_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     reads KV head h // (Hq // Hkv)); cap(x) = softcap * tanh(x / softcap) when
     softcap > 0, else x. bias=None evaluates the static-cache rules (nonpad,
     q_start, slot_kind, window) inside the kernel instead. V may have another
-    head size than Q and K (the output takes V's). Without `workspace`, a
-    per-device workspace is allocated (zero-filled) on the first call that
-    needs it: make that call outside HIP graph capture, or pass a zero-filled
-    `workspace` of attn_bias_gqa_workspace_bytes() bytes."""
+    head size than Q and K (the output takes V's). Without `workspace`, the
+    current stream's own workspace is used, allocated (zero-filled) by the first
+    call that needs it: make that call outside HIP graph capture, or pass a
+    zero-filled `workspace` of attn_bias_gqa_workspace_bytes() bytes."""
     if q.dim() != 4 or k_cache.dim() != 4 or v_cache.dim() != 4:
         raise ValueError("q must be [B, Hq, S_q, D], k_cache [B, Hkv, max_seq, D], "
                          "v_cache [B, Hkv, max_seq, D_v]")

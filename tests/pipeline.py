@@ -25,6 +25,47 @@ def dev(t):
     return None if t is None else t.to("cuda")
 
 
+# Every output and scratch buffer a GPU test hands to the library starts out as
+# a NaN with a distinctive payload, so a kernel that leaves an element unwritten
+# (a skipped query tile, a skipped merge) fails the finiteness check of
+# check_parity instead of passing on memory an earlier call filled correctly.
+POISON = {torch.bfloat16: (torch.int16, 0x7FC1), torch.float32: (torch.int32, 0x7FC00001)}
+
+
+def poisoned(shape, dtype):
+    ibits, pattern = POISON[dtype]
+    return torch.empty(shape, dtype=dtype, device="cuda").view(ibits).fill_(pattern).view(dtype)
+
+
+def poison_(t: torch.Tensor) -> torch.Tensor:
+    ibits, pattern = POISON[t.dtype]
+    t.view(ibits).fill_(pattern)
+    return t
+
+
+def poisoned_workspace(nbytes: int):
+    """Arrival counts (the first 64 KiB) zero, as the library requires; every
+    byte after them 0xFF (a NaN as fp32), so a partial record or live-tile map
+    word that a call reads without having written it shows."""
+    if nbytes == 0:
+        return None
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    ws[:min(nbytes, 65536)] = 0
+    return ws
+
+
+def fwd(q, k, v, bias, nonpad, scale, out=None, workspace=None, **kw):
+    """attn_bias_gqa_fwd with a poisoned output and a poisoned workspace of the
+    size the shape needs, unless the caller passes its own."""
+    B, Hq, S_q, D = q.shape
+    Hkv, T, Dv = k.shape[1], k.shape[2], v.shape[3]
+    if out is None:
+        out = poisoned((B, Hq, S_q, Dv), q.dtype)
+    if workspace is None:
+        workspace = poisoned_workspace(ab.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, T, D, Dv))
+    return ab.attn_bias_gqa_fwd(q, k, v, bias, nonpad, scale, out=out, workspace=workspace, **kw)
+
+
 def gpu_step(w: wl.Workload, step: wl.Step, k_dev, v_dev, rules: bool = False,
              bias_dtype: torch.dtype | None = None, default_q_start: bool = False,
              softcap: float = 0.0):
@@ -39,10 +80,11 @@ def gpu_step(w: wl.Workload, step: wl.Step, k_dev, v_dev, rules: bool = False,
     kind = dev(step.slot_kind)
     bias = None
     if not rules:
+        bt = bias_dtype or w.dtype
         bias = ab.build_static_cache_bias(nonpad, q_start, kind, step.S_q, w.max_seq, w.window,
-                                          dtype=bias_dtype or w.dtype)
-    out = ab.attn_bias_gqa_fwd(dev(step.q), k_dev, v_dev, bias, nonpad, w.scale,
-                               q_start=q_start, slot_kind=kind, window=w.window, softcap=softcap)
+                                          dtype=bt, out=poisoned((w.B, 1, step.S_q, w.max_seq), bt))
+    out = fwd(dev(step.q), k_dev, v_dev, bias, nonpad, w.scale,
+              q_start=q_start, slot_kind=kind, window=w.window, softcap=softcap)
     return bias, out
 
 
@@ -90,13 +132,23 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def sample_rows(w: wl.Workload, step: wl.Step, n: int, seed: int) -> np.ndarray:
-    """Flat (b*Hq + h)*S_q + s row indices: the first and last rows of every
-    batch entry plus n random ones, sorted and unique."""
-    B, Hq, S_q = w.B, w.Hq, step.S_q
+def tile_rows(w: wl.Workload, step: wl.Step, tokens: int, seed: int) -> np.ndarray:
+    """Flat (b*Hq + h)*S_q + s row indices: one random row (a random head of the
+    group, a random token of the tile) of every (batch row, KV head, tile of
+    `tokens` query tokens) - one per workgroup of a prefill kernel whose
+    workgroups hold `tokens` tokens of the G heads of one KV head - plus the
+    first and last row of every (batch row, query head); sorted and unique."""
+    B, Hq, Hkv, S_q = w.B, w.Hq, w.Hkv, step.S_q
+    G = Hq // Hkv
     rng = np.random.Generator(np.random.PCG64(seed))
-    picks = set(rng.integers(0, B * Hq * S_q, size=n).tolist())
+    picks = set()
     for b in range(B):
-        picks.add(b * Hq * S_q)
-        picks.add((b + 1) * Hq * S_q - 1)
+        for hk in range(Hkv):
+            for t0 in range(0, S_q, tokens):
+                h = hk * G + int(rng.integers(0, G))
+                s = int(rng.integers(t0, min(t0 + tokens, S_q)))
+                picks.add((b * Hq + h) * S_q + s)
+        for h in range(Hq):
+            picks.add((b * Hq + h) * S_q)
+            picks.add((b * Hq + h) * S_q + S_q - 1)
     return np.array(sorted(picks), dtype=np.int64)

@@ -14,8 +14,8 @@ import torch
 import additive_bias_gqa_amd as ab
 import oracle
 from additive_bias_gqa_amd import workloads as wl
-from pipeline import (announce, check_parity, dead_rows, dev, gpu_step, oracle_step,
-                      sample_rows, to_f64)
+from pipeline import (announce, check_parity, dead_rows, dev, fwd, gpu_step, oracle_step, poison_,
+                      poisoned, poisoned_workspace, tile_rows, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -211,7 +211,7 @@ def test_softcap_fp32_and_masked_poison():
     bias[:, 0, 0, 10] = float("-inf")
     v_poison = v.clone()
     v_poison[:, :, 10] = 1e30
-    got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v_poison), dev(bias), dev(nonpad), 0.0625, softcap=cap)
+    got = fwd(dev(q), dev(k), dev(v_poison), dev(bias), dev(nonpad), 0.0625, softcap=cap)
     ref2 = oracle.attention(q, k, v, bias, nonpad, 0.0625, softcap=cap)
     check_parity(to_f64(got), ref2, torch.bfloat16, what="softcap/poison")
 
@@ -251,8 +251,8 @@ def test_prefill_live_tile_map(D, bias_dtype):
     ref = oracle.attention(q, k, v, bias, nonpad, 1.0 / math.sqrt(D))
     args = (dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 1.0 / math.sqrt(D))
     assert ab.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, T, D) > 0
-    o_map = ab.attn_bias_gqa_fwd(*args)
-    o_scan = ab.attn_bias_gqa_fwd(*args, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    o_map = fwd(*args)
+    o_scan = fwd(*args, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
     assert torch.equal(o_map.view(torch.int16), o_scan.view(torch.int16))
     check_parity(to_f64(o_map), ref, torch.bfloat16,
                  dead_rows(bias.float().numpy(), nonpad, Hq), f"tilemap/D{D}")
@@ -275,9 +275,9 @@ def test_decode_uneven_rows(D, Hq, Hkv, variant):
     announce(f"decode uneven rows D={D} Hq={Hq} Hkv={Hkv} {variant}")
     ref = oracle.attention(q, k, v, bias, nonpad, 1.0 / math.sqrt(D))
     if variant == "bias":
-        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 1.0 / math.sqrt(D))
+        got = fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 1.0 / math.sqrt(D))
     else:
-        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), None, dev(nonpad), 1.0 / math.sqrt(D),
+        got = fwd(dev(q), dev(k), dev(v), None, dev(nonpad), 1.0 / math.sqrt(D),
                                    q_start=dev(q_start), window=0)
     check_parity(to_f64(got), ref, torch.bfloat16,
                  dead_rows(bias.float().numpy(), nonpad, Hq), f"uneven/{variant}")
@@ -300,7 +300,7 @@ def test_shared_workspace_counts():
         q_start = nonpad - 1
         bias = torch.from_numpy(oracle.bias(nonpad, q_start, None, 1, T, 128)).to(torch.bfloat16)
         assert ab.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, 1, T, D) <= ws.numel()
-        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 1.0 / math.sqrt(D),
+        got = fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 1.0 / math.sqrt(D),
                                    workspace=ws)
         ref = oracle.attention(q, k, v, bias, nonpad, 1.0 / math.sqrt(D))
         check_parity(to_f64(got), ref, torch.bfloat16, dead_rows(bias.float().numpy(), nonpad, Hq),
@@ -323,7 +323,7 @@ def test_shared_workspace_counts():
     q_start = (nonpad - S_q).clamp(min=0)
     bias = torch.from_numpy(oracle.bias(nonpad, q_start, None, S_q, T, 64)).to(torch.bfloat16)
     assert ab.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, T, D) > 65536
-    got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 1.0 / math.sqrt(D), workspace=ws)
+    got = fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 1.0 / math.sqrt(D), workspace=ws)
     ref = oracle.attention(q, k, v, bias, nonpad, 1.0 / math.sqrt(D))
     check_parity(to_f64(got), ref, torch.bfloat16, dead_rows(bias.float().numpy(), nonpad, Hq), "shared ws prefill")
     counts_zero()
@@ -361,9 +361,9 @@ def test_value_head_size(D, Dv, S_q, dtype, variant):
     scale = 1.0 / math.sqrt(D)
     ref = oracle.attention(q, k, v, bias, nonpad, scale)
     if variant == "bias":
-        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), scale)
+        got = fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), scale)
     else:
-        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale,
+        got = fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale,
                                    q_start=dev(q_start), slot_kind=dev(kind), window=window)
     assert got.shape == (B, Hq, S_q, Dv)
     check_parity(to_f64(got), ref, dtype, dead_rows(bias.float().numpy(), nonpad, Hq), f"Dv/{variant}")
@@ -373,10 +373,11 @@ def test_value_head_size(D, Dv, S_q, dtype, variant):
                                          ("bf16", 20.0)])
 @pytest.mark.parametrize("D,Dv", [(256, 512), (512, 256)])
 def test_value_head_size_prefill_mfma(D, Dv, variant, cap):
-    """Prefill with V's own head size on the direct-to-LDS matrix-core kernel:
-    five query tiles (the last ragged), eleven key tiles (the last partial),
-    a batch row whose nonpad ends inside a tile, pads, an image block, and the
-    live-tile map of the bias variant (the binding's workspace holds it)."""
+    """Prefill with V's own head size on the direct-to-LDS matrix-core kernel
+    (64-row workgroups here: 16 query tokens of the 4 heads of a KV head): ten
+    query tiles (the last ragged), eleven key tiles (the last partial), a batch
+    row whose nonpad ends inside a tile, pads, an image block, and the
+    live-tile map of the bias variant (the workspace holds it)."""
     rng = wl.rng_for(680 + D + Dv + int(cap))
     B, Hq, Hkv, T, S_q = 3, 8, 2, 344, 150
     q = wl.normal(rng, (B, Hq, S_q, D), torch.bfloat16)
@@ -395,10 +396,10 @@ def test_value_head_size_prefill_mfma(D, Dv, variant, cap):
     scale = 1.0 / math.sqrt(D)
     ref = oracle.attention(q, k, v, bias, nonpad, scale, softcap=cap)
     if variant == "rules":
-        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale, q_start=dev(q_start),
+        got = fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale, q_start=dev(q_start),
                                    slot_kind=dev(kind), window=window, softcap=cap)
     else:
-        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), scale, softcap=cap)
+        got = fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), scale, softcap=cap)
     assert got.shape == (B, Hq, S_q, Dv)
     check_parity(to_f64(got), ref, torch.bfloat16, dead_rows(bias.float().numpy(), nonpad, Hq),
                  f"Dv prefill/{variant}/cap{cap}")
@@ -406,10 +407,11 @@ def test_value_head_size_prefill_mfma(D, Dv, variant, cap):
 
 @pytest.mark.parametrize("D,Dv", [(256, 512), (512, 256)])
 def test_value_head_size_prefill_shapes(D, Dv):
-    """The same kernel over group sizes and tile counts: G = 2 with a chunk just
-    above the decode limit (one query tile, two key tiles), G = 16 (8 tokens
-    per query tile, nine tiles), G = 2 with 64-token tiles over 32 key tiles;
-    bias and rules variants each."""
+    """The same kernel (64-row workgroups) over group sizes and tile counts:
+    G = 2 with a chunk just above the decode limit (one query tile, two key
+    tiles), G = 16 (4 tokens per query tile, eighteen tiles), G = 2 with
+    32-token tiles (ten, the last ragged) over 32 key tiles; bias and rules
+    variants each."""
     for idx, (Hq, Hkv, S_q, T, npv) in enumerate([(16, 8, 9, 64, [64, 41]),
                                                    (32, 2, 70, 520, [520, 333]),
                                                    (4, 2, 300, 1024, [1000, 300])]):
@@ -428,9 +430,9 @@ def test_value_head_size_prefill_shapes(D, Dv):
         ref = oracle.attention(q, k, v, bias, nonpad, scale)
         dead = dead_rows(bias.float().numpy(), nonpad, Hq)
         announce(f"value head size prefill shapes D={D} Dv={Dv} Hq={Hq} Hkv={Hkv} S_q={S_q} T={T}")
-        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), scale)
+        got = fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), scale)
         check_parity(to_f64(got), ref, torch.bfloat16, dead, f"Dv shapes/bias/{idx}")
-        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale, q_start=dev(q_start),
+        got = fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale, q_start=dev(q_start),
                                    slot_kind=dev(kind), window=window)
         check_parity(to_f64(got), ref, torch.bfloat16, dead, f"Dv shapes/rules/{idx}")
 
@@ -513,9 +515,9 @@ def test_decode_many_rows_vector_path(variant):
     bias = torch.from_numpy(oracle.bias(nonpad, q_start, None, 1, T, 16)).to(torch.bfloat16)
     announce(f"decode B*Hkv={B * Hkv} {variant}")
     if variant == "bias":
-        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 0.125)
+        got = fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 0.125)
     else:
-        got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), None, dev(nonpad), 0.125, q_start=dev(q_start),
+        got = fwd(dev(q), dev(k), dev(v), None, dev(nonpad), 0.125, q_start=dev(q_start),
                                    window=16)
     ref = oracle.attention(q, k, v, bias, nonpad, 0.125)
     check_parity(to_f64(got), ref, torch.bfloat16, dead_rows(bias.float().numpy(), nonpad, Hq),
@@ -546,7 +548,7 @@ def test_maskless_static_cache(B, Hq, Hkv, D, T, S_q, causal):
     scale = 1.0 / math.sqrt(D)
     ws_bytes = ab.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, T, D)
     ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
-    out = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale, q_start=dev(qs),
+    out = fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale, q_start=dev(qs),
                                slot_kind=None, window=0, workspace=ws)
     bias = oracle.bias(nonpad, qs, None, S_q, T, 0)
     ref = oracle.attention(q, k, v, bias, nonpad, scale)
@@ -569,7 +571,7 @@ def test_random_finite_bias(S_q):
     bias[0, 0, 0, :] = float("-inf")          # one fully-masked row
     announce(f"random finite bias S_q={S_q}")
     ref = oracle.attention(q, k, v, bias, nonpad, 1 / math.sqrt(D))
-    out = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 1 / math.sqrt(D))
+    out = fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 1 / math.sqrt(D))
     bias64 = bias.to(torch.float64).numpy()
     check_parity(to_f64(out), ref, torch.bfloat16, dead_rows(bias64, nonpad, Hq), f"randbias/{S_q}")
 
@@ -614,7 +616,7 @@ def test_graph_replay_decode_and_prefill(variant):
     zero after every replay."""
     dec = wl.decode_sliding(B=4, Hq=16, Hkv=8, D=256, max_seq=1024, window=256)
     pre = SMALL["prefill_vision"]()
-    ws = torch.zeros(8 << 20, dtype=torch.uint8, device="cuda")
+    ws = poisoned_workspace(8 << 20)
     jobs = []
     for w in (dec, pre):
         st = w.steps[0]
@@ -625,7 +627,7 @@ def test_graph_replay_decode_and_prefill(variant):
         q, npd, qs = dev(st.q), dev(st.nonpad), dev(st.q_start)
         kind = None if st.slot_kind is None else dev(st.slot_kind)
         bias = ab.build_static_cache_bias(npd, qs, kind, st.S_q, w.max_seq, w.window, dtype=w.dtype)
-        out = torch.empty((w.B, w.Hq, st.S_q, w.Dv), dtype=w.dtype, device="cuda")
+        out = poisoned((w.B, w.Hq, st.S_q, w.Dv), w.dtype)
         jobs.append((w, q, k, v, bias, npd, qs, kind, out))
 
     def run_all():
@@ -650,7 +652,7 @@ def test_graph_replay_decode_and_prefill(variant):
     torch.cuda.synchronize()
     for rep in range(4):
         for j in jobs:
-            j[-1].fill_(0)
+            poison_(j[-1])
         g.replay()
         torch.cuda.synchronize()
         for j, ref in zip(jobs, eager):
@@ -677,10 +679,10 @@ def test_long_cache(S_q, T, D):
     bias = torch.from_numpy(oracle.bias(nonpad, q_start, None, S_q, T, 3000)).to(torch.bfloat16)
     announce(f"long cache S_q={S_q} T={T} D={D}")
     scale = 1.0 / math.sqrt(D)
-    got = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), scale)
+    got = fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), scale)
     ref = oracle.attention(q, k, v, bias, nonpad, scale)
     check_parity(to_f64(got), ref, torch.bfloat16, dead_rows(bias.float().numpy(), nonpad, Hq), f"long/{T}")
-    got_r = ab.attn_bias_gqa_fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale, q_start=dev(q_start),
+    got_r = fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale, q_start=dev(q_start),
                                  window=3000)
     check_parity(to_f64(got_r), ref, torch.bfloat16, dead_rows(bias.float().numpy(), nonpad, Hq), f"long/{T}/rules")
 
@@ -697,6 +699,75 @@ def test_prefill_cache_too_long_raises():
         ab.attn_bias_gqa_fwd(q, k, v, None, nonpad, 0.05)
 
 
+@pytest.mark.parametrize("splits", [1, 2, 3, 5, 8, 16, 64])
+def test_decode_split_sweep(splits, monkeypatch):
+    """Decode with a forced split count (ABGQA_DECODE_SPLITS, read at every
+    call): one split per row (the direct write), a few, and more splits than a
+    short row has 16-key blocks (splits without keys merge as empty); rows of
+    very different live length; both variants; poisoned workspace and output."""
+    monkeypatch.setenv("ABGQA_DECODE_SPLITS", str(splits))
+    rng = wl.rng_for(750)
+    B, Hq, Hkv, T, D = 5, 8, 2, 900, 256
+    q = wl.normal(rng, (B, Hq, 1, D), torch.bfloat16)
+    k = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    v = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
+    nonpad = torch.tensor([T, 1, 333, 0, 40], dtype=torch.int64)
+    q_start = (nonpad - 1).clamp(min=0)
+    bias = torch.from_numpy(oracle.bias(nonpad, q_start, None, 1, T, 300)).to(torch.bfloat16)
+    ref = oracle.attention(q, k, v, bias, nonpad, 1.0 / math.sqrt(D))
+    dead = dead_rows(bias.float().numpy(), nonpad, Hq)
+    announce(f"decode split sweep splits={splits}")
+    got = fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), 1.0 / math.sqrt(D))
+    check_parity(to_f64(got), ref, torch.bfloat16, dead, f"splits{splits}/bias")
+    got_r = fwd(dev(q), dev(k), dev(v), None, dev(nonpad), 1.0 / math.sqrt(D), q_start=dev(q_start),
+                window=300)
+    check_parity(to_f64(got_r), ref, torch.bfloat16, dead, f"splits{splits}/rules")
+
+
+def test_check_mode(monkeypatch):
+    """ABGQA_CHECK=1: device-side index values are validated before anything is
+    enqueued (the kernels never see the bad values), decode arrival counts of
+    the workspace must be zero, and valid calls still give the oracle's result."""
+    monkeypatch.setenv("ABGQA_CHECK", "1")
+    rng = wl.rng_for(760)
+    B, Hq, Hkv, T, D = 2, 8, 2, 128, 256
+    q = dev(wl.normal(rng, (B, Hq, 1, D), torch.bfloat16))
+    k = dev(wl.normal(rng, (B, Hkv, T, D), torch.bfloat16))
+    v = dev(wl.normal(rng, (B, Hkv, T, D), torch.bfloat16))
+    announce("check mode: bad device values refused")
+    with pytest.raises(RuntimeError, match="ABGQA_CHECK: nonpad_kv_seqlen\\[1\\] = 129"):
+        fwd(q, k, v, None, dev(torch.tensor([5, T + 1])), 0.1)
+    with pytest.raises(RuntimeError, match="ABGQA_CHECK: nonpad_kv_seqlen\\[0\\] = -1"):
+        ab.build_static_cache_bias(dev(torch.tensor([-1, 3])), None, None, 1, T, 0)
+    with pytest.raises(RuntimeError, match="ABGQA_CHECK: q_start\\[0\\] = -3"):
+        fwd(q, k, v, None, dev(torch.tensor([5, 9])), 0.1, q_start=dev(torch.tensor([-3, 2])))
+    upd = dev(wl.normal(rng, (B, Hkv, 4, D), torch.bfloat16))
+    with pytest.raises(RuntimeError, match="ABGQA_CHECK: write_indices\\[1\\] = 125"):
+        ab.kv_tensor_scatter(k, upd, dev(torch.tensor([0, 125])))
+    with pytest.raises(RuntimeError, match="ABGQA_CHECK: write_indices\\[0\\] = -1"):
+        ab.kv_scatter_and_bias(k, v, upd, upd, dev(torch.tensor([-1, 0])), dev(torch.tensor([3, 4])),
+                               None, None, 4, 0, bias=torch.empty((B, 1, 4, T), dtype=torch.bfloat16,
+                                                                   device="cuda"))
+    need = ab.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, 1, T, D)
+    ws = poisoned_workspace(need)
+    ws[0:4] = torch.tensor([7, 0, 0, 0], dtype=torch.uint8)    # arrival count 0 left at 7
+    with pytest.raises(RuntimeError, match="ABGQA_CHECK: decode arrival count 0"):
+        fwd(q, k, v, None, dev(torch.tensor([5, 9])), 0.1, workspace=ws)
+    # a good scatter and decode under the check, against the oracle
+    announce("check mode: valid calls")
+    nonpad = torch.tensor([70, T], dtype=torch.int64)
+    k_h, v_h = k.cpu(), v.cpu()
+    ab.kv_tensor_scatter(k, upd, dev(torch.tensor([60, T - 4])))
+    k_h = oracle.scatter(k_h, upd.cpu(), torch.tensor([60, T - 4]))
+    assert torch.equal(k.cpu().view(torch.int16), k_h.view(torch.int16))
+    q_start = nonpad - 1
+    bias = ab.build_static_cache_bias(dev(nonpad), dev(q_start), None, 1, T, 50)
+    got = fwd(q, k, v, bias, dev(nonpad), 0.1)
+    b_ref = oracle.bias(nonpad, q_start, None, 1, T, 50)
+    ref = oracle.attention(q.cpu(), k_h, v_h, b_ref, nonpad, 0.1)
+    check_parity(to_f64(got), ref, torch.bfloat16, dead_rows(b_ref, nonpad, Hq), "check mode")
+
+
 def test_invalid_arguments_raise():
     q = torch.zeros((1, 3, 1, 256), dtype=torch.bfloat16, device="cuda")
     k = torch.zeros((1, 2, 64, 256), dtype=torch.bfloat16, device="cuda")
@@ -710,18 +781,25 @@ def test_invalid_arguments_raise():
 
 
 # --------------------------------------------------------------------------- #
-# the five full-size workloads, sampled rows
+# the five full-size workloads
 # --------------------------------------------------------------------------- #
+# rows compared: "all", or one row per workgroup of a prefill kernel whose
+# workgroups hold `n` query tokens of the G heads of one KV head (plus every
+# query head's first and last row)
 FULL = {
-    "decode_sliding": (lambda: wl.decode_sliding(), None),
-    "decode_full": (lambda: wl.decode_full(), 48),
-    "decode_full_kvshared": (lambda: wl.decode_full(kv_shared=True), 48),
-    "prefill_vision": (lambda: wl.prefill_vision(), 160),
-    "prefill_long": (lambda: wl.prefill_long(), 96),
-    # V of another head size: the 16-row kernel at the vision chunk's grid, the
-    # 32-row one at the long prefill's
-    "prefill_vision_dv512": (lambda: wl.prefill_vision(Dv=512), 160),
-    "prefill_long_dv256": (lambda: wl.prefill_long(Dv=256), 96),
+    "decode_sliding": (lambda: wl.decode_sliding(), "all"),
+    "decode_full": (lambda: wl.decode_full(), "all"),
+    "decode_full_kvshared": (lambda: wl.decode_full(kv_shared=True), "all"),
+    "prefill_vision": (lambda: wl.prefill_vision(), "all"),
+    # 128-row workgroups of 32 tokens (G = 4)
+    "prefill_long": (lambda: wl.prefill_long(), 32),
+    # V of another head size: the 16-row kernel at the vision chunk's grid
+    # (128 workgroups of 128 rows would not fill the CUs), the 32-row one with
+    # O^T in the accumulation registers at the long prefill's grid and at the
+    # vision chunk's with twice the batch (256 workgroups of 128 rows)
+    "prefill_vision_dv512": (lambda: wl.prefill_vision(Dv=512), "all"),
+    "prefill_vision_b4_dv512": (lambda: wl.prefill_vision(B=4, Dv=512), "all"),
+    "prefill_long_dv256": (lambda: wl.prefill_long(Dv=256), 32),
 }
 
 
@@ -729,15 +807,18 @@ _full_cache = {}
 
 
 def _full_reference(name):
-    """Inputs, sampled rows and oracle results of one full-size workload (shared
-    by the bias and rules variants)."""
+    """Inputs, compared rows and oracle results of one full-size workload
+    (shared by the bias and rules variants)."""
     if name not in _full_cache:
         _full_cache.clear()
-        make, n_rows = FULL[name]
+        make, which = FULL[name]
         w = make()
         step = w.steps[0]
-        rows = None if n_rows is None else sample_rows(w, step, n_rows, seed=500)
-        announce(f"oracle for {name} rows={'all' if rows is None else len(rows)}")
+        n_all = w.B * w.Hq * step.S_q
+        # every row, one batch entry at a time in the oracle (its fp64 copies
+        # of the repeated KV heads stay one entry's worth)
+        rows = np.arange(n_all, dtype=np.int64) if which == "all" else tile_rows(w, step, which, seed=500)
+        announce(f"oracle for {name} rows={len(rows)} of {n_all}")
         k_h, v_h, bias_ref, ref = oracle_step(w, step, w.k_cache, w.v_cache, rows=rows)
         _full_cache[name] = (w, rows, k_h, v_h, bias_ref, ref)
     return _full_cache[name]
@@ -748,7 +829,7 @@ def _full_reference(name):
 def test_attention_full_size(name, variant):
     w, rows, k_h, v_h, bias_ref, ref = _full_reference(name)
     step = w.steps[0]
-    announce(f"attention full {name} variant={variant} {w.describe()}")
+    announce(f"attention full {name} variant={variant} rows={len(rows)} {w.describe()}")
     k_d, v_d = dev(w.k_cache), dev(w.v_cache)
     bias, out = gpu_step(w, step, k_d, v_d, rules=(variant == "rules"))
     torch.cuda.synchronize()
@@ -759,9 +840,10 @@ def test_attention_full_size(name, variant):
         g = bias.cpu().to(torch.float32).view(torch.int32)
         assert torch.equal(g, torch.from_numpy(bias_ref).to(torch.float32).view(torch.int32))
     del k_d, v_d, bias
-    got = to_f64(out).reshape(-1, w.Dv)
-    dead = dead_rows(bias_ref, step.nonpad, w.Hq).reshape(-1)
-    exp = ref.reshape(-1, w.Dv)
-    if rows is not None:
-        got, dead = got[rows], dead[rows]
-    check_parity(got, exp, w.dtype, np.repeat(dead[:, None], w.Dv, axis=1), f"full/{name}/{variant}")
+    got_all = to_f64(out).reshape(-1, w.Dv)
+    # every element of the output was written (poisoned before the call), also
+    # in the rows the oracle does not compute
+    assert np.isfinite(got_all).all(), f"{name}/{variant}: unwritten or non-finite output"
+    dead = dead_rows(bias_ref, step.nonpad, w.Hq).reshape(-1)[rows]
+    check_parity(got_all[rows], ref.reshape(-1, w.Dv), w.dtype, np.repeat(dead[:, None], w.Dv, axis=1),
+                 f"full/{name}/{variant}")
