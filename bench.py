@@ -10,21 +10,23 @@ build, fused into one launch (kv_scatter_and_bias), then the attention. The defa
 layer (B8 Hq16 Hkv8 D256, max_seq 4096, window 1024, S_q 1).
 
 Timing. Inputs are resident in HBM before the timed region. R copies of every
-input rotate through the steps so that no step finds its KV cache in the 256 MB
-Infinity Cache left warm by the previous one. The steps of one rotation are
-captured once into a HIP graph (torch.cuda.CUDAGraph over the library's
-launches on the capture stream) and the graph is replayed; the replayed output
-is compared bit for bit with the eager result before anything is timed. A
-second graph holds only the attention launches of one rotation: its replay time
-per launch is the dominant kernel's average duration (HIP events on the stream
-the kernels run on). --eager times launch by launch instead (used under
-rocprofv3 counter runs).
+input rotate through the steps (step i uses copy i % R), R chosen so that the
+bytes the R copies' steps read cover three times the 256 MB Infinity Cache: no
+step finds its data left warm by the steps before it. The K timed steps are
+captured into one HIP graph (torch.cuda.CUDAGraph over the library's launches
+on the capture stream), which is replayed once in the timed region: exactly K
+steps. Its output is compared bit for bit with the eager result first. A second
+graph holds the same K attention launches alone: its replay time per launch is
+the dominant kernel's average duration (HIP events on the stream the kernels
+run on). --eager times launch by launch instead (used under rocprofv3 counter
+runs).
 
 Output: one JSON line. value = algorithmic bytes of a step / step time (GB/s).
 roofline = the attention kernel's algorithmic bytes (decode) or flops
 (prefill) per launch / its average duration, against the MI355X peak (HBM 8 TB/s;
 bf16 dense matrix cores 2.5 PFLOP/s). cpu_baseline = the fp64 oracle timed on the
-host cores on a bounded sample of the same workload.
+host cores on a bounded sample of the same workload (every secondary workload
+carries its own).
 """
 from __future__ import annotations
 
@@ -162,31 +164,41 @@ def bench_workload(name, steps, warmup, eager, torch, ab):
     probe = InputSet(w, step, torch)
     per_set = sum(t.numel() * t.element_size() for t in
                   (probe.k, probe.v, probe.q, probe.bias, probe.out))
-    n_sets = max(2, min(8, math.ceil(3 * CACHE_BYTES / per_set)))
-    sets = [probe] + [InputSet(w, step, torch) for _ in range(n_sets - 1)]
     need = ab.attn_bias_gqa_workspace_bytes(w.B, w.Hq, w.Hkv, step.S_q, w.max_seq, w.D, w.Dv)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda") if need else None
-    log(f"{name}: {n_sets} rotating input sets of {per_set / 2**20:.0f} MiB, workspace {need} B")
 
-    # eager warm-up and reference outputs
+    # the work of a step, counted from the bias it builds (the rules variant
+    # materialises the same rules once for the count)
+    run_scatter_bias(ab, w, step, probe)
+    if VARIANT == "rules":
+        ab.build_static_cache_bias(probe.nonpad, probe.q_start, probe.kind, step.S_q, w.max_seq,
+                                   w.window, dtype=w.dtype, out=probe.bias)
+    counts = work_counts(w, step, probe, torch)
+    if VARIANT == "rules":   # no bias tensor is read or written in this variant
+        counts["attn_bytes"] -= step.S_q * int(probe.nonpad.clamp(0, w.max_seq).sum()) * (
+            2 if w.dtype == torch.bfloat16 else 4)
+        counts["step_bytes"] = counts["attn_bytes"] + counts["scatter_bytes"]
+
+    # Copies of the inputs rotate so that a step never finds the data it reads
+    # in the 256 MB Infinity Cache: the sets' live bytes (what a step actually
+    # reads) cover at least three times the cache.
+    n_sets = max(2, min(32, math.ceil(3 * CACHE_BYTES / max(counts["attn_bytes"], 1))))
+    sets = [probe] + [InputSet(w, step, torch) for _ in range(n_sets - 1)]
+    log(f"{name}: {n_sets} rotating input sets ({counts['attn_bytes'] / 2**20:.0f} MiB read by a step, "
+        f"{per_set / 2**20:.0f} MiB allocated per set), workspace {need} B")
+
+    # eager warm-up (every set at least once) and reference outputs
     for i in range(max(warmup, n_sets)):
         s = sets[i % n_sets]
         run_scatter_bias(ab, w, step, s)
         run_attention(ab, w, s, ws)
     torch.cuda.synchronize()
     ref_out = [s.out.clone() for s in sets]
-    if VARIANT == "rules":   # the work is counted from the same rules, materialised once
-        ab.build_static_cache_bias(sets[0].nonpad, sets[0].q_start, sets[0].kind, step.S_q,
-                                   w.max_seq, w.window, dtype=w.dtype, out=sets[0].bias)
-    counts = work_counts(w, step, sets[0], torch)
-    if VARIANT == "rules":   # no bias tensor is read or written in this variant
-        counts["attn_bytes"] -= step.S_q * int(sets[0].nonpad.clamp(0, w.max_seq).sum()) * (
-            2 if w.dtype == torch.bfloat16 else 4)
-        counts["step_bytes"] = counts["attn_bytes"] + counts["scatter_bytes"]
     for s in sets:
         assert torch.isfinite(s.out.float()).all(), "non-finite output"
 
-    K = max(steps, n_sets)
+    K = steps   # exactly the steps asked for; step i uses set i % n_sets
+    ibits = torch.int16 if w.dtype == torch.bfloat16 else torch.int32
     if eager:
         st = torch.cuda.current_stream()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -206,36 +218,32 @@ def bench_workload(name, steps, warmup, eager, torch, ab):
         attn_ms = sum(a.elapsed_time(b) for a, b in ev) / K
         mode = "eager"
     else:
+        # one graph of the K steps, and one of their K attention launches alone
         g_step, g_attn = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             with torch.cuda.graph(g_step):
-                for s in sets:
+                for i in range(K):
+                    s = sets[i % n_sets]
                     run_scatter_bias(ab, w, step, s)
                     run_attention(ab, w, s, ws)
             with torch.cuda.graph(g_attn):
-                for s in sets:
-                    run_attention(ab, w, s, ws)
+                for i in range(K):
+                    run_attention(ab, w, sets[i % n_sets], ws)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         # the graphs must reproduce the eager outputs bit for bit, replay after replay
-        for check in range(2):
+        for g in (g_step, g_attn, g_step):
             for s in sets:
-                s.out.zero_()
+                s.out.view(ibits).fill_(0x7FC1)
             torch.cuda.synchronize()
-            (g_step if check == 0 else g_attn).replay()
+            g.replay()
             torch.cuda.synchronize()
-            for s, r in zip(sets, ref_out):
-                assert torch.equal(s.out.view(torch.int16 if w.dtype == torch.bfloat16
-                                              else torch.int32),
-                                   r.view(torch.int16 if w.dtype == torch.bfloat16
-                                          else torch.int32)), "graph replay differs from eager"
-        reps = max(1, K // n_sets)
-        time_graph(torch, g_step, 1)
-        step_ms = time_graph(torch, g_step, reps) / (reps * n_sets)
-        attn_ms = time_graph(torch, g_attn, reps) / (reps * n_sets)
-        K = reps * n_sets
+            for s, r in zip(sets[:K], ref_out):
+                assert torch.equal(s.out.view(ibits), r.view(ibits)), "graph replay differs from eager"
+        step_ms = time_graph(torch, g_step, 1) / K
+        attn_ms = time_graph(torch, g_attn, 1) / K
         mode = "graph"
 
     res = dict(workload=name, mode=mode, steps=K, ms_per_step=step_ms, attn_ms=attn_ms,
@@ -370,10 +378,12 @@ def write_traffic(name, fetch_csv, write_csv, copy_bytes=1 << 30):
     print(json.dumps(rec, indent=1))
 
 
-def cpu_baseline(w, counts, budget_s=12.0):
+def cpu_baseline(name, w, counts, budget_s=12.0):
     """The oracle (scatter + bias + attention, fp64, OpenMP) on the workload's
     batch entries, one after another and round again, until ~budget_s of host
-    work; rate in the metric's unit (algorithmic step bytes per second)."""
+    work. value: algorithmic step bytes per second (the unit of the step rate);
+    attn_rate: the attention's algorithmic work per second in the unit of the
+    workload's roofline (GB/s for decode, TFLOP/s for prefill)."""
     import oracle
     step = w.steps[0]
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
@@ -394,9 +404,15 @@ def cpu_baseline(w, counts, budget_s=12.0):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    rate = counts["step_bytes"] * (done / w.B) / dt / 1e9
+    frac_steps = done / w.B
+    rate = counts["step_bytes"] * frac_steps / dt / 1e9
+    if name in DECODE:
+        attn_rate, attn_unit = counts["attn_bytes"] * frac_steps / dt / 1e9, "GB/s"
+    else:
+        attn_rate, attn_unit = counts["attn_flops"] * frac_steps / dt / 1e12, "TFLOP/s"
     return dict(value=round(rate, 4), unit="GB/s", cores=cores, kind="oracle",
-                sample=f"{done} batch-entry passes ({done / w.B:.2f} steps of B={w.B}; "
+                attn_rate=round(attn_rate, 6), attn_unit=attn_unit,
+                sample=f"{done} batch-entry passes ({frac_steps:.2f} steps of B={w.B}; "
                        f"scatter + bias + attention of one batch entry each) in {dt:.1f} s")
 
 
@@ -457,13 +473,18 @@ def main():
         for name in WORKLOADS:
             if name == args.workload:
                 continue
-            r, _ = bench_workload(name, max(8, args.steps // 10), 2, args.eager, torch, ab)
+            r, w2 = bench_workload(name, max(8, args.steps // 10), 2, args.eager, torch, ab)
             secondary[name] = dict(
                 attn_us=round(r["attn_ms"] * 1e3, 2), step_us=round(r["ms_per_step"] * 1e3, 2),
+                steps=r["steps"], rotating_input_sets=r["n_sets"],
                 roofline=r["roofline"], step_gbs=round(r["step_gbs"], 1),
                 config=r["desc"])
             if "hbm_side" in r:
                 secondary[name]["hbm_side"] = r["hbm_side"]
+            if not args.no_cpu_baseline:
+                log(f"{name}: cpu baseline (oracle) ...")
+                secondary[name]["cpu_baseline"] = cpu_baseline(name, w2, r["counts"], budget_s=8.0)
+            del w2
 
     rl = dict(main_res["roofline"])
     rl["traffic"] = traffic_for(args.workload)
@@ -471,7 +492,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline(w, counts)
+        cpu = cpu_baseline(args.workload, w, counts)
     cfg = dict(main_res["desc"])
     cfg.update({"kernel_timing": main_res["mode"], "rotating_input_sets": main_res["n_sets"],
                 "device_copy_gbs": round(copy_gbs, 1), "variant": VARIANT, "softcap": SOFTCAP,
