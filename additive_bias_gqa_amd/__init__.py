@@ -15,6 +15,9 @@ kernels; there is no fallback: a missing library raises at the first call.
                             dtype=torch.bfloat16, out=None)     -> bias
     attn_bias_gqa_fwd(q, k_cache, v_cache, bias, nonpad, scale, q_start=None,
                       slot_kind=None, window=0, out=None)       -> out
+    attn_bias_gqa_fwd_noalloc(q, k_cache, v_cache, bias, nonpad, scale, out,
+                              q_start=None, slot_kind=None, window=0)
+                                  the same with the library's own scratch
 """
 from __future__ import annotations
 
@@ -25,7 +28,8 @@ import threading
 import torch
 
 __all__ = ["kv_tensor_scatter", "kv_scatter_and_bias", "build_static_cache_bias", "attn_bias_gqa_fwd",
-           "attn_bias_gqa_workspace_bytes", "abgqa_last_error", "library_path", "load"]
+           "attn_bias_gqa_fwd_noalloc", "attn_bias_gqa_workspace_bytes", "abgqa_last_error",
+           "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libabgqa.so")
@@ -65,6 +69,10 @@ def load():
                                           i64, i64, i64, i64, i64, i64, i64, ctypes.c_float,
                                           ctypes.c_float, i64, ctypes.c_int, vp, sz, vp]
         lib.attn_bias_gqa_fwd.restype = ctypes.c_int
+        lib.attn_bias_gqa_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
+                                                  i64, i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                                                  ctypes.c_float, i64, ctypes.c_int, vp]
+        lib.attn_bias_gqa_fwd_noalloc.restype = ctypes.c_int
         lib.attn_bias_gqa_workspace_bytes.argtypes = [i64] * 7
         lib.attn_bias_gqa_workspace_bytes.restype = sz
         lib.abgqa_last_error.argtypes = []
@@ -261,4 +269,39 @@ def attn_bias_gqa_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     _check(lib.attn_bias_gqa_fwd(op, qp, kp, vp_, bp, bdt, npd, qs, sk, B, Hq, Hkv, S_q, T, D, Dv,
                                  float(scale), float(softcap), int(window), _DTYPE[q.dtype], wp, wbytes,
                                  _stream(q)), "attn_bias_gqa_fwd")
+    return out
+
+
+def attn_bias_gqa_fwd_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              bias: torch.Tensor | None, nonpad: torch.Tensor, scale: float,
+                              out: torch.Tensor, q_start: torch.Tensor | None = None,
+                              slot_kind: torch.Tensor | None = None, window: int = 0,
+                              softcap: float = 0.0) -> torch.Tensor:
+    """attn_bias_gqa_fwd through the entry point that allocates nothing: the
+    caller passes `out`, and the scratch is the library's static per-GPU array
+    (8 MiB; larger needs are refused). Calls that overlap in time on one GPU
+    race."""
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, S_q, D], k_cache [B, Hkv, max_seq, D], "
+                         "v_cache [B, Hkv, max_seq, D_v]")
+    B, Hq, S_q, D = q.shape
+    Hkv, T = k_cache.shape[1], k_cache.shape[2]
+    Dv = v_cache.shape[3]
+    if q.dtype not in _DTYPE:
+        raise ValueError("q must be float32 or bfloat16")
+    qp = _dev(q, "q")
+    kp = _dev(k_cache, "k_cache", q.dtype, (B, Hkv, T, D))
+    vp_ = _dev(v_cache, "v_cache", q.dtype, (B, Hkv, T, Dv))
+    bp, bdt = None, BF16
+    if bias is not None:
+        if bias.dtype not in _DTYPE:
+            raise ValueError("bias must be float32 or bfloat16")
+        bp, bdt = _dev(bias, "bias", None, (B, 1, S_q, T)), _DTYPE[bias.dtype]
+    npd = _dev(nonpad, "nonpad", torch.int64, (B,))
+    qs = _opt(q_start, "q_start", torch.int64, (B,))
+    sk = _opt(slot_kind, "slot_kind", torch.int32, (B, T))
+    op = _dev(out, "out", q.dtype, (B, Hq, S_q, Dv))
+    _check(load().attn_bias_gqa_fwd_noalloc(op, qp, kp, vp_, bp, bdt, npd, qs, sk, B, Hq, Hkv, S_q, T, D,
+                                            Dv, float(scale), float(softcap), int(window),
+                                            _DTYPE[q.dtype], _stream(q)), "attn_bias_gqa_fwd_noalloc")
     return out

@@ -399,3 +399,85 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
 const char* abgqa_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The entry point that allocates nothing: its scratch is a library-owned
+// device array, one per GPU (each device that runs the library holds its own
+// copy until the process ends). In host code `scratch` names a host-side
+// stand-in, not device memory: only the address hipGetSymbolAddress returns
+// for the current device is ever passed to a kernel.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct DeviceScratch {
+  void* ptr = nullptr;   // this device's copy of `scratch`
+  bool zeroed = false;   // its arrival counts were cleared by an eager launch
+};
+std::mutex g_scratch_mu;
+DeviceScratch g_scratch[kMaxDevices];
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+}  // namespace
+
+extern "C" abgqa_status attn_bias_gqa_fwd_noalloc(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const void* bias,
+    abgqa_dtype bias_dtype, const int64_t* nonpad_kv_seqlen, const int64_t* q_start,
+    const int32_t* slot_kind, int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q, int64_t max_seq,
+    int64_t D, int64_t D_v, float scale, float softcap, int64_t window, abgqa_dtype dtype,
+    void* stream) {
+  g_last_error.clear();
+  const char* me = "attn_bias_gqa_fwd_noalloc";
+  const size_t need = attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, max_seq, D, D_v);
+  if (need > kNoAllocScratchBytes)
+    return fail(ABGQA_ERR_WORKSPACE,
+                "%s: this shape needs %zu bytes of scratch; the entry point that allocates nothing "
+                "holds %zu per GPU (use attn_bias_gqa_fwd with a workspace)",
+                me, need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(me, e);
+    if (dev < 0 || dev >= kMaxDevices) return fail(ABGQA_ERR_UNSUPPORTED, "%s: device %d beyond %d", me, dev, kMaxDevices);
+    const hipStream_t st = (hipStream_t)stream;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    DeviceScratch& ds = g_scratch[dev];
+    if (!ds.ptr) {
+      void* ptr = nullptr;
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) {
+        g_launch_detail = "hipGetSymbolAddress of the no-alloc scratch";
+        return hip_fail(me, e);
+      }
+      ds.ptr = ptr;
+    }
+    if (!ds.zeroed) {
+      // The decode arrival counts must start at zero (every call leaves them
+      // zero). Cleared by a kernel on the caller's stream, not a memset: under
+      // graph capture this launch becomes a kernel node, and the device counts
+      // as cleared only once an eager call has enqueued it.
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      e = hipStreamIsCapturing(st, &cs);
+      if (e != hipSuccess) return hip_fail(me, e);
+      constexpr int n = (int)(abgqa::kWsCounterBytes / sizeof(uint32_t));
+      hipLaunchKernelGGL(zero_words_kernel, dim3(n / 256), dim3(256), 0, st, (uint32_t*)ds.ptr, n);
+      e = hipGetLastError();
+      if (e != hipSuccess) {
+        g_launch_detail = "no-alloc scratch clear";
+        return hip_fail(me, e);
+      }
+      if (cs == hipStreamCaptureStatusNone) ds.zeroed = true;
+    }
+    ws = ds.ptr;
+  }
+  return attn_bias_gqa_fwd(out, q, k_cache, v_cache, bias, bias_dtype, nonpad_kv_seqlen, q_start,
+                           slot_kind, B, Hq, Hkv, S_q, max_seq, D, D_v, scale, softcap, window, dtype,
+                           ws, ws ? kNoAllocScratchBytes : 0, stream);
+}

@@ -27,6 +27,14 @@
  *   - Device-side index values (write_indices, nonpad_kv_seqlen, q_start) cannot
  *     be checked without a synchronisation; the kernels clamp nonpad into
  *     [0, max_seq] and drop writes outside the cache.
+ *   - ABGQA_CHECK=1 in the environment (read at every call; skipped while the
+ *     stream is being captured into a graph) makes every entry point
+ *     synchronise its stream, copy those index arrays to the host and refuse,
+ *     with ABGQA_ERR_INVALID and nothing enqueued, nonpad outside
+ *     [0, max_seq], a negative q_start, or write_indices that put a new token
+ *     outside [0, max_seq); a decode call also refuses a workspace whose
+ *     arrival counts are not zero (ABGQA_ERR_WORKSPACE). After enqueuing, the
+ *     call synchronises again and reports asynchronous errors (ABGQA_ERR_HIP).
  *   - Layout names: B batch, Hq query heads, Hkv KV heads (G = Hq / Hkv query
  *     heads share one KV head), S_q query tokens, max_seq cache slots, D head
  *     size. D must be one of 64, 128, 256, 512.
@@ -230,6 +238,35 @@ abgqa_status attn_bias_gqa_fwd(void *out, const void *q, const void *k_cache,
                                abgqa_dtype dtype,
                                void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/*
+ * attn_bias_gqa_fwd_noalloc - attn_bias_gqa_fwd without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. It allocates
+ * nothing (no hipMalloc, hipFree or allocating library call).
+ *
+ *   Arguments, layouts, results and errors: those of attn_bias_gqa_fwd, with
+ *   the same kernels and bit-identical outputs.
+ *   Scratch: a library-owned static device array of 8 MiB (8388608 bytes) per
+ *   GPU, held until the process ends; its address is looked up once per
+ *   device. A shape whose attn_bias_gqa_workspace_bytes() exceeds 8 MiB is
+ *   refused with ABGQA_ERR_WORKSPACE before anything is enqueued.
+ *   The first call on a device clears the array's decode arrival counts with
+ *   a small kernel on `stream` (a kernel node if the stream is being captured);
+ *   every call leaves them zero again.
+ *   Calls on one GPU share its array: calls that overlap in time on one GPU
+ *   (concurrent streams or host threads) race and give wrong results.
+ *   Calls ordered on one stream do not.
+ */
+abgqa_status attn_bias_gqa_fwd_noalloc(void *out, const void *q, const void *k_cache,
+                                       const void *v_cache, const void *bias,
+                                       abgqa_dtype bias_dtype,
+                                       const int64_t *nonpad_kv_seqlen,
+                                       const int64_t *q_start, const int32_t *slot_kind,
+                                       int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q,
+                                       int64_t max_seq, int64_t D, int64_t D_v,
+                                       float scale, float softcap, int64_t window,
+                                       abgqa_dtype dtype, void *stream);
 
 /* Bytes of workspace attn_bias_gqa_fwd needs for this shape (0 if none). */
 size_t attn_bias_gqa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv,

@@ -167,3 +167,17 @@ def test_workspace_per_stream():
     with pytest.raises(RuntimeError, match="during graph capture"):
         ab._workspace_for((0, 222), 4000, True, alloc)
     ab._workspaces.clear()
+
+
+def test_noalloc_refuses_large_scratch(lib):
+    """The entry point that allocates nothing holds 8 MiB of scratch per GPU:
+    a shape that needs more is refused with a clear message before any HIP
+    call (16384 (batch row, kv head) pairs of 2-row decode records at D = 512)."""
+    need = lib.attn_bias_gqa_workspace_bytes(2048, 16, 8, 1, 64, 512, 512)
+    assert need > 8 << 20
+    st = lib.attn_bias_gqa_fwd_noalloc(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, None, 1,
+                                       FAKE + 16384, None, None, 2048, 16, 8, 1, 64, 512, 512,
+                                       0.05, 0.0, 0, 1, None)
+    assert st == WORKSPACE
+    msg = ab.abgqa_last_error()
+    assert "needs %d bytes of scratch" % need in msg and "holds 8388608" in msg
