@@ -14,6 +14,10 @@ Functions (each cites its passage in ``oracle.c``):
   bias(nonpad, q_start, slot_kind, S_q, max_seq, window)   [B,1,S_q,max_seq] fp64
   repeat_kv(x, G)                             KV head h // G for query head h
   attention(q, k_cache, v_cache, bias, nonpad, scale, rows=None)  fp64 output
+  scatter_circular(cache, update, write_pos)  TensorScatter into a circular cache
+  bias_circular(kv_len, q_start, slot_kind, S_q, capacity, window)  its bias
+A circular cache's attention is attention() with nonpad = min(kv_len, capacity)
+and the circular bias (the bias carries every rule).
 """
 from __future__ import annotations
 
@@ -62,6 +66,10 @@ def _load():
             [_f64p, _f64p, _f64p, _f64p, _f64p, _i64p] + [ctypes.c_int64] * 6
             + [ctypes.c_double, ctypes.c_double, _i64p, ctypes.c_int64, _f64p])
         lib.oracle_attention_mha.restype = None
+        lib.oracle_scatter_circular.argtypes = [_u8p, _u8p, _i64p] + [ctypes.c_int64] * 6
+        lib.oracle_scatter_circular.restype = None
+        lib.oracle_bias_circular.argtypes = [_f64p, _i64p, _i64p, _i32p] + [ctypes.c_int64] * 4
+        lib.oracle_bias_circular.restype = None
         _lib = lib
     return _lib
 
@@ -96,10 +104,7 @@ def _ptr(a: np.ndarray | None, typ):
     return None if a is None else a.ctypes.data_as(typ)
 
 
-def scatter(cache, update, write_indices):
-    """Return a copy of ``cache`` [B,H,max_seq,D] with ``update`` [B,H,S_new,D]
-    written at slots write_indices[b] + t (raw bytes; out-of-range slots dropped).
-    Accepts torch tensors (any dtype) or numpy arrays; returns the same kind."""
+def _scatter(fn, cache, update, write_indices):
     import torch
     is_torch = isinstance(cache, torch.Tensor)
     if is_torch:
@@ -123,9 +128,25 @@ def scatter(cache, update, write_indices):
     B, H, max_seq, D = (out_t.shape if is_torch else out_n.shape)
     S_new = (upd_t.shape if is_torch else upd_n.shape)[2]
     w = _i64(write_indices)
-    _load().oracle_scatter(_ptr(cache_b, _u8p), _ptr(upd_b, _u8p), _ptr(w, _i64p),
+    fn(_ptr(cache_b, _u8p), _ptr(upd_b, _u8p), _ptr(w, _i64p),
                            B, H, max_seq, S_new, D, elem)
     return out_t if is_torch else out_n
+
+
+def scatter(cache, update, write_indices):
+    """Return a copy of ``cache`` [B,H,max_seq,D] with ``update`` [B,H,S_new,D]
+    written at slots write_indices[b] + t (raw bytes; out-of-range slots dropped).
+    Accepts torch tensors (any dtype) or numpy arrays; returns the same kind."""
+    return _scatter(_load().oracle_scatter, cache, update, write_indices)
+
+
+def scatter_circular(cache, update, write_pos):
+    """Return a copy of the circular cache ``cache`` [B,H,C,D] with ``update``
+    [B,H,S_new,D] (S_new <= C) written at slots (write_pos[b] + t) mod C (raw
+    bytes; negative positions dropped)."""
+    if update.shape[2] > cache.shape[2]:
+        raise ValueError("a circular scatter writes at most capacity tokens")
+    return _scatter(_load().oracle_scatter_circular, cache, update, write_pos)
 
 
 def bias(nonpad, q_start, slot_kind, S_q: int, max_seq: int, window: int) -> np.ndarray:
@@ -139,6 +160,21 @@ def bias(nonpad, q_start, slot_kind, S_q: int, max_seq: int, window: int) -> np.
     out = np.empty((B, 1, S_q, max_seq), dtype=np.float64)
     _load().oracle_bias(_ptr(out, _f64p), _ptr(npd, _i64p), _ptr(qs, _i64p),
                         _ptr(kind, _i32p), B, S_q, max_seq, int(window))
+    return out
+
+
+def bias_circular(kv_len, q_start, slot_kind, S_q: int, capacity: int, window: int) -> np.ndarray:
+    """[B,1,S_q,capacity] float64 bias of a circular cache (0.0 / -inf): kv_len[b]
+    tokens written so far, position p in slot p mod capacity."""
+    L = _i64(kv_len)
+    B = L.shape[0]
+    qs = _i64(q_start)
+    kind = _i32(slot_kind)
+    if kind is not None and kind.shape != (B, capacity):
+        raise ValueError("slot_kind must be [B, capacity]")
+    out = np.empty((B, 1, S_q, capacity), dtype=np.float64)
+    _load().oracle_bias_circular(_ptr(out, _f64p), _ptr(L, _i64p), _ptr(qs, _i64p),
+                                 _ptr(kind, _i32p), B, S_q, capacity, int(window))
     return out
 
 

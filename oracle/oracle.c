@@ -199,3 +199,85 @@ void oracle_attention_mha(double *out, const double *q, const double *k,
     for (int64_t d = 0; d < Dv; ++d) o[d] /= denom;
   }
 }
+
+/* ------------------------------------------------------------------------- */
+/* Circular (window-sized) cache. Reading of [OPT] "GQA sliding window via    */
+/* local_window_size", which names a circular cache as a way to bound the     */
+/* memory of a sliding-window layer but leaves its layout open:               */
+/*   capacity C = max_seq slots; the token of absolute position p is written  */
+/*   to slot p mod C; L = kv_len[b] counts the tokens written so far          */
+/*   (absolute, may exceed C), so slot j holds the newest position p < L with */
+/*   p = j (mod C), pos(j) = j + C * floor((L-1-j) / C), and is valid iff     */
+/*   j < min(L, C).                                                           */
+/* ------------------------------------------------------------------------- */
+
+/* TensorScatter into a circular cache: update token t of batch row b has     */
+/* absolute position write_pos[b] + t and lands in slot (that position) mod C; */
+/* a negative position is dropped. Raw-byte copies. S_new <= C, so no two      */
+/* tokens of one call share a slot.                                           */
+void oracle_scatter_circular(unsigned char *cache, const unsigned char *update,
+                             const int64_t *write_pos, int64_t B, int64_t H,
+                             int64_t C, int64_t S_new, int64_t D,
+                             int64_t elem_bytes) {
+  const int64_t row_bytes = D * elem_bytes;
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t start = write_pos ? write_pos[b] : 0;
+    for (int64_t h = 0; h < H; ++h) {
+      for (int64_t t = 0; t < S_new; ++t) {
+        const int64_t p = start + t;
+        if (p < 0) continue;
+        const int64_t slot = p % C;
+        unsigned char *dst = cache + ((b * H + h) * C + slot) * row_bytes;
+        const unsigned char *src = update + ((b * H + h) * S_new + t) * row_bytes;
+        memcpy(dst, src, (size_t)row_bytes);
+      }
+    }
+  }
+}
+
+/* Bias [B, 1, S_q, C] of a circular cache: the rules of oracle_bias, applied  */
+/* to the absolute position each slot holds.                                  */
+/*   query position q = q_start[b] + s; default q_start = max(L - S_q, 0);    */
+/*   its kind is that of slot q mod C when position q is still held           */
+/*   (max(L - C, 0) <= q < L), else 0;                                        */
+/*   key slot j: valid iff j < min(L, C) and kind_j >= 0; position pos(j);    */
+/*   causal pos <= q; window q - pos < W (W <= 0: none); block kind_q > 0 and  */
+/*   kind_j == kind_q; allowed = valid && ((causal && window) || block).      */
+void oracle_bias_circular(double *bias, const int64_t *kv_len, const int64_t *q_start,
+                          const int32_t *slot_kind, int64_t B, int64_t S_q,
+                          int64_t C, int64_t window) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t s = 0; s < S_q; ++s) {
+      int64_t L = kv_len[b];
+      if (L < 0) L = 0;
+      const int64_t n_valid = L < C ? L : C;
+      const int64_t oldest = L > C ? L - C : 0;    /* oldest position still held */
+      int64_t qs;
+      if (q_start) {
+        qs = q_start[b];
+      } else {
+        qs = L - S_q;
+        if (qs < 0) qs = 0;
+      }
+      const int64_t q = qs + s;
+      int32_t kind_q = 0;
+      if (slot_kind && q >= oldest && q < L) kind_q = slot_kind[b * C + q % C];
+      double *row = bias + (b * S_q + s) * C;
+      for (int64_t j = 0; j < C; ++j) {
+        if (j >= n_valid) {
+          row[j] = -INFINITY;
+          continue;
+        }
+        const int64_t pos = j + C * ((L - 1 - j) / C);
+        const int32_t kind_j = slot_kind ? slot_kind[b * C + j] : 0;
+        const int valid = kind_j >= 0;
+        const int causal = pos <= q;
+        const int in_window = (window <= 0) || (q - pos < window);
+        const int block = (kind_q > 0) && (kind_j == kind_q);
+        const int allowed = valid && ((causal && in_window) || block);
+        row[j] = allowed ? 0.0 : -INFINITY;
+      }
+    }
+  }
+}

@@ -24,9 +24,9 @@ NEG_INF = float("-inf")
 # --------------------------------------------------------------------------- #
 # fixture parsing
 # --------------------------------------------------------------------------- #
-def _bias_cases():
+def _bias_cases(fname="bias_cases.txt"):
     cases, cur = [], None
-    with open(os.path.join(GOLDEN, "bias_cases.txt")) as f:
+    with open(os.path.join(GOLDEN, fname)) as f:
         for raw in f:
             line = raw.strip()
             if not line or line.startswith("#"):
@@ -607,3 +607,137 @@ def test_softcap_keeps_masks_and_bounds_weights():
     w0 = oracle.attention(q, k, eye, bias, nonpad, 1.0)
     live0 = w0[0][..., [j for j in range(T) if j != 3]]
     assert np.any(live0.max(axis=-1) / live0.min(axis=-1) > math.exp(2 * cap))
+
+
+# --------------------------------------------------------------------------- #
+# circular (window-sized) cache: position p in slot p mod C, kv_len = L tokens
+# written so far
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("case", _bias_cases("circular_bias_cases.txt"), ids=lambda c: c["name"])
+def test_circular_bias_golden(case):
+    out = oracle.bias_circular(case["nonpad"], case["q_start"], case["kind"], case["S_q"],
+                               case["max_seq"], case["window"])
+    assert out.shape == (case["B"], 1, case["S_q"], case["max_seq"])
+    assert np.all((out == NEG_INF) | ((out == 0.0) & ~np.signbit(out)))
+    assert len(case["expect"]) == case["B"] * case["S_q"]
+    for (b, s), want in case["expect"].items():
+        assert _mask_str(out[b, 0, s]) == want, (case["name"], b, s)
+
+
+def _held_positions(L, C):
+    """slot -> absolute position held, walking the writes in order (position p
+    overwrites slot p % C): an independent statement of the layout."""
+    held = {}
+    for p in range(L):
+        held[p % C] = p
+    return held
+
+
+def test_circular_scatter_matches_numpy_modular_indexing():
+    rng = wl.rng_for(900)
+    B, H, C, D, S = 3, 2, 7, 4, 5
+    cache = rng.standard_normal((B, H, C, D))
+    upd = rng.standard_normal((B, H, S, D))
+    w = np.array([0, 5, 19], dtype=np.int64)           # no wrap, wrap, several laps
+    got = oracle.scatter_circular(cache, upd, w)
+    ref = cache.copy()
+    for b in range(B):
+        ref[b][:, (w[b] + np.arange(S)) % C] = upd[b]
+    assert np.array_equal(got, ref)
+    # negative positions are dropped, the rest land; S_new = C fills every slot
+    w2 = np.array([-2, 3, 0], dtype=np.int64)
+    got2 = oracle.scatter_circular(cache, upd, w2)
+    ref2 = cache.copy()
+    for b in range(B):
+        for t in range(S):
+            if w2[b] + t >= 0:
+                ref2[b][:, (w2[b] + t) % C] = upd[b][:, t]
+    assert np.array_equal(got2, ref2)
+    full = rng.standard_normal((B, H, C, D))
+    got3 = oracle.scatter_circular(cache, full, np.array([4, 4, 4], dtype=np.int64))
+    assert np.array_equal(np.sort(got3.reshape(-1)), np.sort(full.reshape(-1)))
+    with pytest.raises(ValueError):
+        oracle.scatter_circular(cache, rng.standard_normal((B, H, C + 1, D)), w)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_circular_bias_is_linear_bias_at_held_positions(seed):
+    """The bias of a circular cache at slot j equals the bias of a linear cache
+    of the same tokens at the position slot j holds, and is -inf at slots that
+    hold no token yet (L < C). Queries anywhere from the oldest held position to
+    past the newest, blocks and pads among the held tokens."""
+    rng = wl.rng_for(910 + seed)
+    for _ in range(12):
+        C = int(rng.integers(3, 40))
+        L = int(rng.integers(0, 3 * C + 1))
+        S_q = int(rng.integers(1, C + 1))
+        W = int(rng.integers(-1, C + 3))
+        oldest = max(L - C, 0)
+        Tl = L + S_q + 4
+        klin = np.zeros(Tl, dtype=np.int32)
+        klin[oldest:L] = rng.choice([-1, 0, 0, 1, 2], size=L - oldest)
+        held = _held_positions(L, C)
+        kcirc = rng.integers(-1, 3, size=C).astype(np.int32)    # slots holding no token: any kind
+        for j, p in held.items():
+            kcirc[j] = klin[p]
+        qs = None if rng.random() < 0.3 else np.array([int(rng.integers(oldest, L + 3))], dtype=np.int64)
+        circ = oracle.bias_circular([L], qs, kcirc[None], S_q, C, W)
+        qs_lin = qs if qs is not None else np.array([max(L - S_q, 0)], dtype=np.int64)
+        lin = oracle.bias([L], qs_lin, klin[None], S_q, Tl, W)
+        for j in range(C):
+            if j in held:
+                assert np.array_equal(circ[0, 0, :, j], lin[0, 0, :, held[j]]), (C, L, S_q, W, j)
+            else:
+                assert np.all(circ[0, 0, :, j] == NEG_INF)
+
+
+def test_circular_decode_closed_forms():
+    """Decode at the newest position, text only: the allowed slots are exactly
+    those of the last min(W, L) positions, (L-1-k) mod C; a window wider than
+    the cache sees every held slot."""
+    for C in (1, 4, 7, 32):
+        for L in range(0, 3 * C + 2):
+            for W in (1, 2, C - 1, C, C + 5):
+                if W <= 0:
+                    continue
+                row = oracle.bias_circular([L], None, None, 1, C, W)[0, 0, 0]
+                want = {(L - 1 - k) % C for k in range(min(W, L))}
+                got = {j for j in range(C) if row[j] == 0.0}
+                assert got == want, (C, L, W)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_circular_attention_is_linear_attention(seed):
+    """With room for the window and the chunk (C >= W + S_q - 1) and image
+    blocks among the held tokens, attention over a circular cache equals
+    attention over the linear cache of the same tokens (the keys are the same,
+    in another order); slots holding no token carry NaN and never leak."""
+    rng = wl.rng_for(930 + seed)
+    B, Hq, Hkv, D = 2, 4, 2, 8
+    W, S_q = 5, 3
+    C = W + S_q - 1 + int(rng.integers(0, 4))
+    Ls = [int(rng.integers(S_q, C)), int(rng.integers(C, 4 * C))]   # not wrapped, wrapped
+    Tl = max(Ls) + 1
+    q = rng.standard_normal((B, Hq, S_q, D))
+    k_lin = rng.standard_normal((B, Hkv, Tl, D))
+    v_lin = rng.standard_normal((B, Hkv, Tl, D))
+    klin = np.zeros((B, Tl), dtype=np.int32)
+    k_c = np.full((B, Hkv, C, D), np.nan)
+    v_c = np.full((B, Hkv, C, D), np.nan)
+    kcirc = np.zeros((B, C), dtype=np.int32)
+    for b, L in enumerate(Ls):
+        oldest = max(L - C, 0)
+        blk = int(rng.integers(oldest, max(oldest + 1, L - 2)))
+        klin[b, blk:min(blk + 3, L)] = 1
+        klin[b, oldest] = -1 if L - oldest > 4 else klin[b, oldest]
+        for j, p in _held_positions(L, C).items():
+            k_c[b, :, j], v_c[b, :, j], kcirc[b, j] = k_lin[b, :, p], v_lin[b, :, p], klin[b, p]
+    L_arr = np.array(Ls, dtype=np.int64)
+    scale = 1 / math.sqrt(D)
+    b_lin = oracle.bias(L_arr, None, klin, S_q, Tl, W)
+    y_lin = oracle.attention(q, k_lin, v_lin, b_lin, L_arr, scale)
+    b_circ = oracle.bias_circular(L_arr, None, kcirc, S_q, C, W)
+    y_circ = oracle.attention(q, k_c, v_c, b_circ, np.minimum(L_arr, C), scale)
+    assert np.isfinite(y_circ).all()
+    np.testing.assert_allclose(y_circ, y_lin, rtol=0, atol=1e-12)
+    assert np.abs(y_lin).max() > 0.1
