@@ -18,6 +18,10 @@ kernels; there is no fallback: a missing library raises at the first call.
     attn_bias_gqa_fwd_noalloc(q, k_cache, v_cache, bias, nonpad, scale, out,
                               q_start=None, slot_kind=None, window=0)
                                   the same with the library's own scratch
+The same calls for a circular (window-sized) cache: kv_tensor_scatter_circular,
+build_circular_cache_bias, kv_scatter_and_bias_circular and
+attn_bias_gqa_fwd_circular (kv_len tokens written so far, position p in slot
+p mod capacity).
 """
 from __future__ import annotations
 
@@ -29,7 +33,8 @@ import torch
 
 __all__ = ["kv_tensor_scatter", "kv_scatter_and_bias", "build_static_cache_bias", "attn_bias_gqa_fwd",
            "attn_bias_gqa_fwd_noalloc", "attn_bias_gqa_workspace_bytes", "abgqa_last_error",
-           "library_path", "load"]
+           "kv_tensor_scatter_circular", "build_circular_cache_bias", "kv_scatter_and_bias_circular",
+           "attn_bias_gqa_fwd_circular", "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libabgqa.so")
@@ -58,17 +63,21 @@ def load():
                 f"{_LIB_PATH} is missing: build it with `python -m additive_bias_gqa_amd.build`")
         lib = ctypes.CDLL(_LIB_PATH)
         vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
-        lib.kv_tensor_scatter.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, vp]
-        lib.kv_tensor_scatter.restype = ctypes.c_int
-        lib.kv_scatter_and_bias.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
-                                            vp, ctypes.c_int, vp, vp, vp, i64, i64, vp]
-        lib.kv_scatter_and_bias.restype = ctypes.c_int
-        lib.build_static_cache_bias.argtypes = [vp, ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, vp]
-        lib.build_static_cache_bias.restype = ctypes.c_int
-        lib.attn_bias_gqa_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
-                                          i64, i64, i64, i64, i64, i64, i64, ctypes.c_float,
-                                          ctypes.c_float, i64, ctypes.c_int, vp, sz, vp]
-        lib.attn_bias_gqa_fwd.restype = ctypes.c_int
+        for name in ("kv_tensor_scatter", "kv_tensor_scatter_circular"):
+            getattr(lib, name).argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, vp]
+            getattr(lib, name).restype = ctypes.c_int
+        for name in ("kv_scatter_and_bias", "kv_scatter_and_bias_circular"):
+            getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
+                                           vp, ctypes.c_int, vp, vp, vp, i64, i64, vp]
+            getattr(lib, name).restype = ctypes.c_int
+        for name in ("build_static_cache_bias", "build_circular_cache_bias"):
+            getattr(lib, name).argtypes = [vp, ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, vp]
+            getattr(lib, name).restype = ctypes.c_int
+        for name in ("attn_bias_gqa_fwd", "attn_bias_gqa_fwd_circular"):
+            getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
+                                           i64, i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                                           ctypes.c_float, i64, ctypes.c_int, vp, sz, vp]
+            getattr(lib, name).restype = ctypes.c_int
         lib.attn_bias_gqa_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
                                                   i64, i64, i64, i64, i64, i64, i64, ctypes.c_float,
                                                   ctypes.c_float, i64, ctypes.c_int, vp]
@@ -115,6 +124,18 @@ def _opt(t, name, dtype, shape=None) -> int | None:
 def kv_tensor_scatter(cache: torch.Tensor, update: torch.Tensor,
                       write_indices: torch.Tensor | None) -> torch.Tensor:
     """cache[b, h, write_indices[b] + t, :] = update[b, h, t, :] (in place)."""
+    return _scatter("kv_tensor_scatter", cache, update, write_indices)
+
+
+def kv_tensor_scatter_circular(cache: torch.Tensor, update: torch.Tensor,
+                               write_pos: torch.Tensor | None) -> torch.Tensor:
+    """Circular cache of capacity C = cache.shape[2]: update token t of batch
+    row b (absolute position write_pos[b] + t) goes to slot (position) mod C,
+    in place; at most C tokens per call."""
+    return _scatter("kv_tensor_scatter_circular", cache, update, write_pos)
+
+
+def _scatter(fn: str, cache, update, write_indices):
     if cache.dim() != 4 or update.dim() != 4:
         raise ValueError("cache and update must be 4-D [B, Hkv, slots, D]")
     B, H, T, D = cache.shape
@@ -125,8 +146,8 @@ def kv_tensor_scatter(cache: torch.Tensor, update: torch.Tensor,
     c = _dev(cache, "cache")
     u = _dev(update, "update") if update.numel() else None
     w = _opt(write_indices, "write_indices", torch.int64, (B,))
-    _check(load().kv_tensor_scatter(c, u, w, B, H, T, update.shape[2], D, _DTYPE[cache.dtype],
-                                    _stream(cache)), "kv_tensor_scatter")
+    _check(getattr(load(), fn)(c, u, w, B, H, T, update.shape[2], D, _DTYPE[cache.dtype],
+                               _stream(cache)), fn)
     return cache
 
 
@@ -138,6 +159,23 @@ def kv_scatter_and_bias(k_cache: torch.Tensor, v_cache: torch.Tensor,
     """kv_tensor_scatter(k_cache, k_update, write_indices),
     kv_tensor_scatter(v_cache, v_update, write_indices) and, when `bias` is
     given, build_static_cache_bias(..., out=bias), in one launch."""
+    return _prepare("kv_scatter_and_bias", k_cache, v_cache, k_update, v_update, write_indices,
+                    nonpad, q_start, slot_kind, S_q, window, bias)
+
+
+def kv_scatter_and_bias_circular(k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 k_update: torch.Tensor, v_update: torch.Tensor,
+                                 write_pos: torch.Tensor | None, kv_len: torch.Tensor | None,
+                                 q_start: torch.Tensor | None, slot_kind: torch.Tensor | None,
+                                 S_q: int, window: int, bias: torch.Tensor | None = None):
+    """kv_scatter_and_bias for a circular cache (kv_tensor_scatter_circular of
+    K and V, build_circular_cache_bias), in one launch."""
+    return _prepare("kv_scatter_and_bias_circular", k_cache, v_cache, k_update, v_update, write_pos,
+                    kv_len, q_start, slot_kind, S_q, window, bias)
+
+
+def _prepare(fn, k_cache, v_cache, k_update, v_update, write_indices, nonpad, q_start, slot_kind,
+             S_q, window, bias):
     if k_cache.dim() != 4 or k_update.dim() != 4:
         raise ValueError("caches and updates must be 4-D [B, Hkv, slots, D]")
     B, H, T, D = k_cache.shape
@@ -162,9 +200,8 @@ def kv_scatter_and_bias(k_cache: torch.Tensor, v_cache: torch.Tensor,
         npd = _dev(nonpad, "nonpad", torch.int64, (B,))
         qs = _opt(q_start, "q_start", torch.int64, (B,))
         sk = _opt(slot_kind, "slot_kind", torch.int32, (B, T))
-    _check(load().kv_scatter_and_bias(kc, vc, ku, vu, w, B, H, T, S_new, D, _DTYPE[k_cache.dtype],
-                                      bp, bdt, npd, qs, sk, int(S_q), int(window),
-                                      _stream(k_cache)), "kv_scatter_and_bias")
+    _check(getattr(load(), fn)(kc, vc, ku, vu, w, B, H, T, S_new, D, _DTYPE[k_cache.dtype],
+                               bp, bdt, npd, qs, sk, int(S_q), int(window), _stream(k_cache)), fn)
     return bias
 
 
@@ -173,6 +210,20 @@ def build_static_cache_bias(nonpad: torch.Tensor, q_start: torch.Tensor | None,
                             window: int, dtype: torch.dtype = torch.bfloat16,
                             out: torch.Tensor | None = None) -> torch.Tensor:
     """(B, 1, S_q, max_seq) bias: +0.0 where allowed, -inf where masked."""
+    return _bias("build_static_cache_bias", nonpad, q_start, slot_kind, S_q, max_seq, window, dtype, out)
+
+
+def build_circular_cache_bias(kv_len: torch.Tensor, q_start: torch.Tensor | None,
+                              slot_kind: torch.Tensor | None, S_q: int, capacity: int,
+                              window: int, dtype: torch.dtype = torch.bfloat16,
+                              out: torch.Tensor | None = None) -> torch.Tensor:
+    """(B, 1, S_q, capacity) bias of a circular cache: kv_len[b] tokens written
+    so far, position p in slot p mod capacity; +0.0 allowed, -inf masked."""
+    return _bias("build_circular_cache_bias", kv_len, q_start, slot_kind, S_q, capacity, window, dtype,
+                 out)
+
+
+def _bias(fn, nonpad, q_start, slot_kind, S_q, max_seq, window, dtype, out):
     B = nonpad.shape[0]
     if out is None:
         out = torch.empty((B, 1, S_q, max_seq), dtype=dtype, device=nonpad.device)
@@ -182,8 +233,8 @@ def build_static_cache_bias(nonpad: torch.Tensor, q_start: torch.Tensor | None,
     n = _dev(nonpad, "nonpad", torch.int64, (B,))
     qs = _opt(q_start, "q_start", torch.int64, (B,))
     sk = _opt(slot_kind, "slot_kind", torch.int32, (B, max_seq))
-    _check(load().build_static_cache_bias(o, _DTYPE[out.dtype], n, qs, sk, B, S_q, max_seq,
-                                          int(window), _stream(out)), "build_static_cache_bias")
+    _check(getattr(load(), fn)(o, _DTYPE[out.dtype], n, qs, sk, B, S_q, max_seq, int(window),
+                               _stream(out)), fn)
     return out
 
 
@@ -238,6 +289,26 @@ def attn_bias_gqa_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     current stream's own workspace is used, allocated (zero-filled) by the first
     call that needs it: make that call outside HIP graph capture, or pass a
     zero-filled `workspace` of attn_bias_gqa_workspace_bytes() bytes."""
+    return _attn("attn_bias_gqa_fwd", q, k_cache, v_cache, bias, nonpad, scale, q_start, slot_kind,
+                 window, out, workspace, softcap)
+
+
+def attn_bias_gqa_fwd_circular(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                               bias: torch.Tensor | None, kv_len: torch.Tensor, scale: float,
+                               q_start: torch.Tensor | None = None,
+                               slot_kind: torch.Tensor | None = None, window: int = 0,
+                               out: torch.Tensor | None = None,
+                               workspace: torch.Tensor | None = None,
+                               softcap: float = 0.0) -> torch.Tensor:
+    """attn_bias_gqa_fwd over a circular cache of capacity k_cache.shape[2]:
+    kv_len[b] tokens written so far, position p in slot p mod capacity; with
+    bias=None the circular cache's rules are evaluated in the kernel."""
+    return _attn("attn_bias_gqa_fwd_circular", q, k_cache, v_cache, bias, kv_len, scale, q_start,
+                 slot_kind, window, out, workspace, softcap)
+
+
+def _attn(fn, q, k_cache, v_cache, bias, nonpad, scale, q_start, slot_kind, window, out, workspace,
+          softcap):
     if q.dim() != 4 or k_cache.dim() != 4 or v_cache.dim() != 4:
         raise ValueError("q must be [B, Hq, S_q, D], k_cache [B, Hkv, max_seq, D], "
                          "v_cache [B, Hkv, max_seq, D_v]")
@@ -266,9 +337,9 @@ def attn_bias_gqa_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         workspace = _workspace(q.device, need)
     wp = None if workspace is None else _dev(workspace, "workspace")
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.attn_bias_gqa_fwd(op, qp, kp, vp_, bp, bdt, npd, qs, sk, B, Hq, Hkv, S_q, T, D, Dv,
-                                 float(scale), float(softcap), int(window), _DTYPE[q.dtype], wp, wbytes,
-                                 _stream(q)), "attn_bias_gqa_fwd")
+    _check(getattr(lib, fn)(op, qp, kp, vp_, bp, bdt, npd, qs, sk, B, Hq, Hkv, S_q, T, D, Dv,
+                            float(scale), float(softcap), int(window), _DTYPE[q.dtype], wp, wbytes,
+                            _stream(q)), fn)
     return out
 
 

@@ -89,14 +89,18 @@ abgqa_status fetch_i64(const int64_t* dptr, int64_t n, std::vector<int64_t>& out
   return fetch_device(dptr, (size_t)n * sizeof(int64_t), out.data(), st, me, what);
 }
 
-// nonpad_kv_seqlen[b] in [0, max_seq] for every batch row
+// nonpad_kv_seqlen[b] in [0, max_seq] for every batch row (a circular cache:
+// kv_len[b] >= 0, the count of tokens written may exceed the capacity)
 abgqa_status check_nonpad(const int64_t* nonpad, int64_t B, int64_t max_seq, hipStream_t st,
-                          const char* me) {
+                          const char* me, bool circular = false) {
   std::vector<int64_t> v;
-  abgqa_status r = fetch_i64(nonpad, B, v, st, me, "nonpad_kv_seqlen");
+  abgqa_status r = fetch_i64(nonpad, B, v, st, me, circular ? "kv_len" : "nonpad_kv_seqlen");
   if (r != ABGQA_OK) return r;
   for (int64_t b = 0; b < B; ++b)
-    if (v[b] < 0 || v[b] > max_seq)
+    if (circular && v[b] < 0)
+      return fail(ABGQA_ERR_INVALID, "%s: ABGQA_CHECK: kv_len[%lld] = %lld is negative", me,
+                  (long long)b, (long long)v[b]);
+    else if (!circular && (v[b] < 0 || v[b] > max_seq))
       return fail(ABGQA_ERR_INVALID,
                   "%s: ABGQA_CHECK: nonpad_kv_seqlen[%lld] = %lld is outside [0, max_seq = %lld]", me,
                   (long long)b, (long long)v[b], (long long)max_seq);
@@ -117,8 +121,9 @@ abgqa_status check_q_start(const int64_t* q_start, int64_t B, hipStream_t st, co
 }
 
 // every written slot write_indices[b] + t, t < S_new, inside [0, max_seq)
+// (a circular cache: every position >= 0)
 abgqa_status check_write_indices(const int64_t* wi, int64_t B, int64_t max_seq, int64_t S_new,
-                                 hipStream_t st, const char* me) {
+                                 hipStream_t st, const char* me, bool circular = false) {
   if (!wi || S_new == 0) return S_new <= max_seq ? ABGQA_OK
                                                  : fail(ABGQA_ERR_INVALID,
                                                         "%s: ABGQA_CHECK: S_new = %lld slots past max_seq = %lld",
@@ -127,7 +132,7 @@ abgqa_status check_write_indices(const int64_t* wi, int64_t B, int64_t max_seq, 
   abgqa_status r = fetch_i64(wi, B, v, st, me, "write_indices");
   if (r != ABGQA_OK) return r;
   for (int64_t b = 0; b < B; ++b)
-    if (v[b] < 0 || v[b] > max_seq - S_new)
+    if (v[b] < 0 || (!circular && v[b] > max_seq - S_new))
       return fail(ABGQA_ERR_INVALID,
                   "%s: ABGQA_CHECK: write_indices[%lld] = %lld puts slots of the %lld new tokens "
                   "outside [0, max_seq = %lld)",
@@ -162,79 +167,81 @@ hipError_t abgqa::opt_in_dynamic_lds(const void* kern, size_t lds) {
   return e;
 }
 
-extern "C" {
+namespace {
 
-abgqa_status kv_tensor_scatter(void* cache, const void* update, const int64_t* write_indices,
-                               int64_t B, int64_t Hkv, int64_t max_seq, int64_t S_new, int64_t D,
-                               abgqa_dtype dtype, void* stream) {
+abgqa_status scatter_impl(const char* me, bool circular, void* cache, const void* update,
+                          const int64_t* write_indices, int64_t B, int64_t Hkv, int64_t max_seq,
+                          int64_t S_new, int64_t D, abgqa_dtype dtype, void* stream) {
   g_last_error.clear();
   if (B <= 0 || Hkv <= 0 || max_seq <= 0 || D <= 0)
-    return fail(ABGQA_ERR_INVALID, "kv_tensor_scatter: B, Hkv, max_seq and D must be positive");
-  if (S_new < 0) return fail(ABGQA_ERR_INVALID, "kv_tensor_scatter: S_new must be >= 0");
-  if (max_seq > kMaxSeq) return fail(ABGQA_ERR_UNSUPPORTED, "kv_tensor_scatter: max_seq above 2^24");
+    return fail(ABGQA_ERR_INVALID, "%s: B, Hkv, max_seq and D must be positive", me);
+  if (S_new < 0) return fail(ABGQA_ERR_INVALID, "%s: S_new must be >= 0", me);
+  if (circular && S_new > max_seq)
+    return fail(ABGQA_ERR_INVALID, "%s: a circular cache takes at most capacity = %lld new tokens per call",
+                me, (long long)max_seq);
+  if (max_seq > kMaxSeq) return fail(ABGQA_ERR_UNSUPPORTED, "%s: max_seq above 2^24", me);
   if (dtype != ABGQA_F32 && dtype != ABGQA_BF16)
-    return fail(ABGQA_ERR_UNSUPPORTED, "kv_tensor_scatter: dtype must be ABGQA_F32 or ABGQA_BF16");
+    return fail(ABGQA_ERR_UNSUPPORTED, "%s: dtype must be ABGQA_F32 or ABGQA_BF16", me);
   const int64_t row_bytes = D * (dtype == ABGQA_F32 ? 4 : 2);
   if (row_bytes % 16 != 0 || row_bytes > 4096)
-    return fail(ABGQA_ERR_UNSUPPORTED,
-                "kv_tensor_scatter: D * element size must be a multiple of 16 bytes, at most 4096");
+    return fail(ABGQA_ERR_UNSUPPORTED, "%s: D * element size must be a multiple of 16 bytes, at most 4096", me);
   if (S_new == 0) return ABGQA_OK;  // nothing to append
-  if (!cache || !update) return fail(ABGQA_ERR_INVALID, "kv_tensor_scatter: null cache or update");
+  if (!cache || !update) return fail(ABGQA_ERR_INVALID, "%s: null cache or update", me);
   if (!aligned(cache, 16) || !aligned(update, 16) || (write_indices && !aligned(write_indices, 8)))
-    return fail(ABGQA_ERR_INVALID, "kv_tensor_scatter: misaligned pointer");
+    return fail(ABGQA_ERR_INVALID, "%s: misaligned pointer", me);
   const hipStream_t st = (hipStream_t)stream;
   const bool chk = check_enabled(st);
   if (chk) {
-    const abgqa_status r = check_write_indices(write_indices, B, max_seq, S_new, st, "kv_tensor_scatter");
+    const abgqa_status r = check_write_indices(write_indices, B, max_seq, S_new, st, me, circular);
     if (r != ABGQA_OK) return r;
   }
   const hipError_t e = abgqa::launch_scatter(cache, update, write_indices, B, Hkv, max_seq, S_new,
-                                             row_bytes, st);
-  if (e != hipSuccess) return hip_fail("kv_tensor_scatter", e);
-  return chk ? check_after(st, "kv_tensor_scatter") : ABGQA_OK;
-}
-
-abgqa_status build_static_cache_bias(void* bias, abgqa_dtype bias_dtype,
-                                     const int64_t* nonpad_kv_seqlen, const int64_t* q_start,
-                                     const int32_t* slot_kind, int64_t B, int64_t S_q,
-                                     int64_t max_seq, int64_t window, void* stream) {
-  g_last_error.clear();
-  if (B <= 0 || S_q <= 0 || max_seq <= 0)
-    return fail(ABGQA_ERR_INVALID, "build_static_cache_bias: B, S_q and max_seq must be positive");
-  if (max_seq > kMaxSeq) return fail(ABGQA_ERR_UNSUPPORTED, "build_static_cache_bias: max_seq above 2^24");
-  if (bias_dtype != ABGQA_F32 && bias_dtype != ABGQA_BF16)
-    return fail(ABGQA_ERR_UNSUPPORTED, "build_static_cache_bias: bias dtype must be ABGQA_F32 or ABGQA_BF16");
-  if (!bias || !nonpad_kv_seqlen)
-    return fail(ABGQA_ERR_INVALID, "build_static_cache_bias: null bias or nonpad_kv_seqlen");
-  if (!aligned(bias, 16) || !aligned(nonpad_kv_seqlen, 8) || (q_start && !aligned(q_start, 8)) ||
-      (slot_kind && !aligned(slot_kind, 16)))
-    return fail(ABGQA_ERR_INVALID, "build_static_cache_bias: misaligned pointer");
-  const char* me = "build_static_cache_bias";
-  const hipStream_t st = (hipStream_t)stream;
-  const bool chk = check_enabled(st);
-  if (chk) {
-    abgqa_status r = check_nonpad(nonpad_kv_seqlen, B, max_seq, st, me);
-    if (r == ABGQA_OK) r = check_q_start(q_start, B, st, me);
-    if (r != ABGQA_OK) return r;
-  }
-  const hipError_t e = abgqa::launch_bias(bias, bias_dtype == ABGQA_BF16, nonpad_kv_seqlen, q_start,
-                                          slot_kind, B, S_q, max_seq, window, st);
+                                             row_bytes, circular, st);
   if (e != hipSuccess) return hip_fail(me, e);
   return chk ? check_after(st, me) : ABGQA_OK;
 }
 
-abgqa_status kv_scatter_and_bias(void* k_cache, void* v_cache, const void* k_update,
-                                 const void* v_update, const int64_t* write_indices, int64_t B,
-                                 int64_t Hkv, int64_t max_seq, int64_t S_new, int64_t D,
-                                 abgqa_dtype dtype, void* bias, abgqa_dtype bias_dtype,
-                                 const int64_t* nonpad_kv_seqlen, const int64_t* q_start,
-                                 const int32_t* slot_kind, int64_t S_q, int64_t window,
-                                 void* stream) {
+abgqa_status bias_impl(const char* me, bool circular, void* bias, abgqa_dtype bias_dtype,
+                       const int64_t* nonpad_kv_seqlen, const int64_t* q_start,
+                       const int32_t* slot_kind, int64_t B, int64_t S_q, int64_t max_seq,
+                       int64_t window, void* stream) {
   g_last_error.clear();
-  const char* me = "kv_scatter_and_bias";
+  if (B <= 0 || S_q <= 0 || max_seq <= 0)
+    return fail(ABGQA_ERR_INVALID, "%s: B, S_q and max_seq must be positive", me);
+  if (max_seq > kMaxSeq) return fail(ABGQA_ERR_UNSUPPORTED, "%s: max_seq above 2^24", me);
+  if (bias_dtype != ABGQA_F32 && bias_dtype != ABGQA_BF16)
+    return fail(ABGQA_ERR_UNSUPPORTED, "%s: bias dtype must be ABGQA_F32 or ABGQA_BF16", me);
+  if (!bias || !nonpad_kv_seqlen)
+    return fail(ABGQA_ERR_INVALID, "%s: null bias or nonpad_kv_seqlen", me);
+  if (!aligned(bias, 16) || !aligned(nonpad_kv_seqlen, 8) || (q_start && !aligned(q_start, 8)) ||
+      (slot_kind && !aligned(slot_kind, 16)))
+    return fail(ABGQA_ERR_INVALID, "%s: misaligned pointer", me);
+  const hipStream_t st = (hipStream_t)stream;
+  const bool chk = check_enabled(st);
+  if (chk) {
+    abgqa_status r = check_nonpad(nonpad_kv_seqlen, B, max_seq, st, me, circular);
+    if (r == ABGQA_OK) r = check_q_start(q_start, B, st, me);
+    if (r != ABGQA_OK) return r;
+  }
+  const hipError_t e = abgqa::launch_bias(bias, bias_dtype == ABGQA_BF16, nonpad_kv_seqlen, q_start,
+                                          slot_kind, B, S_q, max_seq, window, circular, st);
+  if (e != hipSuccess) return hip_fail(me, e);
+  return chk ? check_after(st, me) : ABGQA_OK;
+}
+
+abgqa_status prepare_impl(const char* me, bool circular, void* k_cache, void* v_cache,
+                          const void* k_update, const void* v_update, const int64_t* write_indices,
+                          int64_t B, int64_t Hkv, int64_t max_seq, int64_t S_new, int64_t D,
+                          abgqa_dtype dtype, void* bias, abgqa_dtype bias_dtype,
+                          const int64_t* nonpad_kv_seqlen, const int64_t* q_start,
+                          const int32_t* slot_kind, int64_t S_q, int64_t window, void* stream) {
+  g_last_error.clear();
   if (B <= 0 || Hkv <= 0 || max_seq <= 0 || D <= 0)
     return fail(ABGQA_ERR_INVALID, "%s: B, Hkv, max_seq and D must be positive", me);
   if (S_new < 0) return fail(ABGQA_ERR_INVALID, "%s: S_new must be >= 0", me);
+  if (circular && S_new > max_seq)
+    return fail(ABGQA_ERR_INVALID, "%s: a circular cache takes at most capacity = %lld new tokens per call",
+                me, (long long)max_seq);
   if (max_seq > kMaxSeq) return fail(ABGQA_ERR_UNSUPPORTED, "%s: max_seq above 2^24", me);
   if (dtype != ABGQA_F32 && dtype != ABGQA_BF16)
     return fail(ABGQA_ERR_UNSUPPORTED, "%s: dtype must be ABGQA_F32 or ABGQA_BF16", me);
@@ -261,18 +268,23 @@ abgqa_status kv_scatter_and_bias(void* k_cache, void* v_cache, const void* k_upd
   const hipStream_t st = (hipStream_t)stream;
   const bool chk = check_enabled(st);
   if (chk) {
-    abgqa_status r = S_new > 0 ? check_write_indices(write_indices, B, max_seq, S_new, st, me) : ABGQA_OK;
-    if (r == ABGQA_OK && bias) r = check_nonpad(nonpad_kv_seqlen, B, max_seq, st, me);
+    abgqa_status r = S_new > 0 ? check_write_indices(write_indices, B, max_seq, S_new, st, me, circular)
+                               : ABGQA_OK;
+    if (r == ABGQA_OK && bias) r = check_nonpad(nonpad_kv_seqlen, B, max_seq, st, me, circular);
     if (r == ABGQA_OK && bias) r = check_q_start(q_start, B, st, me);
     if (r != ABGQA_OK) return r;
   }
   const hipError_t e = abgqa::launch_prepare(k_cache, v_cache, k_update, v_update, write_indices, B,
                                              Hkv, max_seq, S_new, row_bytes, bias,
                                              bias_dtype == ABGQA_BF16, nonpad_kv_seqlen, q_start,
-                                             slot_kind, S_q, window, st);
+                                             slot_kind, S_q, window, circular, st);
   if (e != hipSuccess) return hip_fail(me, e);
   return chk ? check_after(st, me) : ABGQA_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t attn_bias_gqa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q,
                                      int64_t max_seq, int64_t D, int64_t D_v) {
@@ -287,39 +299,42 @@ size_t attn_bias_gqa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   return abgqa::decode_workspace_bytes(B, Hkv, S_q, G, D_v, max_seq);
 }
 
-abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, const void* v_cache,
-                               const void* bias, abgqa_dtype bias_dtype,
-                               const int64_t* nonpad_kv_seqlen, const int64_t* q_start,
-                               const int32_t* slot_kind, int64_t B, int64_t Hq, int64_t Hkv,
-                               int64_t S_q, int64_t max_seq, int64_t D, int64_t D_v, float scale,
-                               float softcap,
-                               int64_t window, abgqa_dtype dtype, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+abgqa_status attn_impl(const char* me, bool circular, void* out, const void* q, const void* k_cache,
+                       const void* v_cache, const void* bias, abgqa_dtype bias_dtype,
+                       const int64_t* nonpad_kv_seqlen, const int64_t* q_start,
+                       const int32_t* slot_kind, int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q,
+                       int64_t max_seq, int64_t D, int64_t D_v, float scale, float softcap,
+                       int64_t window, abgqa_dtype dtype, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   g_last_error.clear();
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_q <= 0 || max_seq <= 0 || D <= 0 || D_v <= 0)
-    return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: B, Hq, Hkv, S_q, max_seq, D and D_v must be positive");
-  if (Hq % Hkv != 0) return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: Hq must be a multiple of Hkv");
+    return fail(ABGQA_ERR_INVALID, "%s: B, Hq, Hkv, S_q, max_seq, D and D_v must be positive", me);
+  if (Hq % Hkv != 0) return fail(ABGQA_ERR_INVALID, "%s: Hq must be a multiple of Hkv", me);
   if (!(softcap >= 0.f) || softcap == INFINITY)
-    return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: softcap must be finite and >= 0 (0 = none)");
-  if (S_q > max_seq) return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: S_q must not exceed max_seq");
+    return fail(ABGQA_ERR_INVALID, "%s: softcap must be finite and >= 0 (0 = none)", me);
+  if (S_q > max_seq) return fail(ABGQA_ERR_INVALID, "%s: S_q must not exceed max_seq", me);
   if (!head_dim_ok(D) || !head_dim_ok(D_v))
-    return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: D and D_v must be 64, 128, 256 or 512");
-  if (max_seq > kMaxSeq) return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: max_seq above 2^24");
+    return fail(ABGQA_ERR_UNSUPPORTED, "%s: D and D_v must be 64, 128, 256 or 512", me);
+  if (max_seq > kMaxSeq) return fail(ABGQA_ERR_UNSUPPORTED, "%s: max_seq above 2^24", me);
   if (dtype != ABGQA_F32 && dtype != ABGQA_BF16)
-    return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: dtype must be ABGQA_F32 or ABGQA_BF16");
+    return fail(ABGQA_ERR_UNSUPPORTED, "%s: dtype must be ABGQA_F32 or ABGQA_BF16", me);
   if (bias && bias_dtype != ABGQA_F32 && bias_dtype != ABGQA_BF16)
-    return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: bias dtype must be ABGQA_F32 or ABGQA_BF16");
+    return fail(ABGQA_ERR_UNSUPPORTED, "%s: bias dtype must be ABGQA_F32 or ABGQA_BF16", me);
   if (!out || !q || !k_cache || !v_cache || !nonpad_kv_seqlen)
-    return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: null out, q, k_cache, v_cache or nonpad_kv_seqlen");
+    return fail(ABGQA_ERR_INVALID, "%s: null out, q, k_cache, v_cache or nonpad_kv_seqlen", me);
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       (bias && !aligned(bias, 16)) || !aligned(nonpad_kv_seqlen, 8) || (q_start && !aligned(q_start, 8)) ||
       (slot_kind && !aligned(slot_kind, 16)))
-    return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: misaligned pointer");
+    return fail(ABGQA_ERR_INVALID, "%s: misaligned pointer", me);
   if (out == q || out == k_cache || out == v_cache || out == bias)
-    return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: out must not alias an input");
+    return fail(ABGQA_ERR_INVALID, "%s: out must not alias an input", me);
   const int64_t G = Hq / Hkv;
   if (B * Hq * S_q > ((int64_t)1 << 31) || B * Hkv > ((int64_t)1 << 24))
-    return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: too many rows");
+    return fail(ABGQA_ERR_UNSUPPORTED, "%s: too many rows", me);
 
   abgqa::AttnParams p{};
   p.out = out; p.q = q; p.k = k_cache; p.v = v_cache; p.bias = bias;
@@ -327,11 +342,11 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
   p.B = (int)B; p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.G = (int)G; p.S_q = (int)S_q;
   p.T = (int)max_seq; p.D = (int)D; p.Dv = (int)D_v; p.window = window; p.scale = scale; p.softcap = softcap;
   p.bias_is_bf16 = (bias_dtype == ABGQA_BF16);
+  p.circular = circular ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
-  const char* me = "attn_bias_gqa_fwd";
   const bool chk = check_enabled(st);
   if (chk) {
-    abgqa_status r = check_nonpad(nonpad_kv_seqlen, B, max_seq, st, me);
+    abgqa_status r = check_nonpad(nonpad_kv_seqlen, B, max_seq, st, me, circular);
     if (r == ABGQA_OK && !bias) r = check_q_start(q_start, B, st, me);
     if (r != ABGQA_OK) return r;
   }
@@ -351,9 +366,9 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
     path = "decode";
     const size_t need = abgqa::decode_workspace_bytes(B, Hkv, S_q, G, D_v, max_seq);
     if (!workspace || workspace_bytes < need)
-      return fail(ABGQA_ERR_WORKSPACE, "attn_bias_gqa_fwd: workspace of %zu bytes needed, %zu given",
+      return fail(ABGQA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", me,
                   need, workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(workspace, 16)) return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: workspace not 16-byte aligned");
+    if (!aligned(workspace, 16)) return fail(ABGQA_ERR_INVALID, "%s: workspace not 16-byte aligned", me);
     if (chk) {
       // the arrival counts this call uses must be zero
       std::vector<int32_t> cnt((size_t)(B * Hkv));
@@ -363,9 +378,9 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
       for (size_t i = 0; i < cnt.size(); ++i)
         if (cnt[i] != 0)
           return fail(ABGQA_ERR_WORKSPACE,
-                      "attn_bias_gqa_fwd: ABGQA_CHECK: decode arrival count %zu of the workspace is %d, "
+                      "%s: ABGQA_CHECK: decode arrival count %zu of the workspace is %d, "
                       "not 0 (workspace not zero-filled, or a call on it did not complete)",
-                      i, (int)cnt[i]);
+                      me, i, (int)cnt[i]);
     }
     p.n_split = abgqa::decode_num_splits(B, Hkv, max_seq);
     p.arrive = (int*)workspace;
@@ -373,13 +388,13 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
     e = abgqa::launch_attn_decode(p, st);
   } else {
     path = "prefill";
-    if (G > 64) return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: more than 64 query heads per KV head");
+    if (G > 64) return fail(ABGQA_ERR_UNSUPPORTED, "%s: more than 64 query heads per KV head", me);
     // live key tiles are numbered in 16 bits and listed in LDS beside the K/V stages
     if ((max_seq + 31) / 32 > 65535 ||
         abgqa::prefill_lds_bytes((int)(D > D_v ? D : D_v), (int)max_seq) > 160 * 1024)
-      return fail(ABGQA_ERR_UNSUPPORTED, "attn_bias_gqa_fwd: max_seq too large for the prefill tile list");
+      return fail(ABGQA_ERR_UNSUPPORTED, "%s: max_seq too large for the prefill tile list", me);
     if (workspace && !aligned(workspace, 16))
-      return fail(ABGQA_ERR_INVALID, "attn_bias_gqa_fwd: workspace not 16-byte aligned");
+      return fail(ABGQA_ERR_INVALID, "%s: workspace not 16-byte aligned", me);
     // optional here: with less than attn_bias_gqa_workspace_bytes() the
     // kernel finds its live tiles from the bias itself. The decode arrival
     // counts at the start of the workspace are left alone.
@@ -394,6 +409,88 @@ abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, co
             (long long)D, (long long)D_v, bias ? "bias" : "rules", p.n_split);
   if (e != hipSuccess) return hip_fail(me, e);
   return chk ? check_after(st, me) : ABGQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+abgqa_status kv_tensor_scatter(void* cache, const void* update, const int64_t* write_indices,
+                               int64_t B, int64_t Hkv, int64_t max_seq, int64_t S_new, int64_t D,
+                               abgqa_dtype dtype, void* stream) {
+  return scatter_impl("kv_tensor_scatter", false, cache, update, write_indices, B, Hkv, max_seq,
+                      S_new, D, dtype, stream);
+}
+
+abgqa_status kv_tensor_scatter_circular(void* cache, const void* update, const int64_t* write_pos,
+                                        int64_t B, int64_t Hkv, int64_t capacity, int64_t S_new,
+                                        int64_t D, abgqa_dtype dtype, void* stream) {
+  return scatter_impl("kv_tensor_scatter_circular", true, cache, update, write_pos, B, Hkv, capacity,
+                      S_new, D, dtype, stream);
+}
+
+abgqa_status build_static_cache_bias(void* bias, abgqa_dtype bias_dtype,
+                                     const int64_t* nonpad_kv_seqlen, const int64_t* q_start,
+                                     const int32_t* slot_kind, int64_t B, int64_t S_q,
+                                     int64_t max_seq, int64_t window, void* stream) {
+  return bias_impl("build_static_cache_bias", false, bias, bias_dtype, nonpad_kv_seqlen, q_start,
+                   slot_kind, B, S_q, max_seq, window, stream);
+}
+
+abgqa_status build_circular_cache_bias(void* bias, abgqa_dtype bias_dtype, const int64_t* kv_len,
+                                       const int64_t* q_start, const int32_t* slot_kind, int64_t B,
+                                       int64_t S_q, int64_t capacity, int64_t window, void* stream) {
+  return bias_impl("build_circular_cache_bias", true, bias, bias_dtype, kv_len, q_start, slot_kind, B,
+                   S_q, capacity, window, stream);
+}
+
+abgqa_status kv_scatter_and_bias(void* k_cache, void* v_cache, const void* k_update,
+                                 const void* v_update, const int64_t* write_indices, int64_t B,
+                                 int64_t Hkv, int64_t max_seq, int64_t S_new, int64_t D,
+                                 abgqa_dtype dtype, void* bias, abgqa_dtype bias_dtype,
+                                 const int64_t* nonpad_kv_seqlen, const int64_t* q_start,
+                                 const int32_t* slot_kind, int64_t S_q, int64_t window,
+                                 void* stream) {
+  return prepare_impl("kv_scatter_and_bias", false, k_cache, v_cache, k_update, v_update,
+                      write_indices, B, Hkv, max_seq, S_new, D, dtype, bias, bias_dtype,
+                      nonpad_kv_seqlen, q_start, slot_kind, S_q, window, stream);
+}
+
+abgqa_status kv_scatter_and_bias_circular(void* k_cache, void* v_cache, const void* k_update,
+                                          const void* v_update, const int64_t* write_pos, int64_t B,
+                                          int64_t Hkv, int64_t capacity, int64_t S_new, int64_t D,
+                                          abgqa_dtype dtype, void* bias, abgqa_dtype bias_dtype,
+                                          const int64_t* kv_len, const int64_t* q_start,
+                                          const int32_t* slot_kind, int64_t S_q, int64_t window,
+                                          void* stream) {
+  return prepare_impl("kv_scatter_and_bias_circular", true, k_cache, v_cache, k_update, v_update,
+                      write_pos, B, Hkv, capacity, S_new, D, dtype, bias, bias_dtype, kv_len, q_start,
+                      slot_kind, S_q, window, stream);
+}
+
+abgqa_status attn_bias_gqa_fwd(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const void* bias, abgqa_dtype bias_dtype,
+                               const int64_t* nonpad_kv_seqlen, const int64_t* q_start,
+                               const int32_t* slot_kind, int64_t B, int64_t Hq, int64_t Hkv,
+                               int64_t S_q, int64_t max_seq, int64_t D, int64_t D_v, float scale,
+                               float softcap, int64_t window, abgqa_dtype dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return attn_impl("attn_bias_gqa_fwd", false, out, q, k_cache, v_cache, bias, bias_dtype,
+                   nonpad_kv_seqlen, q_start, slot_kind, B, Hq, Hkv, S_q, max_seq, D, D_v, scale,
+                   softcap, window, dtype, workspace, workspace_bytes, stream);
+}
+
+abgqa_status attn_bias_gqa_fwd_circular(void* out, const void* q, const void* k_cache,
+                                        const void* v_cache, const void* bias,
+                                        abgqa_dtype bias_dtype, const int64_t* kv_len,
+                                        const int64_t* q_start, const int32_t* slot_kind, int64_t B,
+                                        int64_t Hq, int64_t Hkv, int64_t S_q, int64_t capacity,
+                                        int64_t D, int64_t D_v, float scale, float softcap,
+                                        int64_t window, abgqa_dtype dtype, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return attn_impl("attn_bias_gqa_fwd_circular", true, out, q, k_cache, v_cache, bias, bias_dtype,
+                   kv_len, q_start, slot_kind, B, Hq, Hkv, S_q, capacity, D, D_v, scale, softcap,
+                   window, dtype, workspace, workspace_bytes, stream);
 }
 
 const char* abgqa_last_error(void) { return g_last_error.c_str(); }

@@ -295,7 +295,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
         if constexpr (kRules) {
           const int32_t kj = p.slot_kind ? p.slot_kind[bb * (int64_t)T + j] : 0;
           for (int s = 0; s < p.S_q; ++s) {
-            const RowRule rr = make_row_rule(p.nonpad, p.q_start, p.slot_kind, bb, s, p.S_q, T, p.window);
+            const RowRule rr = make_row_rule(p.nonpad, p.q_start, p.slot_kind, bb, s, p.S_q, T, p.window, p.circular);
             live |= rr.allowed(j, kj);
           }
         } else {
@@ -367,12 +367,12 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
     // causal / window keys of every query row, then the image block of any row
     int lo = INT32_MAX, hi = -1;
     if (tid < p.S_q) {
-      const RowRule rr = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, tid, p.S_q, T, p.window);
+      const RowRule rr = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, tid, p.S_q, T, p.window, p.circular);
       s_kq[tid] = rr.kind_q;
-      int64_t a = (rr.window > 0) ? rr.q - rr.window + 1 : 0;
-      if (a < 0) a = 0;
-      const int64_t z = rr.q < (int64_t)np - 1 ? rr.q : (int64_t)np - 1;
-      if (a <= z) { lo = (int)a; hi = (int)z; }
+      // the row's causal/window key interval(s) below nonpad (a circular
+      // cache's may wrap round into a second one)
+      if (rr.lo <= rr.hi) { lo = rr.lo; hi = rr.hi; }
+      if (rr.lo2 <= rr.hi2) { lo = min(lo, rr.lo2); hi = max(hi, rr.hi2); }
     }
     __syncthreads();
     bool any_block = false;
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
     const int r = 4 * kgrp + e;
     row_ok[e] = r < R;
     row_s[e] = row_ok[e] ? r / G : 0;
-    if constexpr (kRules) rules[e] = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, row_s[e], p.S_q, T, p.window);
+    if constexpr (kRules) rules[e] = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, row_s[e], p.S_q, T, p.window, p.circular);
   }
   const float scale_log2 = p.scale * kLog2e;
   const bool cap_on = p.softcap > 0.f;

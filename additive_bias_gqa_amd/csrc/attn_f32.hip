@@ -46,7 +46,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p, int64_t n_ro
     const int hk = h / p.G;
     const int64_t np = clamp_nonpad(p.nonpad[b], T);
     RowRule rule{};
-    if constexpr (kRules) rule = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s, p.S_q, T, p.window);
+    if constexpr (kRules) rule = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s, p.S_q, T, p.window, p.circular);
     const BiasT* brow = kRules ? nullptr : (const BiasT*)p.bias + (b * p.S_q + s) * T;
     const int32_t* krow = p.slot_kind ? p.slot_kind + b * T : nullptr;
     const Elem* kbase = kg + (b * p.Hkv + hk) * (int64_t)T * D;

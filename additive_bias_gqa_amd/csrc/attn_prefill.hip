@@ -150,7 +150,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnParams p, int
   }
   RowRule rule{};
   if constexpr (kRules) {
-    if (row_ok) rule = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s, p.S_q, T, p.window);
+    if (row_ok) rule = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s, p.S_q, T, p.window, p.circular);
   }
   const BiasT* brow = kRules ? nullptr : (const BiasT*)p.bias + (b * p.S_q + (row_ok ? s : 0)) * (int64_t)T;
   const int32_t* kindb = p.slot_kind ? p.slot_kind + b * T : nullptr;
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill16_kernel(AttnParams p, i
   }
   RowRule rule{};
   if constexpr (kRules) {
-    if (row_ok) rule = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s, p.S_q, T, p.window);
+    if (row_ok) rule = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s, p.S_q, T, p.window, p.circular);
   }
   const BiasT* brow = kRules ? nullptr : (const BiasT*)p.bias + (b * p.S_q + (row_ok ? s : 0)) * (int64_t)T;
   const int32_t* kindb = p.slot_kind ? p.slot_kind + b * T : nullptr;

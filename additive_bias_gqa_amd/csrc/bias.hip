@@ -21,9 +21,10 @@ template <typename T>
 __global__ __launch_bounds__(256) void bias_kernel(
     T* __restrict__ bias, const int64_t* __restrict__ nonpad,
     const int64_t* __restrict__ q_start, const int32_t* __restrict__ slot_kind,
-    int S_q, int max_seq, int64_t window, int chunks_per_row, int64_t n_chunks, bool vec) {
+    int S_q, int max_seq, int64_t window, int chunks_per_row, int64_t n_chunks, bool vec,
+    bool circular) {
   bias_chunks<T>(bias, nonpad, q_start, slot_kind, S_q, max_seq, window, chunks_per_row, n_chunks,
-                 vec, blockIdx.x, gridDim.x);
+                 vec, blockIdx.x, gridDim.x, circular);
 }
 
 int64_t bias_blocks(int64_t B, int64_t S_q, int64_t max_seq) {
@@ -35,7 +36,8 @@ int64_t bias_blocks(int64_t B, int64_t S_q, int64_t max_seq) {
 
 hipError_t launch_bias(void* bias, int bias_is_bf16, const int64_t* nonpad,
                        const int64_t* q_start, const int32_t* slot_kind, int64_t B,
-                       int64_t S_q, int64_t max_seq, int64_t window, hipStream_t stream) {
+                       int64_t S_q, int64_t max_seq, int64_t window, bool circular,
+                       hipStream_t stream) {
   const int chunks_per_row = (int)((max_seq + 7) / 8);
   const int64_t n_chunks = B * S_q * chunks_per_row;
   const bool vec = (max_seq % 8) == 0;
@@ -43,11 +45,11 @@ hipError_t launch_bias(void* bias, int bias_is_bf16, const int64_t* nonpad,
   if (bias_is_bf16) {
     hipLaunchKernelGGL(bias_kernel<uint16_t>, grid, dim3(256), 0, stream,
                        (uint16_t*)bias, nonpad, q_start, slot_kind, (int)S_q, (int)max_seq,
-                       window, chunks_per_row, n_chunks, vec);
+                       window, chunks_per_row, n_chunks, vec, circular);
   } else {
     hipLaunchKernelGGL(bias_kernel<uint32_t>, grid, dim3(256), 0, stream,
                        (uint32_t*)bias, nonpad, q_start, slot_kind, (int)S_q, (int)max_seq,
-                       window, chunks_per_row, n_chunks, vec);
+                       window, chunks_per_row, n_chunks, vec, circular);
   }
   return hipGetLastError();
 }

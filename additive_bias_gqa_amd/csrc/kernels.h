@@ -17,13 +17,17 @@ void set_launch_detail(const char* what);
 // and larger size; safe to call from several threads.
 hipError_t opt_in_dynamic_lds(const void* kern, size_t lds);
 
+// circular: a circular cache of capacity max_seq (mask_rules.h): the scatter
+// writes position p to slot p mod max_seq, the bias takes nonpad as the
+// absolute count of tokens written
 hipError_t launch_scatter(void* cache, const void* update, const int64_t* write_indices,
                           int64_t B, int64_t H, int64_t max_seq, int64_t S_new,
-                          int64_t row_bytes, hipStream_t stream);
+                          int64_t row_bytes, bool circular, hipStream_t stream);
 
 hipError_t launch_bias(void* bias, int bias_is_bf16, const int64_t* nonpad,
                        const int64_t* q_start, const int32_t* slot_kind, int64_t B,
-                       int64_t S_q, int64_t max_seq, int64_t window, hipStream_t stream);
+                       int64_t S_q, int64_t max_seq, int64_t window, bool circular,
+                       hipStream_t stream);
 
 // grid sizes of the two (capped, grid-stride)
 int64_t scatter_blocks(int64_t n_rows, int vec_per_row);
@@ -35,7 +39,7 @@ hipError_t launch_prepare(void* k_cache, void* v_cache, const void* k_update, co
                           const int64_t* write_indices, int64_t B, int64_t H, int64_t max_seq,
                           int64_t S_new, int64_t row_bytes, void* bias, int bias_is_bf16,
                           const int64_t* nonpad, const int64_t* q_start, const int32_t* slot_kind,
-                          int64_t S_q, int64_t window, hipStream_t stream);
+                          int64_t S_q, int64_t window, bool circular, hipStream_t stream);
 
 // Everything an attention kernel reads, passed by value.
 // The first bytes of every attention workspace: the decode kernel's arrival
@@ -60,6 +64,8 @@ struct AttnParams {
   float scale;               // multiplies q.k
   float softcap;             // > 0: softcap * tanh(scale * q.k / softcap) before the bias
   int bias_is_bf16;          // bias dtype when bias != null
+  int circular;              // circular cache: nonpad is the absolute count of
+                             // tokens written, position p in slot p mod T
   // split-KV decode
   float* ws_part;            // partial results, one record per (b, kv head, split)
   int* arrive;               // split arrivals per (kv head, b): zero between calls

@@ -148,10 +148,14 @@ __device__ __forceinline__ int build_live_list(const AttnParams& p, int64_t b, i
     }
   } else {
     // causal + window: the rows' key intervals lie in [a, z] (q is consecutive
-    // over the rows)
+    // over the rows; a circular cache: every valid slot)
     int a = 0, z = -1;
-    if (s_end > s0) {
-      const RowRule r0 = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s0, p.S_q, T, p.window);
+    if (p.circular) {
+      // a circular cache: the rows' intervals may wrap round the slots; take
+      // every valid slot (the cache is about a window long)
+      z = np - 1;
+    } else if (s_end > s0) {
+      const RowRule r0 = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s0, p.S_q, T, p.window, p.circular);
       const int64_t q_last = r0.q + (s_end - 1 - s0);
       int64_t a64 = (p.window > 0) ? r0.q - p.window + 1 : 0;
       if (a64 < 0) a64 = 0;
@@ -166,7 +170,7 @@ __device__ __forceinline__ int build_live_list(const AttnParams& p, int64_t b, i
     } else {
       // the rows' image-block kinds (up to 4 distinct; more: any block key counts)
       for (int s = s0 + tid; s < s_end; s += NT) {
-        const RowRule rr = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s, p.S_q, T, p.window);
+        const RowRule rr = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s, p.S_q, T, p.window, p.circular);
         if (rr.kind_q > 0) {
           bool seen = false;
           for (int i = 0; i < 4; ++i) seen |= (i < s_nids) && (s_ids[i] == rr.kind_q);

@@ -349,11 +349,13 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   }
   RowRule rule{};
   if constexpr (kRules) {
-    if (row_ok) rule = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s, p.S_q, T, p.window);
+    if (row_ok) rule = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s, p.S_q, T, p.window, p.circular);
   }
   // the row's causal/window key interval for the whole-tile test of the rules
   // variant; a row past the chunk passes it (its output is never stored)
   const int rule_lo = row_ok ? rule.lo : INT_MIN, rule_hi = row_ok ? rule.hi : INT_MAX;
+  // a circular cache's interval may wrap round into a second one
+  const int rule_lo2 = row_ok ? rule.lo2 : INT_MIN, rule_hi2 = row_ok ? rule.hi2 : INT_MAX;
 
   // ---- 2. live tiles ---------------------------------------------------------
   // read from LDS, the count is the same in every lane: say so, so that the
@@ -742,7 +744,8 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) kor |= kvs[i][jj];
-        const bool inside = j0 >= rule_lo && j0 + kTileKeys - 1 <= rule_hi;
+        const bool inside = (j0 >= rule_lo && j0 + kTileKeys - 1 <= rule_hi) ||
+                            (j0 >= rule_lo2 && j0 + kTileKeys - 1 <= rule_hi2);
         if (!__any(kor < 0 || !inside)) {
           asm volatile("" ::: "memory");
 #pragma unroll
@@ -925,7 +928,8 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int e = 0; e < 4; ++e) kor |= kvs[kb][e];
-        const bool inside = j0 >= rule_lo && j0 + kTileKeys - 1 <= rule_hi;
+        const bool inside = (j0 >= rule_lo && j0 + kTileKeys - 1 <= rule_hi) ||
+                            (j0 >= rule_lo2 && j0 + kTileKeys - 1 <= rule_hi2);
         if (!__any(kor < 0 || !inside)) {
           asm volatile("" ::: "memory");
 #pragma unroll

@@ -12,13 +12,16 @@ namespace abgqa {
 
 // TensorScatter (mobius skill "attention-optimization", "In-place KV for ONNX
 // Attention via TensorScatter (static cache)"): update row (b, h, t) lands in
-// cache slot write_indices[b] + t; slots outside [0, max_seq) are dropped. One
-// thread moves 16 bytes; a workgroup covers 256 / vec_per_row rows per step.
+// cache slot write_indices[b] + t; slots outside [0, max_seq) are dropped. A
+// circular cache (mask_rules.h) takes position write_indices[b] + t in slot
+// (position) mod max_seq instead, negative positions dropped. One thread moves
+// 16 bytes; a workgroup covers 256 / vec_per_row rows per step.
 __device__ __forceinline__ void scatter_rows(u32x4* __restrict__ cache,
                                              const u32x4* __restrict__ update,
                                              const int64_t* __restrict__ write_indices, int H,
                                              int max_seq, int S_new, int vec_per_row,
-                                             int64_t n_rows, int64_t blk, int64_t nblk) {
+                                             int64_t n_rows, int64_t blk, int64_t nblk,
+                                             bool circular) {
   const int rows_per_iter = 256 / vec_per_row;
   const int sub = threadIdx.x / vec_per_row;
   const int c = threadIdx.x % vec_per_row;
@@ -27,8 +30,10 @@ __device__ __forceinline__ void scatter_rows(u32x4* __restrict__ cache,
     const int64_t bh = row / S_new;
     const int t = (int)(row - bh * S_new);
     const int64_t b = bh / H;
-    const int64_t slot = (write_indices ? write_indices[b] : 0) + t;
-    if (slot < 0 || slot >= max_seq) continue;  // dropped (no wrap-around)
+    int64_t slot = (write_indices ? write_indices[b] : 0) + t;
+    if (slot < 0) continue;                     // dropped
+    if (circular) slot %= max_seq;
+    else if (slot >= max_seq) continue;         // dropped (no wrap-around)
     cache[(bh * max_seq + slot) * vec_per_row + c] = update[row * vec_per_row + c];
   }
 }
@@ -50,13 +55,14 @@ __device__ __forceinline__ void bias_chunks(T* __restrict__ bias, const int64_t*
                                             const int64_t* __restrict__ q_start,
                                             const int32_t* __restrict__ slot_kind, int S_q,
                                             int max_seq, int64_t window, int chunks_per_row,
-                                            int64_t n_chunks, bool vec, int64_t blk, int64_t nblk) {
+                                            int64_t n_chunks, bool vec, int64_t blk, int64_t nblk,
+                                            bool circular) {
   for (int64_t idx = blk * 256 + threadIdx.x; idx < n_chunks; idx += nblk * 256) {
     const int64_t row = idx / chunks_per_row;
     const int j0 = (int)(idx - row * chunks_per_row) * 8;
     const int64_t b = row / S_q;
     const int s = (int)(row - b * S_q);
-    const RowRule rule = make_row_rule(nonpad, q_start, slot_kind, b, s, S_q, max_seq, window);
+    const RowRule rule = make_row_rule(nonpad, q_start, slot_kind, b, s, S_q, max_seq, window, circular);
     const int32_t* kind_row = slot_kind ? slot_kind + b * max_seq : nullptr;
     T* out = bias + row * max_seq + j0;
     if (vec) {

@@ -19,15 +19,15 @@ __global__ __launch_bounds__(256) void prepare_kernel(
     int max_seq, int S_new, int vec_per_row, int64_t n_rows, int n_scatter, T* __restrict__ bias,
     const int64_t* __restrict__ nonpad, const int64_t* __restrict__ q_start,
     const int32_t* __restrict__ slot_kind, int S_q, int64_t window, int chunks_per_row,
-    int64_t n_chunks, bool vec) {
+    int64_t n_chunks, bool vec, bool circular) {
   if ((int)blockIdx.x < n_scatter) {
     scatter_rows(k_cache, k_update, write_indices, H, max_seq, S_new, vec_per_row, n_rows,
-                 blockIdx.x, n_scatter);
+                 blockIdx.x, n_scatter, circular);
     scatter_rows(v_cache, v_update, write_indices, H, max_seq, S_new, vec_per_row, n_rows,
-                 blockIdx.x, n_scatter);
+                 blockIdx.x, n_scatter, circular);
   } else {
     bias_chunks<T>(bias, nonpad, q_start, slot_kind, S_q, max_seq, window, chunks_per_row, n_chunks,
-                   vec, blockIdx.x - n_scatter, gridDim.x - n_scatter);
+                   vec, blockIdx.x - n_scatter, gridDim.x - n_scatter, circular);
   }
 }
 
@@ -35,7 +35,7 @@ hipError_t launch_prepare(void* k_cache, void* v_cache, const void* k_update, co
                           const int64_t* write_indices, int64_t B, int64_t H, int64_t max_seq,
                           int64_t S_new, int64_t row_bytes, void* bias, int bias_is_bf16,
                           const int64_t* nonpad, const int64_t* q_start, const int32_t* slot_kind,
-                          int64_t S_q, int64_t window, hipStream_t stream) {
+                          int64_t S_q, int64_t window, bool circular, hipStream_t stream) {
   const int vec_per_row = (int)(row_bytes / 16);
   const int64_t n_rows = B * H * S_new;
   const int n_scatter = S_new > 0 ? (int)scatter_blocks(n_rows, vec_per_row) : 0;
@@ -50,13 +50,13 @@ hipError_t launch_prepare(void* k_cache, void* v_cache, const void* k_update, co
                        (u32x4*)v_cache, (const u32x4*)k_update, (const u32x4*)v_update,
                        write_indices, (int)H, (int)max_seq, (int)S_new, vec_per_row, n_rows,
                        n_scatter, (uint16_t*)bias, nonpad, q_start, slot_kind, (int)S_q, window,
-                       chunks_per_row, n_chunks, vec);
+                       chunks_per_row, n_chunks, vec, circular);
   } else {
     hipLaunchKernelGGL(prepare_kernel<uint32_t>, grid, dim3(256), 0, stream, (u32x4*)k_cache,
                        (u32x4*)v_cache, (const u32x4*)k_update, (const u32x4*)v_update,
                        write_indices, (int)H, (int)max_seq, (int)S_new, vec_per_row, n_rows,
                        n_scatter, (uint32_t*)bias, nonpad, q_start, slot_kind, (int)S_q, window,
-                       chunks_per_row, n_chunks, vec);
+                       chunks_per_row, n_chunks, vec, circular);
   }
   return hipGetLastError();
 }

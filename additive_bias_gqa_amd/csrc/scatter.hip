@@ -14,9 +14,9 @@ namespace abgqa {
 __global__ __launch_bounds__(256) void scatter_kernel(
     u32x4* __restrict__ cache, const u32x4* __restrict__ update,
     const int64_t* __restrict__ write_indices, int H, int max_seq, int S_new,
-    int vec_per_row, int64_t n_rows) {
+    int vec_per_row, int64_t n_rows, bool circular) {
   scatter_rows(cache, update, write_indices, H, max_seq, S_new, vec_per_row, n_rows, blockIdx.x,
-               gridDim.x);
+               gridDim.x, circular);
 }
 
 int64_t scatter_blocks(int64_t n_rows, int vec_per_row) {
@@ -28,12 +28,12 @@ int64_t scatter_blocks(int64_t n_rows, int vec_per_row) {
 
 hipError_t launch_scatter(void* cache, const void* update, const int64_t* write_indices,
                           int64_t B, int64_t H, int64_t max_seq, int64_t S_new,
-                          int64_t row_bytes, hipStream_t stream) {
+                          int64_t row_bytes, bool circular, hipStream_t stream) {
   const int vec_per_row = (int)(row_bytes / 16);
   const int64_t n_rows = B * H * S_new;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)scatter_blocks(n_rows, vec_per_row)), dim3(256), 0,
                      stream, (u32x4*)cache, (const u32x4*)update, write_indices, (int)H,
-                     (int)max_seq, (int)S_new, vec_per_row, n_rows);
+                     (int)max_seq, (int)S_new, vec_per_row, n_rows, circular);
   return hipGetLastError();
 }
 

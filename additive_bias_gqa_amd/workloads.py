@@ -20,6 +20,10 @@ The default sizes are the five workload shapes of the method's statement:
                    two 256-token image blocks inside the chunk
   prefill_long     B4 Hq16 Hkv4 D512 S_q2048 max_seq8192, left padding,
                    one 256-token image block per row
+and two layers over a circular (window-sized) cache, where the token of
+absolute position p sits in slot p mod capacity:
+  decode_sliding_circular   the sliding decode layer with 1024 slots
+  prefill_vision_circular   the vision chunk with 1536 slots (window + chunk)
 Smaller sizes are used by the parity tests through the same builders.
 """
 from __future__ import annotations
@@ -86,6 +90,9 @@ class Workload:
     k_cache: torch.Tensor  # [B, Hkv, max_seq, D], contents before the first step
     v_cache: torch.Tensor  # [B, Hkv, max_seq, Dv]
     steps: List[Step]
+    # circular cache of capacity max_seq: write_indices are absolute positions
+    # (slot = position mod capacity) and nonpad is the count of tokens written
+    circular: bool = False
 
     @property
     def Dv(self) -> int:
@@ -97,6 +104,8 @@ class Workload:
              "window": self.window, "dtype": str(self.dtype).replace("torch.", "")}
         if self.Dv != self.D:
             d["Dv"] = self.Dv
+        if self.circular:
+            d["cache"] = "circular"
         return d
 
 
@@ -242,3 +251,64 @@ def prefill_long(index: int = 4, B=4, Hq=16, Hkv=4, D=512, S_q=2048, max_seq=819
     vtag = "" if Dv == D else f"_Dv{Dv}"
     return Workload(f"prefill_long_B{B}_Hq{Hq}_Hkv{Hkv}_D{D}{vtag}_Sq{S_q}_T{max_seq}",
                     dtype, B, Hq, Hkv, D, max_seq, 0, 1.0 / math.sqrt(D), kc, vc, [step])
+
+
+def _fill_circular(rng, B, H, C, D, n_written, dtype) -> torch.Tensor:
+    """A circular cache of C slots after n_written[b] tokens: slots
+    [0, min(n_written, C)) hold written tokens ~ N(0,1), the rest garbage bits.
+    Drawn batch row by batch row: normals first, then garbage."""
+    return _fill_cache(rng, B, H, C, D, np.minimum(n_written, C), dtype)
+
+
+def decode_sliding_circular(index: int = 5, B=8, Hq=16, Hkv=8, D=256, capacity=1024, window=1024,
+                            len_lo=512, len_hi=4096, dtype=torch.bfloat16) -> Workload:
+    """Sliding-window decode over a circular cache of ``capacity`` slots (the
+    window: a quarter of the static cache's 4096). L ~ U{len_lo..len_hi} tokens
+    are written after the step; the L-1 earlier ones fill min(L-1, capacity)
+    slots, and the new token (position L-1) is scattered at slot
+    (L-1) mod capacity. Draw order: L, q, K cache, V cache, k_new, v_new."""
+    rng = rng_for(index)
+    L = rng.integers(len_lo, len_hi, size=B, endpoint=True).astype(np.int64)
+    q = normal(rng, (B, Hq, 1, D), dtype)
+    kc = _fill_circular(rng, B, Hkv, capacity, D, L - 1, dtype)
+    vc = _fill_circular(rng, B, Hkv, capacity, D, L - 1, dtype)
+    kn = normal(rng, (B, Hkv, 1, D), dtype)
+    vn = normal(rng, (B, Hkv, 1, D), dtype)
+    Lt = torch.from_numpy(L)
+    kind = torch.zeros((B, capacity), dtype=torch.int32)
+    step = Step(q, kn, vn, Lt - 1, Lt, Lt - 1, kind)
+    return Workload(f"decode_sliding_circular_B{B}_Hq{Hq}_Hkv{Hkv}_D{D}_C{capacity}_W{window}",
+                    dtype, B, Hq, Hkv, D, capacity, window, 1.0 / math.sqrt(D), kc, vc, [step],
+                    circular=True)
+
+
+def prefill_vision_circular(index: int = 6, B=2, Hq=16, Hkv=8, D=256, S_q=512, capacity=1536,
+                            window=1024, start_hi=2048, block=256, n_blocks=2,
+                            dtype=torch.bfloat16) -> Workload:
+    """The vision prefill chunk over a circular cache of ``capacity`` slots
+    (window + chunk: every key a query of the chunk may see is still held). The
+    chunk's S_q tokens start at absolute position start ~ U{0..start_hi}; the
+    start earlier tokens fill min(start, capacity) slots; the chunk is scattered
+    at slots (start + t) mod capacity; image blocks of ``block`` tokens at
+    offsets ~ U{0..S_q-block} inside the chunk (ids 1, 2, ...; a later block
+    overwrites an overlap) mark the slots their tokens land in. Draw order:
+    start, block offsets, q, K cache, V cache, k_new, v_new."""
+    assert block <= S_q <= capacity
+    rng = rng_for(index)
+    start = rng.integers(0, start_hi, size=B, endpoint=True).astype(np.int64)
+    offs = rng.integers(0, S_q - block, size=(B, n_blocks), endpoint=True)
+    q = normal(rng, (B, Hq, S_q, D), dtype)
+    kc = _fill_circular(rng, B, Hkv, capacity, D, start, dtype)
+    vc = _fill_circular(rng, B, Hkv, capacity, D, start, dtype)
+    kn = normal(rng, (B, Hkv, S_q, D), dtype)
+    vn = normal(rng, (B, Hkv, S_q, D), dtype)
+    kind = torch.zeros((B, capacity), dtype=torch.int32)
+    for b in range(B):
+        for i in range(n_blocks):
+            for t in range(int(offs[b, i]), int(offs[b, i]) + block):
+                kind[b, (int(start[b]) + t) % capacity] = i + 1
+    st = torch.from_numpy(start)
+    step = Step(q, kn, vn, st.clone(), st + S_q, st.clone(), kind)
+    return Workload(f"prefill_vision_circular_B{B}_Hq{Hq}_Hkv{Hkv}_D{D}_Sq{S_q}_C{capacity}_W{window}",
+                    dtype, B, Hq, Hkv, D, capacity, window, 1.0 / math.sqrt(D), kc, vc, [step],
+                    circular=True)

@@ -6,8 +6,11 @@
 
 A step is one pass of the whole hot path over one batch of seeded synthetic
 input: TensorScatter of K and V (skipped by the KV-shared variant) and the bias
-build, fused into one launch (kv_scatter_and_bias), then the attention. The default workload is the sliding-window decode
-layer (B8 Hq16 Hkv8 D256, max_seq 4096, window 1024, S_q 1).
+build, fused into one launch (kv_scatter_and_bias), then the attention. The
+default workload is the sliding-window decode layer (B8 Hq16 Hkv8 D256,
+max_seq 4096, window 1024, S_q 1); the secondary lines are the other four
+workload shapes and the two sliding layers over a circular (window-sized)
+cache.
 
 Timing. Inputs are resident in HBM before the timed region. R copies of every
 input rotate through the steps (step i uses copy i % R), R chosen so that the
@@ -46,8 +49,8 @@ BF16_PEAK_TFLOPS = 2500.0
 CACHE_BYTES = 256 << 20  # Infinity Cache
 
 WORKLOADS = ["decode_sliding", "decode_full", "decode_full_kvshared", "prefill_vision",
-             "prefill_long"]
-DECODE = {"decode_sliding", "decode_full", "decode_full_kvshared"}
+             "prefill_long", "decode_sliding_circular", "prefill_vision_circular"]
+DECODE = {"decode_sliding", "decode_full", "decode_full_kvshared", "decode_sliding_circular"}
 
 
 def log(msg):
@@ -65,6 +68,9 @@ def make_workload(name):
         "decode_full_kvshared": lambda: wl.decode_full(kv_shared=True, Dv=V_HEAD),
         "prefill_vision": lambda: wl.prefill_vision(Dv=V_HEAD),
         "prefill_long": lambda: wl.prefill_long(Dv=V_HEAD),
+        # the sliding layers over a circular (window-sized) cache
+        "decode_sliding_circular": wl.decode_sliding_circular,
+        "prefill_vision_circular": wl.prefill_vision_circular,
     }[name]()
 
 
@@ -93,7 +99,12 @@ SOFTCAP = 0.0      # > 0: softcap * tanh(score / softcap) before the bias
 def run_scatter_bias(ab, w, step, s):
     """TensorScatter of K and V and the bias build, as one fused launch
     (kv_scatter_and_bias; bit-identical to the three separate calls). The
-    KV-shared workload has nothing to scatter; the rules variant builds no bias."""
+    KV-shared workload has nothing to scatter; the rules variant builds no bias;
+    a circular cache takes the circular calls."""
+    if w.circular:
+        ab.kv_scatter_and_bias_circular(s.k, s.v, s.k_new, s.v_new, s.wi, s.nonpad, s.q_start, s.kind,
+                                        step.S_q, w.window, bias=s.bias if VARIANT == "bias" else None)
+        return
     if s.k_new is None or s.v.shape[-1] != s.k.shape[-1]:
         # KV-shared: nothing to scatter; V of another head size: the two
         # scatters apart (the fused launch takes one row size)
@@ -109,13 +120,12 @@ def run_scatter_bias(ab, w, step, s):
 
 
 def run_attention(ab, w, s, ws):
+    fwd = ab.attn_bias_gqa_fwd_circular if w.circular else ab.attn_bias_gqa_fwd
     if VARIANT == "bias":
-        ab.attn_bias_gqa_fwd(s.q, s.k, s.v, s.bias, s.nonpad, w.scale, out=s.out, workspace=ws,
-                             softcap=SOFTCAP)
+        fwd(s.q, s.k, s.v, s.bias, s.nonpad, w.scale, out=s.out, workspace=ws, softcap=SOFTCAP)
     else:
-        ab.attn_bias_gqa_fwd(s.q, s.k, s.v, None, s.nonpad, w.scale, q_start=s.q_start,
-                             slot_kind=s.kind, window=w.window, out=s.out, workspace=ws,
-                             softcap=SOFTCAP)
+        fwd(s.q, s.k, s.v, None, s.nonpad, w.scale, q_start=s.q_start, slot_kind=s.kind,
+            window=w.window, out=s.out, workspace=ws, softcap=SOFTCAP)
 
 
 def work_counts(w, step, s, torch):
@@ -394,12 +404,14 @@ def cpu_baseline(name, w, counts, budget_s=12.0):
         b = done % w.B
         sl = slice(b, b + 1)
         k, v = w.k_cache[sl], w.v_cache[sl]
+        scatter = oracle.scatter_circular if w.circular else oracle.scatter
         if step.k_new is not None:
-            k = oracle.scatter(k, step.k_new[sl], step.write_indices[sl])
-            v = oracle.scatter(v, step.v_new[sl], step.write_indices[sl])
+            k = scatter(k, step.k_new[sl], step.write_indices[sl])
+            v = scatter(v, step.v_new[sl], step.write_indices[sl])
         kind = None if step.slot_kind is None else step.slot_kind[sl]
-        bias = oracle.bias(step.nonpad[sl], step.q_start[sl], kind, step.S_q, w.max_seq, w.window)
-        oracle.attention(step.q[sl], k, v, bias, step.nonpad[sl], w.scale)
+        build = oracle.bias_circular if w.circular else oracle.bias
+        bias = build(step.nonpad[sl], step.q_start[sl], kind, step.S_q, w.max_seq, w.window)
+        oracle.attention(step.q[sl], k, v, bias, step.nonpad[sl].clamp(0, w.max_seq), w.scale)
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break

@@ -240,6 +240,73 @@ abgqa_status attn_bias_gqa_fwd(void *out, const void *q, const void *k_cache,
                                void *stream);
 
 /*
+ * Circular (window-sized) cache - the same four calls for a cache whose
+ * buffer is bounded by the window instead of the sequence.
+ *
+ * Passage: mobius skill "attention-optimization", section "GQA sliding window
+ * via local_window_size": the window masks attention but does not shrink the
+ * buffer, so bounding a sliding layer's memory takes a circular (or static)
+ * cache. The page leaves the layout open; the layout taken here:
+ *   capacity C (the max_seq of the layout names above) slots per (b, kv head);
+ *   the token of absolute position p lives in slot p mod C;
+ *   kv_len[b] = L, the count of tokens written so far (absolute, may exceed C,
+ *   int64 on the device): slot j holds the newest position p < L with
+ *   p = j (mod C) and is valid iff j < min(L, C);
+ *   the static cache's rules (causal, window [q-W+1, q], image blocks, pads)
+ *   apply to the absolute positions the slots hold and to the absolute query
+ *   position q = q_start[b] + s (default q_start = max(L - S_q, 0)); a query's
+ *   kind is that of slot q mod C while position q is held, else 0.
+ * With C >= W + S_q - 1 every key a query of the chunk may see is still held,
+ * and the results equal those of a static cache holding the same tokens.
+ *
+ * kv_tensor_scatter_circular: update token t of batch row b (position
+ *   write_pos[b] + t) goes to slot (write_pos[b] + t) mod C; a negative
+ *   position is dropped. S_new <= C (ABGQA_ERR_INVALID otherwise), so no two
+ *   tokens of one call share a slot. Other arguments, errors and the bit-exact
+ *   copy: those of kv_tensor_scatter.
+ * build_circular_cache_bias: the [B, 1, S_q, C] bias (+0.0 / -inf) of the rule
+ *   above, from kv_len; otherwise as build_static_cache_bias.
+ * kv_scatter_and_bias_circular: both scatters and the bias in one launch, as
+ *   kv_scatter_and_bias.
+ * attn_bias_gqa_fwd_circular: the attention over a circular cache, with its
+ *   bias tensor (then the same as attn_bias_gqa_fwd with nonpad = kv_len, which
+ *   the kernels clamp to C) or, bias == NULL, with the rule above evaluated in
+ *   the kernel; workspace as attn_bias_gqa_fwd (attn_bias_gqa_workspace_bytes
+ *   with max_seq = C).
+ * Under ABGQA_CHECK, kv_len must be >= 0 and write_pos >= 0 (no upper bound).
+ */
+abgqa_status kv_tensor_scatter_circular(void *cache, const void *update,
+                                        const int64_t *write_pos, int64_t B,
+                                        int64_t Hkv, int64_t capacity, int64_t S_new,
+                                        int64_t D, abgqa_dtype dtype, void *stream);
+
+abgqa_status build_circular_cache_bias(void *bias, abgqa_dtype bias_dtype,
+                                       const int64_t *kv_len, const int64_t *q_start,
+                                       const int32_t *slot_kind, int64_t B,
+                                       int64_t S_q, int64_t capacity,
+                                       int64_t window, void *stream);
+
+abgqa_status kv_scatter_and_bias_circular(void *k_cache, void *v_cache,
+                                          const void *k_update, const void *v_update,
+                                          const int64_t *write_pos, int64_t B,
+                                          int64_t Hkv, int64_t capacity, int64_t S_new,
+                                          int64_t D, abgqa_dtype dtype, void *bias,
+                                          abgqa_dtype bias_dtype, const int64_t *kv_len,
+                                          const int64_t *q_start,
+                                          const int32_t *slot_kind, int64_t S_q,
+                                          int64_t window, void *stream);
+
+abgqa_status attn_bias_gqa_fwd_circular(void *out, const void *q, const void *k_cache,
+                                        const void *v_cache, const void *bias,
+                                        abgqa_dtype bias_dtype, const int64_t *kv_len,
+                                        const int64_t *q_start, const int32_t *slot_kind,
+                                        int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q,
+                                        int64_t capacity, int64_t D, int64_t D_v,
+                                        float scale, float softcap, int64_t window,
+                                        abgqa_dtype dtype, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+
+/*
  * attn_bias_gqa_fwd_noalloc - attn_bias_gqa_fwd without a workspace argument,
  * for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc. It allocates

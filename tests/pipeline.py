@@ -54,49 +54,62 @@ def poisoned_workspace(nbytes: int):
     return ws
 
 
-def fwd(q, k, v, bias, nonpad, scale, out=None, workspace=None, **kw):
-    """attn_bias_gqa_fwd with a poisoned output and a poisoned workspace of the
-    size the shape needs, unless the caller passes its own."""
+def fwd(q, k, v, bias, nonpad, scale, out=None, workspace=None, entry=None, **kw):
+    """attn_bias_gqa_fwd (or `entry`, a binding of the same arguments) with a
+    poisoned output and a poisoned workspace of the size the shape needs,
+    unless the caller passes its own."""
     B, Hq, S_q, D = q.shape
     Hkv, T, Dv = k.shape[1], k.shape[2], v.shape[3]
     if out is None:
         out = poisoned((B, Hq, S_q, Dv), q.dtype)
     if workspace is None:
         workspace = poisoned_workspace(ab.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, T, D, Dv))
-    return ab.attn_bias_gqa_fwd(q, k, v, bias, nonpad, scale, out=out, workspace=workspace, **kw)
+    entry = entry or ab.attn_bias_gqa_fwd
+    return entry(q, k, v, bias, nonpad, scale, out=out, workspace=workspace, **kw)
 
 
 def gpu_step(w: wl.Workload, step: wl.Step, k_dev, v_dev, rules: bool = False,
              bias_dtype: torch.dtype | None = None, default_q_start: bool = False,
              softcap: float = 0.0):
     """Scatter K/V (unless KV-shared), build the bias (unless rules), attention.
-    Returns (bias or None, out) on the device."""
+    Returns (bias or None, out) on the device. A circular workload takes the
+    circular cache's calls."""
+    circ = w.circular
     if step.k_new is not None:
         wi = dev(step.write_indices)
-        ab.kv_tensor_scatter(k_dev, dev(step.k_new), wi)
-        ab.kv_tensor_scatter(v_dev, dev(step.v_new), wi)
+        scatter = ab.kv_tensor_scatter_circular if circ else ab.kv_tensor_scatter
+        scatter(k_dev, dev(step.k_new), wi)
+        scatter(v_dev, dev(step.v_new), wi)
     nonpad = dev(step.nonpad)
     q_start = None if default_q_start else dev(step.q_start)
     kind = dev(step.slot_kind)
     bias = None
     if not rules:
         bt = bias_dtype or w.dtype
-        bias = ab.build_static_cache_bias(nonpad, q_start, kind, step.S_q, w.max_seq, w.window,
-                                          dtype=bt, out=poisoned((w.B, 1, step.S_q, w.max_seq), bt))
+        build = ab.build_circular_cache_bias if circ else ab.build_static_cache_bias
+        bias = build(nonpad, q_start, kind, step.S_q, w.max_seq, w.window,
+                     dtype=bt, out=poisoned((w.B, 1, step.S_q, w.max_seq), bt))
     out = fwd(dev(step.q), k_dev, v_dev, bias, nonpad, w.scale,
-              q_start=q_start, slot_kind=kind, window=w.window, softcap=softcap)
+              q_start=q_start, slot_kind=kind, window=w.window, softcap=softcap,
+              entry=ab.attn_bias_gqa_fwd_circular if circ else ab.attn_bias_gqa_fwd)
     return bias, out
 
 
 def oracle_step(w: wl.Workload, step: wl.Step, k_host, v_host, rows=None,
                 default_q_start: bool = False, softcap: float = 0.0):
-    """The same pass on the oracle. Returns (k_cache, v_cache, bias, out)."""
+    """The same pass on the oracle. Returns (k_cache, v_cache, bias, out). A
+    circular workload: the circular scatter and bias, and attention over the
+    min(kv_len, capacity) valid slots."""
+    circ = w.circular
     if step.k_new is not None:
-        k_host = oracle.scatter(k_host, step.k_new, step.write_indices)
-        v_host = oracle.scatter(v_host, step.v_new, step.write_indices)
+        scatter = oracle.scatter_circular if circ else oracle.scatter
+        k_host = scatter(k_host, step.k_new, step.write_indices)
+        v_host = scatter(v_host, step.v_new, step.write_indices)
     qs = None if default_q_start else step.q_start
-    bias = oracle.bias(step.nonpad, qs, step.slot_kind, step.S_q, w.max_seq, w.window)
-    out = oracle.attention(step.q, k_host, v_host, bias, step.nonpad, w.scale, rows=rows,
+    build = oracle.bias_circular if circ else oracle.bias
+    bias = build(step.nonpad, qs, step.slot_kind, step.S_q, w.max_seq, w.window)
+    valid = step.nonpad.clamp(0, w.max_seq) if circ else step.nonpad
+    out = oracle.attention(step.q, k_host, v_host, bias, valid, w.scale, rows=rows,
                            softcap=softcap)
     return k_host, v_host, bias, out
 

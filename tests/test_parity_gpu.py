@@ -781,6 +781,122 @@ def test_invalid_arguments_raise():
 
 
 # --------------------------------------------------------------------------- #
+# circular (window-sized) cache: position p in slot p mod capacity
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("D", [64, 256, 512])
+def test_circular_scatter_bit_exact(dtype, D):
+    announce(f"circular scatter dtype={dtype} D={D}")
+    rng = wl.rng_for(800 + D)
+    B, H, C, S_new = 5, 3, 37, 9
+    cache = wl.garbage(rng, (B, H, C, D), dtype)
+    upd = wl.garbage(rng, (B, H, S_new, D), dtype)
+    w = torch.tensor([0, 30, 3 * C + 2, -4, C - S_new], dtype=torch.int64)   # wrap, laps, negative
+    ref = oracle.scatter_circular(cache, upd, w)
+    c = dev(cache)
+    ab.kv_tensor_scatter_circular(c, dev(upd), dev(w))
+    ibits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(c.cpu().view(ibits), ref.view(ibits))
+    with pytest.raises(RuntimeError, match="at most capacity"):
+        ab.kv_tensor_scatter_circular(c, dev(wl.garbage(rng, (B, H, C + 1, D), dtype)), dev(w))
+
+
+@pytest.mark.parametrize("bias_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("C,S_q,W", [(64, 16, 8), (1001, 33, 100), (1024, 1, 1024), (256, 200, 0),
+                                     (40, 40, 1000)])
+def test_circular_bias_bit_exact(bias_dtype, C, S_q, W):
+    announce(f"circular bias dtype={bias_dtype} C={C} S_q={S_q} W={W}")
+    rng = wl.rng_for(820 + C + S_q)
+    B = 4
+    L = torch.from_numpy(rng.integers(0, 3 * C, size=B, endpoint=True).astype(np.int64))
+    L[0] = C // 2                                                    # not wrapped
+    kind = _rand_kinds(rng, B, C)
+    q_start = torch.from_numpy(np.maximum(L.numpy() - S_q - rng.integers(-3, 5, size=B), 0))
+    for qs in (q_start, None):
+        for kd in (kind, None):
+            ref = oracle.bias_circular(L, qs, kd, S_q, C, W)
+            got = ab.build_circular_cache_bias(dev(L), dev(qs), dev(kd), S_q, C, W, dtype=bias_dtype,
+                                               out=poisoned((B, 1, S_q, C), bias_dtype))
+            g = got.cpu().to(torch.float32)
+            r = torch.from_numpy(ref).to(torch.float32)
+            assert torch.equal(g.view(torch.int32), r.view(torch.int32)), (qs is None, kd is None)
+
+
+def test_circular_fused_prepare_bit_exact():
+    rng = wl.rng_for(840)
+    B, H, C, D, S_new, W = 4, 2, 520, 128, 130, 64
+    announce("circular fused prepare")
+    kc, vc = wl.garbage(rng, (B, H, C, D), torch.bfloat16), wl.garbage(rng, (B, H, C, D), torch.bfloat16)
+    ku, vu = wl.garbage(rng, (B, H, S_new, D), torch.bfloat16), wl.garbage(rng, (B, H, S_new, D), torch.bfloat16)
+    pos = torch.tensor([0, 450, 1900, 7], dtype=torch.int64)
+    L = pos + S_new
+    kind = _rand_kinds(rng, B, C)
+    k_d, v_d = dev(kc), dev(vc)
+    bias = poisoned((B, 1, S_new, C), torch.bfloat16)
+    ab.kv_scatter_and_bias_circular(k_d, v_d, dev(ku), dev(vu), dev(pos), dev(L), None, dev(kind), S_new,
+                                    W, bias=bias)
+    torch.cuda.synchronize()
+    assert torch.equal(k_d.cpu().view(torch.int16), oracle.scatter_circular(kc, ku, pos).view(torch.int16))
+    assert torch.equal(v_d.cpu().view(torch.int16), oracle.scatter_circular(vc, vu, pos).view(torch.int16))
+    ref = torch.from_numpy(oracle.bias_circular(L, None, kind, S_new, C, W)).to(torch.float32)
+    assert torch.equal(bias.cpu().to(torch.float32).view(torch.int32), ref.view(torch.int32))
+
+
+CIRCULAR = {
+    # window < capacity, the cache wrapped several times or not yet
+    "decode_d256_w": lambda: wl.decode_sliding_circular(B=5, Hq=8, Hkv=4, D=256, capacity=300, window=200,
+                                                        len_lo=1, len_hi=1000),
+    # window = capacity (every held token allowed)
+    "decode_d512": lambda: wl.decode_sliding_circular(B=4, Hq=16, Hkv=4, D=512, capacity=256, window=256,
+                                                      len_lo=100, len_hi=900),
+    # direct-to-LDS prefill (D 256 key split, D 512 32-row, D 128), chunks that wrap
+    "prefill_d256": lambda: wl.prefill_vision_circular(B=3, Hq=8, Hkv=4, D=256, S_q=100, capacity=352,
+                                                       window=200, start_hi=900, block=40),
+    "prefill_d512": lambda: wl.prefill_vision_circular(B=2, Hq=8, Hkv=2, D=512, S_q=130, capacity=320,
+                                                       window=150, start_hi=700, block=50),
+    "prefill_d128": lambda: wl.prefill_vision_circular(B=2, Hq=6, Hkv=2, D=128, S_q=90, capacity=200,
+                                                       window=90, start_hi=500, block=30),
+    # capacity whose bf16 bias rows are not 16-byte chunks: the register-staged kernel
+    "prefill_d256_ragged": lambda: wl.prefill_vision_circular(B=2, Hq=8, Hkv=4, D=256, S_q=70, capacity=201,
+                                                              window=100, start_hi=600, block=20),
+    "prefill_fp32": lambda: wl.prefill_vision_circular(B=2, Hq=4, Hkv=2, D=64, S_q=20, capacity=48,
+                                                       window=16, start_hi=100, block=8,
+                                                       dtype=torch.float32),
+}
+
+
+@pytest.mark.parametrize("variant", ["bias", "rules"])
+@pytest.mark.parametrize("name", list(CIRCULAR))
+def test_circular_attention(name, variant):
+    """Attention over a circular cache (scatter of the step's tokens, the
+    circular bias or the circular rules in the kernel) against the oracle's
+    circular path, every element, every kernel path."""
+    w = CIRCULAR[name]()
+    step = w.steps[0]
+    announce(f"circular attention {name} variant={variant} {w.describe()}")
+    k_h, v_h, bias_ref, ref = oracle_step(w, step, w.k_cache, w.v_cache)
+    k_d, v_d = dev(w.k_cache), dev(w.v_cache)
+    bias, out = gpu_step(w, step, k_d, v_d, rules=(variant == "rules"))
+    torch.cuda.synchronize()
+    ibits = torch.int16 if w.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(k_d.cpu().view(ibits), k_h.view(ibits))
+    if bias is not None:
+        g = bias.cpu().to(torch.float32).view(torch.int32)
+        assert torch.equal(g, torch.from_numpy(bias_ref).to(torch.float32).view(torch.int32))
+    check_parity(to_f64(out), ref, w.dtype, dead_rows(bias_ref, step.nonpad, w.Hq), f"circular/{name}/{variant}")
+
+
+def test_circular_rules_equal_bias_bitwise():
+    for name in ("decode_d256_w", "prefill_d256", "prefill_d512"):
+        w = CIRCULAR[name]()
+        step = w.steps[0]
+        announce(f"circular rules == bias {name}")
+        _, o_bias = gpu_step(w, step, dev(w.k_cache), dev(w.v_cache), rules=False)
+        _, o_rules = gpu_step(w, step, dev(w.k_cache), dev(w.v_cache), rules=True)
+        assert torch.equal(o_bias.view(torch.int16), o_rules.view(torch.int16)), name
+
+
+# --------------------------------------------------------------------------- #
 # the five full-size workloads
 # --------------------------------------------------------------------------- #
 # rows compared: "all", or one row per workgroup of a prefill kernel whose
@@ -800,6 +916,10 @@ FULL = {
     "prefill_vision_dv512": (lambda: wl.prefill_vision(Dv=512), "all"),
     "prefill_vision_b4_dv512": (lambda: wl.prefill_vision(B=4, Dv=512), "all"),
     "prefill_long_dv256": (lambda: wl.prefill_long(Dv=256), 32),
+    # the circular (window-sized) cache: the sliding decode layer with 1024
+    # slots, the vision chunk with 1536 (window + chunk)
+    "decode_sliding_circular": (lambda: wl.decode_sliding_circular(), "all"),
+    "prefill_vision_circular": (lambda: wl.prefill_vision_circular(), "all"),
 }
 
 
@@ -833,7 +953,7 @@ def test_attention_full_size(name, variant):
     k_d, v_d = dev(w.k_cache), dev(w.v_cache)
     bias, out = gpu_step(w, step, k_d, v_d, rules=(variant == "rules"))
     torch.cuda.synchronize()
-    if step.k_new is not None:   # the scatter landed bit-exactly
+    if step.k_new is not None:   # the scatter landed bit-exactly (a circular cache's too)
         assert torch.equal(k_d.cpu().view(torch.int16), k_h.view(torch.int16))
         assert torch.equal(v_d.cpu().view(torch.int16), v_h.view(torch.int16))
     if bias is not None:         # and so did the bias
