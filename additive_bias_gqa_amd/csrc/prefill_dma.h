@@ -1037,11 +1037,14 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   // (and its LDS) ends
   wait_vmcnt<0>();
   if constexpr (kAsmAcc) acc_settle(oacc);
+  // KS = 2: half 1 leaves (m, l, O^T) in the first XO_BYTES of the stage area;
+  // the output rows are staged after it
+  constexpr int NACC = DBLK * (RW == 32 ? 16 : 4);
+  constexpr int NF = NACC + 2;
+  constexpr int XO_BYTES = KS == 2 ? NWR * NF * 64 * 4 : 0;
   if constexpr (KS == 2) {
     // merge the key halves: half 1 leaves (m, l, O^T) in LDS (the stages are
     // free now), half 0 rescales both to the larger maximum and adds
-    constexpr int NACC = DBLK * (RW == 32 ? 16 : 4);
-    constexpr int NF = NACC + 2;
     float* xo = reinterpret_cast<float*>(stages) + (size_t)rg * NF * 64 + lane;
     __syncthreads();
     if (kh == 1) {
@@ -1064,35 +1067,77 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
 #pragma unroll
       for (int e = 0; e < NACC / DBLK; ++e)
         oacc[blk][e] = oacc[blk][e] * f0 + xo[(2 + blk * (NACC / DBLK) + e) * 64] * f1;
+  } else {
+    // every wavefront is done with the stages (and every fetch has landed)
+    // before any of them is overwritten by the output rows below
+    __syncthreads();
   }
 
-  // ---- 5. normalise and store -----------------------------------------------
+  // ---- 5. normalise, stage the rows in LDS, store whole rows -----------------
+  // O^T holds one query row per lane column, so stored straight from the
+  // registers each instruction would write 8-byte pieces of RW different rows
+  // (measured: the long prefill's 128 MB of output at 1.6 TB/s). The wavefront
+  // writes its normalised bf16 rows into its own part of the stage area
+  // instead (16-byte chunk c of row r at c ^ (r & 15): rows 1 KB apart fall on
+  // different banks) and stores them back row by row: each store instruction
+  // writes 64 consecutive 16-byte chunks of the output. Where the stage area
+  // cannot hold every wavefront's whole rows, the columns go in NPASS passes.
   float l_tot = l_run;
   if constexpr (RW == 16) l_tot += lane_xor(l_tot, 16);
   l_tot += lane_xor(l_tot, 32);
-  if (row_ok) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* op = (uint16_t*)p.out + ((b * p.Hq + h) * p.S_q + s) * (int64_t)DV;
-    if constexpr (RW == 32) {
-      // O^T lane l: row l % 32, d = 32*blk + 8*i + 4*(l/32) + jj
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  constexpr int NPASS = XO_BYTES + NWR * RW * DV * 2 <= NSTAGE * STAGE_BYTES ? 1 : 2;
+  constexpr int DVP = DV / NPASS;                      // columns per pass
+  static_assert(XO_BYTES + NWR * RW * DVP * 2 <= NSTAGE * STAGE_BYTES, "output staging area");
+  constexpr int CPRO = DVP / 8;                        // 16-byte chunks per staged row
+  constexpr int OSWZ = CPRO >= 16 ? 15 : CPRO - 1;
+  constexpr int RPO = 64 / CPRO;                       // rows per store instruction
+  static_assert(64 % CPRO == 0 && RW % RPO == 0 && DBLK % NPASS == 0, "output rows per store");
+  const unsigned ost = (lds_addr(stages) + (unsigned)(XO_BYTES + rg * RW * DVP * 2)) & kLdsMask;
+  auto ost_at = [&](int r, int c) { return (unsigned)(r * DVP * 2 + 16 * (c ^ (r & OSWZ))); };
 #pragma unroll
-      for (int blk = 0; blk < DBLK; ++blk)
+  for (int pass = 0; pass < NPASS; ++pass) {
+    constexpr int BPP = DBLK / NPASS;                  // d blocks per pass
+    if constexpr (RW == 32) {
+      // O^T lane l: row l % 32, d = 32*blk + 8*i + 4*(l/32) + jj: chunk 4*blk + i
+      // of the pass, bytes 8*(l/32) .. +7
+#pragma unroll
+      for (int bb = 0; bb < BPP; ++bb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          const int blk = pass * BPP + bb;
           u32x2 pk;
           pk.x = pack_bf16x2(oacc[blk][4 * i + 0] * inv, oacc[blk][4 * i + 1] * inv);
           pk.y = pack_bf16x2(oacc[blk][4 * i + 2] * inv, oacc[blk][4 * i + 3] * inv);
-          *reinterpret_cast<u32x2*>(op + 32 * blk + 8 * i + 4 * grp) = pk;
+          *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+              (size_t)(ost + ost_at(col, 4 * bb + i) + 8 * grp)) = pk;
         }
     } else {
-      // O^T lane l: row l % 16, d = 16*blk + 4*(l/16) + e
+      // O^T lane l: row l % 16, d = 16*blk + 4*(l/16) + e: chunk 2*blk + (l/16)/2
+      // of the pass, bytes 8*((l/16) % 2) .. +7
 #pragma unroll
-      for (int blk = 0; blk < DBLK; ++blk) {
+      for (int bb = 0; bb < BPP; ++bb) {
+        const int blk = pass * BPP + bb;
         u32x2 pk;
         pk.x = pack_bf16x2(oacc[blk][0] * inv, oacc[blk][1] * inv);
         pk.y = pack_bf16x2(oacc[blk][2] * inv, oacc[blk][3] * inv);
-        *reinterpret_cast<u32x2*>(op + 16 * blk + 4 * grp) = pk;
+        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+            (size_t)(ost + ost_at(col, 2 * bb + (grp >> 1)) + 8 * (grp & 1))) = pk;
       }
+    }
+    // back row by row (this wavefront's own LDS: no barrier; the compiler
+    // waits for the writes before the reads, and LDS accesses of one
+    // wavefront take effect in order, so the next pass overwrites only what
+    // was read)
+#pragma unroll
+    for (int k = 0; k < RW / RPO; ++k) {
+      const int rl = k * RPO + lane / CPRO, c = lane % CPRO;
+      const u32x4 v = lds_at<u32x4>(ost, ost_at(rl, c));
+      const int rr = RW * rg + rl;   // the workgroup's row: token rr / G of the tile, head rr % G
+      const int so = s0 + rr / G;
+      if (rr < MQ * G && so < p.S_q)
+        *reinterpret_cast<u32x4*>((uint16_t*)p.out + ((b * p.Hq + hk * G + rr % G) * p.S_q + so) * (int64_t)DV +
+                                  pass * DVP + 8 * c) = v;
     }
   }
 }
