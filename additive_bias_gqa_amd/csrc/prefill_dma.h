@@ -1150,17 +1150,22 @@ namespace {
 // workgroup's own bias scan finds (build_live_list), computed once per batch
 // row instead of once per KV head, by a grid that keeps the memory busy.
 // One workgroup per (b, query tile, word = 32 key tiles = 1024 keys); a word
-// wholly at or past nonpad is written 0 without loads.
+// wholly at or past nonpad is written 0 without loads. The word is the slowest
+// index of the grid: consecutive workgroups are dealt round-robin over the
+// XCDs, and with the word fastest every workgroup of a low word (the ones below
+// nonpad, which do the loads) could land on the same few XCDs (one word in
+// four below nonpad, 8 words: all on 2 of the 8), leaving the others idle.
 template <typename BiasT>
 __global__ __launch_bounds__(256) void tilemap_kernel(const BiasT* __restrict__ bias,
                                                       const int64_t* __restrict__ nonpad,
                                                       uint32_t* __restrict__ map, int S_q, int T,
                                                       int MQ, int n_qt, int n_words) {
   __shared__ uint32_t s_word;
-  const int wid = blockIdx.x;
-  const int word = wid % n_words;
-  const int qt = (wid / n_words) % n_qt;
-  const int64_t b = wid / (n_words * n_qt);
+  const int n_bq = gridDim.x / n_words;          // (b, query tile) pairs
+  const int word = blockIdx.x / n_bq;
+  const int qt = (blockIdx.x % n_bq) % n_qt;
+  const int64_t b = (blockIdx.x % n_bq) / n_qt;
+  const int wid = (int)(b * n_qt + qt) * n_words + word;   // the map's layout: [b][query tile][word]
   const int np = (int)clamp_nonpad(nonpad[b], T);
   const int s0 = qt * MQ, nrows = min(MQ, S_q - s0);
   const int j_lo = word * 32 * kTileKeys, j_hi = min(j_lo + 32 * kTileKeys, np);
