@@ -61,14 +61,17 @@ hipError_t launch_dma_d(const AttnParams& p, hipStream_t stream) {
 
 // The direct-to-LDS path needs 16-byte-aligned global chunks for every fetch:
 // bias rows (max_seq * bias element size) and slot-kind rows (max_seq * 4) must
-// be multiples of 16 bytes, and the live list must fit next to the stages. Its
+// be multiples of 16 bytes, and the live list must fit next to the stages: at
+// kDmaMaxSeq slots it takes 2048 * 2 bytes of tile numbers and 64 map words
+// (4.3 KiB of the 6 KiB the stages leave; every configuration has at least 128
+// threads to load the 64 words). Its
 // bias stage is sized for grouped heads (G >= 2: at most RW*NW/2 tokens per
 // workgroup); one head per KV head takes the register-staged kernels.
 bool prefill_dma_supported(const AttnParams& p) {
   if (p.D != 64 && p.D != 128 && p.D != 256 && p.D != 512) return false;
   if (p.Dv != p.D && !dma_dv_pair(p.D, p.Dv)) return false;
   if (p.G < 2) return false;   // the bias stage holds the rows of G >= 2 heads per token
-  if (p.T > 32768) return false;
+  if (p.T > kDmaMaxSeq) return false;
   if (p.bias != nullptr) {
     if ((p.T % (p.bias_is_bf16 ? 8 : 4)) != 0) return false;
   } else if (p.slot_kind != nullptr) {
@@ -85,7 +88,7 @@ size_t prefill_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q, 
   if (D != 64 && D != 128 && D != 256 && D != 512) return 0;
   if (D_v != D && !dma_dv_pair((int)D, (int)D_v)) return 0;
   const int64_t G = Hq / Hkv;
-  if (G < 2 || G > 64 || max_seq > 32768) return 0;
+  if (G < 2 || G > 64 || max_seq > kDmaMaxSeq) return 0;
   const int64_t rows = D_v != D ? dv_rows(B, Hkv, S_q, G) : dma_rows((int)D, B, Hkv, S_q, G);
   const int64_t mq = rows / G;
   const int64_t n_qt = (S_q + mq - 1) / mq;

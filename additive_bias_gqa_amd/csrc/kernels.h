@@ -100,6 +100,8 @@ hipError_t launch_attn_prefill(const AttnParams& p, hipStream_t stream);
 // direct-to-LDS prefill pipeline (attn_prefill_dma.hip) and when it applies
 // (the only prefill path for D != Dv: D = 256 with Dv = 512, or the reverse)
 bool prefill_dma_supported(const AttnParams& p);
+// longest cache the direct-to-LDS prefill takes (its live-tile list lives in LDS)
+constexpr int kDmaMaxSeq = 65536;
 hipError_t launch_attn_prefill_dma(const AttnParams& p, hipStream_t stream);
 // scratch bytes the prefill path can use for this shape (its live-tile map)
 size_t prefill_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q, int64_t max_seq,

@@ -224,6 +224,7 @@ struct DmaGeom {
 
 }  // namespace
 
+static_assert(kDmaMaxSeq / 1024 <= 128, "map words of the longest cache: one per thread");
 template <int D, int RW, int NW, bool kRules, typename BiasT, bool kQReg, int KS, int DV = D>
 __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p, int n_qt) {
   using Geo = DmaGeom<D, RW, NW, kRules, BiasT, kQReg, KS, DV>;
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
   const int h = hk * G + g;
   // this workgroup's words of the live-tile map (bias variant with a
   // workspace), loaded before anything waits so that they share the first
-  // memory round trip with Q (n_words <= 32 <= NT: at most 32768 slots)
+  // memory round trip with Q (n_words <= kDmaMaxSeq / 1024 = 64 <= NT)
   const uint32_t* map_row =
       (!kRules && p.tilemap) ? p.tilemap + ((size_t)(b * n_qt + qt)) * n_words : nullptr;
   const uint32_t map_pre = (map_row && tid < n_words) ? map_row[tid] : 0u;

@@ -177,7 +177,7 @@ abgqa_status kv_scatter_and_bias(void *k_cache, void *v_cache, const void *k_upd
  *                    layer with another head size). bf16 decode runs on the
  *                    matrix cores for D_v == D and for (D, D_v) = (256, 512) or
  *                    (512, 256), and so does bf16 prefill (for those two pairs
- *                    when Hq > Hkv, 8 <= max_seq <= 32768 and the bias rows,
+ *                    when Hq > Hkv, 8 <= max_seq <= 65536 and the bias rows,
  *                    or slot-kind rows, are whole 16-byte chunks); other
  *                    cases take a vector-ALU path (fp32 arithmetic) with the
  *                    same results.

@@ -662,13 +662,14 @@ def test_graph_replay_decode_and_prefill(variant):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("S_q,T,D", [
-    (1, 40000, 64),      # decode over a cache longer than the prefill fast path's limit
-    (24, 32768, 128),    # prefill at the direct-to-LDS path's longest cache
-    (24, 40000, 128),    # prefill past it: the register-staged kernel
+@pytest.mark.parametrize("S_q,T,D,W", [
+    (1, 70000, 64, 3000),     # decode over a cache longer than the prefill fast path's limit
+    (24, 65536, 128, 3000),   # prefill at the direct-to-LDS path's longest cache (64 map words)
+    (40, 65536, 512, 0),      # the same on the 32-row kernel, no window: all 2048 tiles live
+    (24, 70000, 128, 3000),   # prefill past it: the register-staged kernel
 ])
-def test_long_cache(S_q, T, D):
-    """The longest caches each path takes, every slot valid, a window and a bias."""
+def test_long_cache(S_q, T, D, W):
+    """The longest caches each path takes, every slot valid, a bias (a window or none)."""
     rng = wl.rng_for(730 + S_q + T)
     B, Hq, Hkv = 1, 4, 2
     q = wl.normal(rng, (B, Hq, S_q, D), torch.bfloat16)
@@ -676,14 +677,13 @@ def test_long_cache(S_q, T, D):
     v = wl.normal(rng, (B, Hkv, T, D), torch.bfloat16)
     nonpad = torch.tensor([T], dtype=torch.int64)
     q_start = nonpad - S_q
-    bias = torch.from_numpy(oracle.bias(nonpad, q_start, None, S_q, T, 3000)).to(torch.bfloat16)
-    announce(f"long cache S_q={S_q} T={T} D={D}")
+    bias = torch.from_numpy(oracle.bias(nonpad, q_start, None, S_q, T, W)).to(torch.bfloat16)
+    announce(f"long cache S_q={S_q} T={T} D={D} W={W}")
     scale = 1.0 / math.sqrt(D)
     got = fwd(dev(q), dev(k), dev(v), dev(bias), dev(nonpad), scale)
     ref = oracle.attention(q, k, v, bias, nonpad, scale)
     check_parity(to_f64(got), ref, torch.bfloat16, dead_rows(bias.float().numpy(), nonpad, Hq), f"long/{T}")
-    got_r = fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale, q_start=dev(q_start),
-                                 window=3000)
+    got_r = fwd(dev(q), dev(k), dev(v), None, dev(nonpad), scale, q_start=dev(q_start), window=W)
     check_parity(to_f64(got_r), ref, torch.bfloat16, dead_rows(bias.float().numpy(), nonpad, Hq), f"long/{T}/rules")
 
 
