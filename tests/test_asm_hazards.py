@@ -6,9 +6,10 @@ MFMA that reads a register a VALU instruction wrote (the softmax weights P^T,
 or an accumulator rewritten by the rescale) needs two wait states in between
 (CDNA3/CDNA4 ISA, MFMA dependency rules: VALU write of a VGPR followed by an
 MFMA read of it is not interlocked). This test disassembles the gfx950 code of
-the built library and checks every such MFMA: scanning back from it to the
-previous MFMA, the last VALU write of one of its source registers must be at
-least two wait states earlier (s_nop N counts N + 1, any other instruction 1).
+the built library and checks every such MFMA: scanning back from it (past
+other MFMAs: VALU work is interleaved with them), the last VALU write of one
+of its source registers must be at least two wait states earlier (s_nop N
+counts N + 1, any other instruction 1).
 The other direction too: a VALU read of an accumulator (v_accvgpr_read) must
 come at least passes + 2 wait states after the MFMA that wrote it; 18 is
 taken (16 passes + 2, more than a 32x32x16 MFMA takes).
@@ -62,11 +63,11 @@ def _min_wait_states(ins):
         asrc = _regs(m.group(7), m.group(8))
         ws = 0
         for k in range(1, 64):
-            if i - k < 0:
+            # VALU work may sit between the MFMAs: scan back past them (each
+            # counts one wait state) until the distance no longer matters
+            if i - k < 0 or ws >= NEED:
                 break
             prev = ins[i - k]
-            if prev.startswith("v_mfma"):
-                break
             d = DEST.match(prev)
             if d:
                 lo = d.group(3) if d.group(3) is not None else d.group(5)
@@ -125,3 +126,15 @@ def test_asm_mfma_operands_have_wait_states(tmp_path):
                 assert worst >= NEED_READ, f"{sym}: an accumulator is read {worst} wait states after its MFMA"
     # the 32-row kernels with accumulation-register O^T are built and checked
     assert checked > 0
+
+
+def test_scanner_sees_writes_behind_other_mfmas():
+    """The scan counts an MFMA between a VALU write and the MFMA reading it as
+    one wait state (it does not stop there), and an s_nop N as N + 1."""
+    mf = "v_mfma_f32_32x32x16_bf16 a[0:15], v[20:23], v[{0}:{1}], a[0:15]"
+    bad = ["v_pack_b32_f16 v10, v1, v2", mf.format(30, 33), mf.format(8, 11)]
+    assert _min_wait_states(bad) == (2, 1)
+    ok = ["v_pack_b32_f16 v10, v1, v2", "s_nop 1", mf.format(8, 11)]
+    assert _min_wait_states(ok)[1] >= NEED
+    far = ["v_pack_b32_f16 v10, v1, v2", mf.format(30, 33), mf.format(40, 43), mf.format(8, 11)]
+    assert _min_wait_states(far)[1] >= NEED
