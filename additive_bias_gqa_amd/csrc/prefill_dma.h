@@ -1150,41 +1150,46 @@ namespace {
 // of key tile kt below nonpad (a bias entry other than -inf) - the set a
 // workgroup's own bias scan finds (build_live_list), computed once per batch
 // row instead of once per KV head, by a grid that keeps the memory busy.
-// One workgroup per (b, query tile, word = 32 key tiles = 1024 keys); a word
-// wholly at or past nonpad is written 0 without loads. The word is the slowest
-// index of the grid: consecutive workgroups are dealt round-robin over the
-// XCDs, and with the word fastest every workgroup of a low word (the ones below
-// nonpad, which do the loads) could land on the same few XCDs (one word in
-// four below nonpad, 8 words: all on 2 of the 8), leaving the others idle.
+// One workgroup per (b, query tile, byte of a word = 8 key tiles = 256 keys),
+// which writes its byte of the word; a byte wholly at or past nonpad is
+// written 0 without loads. Small workgroups keep many of them in flight on
+// every CU, so the pass costs about one memory round trip. The byte is the
+// slowest index of the grid: consecutive workgroups are dealt round-robin over
+// the XCDs, and with the byte fastest every workgroup of a low word (the ones
+// below nonpad, which do the loads) could land on the same few XCDs, leaving
+// the others idle.
+constexpr int kMapTilesPerGroup = 8;
 template <typename BiasT>
 __global__ __launch_bounds__(256) void tilemap_kernel(const BiasT* __restrict__ bias,
                                                       const int64_t* __restrict__ nonpad,
                                                       uint32_t* __restrict__ map, int S_q, int T,
                                                       int MQ, int n_qt, int n_words) {
-  __shared__ uint32_t s_word;
-  const int n_bq = gridDim.x / n_words;          // (b, query tile) pairs
-  const int word = blockIdx.x / n_bq;
+  constexpr int GPW = 32 / kMapTilesPerGroup;    // workgroups (bytes) per word
+  __shared__ uint32_t s_bits;
+  const int n_bq = gridDim.x / (n_words * GPW);  // (b, query tile) pairs
+  const int unit = blockIdx.x / n_bq;            // word * GPW + byte
   const int qt = (blockIdx.x % n_bq) % n_qt;
   const int64_t b = (blockIdx.x % n_bq) / n_qt;
-  const int wid = (int)(b * n_qt + qt) * n_words + word;   // the map's layout: [b][query tile][word]
+  const int wid = (int)(b * n_qt + qt) * n_words + unit / GPW;   // the map's layout: [b][query tile][word]
+  uint8_t* const out = reinterpret_cast<uint8_t*>(map + wid) + unit % GPW;
   const int np = (int)clamp_nonpad(nonpad[b], T);
   const int s0 = qt * MQ, nrows = min(MQ, S_q - s0);
-  const int j_lo = word * 32 * kTileKeys, j_hi = min(j_lo + 32 * kTileKeys, np);
+  const int j_lo = unit * kMapTilesPerGroup * kTileKeys, j_hi = min(j_lo + kMapTilesPerGroup * kTileKeys, np);
   if (j_lo >= np || nrows <= 0) {
-    if (threadIdx.x == 0) map[wid] = 0u;
+    if (threadIdx.x == 0) *out = 0;
     return;
   }
-  if (threadIdx.x == 0) s_word = 0u;
+  if (threadIdx.x == 0) s_bits = 0u;
   __syncthreads();
   constexpr int EPV = 16 / (int)sizeof(BiasT);
-  constexpr int CPW = 32 * kTileKeys / EPV;   // 16-byte chunks of a row's 1024 keys
-  constexpr int RPP = 256 / CPW;              // rows per pass
+  constexpr int CPW = kMapTilesPerGroup * kTileKeys / EPV;   // 16-byte chunks of a row's 256 keys
+  constexpr int RPP = 256 / CPW;                             // rows per pass
   const int c = threadIdx.x % CPW, rr = threadIdx.x / CPW;
   const int j = j_lo + c * EPV;               // rows are multiples of 16 bytes
   bool any = false;
   if (j < j_hi) {
     const BiasT* col = bias + ((int64_t)b * S_q + s0) * T + j;
-    constexpr int U = 16;  // loads in flight per thread (rows past the tile repeat its last)
+    constexpr int U = 8;  // loads in flight per thread (rows past the tile repeat its last)
     for (int r0 = rr; r0 < nrows; r0 += U * RPP) {
       u32x4 raw[U];
 #pragma unroll
@@ -1203,9 +1208,9 @@ __global__ __launch_bounds__(256) void tilemap_kernel(const BiasT* __restrict__ 
   unsigned bits = any ? 1u << ((c * EPV) / kTileKeys) : 0u;
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) bits |= (unsigned)__shfl_xor((int)bits, m);
-  if ((threadIdx.x & 63) == 0 && bits) atomicOr(&s_word, bits);
+  if ((threadIdx.x & 63) == 0 && bits) atomicOr(&s_bits, bits);
   __syncthreads();
-  if (threadIdx.x == 0) map[wid] = s_word;
+  if (threadIdx.x == 0) *out = (uint8_t)s_bits;
 }
 
 template <int D, int RW, int NW, bool kRules, typename BiasT, bool kQReg, int KS, int DV>
@@ -1234,7 +1239,8 @@ hipError_t launch_dma_inst(const AttnParams& p, hipStream_t stream) {
     const int n_words = (n_kt + 31) / 32;
     const size_t need = (size_t)p.B * n_qt * n_words * sizeof(uint32_t);
     if (p.ws != nullptr && p.ws_bytes >= need) {
-      hipLaunchKernelGGL(tilemap_kernel<BiasT>, dim3((unsigned)((int64_t)p.B * n_qt * n_words)), dim3(256),
+      hipLaunchKernelGGL(tilemap_kernel<BiasT>,
+                         dim3((unsigned)((int64_t)p.B * n_qt * n_words * (32 / kMapTilesPerGroup))), dim3(256),
                          0, stream, (const BiasT*)p.bias, p.nonpad, (uint32_t*)p.ws, p.S_q, p.T, MQ, n_qt,
                          n_words);
       const hipError_t e = hipGetLastError();
