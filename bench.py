@@ -489,7 +489,7 @@ def main():
             secondary[name] = dict(
                 attn_us=round(r["attn_ms"] * 1e3, 2), step_us=round(r["ms_per_step"] * 1e3, 2),
                 steps=r["steps"], rotating_input_sets=r["n_sets"],
-                roofline=r["roofline"], step_gbs=round(r["step_gbs"], 1),
+                roofline=dict(r["roofline"], traffic=traffic_for(name)), step_gbs=round(r["step_gbs"], 1),
                 config=r["desc"])
             if "hbm_side" in r:
                 secondary[name]["hbm_side"] = r["hbm_side"]
