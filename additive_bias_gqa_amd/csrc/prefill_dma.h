@@ -1238,9 +1238,11 @@ hipError_t launch_dma_inst(const AttnParams& p, hipStream_t stream) {
     // the live-tile map, when the caller's scratch holds it
     const int n_words = (n_kt + 31) / 32;
     const size_t need = (size_t)p.B * n_qt * n_words * sizeof(uint32_t);
-    if (p.ws != nullptr && p.ws_bytes >= need) {
-      hipLaunchKernelGGL(tilemap_kernel<BiasT>,
-                         dim3((unsigned)((int64_t)p.B * n_qt * n_words * (32 / kMapTilesPerGroup))), dim3(256),
+    const int64_t map_groups = (int64_t)p.B * n_qt * n_words * (32 / kMapTilesPerGroup);
+    // (a launch covers fewer than 2^32 work-items; past that the workgroups
+    // scan their bias rows themselves)
+    if (p.ws != nullptr && p.ws_bytes >= need && map_groups * 256 <= (int64_t)UINT32_MAX) {
+      hipLaunchKernelGGL(tilemap_kernel<BiasT>, dim3((unsigned)map_groups), dim3(256),
                          0, stream, (const BiasT*)p.bias, p.nonpad, (uint32_t*)p.ws, p.S_q, p.T, MQ, n_qt,
                          n_words);
       const hipError_t e = hipGetLastError();

@@ -350,7 +350,8 @@ def write_traffic(name, fetch_csv, write_csv, copy_bytes=1 << 30):
     Each counter is scaled by what it reads for the plain 1 GiB device copy
     that bench.py runs first (the largest __amd_rocclr_copyBuffer dispatch):
     scale = copy bytes / (counter KiB * 1024). The attention call is every
-    abgqa::attn_* kernel it launches, averaged per dispatch and summed."""
+    kernel it launches (abgqa::attn_*, and the prefill's live-tile map pass),
+    averaged per dispatch and summed."""
     import csv
     import collections
 
@@ -362,7 +363,7 @@ def write_traffic(name, fetch_csv, write_csv, copy_bytes=1 << 30):
                 k, v = r["Kernel_Name"], float(r["Counter_Value"])
                 if k == "__amd_rocclr_copyBuffer":
                     copy_max = max(copy_max, v)
-                elif k.startswith("void abgqa::attn_"):
+                elif k.startswith("void abgqa::attn_") or "tilemap_kernel" in k:
                     per[k].append(v)
         if not per or copy_max <= 0:
             raise SystemExit(f"{path}: no attention or copy dispatches found")
