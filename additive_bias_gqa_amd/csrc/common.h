@@ -72,9 +72,21 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-// exchange with lane ^ mask through the LDS crossbar (no LDS memory used)
+// exchange with lane ^ mask. Masks 16 and 32 use the gfx950 lane-swap
+// instructions on the vector ALU: v_permlane16_swap / v_permlane32_swap of v
+// with itself leave the lower and the upper partner half of each 32- (or
+// 64-) lane group in two registers (lane l: v[l & ~m] and v[l | m], checked
+// lane by lane on the device), and the lane picks the one that is not its
+// own. Other masks go through the LDS crossbar (ds_bpermute, no LDS memory
+// used), which queues behind the workgroup's LDS traffic.
 __device__ __forceinline__ float lane_xor(float v, int mask) {
   const int lane = __lane_id();
+  if (mask == 32 || mask == 16) {
+    const unsigned u = __float_as_uint(v);
+    const auto r = mask == 32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                              : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float((lane & mask) ? r[0] : r[1]);
+  }
   return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(v)));
 }
 

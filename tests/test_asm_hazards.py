@@ -26,6 +26,7 @@ import additive_bias_gqa_amd as ab
 OBJDUMP = "/opt/rocm/llvm/bin/llvm-objdump"
 MFMA = re.compile(r"v_mfma_f32_32x32x16_bf16 a\[(\d+):(\d+)\], v\[(\d+):(\d+)\], v\[(\d+):(\d+)\], a\[(\d+):(\d+)\]")
 DEST = re.compile(r"^(v_\S+)\s+([va])(?:\[(\d+):(\d+)\]|(\d+))\b")
+SWAP_SRC = re.compile(r"^v_permlane(?:16|32)_swap\S*\s+v\d+,\s*v(\d+)")
 NEED = 2
 NEED_READ = 18
 
@@ -73,6 +74,11 @@ def _min_wait_states(ins):
                 lo = d.group(3) if d.group(3) is not None else d.group(5)
                 hi = d.group(4) if d.group(4) is not None else d.group(5)
                 written = _regs(lo, hi)
+                if d.group(1).startswith(("v_permlane16_swap", "v_permlane32_swap")):
+                    # a lane swap writes both of its operands
+                    sw = SWAP_SRC.match(prev)
+                    if sw:
+                        written |= {int(sw.group(1))}
                 if written & (vsrc if d.group(2) == "v" else asrc):
                     worst = min(worst, ws)
                     break
@@ -138,3 +144,6 @@ def test_scanner_sees_writes_behind_other_mfmas():
     assert _min_wait_states(ok)[1] >= NEED
     far = ["v_pack_b32_f16 v10, v1, v2", mf.format(30, 33), mf.format(40, 43), mf.format(8, 11)]
     assert _min_wait_states(far)[1] >= NEED
+    # both operands of a lane swap are written
+    swap = ["v_permlane32_swap_b32_e32 v3, v9", mf.format(8, 11)]
+    assert _min_wait_states(swap) == (1, 0)
