@@ -148,12 +148,33 @@ __device__ __forceinline__ int build_live_list(const AttnParams& p, int64_t b, i
     }
   } else {
     // causal + window: the rows' key intervals lie in [a, z] (q is consecutive
-    // over the rows; a circular cache: every valid slot)
-    int a = 0, z = -1;
+    // over the rows); a circular cache: in the slots of positions
+    // [max(q_first - W + 1, oldest held), min(q_last, L - 1)], one interval or,
+    // wrapping round the slots, two ([a, z] and [a2, z2])
+    int a = 0, z = -1, a2 = 0, z2 = -1;
     if (p.circular) {
-      // a circular cache: the rows' intervals may wrap round the slots; take
-      // every valid slot (the cache is about a window long)
-      z = np - 1;
+      if (s_end > s0) {
+        const RowRule r0 = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s0, p.S_q, T, p.window, true);
+        const int64_t L = p.nonpad[b] < 0 ? 0 : p.nonpad[b];
+        const int64_t oldest = L > T ? L - T : 0;
+        const int64_t q_last = r0.q + (s_end - 1 - s0);
+        int64_t plo = p.window > 0 ? r0.q - p.window + 1 : 0;
+        if (plo < oldest) plo = oldest;
+        const int64_t phi = q_last < L - 1 ? q_last : L - 1;
+        if (plo <= phi) {
+          if (phi - plo + 1 >= T) {
+            z = np - 1;
+          } else {
+            a = (int)(plo % T);
+            z = (int)(phi % T);
+            if (a > z) {   // wraps: [a, T - 1] and [0, z]
+              a2 = 0;
+              z2 = z;
+              z = T - 1;
+            }
+          }
+        }
+      }
     } else if (s_end > s0) {
       const RowRule r0 = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, s0, p.S_q, T, p.window, p.circular);
       const int64_t q_last = r0.q + (s_end - 1 - s0);
@@ -164,9 +185,11 @@ __device__ __forceinline__ int build_live_list(const AttnParams& p, int64_t b, i
       z = (int)(z64 < -1 ? -1 : z64);
     }
     if (!p.slot_kind) {
-      // every slot is text: the interval alone
+      // every slot is text: the interval(s) alone
       if (a <= z)
         for (int t = a / kTileKeys + tid; t <= z / kTileKeys; t += NT) atomicOr(&s_bits[t >> 5], 1u << (t & 31));
+      if (a2 <= z2)
+        for (int t = a2 / kTileKeys + tid; t <= z2 / kTileKeys; t += NT) atomicOr(&s_bits[t >> 5], 1u << (t & 31));
     } else {
       // the rows' image-block kinds (up to 4 distinct; more: any block key counts)
       for (int s = s0 + tid; s < s_end; s += NT) {
@@ -182,7 +205,8 @@ __device__ __forceinline__ int build_live_list(const AttnParams& p, int64_t b, i
       }
       __syncthreads();
       const int nids = s_nids;
-      // a tile is live if it holds a key that is no pad inside [a, z], or a
+      // a tile is live if it holds a key that is no pad inside [a, z] or
+      // [a2, z2], or a
       // key of one of the rows' blocks (a superset of the tiles some row
       // allows a key of; pad-only tiles drop out). Lanes 0-31 and 32-63 of a
       // wavefront read one tile each (NT is a multiple of 64), NB kinds per
@@ -197,7 +221,7 @@ __device__ __forceinline__ int build_live_list(const AttnParams& p, int64_t b, i
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
           const int j = base + u * NT;
-          bool hit = (kv[u] >= 0) && (j >= a) && (j <= z);
+          bool hit = (kv[u] >= 0) && (((j >= a) && (j <= z)) || ((j >= a2) && (j <= z2)));
           if (nids > 4) {
             hit |= kv[u] > 0;
           } else {
