@@ -351,14 +351,14 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
         const int incl = wave_incl_sum_i32(n) + carry;
         const int fst = incl - n;
         if (n > 0 && rank >= fst && rank < fst + n) { found = bb; f_first = fst; f_n = n; }
-        carry = __shfl(incl, 63);
+        carry = __builtin_amdgcn_readlane(incl, 63);
       }
       const uint64_t hit = __ballot(found >= 0);
       if (hit == 0) return;   // a rank past every row's splits: no work
-      const int src = __builtin_ctzll(hit);
-      b = __shfl(found, src);
-      first = __shfl(f_first, src);
-      nsp = __shfl(f_n, src);
+      const int src = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+      b = __builtin_amdgcn_readlane(found, src);
+      first = __builtin_amdgcn_readlane(f_first, src);
+      nsp = __builtin_amdgcn_readlane(f_n, src);
       split = rank - first;
     }
   }

@@ -103,32 +103,54 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// exp2 that maps -inf to exactly 0 (v_exp_f32 does) without NaN for finite input
-// minimum / maximum of an int over the 64 lanes of a wavefront
-__device__ __forceinline__ int wave_min_i32(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m));
+// Integer reductions over the 64 lanes of a wavefront, on the vector ALU: DPP
+// within each row of 16 lanes, then the 16- and 32-lane swaps (see lane_xor)
+// across rows. Every lane gets the result. (Shuffles through the LDS crossbar
+// would queue behind the workgroup's LDS traffic.)
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int lane_xor_i32(int v, int mask) {
+  return __float_as_int(lane_xor(__int_as_float(v), mask));
+}
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_i32(int v, Op op) {
+  v = op(v, dpp_i32<kDppQuadXor1>(v));
+  v = op(v, dpp_i32<kDppQuadXor2>(v));
+  v = op(v, dpp_i32<kDppRowHalfMirror>(v));
+  v = op(v, dpp_i32<kDppRowMirror>(v));
+  v = op(v, lane_xor_i32(v, 16));
+  v = op(v, lane_xor_i32(v, 32));
   return v;
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+  return wave_reduce_i32(v, [](int a, int b) { return a < b ? a : b; });
 }
 __device__ __forceinline__ int wave_max_i32(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m));
-  return v;
+  return wave_reduce_i32(v, [](int a, int b) { return a > b ? a : b; });
 }
 __device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
+  return wave_reduce_i32(v, [](int a, int b) { return a + b; });
 }
-// inclusive prefix sum over the lanes of a wavefront (lane order)
+__device__ __forceinline__ unsigned wave_or_u32(unsigned v) {
+  return (unsigned)wave_reduce_i32((int)v, [](int a, int b) { return a | b; });
+}
+// inclusive prefix sum over the lanes of a wavefront (lane order): within each
+// row of 16 by DPP row shifts (lanes shifted in from outside the row add 0),
+// then each row adds the totals of the rows before it (read from lanes 15, 31
+// and 47)
 __device__ __forceinline__ int wave_incl_sum_i32(int v) {
+  constexpr int kRowShr = 0x110;   // DPP row_shr:n = 0x110 + n
+  v += dpp_i32<kRowShr + 1>(v);
+  v += dpp_i32<kRowShr + 2>(v);
+  v += dpp_i32<kRowShr + 4>(v);
+  v += dpp_i32<kRowShr + 8>(v);
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
   const int lane = __lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(v, d);
-    if (lane >= d) v += t;
-  }
-  return v;
+  return v + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
 }
 // workgroup barrier for LDS data only: waits for this wavefront's LDS
 // accesses, not for its outstanding global loads (__syncthreads waits for both)
@@ -136,6 +158,7 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// exp2 that maps -inf to exactly 0 (v_exp_f32 does) without NaN for finite input
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // tanh(y) = 1 - 2 / (e^(2y) + 1), from the definition: e^(2y) = 2^(2y log2 e)

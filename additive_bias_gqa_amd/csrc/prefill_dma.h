@@ -1205,9 +1205,7 @@ __global__ __launch_bounds__(256) void tilemap_kernel(const BiasT* __restrict__ 
   }
   // OR the lanes' tile bits over the wavefront: one LDS atomic per wavefront
   // instead of one per lane on the same word
-  unsigned bits = any ? 1u << ((c * EPV) / kTileKeys) : 0u;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) bits |= (unsigned)__shfl_xor((int)bits, m);
+  const unsigned bits = wave_or_u32(any ? 1u << ((c * EPV) / kTileKeys) : 0u);
   if ((threadIdx.x & 63) == 0 && bits) atomicOr(&s_bits, bits);
   __syncthreads();
   if (threadIdx.x == 0) *out = (uint8_t)s_bits;
