@@ -153,7 +153,10 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   constexpr int NV = 16 / KPI;      // V loads per 16-key block
   constexpr int PART = (int)part_floats(NR, DV);
   constexpr int E = NR < 4 ? NR : 4;      // real rows per lane group (r = 4*grp + e)
-  constexpr bool kQinLds = D >= 256;      // keep the A operand out of VGPRs
+  // the A operand (Q) in LDS only for D = 512 (its 64 registers per lane do
+  // not fit beside the rest at two wavefronts per SIMD); below that in
+  // registers, which keeps its reads off the LDS queue of every block
+  constexpr bool kQinLds = D >= 512;
 
   __shared__ float s_p[kDecWaves][16][NR];  // softmax weights, key-major
   __shared__ float s_alpha[kDecWaves][NR];
