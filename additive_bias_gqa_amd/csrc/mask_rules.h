@@ -55,15 +55,15 @@ __device__ __forceinline__ int64_t default_q_start(int64_t np, int64_t S_q) {
   return qs < 0 ? 0 : qs;
 }
 
-__device__ __forceinline__ RowRule make_row_rule_circular(const int64_t* nonpad,
-                                                          const int64_t* q_start,
+__device__ __forceinline__ RowRule make_row_rule_circular(int64_t np_raw, bool has_qs,
+                                                          int64_t qs_raw,
                                                           const int32_t* slot_kind, int64_t b,
                                                           int64_t s, int64_t S_q, int64_t C,
                                                           int64_t window) {
   RowRule r;
-  const int64_t L = nonpad[b] < 0 ? 0 : nonpad[b];
+  const int64_t L = np_raw < 0 ? 0 : np_raw;
   r.np = L < C ? L : C;
-  const int64_t qs = q_start ? q_start[b] : default_q_start(L, S_q);
+  const int64_t qs = has_qs ? qs_raw : default_q_start(L, S_q);
   r.q = qs + s;
   r.window = window;
   const int64_t oldest = L > C ? L - C : 0;   // oldest position still held
@@ -89,14 +89,17 @@ __device__ __forceinline__ RowRule make_row_rule_circular(const int64_t* nonpad,
   return r;
 }
 
-__device__ __forceinline__ RowRule make_row_rule(const int64_t* nonpad, const int64_t* q_start,
-                                                 const int32_t* slot_kind, int64_t b, int64_t s,
-                                                 int64_t S_q, int64_t max_seq, int64_t window,
-                                                 bool circular = false) {
-  if (circular) return make_row_rule_circular(nonpad, q_start, slot_kind, b, s, S_q, max_seq, window);
+// The rule of row (b, s) from nonpad[b] and q_start[b] already loaded (has_qs
+// false: the default q_start); the one load left is the query slot's kind.
+__device__ __forceinline__ RowRule make_row_rule_from(int64_t np_raw, bool has_qs, int64_t qs_raw,
+                                                      const int32_t* slot_kind, int64_t b,
+                                                      int64_t s, int64_t S_q, int64_t max_seq,
+                                                      int64_t window, bool circular) {
+  if (circular)
+    return make_row_rule_circular(np_raw, has_qs, qs_raw, slot_kind, b, s, S_q, max_seq, window);
   RowRule r;
-  r.np = clamp_nonpad(nonpad[b], max_seq);
-  const int64_t qs = q_start ? q_start[b] : default_q_start(r.np, S_q);
+  r.np = clamp_nonpad(np_raw, max_seq);
+  const int64_t qs = has_qs ? qs_raw : default_q_start(r.np, S_q);
   r.q = qs + s;
   r.window = window;
   r.kind_q = (slot_kind && r.q >= 0 && r.q < max_seq) ? slot_kind[b * max_seq + r.q] : 0;
@@ -108,6 +111,14 @@ __device__ __forceinline__ RowRule make_row_rule(const int64_t* nonpad, const in
   r.hi = (int32_t)(hi < -1 ? -1 : hi);
   r.blk = r.kind_q > 0 ? r.kind_q : -1;
   return r;
+}
+
+__device__ __forceinline__ RowRule make_row_rule(const int64_t* nonpad, const int64_t* q_start,
+                                                 const int32_t* slot_kind, int64_t b, int64_t s,
+                                                 int64_t S_q, int64_t max_seq, int64_t window,
+                                                 bool circular = false) {
+  return make_row_rule_from(nonpad[b], q_start != nullptr, q_start ? q_start[b] : 0, slot_kind, b,
+                            s, S_q, max_seq, window, circular);
 }
 
 }  // namespace abgqa

@@ -15,9 +15,15 @@ namespace abgqa {
 // cache slot write_indices[b] + t; slots outside [0, max_seq) are dropped. A
 // circular cache (mask_rules.h) takes position write_indices[b] + t in slot
 // (position) mod max_seq instead, negative positions dropped. One thread moves
-// 16 bytes; a workgroup covers 256 / vec_per_row rows per step.
+// 16 bytes of a row (of each of the two caches when cache2 is given: K and V
+// rows of one head size, same write indices); a workgroup covers
+// 256 / vec_per_row rows per step. Every load of a row (the update chunks and
+// write_indices[b]) is issued before any is used, so a row costs one memory
+// round trip before its stores.
 __device__ __forceinline__ void scatter_rows(u32x4* __restrict__ cache,
                                              const u32x4* __restrict__ update,
+                                             u32x4* __restrict__ cache2,
+                                             const u32x4* __restrict__ update2,
                                              const int64_t* __restrict__ write_indices, int H,
                                              int max_seq, int S_new, int vec_per_row,
                                              int64_t n_rows, int64_t blk, int64_t nblk,
@@ -26,15 +32,30 @@ __device__ __forceinline__ void scatter_rows(u32x4* __restrict__ cache,
   const int sub = threadIdx.x / vec_per_row;
   const int c = threadIdx.x % vec_per_row;
   if (sub >= rows_per_iter) return;
+  const bool two = cache2 != nullptr;
   for (int64_t row = blk * rows_per_iter + sub; row < n_rows; row += nblk * rows_per_iter) {
-    const int64_t bh = row / S_new;
-    const int t = (int)(row - bh * S_new);
-    const int64_t b = bh / H;
+    int64_t bh, b;
+    int t;
+    if (n_rows <= 0x7fffffff) {   // 32-bit divisions when the indices fit
+      const uint32_t bh32 = (uint32_t)row / (uint32_t)S_new;
+      t = (int)((uint32_t)row - bh32 * (uint32_t)S_new);
+      bh = bh32;
+      b = bh32 / (uint32_t)H;
+    } else {
+      bh = row / S_new;
+      t = (int)(row - bh * S_new);
+      b = bh / H;
+    }
+    const int64_t src = row * vec_per_row + c;
+    const u32x4 u = update[src];
+    const u32x4 u2 = (two ? update2 : update)[src];
     int64_t slot = (write_indices ? write_indices[b] : 0) + t;
     if (slot < 0) continue;                     // dropped
     if (circular) slot %= max_seq;
     else if (slot >= max_seq) continue;         // dropped (no wrap-around)
-    cache[(bh * max_seq + slot) * vec_per_row + c] = update[row * vec_per_row + c];
+    const int64_t dst = (bh * max_seq + slot) * vec_per_row + c;
+    cache[dst] = u;
+    if (two) cache2[dst] = u2;
   }
 }
 
@@ -58,24 +79,38 @@ __device__ __forceinline__ void bias_chunks(T* __restrict__ bias, const int64_t*
                                             int64_t n_chunks, bool vec, int64_t blk, int64_t nblk,
                                             bool circular) {
   for (int64_t idx = blk * 256 + threadIdx.x; idx < n_chunks; idx += nblk * 256) {
-    const int64_t row = idx / chunks_per_row;
-    const int j0 = (int)(idx - row * chunks_per_row) * 8;
-    const int64_t b = row / S_q;
-    const int s = (int)(row - b * S_q);
-    const RowRule rule = make_row_rule(nonpad, q_start, slot_kind, b, s, S_q, max_seq, window, circular);
+    int64_t row, b;
+    int j0, s;
+    if (n_chunks <= 0x7fffffff) {   // 32-bit divisions when the indices fit
+      const uint32_t r32 = (uint32_t)idx / (uint32_t)chunks_per_row;
+      const uint32_t b32 = r32 / (uint32_t)S_q;
+      j0 = (int)((uint32_t)idx - r32 * (uint32_t)chunks_per_row) * 8;
+      s = (int)(r32 - b32 * (uint32_t)S_q);
+      row = r32;
+      b = b32;
+    } else {
+      row = idx / chunks_per_row;
+      j0 = (int)(idx - row * chunks_per_row) * 8;
+      b = row / S_q;
+      s = (int)(row - b * S_q);
+    }
     const int32_t* kind_row = slot_kind ? slot_kind + b * max_seq : nullptr;
+    // Every load that does not need the rule goes out first (the chunk's slot
+    // kinds beside nonpad[b] and q_start[b]), so a chunk waits for two memory
+    // round trips: those loads, then the query slot's kind.
+    // (q_start is read without a branch: from nonpad when absent, unused then.)
+    const int64_t np_raw = nonpad[b];
+    const int64_t qs_raw = (q_start ? q_start : nonpad)[b];
+    int4 k0 = make_int4(0, 0, 0, 0), k1 = make_int4(0, 0, 0, 0);
+    if (vec && kind_row) {
+      k0 = ld_global<int4>(kind_row + j0);
+      k1 = ld_global<int4>(kind_row + j0 + 4);
+    }
+    const RowRule rule = make_row_rule_from(np_raw, q_start != nullptr, qs_raw, slot_kind, b, s, S_q,
+                                            max_seq, window, circular);
     T* out = bias + row * max_seq + j0;
     if (vec) {
-      int32_t kinds[8];
-      if (kind_row) {
-        const int4 k0 = ld_global<int4>(kind_row + j0);
-        const int4 k1 = ld_global<int4>(kind_row + j0 + 4);
-        kinds[0] = k0.x; kinds[1] = k0.y; kinds[2] = k0.z; kinds[3] = k0.w;
-        kinds[4] = k1.x; kinds[5] = k1.y; kinds[6] = k1.z; kinds[7] = k1.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kinds[e] = 0;
-      }
+      const int32_t kinds[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
       T v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)

@@ -21,10 +21,8 @@ __global__ __launch_bounds__(256) void prepare_kernel(
     const int32_t* __restrict__ slot_kind, int S_q, int64_t window, int chunks_per_row,
     int64_t n_chunks, bool vec, bool circular) {
   if ((int)blockIdx.x < n_scatter) {
-    scatter_rows(k_cache, k_update, write_indices, H, max_seq, S_new, vec_per_row, n_rows,
-                 blockIdx.x, n_scatter, circular);
-    scatter_rows(v_cache, v_update, write_indices, H, max_seq, S_new, vec_per_row, n_rows,
-                 blockIdx.x, n_scatter, circular);
+    scatter_rows(k_cache, k_update, v_cache, v_update, write_indices, H, max_seq, S_new,
+                 vec_per_row, n_rows, blockIdx.x, n_scatter, circular);
   } else {
     bias_chunks<T>(bias, nonpad, q_start, slot_kind, S_q, max_seq, window, chunks_per_row, n_chunks,
                    vec, blockIdx.x - n_scatter, gridDim.x - n_scatter, circular);

@@ -15,8 +15,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     u32x4* __restrict__ cache, const u32x4* __restrict__ update,
     const int64_t* __restrict__ write_indices, int H, int max_seq, int S_new,
     int vec_per_row, int64_t n_rows, bool circular) {
-  scatter_rows(cache, update, write_indices, H, max_seq, S_new, vec_per_row, n_rows, blockIdx.x,
-               gridDim.x, circular);
+  scatter_rows(cache, update, nullptr, nullptr, write_indices, H, max_seq, S_new, vec_per_row,
+               n_rows, blockIdx.x, gridDim.x, circular);
 }
 
 int64_t scatter_blocks(int64_t n_rows, int vec_per_row) {
