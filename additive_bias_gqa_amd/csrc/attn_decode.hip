@@ -169,7 +169,10 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   __shared__ float s_o[kParMerge ? NW * NR * DV : NR * DV];
   __shared__ __align__(16) __bf16 s_q[kQinLds ? NR * D : 8];  // Q rows (A operand)
   __shared__ int s_rlo[kDecWaves], s_rhi[kDecWaves];
-  __shared__ int32_t s_kq[16];
+  // rules variant: the 32-bit rule of each query token s < S_q of batch row b,
+  // made once per workgroup (the lanes read it instead of loading nonpad,
+  // q_start and the query slot's kind themselves)
+  __shared__ int32_t s_rule[16][8];
   // several splits per row: live samples of every batch row
   __shared__ int s_cnt[kMaxBalanceRows];
 
@@ -284,6 +287,17 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   // row allows - the bias entry not -inf, or the in-kernel rule, which gives
   // the same mask, so both variants balance alike. One load (or rule) per
   // sample: 64 per row of 8192 keys.
+  auto make_rules = [&](int64_t bq) {
+    if constexpr (kRules) {
+      if (tid < p.S_q) {
+        const RowRule rr = make_row_rule(p.nonpad, p.q_start, p.slot_kind, bq, tid, p.S_q, T, p.window, p.circular);
+        int32_t* d = s_rule[tid];
+        d[0] = rr.np32; d[1] = rr.lo; d[2] = rr.hi; d[3] = rr.blk;
+        d[4] = rr.lo2; d[5] = rr.hi2; d[6] = rr.kind_q; d[7] = 0;
+      }
+    }
+  };
+  make_rules(b);
   if (multi) {
     for (int i = tid; i < p.B; i += kDecThreads) s_cnt[i] = 0;
     lds_barrier();
@@ -294,19 +308,23 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
     for (int i = tid; i < p.B * ns; i += kDecThreads) {
       const int bb = i / ns;
       const int j = (i - bb * ns) * kSampleStride + kSampleStride / 2;
-      const int npb = (int)clamp_nonpad(p.nonpad[bb], T);
       bool live = false;
-      if (j < npb) {
-        if constexpr (kRules) {
-          const int32_t kj = p.slot_kind ? p.slot_kind[bb * (int64_t)T + j] : 0;
+      if constexpr (kRules) {
+        // nonpad, q_start and the sample's kind together, then the query
+        // slots' kinds: two memory round trips
+        const int64_t np_raw = p.nonpad[bb];
+        const int64_t qs_raw = (p.q_start ? p.q_start : p.nonpad)[bb];
+        const int32_t kj = p.slot_kind ? p.slot_kind[bb * (int64_t)T + min(j, T - 1)] : 0;
+        if (j < (int)clamp_nonpad(np_raw, T)) {
           for (int s = 0; s < p.S_q; ++s) {
-            const RowRule rr = make_row_rule(p.nonpad, p.q_start, p.slot_kind, bb, s, p.S_q, T, p.window, p.circular);
+            const RowRule rr = make_row_rule_from(np_raw, p.q_start != nullptr, qs_raw, p.slot_kind,
+                                                  bb, s, p.S_q, T, p.window, p.circular);
             live |= rr.allowed(j, kj);
           }
-        } else {
-          const BiasT* col = (const BiasT*)p.bias + (int64_t)bb * p.S_q * T + j;
-          for (int s = 0; s < p.S_q; ++s) live |= bias_live_bits<BiasT>(col[(int64_t)s * T]);
         }
+      } else if (j < (int)clamp_nonpad(p.nonpad[bb], T)) {
+        const BiasT* col = (const BiasT*)p.bias + (int64_t)bb * p.S_q * T + j;
+        for (int s = 0; s < p.S_q; ++s) live |= bias_live_bits<BiasT>(col[(int64_t)s * T]);
       }
       if (live) atomicAdd(&s_cnt[bb], 1);
     }
@@ -365,30 +383,30 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
       split = rank - first;
     }
   }
-  const int np = (int)clamp_nonpad(p.nonpad[b], T);
 
   // ---- 1c. this row's live range [live_lo, live_hi) ---------------------------
   if constexpr (kRules) {
     // causal / window keys of every query row, then the image block of any row
+    if (b != b_guess) make_rules(b);   // (nothing has read the guessed row's yet)
+    __syncthreads();
     int lo = INT32_MAX, hi = -1;
     if (tid < p.S_q) {
-      const RowRule rr = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, tid, p.S_q, T, p.window, p.circular);
-      s_kq[tid] = rr.kind_q;
       // the row's causal/window key interval(s) below nonpad (a circular
       // cache's may wrap round into a second one)
-      if (rr.lo <= rr.hi) { lo = rr.lo; hi = rr.hi; }
-      if (rr.lo2 <= rr.hi2) { lo = min(lo, rr.lo2); hi = max(hi, rr.hi2); }
+      const int32_t* d = s_rule[tid];
+      if (d[1] <= d[2]) { lo = d[1]; hi = d[2]; }
+      if (d[4] <= d[5]) { lo = min(lo, d[4]); hi = max(hi, d[5]); }
     }
-    __syncthreads();
     bool any_block = false;
-    for (int s = 0; s < p.S_q; ++s) any_block |= s_kq[s] > 0;
+    for (int s = 0; s < p.S_q; ++s) any_block |= s_rule[s][6] > 0;
     if (any_block) {
       const int32_t* kr = p.slot_kind + b * T;
+      const int np = s_rule[0][0];   // valid slots of the row
       for (int j = tid; j < np; j += kDecThreads) {
         const int32_t kj = kr[j];
         if (kj <= 0) continue;
         for (int s = 0; s < p.S_q; ++s) {
-          if (s_kq[s] == kj) { lo = min(lo, j); hi = max(hi, j); break; }
+          if (s_rule[s][6] == kj) { lo = min(lo, j); hi = max(hi, j); break; }
         }
       }
     }
@@ -448,7 +466,11 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
     const int r = 4 * kgrp + e;
     row_ok[e] = r < R;
     row_s[e] = row_ok[e] ? r / G : 0;
-    if constexpr (kRules) rules[e] = make_row_rule(p.nonpad, p.q_start, p.slot_kind, b, row_s[e], p.S_q, T, p.window, p.circular);
+    if constexpr (kRules) {
+      const int32_t* d = s_rule[row_s[e]];
+      rules[e].np32 = d[0]; rules[e].lo = d[1]; rules[e].hi = d[2]; rules[e].blk = d[3];
+      rules[e].lo2 = d[4]; rules[e].hi2 = d[5];
+    }
   }
   const float scale_log2 = p.scale * kLog2e;
   const bool cap_on = p.softcap > 0.f;
@@ -497,7 +519,10 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
 #pragma unroll
       for (int e = 0; e < E; ++e) bl.bias[e] = biasb[(int64_t)row_s[e] * T + jk];
     } else {
-      if (kindb) bl.kj = kindb[jk];
+      // branch-free: without kinds the load reads the first word of the K
+      // row loaded below (no extra traffic) and its value is not used
+      const int32_t kraw = *(kindb ? kindb + jk : (const int32_t*)(kbase + (int64_t)jk * D));
+      bl.kj = kindb ? kraw : 0;
     }
     const __bf16* kp = kbase + (int64_t)jk * D + 8 * kgrp;
 #pragma unroll
