@@ -18,10 +18,14 @@ kernels; there is no fallback: a missing library raises at the first call.
     attn_bias_gqa_fwd_noalloc(q, k_cache, v_cache, bias, nonpad, scale, out,
                               q_start=None, slot_kind=None, window=0)
                                   the same with the library's own scratch
+    attn_bias_gqa_decode_step(q, k_cache, v_cache, k_update, v_update,
+                              write_indices, nonpad, scale, ..., bias=None)
+                                  a decode step (both scatters, the bias and
+                                  the attention) in one launch
 The same calls for a circular (window-sized) cache: kv_tensor_scatter_circular,
 build_circular_cache_bias, kv_scatter_and_bias_circular and
-attn_bias_gqa_fwd_circular (kv_len tokens written so far, position p in slot
-p mod capacity).
+attn_bias_gqa_fwd_circular, attn_bias_gqa_decode_step_circular (kv_len tokens
+written so far, position p in slot p mod capacity).
 """
 from __future__ import annotations
 
@@ -34,7 +38,8 @@ import torch
 __all__ = ["kv_tensor_scatter", "kv_scatter_and_bias", "build_static_cache_bias", "attn_bias_gqa_fwd",
            "attn_bias_gqa_fwd_noalloc", "attn_bias_gqa_workspace_bytes", "abgqa_last_error",
            "kv_tensor_scatter_circular", "build_circular_cache_bias", "kv_scatter_and_bias_circular",
-           "attn_bias_gqa_fwd_circular", "library_path", "load"]
+           "attn_bias_gqa_fwd_circular", "attn_bias_gqa_decode_step",
+           "attn_bias_gqa_decode_step_circular", "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libabgqa.so")
@@ -76,6 +81,11 @@ def load():
         for name in ("attn_bias_gqa_fwd", "attn_bias_gqa_fwd_circular"):
             getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
                                            i64, i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                                           ctypes.c_float, i64, ctypes.c_int, vp, sz, vp]
+            getattr(lib, name).restype = ctypes.c_int
+        for name in ("attn_bias_gqa_decode_step", "attn_bias_gqa_decode_step_circular"):
+            getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, vp, ctypes.c_int, vp, vp,
+                                           vp, i64, i64, i64, i64, i64, i64, i64, ctypes.c_float,
                                            ctypes.c_float, i64, ctypes.c_int, vp, sz, vp]
             getattr(lib, name).restype = ctypes.c_int
         lib.attn_bias_gqa_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
@@ -339,6 +349,81 @@ def _attn(fn, q, k_cache, v_cache, bias, nonpad, scale, q_start, slot_kind, wind
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(getattr(lib, fn)(op, qp, kp, vp_, bp, bdt, npd, qs, sk, B, Hq, Hkv, S_q, T, D, Dv,
                             float(scale), float(softcap), int(window), _DTYPE[q.dtype], wp, wbytes,
+                            _stream(q)), fn)
+    return out
+
+
+def attn_bias_gqa_decode_step(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              k_update: torch.Tensor | None, v_update: torch.Tensor | None,
+                              write_indices: torch.Tensor | None, nonpad: torch.Tensor,
+                              scale: float, q_start: torch.Tensor | None = None,
+                              slot_kind: torch.Tensor | None = None, window: int = 0,
+                              bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                              workspace: torch.Tensor | None = None,
+                              softcap: float = 0.0) -> torch.Tensor:
+    """One decode step in one launch, bit-identical to kv_scatter_and_bias
+    (k_update / v_update rows into the caches at write_indices; the bias into
+    `bias` when given) followed by attn_bias_gqa_fwd. k_update = v_update =
+    None: nothing to scatter (a KV-shared layer). Returns out."""
+    return _step("attn_bias_gqa_decode_step", q, k_cache, v_cache, k_update, v_update, write_indices,
+                 nonpad, scale, q_start, slot_kind, window, bias, out, workspace, softcap)
+
+
+def attn_bias_gqa_decode_step_circular(q: torch.Tensor, k_cache: torch.Tensor,
+                                       v_cache: torch.Tensor, k_update: torch.Tensor | None,
+                                       v_update: torch.Tensor | None,
+                                       write_pos: torch.Tensor | None, kv_len: torch.Tensor,
+                                       scale: float, q_start: torch.Tensor | None = None,
+                                       slot_kind: torch.Tensor | None = None, window: int = 0,
+                                       bias: torch.Tensor | None = None,
+                                       out: torch.Tensor | None = None,
+                                       workspace: torch.Tensor | None = None,
+                                       softcap: float = 0.0) -> torch.Tensor:
+    """attn_bias_gqa_decode_step over a circular cache of capacity
+    k_cache.shape[2] (kv_len tokens written so far, position p in slot p mod
+    capacity)."""
+    return _step("attn_bias_gqa_decode_step_circular", q, k_cache, v_cache, k_update, v_update,
+                 write_pos, kv_len, scale, q_start, slot_kind, window, bias, out, workspace, softcap)
+
+
+def _step(fn, q, k_cache, v_cache, k_update, v_update, write_indices, nonpad, scale, q_start,
+          slot_kind, window, bias, out, workspace, softcap):
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, S_q, D], k_cache [B, Hkv, max_seq, D], "
+                         "v_cache [B, Hkv, max_seq, D_v]")
+    B, Hq, S_q, D = q.shape
+    Hkv, T = k_cache.shape[1], k_cache.shape[2]
+    Dv = v_cache.shape[3]
+    if q.dtype != torch.bfloat16:
+        raise ValueError("the fused decode step takes bfloat16 tensors")
+    qp = _dev(q, "q")
+    kp = _dev(k_cache, "k_cache", q.dtype, (B, Hkv, T, D))
+    vp_ = _dev(v_cache, "v_cache", q.dtype, (B, Hkv, T, Dv))
+    if (k_update is None) != (v_update is None):
+        raise ValueError("k_update and v_update must both be given or both be None")
+    S_new = 0 if k_update is None else k_update.shape[2]
+    ku = _dev(k_update, "k_update", q.dtype, (B, Hkv, S_new, D)) if S_new else None
+    vu = _dev(v_update, "v_update", q.dtype, (B, Hkv, S_new, Dv)) if S_new else None
+    w = _opt(write_indices, "write_indices", torch.int64, (B,))
+    bp, bdt = None, BF16
+    if bias is not None:
+        if bias.dtype not in _DTYPE:
+            raise ValueError("bias must be float32 or bfloat16")
+        bp, bdt = _dev(bias, "bias", None, (B, 1, S_q, T)), _DTYPE[bias.dtype]
+    npd = _dev(nonpad, "nonpad", torch.int64, (B,))
+    qs = _opt(q_start, "q_start", torch.int64, (B,))
+    sk = _opt(slot_kind, "slot_kind", torch.int32, (B, T))
+    if out is None:
+        out = q.new_empty((B, Hq, S_q, Dv))
+    op = _dev(out, "out", q.dtype, (B, Hq, S_q, Dv))
+    lib = load()
+    need = int(lib.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, S_q, T, D, Dv))
+    if workspace is None:
+        workspace = _workspace(q.device, need)
+    wp = None if workspace is None else _dev(workspace, "workspace")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(getattr(lib, fn)(op, qp, kp, vp_, ku, vu, w, S_new, bp, bdt, npd, qs, sk, B, Hq, Hkv, S_q,
+                            T, D, Dv, float(scale), float(softcap), int(window), BF16, wp, wbytes,
                             _stream(q)), fn)
     return out
 

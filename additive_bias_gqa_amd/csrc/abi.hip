@@ -303,6 +303,35 @@ size_t attn_bias_gqa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t
 
 namespace {
 
+// The split-KV decode kernel's workspace: its size for the shape in p, its
+// alignment, and under ABGQA_CHECK its arrival counts (zero between calls);
+// then p's split count and workspace pointers.
+abgqa_status decode_workspace(const char* me, abgqa::AttnParams& p, void* workspace,
+                              size_t workspace_bytes, hipStream_t st, bool chk) {
+  const size_t need = abgqa::decode_workspace_bytes(p.B, p.Hkv, p.S_q, p.G, p.Dv, p.T);
+  if (!workspace || workspace_bytes < need)
+    return fail(ABGQA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", me,
+                need, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(ABGQA_ERR_INVALID, "%s: workspace not 16-byte aligned", me);
+  if (chk) {
+    // the arrival counts this call uses must be zero
+    std::vector<int32_t> cnt((size_t)p.B * p.Hkv);
+    const abgqa_status r = fetch_device(workspace, cnt.size() * sizeof(int32_t), cnt.data(), st, me,
+                                        "workspace");
+    if (r != ABGQA_OK) return r;
+    for (size_t i = 0; i < cnt.size(); ++i)
+      if (cnt[i] != 0)
+        return fail(ABGQA_ERR_WORKSPACE,
+                    "%s: ABGQA_CHECK: decode arrival count %zu of the workspace is %d, "
+                    "not 0 (workspace not zero-filled, or a call on it did not complete)",
+                    me, i, (int)cnt[i]);
+  }
+  p.n_split = abgqa::decode_num_splits(p.B, p.Hkv, p.T);
+  p.arrive = (int*)workspace;
+  p.ws_part = (float*)((char*)workspace + abgqa::kWsCounterBytes);
+  return ABGQA_OK;
+}
+
 abgqa_status attn_impl(const char* me, bool circular, void* out, const void* q, const void* k_cache,
                        const void* v_cache, const void* bias, abgqa_dtype bias_dtype,
                        const int64_t* nonpad_kv_seqlen, const int64_t* q_start,
@@ -364,27 +393,8 @@ abgqa_status attn_impl(const char* me, bool circular, void* out, const void* q, 
     e = abgqa::launch_attn_vec_bf16(p, st);
   } else if (S_q * G <= 16) {
     path = "decode";
-    const size_t need = abgqa::decode_workspace_bytes(B, Hkv, S_q, G, D_v, max_seq);
-    if (!workspace || workspace_bytes < need)
-      return fail(ABGQA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", me,
-                  need, workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(workspace, 16)) return fail(ABGQA_ERR_INVALID, "%s: workspace not 16-byte aligned", me);
-    if (chk) {
-      // the arrival counts this call uses must be zero
-      std::vector<int32_t> cnt((size_t)(B * Hkv));
-      const abgqa_status r = fetch_device(workspace, cnt.size() * sizeof(int32_t), cnt.data(), st, me,
-                                          "workspace");
-      if (r != ABGQA_OK) return r;
-      for (size_t i = 0; i < cnt.size(); ++i)
-        if (cnt[i] != 0)
-          return fail(ABGQA_ERR_WORKSPACE,
-                      "%s: ABGQA_CHECK: decode arrival count %zu of the workspace is %d, "
-                      "not 0 (workspace not zero-filled, or a call on it did not complete)",
-                      me, i, (int)cnt[i]);
-    }
-    p.n_split = abgqa::decode_num_splits(B, Hkv, max_seq);
-    p.arrive = (int*)workspace;
-    p.ws_part = (float*)((char*)workspace + abgqa::kWsCounterBytes);
+    const abgqa_status r = decode_workspace(me, p, workspace, workspace_bytes, st, chk);
+    if (r != ABGQA_OK) return r;
     e = abgqa::launch_attn_decode(p, st);
   } else {
     path = "prefill";
@@ -407,6 +417,78 @@ abgqa_status attn_impl(const char* me, bool circular, void* out, const void* q, 
     fprintf(stderr, "[abgqa] attn_bias_gqa_fwd path=%s B=%lld Hq=%lld Hkv=%lld S_q=%lld T=%lld D=%lld D_v=%lld %s splits=%d\n",
             path, (long long)B, (long long)Hq, (long long)Hkv, (long long)S_q, (long long)max_seq,
             (long long)D, (long long)D_v, bias ? "bias" : "rules", p.n_split);
+  if (e != hipSuccess) return hip_fail(me, e);
+  return chk ? check_after(st, me) : ABGQA_OK;
+}
+
+// One fused decode step (attn_decode_step.hip): the checks of kv_scatter_and_bias
+// and of attn_bias_gqa_fwd for a shape the split-KV decode kernel takes.
+abgqa_status step_impl(const char* me, bool circular, void* out, const void* q, void* k_cache,
+                       void* v_cache, const void* k_update, const void* v_update,
+                       const int64_t* write_indices, int64_t S_new, void* bias,
+                       abgqa_dtype bias_dtype, const int64_t* nonpad_kv_seqlen,
+                       const int64_t* q_start, const int32_t* slot_kind, int64_t B, int64_t Hq,
+                       int64_t Hkv, int64_t S_q, int64_t max_seq, int64_t D, int64_t D_v,
+                       float scale, float softcap, int64_t window, abgqa_dtype dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_q <= 0 || max_seq <= 0 || D <= 0 || D_v <= 0)
+    return fail(ABGQA_ERR_INVALID, "%s: B, Hq, Hkv, S_q, max_seq, D and D_v must be positive", me);
+  if (Hq % Hkv != 0) return fail(ABGQA_ERR_INVALID, "%s: Hq must be a multiple of Hkv", me);
+  if (S_new < 0) return fail(ABGQA_ERR_INVALID, "%s: S_new must be >= 0", me);
+  if (circular && S_new > max_seq)
+    return fail(ABGQA_ERR_INVALID, "%s: a circular cache takes at most capacity = %lld new tokens per call",
+                me, (long long)max_seq);
+  if (!(softcap >= 0.f) || softcap == INFINITY)
+    return fail(ABGQA_ERR_INVALID, "%s: softcap must be finite and >= 0 (0 = none)", me);
+  if (S_q > max_seq) return fail(ABGQA_ERR_INVALID, "%s: S_q must not exceed max_seq", me);
+  if (max_seq > kMaxSeq) return fail(ABGQA_ERR_UNSUPPORTED, "%s: max_seq above 2^24", me);
+  const int64_t G = Hq / Hkv;
+  if (dtype != ABGQA_BF16 || S_q * G > 16 || !abgqa::decode_supports((int)D, (int)D_v) ||
+      B * Hkv > abgqa::kMaxDecodeRows || S_new > 16)
+    return fail(ABGQA_ERR_UNSUPPORTED,
+                "%s: the fused step takes bf16 decode shapes (S_q * Hq / Hkv <= 16, D and D_v of the "
+                "decode kernel, B * Hkv <= %d, S_new <= 16); use kv_scatter_and_bias and "
+                "attn_bias_gqa_fwd", me, (int)abgqa::kMaxDecodeRows);
+  if (bias && bias_dtype != ABGQA_F32 && bias_dtype != ABGQA_BF16)
+    return fail(ABGQA_ERR_UNSUPPORTED, "%s: bias dtype must be ABGQA_F32 or ABGQA_BF16", me);
+  if (!out || !q || !k_cache || !v_cache || !nonpad_kv_seqlen)
+    return fail(ABGQA_ERR_INVALID, "%s: null out, q, k_cache, v_cache or nonpad_kv_seqlen", me);
+  if (S_new > 0 && (!k_update || !v_update)) return fail(ABGQA_ERR_INVALID, "%s: null update", me);
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      (S_new > 0 && (!aligned(k_update, 16) || !aligned(v_update, 16))) ||
+      (write_indices && !aligned(write_indices, 8)) || (bias && !aligned(bias, 16)) ||
+      !aligned(nonpad_kv_seqlen, 8) || (q_start && !aligned(q_start, 8)) ||
+      (slot_kind && !aligned(slot_kind, 16)))
+    return fail(ABGQA_ERR_INVALID, "%s: misaligned pointer", me);
+  if (out == q || out == k_cache || out == v_cache || out == bias || out == k_update || out == v_update ||
+      (bias && (bias == q || bias == k_cache || bias == v_cache)))
+    return fail(ABGQA_ERR_INVALID, "%s: out and bias must not alias an input", me);
+
+  abgqa::AttnParams p{};
+  p.out = out; p.q = q; p.k = k_cache; p.v = v_cache; p.bias = nullptr;
+  p.nonpad = nonpad_kv_seqlen; p.q_start = q_start; p.slot_kind = slot_kind;
+  p.B = (int)B; p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.G = (int)G; p.S_q = (int)S_q;
+  p.T = (int)max_seq; p.D = (int)D; p.Dv = (int)D_v; p.window = window; p.scale = scale; p.softcap = softcap;
+  p.circular = circular ? 1 : 0;
+  p.k_upd = k_update; p.v_upd = v_update; p.write_idx = write_indices; p.S_new = (int)S_new;
+  p.bias_out = bias; p.bias_out_bf16 = (bias_dtype == ABGQA_BF16);
+  hipStream_t st = (hipStream_t)stream;
+  const bool chk = check_enabled(st);
+  if (chk) {
+    abgqa_status r = S_new > 0 ? check_write_indices(write_indices, B, max_seq, S_new, st, me, circular)
+                               : ABGQA_OK;
+    if (r == ABGQA_OK) r = check_nonpad(nonpad_kv_seqlen, B, max_seq, st, me, circular);
+    if (r == ABGQA_OK) r = check_q_start(q_start, B, st, me);
+    if (r != ABGQA_OK) return r;
+  }
+  const abgqa_status r = decode_workspace(me, p, workspace, workspace_bytes, st, chk);
+  if (r != ABGQA_OK) return r;
+  const hipError_t e = abgqa::launch_decode_step(p, st);
+  if (log_enabled())
+    fprintf(stderr, "[abgqa] %s B=%lld Hq=%lld Hkv=%lld S_q=%lld S_new=%lld T=%lld D=%lld D_v=%lld splits=%d\n",
+            me, (long long)B, (long long)Hq, (long long)Hkv, (long long)S_q, (long long)S_new,
+            (long long)max_seq, (long long)D, (long long)D_v, p.n_split);
   if (e != hipSuccess) return hip_fail(me, e);
   return chk ? check_after(st, me) : ABGQA_OK;
 }
@@ -491,6 +573,37 @@ abgqa_status attn_bias_gqa_fwd_circular(void* out, const void* q, const void* k_
   return attn_impl("attn_bias_gqa_fwd_circular", true, out, q, k_cache, v_cache, bias, bias_dtype,
                    kv_len, q_start, slot_kind, B, Hq, Hkv, S_q, capacity, D, D_v, scale, softcap,
                    window, dtype, workspace, workspace_bytes, stream);
+}
+
+abgqa_status attn_bias_gqa_decode_step(void* out, const void* q, void* k_cache, void* v_cache,
+                                       const void* k_update, const void* v_update,
+                                       const int64_t* write_indices, int64_t S_new, void* bias,
+                                       abgqa_dtype bias_dtype, const int64_t* nonpad_kv_seqlen,
+                                       const int64_t* q_start, const int32_t* slot_kind, int64_t B,
+                                       int64_t Hq, int64_t Hkv, int64_t S_q, int64_t max_seq,
+                                       int64_t D, int64_t D_v, float scale, float softcap,
+                                       int64_t window, abgqa_dtype dtype, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return step_impl("attn_bias_gqa_decode_step", false, out, q, k_cache, v_cache, k_update, v_update,
+                   write_indices, S_new, bias, bias_dtype, nonpad_kv_seqlen, q_start, slot_kind, B, Hq,
+                   Hkv, S_q, max_seq, D, D_v, scale, softcap, window, dtype, workspace,
+                   workspace_bytes, stream);
+}
+
+abgqa_status attn_bias_gqa_decode_step_circular(void* out, const void* q, void* k_cache,
+                                                void* v_cache, const void* k_update,
+                                                const void* v_update, const int64_t* write_pos,
+                                                int64_t S_new, void* bias, abgqa_dtype bias_dtype,
+                                                const int64_t* kv_len, const int64_t* q_start,
+                                                const int32_t* slot_kind, int64_t B, int64_t Hq,
+                                                int64_t Hkv, int64_t S_q, int64_t capacity,
+                                                int64_t D, int64_t D_v, float scale, float softcap,
+                                                int64_t window, abgqa_dtype dtype, void* workspace,
+                                                size_t workspace_bytes, void* stream) {
+  return step_impl("attn_bias_gqa_decode_step_circular", true, out, q, k_cache, v_cache, k_update,
+                   v_update, write_pos, S_new, bias, bias_dtype, kv_len, q_start, slot_kind, B, Hq,
+                   Hkv, S_q, capacity, D, D_v, scale, softcap, window, dtype, workspace,
+                   workspace_bytes, stream);
 }
 
 const char* abgqa_last_error(void) { return g_last_error.c_str(); }

@@ -78,6 +78,16 @@ struct AttnParams {
   // pass over the bias before the attention kernel, or null (each workgroup
   // then scans its bias rows itself)
   const uint32_t* tilemap;
+  // one fused decode step (attn_decode_step.hip): before the attention reads
+  // them, the S_new update rows [B, Hkv, S_new, D] / [.., DV] go into k / v at
+  // write_idx[b] + t (TensorScatter; circular: that position mod T), and the
+  // [B, 1, S_q, T] bias of the rules is written to bias_out (null: not written)
+  const void* k_upd;
+  const void* v_upd;
+  const int64_t* write_idx;  // [B] or null (all 0)
+  int S_new;
+  void* bias_out;
+  int bias_out_bf16;
 };
 
 // fp32 path (any S_q): one wavefront per query row.
@@ -93,6 +103,10 @@ size_t decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_q, int64_t G, in
                               int64_t max_seq);
 bool decode_supports(int D, int Dv);
 hipError_t launch_attn_decode(const AttnParams& p, hipStream_t stream);
+// the fused decode step: TensorScatter of K and V, the bias build and the
+// attention (rules variant) in one launch of the split-KV kernel; the same
+// shapes as launch_attn_decode, S_new <= 16
+hipError_t launch_decode_step(const AttnParams& p, hipStream_t stream);
 
 // bf16 prefill path: matrix-core tiles, K/V tiles in LDS shared by the G heads.
 // Returns hipErrorInvalidValue when the shape needs more LDS than a CU has.

@@ -5,12 +5,15 @@
                     [--secondary | --no-secondary] [--eager] [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over one batch of seeded synthetic
-input: TensorScatter of K and V (skipped by the KV-shared variant) and the bias
-build, fused into one launch (kv_scatter_and_bias), then the attention. The
+input: TensorScatter of K and V (skipped by the KV-shared variant), the bias
+build and the attention. A decode step is one launch (attn_bias_gqa_decode_step:
+the scatters, the bias and the attention in the split-KV kernel); a prefill
+step is two, the scatters and the bias fused (kv_scatter_and_bias), then the
+attention. --separate-calls times a decode step as those two launches too. The
 default workload is the sliding-window decode layer (B8 Hq16 Hkv8 D256,
 max_seq 4096, window 1024, S_q 1); the secondary lines are the other four
-workload shapes and the two sliding layers over a circular (window-sized)
-cache.
+workload shapes, the two sliding layers over a circular (window-sized) cache,
+and the main decode workload as separate calls.
 
 Timing. Inputs are resident in HBM before the timed region. R copies of every
 input rotate through the steps (step i uses copy i % R), R chosen so that the
@@ -25,9 +28,10 @@ run on). --eager times launch by launch instead (used under rocprofv3 counter
 runs).
 
 Output: one JSON line. value = algorithmic bytes of a step / step time (GB/s).
-roofline = the attention kernel's algorithmic bytes (decode) or flops
-(prefill) per launch / its average duration, against the MI355X peak (HBM 8 TB/s;
-bf16 dense matrix cores 2.5 PFLOP/s). cpu_baseline = the fp64 oracle timed on the
+roofline = the dominant kernel's algorithmic bytes (decode: the fused step
+kernel, or the attention kernel of separate calls) or flops (prefill) per
+launch / its average duration, against the MI355X peak (HBM 8 TB/s; bf16 dense
+matrix cores 2.5 PFLOP/s). cpu_baseline = the fp64 oracle timed on the
 host cores on a bounded sample of the same workload (every secondary workload
 carries its own).
 """
@@ -119,6 +123,24 @@ def run_scatter_bias(ab, w, step, s):
                            w.window, bias=s.bias if VARIANT == "bias" else None)
 
 
+def fused_step(w, step, fused):
+    """Whether this step runs as one launch (bf16 decode: rows of the split-KV kernel)."""
+    return fused and w.dtype.is_floating_point and w.dtype.itemsize == 2 and \
+        step.S_q * (w.Hq // w.Hkv) <= 16
+
+
+def run_step(ab, w, step, s, ws, fused):
+    """One whole step: the fused decode step, or the separate launches."""
+    if fused:
+        fn = ab.attn_bias_gqa_decode_step_circular if w.circular else ab.attn_bias_gqa_decode_step
+        fn(s.q, s.k, s.v, s.k_new, s.v_new, s.wi, s.nonpad, w.scale, q_start=s.q_start,
+           slot_kind=s.kind, window=w.window, bias=s.bias if VARIANT == "bias" else None, out=s.out,
+           workspace=ws, softcap=SOFTCAP)
+        return
+    run_scatter_bias(ab, w, step, s)
+    run_attention(ab, w, s, ws)
+
+
 def run_attention(ab, w, s, ws):
     fwd = ab.attn_bias_gqa_fwd_circular if w.circular else ab.attn_bias_gqa_fwd
     if VARIANT == "bias":
@@ -151,7 +173,7 @@ def work_counts(w, step, s, torch):
     bias_bytes = B * S_q * T * e + kind_bytes                      # written once, kinds read
     return dict(pairs=pairs, live_keys=live_keys, attn_bytes=attn_bytes, attn_flops=attn_flops,
                 step_bytes=attn_bytes + scatter_bytes + bias_bytes,
-                scatter_bytes=scatter_bytes, bias_bytes=bias_bytes)
+                scatter_bytes=scatter_bytes, bias_bytes=bias_bytes, bias_read=bias_read)
 
 
 def time_graph(torch, g, reps):
@@ -167,10 +189,11 @@ def time_graph(torch, g, reps):
     return e0.elapsed_time(e1)  # ms
 
 
-def bench_workload(name, steps, warmup, eager, torch, ab):
+def bench_workload(name, steps, warmup, eager, torch, ab, fused=True):
     w = make_workload(name)
     step = w.steps[0]
-    log(f"{name}: {w.describe()}")
+    fused = fused_step(w, step, fused)
+    log(f"{name}: {w.describe()}, {'one fused launch' if fused else 'separate launches'} per step")
     probe = InputSet(w, step, torch)
     per_set = sum(t.numel() * t.element_size() for t in
                   (probe.k, probe.v, probe.q, probe.bias, probe.out))
@@ -185,9 +208,12 @@ def bench_workload(name, steps, warmup, eager, torch, ab):
                                    w.window, dtype=w.dtype, out=probe.bias)
     counts = work_counts(w, step, probe, torch)
     if VARIANT == "rules":   # no bias tensor is read or written in this variant
-        counts["attn_bytes"] -= step.S_q * int(probe.nonpad.clamp(0, w.max_seq).sum()) * (
-            2 if w.dtype == torch.bfloat16 else 4)
+        counts["attn_bytes"] -= counts["bias_read"]
         counts["step_bytes"] = counts["attn_bytes"] + counts["scatter_bytes"]
+    elif fused:              # the fused step writes the bias but never reads it
+        counts["step_bytes"] -= counts["bias_read"]
+    # bytes of the dominant kernel: the fused step's whole step, or the attention
+    counts["kernel_bytes"] = counts["step_bytes"] if fused else counts["attn_bytes"]
 
     # Copies of the inputs rotate so that a step never finds the data it reads
     # in the 256 MB Infinity Cache: the sets' live bytes (what a step actually
@@ -199,9 +225,7 @@ def bench_workload(name, steps, warmup, eager, torch, ab):
 
     # eager warm-up (every set at least once) and reference outputs
     for i in range(max(warmup, n_sets)):
-        s = sets[i % n_sets]
-        run_scatter_bias(ab, w, step, s)
-        run_attention(ab, w, s, ws)
+        run_step(ab, w, step, sets[i % n_sets], ws, fused)
     torch.cuda.synchronize()
     ref_out = [s.out.clone() for s in sets]
     for s in sets:
@@ -218,9 +242,13 @@ def bench_workload(name, steps, warmup, eager, torch, ab):
         e0.record(st)
         for i in range(K):
             s = sets[i % n_sets]
-            run_scatter_bias(ab, w, step, s)
+            if not fused:
+                run_scatter_bias(ab, w, step, s)
             ev[i][0].record(st)
-            run_attention(ab, w, s, ws)
+            if fused:
+                run_step(ab, w, step, s, ws, True)
+            else:
+                run_attention(ab, w, s, ws)
             ev[i][1].record(st)
         e1.record(st)
         torch.cuda.synchronize()
@@ -235,12 +263,13 @@ def bench_workload(name, steps, warmup, eager, torch, ab):
         with torch.cuda.stream(side):
             with torch.cuda.graph(g_step):
                 for i in range(K):
-                    s = sets[i % n_sets]
-                    run_scatter_bias(ab, w, step, s)
-                    run_attention(ab, w, s, ws)
+                    run_step(ab, w, step, sets[i % n_sets], ws, fused)
             with torch.cuda.graph(g_attn):
                 for i in range(K):
-                    run_attention(ab, w, sets[i % n_sets], ws)
+                    if fused:   # the one kernel of the step
+                        run_step(ab, w, step, sets[i % n_sets], ws, True)
+                    else:
+                        run_attention(ab, w, sets[i % n_sets], ws)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         # the graphs must reproduce the eager outputs bit for bit, replay after replay
@@ -257,9 +286,9 @@ def bench_workload(name, steps, warmup, eager, torch, ab):
         mode = "graph"
 
     res = dict(workload=name, mode=mode, steps=K, ms_per_step=step_ms, attn_ms=attn_ms,
-               counts=counts, desc=w.describe(), n_sets=n_sets)
+               counts=counts, desc=w.describe(), n_sets=n_sets, fused=fused)
     if name in DECODE:
-        res["attn_rate"] = counts["attn_bytes"] / (attn_ms * 1e-3) / 1e9       # GB/s
+        res["attn_rate"] = counts["kernel_bytes"] / (attn_ms * 1e-3) / 1e9     # GB/s
         res["roofline"] = dict(bound="hbm", achieved=round(res["attn_rate"], 1),
                                peak=HBM_PEAK_GBS, unit="GB/s",
                                frac=round(res["attn_rate"] / HBM_PEAK_GBS, 4))
@@ -275,7 +304,8 @@ def bench_workload(name, steps, warmup, eager, torch, ab):
                                frac=round(hbm / HBM_PEAK_GBS, 4))
     res["step_gbs"] = counts["step_bytes"] / (step_ms * 1e-3) / 1e9
     side = f", HBM side {100 * res['hbm_side']['frac']:.1f}%" if "hbm_side" in res else ""
-    log(f"{name}: {mode} step {step_ms * 1e3:.1f} us, attention {attn_ms * 1e3:.1f} us, "
+    log(f"{name}: {mode} step {step_ms * 1e3:.1f} us, {'fused kernel' if fused else 'attention'} "
+        f"{attn_ms * 1e3:.1f} us, "
         f"{res['roofline']['achieved']} {res['roofline']['unit']} "
         f"({100 * res['roofline']['frac']:.1f}% of peak{side})")
     del sets, probe, ws
@@ -306,12 +336,18 @@ def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
 KERNEL_SOURCES_DIR = os.path.join("additive_bias_gqa_amd", "csrc")
 
 
+def fused_default(name):
+    """The step form a default run takes (traffic records are taken on it):
+    one fused launch for the decode workloads."""
+    return name in DECODE
+
+
 def kernel_sources(name):
-    """The sources that build the attention call of a workload: the ABI
+    """The sources that build the dominant kernel of a workload's step: the ABI
     dispatch, the phase's kernel files and the headers they include."""
     common = ["abi.hip", "common.h", "kernels.h", "mask_rules.h"]
     if name.startswith("decode"):
-        files = common + ["attn_decode.hip"]
+        files = common + ["attn_decode_step.hip", "decode_kernel.h"]
     else:
         files = common + ["attn_prefill_dma.hip", "attn_prefill_dma_wide.hip", "prefill_dma.h",
                           "prefill_common.h"]
@@ -447,6 +483,9 @@ def main():
                          "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) and exit")
     ap.add_argument("--softcap", type=float, default=0.0,
                     help="softcap of the attention scores (0 = none, the workloads' setting)")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="time a decode step as kv_scatter_and_bias + attn_bias_gqa_fwd (two "
+                         "launches) instead of the fused step")
     ap.add_argument("--v-head-size", type=int, default=None,
                     help="head size of V for decode_full_kvshared, prefill_vision or prefill_long (V "
                          "may have another head size than Q and K; default: the query's)")
@@ -480,27 +519,31 @@ def main():
     t_start = time.perf_counter()
     copy_gbs = copy_bandwidth(torch)
     log(f"device copy bandwidth {copy_gbs:.0f} GB/s (read + write)")
-    main_res, w = bench_workload(args.workload, args.steps, args.warmup, args.eager, torch, ab)
+    fused = not args.separate_calls
+    main_res, w = bench_workload(args.workload, args.steps, args.warmup, args.eager, torch, ab, fused)
     secondary = {}
     if args.secondary:
-        for name in WORKLOADS:
-            if name == args.workload:
-                continue
-            r, w2 = bench_workload(name, max(8, args.steps // 10), 2, args.eager, torch, ab)
-            secondary[name] = dict(
+        runs = [(n, fused) for n in WORKLOADS if n != args.workload]
+        if main_res["fused"]:   # the main decode workload as separate calls, for comparison
+            runs.append((args.workload, False))
+        for name, fz in runs:
+            r, w2 = bench_workload(name, max(8, args.steps // 10), 2, args.eager, torch, ab, fz)
+            key = name if fz or not main_res["fused"] or name != args.workload else f"{name}_separate_calls"
+            secondary[key] = dict(
                 attn_us=round(r["attn_ms"] * 1e3, 2), step_us=round(r["ms_per_step"] * 1e3, 2),
                 steps=r["steps"], rotating_input_sets=r["n_sets"],
-                roofline=dict(r["roofline"], traffic=traffic_for(name)), step_gbs=round(r["step_gbs"], 1),
-                config=r["desc"])
+                step_form="fused" if r["fused"] else "separate",
+                roofline=dict(r["roofline"], traffic=traffic_for(name) if r["fused"] == fused_default(name) else None),
+                step_gbs=round(r["step_gbs"], 1), config=r["desc"])
             if "hbm_side" in r:
-                secondary[name]["hbm_side"] = r["hbm_side"]
-            if not args.no_cpu_baseline:
+                secondary[key]["hbm_side"] = r["hbm_side"]
+            if not args.no_cpu_baseline and key == name:
                 log(f"{name}: cpu baseline (oracle) ...")
-                secondary[name]["cpu_baseline"] = cpu_baseline(name, w2, r["counts"], budget_s=8.0)
+                secondary[key]["cpu_baseline"] = cpu_baseline(name, w2, r["counts"], budget_s=8.0)
             del w2
 
     rl = dict(main_res["roofline"])
-    rl["traffic"] = traffic_for(args.workload)
+    rl["traffic"] = traffic_for(args.workload) if main_res["fused"] == fused_default(args.workload) else None
     counts = main_res["counts"]
     cpu = None
     if not args.no_cpu_baseline:
@@ -509,8 +552,10 @@ def main():
     cfg = dict(main_res["desc"])
     cfg.update({"kernel_timing": main_res["mode"], "rotating_input_sets": main_res["n_sets"],
                 "device_copy_gbs": round(copy_gbs, 1), "variant": VARIANT, "softcap": SOFTCAP,
-                "attn_us": round(main_res["attn_ms"] * 1e3, 2),
-                "attn_bytes": counts["attn_bytes"], "step_bytes": counts["step_bytes"],
+                "step_form": ("one launch (attn_bias_gqa_decode_step: scatters, bias, attention)"
+                              if main_res["fused"] else "separate launches"),
+                "kernel_us": round(main_res["attn_ms"] * 1e3, 2),
+                "kernel_bytes": counts["kernel_bytes"], "step_bytes": counts["step_bytes"],
                 **({"hbm_side": main_res["hbm_side"]} if "hbm_side" in main_res else {}),
                 "live_keys": counts["live_keys"]})
     line = {

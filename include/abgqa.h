@@ -307,6 +307,70 @@ abgqa_status attn_bias_gqa_fwd_circular(void *out, const void *q, const void *k_
                                         size_t workspace_bytes, void *stream);
 
 /*
+ * attn_bias_gqa_decode_step - one decode step in one launch: the TensorScatter
+ * of the new K and V rows, the bias build and the attention.
+ *
+ * Passages: mobius skill "attention-optimization", "In-place KV for ONNX
+ * Attention via TensorScatter (static cache)" (a step writes its new K/V rows
+ * into the preallocated cache, then attends over it); mobius issue #366,
+ * "Mobius-side deliverable" (the bias rules); the attention as
+ * attn_bias_gqa_fwd.
+ *
+ * Results, bit for bit: those of
+ *   kv_scatter_and_bias(k_cache, v_cache, k_update, v_update, write_indices,
+ *                       B, Hkv, max_seq, S_new, ..., bias, bias_dtype,
+ *                       nonpad_kv_seqlen, q_start, slot_kind, S_q, window)
+ * followed by attn_bias_gqa_fwd with that bias (or, bias == NULL, with the
+ * in-kernel rules, which give the same output): k_cache and v_cache hold the
+ * new rows, bias (if not NULL) holds the [B, 1, S_q, max_seq] mask, out the
+ * attention. The attention masks with the rules evaluated in the kernel, so it
+ * does not wait for the bias; a key of a slot this call writes is taken from
+ * the update rows.
+ *   k_update, v_update [B, Hkv, S_new, D] and [B, Hkv, S_new, D_v] bf16
+ *   (S_new = 0: no scatter, e.g. a KV-shared layer reading a borrowed
+ *   cache); V rows may have their own head size, unlike kv_scatter_and_bias.
+ *   Other arguments as kv_scatter_and_bias and attn_bias_gqa_fwd; workspace
+ *   as attn_bias_gqa_fwd (required).
+ * Shapes: bf16 decode shapes of the split-KV kernel only: S_q * Hq / Hkv <= 16,
+ * D = D_v in {64, 128, 256, 512} or (D, D_v) = (256, 512) / (512, 256),
+ * B * Hkv <= 16384, S_new <= 16; anything else is ABGQA_ERR_UNSUPPORTED (use
+ * the separate calls). The call must not overlap other calls that read or
+ * write the same caches or workspace.
+ * Errors: those of kv_scatter_and_bias and attn_bias_gqa_fwd;
+ * ABGQA_ERR_UNSUPPORTED as above.
+ *
+ * attn_bias_gqa_decode_step_circular: the same step over a circular cache of
+ * capacity C (kv_tensor_scatter_circular, build_circular_cache_bias and
+ * attn_bias_gqa_fwd_circular in one launch); S_new <= C.
+ */
+abgqa_status attn_bias_gqa_decode_step(void *out, const void *q, void *k_cache,
+                                       void *v_cache, const void *k_update,
+                                       const void *v_update,
+                                       const int64_t *write_indices, int64_t S_new,
+                                       void *bias, abgqa_dtype bias_dtype,
+                                       const int64_t *nonpad_kv_seqlen,
+                                       const int64_t *q_start, const int32_t *slot_kind,
+                                       int64_t B, int64_t Hq, int64_t Hkv, int64_t S_q,
+                                       int64_t max_seq, int64_t D, int64_t D_v,
+                                       float scale, float softcap, int64_t window,
+                                       abgqa_dtype dtype, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
+abgqa_status attn_bias_gqa_decode_step_circular(void *out, const void *q, void *k_cache,
+                                                void *v_cache, const void *k_update,
+                                                const void *v_update,
+                                                const int64_t *write_pos, int64_t S_new,
+                                                void *bias, abgqa_dtype bias_dtype,
+                                                const int64_t *kv_len,
+                                                const int64_t *q_start,
+                                                const int32_t *slot_kind, int64_t B,
+                                                int64_t Hq, int64_t Hkv, int64_t S_q,
+                                                int64_t capacity, int64_t D, int64_t D_v,
+                                                float scale, float softcap, int64_t window,
+                                                abgqa_dtype dtype, void *workspace,
+                                                size_t workspace_bytes, void *stream);
+
+/*
  * attn_bias_gqa_fwd_noalloc - attn_bias_gqa_fwd without a workspace argument,
  * for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc. It allocates

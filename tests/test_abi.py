@@ -181,3 +181,43 @@ def test_noalloc_refuses_large_scratch(lib):
     assert st == WORKSPACE
     msg = ab.abgqa_last_error()
     assert "needs %d bytes of scratch" % need in msg and "holds 8388608" in msg
+
+
+def _step(lib, circular=False, **kw):
+    a = dict(out=None, q=None, k=None, v=None, ku=None, vu=None, wi=None, S_new=1, bias=None, bdt=1,
+             nonpad=None, qs=None, kind=None, B=1, Hq=4, Hkv=2, S_q=1, T=64, D=64, Dv=64, scale=0.125,
+             softcap=0.0, window=0, dtype=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    f = lib.attn_bias_gqa_decode_step_circular if circular else lib.attn_bias_gqa_decode_step
+    return f(a["out"], a["q"], a["k"], a["v"], a["ku"], a["vu"], a["wi"], a["S_new"], a["bias"], a["bdt"],
+             a["nonpad"], a["qs"], a["kind"], a["B"], a["Hq"], a["Hkv"], a["S_q"], a["T"], a["D"], a["Dv"],
+             a["scale"], a["softcap"], a["window"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+PTRS = dict(out=FAKE, q=FAKE + 4096, k=FAKE + 8192, v=FAKE + 12288, ku=FAKE + 16384, vu=FAKE + 20480,
+            nonpad=FAKE + 24576)
+
+
+@pytest.mark.parametrize("kw,circular,status,msg", [
+    (dict(B=0), False, INVALID, "must be positive"),
+    (dict(S_new=-1), False, INVALID, "S_new must be >= 0"),
+    (dict(S_new=65), True, INVALID, "at most capacity"),
+    (dict(S_new=17), False, UNSUPPORTED, "fused step takes bf16 decode shapes"),
+    (dict(dtype=0), False, UNSUPPORTED, "fused step takes bf16 decode shapes"),   # fp32
+    (dict(S_q=16, Hq=4, Hkv=2), False, UNSUPPORTED, "fused step"),                 # 32 rows: prefill
+    (dict(D=96), False, UNSUPPORTED, "fused step"),
+    (dict(B=8193, Hkv=2, Hq=4), False, UNSUPPORTED, "fused step"),                 # > 16384 pairs
+    (dict(softcap=-1.0), False, INVALID, "softcap"),
+    (dict(), False, INVALID, "null out"),
+    (dict(PTRS, ku=None), False, INVALID, "null update"),
+    (dict(PTRS, vu=FAKE + 20488), False, INVALID, "misaligned"),
+    (dict(PTRS, wi=FAKE + 28676), False, INVALID, "misaligned"),
+    (dict(PTRS, out=FAKE + 16384), False, INVALID, "alias"),
+    (dict(PTRS, bias=FAKE + 4096), False, INVALID, "alias"),
+    (dict(PTRS, bias=FAKE + 32768, bdt=5), False, UNSUPPORTED, "bias dtype"),
+    (dict(PTRS), False, WORKSPACE, "workspace"),
+    (dict(PTRS, S_new=0, ku=None, vu=None), True, WORKSPACE, "workspace"),
+])
+def test_decode_step_validation(lib, kw, circular, status, msg):
+    assert _step(lib, circular, **kw) == status
+    assert msg in ab.abgqa_last_error()

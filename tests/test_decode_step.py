@@ -1,0 +1,173 @@
+"""The fused decode step (attn_bias_gqa_decode_step and its circular form)
+against the separate calls it replaces and against the oracle.
+
+The step does a decode step's TensorScatter of K and V, its bias build and its
+attention in one launch. Its results must be those of kv_tensor_scatter (K, V),
+build_static_cache_bias and attn_bias_gqa_fwd with that bias, bit for bit
+(caches, bias and output), and the output must match the fp64 oracle within the
+bf16 tolerance. Every output, bias and workspace starts poisoned."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import additive_bias_gqa_amd as ab
+from additive_bias_gqa_amd import workloads as wl
+from pipeline import (announce, check_parity, dead_rows, dev, gpu_step, oracle_step, poisoned,
+                      poisoned_workspace)
+
+pytestmark = pytest.mark.gpu
+
+
+def fused_step(w: wl.Workload, step: wl.Step, k_dev, v_dev, bias_dtype=torch.bfloat16,
+               with_bias=True, softcap=0.0, default_q_start=False):
+    """The step through the fused entry point; returns (bias or None, out)."""
+    B, Hq, S_q, D = step.q.shape
+    Dv = v_dev.shape[3]
+    bias = poisoned((w.B, 1, S_q, w.max_seq), bias_dtype) if with_bias else None
+    out = poisoned((B, Hq, S_q, Dv), w.dtype)
+    ws = poisoned_workspace(ab.attn_bias_gqa_workspace_bytes(B, Hq, w.Hkv, S_q, w.max_seq, D, Dv))
+    fn = ab.attn_bias_gqa_decode_step_circular if w.circular else ab.attn_bias_gqa_decode_step
+    fn(dev(step.q), k_dev, v_dev, dev(step.k_new), dev(step.v_new), dev(step.write_indices),
+       dev(step.nonpad), w.scale, q_start=None if default_q_start else dev(step.q_start),
+       slot_kind=dev(step.slot_kind), window=w.window, bias=bias, out=out, workspace=ws,
+       softcap=softcap)
+    return bias, out
+
+
+def same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+def check_step(w: wl.Workload, step: wl.Step, bias_dtype=torch.bfloat16, with_bias=True,
+               softcap=0.0, default_q_start=False, oracle_check=True):
+    k1, v1 = dev(w.k_cache.clone()), dev(w.v_cache.clone())
+    k2, v2 = dev(w.k_cache.clone()), dev(w.v_cache.clone())
+    bias1, out1 = gpu_step(w, step, k1, v1, bias_dtype=bias_dtype, softcap=softcap,
+                           default_q_start=default_q_start)
+    bias2, out2 = fused_step(w, step, k2, v2, bias_dtype=bias_dtype, with_bias=with_bias,
+                             softcap=softcap, default_q_start=default_q_start)
+    torch.cuda.synchronize()
+    assert same_bits(k1, k2), "K cache after the step"
+    assert same_bits(v1, v2), "V cache after the step"
+    if with_bias:
+        assert same_bits(bias1, bias2), "bias"
+    assert same_bits(out1, out2), "output differs from the separate calls"
+    if oracle_check:
+        k_ref, v_ref, bias_ref, ref = oracle_step(w, step, w.k_cache.clone(), w.v_cache.clone(),
+                                                  default_q_start=default_q_start, softcap=softcap)
+        assert same_bits(k2.cpu(), k_ref), "K cache against the oracle"
+        assert same_bits(v2.cpu(), v_ref), "V cache against the oracle"
+        valid = step.nonpad.clamp(0, w.max_seq) if w.circular else step.nonpad
+        got = out2.float().cpu().numpy().astype(np.float64)
+        check_parity(got, ref, w.dtype, dead_rows(bias_ref, valid, w.Hq), w.name)
+
+
+CASES = {
+    "sliding_d256": lambda: wl.decode_sliding(B=3, Hq=4, Hkv=2, D=256, max_seq=1001, window=300,
+                                              nonpad_lo=1),
+    "full_d512": lambda: wl.decode_full(B=3, Hq=8, Hkv=2, D=512, max_seq=777, nonpad_lo=1),
+    "full_kvshared": lambda: wl.decode_full(B=3, Hq=8, Hkv=2, D=512, max_seq=777, nonpad_lo=1,
+                                            kv_shared=True),
+    "d64_g8": lambda: wl.decode_sliding(B=2, Hq=16, Hkv=2, D=64, max_seq=300, window=50, nonpad_lo=1),
+    "d128_g1": lambda: wl.decode_full(B=2, Hq=4, Hkv=4, D=128, max_seq=512, nonpad_lo=1),
+    "g3": lambda: wl.decode_full(B=2, Hq=6, Hkv=2, D=256, max_seq=200, nonpad_lo=1),
+    "g16": lambda: wl.decode_sliding(B=2, Hq=32, Hkv=2, D=128, max_seq=400, window=0, nonpad_lo=1),
+    "b64": lambda: wl.decode_full(B=64, Hq=8, Hkv=4, D=128, max_seq=300, nonpad_lo=1),
+    "dv256": lambda: wl.decode_full(B=3, Hq=8, Hkv=2, D=512, Dv=256, max_seq=640, nonpad_lo=1),
+    "dv512": lambda: wl.decode_full(B=3, Hq=8, Hkv=2, D=256, Dv=512, max_seq=640, nonpad_lo=1),
+    "circ_d256": lambda: wl.decode_sliding_circular(B=5, Hq=8, Hkv=4, D=256, capacity=300, window=200,
+                                                    len_lo=1, len_hi=1000),
+    "circ_d512": lambda: wl.decode_sliding_circular(B=4, Hq=16, Hkv=4, D=512, capacity=256, window=256,
+                                                    len_lo=100, len_hi=900),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_step_equals_separate_calls(name):
+    w = CASES[name]()
+    announce(f"decode step {name} {w.name}")
+    check_step(w, w.steps[0])
+
+
+@pytest.mark.parametrize("bias_dtype,with_bias", [(torch.float32, True), (torch.bfloat16, False)])
+def test_step_bias_output(bias_dtype, with_bias):
+    w = CASES["sliding_d256"]()
+    announce(f"decode step bias {bias_dtype} written={with_bias}")
+    check_step(w, w.steps[0], bias_dtype=bias_dtype, with_bias=with_bias)
+
+
+def test_step_softcap_and_default_q_start():
+    w = CASES["full_d512"]()
+    announce("decode step softcap 50, default q_start")
+    check_step(w, w.steps[0], softcap=50.0, default_q_start=True)
+
+
+def test_step_edges():
+    """Two new tokens per row (S_q = S_new = 2) with write slots that drop a
+    token (the last slot of the cache, a negative first position), a new token
+    past nonpad, a batch row with nonpad = 0, slots of an image block and pads."""
+    B, Hq, Hkv, D, T, S = 5, 8, 4, 256, 96, 2
+    dt = torch.bfloat16
+    rng = np.random.Generator(np.random.PCG64(4242))
+    kc = wl.normal(rng, (B, Hkv, T, D), dt)   # every slot finite: nonpad reaches T in row 0
+    vc = wl.normal(rng, (B, Hkv, T, D), dt)
+    q = wl.normal(rng, (B, Hq, S, D), dt)
+    kn = wl.normal(rng, (B, Hkv, S, D), dt)
+    vn = wl.normal(rng, (B, Hkv, S, D), dt)
+    wi = torch.tensor([T - 1, -1, 40, 10, 60], dtype=torch.int64)   # row 0: 2nd token dropped; row 1: 1st
+    nonpad = torch.tensor([T, 1, 30, 0, 62], dtype=torch.int64)    # row 2: tokens past nonpad
+    q_start = torch.tensor([T - 2, 0, 40, 0, 60], dtype=torch.int64)
+    kind = torch.zeros((B, T), dtype=torch.int32)
+    kind[4, 50:62] = 1            # an image block holding both queries of row 4
+    kind[2, 0:5] = wl.PAD
+    step = wl.Step(q, kn, vn, wi, nonpad, q_start, kind)
+    w = wl.Workload("step_edges", dt, B, Hq, Hkv, D, T, 20, D ** -0.5, kc, vc, [step])
+    announce("decode step edges")
+    check_step(w, step)
+
+
+@pytest.mark.parametrize("name", ["decode_sliding", "decode_full", "decode_sliding_circular"])
+def test_step_full_size(name):
+    """The full-size workloads, bit for bit against the separate calls (whose
+    output the full-size parity tests compare with the oracle)."""
+    w = getattr(wl, name)()
+    announce(f"decode step full size {w.name}")
+    check_step(w, w.steps[0], oracle_check=False)
+
+
+def test_step_graph_replay():
+    """The step captured in a HIP graph and replayed three times, eager work
+    and synchronisations between the replays: every replay gives the eager
+    result (the step rewrites the same cache rows each time)."""
+    w = CASES["sliding_d256"]()
+    step = w.steps[0]
+    announce("decode step graph replay")
+    k, v = dev(w.k_cache.clone()), dev(w.v_cache.clone())
+    bias_e, out_e = fused_step(w, step, k, v)
+    B, Hq, S_q, D = step.q.shape
+    q, kn, vn = dev(step.q), dev(step.k_new), dev(step.v_new)
+    wi, npd, qs, kind = dev(step.write_indices), dev(step.nonpad), dev(step.q_start), dev(step.slot_kind)
+    bias = poisoned((w.B, 1, S_q, w.max_seq), torch.bfloat16)
+    out = poisoned((B, Hq, S_q, D), w.dtype)
+    ws = poisoned_workspace(ab.attn_bias_gqa_workspace_bytes(B, Hq, w.Hkv, S_q, w.max_seq, D, D))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ab.attn_bias_gqa_decode_step(q, k, v, kn, vn, wi, npd, w.scale, q_start=qs, slot_kind=kind,
+                                     window=w.window, bias=bias, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ab.attn_bias_gqa_decode_step(q, k, v, kn, vn, wi, npd, w.scale, q_start=qs, slot_kind=kind,
+                                     window=w.window, bias=bias, out=out, workspace=ws)
+    for rep in range(3):
+        out.view(torch.int16).fill_(0x7FC1)
+        bias.view(torch.int16).fill_(0x7FC1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert same_bits(out, out_e), f"replay {rep}: output"
+        assert same_bits(bias, bias_e), f"replay {rep}: bias"
+        _ = (q.float() * 2).sum().item()   # eager work between replays
