@@ -616,6 +616,9 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   const __bf16* vbase = (const __bf16*)p.v + (b * p.Hkv + hk) * (int64_t)T * DV;
   const BiasT* biasb = kRules ? nullptr : (const BiasT*)p.bias + b * p.S_q * (int64_t)T;
   const int32_t* kindb = p.slot_kind ? p.slot_kind + b * T : nullptr;
+  // the next block's K/V are loaded while this one is computed, except for
+  // D = 512 with 8 wavefronts (section 3)
+  constexpr bool kPrefetch = (D <= 256 && DV <= 256) || NW == 4;
   // ---- 2b. fused decode step: the written slots this workgroup streams -------
   // Row b's update rows t in [st_tlo, st_thi) go to slots st_wb + t (mod T for
   // a circular cache). The wavefront that streams such a slot first stores the
@@ -625,9 +628,12 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   // other workgroup reads the slot (the splits' ranges are disjoint), and the
   // other wavefronts load it at most as a clamped index whose data is never
   // used. So the stream itself is the attention-only kernel's.
+  // A slot in the wavefront's first block is stored before the stream; one in a
+  // later block after the first block's loads (see side_stores), where the
+  // stores do not sit ahead of loads the stream waits for next.
+  int st_wb = 0, st_tlo = 0, st_thi = 0;
   if constexpr (kStep) {
     if (p.S_new > 0) {
-      int st_wb = 0, st_tlo = 0, st_thi = 0;
       const int64_t wpos = (b == b_guess || !p.write_idx) ? st_w_guess : p.write_idx[b];
       if (p.circular) {
         st_wb = (int)(((wpos % T) + T) % T);
@@ -638,10 +644,18 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
         st_tlo = (int)max<int64_t>(0, -wpos);
         st_thi = (int)min<int64_t>(p.S_new, T - wpos);
       }
+    }
+  }
+  // which: 0 = slots in this wavefront's first block, 1 = in its later blocks,
+  // 2 = all of its slots
+  auto reader_stores = [&](int which) {
+    if constexpr (kStep) {
       for (int t = st_tlo; t < st_thi; ++t) {
         int j = st_wb + t;
         if (p.circular && j >= T) j -= T;
         if (j < my_lo || j >= my_hi || ((j - my_lo) >> 4) % kDecWaves != w) continue;
+        const bool first = ((j - my_lo) >> 4) == w;
+        if ((which == 0 && !first) || (which == 1 && first)) continue;
         const int64_t slot = (b * p.Hkv + hk) * (int64_t)T + j;
 #pragma unroll
         for (int i = 0; i < UPL; ++i) {
@@ -653,7 +667,8 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
         }
       }
     }
-  }
+  };
+  reader_stores(kPrefetch ? 0 : 2);
 
   float m_run[E], l_run[E];
 #pragma unroll
@@ -676,7 +691,6 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   // D = 512 with 8 wavefronts (two 32 KiB blocks per lane set do not fit the
   // 256 registers a wavefront gets at two per SIMD; with one wavefront per
   // SIMD the second buffer lives in the accumulation registers).
-  constexpr bool kPrefetch = (D <= 256 && DV <= 256) || NW == 4;
   struct Blk {
     BiasT bias[E];
     int32_t kj;
@@ -824,7 +838,13 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
     Blk A, B;
     int j0 = my_lo + 16 * w;
     if (j0 < my_hi) load_blk(j0, A);
-    side_stores();   // after the first block's loads: see side_stores
+    if constexpr (kStep) {
+      // after the first block's loads (the compiler would otherwise hoist the
+      // stores above them): see side_stores
+      asm volatile("" ::: "memory");
+      reader_stores(1);
+      side_stores();
+    }
     while (j0 < my_hi) {
       const int j1 = j0 + stride;
       load_blk(j1, B);
