@@ -95,6 +95,28 @@ def gpu_step(w: wl.Workload, step: wl.Step, k_dev, v_dev, rules: bool = False,
     return bias, out
 
 
+def fused_step(w: wl.Workload, step: wl.Step, k_dev, v_dev, bias_dtype=torch.bfloat16,
+               with_bias=True, softcap=0.0, default_q_start=False):
+    """The step through the fused entry point (attn_bias_gqa_decode_step, or
+    its circular form) with poisoned bias, output and workspace; returns (bias or
+    None, out)."""
+    B, Hq, S_q, D = step.q.shape
+    Dv = v_dev.shape[3]
+    bias = poisoned((w.B, 1, S_q, w.max_seq), bias_dtype) if with_bias else None
+    out = poisoned((B, Hq, S_q, Dv), w.dtype)
+    ws = poisoned_workspace(ab.attn_bias_gqa_workspace_bytes(B, Hq, w.Hkv, S_q, w.max_seq, D, Dv))
+    fn = ab.attn_bias_gqa_decode_step_circular if w.circular else ab.attn_bias_gqa_decode_step
+    fn(dev(step.q), k_dev, v_dev, dev(step.k_new), dev(step.v_new), dev(step.write_indices),
+       dev(step.nonpad), w.scale, q_start=None if default_q_start else dev(step.q_start),
+       slot_kind=dev(step.slot_kind), window=w.window, bias=bias, out=out, workspace=ws,
+       softcap=softcap)
+    return bias, out
+
+
+def same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
 def oracle_step(w: wl.Workload, step: wl.Step, k_host, v_host, rows=None,
                 default_q_start: bool = False, softcap: float = 0.0):
     """The same pass on the oracle. Returns (k_cache, v_cache, bias, out). A

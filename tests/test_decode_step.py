@@ -14,30 +14,10 @@ import torch
 
 import additive_bias_gqa_amd as ab
 from additive_bias_gqa_amd import workloads as wl
-from pipeline import (announce, check_parity, dead_rows, dev, gpu_step, oracle_step, poisoned,
-                      poisoned_workspace)
+from pipeline import (announce, check_parity, dead_rows, dev, fused_step, gpu_step, oracle_step,
+                      poisoned, poisoned_workspace, same_bits)
 
 pytestmark = pytest.mark.gpu
-
-
-def fused_step(w: wl.Workload, step: wl.Step, k_dev, v_dev, bias_dtype=torch.bfloat16,
-               with_bias=True, softcap=0.0, default_q_start=False):
-    """The step through the fused entry point; returns (bias or None, out)."""
-    B, Hq, S_q, D = step.q.shape
-    Dv = v_dev.shape[3]
-    bias = poisoned((w.B, 1, S_q, w.max_seq), bias_dtype) if with_bias else None
-    out = poisoned((B, Hq, S_q, Dv), w.dtype)
-    ws = poisoned_workspace(ab.attn_bias_gqa_workspace_bytes(B, Hq, w.Hkv, S_q, w.max_seq, D, Dv))
-    fn = ab.attn_bias_gqa_decode_step_circular if w.circular else ab.attn_bias_gqa_decode_step
-    fn(dev(step.q), k_dev, v_dev, dev(step.k_new), dev(step.v_new), dev(step.write_indices),
-       dev(step.nonpad), w.scale, q_start=None if default_q_start else dev(step.q_start),
-       slot_kind=dev(step.slot_kind), window=w.window, bias=bias, out=out, workspace=ws,
-       softcap=softcap)
-    return bias, out
-
-
-def same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
-    return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
 
 
 def check_step(w: wl.Workload, step: wl.Step, bias_dtype=torch.bfloat16, with_bias=True,

@@ -7,9 +7,11 @@ window or none, image blocks, left padding, softcap, bf16 or fp32, bias
 variant with a bf16 or fp32 bias, or the in-kernel rules) and runs TensorScatter
 of K and V, the bias build and the attention on both sides: the caches and the
 bias must match bit for bit, the output within the stated tolerance, and rows
-with no allowed key must be exact zeros. Outputs, biases and workspaces start
-poisoned, so an unwritten element fails. Sizes keep the fp64 oracle to well
-under a second per case.
+with no allowed key must be exact zeros. A bf16 decode shape also runs the
+fused decode step (scatters, bias and attention in one launch), which must give
+the separate calls' caches, bias and output bit for bit. Outputs, biases and
+workspaces start poisoned, so an unwritten element fails. Sizes keep the fp64
+oracle to well under a second per case.
 """
 from __future__ import annotations
 
@@ -20,7 +22,7 @@ import pytest
 import torch
 
 from additive_bias_gqa_amd import workloads as wl
-from pipeline import announce, check_parity, dead_rows, dev, gpu_step, oracle_step
+from pipeline import announce, check_parity, dead_rows, dev, fused_step, gpu_step, oracle_step, same_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -112,3 +114,16 @@ def test_fuzz_case(i):
     valid = step.nonpad.clamp(0, w.max_seq) if w.circular else step.nonpad
     got = out.float().cpu().numpy().astype(np.float64)
     check_parity(got, ref, w.dtype, dead_rows(bias_ref, valid, w.Hq), f"fuzz{i}")
+    # a bf16 decode shape (S_q * Hq / Hkv <= 16, head sizes of the split-KV
+    # kernel): the fused decode step must reproduce the separate calls bit for
+    # bit (caches, the bias when built, output)
+    Dv = w.v_cache.shape[3]
+    decode_pair = (w.D == Dv and w.D in (64, 128, 256, 512)) or (w.D, Dv) in ((256, 512), (512, 256))
+    if w.dtype == torch.bfloat16 and step.S_q * (w.Hq // w.Hkv) <= 16 and decode_pair:
+        k2, v2 = dev(w.k_cache.clone()), dev(w.v_cache.clone())
+        bias2, out2 = fused_step(w, step, k2, v2, bias_dtype=bias_dtype, with_bias=not rules,
+                                 softcap=softcap, default_q_start=default_q_start)
+        assert same_bits(k2, k_dev) and same_bits(v2, v_dev), "fused step: caches"
+        if not rules:
+            assert same_bits(bias2, bias), "fused step: bias"
+        assert same_bits(out2, out), "fused step: output differs from the separate calls"
