@@ -151,3 +151,42 @@ def test_step_graph_replay():
         assert same_bits(out, out_e), f"replay {rep}: output"
         assert same_bits(bias, bias_e), f"replay {rep}: bias"
         _ = (q.float() * 2).sum().item()   # eager work between replays
+
+
+def test_step_check_mode(monkeypatch):
+    """ABGQA_CHECK=1 on the fused step: write indices, nonpad and q_start are
+    validated on the host before anything is enqueued, a workspace with a
+    nonzero arrival count is refused, and a valid step under the check still
+    matches the separate calls bit for bit."""
+    monkeypatch.setenv("ABGQA_CHECK", "1")
+    w = CASES["sliding_d256"]()
+    step = w.steps[0]
+    B = w.B
+    k, v = dev(w.k_cache.clone()), dev(w.v_cache.clone())
+    q, kn, vn = dev(step.q), dev(step.k_new), dev(step.v_new)
+    npd, qs = dev(step.nonpad), dev(step.q_start)
+    bad_w = step.write_indices.clone()
+    bad_w[1] = w.max_seq            # the new token's slot past the cache
+    announce("decode step check mode: bad device values refused")
+    with pytest.raises(RuntimeError, match=r"ABGQA_CHECK: write_indices\[1\]"):
+        ab.attn_bias_gqa_decode_step(q, k, v, kn, vn, dev(bad_w), npd, w.scale, q_start=qs,
+                                     window=w.window)
+    bad_np = step.nonpad.clone()
+    bad_np[0] = -2
+    with pytest.raises(RuntimeError, match=r"ABGQA_CHECK: nonpad_kv_seqlen\[0\] = -2"):
+        ab.attn_bias_gqa_decode_step(q, k, v, kn, vn, dev(step.write_indices), dev(bad_np), w.scale,
+                                     q_start=qs, window=w.window)
+    bad_qs = step.q_start.clone()
+    bad_qs[2] = -5
+    with pytest.raises(RuntimeError, match=r"ABGQA_CHECK: q_start\[2\] = -5"):
+        ab.attn_bias_gqa_decode_step(q, k, v, kn, vn, dev(step.write_indices), npd, w.scale,
+                                     q_start=dev(bad_qs), window=w.window)
+    D = step.q.shape[3]
+    ws = poisoned_workspace(ab.attn_bias_gqa_workspace_bytes(B, w.Hq, w.Hkv, 1, w.max_seq, D, D))
+    ws[4:8] = torch.tensor([3, 0, 0, 0], dtype=torch.uint8)    # arrival count 1 left at 3
+    with pytest.raises(RuntimeError, match="ABGQA_CHECK: decode arrival count 1"):
+        ab.attn_bias_gqa_decode_step(q, k, v, kn, vn, dev(step.write_indices), npd, w.scale,
+                                     q_start=qs, window=w.window, workspace=ws)
+    assert same_bits(k, dev(w.k_cache)), "a refused call must not have touched the cache"
+    announce("decode step check mode: valid step")
+    check_step(w, step, oracle_check=False)
