@@ -187,14 +187,14 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   // ---- 0a. fused decode step: the loads of its two side outputs --------------
   // The launch also does the step's TensorScatter of K and V and its bias
   // build, and no workgroup waits for another: rank r < B of each kv head
-  // writes batch row r's new K/V rows into the cache; the workgroups of a
-  // guessed batch row (Hkv * n_split of them) share that row's bias chunks, so
-  // every chunk of every row is written once; and a workgroup that reads a
-  // slot this step writes takes that key from the update rows, not from the
-  // cache, so no cache slot is read while it is written. The attention masks
-  // with the in-kernel rules, which give exactly the mask the bias holds.
-  // The loads go out here (they retire before the range scan's, which the
-  // workgroup waits for anyway); the stores follow the first barrier.
+  // writes batch row r's new K/V rows into the cache; the wavefront that
+  // streams a slot this step writes stores that slot's update row itself
+  // before its own loads of it (section 2b); the workgroups of a guessed batch
+  // row (Hkv * n_split of them) share that row's bias chunks, so every chunk
+  // of every row is written once. The attention masks with the in-kernel
+  // rules, which give exactly the mask the bias holds. The loads go out here
+  // (they retire before the range scan's, which the workgroup waits for
+  // anyway); the stores go out later (sections 1a and 2b, side_stores).
   constexpr int KCH = D / 8, VCH = DV / 8;   // 16-byte chunks of a K / V row
   const bool st_writer = kStep && rank < p.B && p.S_new > 0;
   const int st_nch = kStep ? p.S_new * (KCH + VCH) : 0;   // chunks of a writer
