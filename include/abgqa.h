@@ -13,7 +13,10 @@
  *
  * mobius issue #366, "Emit bias-aware external-KV (TensorScatter +
  * nonpad_kv_seqlen) attention for float-bias decoders", states the problem
- * these three calls solve.
+ * these three calls solve. kv_scatter_and_bias does the first two in one
+ * launch, attn_bias_gqa_decode_step all three for decode shapes; each has a
+ * circular-cache form (*_circular), and attn_bias_gqa_fwd_noalloc is the
+ * attention for callers that cannot allocate.
  *
  * Conventions shared by every entry point
  *   - Tensors are dense, row-major (last index fastest), in caller-owned device
