@@ -234,9 +234,12 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
     }
   };
   bf16x8 st_val{};
-  int64_t st_w_own = 0, st_w_guess = 0;
+  int64_t st_w_own = 0;
+  int64_t st_wpos = 0;   // write position of the row this workgroup streams
   // update row 0 of the guessed batch row (its K then V chunks, chunk
-  // lane + 64 i), for the wavefront that streams its slot (section 2b)
+  // lane + 64 i), for the wavefront that streams its slot (section 2b;
+  // reloaded in section 1c when the assignment moves the workgroup to another
+  // row)
   constexpr int UPL = (KCH + VCH + 63) / 64;
   bf16x8 st_row[UPL];
   auto upd_chunk = [&](int64_t bq, int t, int c) -> const bf16x8* {
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
     if (st_writer && tid < st_nch) st_val = ld_global<bf16x8>(st_src(tid));
     if (p.write_idx) {
       if (st_writer) st_w_own = p.write_idx[rank];
-      st_w_guess = p.write_idx[b_guess];
+      st_wpos = p.write_idx[b_guess];
     }
   }
   // bias chunks (8 keys each) of the guessed row: workgroup wid of the row's
@@ -520,8 +523,18 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   if constexpr (kRules) {
     // causal / window keys of every query row, then the image block of any row
     if (b != b_guess) {
-      // the fused step's bias chunks (section 1a) read the guessed row's rules
-      if constexpr (kStep) __syncthreads();
+      // the fused step's bias chunks (section 1a) read the guessed row's rules;
+      // the new row's write position and update row 0 share the rules' memory
+      // round trip
+      if constexpr (kStep) {
+        if (p.S_new > 0) {
+          if (p.write_idx) st_wpos = p.write_idx[b];
+#pragma unroll
+          for (int i = 0; i < UPL; ++i)
+            st_row[i] = ld_global<bf16x8>(upd_chunk(b, 0, min(lane + 64 * i, KCH + VCH - 1)));
+        }
+        __syncthreads();
+      }
       make_rules(b);
     }
     __syncthreads();
@@ -578,21 +591,10 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   const int my_hi = min(live_hi, my_lo + per);
 
   // ---- 2. per-lane row data -------------------------------------------------
-  // Q as the A operand: lane holds row (lane % 16), d-slots 32*i + 8*(lane/16)
+  // lane layouts: Q as the A operand (row lane % 16, d-slots 32*i + 8*(lane/16),
+  // loaded in section 2c); S with key lane % 16 and rows 4*(lane/16) + e
   const int qrow = lane & 15;
   const int kgrp = lane >> 4;
-  bf16x8 qa[kQinLds ? 1 : KSTEPS];
-  if constexpr (!kQinLds) {
-    const bool ok = qrow < R;
-    const int s = ok ? qrow / G : 0, g = ok ? qrow % G : 0;
-    const __bf16* qp = (const __bf16*)p.q +
-        (((b * p.Hq + hk * G + g) * p.S_q + s) * (int64_t)D) + 8 * kgrp;
-#pragma unroll
-    for (int i = 0; i < KSTEPS; ++i) {
-      if (ok) qa[i] = ld_global<bf16x8>(qp + 32 * i);
-      else qa[i] = bf16x8{};
-    }
-  }
   // rows this lane holds in the S layout: r = 4 * kgrp + e
   int row_s[E];
   bool row_ok[E];
@@ -634,7 +636,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   int st_wb = 0, st_tlo = 0, st_thi = 0;
   if constexpr (kStep) {
     if (p.S_new > 0) {
-      const int64_t wpos = (b == b_guess || !p.write_idx) ? st_w_guess : p.write_idx[b];
+      const int64_t wpos = st_wpos;
       if (p.circular) {
         st_wb = (int)(((wpos % T) + T) % T);
         st_tlo = (int)min<int64_t>(p.S_new, max<int64_t>(0, -wpos));
@@ -661,7 +663,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
         for (int i = 0; i < UPL; ++i) {
           const int c = lane + 64 * i;
           if (c >= KCH + VCH) break;
-          const bf16x8 v = (t == 0 && b == b_guess) ? st_row[i] : ld_global<bf16x8>(upd_chunk(b, t, c));
+          const bf16x8 v = t == 0 ? st_row[i] : ld_global<bf16x8>(upd_chunk(b, t, c));
           bf16x8* dst = c < KCH ? (bf16x8*)p.k + slot * KCH + c : (bf16x8*)p.v + slot * VCH + (c - KCH);
           *dst = v;
         }
@@ -669,6 +671,25 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
     }
   };
   reader_stores(kPrefetch ? 0 : 2);
+
+  // ---- 2c. Q as the A operand (head sizes below 512: in registers) -----------
+  // Issued only now: the memory counter retires in order, so a wait for any
+  // earlier load (the step's write position, the update rows the reader stores
+  // above hold) would otherwise also wait for these cold loads, a whole memory
+  // round trip ahead of the first K/V loads. Unconditional (rows past R load
+  // row 0 and take zeros), so no exec-masked branch hides their count.
+  bf16x8 qa[kQinLds ? 1 : KSTEPS];
+  if constexpr (!kQinLds) {
+    const bool ok = qrow < R;
+    const int s = ok ? qrow / G : 0, g = ok ? qrow % G : 0;
+    const __bf16* qp = (const __bf16*)p.q +
+        (((b * p.Hq + hk * G + g) * p.S_q + s) * (int64_t)D) + 8 * kgrp;
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
+      const bf16x8 v = ld_global<bf16x8>(qp + 32 * i);
+      qa[i] = ok ? v : bf16x8{};
+    }
+  }
 
   float m_run[E], l_run[E];
 #pragma unroll
