@@ -621,6 +621,31 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   // the next block's K/V are loaded while this one is computed, except for
   // D = 512 with 8 wavefronts (section 3)
   constexpr bool kPrefetch = (D <= 256 && DV <= 256) || NW == 4;
+  // Which wavefront streams block i (keys my_lo + 16 i ...). One wavefront per
+  // SIMD: block i goes to wavefront i % NW. Two per SIMD (NW = 8, waves w and
+  // w + 4 share a SIMD, w launched first): the SIMD issues the older
+  // wavefront's instructions first when both are ready, so with equal shares
+  // the younger ones (4..7) stream about a third slower (measured on the
+  // 16-row, 8192-slot, head-512 decode: 96 against 72 us) and run on alone
+  // after the older ones finish, one block in flight per SIMD. So waves 0..3
+  // take the first three quarters of the blocks (block i to wave i % 4) and
+  // waves 4..7 the rest (block n_old + i to wave 4 + i % 4); shares of 9/16 to
+  // 14/16 measured, 11/16 and 12/16 fastest. A fixed function of the split, so
+  // results stay bit-identical from run to run.
+  constexpr bool kTwoPerSimd = NW == 8;
+  static_assert(!kTwoPerSimd || !kPrefetch, "two wavefronts per SIMD stream one block at a time");
+  constexpr int kOldShare = 12;   // sixteenths of the blocks for waves 0..3
+  const int n_blk = my_hi > my_lo ? (my_hi - my_lo + 15) >> 4 : 0;
+  const int n_old = kTwoPerSimd ? (n_blk * kOldShare + 15) / 16 : n_blk;
+  auto blk_wave = [&](int i) {
+    if constexpr (kTwoPerSimd) return i < n_old ? (i & 3) : 4 + ((i - n_old) & 3);
+    else return i % NW;
+  };
+  // the wavefront's own first block
+  auto blk_first = [&](int i) {
+    if constexpr (kTwoPerSimd) return i < n_old ? i < 4 : i - n_old < 4;
+    else return i < NW;
+  };
   // ---- 2b. fused decode step: the written slots this workgroup streams -------
   // Row b's update rows t in [st_tlo, st_thi) go to slots st_wb + t (mod T for
   // a circular cache). The wavefront that streams such a slot first stores the
@@ -655,8 +680,8 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
       for (int t = st_tlo; t < st_thi; ++t) {
         int j = st_wb + t;
         if (p.circular && j >= T) j -= T;
-        if (j < my_lo || j >= my_hi || ((j - my_lo) >> 4) % kDecWaves != w) continue;
-        const bool first = ((j - my_lo) >> 4) == w;
+        if (j < my_lo || j >= my_hi || blk_wave((j - my_lo) >> 4) != w) continue;
+        const bool first = blk_first((j - my_lo) >> 4);
         if ((which == 0 && !first) || (which == 1 && first)) continue;
         const int64_t slot = (b * p.Hkv + hk) * (int64_t)T + j;
 #pragma unroll
@@ -703,7 +728,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
   const int vkey = lane / LPR;       // key offset within a V load
   const int vd = 8 * (lane % LPR);   // first d of this lane in the PV layout
 
-  // ---- 3. stream 16-key blocks, wavefront w takes blocks w, w+NW, ... -------
+  // ---- 3. stream 16-key blocks (block i by wavefront blk_wave(i)) -----------
   // Loads are unconditional: a key index past the range is clamped to the last
   // key of the range (a valid, finite row), and its score is masked by `keep`
   // below, so its weight is exactly 0. No exec-masked branches means the
@@ -877,7 +902,10 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
       j0 = j2;
     }
   } else {
-    for (int j0 = my_lo + 16 * w; j0 < my_hi; j0 += stride) {
+    const int i_end = (!kTwoPerSimd || w >= 4) ? n_blk : n_old;
+    const int i_step = kTwoPerSimd ? 4 : NW;
+    for (int i = kTwoPerSimd && w >= 4 ? n_old + w - 4 : w; i < i_end; i += i_step) {
+      const int j0 = my_lo + 16 * i;
       Blk A;
       load_blk(j0, A);
       compute_blk(j0, A);
