@@ -498,7 +498,6 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
         dma16_sl(kindb ? (const void*)(kindb + j0) : (const void*)kg, off, dst);
       } else {
         constexpr int EPV = 16 / (int)sizeof(BiasT);
-        constexpr int CB = Geo::BROW / 16;
         const int col = m_col[m];   // this lane's first key in the row
         const unsigned off = m_off[m] + (unsigned)(min(T - EPV - j0 - col, 0) * (int)sizeof(BiasT));
         dma16_sl(biasb + (int64_t)s0 * T + j0, off, dst);
