@@ -16,15 +16,31 @@ int decode_num_splits(int64_t B, int64_t Hkv, int64_t max_seq) {
   const char* v = getenv("ABGQA_DECODE_SPLITS");
   const int forced = v ? atoi(v) : 0;
   if (forced > 0) return forced > 256 ? 256 : forced;
-  // about one workgroup per CU (256 CUs): fewer, longer-lived workgroups keep
-  // their loads streaming; fixed per-workgroup costs (range scan, merge,
-  // partial write) dominate when each gets only a few blocks
-  int64_t n = (256 + B * Hkv - 1) / (B * Hkv);
-  const int64_t by_len = (max_seq + 63) / 64;
-  if (n > by_len) n = by_len;
-  if (n > 64) n = 64;
-  if (n < 1) n = 1;
-  return (int)n;
+  // The grid runs in rounds of 256 workgroups (one per CU): a round that is
+  // only partly filled leaves CUs idle while the rest run, and the longest
+  // workgroup of a round sets its end. Splits let the balancing pass (section
+  // 1b of the kernel) even out rows of different live length, but each adds a
+  // workgroup's fixed costs (range, merge, record). So: among the split counts
+  // that keep the grid within two rounds, the one whose rounds are fullest;
+  // ties go to fewer splits. One split once B * Hkv fills two rounds by itself.
+  // Measured (decode over 8192 slots, head 512, lengths U{1024..8192}): B * Hkv
+  // 48 -> 5 splits 105.6 us (6: 146.7), 96 -> 5 202.7 us (3: 271), 160 -> 3
+  // 299.6 us (2: 391); sliding window 1024 over 4096 slots, head 256: 136 -> 3
+  // 38.5 us (2: 45.1), 200 -> 1 42.1 us (2: 52.1).
+  const int64_t P = B * Hkv;
+  int64_t cap = (max_seq + 63) / 64;   // at least 64 slots per split
+  if (cap > 64) cap = 64;
+  if (cap < 1) cap = 1;
+  int64_t best = 1, best_rounds = (P + 255) / 256;
+  for (int64_t n = 2; n <= cap; ++n) {
+    const int64_t rounds = (P * n + 255) / 256;
+    if (rounds > 2) break;
+    if (n * best_rounds > best * rounds) {   // fuller rounds: n / rounds larger
+      best = n;
+      best_rounds = rounds;
+    }
+  }
+  return (int)best;
 }
 
 // workspace: the arrival counts, then one partial record per (kv head, rank),

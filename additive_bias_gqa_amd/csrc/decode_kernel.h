@@ -127,9 +127,24 @@ __device__ __forceinline__ void ld_agent2(const float* p, float& x, float& y) {
   y = __uint_as_float((uint32_t)(u >> 32));
 }
 
+// Wavefronts per SIMD the register allocation must allow. The head-256
+// kernels with up to 2 rows and the smaller heads with up to 8 fit in 256
+// registers without spilling, which lets two workgroups share a CU: a grid of
+// more than 256 workgroups (several splits per row, or B * Hkv > 256) then
+// runs at once instead of in two rounds (B 40, Hkv 8, sliding window 1024,
+// head 256: 79.9 -> 76.4 us). Larger ones keep one wavefront per SIMD (the
+// head-512 kernels already run two, at eight wavefronts per workgroup).
+template <int D, int DV, int NR, int NW>
+constexpr int decode_min_waves_per_simd() {
+  constexpr int H = D > DV ? D : DV;
+  return (NW == 4 && ((H <= 256 && NR <= 2) || (H <= 128 && NR <= 8))) ? 2 : 1;
+}
+
 // D: head size of Q and K; DV: of V and the output (they may differ)
 template <int D, int DV, int NR, int NW, bool kRules, typename BiasT, bool kStep = false>
-__global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams p) {
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(decode_min_waves_per_simd<D, DV, NR, NW>())))
+void attn_decode_kernel(AttnParams p) {
   static_assert(!kStep || kRules, "the fused step masks with the in-kernel rules");
   constexpr int kDecThreads = NW * 64;
   constexpr int kDecWaves = NW;
