@@ -221,3 +221,36 @@ PTRS = dict(out=FAKE, q=FAKE + 4096, k=FAKE + 8192, v=FAKE + 12288, ku=FAKE + 16
 def test_decode_step_validation(lib, kw, circular, status, msg):
     assert _step(lib, circular, **kw) == status
     assert msg in ab.abgqa_last_error()
+
+
+def test_decode_split_count(lib, monkeypatch):
+    """The decode grid's split count, read off the workspace size (one record
+    per (kv head, batch row, split)): among the counts that keep B * Hkv *
+    n_split within two rounds of 256 workgroups (at most max_seq / 64 and 64),
+    the one whose rounds are fullest, ties to fewer splits."""
+    monkeypatch.delenv("ABGQA_DECODE_SPLITS", raising=False)
+    CNT = 64 * 1024
+
+    def splits(B, Hq, Hkv, T, D):
+        G = Hq // Hkv
+        nr = 1
+        while nr < G:
+            nr *= 2
+        rec = (nr * D + 2 * nr + 3) // 4 * 4 * 4
+        got = lib.attn_bias_gqa_workspace_bytes(B, Hq, Hkv, 1, T, D, D) - CNT
+        assert got % (B * Hkv * rec) == 0
+        return got // (B * Hkv * rec)
+
+    # sliding layers (Hkv 8, head 256, 4096 slots): 64 pairs fill one round at
+    # 4 splits; 96 -> 5 (480 of 512); 136 -> 3 (408 of 512); 200 and more: 1
+    assert [splits(B, 16, 8, 4096, 256) for B in (8, 12, 17, 25, 40, 64)] == [4, 5, 3, 1, 1, 1]
+    # full-attention layers (Hkv 4, head 512, 8192 slots): 48 pairs -> 5
+    # (240 of 256), 64 -> 4, 96 -> 5, 160 -> 3
+    assert [splits(B, 16, 4, 8192, 512) for B in (12, 16, 24, 40)] == [5, 4, 5, 3]
+    # few pairs: capped at 64 splits and at one split per 64 slots
+    assert splits(1, 8, 8, 4096, 128) == 32
+    assert splits(1, 2, 1, 8192, 128) == 64
+    assert splits(1, 2, 1, 300, 128) == 5
+    # the override is read at every call
+    monkeypatch.setenv("ABGQA_DECODE_SPLITS", "7")
+    assert splits(8, 16, 8, 4096, 256) == 7

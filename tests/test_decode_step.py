@@ -108,11 +108,22 @@ def test_step_edges():
     check_step(w, step)
 
 
-@pytest.mark.parametrize("name", ["decode_sliding", "decode_full", "decode_sliding_circular"])
+FULL_STEP = {
+    "decode_sliding": wl.decode_sliding,
+    "decode_full": wl.decode_full,
+    "decode_sliding_circular": wl.decode_sliding_circular,
+    # batches that do not divide the 256 CUs (5 splits of 96 pairs; 1 split of 320)
+    "decode_sliding_b12": lambda: wl.decode_sliding(B=12),
+    "decode_sliding_b40": lambda: wl.decode_sliding(B=40),
+    "decode_full_b24": lambda: wl.decode_full(B=24),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_STEP))
 def test_step_full_size(name):
     """The full-size workloads, bit for bit against the separate calls (whose
     output the full-size parity tests compare with the oracle)."""
-    w = getattr(wl, name)()
+    w = FULL_STEP[name]()
     announce(f"decode step full size {w.name}")
     check_step(w, w.steps[0], oracle_check=False)
 

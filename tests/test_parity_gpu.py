@@ -920,6 +920,13 @@ FULL = {
     # slots, the vision chunk with 1536 (window + chunk)
     "decode_sliding_circular": (lambda: wl.decode_sliding_circular(), "all"),
     "prefill_vision_circular": (lambda: wl.prefill_vision_circular(), "all"),
+    # decode batches that do not divide the 256 CUs: 96 (b, kv head) pairs x 5
+    # splits (480 workgroups, two to a CU), 320 pairs x 1 split (more
+    # workgroups than CUs), and the full layer's 96 pairs x 5 splits (two
+    # rounds of one workgroup per CU)
+    "decode_sliding_b12": (lambda: wl.decode_sliding(B=12), "all"),
+    "decode_sliding_b40": (lambda: wl.decode_sliding(B=40), "all"),
+    "decode_full_b24": (lambda: wl.decode_full(B=24), "all"),
 }
 
 
