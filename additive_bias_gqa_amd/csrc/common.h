@@ -195,6 +195,13 @@ template <typename T>
 __device__ __forceinline__ T ld_global(const void* p) {
   return *reinterpret_cast<const T*>(p);
 }
+// A load of data that is read once (the K and V rows a decode call streams):
+// non-temporal, so the lines are not kept in the caches for reuse that will
+// not come, and do not push out what will be reused.
+template <typename T>
+__device__ __forceinline__ T ld_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+}
 
 __device__ __forceinline__ int64_t clamp_nonpad(int64_t np, int64_t max_seq) {
   return np < 0 ? 0 : (np > max_seq ? max_seq : np);

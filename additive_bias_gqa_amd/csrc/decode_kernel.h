@@ -643,13 +643,14 @@ void attn_decode_kernel(AttnParams p) {
   // the younger ones (4..7) stream about a third slower (measured on the
   // 16-row, 8192-slot, head-512 decode: 96 against 72 us) and run on alone
   // after the older ones finish, one block in flight per SIMD. So waves 0..3
-  // take the first three quarters of the blocks (block i to wave i % 4) and
-  // waves 4..7 the rest (block n_old + i to wave 4 + i % 4); shares of 9/16 to
-  // 14/16 measured, 11/16 and 12/16 fastest. A fixed function of the split, so
-  // results stay bit-identical from run to run.
+  // take the first 11/16 of the blocks (block i to wave i % 4) and waves 4..7
+  // the rest (block n_old + i to wave 4 + i % 4); shares of 8/16 to 14/16
+  // measured, 11/16 fastest with the K/V loads non-temporal (12/16 before).
+  // A fixed function of the split, so results stay bit-identical from run to
+  // run.
   constexpr bool kTwoPerSimd = NW == 8;
   static_assert(!kTwoPerSimd || !kPrefetch, "two wavefronts per SIMD stream one block at a time");
-  constexpr int kOldShare = 12;   // sixteenths of the blocks for waves 0..3
+  constexpr int kOldShare = 11;   // sixteenths of the blocks for waves 0..3
   const int n_blk = my_hi > my_lo ? (my_hi - my_lo + 15) >> 4 : 0;
   const int n_old = kTwoPerSimd ? (n_blk * kOldShare + 15) / 16 : n_blk;
   auto blk_wave = [&](int i) {
@@ -775,11 +776,11 @@ void attn_decode_kernel(AttnParams p) {
     }
     const __bf16* kp = kbase + (int64_t)jk * D + 8 * kgrp;
 #pragma unroll
-    for (int i = 0; i < KSTEPS; ++i) bl.k[i] = ld_global<bf16x8>(kp + 32 * i);
+    for (int i = 0; i < KSTEPS; ++i) bl.k[i] = ld_stream<bf16x8>(kp + 32 * i);
 #pragma unroll
     for (int it = 0; it < NV; ++it) {
       const int jv = min(j0 + it * KPI + vkey, my_hi - 1);
-      bl.v[it] = ld_global<bf16x8>(vbase + (int64_t)jv * DV + vd);
+      bl.v[it] = ld_stream<bf16x8>(vbase + (int64_t)jv * DV + vd);
     }
   };
   const int stride = 16 * kDecWaves;
