@@ -202,6 +202,13 @@ template <typename T>
 __device__ __forceinline__ T ld_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
 }
+// A store of data that is not read again by this call (the prefill output
+// rows): non-temporal, so it does not push the K/V tiles that the other query
+// tiles still fetch out of the caches.
+template <typename T>
+__device__ __forceinline__ void st_stream(void* p, const T& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));
+}
 
 __device__ __forceinline__ int64_t clamp_nonpad(int64_t np, int64_t max_seq) {
   return np < 0 ? 0 : (np > max_seq ? max_seq : np);

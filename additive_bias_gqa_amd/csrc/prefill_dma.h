@@ -1128,7 +1128,9 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
     // back row by row (this wavefront's own LDS: no barrier; the compiler
     // waits for the writes before the reads, and LDS accesses of one
     // wavefront take effect in order, so the next pass overwrites only what
-    // was read)
+    // was read), with non-temporal stores: the output is not read again here,
+    // and the caches keep the K/V tiles other workgroups still fetch (vision
+    // chunk 41.9 -> 40.6 us, long prefill 349.9 -> 343.4 us)
 #pragma unroll
     for (int k = 0; k < RW / RPO; ++k) {
       const int rl = k * RPO + lane / CPRO, c = lane % CPRO;
@@ -1136,8 +1138,8 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
       const int rr = RW * rg + rl;   // the workgroup's row: token rr / G of the tile, head rr % G
       const int so = s0 + rr / G;
       if (rr < MQ * G && so < p.S_q)
-        *reinterpret_cast<u32x4*>((uint16_t*)p.out + ((b * p.Hq + hk * G + rr % G) * p.S_q + so) * (int64_t)DV +
-                                  pass * DVP + 8 * c) = v;
+        st_stream<u32x4>((uint16_t*)p.out + ((b * p.Hq + hk * G + rr % G) * p.S_q + so) * (int64_t)DV +
+                             pass * DVP + 8 * c, v);
     }
   }
 }
