@@ -81,6 +81,23 @@ __device__ __forceinline__ void dma16(const void* gsrc, const unsigned char* lds
       : "v"(gsrc), "s"(lds));
 }
 
+// The same fetch, non-temporal: for data read once (a workgroup's Q rows),
+// which should not push the K/V tiles other workgroups still fetch out of the
+// caches.
+__device__ __forceinline__ void dma16_stream(const void* gsrc, const unsigned char* lds_wave_base) {
+  const unsigned lds = __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)((__attribute__((address_space(3))) const unsigned char*)lds_wave_base));
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gsrc), "s"(lds));
+}
+
 // The same fetch from a wave-uniform base address plus a per-lane 32-bit byte
 // offset (the scalar-base form: no per-lane address arithmetic).
 __device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff,
@@ -333,7 +350,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_dma_kernel(AttnParams p,
       const int rq = RW * rg + rl;
       const int sq = min(s0 + rq / G, p.S_q - 1);
       const __bf16* src = (const __bf16*)p.q + ((b * p.Hq + hk * G + rq % G) * p.S_q + sq) * (int64_t)D;
-      dma16(src + 8 * (cc ^ swz_bits<D>(rl)), qw + k * 1024);
+      dma16_stream(src + 8 * (cc ^ swz_bits<D>(rl)), qw + k * 1024);   // long prefill 337.6 -> 332.0 us
     }
     wait_vmcnt<0>();
     const unsigned qb = lds_addr(qw) & kLdsMask;
