@@ -15,15 +15,20 @@
 // every such read is shared by the G query heads of the group.
 //
 // Layout of the work
-//   grid      B * Hkv * n_split workgroups of 4 wavefronts; consecutive
-//             logical ids (the splits of one (b, kv head)) share an XCD.
+//   grid      B * Hkv * n_split workgroups of 4 wavefronts (8 for heads of
+//             512 with up to 4 rows per lane group); consecutive logical ids
+//             (the splits of one (b, kv head)) share an XCD. n_split fills
+//             whole rounds of 256 workgroups (decode_num_splits).
 //   rows      r = s * G + g (query token s, head g of the group), R <= 16;
 //             the 16 rows of the matrix-core tile are padded with zeros.
 //   live      [lo, hi): the first and last key any row may attend, found from
 //             the bias (or from the rules); split i takes an even share of it.
-//   block     16 keys per wavefront step:
+//   block     16 keys per wavefront step (block i by one wavefront: i mod
+//             NW, or unevenly between the two wavefronts of a SIMD, see
+//             blk_wave):
 //             S = Q K^T on the matrix cores (K read straight from HBM into the
-//             B-operand registers, 16 bytes per lane), online softmax on the
+//             B-operand registers, 16 bytes per lane, non-temporal like the V
+//             loads: every K/V byte is read once), online softmax on the
 //             S layout (lane = key, 4 rows per lane), then O += P V on the
 //             vector ALU with V rows read coalesced (lane = 8 values of d).
 //             The softmax weights cross layouts through a small LDS buffer.
