@@ -66,7 +66,12 @@ static void launch_decode_nw(const AttnParams& p, hipStream_t stream) {
 template <int D, int DV, int NR>
 static hipError_t launch_decode_d(const AttnParams& p, hipStream_t stream) {
   constexpr int NW = decode_waves<D, DV, NR>();
-  launch_decode_nw<D, DV, NR, NW>(p, stream);
+  if constexpr (decode_has_eight<D, DV, NR>()) {
+    if (decode_use_eight(p)) launch_decode_nw<D, DV, NR, 8>(p, stream);
+    else launch_decode_nw<D, DV, NR, NW>(p, stream);
+  } else {
+    launch_decode_nw<D, DV, NR, NW>(p, stream);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) set_launch_detail("decode kernel launch");
   return e;

@@ -12,12 +12,23 @@
 
 namespace abgqa {
 
-template <int D, int DV, int NR>
-static hipError_t launch_step_d(const AttnParams& p, hipStream_t stream) {
-  constexpr int NW = decode_waves<D, DV, NR>();
+template <int D, int DV, int NR, int NW>
+static void launch_step_nw(const AttnParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.n_split));
   hipLaunchKernelGGL((attn_decode_kernel<D, DV, NR, NW, true, uint16_t, true>), grid, dim3(NW * 64), 0,
                      stream, p);
+}
+
+template <int D, int DV, int NR>
+static hipError_t launch_step_d(const AttnParams& p, hipStream_t stream) {
+  constexpr int NW = decode_waves<D, DV, NR>();
+  // the instantiation the attention-only launch picks for the same shape
+  if constexpr (decode_has_eight<D, DV, NR>()) {
+    if (decode_use_eight(p)) launch_step_nw<D, DV, NR, 8>(p, stream);
+    else launch_step_nw<D, DV, NR, NW>(p, stream);
+  } else {
+    launch_step_nw<D, DV, NR, NW>(p, stream);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) set_launch_detail("decode step kernel launch");
   return e;

@@ -16,7 +16,8 @@
 //
 // Layout of the work
 //   grid      B * Hkv * n_split workgroups of 4 wavefronts (8 for heads of
-//             512 with up to 4 rows per lane group); consecutive logical ids
+//             512 with up to 4 rows per lane group, and for heads of 256 with
+//             up to 2 when the grid is one round); consecutive logical ids
 //             (the splits of one (b, kv head)) share an XCD. n_split fills
 //             whole rounds of 256 workgroups (decode_num_splits).
 //   rows      r = s * G + g (query token s, head g of the group), R <= 16;
@@ -105,6 +106,19 @@ constexpr int kSampleStride = 128;
 template <int D, int DV, int NR>
 constexpr int decode_waves() {
   return (NR <= 4 && (D > DV ? D : DV) >= 512) ? 8 : 4;
+}
+// Heads of 256 with up to 2 rows per lane group also have an eight-wavefront
+// form (two per SIMD, one block in flight each, blocks dealt as for head 512),
+// launched when the grid is one round of at most 256 workgroups: the sliding
+// decode step (B 8, Hkv 8, 4 splits) 20.45 -> 20.0 us, its circular form 20.7
+// -> 20.0. Above 256 workgroups the four-wavefront form stays, whose
+// workgroups can share a CU (B 12: 28.6 against 34.3 us with eight).
+template <int D, int DV, int NR>
+constexpr bool decode_has_eight() {
+  return (D > DV ? D : DV) == 256 && NR <= 2;
+}
+inline bool decode_use_eight(const AttnParams& p) {
+  return (int64_t)p.B * p.Hkv * p.n_split <= 256;
 }
 
 // Agent-scope (whole-GPU) stores and loads: they complete at, and read from,
@@ -638,9 +652,9 @@ void attn_decode_kernel(AttnParams p) {
   const __bf16* vbase = (const __bf16*)p.v + (b * p.Hkv + hk) * (int64_t)T * DV;
   const BiasT* biasb = kRules ? nullptr : (const BiasT*)p.bias + b * p.S_q * (int64_t)T;
   const int32_t* kindb = p.slot_kind ? p.slot_kind + b * T : nullptr;
-  // the next block's K/V are loaded while this one is computed, except for
-  // D = 512 with 8 wavefronts (section 3)
-  constexpr bool kPrefetch = (D <= 256 && DV <= 256) || NW == 4;
+  // the next block's K/V are loaded while this one is computed, except with
+  // eight wavefronts (section 3)
+  constexpr bool kPrefetch = NW == 4;
   // Which wavefront streams block i (keys my_lo + 16 i ...). One wavefront per
   // SIMD: block i goes to wavefront i % NW. Two per SIMD (NW = 8, waves w and
   // w + 4 share a SIMD, w launched first): the SIMD issues the older
@@ -655,7 +669,9 @@ void attn_decode_kernel(AttnParams p) {
   // run.
   constexpr bool kTwoPerSimd = NW == 8;
   static_assert(!kTwoPerSimd || !kPrefetch, "two wavefronts per SIMD stream one block at a time");
-  constexpr int kOldShare = 11;   // sixteenths of the blocks for waves 0..3
+  // sixteenths of the blocks for waves 0..3 (head 256: 12/16 fastest of 8,
+  // 11 to 14)
+  constexpr int kOldShare = (D > DV ? D : DV) >= 512 ? 11 : 12;
   const int n_blk = my_hi > my_lo ? (my_hi - my_lo + 15) >> 4 : 0;
   const int n_old = kTwoPerSimd ? (n_blk * kOldShare + 15) / 16 : n_blk;
   auto blk_wave = [&](int i) {
@@ -754,10 +770,12 @@ void attn_decode_kernel(AttnParams p) {
   // key of the range (a valid, finite row), and its score is masked by `keep`
   // below, so its weight is exactly 0. No exec-masked branches means the
   // compiler can keep every load of a block in flight at once.
-  // The next block's K/V are loaded while this one is computed, except for
-  // D = 512 with 8 wavefronts (two 32 KiB blocks per lane set do not fit the
-  // 256 registers a wavefront gets at two per SIMD; with one wavefront per
-  // SIMD the second buffer lives in the accumulation registers).
+  // With four wavefronts the next block's K/V are loaded while this one is
+  // computed (at D = 512 the second buffer lives in the accumulation
+  // registers); with eight (two per SIMD) each wavefront has one block in
+  // flight: two 32 KiB head-512 blocks per lane set do not fit the 256
+  // registers a wavefront gets at two per SIMD, and the SIMD's two wavefronts
+  // keep two blocks in flight between them.
   struct Blk {
     BiasT bias[E];
     int32_t kj;
