@@ -17,13 +17,15 @@
 // Layout of the work
 //   grid      B * Hkv * n_split workgroups of 4 wavefronts (8 for heads of
 //             512 with up to 4 rows per lane group, and for heads of 256 with
-//             up to 2 when the grid is one round); consecutive logical ids
+//             up to 4 when the grid is one round); consecutive logical ids
 //             (the splits of one (b, kv head)) share an XCD. n_split fills
 //             whole rounds of 256 workgroups (decode_num_splits).
 //   rows      r = s * G + g (query token s, head g of the group), R <= 16;
 //             the 16 rows of the matrix-core tile are padded with zeros.
 //   live      [lo, hi): the first and last key any row may attend, found from
-//             the bias (or from the rules); split i takes an even share of it.
+//             the bias (or from the rules: the same keys, pads at the ends of
+//             the causal/window interval excluded, so both forms split alike
+//             and give the same bits); split i takes an even share of it.
 //   block     16 keys per wavefront step (block i by one wavefront: i mod
 //             NW, or unevenly between the two wavefronts of a SIMD, see
 //             blk_wave):
@@ -107,15 +109,17 @@ template <int D, int DV, int NR>
 constexpr int decode_waves() {
   return (NR <= 4 && (D > DV ? D : DV) >= 512) ? 8 : 4;
 }
-// Heads of 256 with up to 2 rows per lane group also have an eight-wavefront
+// Heads of 256 with up to 4 rows per lane group also have an eight-wavefront
 // form (two per SIMD, one block in flight each, blocks dealt as for head 512),
 // launched when the grid is one round of at most 256 workgroups: the sliding
-// decode step (B 8, Hkv 8, 4 splits) 20.45 -> 20.0 us, its circular form 20.7
-// -> 20.0. Above 256 workgroups the four-wavefront form stays, whose
-// workgroups can share a CU (B 12: 28.6 against 34.3 us with eight).
+// decode step (B 8, Hkv 8, 4 splits) 20.45 -> 20.0 us with 2 rows per KV head,
+// 23.3 -> 21.5 us with 4, its circular form 20.7 -> 20.0. Above 256
+// workgroups the four-wavefront form stays, whose workgroups (up to 2 rows)
+// can share a CU (B 12: 28.6 against 34.3 us with eight). Not for 8 rows (the
+// eight-wavefront form spills) nor for heads of 128 (15.5 -> 15.7 us, slower).
 template <int D, int DV, int NR>
 constexpr bool decode_has_eight() {
-  return (D > DV ? D : DV) == 256 && NR <= 2;
+  return (D > DV ? D : DV) == 256 && NR <= 4;
 }
 inline bool decode_use_eight(const AttnParams& p) {
   return (int64_t)p.B * p.Hkv * p.n_split <= 256;
@@ -406,9 +410,18 @@ void attn_decode_kernel(AttnParams p) {
     if constexpr (kRules) {
       if (tid < p.S_q) {
         const RowRule rr = make_row_rule(p.nonpad, p.q_start, p.slot_kind, bq, tid, p.S_q, T, p.window, p.circular);
+        // whether a pad slot ends one of the row's causal/window intervals:
+        // then the interval is wider than the keys the row allows (the kinds
+        // at the ends are loaded in the same round trip as the query slot's)
+        int pad_end = 0;
+        if (p.slot_kind) {
+          const int32_t* kr = p.slot_kind + bq * T;
+          if (rr.lo <= rr.hi) pad_end |= (kr[rr.lo] < 0) | (kr[rr.hi] < 0);
+          if (rr.lo2 <= rr.hi2) pad_end |= (kr[rr.lo2] < 0) | (kr[rr.hi2] < 0);
+        }
         int32_t* d = s_rule[tid];
         d[0] = rr.np32; d[1] = rr.lo; d[2] = rr.hi; d[3] = rr.blk;
-        d[4] = rr.lo2; d[5] = rr.hi2; d[6] = rr.kind_q; d[7] = 0;
+        d[4] = rr.lo2; d[5] = rr.hi2; d[6] = rr.kind_q; d[7] = pad_end;
       }
     }
   };
@@ -572,17 +585,35 @@ void attn_decode_kernel(AttnParams p) {
       make_rules(b);
     }
     __syncthreads();
+    bool any_block = false, pad_end = false;
+    for (int s = 0; s < p.S_q; ++s) {
+      any_block |= s_rule[s][6] > 0;
+      pad_end |= s_rule[s][7] != 0;
+    }
     int lo = INT32_MAX, hi = -1;
-    if (tid < p.S_q) {
+    if (tid < p.S_q && !pad_end) {
       // the row's causal/window key interval(s) below nonpad (a circular
-      // cache's may wrap round into a second one)
+      // cache's may wrap round into a second one), exact at both ends
       const int32_t* d = s_rule[tid];
       if (d[1] <= d[2]) { lo = d[1]; hi = d[2]; }
       if (d[4] <= d[5]) { lo = min(lo, d[4]); hi = max(hi, d[5]); }
     }
-    bool any_block = false;
-    for (int s = 0; s < p.S_q; ++s) any_block |= s_rule[s][6] > 0;
-    if (any_block) {
+    if (pad_end) {
+      // a pad ends an interval: the first and last key that some row allows,
+      // from the kinds of every valid slot (the bias variant's scan finds the
+      // same two keys in the bias)
+      const int32_t* kr = p.slot_kind + b * T;
+      const int np = s_rule[0][0];
+      for (int j = tid; j < np; j += kDecThreads) {
+        const int32_t kj = kr[j];
+        for (int s = 0; s < p.S_q; ++s) {
+          const int32_t* d = s_rule[s];
+          RowRule rr;
+          rr.np32 = d[0]; rr.lo = d[1]; rr.hi = d[2]; rr.blk = d[3]; rr.lo2 = d[4]; rr.hi2 = d[5];
+          if (rr.allowed(j, kj)) { lo = min(lo, j); hi = max(hi, j); break; }
+        }
+      }
+    } else if (any_block) {
       const int32_t* kr = p.slot_kind + b * T;
       const int np = s_rule[0][0];   // valid slots of the row
       for (int j = tid; j < np; j += kDecThreads) {

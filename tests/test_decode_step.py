@@ -108,6 +108,62 @@ def test_step_edges():
     check_step(w, step)
 
 
+def _with_pads(w: wl.Workload) -> wl.Step:
+    """The workload's step with pad slots placed at the ends of the batch rows'
+    causal/window intervals (and elsewhere), one pattern per row."""
+    st = w.steps[0]
+    kind = torch.zeros((w.B, w.max_seq), dtype=torch.int32)
+    for b in range(w.B):
+        n = int(st.nonpad[b])
+        q = n - 1
+        lo = max(q - w.window + 1, 0) if w.window > 0 else 0
+        pattern = b % 8
+        if pattern == 1:
+            kind[b, :min(75, n)] = wl.PAD                 # leading pads
+        elif pattern == 2:
+            kind[b, :max(n - 200, 1)] = wl.PAD            # all but the last 200 keys
+        elif pattern == 3:
+            kind[b, max(n - 3, 0):n] = wl.PAD             # trailing pads, the query slot among them
+        elif pattern == 4:
+            kind[b, lo + 20:lo + 50] = wl.PAD             # inside the interval only: ends exact
+        elif pattern == 5:
+            kind[b, :n] = wl.PAD                          # every valid slot: no live key
+        elif pattern == 6:
+            kind[b, lo:lo + 9] = wl.PAD                   # the interval's first keys
+        elif pattern == 7:
+            kind[b, lo] = wl.PAD                          # exactly the first key
+            kind[b, q] = wl.PAD                           # and the last
+    return wl.Step(st.q, st.k_new, st.v_new, st.write_indices, st.nonpad, st.q_start, kind)
+
+
+PAD_CASES = {
+    # 2 and 4 rows per lane group at head 256 (eight wavefronts), head 512, head 128
+    "sliding_g2": lambda: wl.decode_sliding(B=8, Hq=16, Hkv=8, D=256, max_seq=2048, window=700,
+                                            nonpad_lo=400),
+    "sliding_g4": lambda: wl.decode_sliding(B=8, Hq=32, Hkv=8, D=256, max_seq=2048, window=700,
+                                            nonpad_lo=400),
+    "full_d512": lambda: wl.decode_full(B=8, Hq=16, Hkv=4, D=512, max_seq=2048, nonpad_lo=400),
+    "full_d128": lambda: wl.decode_full(B=16, Hq=32, Hkv=8, D=128, max_seq=1500, nonpad_lo=300),
+}
+
+
+@pytest.mark.parametrize("name", list(PAD_CASES))
+def test_step_pad_ends(name):
+    """Pad slots at the ends of the causal/window interval: the rules form (the
+    fused step's and attn_bias_gqa_fwd's without a bias) must find the same live
+    key range as a scan of the bias, or its splits would sum in another order.
+    Outputs of many rows and heads, so that a changed order shows through the
+    bf16 rounding of the output."""
+    w = PAD_CASES[name]()
+    step = _with_pads(w)
+    announce(f"decode step pad ends {w.name}")
+    check_step(w, step)
+    _, o_bias = gpu_step(w, step, dev(w.k_cache.clone()), dev(w.v_cache.clone()), rules=False)
+    _, o_rules = gpu_step(w, step, dev(w.k_cache.clone()), dev(w.v_cache.clone()), rules=True)
+    torch.cuda.synchronize()
+    assert same_bits(o_bias, o_rules), "rules form differs from the bias form"
+
+
 FULL_STEP = {
     "decode_sliding": wl.decode_sliding,
     "decode_full": wl.decode_full,
