@@ -7,9 +7,11 @@ window or none, image blocks, left padding, softcap, bf16 or fp32, bias
 variant with a bf16 or fp32 bias, or the in-kernel rules) and runs TensorScatter
 of K and V, the bias build and the attention on both sides: the caches and the
 bias must match bit for bit, the output within the stated tolerance, and rows
-with no allowed key must be exact zeros. A bf16 decode shape also runs the
-fused decode step (scatters, bias and attention in one launch), which must give
-the separate calls' caches, bias and output bit for bit. Outputs, biases and
+with no allowed key must be exact zeros. A decode-sized shape (S_q * G <= 16)
+also runs the attention's other form (bias <-> rules), which must give the
+same bits, and in bf16 the fused decode step (scatters, bias and attention in
+one launch), which must give the separate calls' caches, bias and output bit
+for bit. Outputs, biases and
 workspaces start poisoned, so an unwritten element fails. Sizes keep the fp64
 oracle to well under a second per case.
 """
@@ -26,7 +28,7 @@ from pipeline import announce, check_parity, dead_rows, dev, fused_step, gpu_ste
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 160
+N_CASES = 240
 PAIRS_BF16 = [(64, 64), (128, 128), (256, 256), (512, 512), (256, 512), (512, 256)]
 PAIRS_F32 = [(64, 64), (128, 128), (64, 128)]
 
@@ -114,6 +116,14 @@ def test_fuzz_case(i):
     valid = step.nonpad.clamp(0, w.max_seq) if w.circular else step.nonpad
     got = out.float().cpu().numpy().astype(np.float64)
     check_parity(got, ref, w.dtype, dead_rows(bias_ref, valid, w.Hq), f"fuzz{i}")
+    # a decode shape (S_q * Hq / Hkv <= 16): the bias and the rules forms of
+    # the attention take the same kernel and must give the same bits (the
+    # rules form finds the same live key range as a scan of the bias)
+    if step.S_q * (w.Hq // w.Hkv) <= 16:
+        k3, v3 = dev(w.k_cache.clone()), dev(w.v_cache.clone())
+        _, out3 = gpu_step(w, step, k3, v3, rules=not rules, bias_dtype=bias_dtype,
+                           default_q_start=default_q_start, softcap=softcap)
+        assert same_bits(out3, out), "bias and rules forms differ"
     # a bf16 decode shape (S_q * Hq / Hkv <= 16, head sizes of the split-KV
     # kernel): the fused decode step must reproduce the separate calls bit for
     # bit (caches, the bias when built, output)
